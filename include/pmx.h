@@ -1,0 +1,221 @@
+/*
+ * pmx.h -- PRISM matrix functions for Shampoo/Muon-style preconditioners on
+ * AMD Instinct MI355X (gfx950).  C ABI of libpmx.so.
+ *
+ * Sources of the operations (web pages; section names as printed there):
+ *   [Shampoo blog]     "深度学习中的优化器之Shampoo算法原理与二阶优化机制"
+ *                      (idocdown), sections 2.2, 2.3, 3.1, 6.3.
+ *   [PRISM summary]    "PRISM：分布无关的自适应矩阵函数计算以加速神经网络训练"
+ *                      (euno.news summary of arXiv 2601.22137), "方法论".
+ *   [PRISM synthesis]  "Sintesi Tecnica: PRISM" (gist.science), Part I and
+ *                      Part II ("Adaptive Polynomial Fitting",
+ *                      "Randomized Sketching").
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major.  "ld" is the distance in elements between
+ *     consecutive rows and must be >= the number of columns.  Batched forms
+ *     take a batch count and, per matrix argument, a batch stride in elements.
+ *   - Every matrix, workspace and info pointer is a DEVICE pointer owned by
+ *     the caller; the library never allocates, frees or retains device memory
+ *     and keeps no pointer after a call returns.  Scalars are host values.
+ *   - Every call validates its arguments on the host first.  On any error it
+ *     returns a non-zero pmx_status and enqueues NOTHING.  On PMX_OK all work
+ *     has been enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting for the device.
+ *   - Numerical outcomes of the iterative functions (converged, stagnated,
+ *     ...) are written asynchronously to the caller's device-resident
+ *     pmx_matfn_info array (one element per matrix); the host never waits.
+ *   - Input and output matrices of one call must not overlap, except that
+ *     pmx_shampoo_stats_update updates L and R in place.  Overlap of
+ *     distinct arguments is reported as PMX_ERR_ALIAS.
+ *   - A handle serves one device; use one handle per host thread.  Calls on
+ *     one stream are ordered; calls sharing a workspace must be ordered.
+ */
+#ifndef PMX_H
+#define PMX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PMX_VERSION_MAJOR 0
+#define PMX_VERSION_MINOR 1
+#define PMX_OPTS_VERSION 1
+#define PMX_TRACE_LEN 64   /* alpha / residual trace entries kept per stage */
+#define PMX_MAX_SKETCH 16  /* largest supported sketch width p */
+
+/* Synchronous result of every call. */
+typedef enum {
+  PMX_OK = 0,
+  PMX_ERR_INVALID_VALUE = 1, /* bad size, ld, pointer, option or exponent */
+  PMX_ERR_NOT_SUPPORTED = 2, /* valid request this build does not implement */
+  PMX_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than the query says */
+  PMX_ERR_ALIAS = 4,         /* an output overlaps an input or another output */
+  PMX_ERR_HIP = 5            /* the HIP runtime reported an error */
+} pmx_status;
+
+/* Asynchronous numerical outcome, written to pmx_matfn_info.status. */
+typedef enum {
+  PMX_RUNNING = -1,  /* never left in a finished call's info */
+  PMX_CONVERGED = 0, /* residual r_k <= tol */
+  PMX_MAXITER = 1,   /* max_iter updates done without reaching tol */
+  PMX_STAGNATED = 2, /* r_{k-1} < 1e-2 and r_k > 0.9 r_{k-1}: rounding floor */
+  PMX_NONFINITE = 3, /* NaN/Inf in the input, the scale or the residual */
+  PMX_DIVERGED = 4   /* r_k > 2: input not positive definite */
+} pmx_numeric;
+
+typedef enum { PMX_F32 = 0, PMX_BF16 = 1 } pmx_dtype;
+
+/* Operation codes for pmx_workspace_size. */
+typedef enum {
+  PMX_OP_STATS = 0,
+  PMX_OP_INV_ROOT = 1,
+  PMX_OP_POLAR = 2,
+  PMX_OP_APPLY = 3
+} pmx_op;
+
+/*
+ * Options of the iterative matrix functions ([PRISM synthesis] Part I and
+ * Part II).  pmx_matfn_opts_default fills the defaults given per field.
+ */
+typedef struct {
+  int32_t struct_version; /* must be PMX_OPTS_VERSION */
+  int32_t degree;         /* d in {1, 2}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2 */
+  int32_t sketch_p;       /* Gaussian sketch width p, 1..PMX_MAX_SKETCH; default 8 */
+  int32_t max_iter;       /* updates per stage, 1..1000; default 100 */
+  int32_t accelerate;     /* 1: fitted alpha (PRISM); 0: alpha = Taylor c_d; default 1 */
+  float alpha_lo;         /* alpha interval; NaN selects the default:       */
+  float alpha_hi;         /*   d = 1: [1/2, 1], d = 2: [3/8, 1.47]          */
+  float tol;              /* stop when ||R_k||_F / sqrt(n) <= tol; default 1e-6 */
+  uint64_t seed;          /* key of the Philox4x32-10 sketch stream; default 0 */
+} pmx_matfn_opts;
+
+/*
+ * Per-matrix outcome, device resident, written by the library.
+ * residual[s] / rtrace[s][k] hold r_k = ||R_k||_F / sqrt(n) of stage s
+ * (stage 1 only for the chained inverse 4th root), alpha[s][k] the fitted
+ * coefficient of update k (first PMX_TRACE_LEN entries; unused entries 0).
+ */
+typedef struct {
+  int32_t status;          /* pmx_numeric of the whole call (worst stage) */
+  int32_t iters[2];        /* updates per stage */
+  int32_t gemms;           /* dense products (n x n x n, or the polar shapes) */
+  int32_t sketch_products; /* skinny n x n x p products of the alpha fit */
+  int32_t stages;          /* stages run */
+  float scale;             /* c = ||A||_F (or ||G||_F) used to scale the input */
+  float residual[2];       /* final r per stage */
+  float alpha[2][PMX_TRACE_LEN];
+  float rtrace[2][PMX_TRACE_LEN];
+} pmx_matfn_info;
+
+typedef struct pmx_context* pmx_handle;
+
+/* Create a handle bound to HIP device `device` (loads nothing else; no
+ * device memory is allocated).  Returns PMX_ERR_INVALID_VALUE for a NULL
+ * out-pointer or a device index out of range, PMX_ERR_NOT_SUPPORTED for a
+ * device that is not gfx950. */
+pmx_status pmx_create(pmx_handle* handle, int device);
+pmx_status pmx_destroy(pmx_handle handle);
+const char* pmx_status_string(pmx_status status);
+/* Library version as major * 1000 + minor. */
+int pmx_version(void);
+
+/* Fill `opts` with the defaults listed in pmx_matfn_opts. */
+pmx_status pmx_matfn_opts_default(pmx_matfn_opts* opts);
+
+/*
+ * Workspace bytes a call needs.  m, n are the shapes as passed to the call
+ * (for PMX_OP_INV_ROOT m is ignored; for PMX_OP_STATS and PMX_OP_APPLY the
+ * gradient is m x n).  `opts` may be NULL for the operations without options.
+ * The workspace must be 256-byte aligned.  `handle` may be NULL (the sizes
+ * do not depend on the device), so sizes can be queried without a GPU.
+ */
+pmx_status pmx_workspace_size(pmx_handle handle, pmx_op op, int m, int n, int batch,
+                              pmx_dtype dtype, const pmx_matfn_opts* opts, size_t* bytes);
+
+/*
+ * Shampoo statistics update ([Shampoo blog] sections 2.2 and 2.3, step 2):
+ *   L <- beta L + (1 - beta) G G^T + eps I   (m x m)
+ *   R <- beta R + (1 - beta) G^T G + eps I   (n x n)
+ * in place on L and R (full symmetric storage, fp32).  G is m x n with
+ * element type `dtype` (fp32 or bf16; products accumulate in fp32).
+ * Either L or R may be NULL to skip that side.  Requires 0 <= beta <= 1.
+ */
+pmx_status pmx_shampoo_stats_update(pmx_handle handle, const void* G, pmx_dtype dtype,
+                                    int m, int n, int ldg, float* L, int ldl, float* R,
+                                    int ldr, float beta, float eps, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+pmx_status pmx_shampoo_stats_update_batched(pmx_handle handle, const void* G,
+                                            pmx_dtype dtype, int m, int n, int ldg,
+                                            int64_t stride_g, float* L, int ldl,
+                                            int64_t stride_l, float* R, int ldr,
+                                            int64_t stride_r, float beta, float eps,
+                                            int batch, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
+ * Inverse p-th root by PRISM-accelerated coupled Newton-Schulz
+ * ([Shampoo blog] section 3.1; [PRISM synthesis] Part I, Part II):
+ *   c = ||A||_F, Y_0 = A / c, Z_0 = I;  per update k:
+ *   R_k = I - Z_k Y_k, alpha_k fitted on a Gaussian sketch of R_k,
+ *   g = f_{d-1}(R_k) + alpha_k R_k^d, Y <- Y g, Z <- g Z.
+ * p = 2: X = A^{-1/2} = Z / sqrt(c), X_aux = A^{1/2} = sqrt(c) Y.
+ * p = 4: a second stage from the first stage's Y; X = A^{-1/4},
+ *        X_aux = A^{1/4}.
+ * A is n x n fp32, symmetric positive definite (full storage read).  X_aux
+ * may be NULL.  info_dev points to `batch` pmx_matfn_info (may be NULL).
+ * opts may be NULL for the defaults.
+ */
+pmx_status pmx_matfn_inv_root(pmx_handle handle, const float* A, int n, int lda, int p,
+                              float* X, int ldx, float* X_aux, int ldaux,
+                              const pmx_matfn_opts* opts, pmx_matfn_info* info_dev,
+                              void* workspace, size_t workspace_bytes, void* stream);
+pmx_status pmx_matfn_inv_root_batched(pmx_handle handle, const float* A, int n, int lda,
+                                      int64_t stride_a, int p, float* X, int ldx,
+                                      int64_t stride_x, float* X_aux, int ldaux,
+                                      int64_t stride_aux, int batch,
+                                      const pmx_matfn_opts* opts,
+                                      pmx_matfn_info* info_dev, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Polar factor U of G (m x n) by PRISM-accelerated Newton-Schulz
+ * ([PRISM synthesis] Part I: sign/polar functions; Part II):
+ *   X_0 = G / ||G||_F, R_k = I - X_k^T X_k, X <- X g(R_k).
+ * For m < n the iteration runs on G^T.  G and U have element type `dtype`
+ * (fp32: fp32 iterates; bf16: bf16 iterates with fp32 accumulation).
+ */
+pmx_status pmx_matfn_polar(pmx_handle handle, const void* G, pmx_dtype dtype, int m, int n,
+                           int ldg, void* U, int ldu, const pmx_matfn_opts* opts,
+                           pmx_matfn_info* info_dev, void* workspace,
+                           size_t workspace_bytes, void* stream);
+pmx_status pmx_matfn_polar_batched(pmx_handle handle, const void* G, pmx_dtype dtype,
+                                   int m, int n, int ldg, int64_t stride_g, void* U,
+                                   int ldu, int64_t stride_u, int batch,
+                                   const pmx_matfn_opts* opts, pmx_matfn_info* info_dev,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Preconditioned step ([Shampoo blog] sections 2.1 and 2.3, step 4):
+ *   P = Linv * G * Rinv,  Linv m x m, G m x n, Rinv n x n (fp32),
+ * G and P of element type `dtype`; accumulation in fp32.
+ */
+pmx_status pmx_precond_apply(pmx_handle handle, const float* Linv, int ldl, const void* G,
+                             pmx_dtype dtype, int m, int n, int ldg, const float* Rinv,
+                             int ldr, void* P, int ldp, void* workspace,
+                             size_t workspace_bytes, void* stream);
+pmx_status pmx_precond_apply_batched(pmx_handle handle, const float* Linv, int ldl,
+                                     int64_t stride_l, const void* G, pmx_dtype dtype,
+                                     int m, int n, int ldg, int64_t stride_g,
+                                     const float* Rinv, int ldr, int64_t stride_r, void* P,
+                                     int ldp, int64_t stride_p, int batch, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMX_H */

@@ -1,0 +1,786 @@
+// Host runtime and C ABI of libpmx: argument validation, workspace layout and
+// the launch sequences of the four operations.  Every sequence is enqueued
+// in full on the caller's stream; iteration kernels skip themselves on the
+// device once their matrix has finished, so no call waits for the GPU.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "pmx_kernels.h"
+
+struct pmx_context {
+  int device;
+  int num_cu;
+};
+
+namespace pmx {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxN = 32768;
+constexpr int kMaxIter = 1000;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Current-device guard: make the handle's device current for the call and
+// restore the caller's device afterwards.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) {
+      ok = false;
+      return;
+    }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+// Byte extent of a (strided batch of) row-major matrices.
+struct Extent {
+  uintptr_t lo = 0, hi = 0;
+  bool valid = false;
+};
+
+Extent extent_of(const void* p, int rows, int cols, int64_t ld, int64_t stride, int batch,
+                 size_t elem) {
+  Extent e;
+  if (!p || rows <= 0 || cols <= 0) return e;
+  const int64_t last = (int64_t)(batch - 1) * stride + (int64_t)(rows - 1) * ld + cols;
+  e.lo = (uintptr_t)p;
+  e.hi = e.lo + (uintptr_t)last * elem;
+  e.valid = true;
+  return e;
+}
+
+bool overlap(const Extent& a, const Extent& b) {
+  return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Distinct matrices of one batch must not overlap when written.
+bool batch_layout_ok(int rows, int cols, int64_t ld, int64_t stride, int batch) {
+  if (ld < cols) return false;
+  if (batch > 1 && stride < (int64_t)(rows - 1) * ld + cols) return false;
+  return stride >= 0;
+}
+
+pmx_status from_hip(hipError_t e) { return e == hipSuccess ? PMX_OK : PMX_ERR_HIP; }
+
+#define PMX_TRY(expr)                          \
+  do {                                         \
+    hipError_t _e = (expr);                    \
+    if (_e != hipSuccess) return PMX_ERR_HIP;  \
+  } while (0)
+
+// Taylor coefficient c_j of (1 - xi)^{-1/2}: c_0 = 1, c_j = c_{j-1} (2j - 1) / (2j).
+double taylor(int j) {
+  double c = 1.0;
+  for (int i = 1; i <= j; ++i) c *= (2.0 * i - 1.0) / (2.0 * i);
+  return c;
+}
+
+// Polynomials as coefficient arrays (increasing powers), small fixed size.
+struct Poly {
+  double c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+};
+Poly pmul(const Poly& a, const Poly& b) {
+  Poly r;
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; i + j < 8; ++j) r.c[i + j] += a.c[i] * b.c[j];
+  return r;
+}
+
+// r(xi; alpha) = 1 - (1 - xi) (f + alpha xi^d)^2 with f = sum_{j<d} c_j xi^j,
+// split as A0 + alpha A1 + alpha^2 A2:
+//   A0 = 1 - (1 - xi) f^2,  A1 = -2 (1 - xi) f xi^d,  A2 = -(1 - xi) xi^{2d}.
+AlphaCoef make_coef(int d) {
+  Poly f, om, xd, x2d;
+  for (int j = 0; j < d; ++j) f.c[j] = taylor(j);
+  om.c[0] = 1.0;
+  om.c[1] = -1.0;
+  xd.c[d] = 1.0;
+  x2d.c[2 * d] = 1.0;
+  Poly ff = pmul(f, f);
+  Poly A0 = pmul(om, ff);
+  for (int i = 0; i < 8; ++i) A0.c[i] = -A0.c[i];
+  A0.c[0] += 1.0;
+  Poly A1 = pmul(pmul(om, f), xd);
+  for (int i = 0; i < 8; ++i) A1.c[i] *= -2.0;
+  Poly A2 = pmul(om, x2d);
+  for (int i = 0; i < 8; ++i) A2.c[i] = -A2.c[i];
+  AlphaCoef co;
+  for (int j = 0; j < 6; ++j) {
+    co.a[0][j] = A0.c[j];
+    co.a[1][j] = A1.c[j];
+    co.a[2][j] = A2.c[j];
+  }
+  co.taylor_d = taylor(d);
+  return co;
+}
+
+// Effective options after defaults; returns false if invalid.
+bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out) {
+  pmx_matfn_opts o;
+  pmx_matfn_opts_default(&o);
+  if (in) {
+    if (in->struct_version != PMX_OPTS_VERSION) return false;
+    o = *in;
+  }
+  if (o.degree != 1 && o.degree != 2) return false;
+  if (o.sketch_p < 1 || o.sketch_p > PMX_MAX_SKETCH) return false;
+  if (o.max_iter < 1 || o.max_iter > kMaxIter) return false;
+  if (o.accelerate != 0 && o.accelerate != 1) return false;
+  if (isnan(o.alpha_lo) != isnan(o.alpha_hi)) return false;
+  if (isnan(o.alpha_lo)) {
+    o.alpha_lo = o.degree == 1 ? 0.5f : 0.375f;
+    o.alpha_hi = o.degree == 1 ? 1.0f : 1.47f;
+  }
+  if (!isfinite(o.alpha_lo) || !isfinite(o.alpha_hi) || o.alpha_lo > o.alpha_hi) return false;
+  if (!isfinite(o.tol) || o.tol < 0.f) return false;
+  *out = o;
+  return true;
+}
+
+IterCfg make_cfg(const pmx_matfn_opts& o, int n, pmx_matfn_info* info) {
+  IterCfg c;
+  c.n = n;
+  c.degree = o.degree;
+  c.p = o.sketch_p;
+  c.max_iter = o.max_iter;
+  c.accelerate = o.accelerate;
+  c.lo = o.alpha_lo;
+  c.hi = o.alpha_hi;
+  c.tol = o.tol;
+  c.seed_lo = (uint32_t)(o.seed & 0xFFFFFFFFull);
+  c.seed_hi = (uint32_t)(o.seed >> 32);
+  c.info = info;
+  return c;
+}
+
+// ------------------------------------------------------------------ workspace
+struct IterLayout {
+  size_t ctrl, partials, bufs[6], kbuf, total;
+  int64_t buf_stride, kstride, kld, pstride;
+};
+
+// Work buffers of the iterative functions: `nbig` matrices of rows x cols
+// (the iterates) and `nsmall` of cols x cols (R, R^2/g), per batch matrix.
+IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, int nbig,
+                       int nsmall, size_t big_elem) {
+  IterLayout L;
+  size_t off = 0;
+  L.ctrl = off;
+  off = align_up(off + sizeof(Ctrl) * (size_t)batch);
+  L.pstride = std::max<int64_t>(kPartialsPerMatrix, gemm_f32_tiles(cols, cols));
+  L.partials = off;
+  off = align_up(off + sizeof(double) * (size_t)L.pstride * batch);
+  const int64_t big = (int64_t)rows * cols, small = (int64_t)cols * cols;
+  (void)big_elem;
+  L.buf_stride = ((std::max(big, small) + 63) / 64) * 64;  // elements (fp32 slots)
+  for (int i = 0; i < 6; ++i) {
+    L.bufs[i] = 0;
+    if (i < nbig + nsmall) {
+      L.bufs[i] = off;
+      off = align_up(off + sizeof(float) * (size_t)L.buf_stride * batch);
+    }
+  }
+  L.kld = (int64_t)(2 * o.degree + 2) * o.sketch_p;
+  L.kstride = (((int64_t)cols * L.kld + 63) / 64) * 64;
+  L.kbuf = off;
+  off = align_up(off + sizeof(float) * (size_t)L.kstride * batch);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+bool ptr_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+GemmParams gemm_base(int M, int N, int K, int batch) {
+  GemmParams g;
+  memset(&g, 0, sizeof(g));
+  g.nprob = 1;
+  g.batch = batch;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return g;
+}
+
+void set_vec(GemmParams& g) {
+  bool v = true;
+  for (int i = 0; i < g.nprob; ++i) {
+    const GemmProblem& p = g.prob[i];
+    v = v && ptr_aligned16(p.a.ptr) && ptr_aligned16(p.b.ptr) && (p.a.ld % 4 == 0) &&
+        (p.b.ld % 4 == 0) && (p.a.stride % 4 == 0) && (p.b.stride % 4 == 0);
+  }
+  g.vec = v ? 1 : 0;
+}
+
+// One PRISM iteration (update k of `stage`) of the sketch / alpha / g part,
+// shared by the square-root and polar sequences.  R and R2 are cols x cols.
+hipError_t enqueue_alpha_and_g(void* ws, const IterLayout& L, const pmx_matfn_opts& o,
+                               const IterCfg& cfg, const AlphaCoef& coef, int n, int batch,
+                               int stage, int k, float* R, float* R2, float* gdst,
+                               hipStream_t s) {
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  float* kbuf = at<float>(ws, L.kbuf);
+  const int d = o.degree, pp = o.sketch_p;
+  hipError_t e;
+  if (d == 2) {
+    GemmParams g = gemm_base(n, n, n, batch);
+    g.prob[0].a = {R, n, L.buf_stride};
+    g.prob[0].b = {R, n, L.buf_stride};
+    g.prob[0].c = R2;
+    g.prob[0].ldc = n;
+    g.prob[0].stride_c = L.buf_stride;
+    g.ctrl = ctrl;
+    set_vec(g);
+    if ((e = launch_gemm_f32(g, false, false, EPI_STORE, s)) != hipSuccess) return e;
+  }
+  if (o.accelerate) {
+    SketchParams sp;
+    sp.kbuf = kbuf;
+    sp.kld = L.kld;
+    sp.kstride = L.kstride;
+    sp.n = n;
+    sp.p = pp;
+    sp.k = k;
+    sp.stage = stage;
+    sp.seed_lo = cfg.seed_lo;
+    sp.seed_hi = cfg.seed_hi;
+    sp.ctrl = ctrl;
+    if ((e = launch_sketch(sp, batch, s)) != hipSuccess) return e;
+    SkinnyParams kp;
+    memset(&kp, 0, sizeof(kp));
+    kp.kbuf = kbuf;
+    kp.kld = L.kld;
+    kp.kstride = L.kstride;
+    kp.n = n;
+    kp.ctrl = ctrl;
+    auto job = [&](const float* m, int ic, int oc, int pw) {
+      SkinnyJob j;
+      j.mat = m;
+      j.mat_ld = n;
+      j.mat_stride = L.buf_stride;
+      j.in_col = ic;
+      j.out_col = oc;
+      j.pow = pw;
+      return j;
+    };
+    if (d == 2) {
+      // K1 = R S / s, K2 = R^2 S / s^2; [K3 | K4] = R^2 [K1 | K2] / s^2; K5 = R^2 K3 / s^2
+      kp.q = pp;
+      kp.job[0] = job(R, 0, pp, 1);
+      kp.job[1] = job(R2, 0, 2 * pp, 2);
+      if ((e = launch_skinny(kp, 2, batch, s)) != hipSuccess) return e;
+      kp.q = 2 * pp;
+      kp.job[0] = job(R2, pp, 3 * pp, 2);
+      if ((e = launch_skinny(kp, 1, batch, s)) != hipSuccess) return e;
+      kp.q = pp;
+      kp.job[0] = job(R2, 3 * pp, 5 * pp, 2);
+      if ((e = launch_skinny(kp, 1, batch, s)) != hipSuccess) return e;
+    } else {
+      // K_j = R K_{j-1} / s, j = 1..3
+      kp.q = pp;
+      for (int j = 1; j <= 3; ++j) {
+        kp.job[0] = job(R, (j - 1) * pp, j * pp, 1);
+        if ((e = launch_skinny(kp, 1, batch, s)) != hipSuccess) return e;
+      }
+    }
+  }
+  AlphaParams ap;
+  ap.kbuf = kbuf;
+  ap.kld = L.kld;
+  ap.kstride = L.kstride;
+  ap.ctrl = ctrl;
+  ap.cfg = cfg;
+  ap.coef = coef;
+  if ((e = launch_alpha(ap, batch, s)) != hipSuccess) return e;
+  FormGParams fp;
+  fp.r = R;
+  fp.r2 = (d == 2) ? R2 : nullptr;
+  fp.dst = gdst;
+  fp.stride = L.buf_stride;
+  fp.n = n;
+  fp.degree = d;
+  fp.c0 = (float)taylor(0);
+  fp.c1 = (float)taylor(1);
+  fp.ctrl = ctrl;
+  return launch_form_g(fp, batch, s);
+}
+
+}  // namespace
+}  // namespace pmx
+
+using namespace pmx;
+
+// ======================================================================= ABI
+extern "C" {
+
+const char* pmx_status_string(pmx_status s) {
+  switch (s) {
+    case PMX_OK: return "PMX_OK";
+    case PMX_ERR_INVALID_VALUE: return "PMX_ERR_INVALID_VALUE: invalid argument";
+    case PMX_ERR_NOT_SUPPORTED: return "PMX_ERR_NOT_SUPPORTED: not supported by this build";
+    case PMX_ERR_WORKSPACE: return "PMX_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case PMX_ERR_ALIAS: return "PMX_ERR_ALIAS: overlapping input/output arguments";
+    case PMX_ERR_HIP: return "PMX_ERR_HIP: HIP runtime error";
+  }
+  return "unknown pmx_status";
+}
+
+int pmx_version(void) { return PMX_VERSION_MAJOR * 1000 + PMX_VERSION_MINOR; }
+
+pmx_status pmx_matfn_opts_default(pmx_matfn_opts* o) {
+  if (!o) return PMX_ERR_INVALID_VALUE;
+  o->struct_version = PMX_OPTS_VERSION;
+  o->degree = 2;
+  o->sketch_p = 8;
+  o->max_iter = 100;
+  o->accelerate = 1;
+  o->alpha_lo = NAN;
+  o->alpha_hi = NAN;
+  o->tol = 1e-6f;
+  o->seed = 0;
+  return PMX_OK;
+}
+
+pmx_status pmx_create(pmx_handle* handle, int device) {
+  if (!handle) return PMX_ERR_INVALID_VALUE;
+  *handle = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess) return PMX_ERR_HIP;
+  if (device < 0 || device >= count) return PMX_ERR_INVALID_VALUE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return PMX_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return PMX_ERR_NOT_SUPPORTED;
+  pmx_context* c = new (std::nothrow) pmx_context;
+  if (!c) return PMX_ERR_HIP;
+  c->device = device;
+  c->num_cu = prop.multiProcessorCount;
+  *handle = c;
+  return PMX_OK;
+}
+
+pmx_status pmx_destroy(pmx_handle h) {
+  if (!h) return PMX_ERR_INVALID_VALUE;
+  delete h;
+  return PMX_OK;
+}
+
+static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
+  return iter_layout(n, n, batch, o, 4, 2, sizeof(float)).total;
+}
+static size_t polar_ws(int m, int n, int batch, const pmx_matfn_opts& o) {
+  const int rows = std::max(m, n), cols = std::min(m, n);
+  return iter_layout(rows, cols, batch, o, 2, 2, sizeof(float)).total;
+}
+static size_t apply_ws(int m, int n, int batch) {
+  return align_up(sizeof(float) * (size_t)m * n * batch);
+}
+
+pmx_status pmx_workspace_size(pmx_handle h, pmx_op op, int m, int n, int batch,
+                              pmx_dtype dtype, const pmx_matfn_opts* opts, size_t* bytes) {
+  (void)h;  // sizes do not depend on the device; the handle may be NULL
+  if (!bytes || batch < 1 || n < 1 || n > kMaxN) return PMX_ERR_INVALID_VALUE;
+  if (dtype != PMX_F32 && dtype != PMX_BF16) return PMX_ERR_INVALID_VALUE;
+  pmx_matfn_opts o;
+  switch (op) {
+    case PMX_OP_STATS:
+      if (m < 1 || m > kMaxN) return PMX_ERR_INVALID_VALUE;
+      *bytes = 0;
+      return PMX_OK;
+    case PMX_OP_APPLY:
+      if (m < 1 || m > kMaxN) return PMX_ERR_INVALID_VALUE;
+      *bytes = apply_ws(m, n, batch);
+      return PMX_OK;
+    case PMX_OP_INV_ROOT:
+      if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
+      *bytes = inv_root_ws(n, batch, o);
+      return PMX_OK;
+    case PMX_OP_POLAR:
+      if (m < 1 || m > kMaxN) return PMX_ERR_INVALID_VALUE;
+      if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
+      *bytes = polar_ws(m, n, batch, o);
+      return PMX_OK;
+  }
+  return PMX_ERR_INVALID_VALUE;
+}
+
+static pmx_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return PMX_OK;
+  if (!ws || have < need || ((uintptr_t)ws % kAlign) != 0) return PMX_ERR_WORKSPACE;
+  return PMX_OK;
+}
+
+// ------------------------------------------------------------------ stats
+pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dtype dtype,
+                                            int m, int n, int ldg, int64_t sg, float* L,
+                                            int ldl, int64_t sl, float* R, int ldr,
+                                            int64_t sr, float beta, float eps, int batch,
+                                            void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!h || !G || m < 1 || n < 1 || m > kMaxN || n > kMaxN || batch < 1)
+    return PMX_ERR_INVALID_VALUE;
+  if (!L && !R) return PMX_ERR_INVALID_VALUE;
+  if (!(beta >= 0.f && beta <= 1.f) || !isfinite(eps)) return PMX_ERR_INVALID_VALUE;
+  if (dtype != PMX_F32 && dtype != PMX_BF16) return PMX_ERR_INVALID_VALUE;
+  if (!batch_layout_ok(m, n, ldg, sg, 1) || sg < 0) return PMX_ERR_INVALID_VALUE;
+  if (batch > 1 && sg < (int64_t)(m - 1) * ldg + n && sg != 0) return PMX_ERR_INVALID_VALUE;
+  if (L && !batch_layout_ok(m, m, ldl, sl, batch)) return PMX_ERR_INVALID_VALUE;
+  if (R && !batch_layout_ok(n, n, ldr, sr, batch)) return PMX_ERR_INVALID_VALUE;
+  if (dtype == PMX_BF16) return PMX_ERR_NOT_SUPPORTED;
+  const Extent eg = extent_of(G, m, n, ldg, sg, batch, 4);
+  const Extent el = extent_of(L, m, m, ldl, sl, batch, 4);
+  const Extent er = extent_of(R, n, n, ldr, sr, batch, 4);
+  if (overlap(eg, el) || overlap(eg, er) || overlap(el, er)) return PMX_ERR_ALIAS;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return PMX_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  const float* g = (const float*)G;
+  const float omb = 1.f - beta;
+  if (L) {
+    GemmParams p = gemm_base(m, m, n, batch);
+    p.prob[0].a = {g, ldg, sg};
+    p.prob[0].b = {g, ldg, sg};
+    p.prob[0].c = L;
+    p.prob[0].ldc = ldl;
+    p.prob[0].stride_c = sl;
+    p.beta = beta;
+    p.omb = omb;
+    p.eps = eps;
+    set_vec(p);
+    PMX_TRY(launch_gemm_f32(p, false, true, EPI_EMA, s));
+  }
+  if (R) {
+    GemmParams p = gemm_base(n, n, m, batch);
+    p.prob[0].a = {g, ldg, sg};
+    p.prob[0].b = {g, ldg, sg};
+    p.prob[0].c = R;
+    p.prob[0].ldc = ldr;
+    p.prob[0].stride_c = sr;
+    p.beta = beta;
+    p.omb = omb;
+    p.eps = eps;
+    set_vec(p);
+    PMX_TRY(launch_gemm_f32(p, true, false, EPI_EMA, s));
+  }
+  return PMX_OK;
+}
+
+pmx_status pmx_shampoo_stats_update(pmx_handle h, const void* G, pmx_dtype dtype, int m,
+                                    int n, int ldg, float* L, int ldl, float* R, int ldr,
+                                    float beta, float eps, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return pmx_shampoo_stats_update_batched(h, G, dtype, m, n, ldg, 0, L, ldl, 0, R, ldr, 0,
+                                          beta, eps, 1, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ inverse roots
+pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int lda,
+                                      int64_t sa, int p, float* X, int ldx, int64_t sx,
+                                      float* XA, int ldaux, int64_t saux, int batch,
+                                      const pmx_matfn_opts* opts, pmx_matfn_info* info,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !A || !X || n < 1 || n > kMaxN || batch < 1) return PMX_ERR_INVALID_VALUE;
+  if (p != 2 && p != 4) return PMX_ERR_INVALID_VALUE;
+  pmx_matfn_opts o;
+  if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
+  if (lda < n || sa < 0 || (batch > 1 && sa != 0 && sa < (int64_t)(n - 1) * lda + n))
+    return PMX_ERR_INVALID_VALUE;
+  if (!batch_layout_ok(n, n, ldx, sx, batch)) return PMX_ERR_INVALID_VALUE;
+  if (XA && !batch_layout_ok(n, n, ldaux, saux, batch)) return PMX_ERR_INVALID_VALUE;
+  const IterLayout Lw = iter_layout(n, n, batch, o, 4, 2, sizeof(float));
+  pmx_status st = check_ws(ws, ws_bytes, Lw.total);
+  if (st != PMX_OK) return st;
+  const Extent ea = extent_of(A, n, n, lda, sa, batch, 4);
+  const Extent ex = extent_of(X, n, n, ldx, sx, batch, 4);
+  const Extent eaux = extent_of(XA, n, n, ldaux, saux, batch, 4);
+  Extent ew;
+  ew.lo = (uintptr_t)ws;
+  ew.hi = ew.lo + Lw.total;
+  ew.valid = true;
+  Extent ei = extent_of(info, 1, (int)sizeof(pmx_matfn_info), 0, sizeof(pmx_matfn_info), batch, 1);
+  if (overlap(ea, ex) || overlap(ea, eaux) || overlap(ex, eaux) || overlap(ew, ea) ||
+      overlap(ew, ex) || overlap(ew, eaux) || overlap(ei, ea) || overlap(ei, ex) ||
+      overlap(ei, eaux) || overlap(ei, ew))
+    return PMX_ERR_ALIAS;
+
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return PMX_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  Ctrl* ctrl = at<Ctrl>(ws, Lw.ctrl);
+  double* partials = at<double>(ws, Lw.partials);
+  float* Yb[2] = {at<float>(ws, Lw.bufs[0]), at<float>(ws, Lw.bufs[1])};
+  float* Zb[2] = {at<float>(ws, Lw.bufs[2]), at<float>(ws, Lw.bufs[3])};
+  float* Rb = at<float>(ws, Lw.bufs[4]);
+  float* R2b = at<float>(ws, Lw.bufs[5]);
+  const IterCfg cfg = make_cfg(o, n, info);
+  const AlphaCoef coef = make_coef(o.degree);
+  const int d = o.degree;
+
+  PMX_TRY(launch_ctrl_reset(ctrl, info, batch, s));
+  PMX_TRY(launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, s));
+  const int stages = (p == 4) ? 2 : 1;
+  for (int stage = 0; stage < stages; ++stage) {
+    StageInitParams ip;
+    ip.a = A;
+    ip.lda = lda;
+    ip.a_stride = sa;
+    ip.ybuf[0] = Yb[0];
+    ip.ybuf[1] = Yb[1];
+    ip.r = Rb;
+    ip.buf_stride = Lw.buf_stride;
+    ip.n = n;
+    ip.stage = stage;
+    ip.ctrl = ctrl;
+    ip.partials = partials;
+    ip.partial_stride = Lw.pstride;
+    ip.cfg = cfg;
+    PMX_TRY(launch_sqrt_stage_init(ip, batch, s));
+    for (int k = 0; k < o.max_iter; ++k) {
+      float* gdst = (k == 0) ? Zb[1] : R2b;
+      PMX_TRY(enqueue_alpha_and_g(ws, Lw, o, cfg, coef, n, batch, stage, k, Rb, R2b, gdst, s));
+      const int cur = k & 1, nxt = cur ^ 1;
+      GemmParams u = gemm_base(n, n, n, batch);
+      u.ctrl = ctrl;
+      u.prob[0].a = {Yb[cur], n, Lw.buf_stride};
+      u.prob[0].b = {gdst, n, Lw.buf_stride};
+      u.prob[0].c = Yb[nxt];
+      u.prob[0].ldc = n;
+      u.prob[0].stride_c = Lw.buf_stride;
+      if (k > 0) {
+        u.nprob = 2;
+        u.prob[1].a = {gdst, n, Lw.buf_stride};
+        u.prob[1].b = {Zb[cur], n, Lw.buf_stride};
+        u.prob[1].c = Zb[nxt];
+        u.prob[1].ldc = n;
+        u.prob[1].stride_c = Lw.buf_stride;
+      }
+      set_vec(u);
+      PMX_TRY(launch_gemm_f32(u, false, false, EPI_STORE, s));
+      GemmParams r = gemm_base(n, n, n, batch);
+      r.ctrl = ctrl;
+      r.prob[0].a = {Zb[nxt], n, Lw.buf_stride};
+      r.prob[0].b = {Yb[nxt], n, Lw.buf_stride};
+      r.prob[0].c = Rb;
+      r.prob[0].ldc = n;
+      r.prob[0].stride_c = Lw.buf_stride;
+      r.partials = partials;
+      r.partial_stride = Lw.pstride;
+      r.products = (d - 1) + 1 + (k > 0 ? 1 : 0) + 1;
+      r.count_update = 1;
+      r.cfg = cfg;
+      set_vec(r);
+      PMX_TRY(launch_gemm_f32(r, false, false, EPI_RESID, s));
+    }
+  }
+  RootFinishParams fp;
+  fp.ybuf[0] = Yb[0];
+  fp.ybuf[1] = Yb[1];
+  fp.zbuf[0] = Zb[0];
+  fp.zbuf[1] = Zb[1];
+  fp.buf_stride = Lw.buf_stride;
+  fp.x = X;
+  fp.ldx = ldx;
+  fp.x_stride = sx;
+  fp.aux = XA;
+  fp.ldaux = ldaux;
+  fp.aux_stride = saux;
+  fp.n = n;
+  fp.expo_x = -1.0 / p;
+  fp.expo_aux = 1.0 / p;
+  fp.ctrl = ctrl;
+  PMX_TRY(launch_root_finish(fp, batch, s));
+  return PMX_OK;
+}
+
+pmx_status pmx_matfn_inv_root(pmx_handle h, const float* A, int n, int lda, int p, float* X,
+                              int ldx, float* XA, int ldaux, const pmx_matfn_opts* opts,
+                              pmx_matfn_info* info, void* ws, size_t ws_bytes, void* stream) {
+  return pmx_matfn_inv_root_batched(h, A, n, lda, 0, p, X, ldx, 0, XA, ldaux, 0, 1, opts,
+                                    info, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ polar
+pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype, int m, int n,
+                                   int ldg, int64_t sg, void* U, int ldu, int64_t su,
+                                   int batch, const pmx_matfn_opts* opts,
+                                   pmx_matfn_info* info, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!h || !G || !U || m < 1 || n < 1 || m > kMaxN || n > kMaxN || batch < 1)
+    return PMX_ERR_INVALID_VALUE;
+  if (dtype != PMX_F32 && dtype != PMX_BF16) return PMX_ERR_INVALID_VALUE;
+  pmx_matfn_opts o;
+  if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
+  if (ldg < n || sg < 0 || (batch > 1 && sg != 0 && sg < (int64_t)(m - 1) * ldg + n))
+    return PMX_ERR_INVALID_VALUE;
+  if (!batch_layout_ok(m, n, ldu, su, batch)) return PMX_ERR_INVALID_VALUE;
+  if (dtype == PMX_BF16) return PMX_ERR_NOT_SUPPORTED;
+  const int rows = std::max(m, n), cols = std::min(m, n);
+  const bool tr = m < n;
+  const IterLayout Lw = iter_layout(rows, cols, batch, o, 2, 2, sizeof(float));
+  pmx_status st = check_ws(ws, ws_bytes, Lw.total);
+  if (st != PMX_OK) return st;
+  const Extent eg = extent_of(G, m, n, ldg, sg, batch, 4);
+  const Extent eu = extent_of(U, m, n, ldu, su, batch, 4);
+  Extent ew;
+  ew.lo = (uintptr_t)ws;
+  ew.hi = ew.lo + Lw.total;
+  ew.valid = true;
+  Extent ei = extent_of(info, 1, (int)sizeof(pmx_matfn_info), 0, sizeof(pmx_matfn_info), batch, 1);
+  if (overlap(eg, eu) || overlap(ew, eg) || overlap(ew, eu) || overlap(ei, eg) ||
+      overlap(ei, eu) || overlap(ei, ew))
+    return PMX_ERR_ALIAS;
+
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return PMX_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  Ctrl* ctrl = at<Ctrl>(ws, Lw.ctrl);
+  double* partials = at<double>(ws, Lw.partials);
+  float* Xb[2] = {at<float>(ws, Lw.bufs[0]), at<float>(ws, Lw.bufs[1])};
+  float* Rb = at<float>(ws, Lw.bufs[2]);
+  float* R2b = at<float>(ws, Lw.bufs[3]);
+  const IterCfg cfg = make_cfg(o, cols, info);
+  const AlphaCoef coef = make_coef(o.degree);
+  const int d = o.degree;
+
+  PMX_TRY(launch_ctrl_reset(ctrl, info, batch, s));
+  PMX_TRY(launch_fro_scale(G, false, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, s));
+  PolarInitParams pi;
+  pi.g = G;
+  pi.ldg = ldg;
+  pi.g_stride = sg;
+  pi.x = Xb[0];
+  pi.x_stride = Lw.buf_stride;
+  pi.rows = rows;
+  pi.cols = cols;
+  pi.transpose = tr ? 1 : 0;
+  pi.ctrl = ctrl;
+  PMX_TRY(launch_polar_init(pi, false, batch, s));
+
+  auto residual = [&](float* Xc, int products, int count) {
+    GemmParams r = gemm_base(cols, cols, rows, batch);
+    r.ctrl = ctrl;
+    r.prob[0].a = {Xc, cols, Lw.buf_stride};
+    r.prob[0].b = {Xc, cols, Lw.buf_stride};
+    r.prob[0].c = Rb;
+    r.prob[0].ldc = cols;
+    r.prob[0].stride_c = Lw.buf_stride;
+    r.partials = partials;
+    r.partial_stride = Lw.pstride;
+    r.products = products;
+    r.count_update = count;
+    r.cfg = cfg;
+    set_vec(r);
+    return launch_gemm_f32(r, true, false, EPI_RESID, s);
+  };
+  PMX_TRY(residual(Xb[0], 1, 0));
+  for (int k = 0; k < o.max_iter; ++k) {
+    PMX_TRY(enqueue_alpha_and_g(ws, Lw, o, cfg, coef, cols, batch, 0, k, Rb, R2b, R2b, s));
+    const int cur = k & 1, nxt = cur ^ 1;
+    GemmParams u = gemm_base(rows, cols, cols, batch);
+    u.ctrl = ctrl;
+    u.prob[0].a = {Xb[cur], cols, Lw.buf_stride};
+    u.prob[0].b = {R2b, cols, Lw.buf_stride};
+    u.prob[0].c = Xb[nxt];
+    u.prob[0].ldc = cols;
+    u.prob[0].stride_c = Lw.buf_stride;
+    set_vec(u);
+    PMX_TRY(launch_gemm_f32(u, false, false, EPI_STORE, s));
+    PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1));
+  }
+  PolarFinishParams fp;
+  fp.xbuf[0] = Xb[0];
+  fp.xbuf[1] = Xb[1];
+  fp.buf_stride = Lw.buf_stride;
+  fp.u = U;
+  fp.ldu = ldu;
+  fp.u_stride = su;
+  fp.rows = rows;
+  fp.cols = cols;
+  fp.transpose = tr ? 1 : 0;
+  fp.ctrl = ctrl;
+  PMX_TRY(launch_polar_finish(fp, false, batch, s));
+  return PMX_OK;
+}
+
+pmx_status pmx_matfn_polar(pmx_handle h, const void* G, pmx_dtype dtype, int m, int n, int ldg,
+                           void* U, int ldu, const pmx_matfn_opts* opts, pmx_matfn_info* info,
+                           void* ws, size_t ws_bytes, void* stream) {
+  return pmx_matfn_polar_batched(h, G, dtype, m, n, ldg, 0, U, ldu, 0, 1, opts, info, ws,
+                                 ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ apply
+pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, int64_t sl,
+                                     const void* G, pmx_dtype dtype, int m, int n, int ldg,
+                                     int64_t sg, const float* Rinv, int ldr, int64_t sr,
+                                     void* P, int ldp, int64_t sp, int batch, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (!h || !Linv || !G || !Rinv || !P || m < 1 || n < 1 || m > kMaxN || n > kMaxN ||
+      batch < 1)
+    return PMX_ERR_INVALID_VALUE;
+  if (dtype != PMX_F32 && dtype != PMX_BF16) return PMX_ERR_INVALID_VALUE;
+  if (ldl < m || ldg < n || ldr < n || sl < 0 || sg < 0 || sr < 0)
+    return PMX_ERR_INVALID_VALUE;
+  if (!batch_layout_ok(m, n, ldp, sp, batch)) return PMX_ERR_INVALID_VALUE;
+  if (dtype == PMX_BF16) return PMX_ERR_NOT_SUPPORTED;
+  const size_t need = apply_ws(m, n, batch);
+  pmx_status st = check_ws(ws, ws_bytes, need);
+  if (st != PMX_OK) return st;
+  const Extent ep = extent_of(P, m, n, ldp, sp, batch, 4);
+  const Extent el = extent_of(Linv, m, m, ldl, sl, batch, 4);
+  const Extent eg = extent_of(G, m, n, ldg, sg, batch, 4);
+  const Extent er = extent_of(Rinv, n, n, ldr, sr, batch, 4);
+  Extent ew;
+  ew.lo = (uintptr_t)ws;
+  ew.hi = ew.lo + need;
+  ew.valid = true;
+  if (overlap(ep, el) || overlap(ep, eg) || overlap(ep, er) || overlap(ew, ep) ||
+      overlap(ew, el) || overlap(ew, eg) || overlap(ew, er))
+    return PMX_ERR_ALIAS;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return PMX_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  float* T = (float*)ws;
+  const int64_t st_t = (int64_t)m * n;
+  GemmParams a = gemm_base(m, n, m, batch);
+  a.prob[0].a = {Linv, ldl, sl};
+  a.prob[0].b = {(const float*)G, ldg, sg};
+  a.prob[0].c = T;
+  a.prob[0].ldc = n;
+  a.prob[0].stride_c = st_t;
+  set_vec(a);
+  PMX_TRY(launch_gemm_f32(a, false, false, EPI_STORE, s));
+  GemmParams b = gemm_base(m, n, n, batch);
+  b.prob[0].a = {T, n, st_t};
+  b.prob[0].b = {Rinv, ldr, sr};
+  b.prob[0].c = (float*)P;
+  b.prob[0].ldc = ldp;
+  b.prob[0].stride_c = sp;
+  set_vec(b);
+  PMX_TRY(launch_gemm_f32(b, false, false, EPI_STORE, s));
+  return PMX_OK;
+}
+
+pmx_status pmx_precond_apply(pmx_handle h, const float* Linv, int ldl, const void* G,
+                             pmx_dtype dtype, int m, int n, int ldg, const float* Rinv, int ldr,
+                             void* P, int ldp, void* ws, size_t ws_bytes, void* stream) {
+  return pmx_precond_apply_batched(h, Linv, ldl, 0, G, dtype, m, n, ldg, 0, Rinv, ldr, 0, P,
+                                   ldp, 0, 1, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

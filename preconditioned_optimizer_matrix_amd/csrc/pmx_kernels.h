@@ -1,0 +1,141 @@
+// Parameter blocks and launchers of the non-GEMM kernels of libpmx.
+#pragma once
+
+#include "pmx_internal.h"
+
+namespace pmx {
+
+// Partial-sum slots reserved per matrix for the elementwise reductions and
+// for the residual GEMM (one slot per output tile).
+constexpr int kPartialsPerMatrix = 1024;
+
+// bf16 storage type: raw bits, converted explicitly (round to nearest even).
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float((uint32_t)x.bits << 16);
+}
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return bf16_t{(uint16_t)0x7FC0};
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return bf16_t{(uint16_t)(u >> 16)};
+}
+
+struct StageInitParams {
+  const float* a;        // stage 0 input A
+  int64_t lda, a_stride;
+  float* ybuf[2];        // ping-pong Y buffers (n x n, ld n)
+  float* r;              // residual buffer
+  int64_t buf_stride;    // batch stride of the work buffers
+  int n, stage;
+  Ctrl* ctrl;
+  double* partials;
+  int64_t partial_stride;
+  IterCfg cfg;
+};
+
+struct PolarInitParams {
+  const void* g;
+  int64_t ldg, g_stride;
+  void* x;               // X_0 (rows x cols, ld cols)
+  int64_t x_stride;
+  int rows, cols, transpose;
+  Ctrl* ctrl;
+};
+
+struct SketchParams {
+  float* kbuf;           // Krylov buffer: n x (2d+2) p, columns [0, p) = S
+  int64_t kld, kstride;
+  int n, p, k, stage;
+  uint32_t seed_lo, seed_hi;
+  Ctrl* ctrl;
+};
+
+struct SkinnyJob {
+  const float* mat;
+  int64_t mat_ld, mat_stride;
+  int in_col, out_col;
+  int pow;               // output scaled by ||R||_F^-pow
+};
+
+struct SkinnyParams {
+  SkinnyJob job[2];
+  float* kbuf;
+  int64_t kld, kstride;
+  int n, q;
+  Ctrl* ctrl;
+};
+
+// Coefficient vectors of r(xi; alpha) = sum_j (a0_j + alpha a1_j + alpha^2 a2_j) xi^j.
+struct AlphaCoef {
+  double a[3][6];
+  double taylor_d;
+};
+
+struct AlphaParams {
+  const float* kbuf;
+  int64_t kld, kstride;
+  Ctrl* ctrl;
+  IterCfg cfg;
+  AlphaCoef coef;
+};
+
+struct FormGParams {
+  const float* r;
+  const float* r2;       // R^2 (d = 2), may alias dst
+  float* dst;
+  int64_t stride;
+  int n, degree;
+  float c0, c1;
+  Ctrl* ctrl;
+};
+
+struct RootFinishParams {
+  float* ybuf[2];
+  float* zbuf[2];
+  int64_t buf_stride;
+  float* x;
+  int64_t ldx, x_stride;
+  float* aux;
+  int64_t ldaux, aux_stride;
+  int n;
+  double expo_x, expo_aux;  // X = c^expo_x Z, aux = c^expo_aux Y
+  Ctrl* ctrl;
+};
+
+struct PolarFinishParams {
+  void* xbuf[2];
+  int64_t buf_stride;
+  void* u;
+  int64_t ldu, u_stride;
+  int rows, cols, transpose;
+  Ctrl* ctrl;
+};
+
+hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStream_t s);
+hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
+                            int64_t stride, int batch, Ctrl* ctrl, double* partials,
+                            int64_t pstride, pmx_matfn_info* info, hipStream_t s);
+hipError_t launch_sqrt_stage_init(const StageInitParams& p, int batch, hipStream_t s);
+hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hipStream_t s);
+hipError_t launch_sketch(const SketchParams& p, int batch, hipStream_t s);
+hipError_t launch_skinny(const SkinnyParams& p, int njobs, int batch, hipStream_t s);
+hipError_t launch_alpha(const AlphaParams& p, int batch, hipStream_t s);
+hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s);
+hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t s);
+hipError_t launch_polar_finish(const PolarFinishParams& p, bool bf16, int batch, hipStream_t s);
+
+int gemm_f32_tiles(int M, int N);
+
+}  // namespace pmx

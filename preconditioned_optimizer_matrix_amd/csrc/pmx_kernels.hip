@@ -1,0 +1,649 @@
+// Bandwidth- and latency-bound kernels of the PRISM iteration on gfx950:
+// control reset, input scaling, stage set-up, the Gaussian sketch, the skinny
+// Krylov products R^j S, the on-device alpha fit, the polynomial combination
+// g = f_{d-1}(R) + alpha R^d, and the scaled outputs.
+#include <math.h>
+
+#include "pmx_kernels.h"
+
+namespace pmx {
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ int32_t load_status(const Ctrl* c) {
+  return *(const volatile int32_t*)&c->status;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- control
+__global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch) {
+  const int b = blockIdx.x;
+  if (b >= batch) return;
+  if (threadIdx.x == 0) {
+    Ctrl c;
+    c.c = 0.0;
+    c.r_prev = 0.0;
+    c.fro = 0.0;
+    c.alpha = 0.0;
+    c.status = PMX_RUNNING;
+    c.status_all = PMX_CONVERGED;
+    c.iter = 0;
+    c.stage = 0;
+    c.gemms = 0;
+    c.sketch_products = 0;
+    c.counter = 0u;
+    c.pad = 0;
+    ctrl[b] = c;
+  }
+  if (info) {
+    int32_t* w = reinterpret_cast<int32_t*>(info + b);
+    const int words = (int)(sizeof(pmx_matfn_info) / 4);
+    for (int i = threadIdx.x; i < words; i += blockDim.x) w[i] = 0;
+  }
+}
+
+// ---------------------------------------------------------------- scale
+// c = ||X||_F over an rows x cols matrix (fp32 or bf16), fp64 accumulation,
+// deterministic last-block reduction.  Sets status NONFINITE if c is not a
+// positive finite number.
+template <typename T>
+__global__ __launch_bounds__(NT) void fro_scale_kernel(const T* __restrict__ X, int rows,
+                                                       int cols, int64_t ld, int64_t stride,
+                                                       Ctrl* ctrl, double* partials,
+                                                       int64_t pstride, pmx_matfn_info* info) {
+  const int b = blockIdx.y;
+  const T* x = X + (int64_t)b * stride;
+  double acc = 0.0;
+  const int64_t total = (int64_t)rows * cols;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
+    const double v = (double)to_f32(x[(int64_t)r * ld + c]);
+    acc += v * v;
+  }
+  __shared__ double red[NT / 64];
+  const double bs = block_sum<NT / 64>(acc, red);
+  double tot;
+  if (last_block_sum<NT / 64>(bs, partials + (int64_t)b * pstride, &ctrl[b].counter,
+                              gridDim.x, blockIdx.x, red, &tot)) {
+    if (threadIdx.x == 0) {
+      Ctrl& c = ctrl[b];
+      const double s = sqrt(tot);
+      c.c = s;
+      if (info) info[b].scale = (float)s;
+      if (!(s > 0.0) || !isfinite(s)) {
+        c.status = PMX_NONFINITE;
+        c.status_all = PMX_NONFINITE;
+        if (info) info[b].status = PMX_NONFINITE;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stage init
+// Coupled square-root stage set-up: Y_0 = scale * src (src = A for stage 0,
+// the previous stage's Y for stage 1), R_0 = I - Y_0 (Z_0 = I), and the
+// convergence decision on r_0.
+__global__ __launch_bounds__(NT) void sqrt_stage_init_kernel(StageInitParams p) {
+  const int b = blockIdx.y;
+  Ctrl* cb = p.ctrl + b;
+  if (p.stage == 0) {
+    if (load_status(cb) != PMX_RUNNING) return;
+  } else {
+    const int prev = *(const volatile int32_t*)&cb->status_all;
+    if (prev == PMX_NONFINITE || prev == PMX_DIVERGED) return;
+  }
+  const int n = p.n;
+  double scale;
+  const float* src;
+  int64_t sld;
+  if (p.stage == 0) {
+    scale = 1.0 / cb->c;
+    src = p.a + (int64_t)b * p.a_stride;
+    sld = p.lda;
+  } else {
+    scale = 1.0;
+    const int it = *(const volatile int32_t*)&cb->iter;
+    src = p.ybuf[it & 1] + (int64_t)b * p.buf_stride;
+    sld = n;
+  }
+  const float fs = (float)scale;
+  float* y0 = p.ybuf[0] + (int64_t)b * p.buf_stride;
+  float* R = p.r + (int64_t)b * p.buf_stride;
+  double acc = 0.0;
+  const int64_t total = (int64_t)n * n;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int r = (int)(e / n), c = (int)(e - (int64_t)r * n);
+    const float y = src[(int64_t)r * sld + c] * fs;
+    y0[e] = y;
+    const float rv = (r == c ? 1.f : 0.f) - y;
+    R[e] = rv;
+    acc += (double)rv * (double)rv;
+  }
+  __shared__ double red[NT / 64];
+  const double bs = block_sum<NT / 64>(acc, red);
+  double tot;
+  if (last_block_sum<NT / 64>(bs, p.partials + (int64_t)b * p.partial_stride, &cb->counter,
+                              gridDim.x, blockIdx.x, red, &tot)) {
+    if (threadIdx.x == 0) {
+      cb->stage = p.stage;
+      cb->iter = 0;
+      cb->r_prev = 0.0;
+      cb->status = PMX_RUNNING;
+      decide(*cb, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
+    }
+  }
+}
+
+// Polar set-up: X_0 = G / c (transposed when the iteration runs on G^T).
+template <typename T>
+__global__ __launch_bounds__(NT) void polar_init_kernel(PolarInitParams p) {
+  const int b = blockIdx.y;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const T* g = reinterpret_cast<const T*>(p.g) + (int64_t)b * p.g_stride;
+  T* x = reinterpret_cast<T*>(p.x) + (int64_t)b * p.x_stride;
+  const float fs = (float)(1.0 / cb->c);
+  const int64_t total = (int64_t)p.rows * p.cols;  // X is rows x cols (rows >= cols)
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int r = (int)(e / p.cols), c = (int)(e - (int64_t)r * p.cols);
+    const float v = p.transpose ? to_f32(g[(int64_t)c * p.ldg + r]) : to_f32(g[(int64_t)r * p.ldg + c]);
+    x[e] = from_f32<T>(v * fs);
+  }
+}
+
+// ---------------------------------------------------------------- sketch
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
+// multiplies, high halves mixed with the other counter words and the key,
+// key advanced by two Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// S (n x p) of matrix b, stage, iteration k: element e = i p + j takes word
+// e % 4 of the Philox call with counter (e / 4, k, stage, b); uniforms
+// ((x >> 8) + 1/2) 2^-24, Box-Muller on the word pairs (0,1) and (2,3),
+// evaluated in fp64 and rounded to fp32.  Written to columns [0, p) of the
+// Krylov buffer.
+__global__ __launch_bounds__(NT) void sketch_kernel(SketchParams p) {
+  const int b = blockIdx.y;
+  if (load_status(p.ctrl + b) != PMX_RUNNING) return;
+  const int64_t total = (int64_t)p.n * p.p;
+  const int64_t calls = (total + 3) / 4;
+  float* kb = p.kbuf + (int64_t)b * p.kstride;
+  for (int64_t q = (int64_t)blockIdx.x * NT + threadIdx.x; q < calls;
+       q += (int64_t)gridDim.x * NT) {
+    uint32_t c[4] = {(uint32_t)q, (uint32_t)p.k, (uint32_t)p.stage, (uint32_t)b};
+    philox4x32_10(c, p.seed_lo, p.seed_hi);
+    double u[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) u[w] = ((double)(c[w] >> 8) + 0.5) * 0x1p-24;
+    double z[4];
+    const double r01 = sqrt(-2.0 * log(u[0])), r23 = sqrt(-2.0 * log(u[2]));
+    double s01, c01, s23, c23;
+    sincos(2.0 * M_PI * u[1], &s01, &c01);
+    sincos(2.0 * M_PI * u[3], &s23, &c23);
+    z[0] = r01 * c01;
+    z[1] = r01 * s01;
+    z[2] = r23 * c23;
+    z[3] = r23 * s23;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int64_t e = q * 4 + w;
+      if (e < total) {
+        const int i = (int)(e / p.p), j = (int)(e - (int64_t)i * p.p);
+        kb[(int64_t)i * p.kld + j] = (float)z[w];
+      }
+    }
+  }
+}
+
+// Recursive-halving reduction over a 64-lane wave of CNT values per lane:
+// at the step with offset O the lanes with bit O set keep the upper half of
+// their remaining values and add the partner's copy of it.  With CNT = 64,
+// lane l ends holding the wave-wide sum of value index l in acc[0].
+template <int CNT, int O>
+__device__ __forceinline__ void halve_reduce(float* acc, int lane) {
+  if constexpr (CNT > 1 && O >= 1) {
+    constexpr int H = CNT / 2;
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float send = upper ? acc[i] : acc[i + H];
+      const float keep = upper ? acc[i + H] : acc[i];
+      acc[i] = keep + __shfl_xor(send, O, 64);
+    }
+    halve_reduce<H, O / 2>(acc, lane);
+  }
+}
+
+// ---------------------------------------------------------------- skinny products
+// out[:, oc : oc + q] = fro^-pow * Mat * in[:, ic : ic + q] for an n x n Mat
+// and an n x q block of the Krylov buffer (q <= Q).  HBM-bound on Mat: each
+// block streams 4 * (64 / Q) rows of Mat once; In is staged through LDS in
+// chunks of 256 rows and shared by those rows.  Each lane accumulates
+// (64 / Q) x Q partial sums; a recursive-halving exchange over the wave
+// leaves lane l with the complete sum for (row l / Q, column l % Q).
+template <int Q>
+__global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
+  constexpr int RW = 64 / Q;       // rows per wave
+  constexpr int RB = 4 * RW;       // rows per block
+  constexpr int LD = Q + 4;
+  const int b = blockIdx.z;
+  const Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const SkinnyJob& job = p.job[blockIdx.y];
+  const int n = p.n;
+  const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
+  float* kb = p.kbuf + (int64_t)b * p.kstride;
+  const double fro = cb->fro;
+  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+
+  __shared__ __attribute__((aligned(16))) float in_lds[256 * LD];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * RB + wid * RW;
+
+  float acc[RW * Q];
+#pragma unroll
+  for (int i = 0; i < RW * Q; ++i) acc[i] = 0.f;
+
+  for (int j0 = 0; j0 < n; j0 += 256) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 256 * Q; idx += NT) {
+      const int r = idx / Q, c = idx - r * Q;
+      float v = 0.f;
+      if (j0 + r < n && c < p.q) v = kb[(int64_t)(j0 + r) * p.kld + job.in_col + c];
+      in_lds[r * LD + c] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int jj = lane + 64 * t;
+      const int j = j0 + jj;
+      if (j < n) {
+        float m[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr)
+          m[rr] = (row0 + rr < n) ? mat[(int64_t)(row0 + rr) * job.mat_ld + j] : 0.f;
+        const float4* src = reinterpret_cast<const float4*>(in_lds + jj * LD);
+#pragma unroll
+        for (int c4 = 0; c4 < Q / 4; ++c4) {
+          const float4 v = src[c4];
+#pragma unroll
+          for (int rr = 0; rr < RW; ++rr) {
+            acc[rr * Q + 4 * c4 + 0] += m[rr] * v.x;
+            acc[rr * Q + 4 * c4 + 1] += m[rr] * v.y;
+            acc[rr * Q + 4 * c4 + 2] += m[rr] * v.z;
+            acc[rr * Q + 4 * c4 + 3] += m[rr] * v.w;
+          }
+        }
+      }
+    }
+  }
+  halve_reduce<64, 32>(acc, lane);
+  // lane l now holds value index l = rr * Q + c
+  const int rr = lane / Q, c = lane - rr * Q;
+  const int row = row0 + rr;
+  if (row < n && c < p.q) kb[(int64_t)row * p.kld + job.out_col + c] = acc[0] * scale;
+}
+
+// ---------------------------------------------------------------- alpha fit
+// Real roots of a x^2 + b x + c inside (lo, hi), appended to out (ascending
+// order not required).
+__device__ int quad_roots_in(double a, double b, double c, double lo, double hi, double* out) {
+  int n = 0;
+  const double scale = fmax(fabs(a), fmax(fabs(b), fabs(c)));
+  if (scale == 0.0) return 0;
+  if (fabs(a) <= 1e-14 * scale) {
+    if (b != 0.0) {
+      const double x = -c / b;
+      if (x > lo && x < hi) out[n++] = x;
+    }
+    return n;
+  }
+  const double disc = b * b - 4.0 * a * c;
+  if (disc < 0.0) return 0;
+  const double sq = sqrt(disc);
+  const double q = -0.5 * (b + (b >= 0.0 ? sq : -sq));
+  const double x1 = q / a;
+  const double x2 = (q != 0.0) ? c / q : x1;
+  if (x1 > lo && x1 < hi) out[n++] = x1;
+  if (x2 > lo && x2 < hi && x2 != x1) out[n++] = x2;
+  return n;
+}
+
+// argmin over [lo, hi] of phi(a) = w0 + w1 a + w2 a^2 + w3 a^3 + w4 a^4.
+// phi' is a cubic; the roots of phi'' split [lo, hi] into pieces on which
+// phi' is monotone, and every sign change of phi' on a piece is bisected to
+// full double precision.  Candidates are both ends and those critical
+// points; the smallest phi wins, ties to the smaller alpha.
+__device__ double argmin_quartic(const double (&w)[5], double lo, double hi) {
+  auto phi = [&](double a) { return w[0] + a * (w[1] + a * (w[2] + a * (w[3] + a * w[4]))); };
+  auto dphi = [&](double a) { return w[1] + a * (2.0 * w[2] + a * (3.0 * w[3] + a * 4.0 * w[4])); };
+  double brk[4];
+  int nb = 0;
+  brk[nb++] = lo;
+  double qr[2];
+  const int nq = quad_roots_in(12.0 * w[4], 6.0 * w[3], 2.0 * w[2], lo, hi, qr);
+  if (nq == 2 && qr[1] < qr[0]) {
+    const double t = qr[0];
+    qr[0] = qr[1];
+    qr[1] = t;
+  }
+  for (int i = 0; i < nq; ++i) brk[nb++] = qr[i];
+  brk[nb++] = hi;
+  double cand[6];
+  int nc = 0;
+  cand[nc++] = lo;
+  for (int i = 0; i + 1 < nb; ++i) {
+    double x0 = brk[i], x1 = brk[i + 1];
+    double f0 = dphi(x0), f1 = dphi(x1);
+    if (f0 == 0.0) {
+      if (x0 > lo && x0 < hi) cand[nc++] = x0;
+      continue;
+    }
+    if ((f0 < 0.0) == (f1 < 0.0) || f1 == 0.0) continue;
+    for (int it = 0; it < 200; ++it) {
+      const double xm = 0.5 * (x0 + x1);
+      if (xm <= x0 || xm >= x1) break;
+      const double fm = dphi(xm);
+      if (fm == 0.0) {
+        x0 = x1 = xm;
+        break;
+      }
+      if ((fm < 0.0) == (f0 < 0.0)) {
+        x0 = xm;
+        f0 = fm;
+      } else {
+        x1 = xm;
+      }
+    }
+    const double x = 0.5 * (x0 + x1);
+    if (x > lo && x < hi) cand[nc++] = x;
+  }
+  cand[nc++] = hi;
+  // ascending order for the tie rule
+  for (int i = 1; i < nc; ++i)
+    for (int j = i; j > 0 && cand[j] < cand[j - 1]; --j) {
+      const double t = cand[j];
+      cand[j] = cand[j - 1];
+      cand[j - 1] = t;
+    }
+  double best = cand[0], bv = phi(cand[0]);
+  for (int i = 1; i < nc; ++i) {
+    const double v = phi(cand[i]);
+    if (v < bv) {
+      bv = v;
+      best = cand[i];
+    }
+  }
+  return best;
+}
+
+// One block per matrix: Gram of the scaled Krylov blocks K~_j = (R/s)^j S
+// (j = 1..2d+1, fp64 accumulation), the quartic in alpha (the coefficient
+// vectors rescaled by s^j undo the Krylov scaling), and its argmin on
+// [lo, hi].  alpha_k lands in the control block; the host never waits.
+__global__ __launch_bounds__(NT) void alpha_kernel(AlphaParams p) {
+  const int b = blockIdx.x;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const int J = 2 * p.cfg.degree + 1;
+  const double cd = p.coef.taylor_d;
+  double alpha = cd;
+  __shared__ double red[NT / 64];
+  if (p.cfg.accelerate) {
+    const float* kb = p.kbuf + (int64_t)b * p.kstride;
+    const int n = p.cfg.n, pp = p.cfg.p;
+    double g[15];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) g[i] = 0.0;
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const float* row = kb + (int64_t)i * p.kld;
+      for (int c = 0; c < pp; ++c) {
+        double v[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) v[j] = (j < J) ? (double)row[(j + 1) * pp + c] : 0.0;
+        int t = 0;
+#pragma unroll
+        for (int a = 0; a < 5; ++a)
+#pragma unroll
+          for (int bb = a; bb < 5; ++bb) g[t++] += v[a] * v[bb];
+      }
+    }
+    double G[15];
+    for (int i = 0; i < 15; ++i) G[i] = block_sum<NT / 64>(g[i], red);
+    if (threadIdx.x == 0) {
+      // scaled coefficient vectors: a_i[j] s^j, j = 1..J
+      const double s = cb->fro;
+      double av[3][5];
+      double sp = 1.0;
+      for (int j = 1; j <= J; ++j) {
+        sp *= s;
+        for (int i = 0; i < 3; ++i) av[i][j - 1] = p.coef.a[i][j] * sp;
+      }
+      for (int j = J; j < 5; ++j)
+        for (int i = 0; i < 3; ++i) av[i][j] = 0.0;
+      auto gram = [&](int x, int y) {
+        if (x > y) {
+          const int t = x;
+          x = y;
+          y = t;
+        }
+        // index of (x, y), x <= y, in the row-major upper triangle of 5 x 5
+        const int idx = x * 5 - x * (x - 1) / 2 + (y - x);
+        return G[idx];
+      };
+      auto q = [&](int i1, int i2) {
+        double t = 0.0;
+        for (int x = 0; x < J; ++x)
+          for (int y = 0; y < J; ++y) t += av[i1][x] * gram(x, y) * av[i2][y];
+        return t;
+      };
+      double w[5];
+      w[0] = q(0, 0);
+      w[1] = q(0, 1) + q(1, 0);
+      w[2] = q(1, 1) + q(0, 2) + q(2, 0);
+      w[3] = q(1, 2) + q(2, 1);
+      w[4] = q(2, 2);
+      bool ok = true;
+      double mx = 0.0;
+      for (int e = 0; e < 5; ++e) ok = ok && isfinite(w[e]);
+      for (int e = 1; e < 5; ++e) mx = fmax(mx, fabs(w[e]));
+      const double lo = p.cfg.lo, hi = p.cfg.hi;
+      if (!ok || mx <= 1e-300) alpha = fmin(fmax(cd, lo), hi);
+      else if (hi <= lo) alpha = lo;
+      else alpha = argmin_quartic(w, lo, hi);
+    }
+  }
+  if (threadIdx.x == 0) {
+    cb->alpha = alpha;
+    if (p.cfg.accelerate) cb->sketch_products += J;
+    const int k = cb->iter;
+    if (p.cfg.info && k < PMX_TRACE_LEN) p.cfg.info[b].alpha[cb->stage][k] = (float)alpha;
+  }
+}
+
+// ---------------------------------------------------------------- polynomial
+// g = c_0 I + c_1 R + ... + c_{d-1} R^{d-1} + alpha R^d for d in {1, 2}
+// (R^2 given); dst may alias r2.
+__global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
+  const int b = blockIdx.y;
+  const Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const float alpha = (float)cb->alpha;
+  const int n = p.n;
+  const float* R = p.r + (int64_t)b * p.stride;
+  const float* R2 = p.r2 ? p.r2 + (int64_t)b * p.stride : nullptr;
+  float* G = p.dst + (int64_t)b * p.stride;
+  const float c0 = p.c0, c1 = p.c1;
+  const int64_t total = (int64_t)n * n;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int r = (int)(e / n), c = (int)(e - (int64_t)r * n);
+    float v;
+    if (p.degree == 1) v = alpha * R[e];
+    else v = c1 * R[e] + alpha * R2[e];
+    if (r == c) v += c0;
+    G[e] = v;
+  }
+}
+
+// ---------------------------------------------------------------- outputs
+// X = sx * Z_cur, X_aux = sa * Y_cur of the last stage.  Z_0 = I is implicit
+// when the stage ended before its first update.  NaN when the call failed.
+__global__ __launch_bounds__(NT) void root_finish_kernel(RootFinishParams p) {
+  const int b = blockIdx.y;
+  const Ctrl* cb = p.ctrl + b;
+  const int st = *(const volatile int32_t*)&cb->status_all;
+  const bool bad = (st == PMX_NONFINITE || st == PMX_DIVERGED);
+  const int it = cb->iter;
+  const double c = cb->c;
+  const float sx = (float)pow(c, p.expo_x), sa = (float)pow(c, p.expo_aux);
+  const float* Z = p.zbuf[it & 1] + (int64_t)b * p.buf_stride;
+  const float* Y = p.ybuf[it & 1] + (int64_t)b * p.buf_stride;
+  float* X = p.x + (int64_t)b * p.x_stride;
+  float* XA = p.aux ? p.aux + (int64_t)b * p.aux_stride : nullptr;
+  const int n = p.n;
+  const int64_t total = (int64_t)n * n;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int r = (int)(e / n), col = (int)(e - (int64_t)r * n);
+    float zx, ya;
+    if (bad) {
+      zx = NAN;
+      ya = NAN;
+    } else {
+      zx = (it == 0) ? (r == col ? 1.f : 0.f) : Z[e];
+      ya = Y[e];
+    }
+    X[(int64_t)r * p.ldx + col] = bad ? zx : zx * sx;
+    if (XA) XA[(int64_t)r * p.ldaux + col] = bad ? ya : ya * sa;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(NT) void polar_finish_kernel(PolarFinishParams p) {
+  const int b = blockIdx.y;
+  const Ctrl* cb = p.ctrl + b;
+  const int st = *(const volatile int32_t*)&cb->status_all;
+  const bool bad = (st == PMX_NONFINITE || st == PMX_DIVERGED);
+  const int it = cb->iter;
+  const T* X = reinterpret_cast<const T*>(p.xbuf[it & 1]) + (int64_t)b * p.buf_stride;
+  T* U = reinterpret_cast<T*>(p.u) + (int64_t)b * p.u_stride;
+  const int64_t total = (int64_t)p.rows * p.cols;  // X is rows x cols
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int r = (int)(e / p.cols), c = (int)(e - (int64_t)r * p.cols);
+    const T v = bad ? from_f32<T>(NAN) : X[e];
+    if (p.transpose) U[(int64_t)c * p.ldu + r] = v;
+    else U[(int64_t)r * p.ldu + c] = v;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+static int grid_for(int64_t elems, int cap) {
+  int64_t g = (elems + NT * 4 - 1) / (NT * 4);
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(ctrl_reset_kernel, dim3(batch), dim3(NT), 0, s, ctrl, info, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
+                            int64_t stride, int batch, Ctrl* ctrl, double* partials,
+                            int64_t pstride, pmx_matfn_info* info, hipStream_t s) {
+  dim3 grid(grid_for((int64_t)rows * cols, kPartialsPerMatrix), batch);
+  if (bf16)
+    hipLaunchKernelGGL(fro_scale_kernel<bf16_t>, grid, dim3(NT), 0, s,
+                       (const bf16_t*)x, rows, cols, ld, stride, ctrl, partials, pstride, info);
+  else
+    hipLaunchKernelGGL(fro_scale_kernel<float>, grid, dim3(NT), 0, s, (const float*)x, rows,
+                       cols, ld, stride, ctrl, partials, pstride, info);
+  return hipGetLastError();
+}
+
+hipError_t launch_sqrt_stage_init(const StageInitParams& p, int batch, hipStream_t s) {
+  dim3 grid(grid_for((int64_t)p.n * p.n, kPartialsPerMatrix), batch);
+  hipLaunchKernelGGL(sqrt_stage_init_kernel, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hipStream_t s) {
+  dim3 grid(grid_for((int64_t)p.rows * p.cols, 2048), batch);
+  if (bf16) hipLaunchKernelGGL(polar_init_kernel<bf16_t>, grid, dim3(NT), 0, s, p);
+  else hipLaunchKernelGGL(polar_init_kernel<float>, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_sketch(const SketchParams& p, int batch, hipStream_t s) {
+  const int64_t calls = ((int64_t)p.n * p.p + 3) / 4;
+  int g = (int)((calls + NT - 1) / NT);
+  if (g > 1024) g = 1024;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(sketch_kernel, dim3(g, batch), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny(const SkinnyParams& p, int njobs, int batch, hipStream_t s) {
+  if (p.q <= 8) {
+    dim3 grid((p.n + 31) / 32, njobs, batch);
+    hipLaunchKernelGGL(skinny_kernel<8>, grid, dim3(NT), 0, s, p);
+  } else if (p.q <= 16) {
+    dim3 grid((p.n + 15) / 16, njobs, batch);
+    hipLaunchKernelGGL(skinny_kernel<16>, grid, dim3(NT), 0, s, p);
+  } else if (p.q <= 32) {
+    dim3 grid((p.n + 7) / 8, njobs, batch);
+    hipLaunchKernelGGL(skinny_kernel<32>, grid, dim3(NT), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_alpha(const AlphaParams& p, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(alpha_kernel, dim3(batch), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s) {
+  dim3 grid(grid_for((int64_t)p.n * p.n, 2048), batch);
+  hipLaunchKernelGGL(form_g_kernel, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t s) {
+  dim3 grid(grid_for((int64_t)p.n * p.n, 2048), batch);
+  hipLaunchKernelGGL(root_finish_kernel, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_polar_finish(const PolarFinishParams& p, bool bf16, int batch, hipStream_t s) {
+  dim3 grid(grid_for((int64_t)p.rows * p.cols, 2048), batch);
+  if (bf16) hipLaunchKernelGGL(polar_finish_kernel<bf16_t>, grid, dim3(NT), 0, s, p);
+  else hipLaunchKernelGGL(polar_finish_kernel<float>, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace pmx

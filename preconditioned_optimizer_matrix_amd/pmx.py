@@ -1,0 +1,291 @@
+"""ctypes binding of libpmx.so (the C ABI declared in include/pmx.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every step of the computation runs in libpmx's kernels.
+Importing this module raises if the built library is missing, so no caller
+can silently fall back to another implementation.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpmx.so")
+
+OK, ERR_INVALID_VALUE, ERR_NOT_SUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(6)
+RUNNING, CONVERGED, MAXITER, STAGNATED, NONFINITE, DIVERGED = -1, 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+OP_STATS, OP_INV_ROOT, OP_POLAR, OP_APPLY = range(4)
+OPTS_VERSION = 1
+TRACE_LEN = 64
+MAX_SKETCH = 16
+STATUS_NAMES = {RUNNING: "RUNNING", CONVERGED: "CONVERGED", MAXITER: "MAXITER",
+                STAGNATED: "STAGNATED", NONFINITE: "NONFINITE", DIVERGED: "DIVERGED"}
+
+EXPORTS = [
+    "pmx_create", "pmx_destroy", "pmx_status_string", "pmx_version",
+    "pmx_matfn_opts_default", "pmx_workspace_size",
+    "pmx_shampoo_stats_update", "pmx_shampoo_stats_update_batched",
+    "pmx_matfn_inv_root", "pmx_matfn_inv_root_batched",
+    "pmx_matfn_polar", "pmx_matfn_polar_batched",
+    "pmx_precond_apply", "pmx_precond_apply_batched",
+]
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("struct_version", ctypes.c_int32), ("degree", ctypes.c_int32),
+                ("sketch_p", ctypes.c_int32), ("max_iter", ctypes.c_int32),
+                ("accelerate", ctypes.c_int32), ("alpha_lo", ctypes.c_float),
+                ("alpha_hi", ctypes.c_float), ("tol", ctypes.c_float),
+                ("seed", ctypes.c_uint64)]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_int32), ("iters", ctypes.c_int32 * 2),
+                ("gemms", ctypes.c_int32), ("sketch_products", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("residual", ctypes.c_float * 2),
+                ("alpha", (ctypes.c_float * TRACE_LEN) * 2),
+                ("rtrace", (ctypes.c_float * TRACE_LEN) * 2)]
+
+
+INFO_DTYPE = np.dtype([("status", "<i4"), ("iters", "<i4", (2,)), ("gemms", "<i4"),
+                       ("sketch_products", "<i4"), ("stages", "<i4"), ("scale", "<f4"),
+                       ("residual", "<f4", (2,)), ("alpha", "<f4", (2, TRACE_LEN)),
+                       ("rtrace", "<f4", (2, TRACE_LEN))])
+assert INFO_DTYPE.itemsize == ctypes.sizeof(Info)
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpmx.so is not built (%s); run "
+                          "`python -m preconditioned_optimizer_matrix_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "pmx_create": (_i32, [ctypes.POINTER(_vp), _i32]),
+        "pmx_destroy": (_i32, [_vp]),
+        "pmx_status_string": (ctypes.c_char_p, [_i32]),
+        "pmx_version": (_i32, []),
+        "pmx_matfn_opts_default": (_i32, [ctypes.POINTER(Opts)]),
+        "pmx_workspace_size": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts),
+                                      ctypes.POINTER(_sz)]),
+        "pmx_shampoo_stats_update": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
+                                            _i32, _f32, _f32, _vp, _sz, _vp]),
+        "pmx_shampoo_stats_update_batched": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp,
+                                                    _i32, _i64, _vp, _i32, _i64, _f32, _f32,
+                                                    _i32, _vp, _sz, _vp]),
+        "pmx_matfn_inv_root": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
+                                      ctypes.POINTER(Opts), _vp, _vp, _sz, _vp]),
+        "pmx_matfn_inv_root_batched": (_i32, [_vp, _vp, _i32, _i32, _i64, _i32, _vp, _i32, _i64,
+                                              _vp, _i32, _i64, _i32, ctypes.POINTER(Opts), _vp,
+                                              _vp, _sz, _vp]),
+        "pmx_matfn_polar": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32,
+                                   ctypes.POINTER(Opts), _vp, _vp, _sz, _vp]),
+        "pmx_matfn_polar_batched": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _i32,
+                                           _i64, _i32, ctypes.POINTER(Opts), _vp, _vp, _sz,
+                                           _vp]),
+        "pmx_precond_apply": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i32,
+                                     _vp, _i32, _vp, _sz, _vp]),
+        "pmx_precond_apply_batched": (_i32, [_vp, _vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32,
+                                             _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32, _vp,
+                                             _sz, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class PmxError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        msg = lib.pmx_status_string(code).decode()
+        super().__init__("%s: %s" % (where, msg))
+
+
+def check(code, where=""):
+    if code != OK:
+        raise PmxError(code, where)
+
+
+def default_opts(**kw):
+    """pmx_matfn_opts with the library defaults, fields overridden by kw."""
+    o = Opts()
+    check(lib.pmx_matfn_opts_default(ctypes.byref(o)), "opts_default")
+    for k, v in kw.items():
+        if not hasattr(o, k):
+            raise KeyError(k)
+        setattr(o, k, v)
+    return o
+
+
+# ---------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+_handles = {}
+
+
+def handle(device=None):
+    torch = _torch()
+    dev = torch.cuda.current_device() if device is None else int(device)
+    h = _handles.get(dev)
+    if h is None:
+        hv = _vp()
+        check(lib.pmx_create(ctypes.byref(hv), dev), "pmx_create")
+        h = _handles[dev] = hv
+    return h
+
+
+def _stream(t):
+    torch = _torch()
+    return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _mat(t):
+    """(rows, cols, ld, batch_stride, batch) of a 2-D or 3-D row-major tensor."""
+    if t.dim() == 2:
+        if t.stride(1) != 1:
+            raise ValueError("matrices must have unit column stride")
+        return t.shape[0], t.shape[1], t.stride(0), 0, 1
+    if t.dim() == 3:
+        if t.stride(2) != 1:
+            raise ValueError("matrices must have unit column stride")
+        return t.shape[1], t.shape[2], t.stride(1), t.stride(0), t.shape[0]
+    raise ValueError("expected a 2-D matrix or a 3-D batch")
+
+
+def _ptr(t):
+    return _vp(t.data_ptr()) if t is not None else _vp(0)
+
+
+def workspace_bytes(op, m, n, batch=1, dtype=F32, opts=None):
+    sz = _sz()
+    check(lib.pmx_workspace_size(None, op, m, n, batch, dtype,
+                                 ctypes.byref(opts) if opts is not None else None,
+                                 ctypes.byref(sz)), "workspace_size")
+    return sz.value
+
+
+def workspace(nbytes, device):
+    """Workspace tensor (256-byte aligned: torch's caching allocator aligns to 512 B)."""
+    torch = _torch()
+    t = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def new_info(batch, device):
+    torch = _torch()
+    return torch.zeros(batch * INFO_DTYPE.itemsize, dtype=torch.uint8, device=device)
+
+
+def parse_info(info_tensor):
+    """Device info buffer -> numpy structured array (synchronises via .cpu())."""
+    raw = info_tensor.detach().cpu().numpy().tobytes()
+    return np.frombuffer(raw, dtype=INFO_DTYPE)
+
+
+def shampoo_stats_update(G, L, R, beta, eps):
+    """In place: L <- beta L + (1-beta) G G^T + eps I, R <- beta R + (1-beta) G^T G + eps I."""
+    m, n, ldg, sg, batch = _mat(G)
+    if L is not None:
+        _, _, ldl, sl, _ = _mat(L)
+    else:
+        ldl, sl = m, 0
+    if R is not None:
+        _, _, ldr, sr, _ = _mat(R)
+    else:
+        ldr, sr = n, 0
+    check(lib.pmx_shampoo_stats_update_batched(
+        handle(G.device.index), _ptr(G), _dtype_code(G), m, n, ldg, sg, _ptr(L), ldl, sl,
+        _ptr(R), ldr, sr, float(beta), float(eps), batch, None, 0, _stream(G)),
+        "shampoo_stats_update")
+    return L, R
+
+
+def inv_root(A, p, opts=None, aux=True, out=None, out_aux=None, info=None, ws=None):
+    """A^{-1/p} (and A^{1/p} if aux) of an SPD matrix or a batch of them.
+    Returns (X, X_aux or None, info_tensor)."""
+    torch = _torch()
+    n, n2, lda, sa, batch = _mat(A)
+    if n != n2:
+        raise ValueError("A must be square")
+    if opts is None:
+        opts = default_opts()
+    X = out if out is not None else torch.empty_like(A, memory_format=torch.contiguous_format)
+    XA = None
+    if aux:
+        XA = out_aux if out_aux is not None else torch.empty_like(X)
+    _, _, ldx, sx, _ = _mat(X)
+    ldaux, saux = (n, 0)
+    if XA is not None:
+        _, _, ldaux, saux, _ = _mat(XA)
+    if info is None:
+        info = new_info(batch, A.device)
+    need = workspace_bytes(OP_INV_ROOT, n, n, batch, F32, opts)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, A.device)
+    check(lib.pmx_matfn_inv_root_batched(
+        handle(A.device.index), _ptr(A), n, lda, sa, int(p), _ptr(X), ldx, sx, _ptr(XA),
+        ldaux, saux, batch, ctypes.byref(opts), _ptr(info), _ptr(ws), ws.numel(),
+        _stream(A)), "matfn_inv_root")
+    return X, XA, info
+
+
+def polar(G, opts=None, out=None, info=None, ws=None):
+    """Polar factor of G (m x n) or a batch; returns (U, info_tensor)."""
+    torch = _torch()
+    m, n, ldg, sg, batch = _mat(G)
+    if opts is None:
+        opts = default_opts()
+    U = out if out is not None else torch.empty_like(G, memory_format=torch.contiguous_format)
+    _, _, ldu, su, _ = _mat(U)
+    if info is None:
+        info = new_info(batch, G.device)
+    dt = _dtype_code(G)
+    need = workspace_bytes(OP_POLAR, m, n, batch, dt, opts)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, G.device)
+    check(lib.pmx_matfn_polar_batched(
+        handle(G.device.index), _ptr(G), dt, m, n, ldg, sg, _ptr(U), ldu, su, batch,
+        ctypes.byref(opts), _ptr(info), _ptr(ws), ws.numel(), _stream(G)), "matfn_polar")
+    return U, info
+
+
+def precond_apply(Linv, G, Rinv, out=None, ws=None):
+    """P = Linv G Rinv (single or batched)."""
+    torch = _torch()
+    m, n, ldg, sg, batch = _mat(G)
+    _, _, ldl, sl, _ = _mat(Linv)
+    _, _, ldr, sr, _ = _mat(Rinv)
+    P = out if out is not None else torch.empty_like(G, memory_format=torch.contiguous_format)
+    _, _, ldp, sp, _ = _mat(P)
+    dt = _dtype_code(G)
+    need = workspace_bytes(OP_APPLY, m, n, batch, dt, None)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, G.device)
+    check(lib.pmx_precond_apply_batched(
+        handle(G.device.index), _ptr(Linv), ldl, sl, _ptr(G), dt, m, n, ldg, sg, _ptr(Rinv),
+        ldr, sr, _ptr(P), ldp, sp, batch, _ptr(ws), ws.numel(), _stream(G)),
+        "precond_apply")
+    return P

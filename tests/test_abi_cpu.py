@@ -1,0 +1,114 @@
+"""Host-side checks of libpmx.so that need no GPU: the library loads, exports
+every entry point include/pmx.h declares, and validates options and sizes."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pmx.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pmx_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    from preconditioned_optimizer_matrix_amd import pmx
+    names = _declared()
+    assert len(names) >= 14
+    raw = ctypes.CDLL(pmx.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+    assert set(pmx.EXPORTS) == set(names)
+
+
+def test_struct_layouts_match_header():
+    from preconditioned_optimizer_matrix_amd import pmx
+    # pmx_matfn_opts: 5 int32 + 3 float + uint64 (8-aligned) = 40 bytes
+    assert ctypes.sizeof(pmx.Opts) == 40
+    # pmx_matfn_info: 6 int32 + 3 float + 4 * 64 float
+    assert ctypes.sizeof(pmx.Info) == 4 * (6 + 3 + 4 * pmx.TRACE_LEN)
+    src = open(HEADER).read()
+    assert "#define PMX_TRACE_LEN %d" % pmx.TRACE_LEN in src
+    assert "#define PMX_OPTS_VERSION %d" % pmx.OPTS_VERSION in src
+
+
+def test_host_only_calls():
+    from preconditioned_optimizer_matrix_amd import pmx
+    assert pmx.lib.pmx_version() == 1
+    for code in range(6):
+        assert pmx.lib.pmx_status_string(code)
+    o = pmx.default_opts()
+    assert (o.degree, o.sketch_p, o.max_iter, o.accelerate) == (2, 8, 100, 1)
+    assert math.isnan(o.alpha_lo) and math.isnan(o.alpha_hi)
+    assert o.tol == pytest.approx(1e-6)
+    assert pmx.lib.pmx_matfn_opts_default(None) == pmx.ERR_INVALID_VALUE
+
+
+def test_workspace_sizes_and_option_validation():
+    from preconditioned_optimizer_matrix_amd import pmx
+    o = pmx.default_opts()
+    n = 4096
+    b = pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, o)
+    # six n x n fp32 work matrices dominate
+    assert 6 * 4 * n * n <= b < 6 * 4 * n * n + (1 << 20)
+    bb = pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 64, pmx.F32, o)
+    assert bb >= 64 * 6 * 4 * 512 * 512
+    assert pmx.workspace_bytes(pmx.OP_STATS, 1024, 4096, 1, pmx.F32, None) == 0
+    assert pmx.workspace_bytes(pmx.OP_APPLY, 1024, 4096, 1, pmx.F32, None) >= 4 * 1024 * 4096
+    pb = pmx.workspace_bytes(pmx.OP_POLAR, 4096, 1024, 1, pmx.F32, o)
+    assert pb >= 2 * 4 * 4096 * 1024 + 2 * 4 * 1024 * 1024
+
+    def ws(**kw):
+        sz = ctypes.c_size_t()
+        oo = pmx.default_opts(**kw)
+        return pmx.lib.pmx_workspace_size(None, pmx.OP_INV_ROOT, 64, 64, 1, pmx.F32,
+                                          ctypes.byref(oo), ctypes.byref(sz))
+
+    assert ws() == pmx.OK
+    assert ws(degree=3) == pmx.ERR_INVALID_VALUE
+    assert ws(sketch_p=0) == pmx.ERR_INVALID_VALUE
+    assert ws(sketch_p=pmx.MAX_SKETCH + 1) == pmx.ERR_INVALID_VALUE
+    assert ws(max_iter=0) == pmx.ERR_INVALID_VALUE
+    assert ws(tol=-1.0) == pmx.ERR_INVALID_VALUE
+    assert ws(alpha_lo=0.9, alpha_hi=0.5) == pmx.ERR_INVALID_VALUE
+    assert ws(alpha_lo=0.4, alpha_hi=float("nan")) == pmx.ERR_INVALID_VALUE
+    assert ws(struct_version=99) == pmx.ERR_INVALID_VALUE
+    assert ws(alpha_lo=0.5, alpha_hi=0.5) == pmx.OK
+    sz = ctypes.c_size_t()
+    assert pmx.lib.pmx_workspace_size(None, pmx.OP_INV_ROOT, 0, 0, 1, pmx.F32, None,
+                                      ctypes.byref(sz)) == pmx.ERR_INVALID_VALUE
+    assert pmx.lib.pmx_workspace_size(None, 9, 8, 8, 1, pmx.F32, None,
+                                      ctypes.byref(sz)) == pmx.ERR_INVALID_VALUE
+
+
+def test_calls_without_handle_enqueue_nothing():
+    from preconditioned_optimizer_matrix_amd import pmx
+    L = pmx.lib
+    assert L.pmx_matfn_inv_root(None, None, 8, 8, 4, None, 8, None, 8, None, None, None, 0,
+                                None) == pmx.ERR_INVALID_VALUE
+    assert L.pmx_matfn_polar(None, None, pmx.F32, 8, 4, 4, None, 4, None, None, None, 0,
+                             None) == pmx.ERR_INVALID_VALUE
+    assert L.pmx_precond_apply(None, None, 8, None, pmx.F32, 8, 4, 4, None, 4, None, 4,
+                               None, 0, None) == pmx.ERR_INVALID_VALUE
+    assert L.pmx_shampoo_stats_update(None, None, pmx.F32, 8, 4, 4, None, 8, None, 4, 0.9,
+                                      1e-6, None, 0, None) == pmx.ERR_INVALID_VALUE
+    h = ctypes.c_void_p()
+    assert L.pmx_create(None, 0) == pmx.ERR_INVALID_VALUE
+    assert L.pmx_destroy(None) == pmx.ERR_INVALID_VALUE
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    # the package never imports the oracle and its binding fails loudly
+    pkg = os.path.join(ROOT, "preconditioned_optimizer_matrix_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "numpy.linalg" not in txt and "np.linalg" not in txt, f

@@ -1,0 +1,203 @@
+"""GPU parity of libpmx against the fp64 oracle on small and ragged shapes.
+
+Tolerances: the fp32 path is held to a relative Frobenius error of 1e-4
+against the exact (eigendecomposition / SVD) results; single GEMM-based
+operations (statistics, apply) to 1e-5, which covers fp32 accumulation over
+K <= 512 (worst case K u ~ 3e-5, typical sqrt(K) u ~ 1e-6).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import closed_form as cf
+from oracle import prism
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from preconditioned_optimizer_matrix_amd import pmx
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    return torch, pmx, dev
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("m,n", [(17, 33), (64, 32), (130, 200), (256, 384), (1, 5)])
+def test_precond_apply(env, m, n):
+    torch, pmx, dev = env
+    _say("apply", m, n)
+    rng = np.random.default_rng(m * 1000 + n)
+    Li = rng.standard_normal((m, m)).astype(np.float32)
+    Ri = rng.standard_normal((n, n)).astype(np.float32)
+    G = rng.standard_normal((m, n)).astype(np.float32)
+    P = pmx.precond_apply(torch.from_numpy(Li).to(dev), torch.from_numpy(G).to(dev),
+                          torch.from_numpy(Ri).to(dev))
+    torch.cuda.synchronize()
+    assert cf.rel_fro(P.cpu().numpy(), cf.precond_apply(Li, G, Ri)) < 1e-5
+
+
+@pytest.mark.parametrize("m,n", [(17, 45), (100, 260), (128, 128), (3, 1)])
+def test_stats_update(env, m, n):
+    torch, pmx, dev = env
+    _say("stats", m, n)
+    rng = np.random.default_rng(m + n)
+    Gs = [rng.standard_normal((m, n)).astype(np.float32) for _ in range(3)]
+    L0 = (1e-3 * np.eye(m)).astype(np.float32)
+    R0 = (1e-3 * np.eye(n)).astype(np.float32)
+    L = torch.from_numpy(L0).to(dev)
+    R = torch.from_numpy(R0).to(dev)
+    for G in Gs:
+        pmx.shampoo_stats_update(torch.from_numpy(G).to(dev), L, R, 0.95, 1e-4)
+    torch.cuda.synchronize()
+    Lr, Rr = cf.stats_sequence(L0, R0, Gs, 0.95, 1e-4)
+    assert cf.rel_fro(L.cpu().numpy(), Lr) < 1e-5
+    assert cf.rel_fro(R.cpu().numpy(), Rr) < 1e-5
+
+
+def _run_root(env, A, p, **kw):
+    torch, pmx, dev = env
+    opts = pmx.default_opts(**kw)
+    X, XA, info = pmx.inv_root(torch.from_numpy(A).to(dev), p, opts=opts)
+    torch.cuda.synchronize()
+    return X.cpu().numpy(), XA.cpu().numpy(), pmx.parse_info(info)
+
+
+@pytest.mark.parametrize("n", [17, 64, 200])
+@pytest.mark.parametrize("p", [2, 4])
+def test_inv_root_matches_closed_form(env, n, p):
+    _, pmx, _ = env
+    _say("inv_root", n, p)
+    A, Q, lam = W.spd_logu(n, 1000 + n)
+    X, XA, info = _run_root(env, A, p, seed=11)
+    ref, ref_aux = cf.inv_root(A, p)
+    # fp32 floors the measured residual near u sqrt(n); reaching it is success
+    assert int(info[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+    assert cf.rel_fro(X, ref) < 1e-4
+    assert cf.rel_fro(XA, ref_aux) < 1e-4
+
+
+@pytest.mark.parametrize("p", [2, 4])
+def test_inv_root_iterations_and_alpha_follow_reference(env, p):
+    # same sketches on both sides: alpha traces agree while the residual is
+    # large enough for alpha to be well determined, iteration counts within 1
+    _, pmx, _ = env
+    A, _, _ = W.spd_logu(96, 77)
+    _say("alpha trace", p)
+    X, XA, info = _run_root(env, A, p, seed=5)
+    _, _, ref = prism.inv_root(A.astype(np.float64), p=p,
+                               sketch_fn=prism.make_sketch_fn(5, b=0, p=8))
+    inf = info[0]
+    assert int(inf["gemms"]) > 0
+    for s, st in enumerate(ref["stages"]):
+        it = int(inf["iters"][s])
+        assert abs(it - st.iters) <= 1, (s, it, st.iters)
+        for k in range(min(it, st.iters)):
+            if st.r[k] >= 1e-3:
+                assert abs(inf["alpha"][s][k] - st.alpha[k]) < 1e-3, (s, k)
+                assert inf["rtrace"][s][k] == pytest.approx(st.r[k], rel=1e-3)
+    total_ref = sum(st.gemms for st in ref["stages"])
+    assert abs(int(inf["gemms"]) - total_ref) <= 4 * len(ref["stages"])
+
+
+@pytest.mark.parametrize("d", [1, 2])
+def test_taylor_and_degree_variants(env, d):
+    _, pmx, _ = env
+    A, _, _ = W.spd_logu(80, 3, 1e-2, 1.0)
+    _say("variants d", d)
+    ref, _ = cf.inv_root(A, 2)
+    for acc in (0, 1):
+        X, _, info = _run_root(env, A, 2, degree=d, accelerate=acc)
+        assert int(info[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+        assert cf.rel_fro(X, ref) < 1e-4
+        _, _, r = prism.inv_root(A.astype(np.float64), p=2, d=d, accelerate=bool(acc),
+                                 sketch_fn=prism.make_sketch_fn(0))
+        assert abs(int(info[0]["iters"][0]) - r["stages"][0].iters) <= 1
+
+
+def test_inv_root_batched(env):
+    torch, pmx, dev = env
+    _say("batched inv_root")
+    As = np.stack([W.spd_logu(72, 50 + b, 10.0 ** -(b + 1), 1.0)[0] for b in range(4)])
+    X, XA, info = pmx.inv_root(torch.from_numpy(As).to(dev), 4)
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)
+    Xn = X.cpu().numpy()
+    for b in range(4):
+        assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+        assert cf.rel_fro(Xn[b], cf.inv_root(As[b], 4)[0]) < 1e-4
+    # matrices converge in different numbers of iterations
+    assert len(set(int(i) for i in inf["iters"][:, 0])) > 1
+
+
+@pytest.mark.parametrize("m,n", [(64, 32), (33, 70), (150, 150), (300, 17)])
+def test_polar_fp32(env, m, n):
+    torch, pmx, dev = env
+    _say("polar", m, n)
+    G = W.gaussian(m, n, m + 7 * n)
+    U, info = pmx.polar(torch.from_numpy(G).to(dev))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)[0]
+    Un = U.cpu().numpy()
+    ref, _ = cf.polar(G)
+    assert int(inf["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+    assert cf.rel_fro(Un, ref) < 1e-4
+    k = min(m, n)
+    gram = Un.T.astype(np.float64) @ Un if m >= n else Un.astype(np.float64) @ Un.T
+    assert np.linalg.norm(gram - np.eye(k)) / np.sqrt(k) < 1e-5
+
+
+def test_status_codes(env):
+    _, pmx, _ = env
+    _say("status codes")
+    A = np.diag([1.0, 0.5, -0.3, 0.2]).astype(np.float32)
+    X, _, info = _run_root(env, A, 2)
+    assert int(info[0]["status"]) == pmx.DIVERGED
+    assert np.all(np.isnan(X))
+    A = np.eye(6, dtype=np.float32)
+    A[1, 2] = np.nan
+    _, _, info = _run_root(env, A, 4)
+    assert int(info[0]["status"]) == pmx.NONFINITE
+    _, _, info = _run_root(env, np.zeros((5, 5), np.float32), 2)
+    assert int(info[0]["status"]) == pmx.NONFINITE
+    A64 = W.spd_64()["A"]
+    _, _, info = _run_root(env, A64, 2, max_iter=1)
+    assert int(info[0]["status"]) == pmx.MAXITER and int(info[0]["iters"][0]) == 1
+    _, _, info = _run_root(env, A64, 2, tol=0.0)
+    assert int(info[0]["status"]) == pmx.STAGNATED
+    # 1 x 1 and identity inputs
+    X, XA, info = _run_root(env, np.array([[4.0]], np.float32), 4)
+    assert int(info[0]["status"]) == pmx.CONVERGED
+    assert X[0, 0] == pytest.approx(4.0 ** -0.25, rel=1e-5)
+
+
+def test_argument_errors_enqueue_nothing(env):
+    import ctypes
+    torch, pmx, dev = env
+    h = pmx.handle()
+    A = torch.eye(8, device=dev)
+    X = torch.empty_like(A)
+    ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, 8, 8), dev)
+    L = pmx.lib
+    args = lambda **o: dict(dict(A=A.data_ptr(), n=8, lda=8, p=4, X=X.data_ptr(), ldx=8,
+                                 ws=ws.data_ptr(), wsb=ws.numel()), **o)
+
+    def call(a):
+        return L.pmx_matfn_inv_root(h, a["A"], a["n"], a["lda"], a["p"], a["X"], a["ldx"],
+                                    None, 8, None, None, a["ws"], a["wsb"], None)
+
+    assert call(args()) == pmx.OK
+    assert call(args(p=3)) == pmx.ERR_INVALID_VALUE
+    assert call(args(lda=4)) == pmx.ERR_INVALID_VALUE
+    assert call(args(n=0)) == pmx.ERR_INVALID_VALUE
+    assert call(args(X=A.data_ptr())) == pmx.ERR_ALIAS
+    assert call(args(wsb=16)) == pmx.ERR_WORKSPACE
+    assert call(args(ws=ws.data_ptr() + 4)) == pmx.ERR_WORKSPACE
+    assert call(args(ws=None)) == pmx.ERR_WORKSPACE
+    torch.cuda.synchronize()
