@@ -1,0 +1,196 @@
+"""Benchmark of the PRISM Shampoo hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step = one Shampoo step for one 1024 x 4096 layer (fp32): restore the
+statistics after nine warm-up updates, the tenth statistics update
+L <- beta L + (1 - beta) G G^T + eps I, R <- beta R + (1 - beta) G^T G + eps I,
+the inverse 4th roots L^{-1/4} (n = 1024) and R^{-1/4} (n = 4096) by PRISM
+coupled Newton-Schulz, and the preconditioned step L^{-1/4} G R^{-1/4}.
+Inputs are seeded synthetic gradients (workloads.shampoo_1024x4096), resident
+in HBM before timing starts.  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per inverse-4th-root (n=4096) + MFMA TFLOP/s vs peak; GEMMs to converge"
+PEAK_FP32_MFMA = 157.3  # TFLOP/s, MI355X dense fp32 matrix
+PEAK_HBM = 8000.0       # GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--max-iter", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(G, L0, R0, beta, eps):
+    """The fp64 oracle (closed forms: eigendecomposition roots) for one full
+    step at the full size, timed on the host cores."""
+    from oracle import closed_form as cf
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    L, R = cf.stats_update(L0, R0, G, beta, eps)
+    t1 = time.perf_counter()
+    Linv, _ = cf.inv_root(L, 4)
+    t2 = time.perf_counter()
+    Rinv, _ = cf.inv_root(R, 4)
+    t3 = time.perf_counter()
+    cf.precond_apply(Linv, G, Rinv)
+    t4 = time.perf_counter()
+    return dict(value=round((t3 - t2) * 1e3, 1), unit="ms per inverse-4th-root (n=4096)",
+                cores=int(threads), kind="oracle",
+                sample="one full step at full size (fp64 stats update, eigh-based L^-1/4 and "
+                       "R^-1/4, apply) = %.1f s; value is the R^-1/4 part" % (t4 - t0),
+                step_s=round(t4 - t0, 2))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: every GPU box here has one GPU, and the path "
+              "has no multi-GPU implementation (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as W
+    from preconditioned_optimizer_matrix_amd import pmx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.shampoo_1024x4096()
+    m, n = cfg["Gs"][0].shape
+    beta, eps = cfg["beta"], cfg["eps"]
+    Gs = [torch.from_numpy(g).to(dev) for g in cfg["Gs"]]
+    L = torch.from_numpy(cfg["L0"]).to(dev)
+    R = torch.from_numpy(cfg["R0"]).to(dev)
+    for g in Gs[:-1]:
+        pmx.shampoo_stats_update(g, L, R, beta, eps)
+    L9, R9 = L.clone(), R.clone()
+    G = Gs[-1]
+    opts = pmx.default_opts(max_iter=args.max_iter)
+    wsL = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, m, m, 1, pmx.F32, opts), dev)
+    wsR = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, opts), dev)
+    wsA = pmx.workspace(pmx.workspace_bytes(pmx.OP_APPLY, m, n, 1, pmx.F32, None), dev)
+    Li, Ri, P = torch.empty_like(L), torch.empty_like(R), torch.empty_like(G)
+    infoL, infoR = pmx.new_info(1, dev), pmx.new_info(1, dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    r_ev = [(ev(), ev()) for _ in range(args.steps)]
+
+    def step(i=None):
+        L.copy_(L9)
+        R.copy_(R9)
+        pmx.shampoo_stats_update(G, L, R, beta, eps)
+        pmx.inv_root(L, 4, opts=opts, aux=False, out=Li, info=infoL, ws=wsL)
+        if i is not None:
+            r_ev[i][0].record()
+        pmx.inv_root(R, 4, opts=opts, aux=False, out=Ri, info=infoR, ws=wsR)
+        if i is not None:
+            r_ev[i][1].record()
+        pmx.precond_apply(Li, G, Ri, out=P, ws=wsA)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = ev(), ev()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    r_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ev]))
+    iL, iR = pmx.parse_info(infoL)[0], pmx.parse_info(infoR)[0]
+    gemmsR, gemmsL = int(iR["gemms"]), int(iL["gemms"])
+    tflops_r = gemmsR * 2.0 * n ** 3 / (r_ms * 1e-3) / 1e12
+    log("step %.3f ms, R^-1/4 %.3f ms, gemms R %d L %d, iters R %s L %s, status R %s L %s"
+        % (ms_step, r_ms, gemmsR, gemmsL, list(iR["iters"]), list(iL["iters"]),
+           pmx.STATUS_NAMES[int(iR["status"])], pmx.STATUS_NAMES[int(iL["status"])]))
+
+    # property check at full size: || X^4 R e_j - e_j || on sampled columns (fp64)
+    cols = torch.arange(0, n, n // 8, device=dev)
+    E = torch.zeros(n, len(cols), dtype=torch.float64, device=dev)
+    E[cols, torch.arange(len(cols), device=dev)] = 1.0
+    V = R.double() @ E
+    Xd = Ri.double()
+    for _ in range(4):
+        V = Xd @ V
+    prop = float((V - E).norm(dim=0).max())
+    log("max_j ||R^{-1/4}^4 R e_j - e_j|| over 8 sampled columns: %.2e" % prop)
+
+    roofline = None
+    trace = None
+    if not args.no_trace:
+        # one more step with the launch trace: per-class kernel time and launches
+        pmx.trace_enable(True)
+        step()
+        trace = pmx.trace_collect()
+        pmx.trace_enable(False)
+        t_ms, launches = trace["gemm_update"]
+        iL2, iR2 = pmx.parse_info(infoL)[0], pmx.parse_info(infoR)[0]
+
+        def upd_products(info):
+            return sum(2 * int(it) - 1 for it in info["iters"] if int(it) > 0)
+
+        flops = (upd_products(iL2) * 2.0 * m ** 3 + upd_products(iR2) * 2.0 * n ** 3)
+        avg_ms = t_ms / max(launches, 1)
+        achieved = flops / launches / (avg_ms * 1e-3) / 1e12
+        roofline = dict(bound="mfma", kernel="gemm_f32_kernel<false,false,ROLE_UPDATE>",
+                        achieved=round(achieved, 2), peak=PEAK_FP32_MFMA, unit="TFLOP/s",
+                        frac=round(achieved / PEAK_FP32_MFMA, 4), traffic=None,
+                        launches=int(launches), avg_launch_ms=round(avg_ms, 4),
+                        algorithmic_flops_per_launch=round(flops / launches, 1))
+        log("trace:", {k: (round(v[0], 3), v[1]) for k, v in trace.items()})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg["Gs"][-1], L9.cpu().numpy(), R9.cpu().numpy(), beta, eps)
+        log("cpu baseline:", cpu)
+
+    out = {
+        "metric": METRIC, "value": round(r_ms, 3), "unit": "ms", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "shampoo_1024x4096", "m": m, "n": n, "beta": beta, "eps": eps,
+                   "warmup_updates": 9, "degree": 2, "sketch_p": 8, "tol": 1e-6,
+                   "max_iter": args.max_iter,
+                   "step": "restore L,R; stats update; L^-1/4; R^-1/4; apply"},
+        "gemms_to_converge": {"R": gemmsR, "L": gemmsL},
+        "iters": {"R": [int(x) for x in iR["iters"]], "L": [int(x) for x in iL["iters"]]},
+        "status": {"R": pmx.STATUS_NAMES[int(iR["status"])],
+                   "L": pmx.STATUS_NAMES[int(iL["status"])]},
+        "mfma_tflops_r_root": round(tflops_r, 2),
+        "mfma_frac_r_root": round(tflops_r / PEAK_FP32_MFMA, 4),
+        "property_x4r_minus_i": prop,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if trace is not None:
+        out["kernel_trace_ms"] = {k: [round(v[0], 3), v[1]] for k, v in trace.items()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -85,7 +85,7 @@ typedef struct {
   int32_t struct_version; /* must be PMX_OPTS_VERSION */
   int32_t degree;         /* d in {1, 2}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2 */
   int32_t sketch_p;       /* Gaussian sketch width p, 1..PMX_MAX_SKETCH; default 8 */
-  int32_t max_iter;       /* updates per stage, 1..1000; default 100 */
+  int32_t max_iter;       /* updates per stage, 1..1000; default 40 */
   int32_t accelerate;     /* 1: fitted alpha (PRISM); 0: alpha = Taylor c_d; default 1 */
   float alpha_lo;         /* alpha interval; NaN selects the default:       */
   float alpha_hi;         /*   d = 1: [1/2, 1], d = 2: [3/8, 1.47]          */
@@ -213,6 +213,32 @@ pmx_status pmx_precond_apply_batched(pmx_handle handle, const float* Linv, int l
                                      const float* Rinv, int ldr, int64_t stride_r, void* P,
                                      int ldp, int64_t stride_p, int batch, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Launch trace for benchmarking.  While enabled, every kernel that a call on
+ * this handle enqueues is bracketed by a pair of HIP events recorded on the
+ * call's stream (host-side event objects owned by the handle; no device
+ * memory).  Kernels are grouped into the classes below; each class is one
+ * kernel symbol family of the library.
+ */
+typedef enum {
+  PMX_KC_GEMM_POWER = 0,   /* R^2 = R R */
+  PMX_KC_GEMM_UPDATE = 1,  /* Y g and g Z (one launch), X g; g formed in the operand load */
+  PMX_KC_GEMM_RESID = 2,   /* I - Z Y, I - X^T X, Frobenius norm, convergence decision */
+  PMX_KC_GEMM_STATS = 3,   /* G G^T, G^T G with the EMA epilogue */
+  PMX_KC_GEMM_APPLY = 4,   /* L^{-1/4} G, then (L^{-1/4} G) R^{-1/4} */
+  PMX_KC_SKINNY = 5,       /* Krylov passes R^j S */
+  PMX_KC_SKINNY_ALPHA = 6, /* last Krylov pass with the Gram and the alpha solve */
+  PMX_KC_OTHER = 7,        /* control reset, scaling, stage set-up, first g, outputs */
+  PMX_KC_COUNT = 8
+} pmx_kernel_class;
+
+/* Enable (1) or disable (0) the launch trace; enabling discards old records. */
+pmx_status pmx_trace_enable(pmx_handle handle, int enable);
+/* Wait for the recorded events, write per kernel class the summed
+ * event-to-event time in milliseconds and the number of launches into
+ * ms[PMX_KC_COUNT] and launches[PMX_KC_COUNT], then clear the records. */
+pmx_status pmx_trace_collect(pmx_handle handle, double* ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,23 @@
 struct pmx_context {
   int device;
   int num_cu;
+  // launch trace (benchmarking): event pairs recorded around every launch
+  bool trace = false;
+  struct Rec {
+    int cls;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  hipEvent_t next_event() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
 };
 
 namespace pmx {
@@ -72,6 +89,28 @@ bool batch_layout_ok(int rows, int cols, int64_t ld, int64_t stride, int batch) 
 }
 
 pmx_status from_hip(hipError_t e) { return e == hipSuccess ? PMX_OK : PMX_ERR_HIP; }
+
+// Enqueue helper: runs a launcher on the call's stream, bracketed by trace
+// events when the handle's trace is enabled.
+struct Enq {
+  pmx_context* h;
+  hipStream_t s;
+  template <typename F>
+  hipError_t run(int cls, F&& f) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (h && h->trace) {
+      a = h->next_event();
+      b = h->next_event();
+      if (a && b) (void)hipEventRecord(a, s);
+    }
+    const hipError_t e = f();
+    if (a && b) {
+      (void)hipEventRecord(b, s);
+      h->recs.push_back({cls, a, b});
+    }
+    return e;
+  }
+};
 
 #define PMX_TRY(expr)                          \
   do {                                         \
@@ -158,6 +197,7 @@ IterCfg make_cfg(const pmx_matfn_opts& o, int n, pmx_matfn_info* info) {
   c.lo = o.alpha_lo;
   c.hi = o.alpha_hi;
   c.tol = o.tol;
+  c.taylor_d = (float)taylor(o.degree);
   c.seed_lo = (uint32_t)(o.seed & 0xFFFFFFFFull);
   c.seed_hi = (uint32_t)(o.seed >> 32);
   c.info = info;
@@ -166,8 +206,8 @@ IterCfg make_cfg(const pmx_matfn_opts& o, int n, pmx_matfn_info* info) {
 
 // ------------------------------------------------------------------ workspace
 struct IterLayout {
-  size_t ctrl, partials, bufs[6], kbuf, total;
-  int64_t buf_stride, kstride, kld, pstride;
+  size_t ctrl, partials, gram, bufs[6], kbuf, total;
+  int64_t buf_stride, kstride, kld, pstride, gstride;
 };
 
 // Work buffers of the iterative functions: `nbig` matrices of rows x cols
@@ -181,6 +221,9 @@ IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, i
   L.pstride = std::max<int64_t>(kPartialsPerMatrix, gemm_f32_tiles(cols, cols));
   L.partials = off;
   off = align_up(off + sizeof(double) * (size_t)L.pstride * batch);
+  L.gstride = (int64_t)16 * (skinny_blocks(cols, 1) + 1);
+  L.gram = off;
+  off = align_up(off + sizeof(double) * (size_t)L.gstride * batch);
   const int64_t big = (int64_t)rows * cols, small = (int64_t)cols * cols;
   (void)big_elem;
   L.buf_stride = ((std::max(big, small) + 63) / 64) * 64;  // elements (fp32 slots)
@@ -227,97 +270,93 @@ void set_vec(GemmParams& g) {
   g.vec = v ? 1 : 0;
 }
 
-// One PRISM iteration (update k of `stage`) of the sketch / alpha / g part,
-// shared by the square-root and polar sequences.  R and R2 are cols x cols.
-hipError_t enqueue_alpha_and_g(void* ws, const IterLayout& L, const pmx_matfn_opts& o,
-                               const IterCfg& cfg, const AlphaCoef& coef, int n, int batch,
-                               int stage, int k, float* R, float* R2, float* gdst,
-                               hipStream_t s) {
+SketchJob make_sketch(const IterLayout& L, void* ws, const IterCfg& cfg, int n, int k,
+                      int stage, bool on) {
+  SketchJob sj;
+  memset(&sj, 0, sizeof(sj));
+  if (!on) return sj;
+  sj.kbuf = at<float>(ws, L.kbuf);
+  sj.kld = L.kld;
+  sj.kstride = L.kstride;
+  sj.n = n;
+  sj.p = cfg.p;
+  sj.k = k;
+  sj.stage = stage;
+  sj.seed_lo = cfg.seed_lo;
+  sj.seed_hi = cfg.seed_hi;
+  return sj;
+}
+
+// The power R^2 (d = 2) and the alpha fit of one PRISM update, shared by the
+// square-root and polar sequences (R, R2 are n x n).  The sketch S_k is
+// already in the Krylov buffer (generated by the kernel that produced R_k).
+//   d = 2: K1 = R S / s, K2 = R^2 S / s^2; [K3 | K4] = R^2 [K1 | K2] / s^2;
+//          K5 = R^2 K3 / s^2 (+ Gram, alpha)
+//   d = 1: K_j = R K_{j-1} / s, j = 1..3 (+ Gram, alpha on the last pass)
+hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
+                                   const pmx_matfn_opts& o, const IterCfg& cfg,
+                                   const AlphaCoef& coef, int n, int batch, float* R,
+                                   float* R2) {
   Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
   float* kbuf = at<float>(ws, L.kbuf);
   const int d = o.degree, pp = o.sketch_p;
   hipError_t e;
   if (d == 2) {
     GemmParams g = gemm_base(n, n, n, batch);
-    g.prob[0].a = {R, n, L.buf_stride};
-    g.prob[0].b = {R, n, L.buf_stride};
+    g.prob[0].a = {R, n, L.buf_stride, nullptr, 0};
+    g.prob[0].b = {R, n, L.buf_stride, nullptr, 0};
     g.prob[0].c = R2;
     g.prob[0].ldc = n;
     g.prob[0].stride_c = L.buf_stride;
     g.ctrl = ctrl;
     set_vec(g);
-    if ((e = launch_gemm_f32(g, false, false, EPI_STORE, s)) != hipSuccess) return e;
+    e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
+    if (e != hipSuccess) return e;
   }
-  if (o.accelerate) {
-    SketchParams sp;
-    sp.kbuf = kbuf;
-    sp.kld = L.kld;
-    sp.kstride = L.kstride;
-    sp.n = n;
-    sp.p = pp;
-    sp.k = k;
-    sp.stage = stage;
-    sp.seed_lo = cfg.seed_lo;
-    sp.seed_hi = cfg.seed_hi;
-    sp.ctrl = ctrl;
-    if ((e = launch_sketch(sp, batch, s)) != hipSuccess) return e;
-    SkinnyParams kp;
-    memset(&kp, 0, sizeof(kp));
-    kp.kbuf = kbuf;
-    kp.kld = L.kld;
-    kp.kstride = L.kstride;
-    kp.n = n;
-    kp.ctrl = ctrl;
-    auto job = [&](const float* m, int ic, int oc, int pw) {
-      SkinnyJob j;
-      j.mat = m;
-      j.mat_ld = n;
-      j.mat_stride = L.buf_stride;
-      j.in_col = ic;
-      j.out_col = oc;
-      j.pow = pw;
-      return j;
-    };
-    if (d == 2) {
-      // K1 = R S / s, K2 = R^2 S / s^2; [K3 | K4] = R^2 [K1 | K2] / s^2; K5 = R^2 K3 / s^2
-      kp.q = pp;
-      kp.job[0] = job(R, 0, pp, 1);
-      kp.job[1] = job(R2, 0, 2 * pp, 2);
-      if ((e = launch_skinny(kp, 2, batch, s)) != hipSuccess) return e;
-      kp.q = 2 * pp;
-      kp.job[0] = job(R2, pp, 3 * pp, 2);
-      if ((e = launch_skinny(kp, 1, batch, s)) != hipSuccess) return e;
-      kp.q = pp;
-      kp.job[0] = job(R2, 3 * pp, 5 * pp, 2);
-      if ((e = launch_skinny(kp, 1, batch, s)) != hipSuccess) return e;
-    } else {
-      // K_j = R K_{j-1} / s, j = 1..3
-      kp.q = pp;
-      for (int j = 1; j <= 3; ++j) {
-        kp.job[0] = job(R, (j - 1) * pp, j * pp, 1);
-        if ((e = launch_skinny(kp, 1, batch, s)) != hipSuccess) return e;
-      }
-    }
+  if (!o.accelerate) return hipSuccess;
+  SkinnyParams kp;
+  memset(&kp, 0, sizeof(kp));
+  kp.kbuf = kbuf;
+  kp.kld = L.kld;
+  kp.kstride = L.kstride;
+  kp.n = n;
+  kp.ctrl = ctrl;
+  kp.gram_partials = at<double>(ws, L.gram);
+  kp.gram_stride = L.gstride;
+  kp.cfg = cfg;
+  kp.coef = coef;
+  auto job = [&](const float* m, int ic, int oc, int pw) {
+    SkinnyJob j;
+    j.mat = m;
+    j.mat_ld = n;
+    j.mat_stride = L.buf_stride;
+    j.in_col = ic;
+    j.out_col = oc;
+    j.pow = pw;
+    return j;
+  };
+  auto pass = [&](int njobs, bool gram) {
+    return q.run(gram ? PMX_KC_SKINNY_ALPHA : PMX_KC_SKINNY,
+                 [&] { return launch_skinny(kp, njobs, gram, batch, q.s); });
+  };
+  if (d == 2) {
+    kp.q = pp;
+    kp.job[0] = job(R, 0, pp, 1);
+    kp.job[1] = job(R2, 0, 2 * pp, 2);
+    if ((e = pass(2, false)) != hipSuccess) return e;
+    kp.q = 2 * pp;
+    kp.job[0] = job(R2, pp, 3 * pp, 2);
+    if ((e = pass(1, false)) != hipSuccess) return e;
+    kp.q = pp;
+    kp.job[0] = job(R2, 3 * pp, 5 * pp, 2);
+    return pass(1, true);
   }
-  AlphaParams ap;
-  ap.kbuf = kbuf;
-  ap.kld = L.kld;
-  ap.kstride = L.kstride;
-  ap.ctrl = ctrl;
-  ap.cfg = cfg;
-  ap.coef = coef;
-  if ((e = launch_alpha(ap, batch, s)) != hipSuccess) return e;
-  FormGParams fp;
-  fp.r = R;
-  fp.r2 = (d == 2) ? R2 : nullptr;
-  fp.dst = gdst;
-  fp.stride = L.buf_stride;
-  fp.n = n;
-  fp.degree = d;
-  fp.c0 = (float)taylor(0);
-  fp.c1 = (float)taylor(1);
-  fp.ctrl = ctrl;
-  return launch_form_g(fp, batch, s);
+  kp.q = pp;
+  for (int j = 1; j <= 3; ++j) {
+    kp.job[0] = job(R, (j - 1) * pp, j * pp, 1);
+    if ((e = pass(1, j == 3)) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -347,7 +386,7 @@ pmx_status pmx_matfn_opts_default(pmx_matfn_opts* o) {
   o->struct_version = PMX_OPTS_VERSION;
   o->degree = 2;
   o->sketch_p = 8;
-  o->max_iter = 100;
+  o->max_iter = 40;
   o->accelerate = 1;
   o->alpha_lo = NAN;
   o->alpha_hi = NAN;
@@ -375,8 +414,42 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
 
 pmx_status pmx_destroy(pmx_handle h) {
   if (!h) return PMX_ERR_INVALID_VALUE;
+  for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
   delete h;
   return PMX_OK;
+}
+
+pmx_status pmx_trace_enable(pmx_handle h, int enable) {
+  if (!h || (enable != 0 && enable != 1)) return PMX_ERR_INVALID_VALUE;
+  h->trace = enable != 0;
+  h->recs.clear();
+  h->used = 0;
+  return PMX_OK;
+}
+
+pmx_status pmx_trace_collect(pmx_handle h, double* ms, int64_t* launches) {
+  if (!h || !ms || !launches) return PMX_ERR_INVALID_VALUE;
+  for (int i = 0; i < PMX_KC_COUNT; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  pmx_status st = PMX_OK;
+  for (const auto& r : h->recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) {
+      st = PMX_ERR_HIP;
+      break;
+    }
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      st = PMX_ERR_HIP;
+      break;
+    }
+    ms[r.cls] += t;
+    launches[r.cls] += 1;
+  }
+  h->recs.clear();
+  h->used = 0;
+  return st;
 }
 
 static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
@@ -448,13 +521,13 @@ pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dty
   if (overlap(eg, el) || overlap(eg, er) || overlap(el, er)) return PMX_ERR_ALIAS;
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
-  hipStream_t s = (hipStream_t)stream;
+  Enq q{h, (hipStream_t)stream};
   const float* g = (const float*)G;
   const float omb = 1.f - beta;
   if (L) {
     GemmParams p = gemm_base(m, m, n, batch);
-    p.prob[0].a = {g, ldg, sg};
-    p.prob[0].b = {g, ldg, sg};
+    p.prob[0].a = {g, ldg, sg, nullptr, 0};
+    p.prob[0].b = {g, ldg, sg, nullptr, 0};
     p.prob[0].c = L;
     p.prob[0].ldc = ldl;
     p.prob[0].stride_c = sl;
@@ -462,12 +535,12 @@ pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dty
     p.omb = omb;
     p.eps = eps;
     set_vec(p);
-    PMX_TRY(launch_gemm_f32(p, false, true, EPI_EMA, s));
+    PMX_TRY(q.run(PMX_KC_GEMM_STATS, [&] { return launch_gemm_f32(p, false, true, ROLE_STATS, q.s); }));
   }
   if (R) {
     GemmParams p = gemm_base(n, n, m, batch);
-    p.prob[0].a = {g, ldg, sg};
-    p.prob[0].b = {g, ldg, sg};
+    p.prob[0].a = {g, ldg, sg, nullptr, 0};
+    p.prob[0].b = {g, ldg, sg, nullptr, 0};
     p.prob[0].c = R;
     p.prob[0].ldc = ldr;
     p.prob[0].stride_c = sr;
@@ -475,7 +548,7 @@ pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dty
     p.omb = omb;
     p.eps = eps;
     set_vec(p);
-    PMX_TRY(launch_gemm_f32(p, true, false, EPI_EMA, s));
+    PMX_TRY(q.run(PMX_KC_GEMM_STATS, [&] { return launch_gemm_f32(p, true, false, ROLE_STATS, q.s); }));
   }
   return PMX_OK;
 }
@@ -520,7 +593,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
 
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
-  hipStream_t s = (hipStream_t)stream;
+  Enq q{h, (hipStream_t)stream};
   Ctrl* ctrl = at<Ctrl>(ws, Lw.ctrl);
   double* partials = at<double>(ws, Lw.partials);
   float* Yb[2] = {at<float>(ws, Lw.bufs[0]), at<float>(ws, Lw.bufs[1])};
@@ -530,9 +603,12 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   const IterCfg cfg = make_cfg(o, n, info);
   const AlphaCoef coef = make_coef(o.degree);
   const int d = o.degree;
+  const bool acc = o.accelerate != 0;
 
-  PMX_TRY(launch_ctrl_reset(ctrl, info, batch, s));
-  PMX_TRY(launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, s));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+    return launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, q.s);
+  }));
   const int stages = (p == 4) ? 2 : 1;
   for (int stage = 0; stage < stages; ++stage) {
     StageInitParams ip;
@@ -549,32 +625,54 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
     ip.partials = partials;
     ip.partial_stride = Lw.pstride;
     ip.cfg = cfg;
-    PMX_TRY(launch_sqrt_stage_init(ip, batch, s));
+    ip.sketch = make_sketch(Lw, ws, cfg, n, 0, stage, acc);
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_sqrt_stage_init(ip, batch, q.s); }));
     for (int k = 0; k < o.max_iter; ++k) {
-      float* gdst = (k == 0) ? Zb[1] : R2b;
-      PMX_TRY(enqueue_alpha_and_g(ws, Lw, o, cfg, coef, n, batch, stage, k, Rb, R2b, gdst, s));
+      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b));
       const int cur = k & 1, nxt = cur ^ 1;
       GemmParams u = gemm_base(n, n, n, batch);
       u.ctrl = ctrl;
-      u.prob[0].a = {Yb[cur], n, Lw.buf_stride};
-      u.prob[0].b = {gdst, n, Lw.buf_stride};
-      u.prob[0].c = Yb[nxt];
-      u.prob[0].ldc = n;
-      u.prob[0].stride_c = Lw.buf_stride;
-      if (k > 0) {
+      u.degree = d;
+      u.c0 = (float)taylor(0);
+      u.c1 = (float)taylor(1);
+      if (k == 0) {
+        // Z_1 = g Z_0 = g is written explicitly; Y_1 = Y_0 g reads it back.
+        FormGParams fp;
+        fp.r = Rb;
+        fp.r2 = (d == 2) ? R2b : nullptr;
+        fp.dst = Zb[1];
+        fp.stride = Lw.buf_stride;
+        fp.n = n;
+        fp.degree = d;
+        fp.c0 = (float)taylor(0);
+        fp.c1 = (float)taylor(1);
+        fp.ctrl = ctrl;
+        PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
+        u.prob[0].a = {Yb[0], n, Lw.buf_stride, nullptr, 0};
+        u.prob[0].b = {Zb[1], n, Lw.buf_stride, nullptr, 0};
+        u.prob[0].c = Yb[1];
+        u.prob[0].ldc = n;
+        u.prob[0].stride_c = Lw.buf_stride;
+      } else {
+        // Y_{k+1} = Y_k g and Z_{k+1} = g Z_k, g = f_{d-1}(R) + alpha R^d formed on load
         u.nprob = 2;
-        u.prob[1].a = {gdst, n, Lw.buf_stride};
-        u.prob[1].b = {Zb[cur], n, Lw.buf_stride};
+        u.prob[0].a = {Yb[cur], n, Lw.buf_stride, nullptr, 0};
+        u.prob[0].b = {Rb, n, Lw.buf_stride, R2b, 1};
+        u.prob[0].c = Yb[nxt];
+        u.prob[0].ldc = n;
+        u.prob[0].stride_c = Lw.buf_stride;
+        u.prob[1].a = {Rb, n, Lw.buf_stride, R2b, 1};
+        u.prob[1].b = {Zb[cur], n, Lw.buf_stride, nullptr, 0};
         u.prob[1].c = Zb[nxt];
         u.prob[1].ldc = n;
         u.prob[1].stride_c = Lw.buf_stride;
       }
       set_vec(u);
-      PMX_TRY(launch_gemm_f32(u, false, false, EPI_STORE, s));
+      PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
       GemmParams r = gemm_base(n, n, n, batch);
       r.ctrl = ctrl;
-      r.prob[0].a = {Zb[nxt], n, Lw.buf_stride};
-      r.prob[0].b = {Yb[nxt], n, Lw.buf_stride};
+      r.prob[0].a = {Zb[nxt], n, Lw.buf_stride, nullptr, 0};
+      r.prob[0].b = {Yb[nxt], n, Lw.buf_stride, nullptr, 0};
       r.prob[0].c = Rb;
       r.prob[0].ldc = n;
       r.prob[0].stride_c = Lw.buf_stride;
@@ -583,8 +681,9 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       r.products = (d - 1) + 1 + (k > 0 ? 1 : 0) + 1;
       r.count_update = 1;
       r.cfg = cfg;
+      r.sketch = make_sketch(Lw, ws, cfg, n, k + 1, stage, acc && k + 1 < o.max_iter);
       set_vec(r);
-      PMX_TRY(launch_gemm_f32(r, false, false, EPI_RESID, s));
+      PMX_TRY(q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, false, false, ROLE_RESID, q.s); }));
     }
   }
   RootFinishParams fp;
@@ -603,7 +702,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   fp.expo_x = -1.0 / p;
   fp.expo_aux = 1.0 / p;
   fp.ctrl = ctrl;
-  PMX_TRY(launch_root_finish(fp, batch, s));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_root_finish(fp, batch, q.s); }));
   return PMX_OK;
 }
 
@@ -647,7 +746,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
 
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
-  hipStream_t s = (hipStream_t)stream;
+  Enq q{h, (hipStream_t)stream};
   Ctrl* ctrl = at<Ctrl>(ws, Lw.ctrl);
   double* partials = at<double>(ws, Lw.partials);
   float* Xb[2] = {at<float>(ws, Lw.bufs[0]), at<float>(ws, Lw.bufs[1])};
@@ -656,9 +755,12 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const IterCfg cfg = make_cfg(o, cols, info);
   const AlphaCoef coef = make_coef(o.degree);
   const int d = o.degree;
+  const bool acc = o.accelerate != 0;
 
-  PMX_TRY(launch_ctrl_reset(ctrl, info, batch, s));
-  PMX_TRY(launch_fro_scale(G, false, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, s));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+    return launch_fro_scale(G, false, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, q.s);
+  }));
   PolarInitParams pi;
   pi.g = G;
   pi.ldg = ldg;
@@ -669,13 +771,13 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   pi.cols = cols;
   pi.transpose = tr ? 1 : 0;
   pi.ctrl = ctrl;
-  PMX_TRY(launch_polar_init(pi, false, batch, s));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_init(pi, false, batch, q.s); }));
 
-  auto residual = [&](float* Xc, int products, int count) {
+  auto residual = [&](float* Xc, int products, int count, int k_next) {
     GemmParams r = gemm_base(cols, cols, rows, batch);
     r.ctrl = ctrl;
-    r.prob[0].a = {Xc, cols, Lw.buf_stride};
-    r.prob[0].b = {Xc, cols, Lw.buf_stride};
+    r.prob[0].a = {Xc, cols, Lw.buf_stride, nullptr, 0};
+    r.prob[0].b = {Xc, cols, Lw.buf_stride, nullptr, 0};
     r.prob[0].c = Rb;
     r.prob[0].ldc = cols;
     r.prob[0].stride_c = Lw.buf_stride;
@@ -684,23 +786,27 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     r.products = products;
     r.count_update = count;
     r.cfg = cfg;
+    r.sketch = make_sketch(Lw, ws, cfg, cols, k_next, 0, acc && k_next < o.max_iter);
     set_vec(r);
-    return launch_gemm_f32(r, true, false, EPI_RESID, s);
+    return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
   };
-  PMX_TRY(residual(Xb[0], 1, 0));
+  PMX_TRY(residual(Xb[0], 1, 0, 0));
   for (int k = 0; k < o.max_iter; ++k) {
-    PMX_TRY(enqueue_alpha_and_g(ws, Lw, o, cfg, coef, cols, batch, 0, k, Rb, R2b, R2b, s));
+    PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b));
     const int cur = k & 1, nxt = cur ^ 1;
     GemmParams u = gemm_base(rows, cols, cols, batch);
     u.ctrl = ctrl;
-    u.prob[0].a = {Xb[cur], cols, Lw.buf_stride};
-    u.prob[0].b = {R2b, cols, Lw.buf_stride};
+    u.degree = d;
+    u.c0 = (float)taylor(0);
+    u.c1 = (float)taylor(1);
+    u.prob[0].a = {Xb[cur], cols, Lw.buf_stride, nullptr, 0};
+    u.prob[0].b = {Rb, cols, Lw.buf_stride, R2b, 1};
     u.prob[0].c = Xb[nxt];
     u.prob[0].ldc = cols;
     u.prob[0].stride_c = Lw.buf_stride;
     set_vec(u);
-    PMX_TRY(launch_gemm_f32(u, false, false, EPI_STORE, s));
-    PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1));
+    PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
+    PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1, k + 1));
   }
   PolarFinishParams fp;
   fp.xbuf[0] = Xb[0];
@@ -713,7 +819,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   fp.cols = cols;
   fp.transpose = tr ? 1 : 0;
   fp.ctrl = ctrl;
-  PMX_TRY(launch_polar_finish(fp, false, batch, s));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_finish(fp, false, batch, q.s); }));
   return PMX_OK;
 }
 
@@ -754,25 +860,25 @@ pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, i
     return PMX_ERR_ALIAS;
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
-  hipStream_t s = (hipStream_t)stream;
+  Enq q{h, (hipStream_t)stream};
   float* T = (float*)ws;
   const int64_t st_t = (int64_t)m * n;
   GemmParams a = gemm_base(m, n, m, batch);
-  a.prob[0].a = {Linv, ldl, sl};
-  a.prob[0].b = {(const float*)G, ldg, sg};
+  a.prob[0].a = {Linv, ldl, sl, nullptr, 0};
+  a.prob[0].b = {(const float*)G, ldg, sg, nullptr, 0};
   a.prob[0].c = T;
   a.prob[0].ldc = n;
   a.prob[0].stride_c = st_t;
   set_vec(a);
-  PMX_TRY(launch_gemm_f32(a, false, false, EPI_STORE, s));
+  PMX_TRY(q.run(PMX_KC_GEMM_APPLY, [&] { return launch_gemm_f32(a, false, false, ROLE_APPLY, q.s); }));
   GemmParams b = gemm_base(m, n, n, batch);
-  b.prob[0].a = {T, n, st_t};
-  b.prob[0].b = {Rinv, ldr, sr};
+  b.prob[0].a = {T, n, st_t, nullptr, 0};
+  b.prob[0].b = {Rinv, ldr, sr, nullptr, 0};
   b.prob[0].c = (float*)P;
   b.prob[0].ldc = ldp;
   b.prob[0].stride_c = sp;
   set_vec(b);
-  PMX_TRY(launch_gemm_f32(b, false, false, EPI_STORE, s));
+  PMX_TRY(q.run(PMX_KC_GEMM_APPLY, [&] { return launch_gemm_f32(b, false, false, ROLE_APPLY, q.s); }));
   return PMX_OK;
 }
 

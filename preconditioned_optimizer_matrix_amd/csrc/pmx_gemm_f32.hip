@@ -21,13 +21,19 @@
 //    with 16-byte stores straight from the 16-byte global loads.
 //  * LDS is double buffered with a register prefetch of the next k-tile:
 //    one barrier per k-tile.
-//  * Epilogues: plain store; residual R = I - acc with a deterministic
-//    Frobenius reduction and the convergence decision (last block per matrix);
+//  * An operand may be the PRISM polynomial g = c0 I + c1 R + alpha R^2
+//    (or c0 I + alpha R for d = 1), formed while its tile is loaded from R and
+//    R^2, so g is never written to memory.
+//  * Epilogues by role: plain store; residual R = I - acc with a deterministic
+//    Frobenius reduction and the convergence decision (last block per matrix),
+//    while the blocks also generate the next iteration's Gaussian sketch;
 //    Shampoo EMA C = beta C + (1 - beta) acc + eps I in place.
 #include "pmx_internal.h"
 
 namespace pmx {
 namespace {
+
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_EMA = 2 };
 
 constexpr int BM = 128, BN = 128, BK = 16;
 constexpr int KC_LD = BK + 4;    // KC layout: [row][k], row stride 20 floats (80 B)
@@ -48,13 +54,22 @@ struct Layout {
   static constexpr bool kc = IS_A ? !TRANS : TRANS;
 };
 
+// Polynomial operand constants for one block.
+struct PolyCtx {
+  float c0, c1, alpha;
+  int degree;
+};
+
 // Global -> register prefetch of one 128 x 16 operand tile: two float4 per thread.
 // KC: storage rows are the tile's m/n rows, 16 k values = 4 float4 per row.
 // MC: storage rows are k, 128 m/n values = 32 float4 per row.
+// With `poly` the element (i, j) of the stored matrix is
+// c0 [i == j] + c1 R[i][j] + alpha R2[i][j] (d = 2) or c0 [i == j] + alpha R[i][j].
 template <bool KCL>
 __device__ __forceinline__ void load_tile(f32x4 (&r)[2], const float* __restrict__ base,
-                                          int64_t ld, int row0, int nrows, int k0, int K,
-                                          bool vec) {
+                                          const float* __restrict__ base2, bool poly,
+                                          const PolyCtx& pc, int64_t ld, int row0, int nrows,
+                                          int k0, int K, bool vec) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int idx = threadIdx.x + NT * i;
@@ -72,13 +87,37 @@ __device__ __forceinline__ void load_tile(f32x4 (&r)[2], const float* __restrict
     }
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (srow < lim_row) {
-      const float* src = base + (int64_t)srow * ld + scol;
-      if (vec && scol + 3 < lim_col) {
-        v = *reinterpret_cast<const f32x4*>(src);
-      } else {
+      const int64_t off = (int64_t)srow * ld + scol;
+      const float* src = base + off;
+      const bool full = vec && scol + 3 < lim_col;
+      if (!poly) {
+        if (full) {
+          v = *reinterpret_cast<const f32x4*>(src);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (scol + j < lim_col) v[j] = src[j];
+          for (int j = 0; j < 4; ++j)
+            if (scol + j < lim_col) v[j] = src[j];
+        }
+      } else {
+        f32x4 r1 = {0.f, 0.f, 0.f, 0.f}, r2 = {0.f, 0.f, 0.f, 0.f};
+        const float* src2 = base2 + off;
+        if (full) {
+          r1 = *reinterpret_cast<const f32x4*>(src);
+          if (pc.degree == 2) r2 = *reinterpret_cast<const f32x4*>(src2);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (scol + j < lim_col) {
+              r1[j] = src[j];
+              if (pc.degree == 2) r2[j] = src2[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float g = (pc.degree == 2) ? (pc.c1 * r1[j] + pc.alpha * r2[j]) : pc.alpha * r1[j];
+          if (srow == scol + j) g += pc.c0;
+          v[j] = (scol + j < lim_col) ? g : 0.f;
+        }
       }
     }
     r[i] = v;
@@ -116,8 +155,9 @@ __device__ __forceinline__ void read_frag(float (&f)[8], const float* __restrict
   }
 }
 
-template <bool TA, bool TB, int EPI>
+template <bool TA, bool TB, int ROLE>
 __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmParams p) {
+  constexpr int EPI = ROLE == ROLE_RESID ? EPI_RESID : (ROLE == ROLE_STATS ? EPI_EMA : EPI_STORE);
   const int z = blockIdx.z;
   const int pi = z % p.nprob;
   const int b = z / p.nprob;
@@ -132,6 +172,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmParams p) {
 
   const int tile = blockIdx.x;
   const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+  PolyCtx pc;
+  pc.c0 = p.c0;
+  pc.c1 = p.c1;
+  pc.degree = p.degree;
+  pc.alpha = (p.ctrl && (pr.a.poly || pr.b.poly)) ? (float)p.ctrl[b].alpha : 0.f;
+  if (EPI == EPI_RESID) sketch_share(p.sketch, b, tile, gridDim.x);
   const int m0 = tm * BM, n0 = tn * BN;
 
   constexpr bool AKC = Layout<true, TA>::kc;
@@ -154,8 +200,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmParams p) {
   const bool vec = p.vec != 0;
   const int nk = (p.K + BK - 1) / BK;
   f32x4 ra[2], rb[2];
-  load_tile<AKC>(ra, A, pr.a.ld, m0, p.M, 0, p.K, vec);
-  load_tile<BKC>(rb, B, pr.b.ld, n0, p.N, 0, p.K, vec);
+  const float* __restrict__ A2 = pr.a.poly && pr.a.ptr2 ? pr.a.ptr2 + (int64_t)b * pr.a.stride : A;
+  const float* __restrict__ B2 = pr.b.poly && pr.b.ptr2 ? pr.b.ptr2 + (int64_t)b * pr.b.stride : B;
+  const bool apoly = pr.a.poly != 0, bpoly = pr.b.poly != 0;
+  load_tile<AKC>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, 0, p.K, vec);
+  load_tile<BKC>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, 0, p.K, vec);
   store_tile<AKC>(smem[0][0], ra);
   store_tile<BKC>(smem[0][1], rb);
   __syncthreads();
@@ -164,8 +213,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmParams p) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
-      load_tile<AKC>(ra, A, pr.a.ld, m0, p.M, (kt + 1) * BK, p.K, vec);
-      load_tile<BKC>(rb, B, pr.b.ld, n0, p.N, (kt + 1) * BK, p.K, vec);
+      load_tile<AKC>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, (kt + 1) * BK, p.K, vec);
+      load_tile<BKC>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, (kt + 1) * BK, p.K, vec);
     }
     float fa[2][8], fb[2][8];
 #pragma unroll
@@ -229,30 +278,40 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmParams p) {
   }
 }
 
-template <bool TA, bool TB>
-hipError_t launch_t(const GemmParams& p, int epi, dim3 grid, hipStream_t s) {
-  switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, EPI_STORE>), grid, dim3(NT), 0, s, p); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, EPI_RESID>), grid, dim3(NT), 0, s, p); break;
-    case EPI_EMA: hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, EPI_EMA>), grid, dim3(NT), 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
+#define PMX_GEMM_LAUNCH(TA, TB, ROLE) \
+  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, ROLE>), grid, dim3(NT), 0, s, p)
 
 }  // namespace
 
 int gemm_f32_tiles(int M, int N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
-hipError_t launch_gemm_f32(const GemmParams& pin, bool ta, bool tb, int epi, hipStream_t s) {
+// Instantiated combinations: every NN role, G G^T (NT) and G^T G / X^T X (TN).
+hipError_t launch_gemm_f32(const GemmParams& pin, bool ta, bool tb, int role, hipStream_t s) {
   GemmParams p = pin;
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   dim3 grid(p.tiles_m * p.tiles_n, 1, p.batch * p.nprob);
-  if (ta && tb) return launch_t<true, true>(p, epi, grid, s);
-  if (ta) return launch_t<true, false>(p, epi, grid, s);
-  if (tb) return launch_t<false, true>(p, epi, grid, s);
-  return launch_t<false, false>(p, epi, grid, s);
+  if (!ta && !tb) {
+    switch (role) {
+      case ROLE_POWER: PMX_GEMM_LAUNCH(false, false, ROLE_POWER); break;
+      case ROLE_UPDATE: PMX_GEMM_LAUNCH(false, false, ROLE_UPDATE); break;
+      case ROLE_RESID: PMX_GEMM_LAUNCH(false, false, ROLE_RESID); break;
+      case ROLE_APPLY: PMX_GEMM_LAUNCH(false, false, ROLE_APPLY); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (!ta && tb) {
+    if (role != ROLE_STATS) return hipErrorInvalidValue;
+    PMX_GEMM_LAUNCH(false, true, ROLE_STATS);
+  } else if (ta && !tb) {
+    switch (role) {
+      case ROLE_STATS: PMX_GEMM_LAUNCH(true, false, ROLE_STATS); break;
+      case ROLE_RESID: PMX_GEMM_LAUNCH(true, false, ROLE_RESID); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace pmx

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/pmx.h"
@@ -37,6 +38,7 @@ struct IterCfg {
   int max_iter;
   int accelerate;
   float lo, hi, tol;
+  float taylor_d;  // c_d, the coefficient used when accelerate == 0
   uint32_t seed_lo, seed_hi;
   pmx_matfn_info* info;  // may be null
 };
@@ -72,6 +74,10 @@ __device__ __forceinline__ void decide(Ctrl& c, const IterCfg& cfg, pmx_matfn_in
   if (info && k < PMX_TRACE_LEN) info->rtrace[s][k] = (float)r;
   c.r_prev = r;
   c.fro = sqrt(fro2);
+  if (st == PMX_RUNNING && !cfg.accelerate) {
+    c.alpha = cfg.taylor_d;
+    if (info && k < PMX_TRACE_LEN) info->alpha[s][k] = cfg.taylor_d;
+  }
   if (st != PMX_RUNNING) {
     if (severity(st) > severity(c.status_all)) c.status_all = st;
     if (info) {
@@ -134,17 +140,96 @@ __device__ __forceinline__ bool last_block_sum(double my_partial, double* partia
 }
 
 // ---------------------------------------------------------------------------
+// Gaussian sketch (shared by every kernel that generates it).
+//
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
+// multiplies, high halves mixed with the other counter words and the key,
+// key advanced by two Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// Where and which sketch to generate: S (n x p) of matrix b, stage, iteration
+// k goes to columns [0, p) of the Krylov buffer (row stride kld).
+struct SketchJob {
+  float* kbuf;      // null: no sketch to generate
+  int64_t kld, kstride;
+  int n, p, k, stage;
+  uint32_t seed_lo, seed_hi;
+};
+
+// Philox calls [q0, q1) of the sketch of matrix b: element e = i p + j takes
+// word e % 4 of the call with counter (e / 4, k, stage, b); uniforms
+// ((x >> 8) + 1/2) 2^-24, Box-Muller on the word pairs (0,1) and (2,3),
+// evaluated in fp64 and rounded to fp32.  One call per thread.
+__device__ __forceinline__ void sketch_calls(const SketchJob& sj, int b, int64_t q0, int64_t q1) {
+  const int64_t total = (int64_t)sj.n * sj.p;
+  float* kb = sj.kbuf + (int64_t)b * sj.kstride;
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += blockDim.x) {
+    uint32_t c[4] = {(uint32_t)q, (uint32_t)sj.k, (uint32_t)sj.stage, (uint32_t)b};
+    philox4x32_10(c, sj.seed_lo, sj.seed_hi);
+    double u[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) u[w] = ((double)(c[w] >> 8) + 0.5) * 0x1p-24;
+    const double r01 = sqrt(-2.0 * log(u[0])), r23 = sqrt(-2.0 * log(u[2]));
+    double s01, c01, s23, c23;
+    sincos(2.0 * M_PI * u[1], &s01, &c01);
+    sincos(2.0 * M_PI * u[3], &s23, &c23);
+    const double z[4] = {r01 * c01, r01 * s01, r23 * c23, r23 * s23};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int64_t e = q * 4 + w;
+      if (e < total) {
+        const int i = (int)(e / sj.p), j = (int)(e - (int64_t)i * sj.p);
+        kb[(int64_t)i * sj.kld + j] = (float)z[w];
+      }
+    }
+  }
+}
+
+// This block's share [q0, q1) of the ceil(n p / 4) Philox calls when `nblocks`
+// blocks split the sketch of one matrix.
+__device__ __forceinline__ void sketch_share(const SketchJob& sj, int b, int blk, int nblocks) {
+  if (!sj.kbuf) return;
+  const int64_t calls = ((int64_t)sj.n * sj.p + 3) / 4;
+  const int64_t per = (calls + nblocks - 1) / nblocks;
+  const int64_t q0 = (int64_t)blk * per;
+  const int64_t q1 = q0 + per < calls ? q0 + per : calls;
+  if (q0 < q1) sketch_calls(sj, b, q0, q1);
+}
+
+// ---------------------------------------------------------------------------
 // GEMM parameter block (fp32 MFMA kernel, row-major, optional transposes).
-enum Epi : int {
-  EPI_STORE = 0,  // C = acc
-  EPI_RESID = 1,  // C = I - acc, then ||C||_F^2 -> convergence decision
-  EPI_EMA = 2,    // C = beta C + (1 - beta) acc + eps I (in place)
+// The role selects the epilogue and gives every use its own kernel symbol:
+enum Role : int {
+  ROLE_POWER = 0,   // R^2 = R R                       (plain store)
+  ROLE_UPDATE = 1,  // Y g, g Z, X g with g formed on the fly (plain store)
+  ROLE_RESID = 2,   // R = I - Z Y or I - X^T X, ||R||_F, convergence decision
+  ROLE_STATS = 3,   // C = beta C + (1 - beta) G G^T (or G^T G) + eps I, in place
+  ROLE_APPLY = 4,   // L^{-1/4} G and (L^{-1/4} G) R^{-1/4}   (plain store)
 };
 
 struct GemmOperand {
   const float* ptr;
   int64_t ld;
-  int64_t stride;  // batch stride in elements
+  int64_t stride;    // batch stride in elements
+  // polynomial operand g = c0 I + c1 R + alpha R2 (d = 2) or c0 I + alpha R
+  // (d = 1), formed while loading: ptr = R, ptr2 = R2 (same ld / stride)
+  const float* ptr2;
+  int poly;
 };
 
 struct GemmProblem {
@@ -162,16 +247,21 @@ struct GemmParams {
   int tiles_m, tiles_n;
   int vec;         // 1: every operand allows 16-byte loads
   Ctrl* ctrl;      // per-matrix control blocks; null = unconditional
-  // EPI_EMA
+  // polynomial operands
+  int degree;
+  float c0, c1;
+  // ROLE_STATS
   float beta, omb, eps;
-  // EPI_RESID
+  // ROLE_RESID
   double* partials;      // [batch][tiles]
   int64_t partial_stride;
   int products;          // dense products to add to ctrl.gemms on completion
   int count_update;      // 1: this residual ends an update (iter += 1)
   IterCfg cfg;
+  SketchJob sketch;      // sketch of the next iteration, generated on the side
 };
 
-hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int epi, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s);
+int gemm_f32_tiles(int M, int N);
 
 }  // namespace pmx

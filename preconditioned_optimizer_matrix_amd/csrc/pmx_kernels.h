@@ -43,6 +43,7 @@ struct StageInitParams {
   double* partials;
   int64_t partial_stride;
   IterCfg cfg;
+  SketchJob sketch;      // S_0 of this stage
 };
 
 struct PolarInitParams {
@@ -54,27 +55,11 @@ struct PolarInitParams {
   Ctrl* ctrl;
 };
 
-struct SketchParams {
-  float* kbuf;           // Krylov buffer: n x (2d+2) p, columns [0, p) = S
-  int64_t kld, kstride;
-  int n, p, k, stage;
-  uint32_t seed_lo, seed_hi;
-  Ctrl* ctrl;
-};
-
 struct SkinnyJob {
   const float* mat;
   int64_t mat_ld, mat_stride;
   int in_col, out_col;
   int pow;               // output scaled by ||R||_F^-pow
-};
-
-struct SkinnyParams {
-  SkinnyJob job[2];
-  float* kbuf;
-  int64_t kld, kstride;
-  int n, q;
-  Ctrl* ctrl;
 };
 
 // Coefficient vectors of r(xi; alpha) = sum_j (a0_j + alpha a1_j + alpha^2 a2_j) xi^j.
@@ -83,10 +68,15 @@ struct AlphaCoef {
   double taylor_d;
 };
 
-struct AlphaParams {
-  const float* kbuf;
+struct SkinnyParams {
+  SkinnyJob job[2];
+  float* kbuf;
   int64_t kld, kstride;
+  int n, q;
   Ctrl* ctrl;
+  // last pass only: Gram shares (16 doubles per block) and the alpha solve
+  double* gram_partials;
+  int64_t gram_stride;
   IterCfg cfg;
   AlphaCoef coef;
 };
@@ -129,13 +119,11 @@ hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_
                             int64_t pstride, pmx_matfn_info* info, hipStream_t s);
 hipError_t launch_sqrt_stage_init(const StageInitParams& p, int batch, hipStream_t s);
 hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hipStream_t s);
-hipError_t launch_sketch(const SketchParams& p, int batch, hipStream_t s);
-hipError_t launch_skinny(const SkinnyParams& p, int njobs, int batch, hipStream_t s);
-hipError_t launch_alpha(const AlphaParams& p, int batch, hipStream_t s);
+hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s);
+int skinny_blocks(int n, int q);
 hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s);
 hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t s);
 hipError_t launch_polar_finish(const PolarFinishParams& p, bool bf16, int batch, hipStream_t s);
 
-int gemm_f32_tiles(int M, int N);
 
 }  // namespace pmx

@@ -1,7 +1,7 @@
 // Bandwidth- and latency-bound kernels of the PRISM iteration on gfx950:
-// control reset, input scaling, stage set-up, the Gaussian sketch, the skinny
-// Krylov products R^j S, the on-device alpha fit, the polynomial combination
-// g = f_{d-1}(R) + alpha R^d, and the scaled outputs.
+// control reset, input scaling, stage set-up, the skinny Krylov products
+// R^j S with the fused Gram / alpha fit, the explicit polynomial g for the
+// first update, and the scaled outputs.
 #include <math.h>
 
 #include "pmx_kernels.h"
@@ -84,8 +84,8 @@ __global__ __launch_bounds__(NT) void fro_scale_kernel(const T* __restrict__ X, 
 
 // ---------------------------------------------------------------- stage init
 // Coupled square-root stage set-up: Y_0 = scale * src (src = A for stage 0,
-// the previous stage's Y for stage 1), R_0 = I - Y_0 (Z_0 = I), and the
-// convergence decision on r_0.
+// the previous stage's Y for stage 1), R_0 = I - Y_0 (Z_0 = I), the
+// convergence decision on r_0, and the first sketch S_0.
 __global__ __launch_bounds__(NT) void sqrt_stage_init_kernel(StageInitParams p) {
   const int b = blockIdx.y;
   Ctrl* cb = p.ctrl + b;
@@ -95,6 +95,7 @@ __global__ __launch_bounds__(NT) void sqrt_stage_init_kernel(StageInitParams p) 
     const int prev = *(const volatile int32_t*)&cb->status_all;
     if (prev == PMX_NONFINITE || prev == PMX_DIVERGED) return;
   }
+  sketch_share(p.sketch, b, blockIdx.x, gridDim.x);
   const int n = p.n;
   double scale;
   const float* src;
@@ -156,65 +157,141 @@ __global__ __launch_bounds__(NT) void polar_init_kernel(PolarInitParams p) {
   }
 }
 
-// ---------------------------------------------------------------- sketch
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
-// multiplies, high halves mixed with the other counter words and the key,
-// key advanced by two Weyl constants between rounds.
-__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
+// ---------------------------------------------------------------- alpha fit
+// Real roots of a x^2 + b x + c inside (lo, hi).
+__device__ int quad_roots_in(double a, double b, double c, double lo, double hi, double* out) {
+  int n = 0;
+  const double scale = fmax(fabs(a), fmax(fabs(b), fabs(c)));
+  if (scale == 0.0) return 0;
+  if (fabs(a) <= 1e-14 * scale) {
+    if (b != 0.0) {
+      const double x = -c / b;
+      if (x > lo && x < hi) out[n++] = x;
     }
-    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
-    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
+    return n;
   }
+  const double disc = b * b - 4.0 * a * c;
+  if (disc < 0.0) return 0;
+  const double sq = sqrt(disc);
+  const double q = -0.5 * (b + (b >= 0.0 ? sq : -sq));
+  const double x1 = q / a;
+  const double x2 = (q != 0.0) ? c / q : x1;
+  if (x1 > lo && x1 < hi) out[n++] = x1;
+  if (x2 > lo && x2 < hi && x2 != x1) out[n++] = x2;
+  return n;
 }
 
-// S (n x p) of matrix b, stage, iteration k: element e = i p + j takes word
-// e % 4 of the Philox call with counter (e / 4, k, stage, b); uniforms
-// ((x >> 8) + 1/2) 2^-24, Box-Muller on the word pairs (0,1) and (2,3),
-// evaluated in fp64 and rounded to fp32.  Written to columns [0, p) of the
-// Krylov buffer.
-__global__ __launch_bounds__(NT) void sketch_kernel(SketchParams p) {
-  const int b = blockIdx.y;
-  if (load_status(p.ctrl + b) != PMX_RUNNING) return;
-  const int64_t total = (int64_t)p.n * p.p;
-  const int64_t calls = (total + 3) / 4;
-  float* kb = p.kbuf + (int64_t)b * p.kstride;
-  for (int64_t q = (int64_t)blockIdx.x * NT + threadIdx.x; q < calls;
-       q += (int64_t)gridDim.x * NT) {
-    uint32_t c[4] = {(uint32_t)q, (uint32_t)p.k, (uint32_t)p.stage, (uint32_t)b};
-    philox4x32_10(c, p.seed_lo, p.seed_hi);
-    double u[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) u[w] = ((double)(c[w] >> 8) + 0.5) * 0x1p-24;
-    double z[4];
-    const double r01 = sqrt(-2.0 * log(u[0])), r23 = sqrt(-2.0 * log(u[2]));
-    double s01, c01, s23, c23;
-    sincos(2.0 * M_PI * u[1], &s01, &c01);
-    sincos(2.0 * M_PI * u[3], &s23, &c23);
-    z[0] = r01 * c01;
-    z[1] = r01 * s01;
-    z[2] = r23 * c23;
-    z[3] = r23 * s23;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int64_t e = q * 4 + w;
-      if (e < total) {
-        const int i = (int)(e / p.p), j = (int)(e - (int64_t)i * p.p);
-        kb[(int64_t)i * p.kld + j] = (float)z[w];
+// argmin over [lo, hi] of phi(a) = w0 + w1 a + w2 a^2 + w3 a^3 + w4 a^4.
+// phi' is a cubic; the roots of phi'' split [lo, hi] into pieces on which
+// phi' is monotone, and every sign change of phi' on a piece is bisected to
+// full double precision.  Candidates are both ends and those critical
+// points; the smallest phi wins, ties to the smaller alpha.
+__device__ double argmin_quartic(const double (&w)[5], double lo, double hi) {
+  auto phi = [&](double a) { return w[0] + a * (w[1] + a * (w[2] + a * (w[3] + a * w[4]))); };
+  auto dphi = [&](double a) { return w[1] + a * (2.0 * w[2] + a * (3.0 * w[3] + a * 4.0 * w[4])); };
+  double brk[4];
+  int nb = 0;
+  brk[nb++] = lo;
+  double qr[2];
+  const int nq = quad_roots_in(12.0 * w[4], 6.0 * w[3], 2.0 * w[2], lo, hi, qr);
+  if (nq == 2 && qr[1] < qr[0]) {
+    const double t = qr[0];
+    qr[0] = qr[1];
+    qr[1] = t;
+  }
+  for (int i = 0; i < nq; ++i) brk[nb++] = qr[i];
+  brk[nb++] = hi;
+  double cand[6];
+  int nc = 0;
+  cand[nc++] = lo;
+  for (int i = 0; i + 1 < nb; ++i) {
+    double x0 = brk[i], x1 = brk[i + 1];
+    double f0 = dphi(x0);
+    const double f1 = dphi(x1);
+    if (f0 == 0.0) {
+      if (x0 > lo && x0 < hi) cand[nc++] = x0;
+      continue;
+    }
+    if ((f0 < 0.0) == (f1 < 0.0) || f1 == 0.0) continue;
+    for (int it = 0; it < 200; ++it) {
+      const double xm = 0.5 * (x0 + x1);
+      if (xm <= x0 || xm >= x1) break;
+      const double fm = dphi(xm);
+      if (fm == 0.0) {
+        x0 = x1 = xm;
+        break;
+      }
+      if ((fm < 0.0) == (f0 < 0.0)) {
+        x0 = xm;
+        f0 = fm;
+      } else {
+        x1 = xm;
       }
     }
+    const double x = 0.5 * (x0 + x1);
+    if (x > lo && x < hi) cand[nc++] = x;
   }
+  cand[nc++] = hi;
+  for (int i = 1; i < nc; ++i)
+    for (int j = i; j > 0 && cand[j] < cand[j - 1]; --j) {
+      const double t = cand[j];
+      cand[j] = cand[j - 1];
+      cand[j - 1] = t;
+    }
+  double best = cand[0], bv = phi(cand[0]);
+  for (int i = 1; i < nc; ++i) {
+    const double v = phi(cand[i]);
+    if (v < bv) {
+      bv = v;
+      best = cand[i];
+    }
+  }
+  return best;
 }
 
+// alpha from the Gram G (upper triangle, row-major, of the J x J Gram of the
+// scaled Krylov blocks K~_j = (R/s)^j S, j = 1..J, J = 2d + 1): the
+// coefficient vectors of r(xi; alpha) are rescaled by s^j to undo the Krylov
+// scaling, the quartic phi_S(alpha) = c(alpha)^T M c(alpha) is formed, and its
+// argmin on [lo, hi] is taken.  A degenerate or non-finite quartic gives c_d.
+__device__ double alpha_from_gram(const double* G, int J, double s, const AlphaCoef& co,
+                                  double lo, double hi) {
+  double av[3][5];
+  double sp = 1.0;
+  for (int j = 1; j <= 5; ++j) {
+    sp *= s;
+    for (int i = 0; i < 3; ++i) av[i][j - 1] = (j <= J) ? co.a[i][j] * sp : 0.0;
+  }
+  auto gram = [&](int x, int y) {
+    if (x > y) {
+      const int t = x;
+      x = y;
+      y = t;
+    }
+    return G[x * J - x * (x - 1) / 2 + (y - x)];
+  };
+  auto q = [&](int i1, int i2) {
+    double t = 0.0;
+    for (int x = 0; x < J; ++x)
+      for (int y = 0; y < J; ++y) t += av[i1][x] * gram(x, y) * av[i2][y];
+    return t;
+  };
+  double w[5];
+  w[0] = q(0, 0);
+  w[1] = q(0, 1) + q(1, 0);
+  w[2] = q(1, 1) + q(0, 2) + q(2, 0);
+  w[3] = q(1, 2) + q(2, 1);
+  w[4] = q(2, 2);
+  bool ok = true;
+  double mx = 0.0;
+  for (int e = 0; e < 5; ++e) ok = ok && isfinite(w[e]);
+  for (int e = 1; e < 5; ++e) mx = fmax(mx, fabs(w[e]));
+  if (!ok || mx <= 1e-300) return fmin(fmax(co.taylor_d, lo), hi);
+  if (hi <= lo) return lo;
+  return argmin_quartic(w, lo, hi);
+}
+
+// ---------------------------------------------------------------- skinny products
 // Recursive-halving reduction over a 64-lane wave of CNT values per lane:
 // at the step with offset O the lanes with bit O set keep the upper half of
 // their remaining values and add the partner's copy of it.  With CNT = 64,
@@ -234,20 +311,22 @@ __device__ __forceinline__ void halve_reduce(float* acc, int lane) {
   }
 }
 
-// ---------------------------------------------------------------- skinny products
-// out[:, oc : oc + q] = fro^-pow * Mat * in[:, ic : ic + q] for an n x n Mat
+// out[:, oc : oc + q] = ||R||_F^-pow * Mat * in[:, ic : ic + q] for an n x n Mat
 // and an n x q block of the Krylov buffer (q <= Q).  HBM-bound on Mat: each
 // block streams 4 * (64 / Q) rows of Mat once; In is staged through LDS in
 // chunks of 256 rows and shared by those rows.  Each lane accumulates
 // (64 / Q) x Q partial sums; a recursive-halving exchange over the wave
 // leaves lane l with the complete sum for (row l / Q, column l % Q).
-template <int Q>
+// GRAM (last Krylov pass): every block also adds its rows' share of the
+// J x J Gram of K_1..K_J in fp64; the last block to arrive reduces the
+// shares in block order and solves for alpha.
+template <int Q, bool GRAM>
 __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   constexpr int RW = 64 / Q;       // rows per wave
   constexpr int RB = 4 * RW;       // rows per block
   constexpr int LD = Q + 4;
   const int b = blockIdx.z;
-  const Ctrl* cb = p.ctrl + b;
+  Ctrl* cb = p.ctrl + b;
   if (load_status(cb) != PMX_RUNNING) return;
   const SkinnyJob& job = p.job[blockIdx.y];
   const int n = p.n;
@@ -301,189 +380,60 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   // lane l now holds value index l = rr * Q + c
   const int rr = lane / Q, c = lane - rr * Q;
   const int row = row0 + rr;
-  if (row < n && c < p.q) kb[(int64_t)row * p.kld + job.out_col + c] = acc[0] * scale;
-}
+  const bool valid = row < n && c < p.q;
+  const float val = acc[0] * scale;
+  if (valid) kb[(int64_t)row * p.kld + job.out_col + c] = val;
 
-// ---------------------------------------------------------------- alpha fit
-// Real roots of a x^2 + b x + c inside (lo, hi), appended to out (ascending
-// order not required).
-__device__ int quad_roots_in(double a, double b, double c, double lo, double hi, double* out) {
-  int n = 0;
-  const double scale = fmax(fabs(a), fmax(fabs(b), fabs(c)));
-  if (scale == 0.0) return 0;
-  if (fabs(a) <= 1e-14 * scale) {
-    if (b != 0.0) {
-      const double x = -c / b;
-      if (x > lo && x < hi) out[n++] = x;
+  if constexpr (GRAM) {
+    const int J = 2 * p.cfg.degree + 1;
+    const int pp = p.cfg.p;
+    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    if (valid) {
+      for (int j = 1; j < J; ++j) v[j - 1] = (double)kb[(int64_t)row * p.kld + j * pp + c];
+      v[J - 1] = (double)val;
     }
-    return n;
-  }
-  const double disc = b * b - 4.0 * a * c;
-  if (disc < 0.0) return 0;
-  const double sq = sqrt(disc);
-  const double q = -0.5 * (b + (b >= 0.0 ? sq : -sq));
-  const double x1 = q / a;
-  const double x2 = (q != 0.0) ? c / q : x1;
-  if (x1 > lo && x1 < hi) out[n++] = x1;
-  if (x2 > lo && x2 < hi && x2 != x1) out[n++] = x2;
-  return n;
-}
-
-// argmin over [lo, hi] of phi(a) = w0 + w1 a + w2 a^2 + w3 a^3 + w4 a^4.
-// phi' is a cubic; the roots of phi'' split [lo, hi] into pieces on which
-// phi' is monotone, and every sign change of phi' on a piece is bisected to
-// full double precision.  Candidates are both ends and those critical
-// points; the smallest phi wins, ties to the smaller alpha.
-__device__ double argmin_quartic(const double (&w)[5], double lo, double hi) {
-  auto phi = [&](double a) { return w[0] + a * (w[1] + a * (w[2] + a * (w[3] + a * w[4]))); };
-  auto dphi = [&](double a) { return w[1] + a * (2.0 * w[2] + a * (3.0 * w[3] + a * 4.0 * w[4])); };
-  double brk[4];
-  int nb = 0;
-  brk[nb++] = lo;
-  double qr[2];
-  const int nq = quad_roots_in(12.0 * w[4], 6.0 * w[3], 2.0 * w[2], lo, hi, qr);
-  if (nq == 2 && qr[1] < qr[0]) {
-    const double t = qr[0];
-    qr[0] = qr[1];
-    qr[1] = t;
-  }
-  for (int i = 0; i < nq; ++i) brk[nb++] = qr[i];
-  brk[nb++] = hi;
-  double cand[6];
-  int nc = 0;
-  cand[nc++] = lo;
-  for (int i = 0; i + 1 < nb; ++i) {
-    double x0 = brk[i], x1 = brk[i + 1];
-    double f0 = dphi(x0), f1 = dphi(x1);
-    if (f0 == 0.0) {
-      if (x0 > lo && x0 < hi) cand[nc++] = x0;
-      continue;
-    }
-    if ((f0 < 0.0) == (f1 < 0.0) || f1 == 0.0) continue;
-    for (int it = 0; it < 200; ++it) {
-      const double xm = 0.5 * (x0 + x1);
-      if (xm <= x0 || xm >= x1) break;
-      const double fm = dphi(xm);
-      if (fm == 0.0) {
-        x0 = x1 = xm;
-        break;
+    __shared__ double red[NT / 64];
+    __shared__ double gsum[15];
+    int t = 0;
+    for (int a = 0; a < J; ++a)
+      for (int bb = a; bb < J; ++bb, ++t) {
+        const double s = block_sum<NT / 64>(v[a] * v[bb], red);
+        if (threadIdx.x == 0) gsum[t] = s;
       }
-      if ((fm < 0.0) == (f0 < 0.0)) {
-        x0 = xm;
-        f0 = fm;
-      } else {
-        x1 = xm;
-      }
-    }
-    const double x = 0.5 * (x0 + x1);
-    if (x > lo && x < hi) cand[nc++] = x;
-  }
-  cand[nc++] = hi;
-  // ascending order for the tie rule
-  for (int i = 1; i < nc; ++i)
-    for (int j = i; j > 0 && cand[j] < cand[j - 1]; --j) {
-      const double t = cand[j];
-      cand[j] = cand[j - 1];
-      cand[j - 1] = t;
-    }
-  double best = cand[0], bv = phi(cand[0]);
-  for (int i = 1; i < nc; ++i) {
-    const double v = phi(cand[i]);
-    if (v < bv) {
-      bv = v;
-      best = cand[i];
-    }
-  }
-  return best;
-}
-
-// One block per matrix: Gram of the scaled Krylov blocks K~_j = (R/s)^j S
-// (j = 1..2d+1, fp64 accumulation), the quartic in alpha (the coefficient
-// vectors rescaled by s^j undo the Krylov scaling), and its argmin on
-// [lo, hi].  alpha_k lands in the control block; the host never waits.
-__global__ __launch_bounds__(NT) void alpha_kernel(AlphaParams p) {
-  const int b = blockIdx.x;
-  Ctrl* cb = p.ctrl + b;
-  if (load_status(cb) != PMX_RUNNING) return;
-  const int J = 2 * p.cfg.degree + 1;
-  const double cd = p.coef.taylor_d;
-  double alpha = cd;
-  __shared__ double red[NT / 64];
-  if (p.cfg.accelerate) {
-    const float* kb = p.kbuf + (int64_t)b * p.kstride;
-    const int n = p.cfg.n, pp = p.cfg.p;
-    double g[15];
-#pragma unroll
-    for (int i = 0; i < 15; ++i) g[i] = 0.0;
-    for (int i = threadIdx.x; i < n; i += NT) {
-      const float* row = kb + (int64_t)i * p.kld;
-      for (int c = 0; c < pp; ++c) {
-        double v[5];
-#pragma unroll
-        for (int j = 0; j < 5; ++j) v[j] = (j < J) ? (double)row[(j + 1) * pp + c] : 0.0;
-        int t = 0;
-#pragma unroll
-        for (int a = 0; a < 5; ++a)
-#pragma unroll
-          for (int bb = a; bb < 5; ++bb) g[t++] += v[a] * v[bb];
-      }
-    }
-    double G[15];
-    for (int i = 0; i < 15; ++i) G[i] = block_sum<NT / 64>(g[i], red);
+    const int ng = t;
+    __shared__ int is_last;
+    double* part = p.gram_partials + (int64_t)b * p.gram_stride;
     if (threadIdx.x == 0) {
-      // scaled coefficient vectors: a_i[j] s^j, j = 1..J
-      const double s = cb->fro;
-      double av[3][5];
-      double sp = 1.0;
-      for (int j = 1; j <= J; ++j) {
-        sp *= s;
-        for (int i = 0; i < 3; ++i) av[i][j - 1] = p.coef.a[i][j] * sp;
-      }
-      for (int j = J; j < 5; ++j)
-        for (int i = 0; i < 3; ++i) av[i][j] = 0.0;
-      auto gram = [&](int x, int y) {
-        if (x > y) {
-          const int t = x;
-          x = y;
-          y = t;
-        }
-        // index of (x, y), x <= y, in the row-major upper triangle of 5 x 5
-        const int idx = x * 5 - x * (x - 1) / 2 + (y - x);
-        return G[idx];
-      };
-      auto q = [&](int i1, int i2) {
-        double t = 0.0;
-        for (int x = 0; x < J; ++x)
-          for (int y = 0; y < J; ++y) t += av[i1][x] * gram(x, y) * av[i2][y];
-        return t;
-      };
-      double w[5];
-      w[0] = q(0, 0);
-      w[1] = q(0, 1) + q(1, 0);
-      w[2] = q(1, 1) + q(0, 2) + q(2, 0);
-      w[3] = q(1, 2) + q(2, 1);
-      w[4] = q(2, 2);
-      bool ok = true;
-      double mx = 0.0;
-      for (int e = 0; e < 5; ++e) ok = ok && isfinite(w[e]);
-      for (int e = 1; e < 5; ++e) mx = fmax(mx, fabs(w[e]));
-      const double lo = p.cfg.lo, hi = p.cfg.hi;
-      if (!ok || mx <= 1e-300) alpha = fmin(fmax(cd, lo), hi);
-      else if (hi <= lo) alpha = lo;
-      else alpha = argmin_quartic(w, lo, hi);
+      for (int i = 0; i < ng; ++i) part[(int64_t)blockIdx.x * 16 + i] = gsum[i];
+      __threadfence();
+      const uint32_t prev = atomicAdd(&cb->counter, 1u);
+      is_last = (prev == gridDim.x - 1);
     }
-  }
-  if (threadIdx.x == 0) {
-    cb->alpha = alpha;
-    if (p.cfg.accelerate) cb->sketch_products += J;
-    const int k = cb->iter;
-    if (p.cfg.info && k < PMX_TRACE_LEN) p.cfg.info[b].alpha[cb->stage][k] = (float)alpha;
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    if (threadIdx.x < ng) {
+      double s = 0.0;
+      for (int i = 0; i < (int)gridDim.x; ++i)
+        s += __hip_atomic_load(&part[(int64_t)i * 16 + threadIdx.x], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      gsum[threadIdx.x] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const double alpha = alpha_from_gram(gsum, J, fro, p.coef, p.cfg.lo, p.cfg.hi);
+      cb->alpha = alpha;
+      cb->sketch_products += J;
+      const int k = cb->iter;
+      if (p.cfg.info && k < PMX_TRACE_LEN) p.cfg.info[b].alpha[cb->stage][k] = (float)alpha;
+      cb->counter = 0u;
+    }
   }
 }
 
 // ---------------------------------------------------------------- polynomial
-// g = c_0 I + c_1 R + ... + c_{d-1} R^{d-1} + alpha R^d for d in {1, 2}
-// (R^2 given); dst may alias r2.
+// g = c_0 I + c_1 R + alpha R^2 (d = 2) or c_0 I + alpha R (d = 1), written
+// explicitly: it is Z_1 of the coupled iteration (Z_0 = I).
 __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   const int b = blockIdx.y;
   const Ctrl* cb = p.ctrl + b;
@@ -531,11 +481,11 @@ __global__ __launch_bounds__(NT) void root_finish_kernel(RootFinishParams p) {
       zx = NAN;
       ya = NAN;
     } else {
-      zx = (it == 0) ? (r == col ? 1.f : 0.f) : Z[e];
-      ya = Y[e];
+      zx = ((it == 0) ? (r == col ? 1.f : 0.f) : Z[e]) * sx;
+      ya = Y[e] * sa;
     }
-    X[(int64_t)r * p.ldx + col] = bad ? zx : zx * sx;
-    if (XA) XA[(int64_t)r * p.ldaux + col] = bad ? ya : ya * sa;
+    X[(int64_t)r * p.ldx + col] = zx;
+    if (XA) XA[(int64_t)r * p.ldaux + col] = ya;
   }
 }
 
@@ -597,33 +547,26 @@ hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hip
   return hipGetLastError();
 }
 
-hipError_t launch_sketch(const SketchParams& p, int batch, hipStream_t s) {
-  const int64_t calls = ((int64_t)p.n * p.p + 3) / 4;
-  int g = (int)((calls + NT - 1) / NT);
-  if (g > 1024) g = 1024;
-  if (g < 1) g = 1;
-  hipLaunchKernelGGL(sketch_kernel, dim3(g, batch), dim3(NT), 0, s, p);
-  return hipGetLastError();
+int skinny_blocks(int n, int q) {
+  const int rb = q <= 8 ? 32 : (q <= 16 ? 16 : 8);
+  return (n + rb - 1) / rb;
 }
 
-hipError_t launch_skinny(const SkinnyParams& p, int njobs, int batch, hipStream_t s) {
+hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
+  dim3 grid(skinny_blocks(p.n, p.q), njobs, batch);
+  if (gram && njobs != 1) return hipErrorInvalidValue;
   if (p.q <= 8) {
-    dim3 grid((p.n + 31) / 32, njobs, batch);
-    hipLaunchKernelGGL(skinny_kernel<8>, grid, dim3(NT), 0, s, p);
+    if (gram) hipLaunchKernelGGL((skinny_kernel<8, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((skinny_kernel<8, false>), grid, dim3(NT), 0, s, p);
   } else if (p.q <= 16) {
-    dim3 grid((p.n + 15) / 16, njobs, batch);
-    hipLaunchKernelGGL(skinny_kernel<16>, grid, dim3(NT), 0, s, p);
+    if (gram) hipLaunchKernelGGL((skinny_kernel<16, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((skinny_kernel<16, false>), grid, dim3(NT), 0, s, p);
   } else if (p.q <= 32) {
-    dim3 grid((p.n + 7) / 8, njobs, batch);
-    hipLaunchKernelGGL(skinny_kernel<32>, grid, dim3(NT), 0, s, p);
+    if (gram) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((skinny_kernel<32, false>), grid, dim3(NT), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_alpha(const AlphaParams& p, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(alpha_kernel, dim3(batch), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -31,7 +31,12 @@ EXPORTS = [
     "pmx_matfn_inv_root", "pmx_matfn_inv_root_batched",
     "pmx_matfn_polar", "pmx_matfn_polar_batched",
     "pmx_precond_apply", "pmx_precond_apply_batched",
+    "pmx_trace_enable", "pmx_trace_collect",
 ]
+
+# kernel classes of the launch trace (pmx_kernel_class)
+KERNEL_CLASSES = ["gemm_power", "gemm_update", "gemm_resid", "gemm_stats", "gemm_apply",
+                  "skinny", "skinny_alpha", "other"]
 
 
 class Opts(ctypes.Structure):
@@ -93,6 +98,9 @@ def _load():
         "pmx_precond_apply_batched": (_i32, [_vp, _vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32,
                                              _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32, _vp,
                                              _sz, _vp]),
+        "pmx_trace_enable": (_i32, [_vp, _i32]),
+        "pmx_trace_collect": (_i32, [_vp, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -289,3 +297,18 @@ def precond_apply(Linv, G, Rinv, out=None, ws=None):
         ldr, sr, _ptr(P), ldp, sp, batch, _ptr(ws), ws.numel(), _stream(G)),
         "precond_apply")
     return P
+
+
+def trace_enable(enable=True, device=None):
+    """Bracket every launch of this device's handle with HIP events."""
+    check(lib.pmx_trace_enable(handle(device), 1 if enable else 0), "trace_enable")
+
+
+def trace_collect(device=None):
+    """{kernel class: (total ms, launches)} of the launches since trace_enable
+    or the previous collect (waits for the recorded events)."""
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    check(lib.pmx_trace_collect(handle(device), ms, cnt), "trace_collect")
+    return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
