@@ -85,7 +85,7 @@ typedef struct {
   int32_t struct_version; /* must be PMX_OPTS_VERSION */
   int32_t degree;         /* d in {1, 2}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2 */
   int32_t sketch_p;       /* Gaussian sketch width p, 1..PMX_MAX_SKETCH; default 8 */
-  int32_t max_iter;       /* updates per stage, 1..1000; default 40 */
+  int32_t max_iter;       /* updates per stage, 1..1000; default 30 */
   int32_t accelerate;     /* 1: fitted alpha (PRISM); 0: alpha = Taylor c_d; default 1 */
   float alpha_lo;         /* alpha interval; NaN selects the default:       */
   float alpha_hi;         /*   d = 1: [1/2, 1], d = 2: [3/8, 1.47]          */

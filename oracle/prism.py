@@ -203,7 +203,7 @@ def _alpha_for(R, d, lo, hi, accelerate, sketch_fn, stage, k, trace):
     return fit_alpha(krylov_gram(R, S, d), d, lo, hi)
 
 
-def coupled_sqrt_stage(Y0, d=2, lo=None, hi=None, tol=1e-6, max_iter=40,
+def coupled_sqrt_stage(Y0, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
                        sketch_fn=None, stage=0, accelerate=True):
     """One coupled Newton-Schulz square-root stage from Y_0 (Z_0 = I).
     Y_0 must have its spectrum in (0, 1].  Returns (Y, Z, StageTrace)
@@ -256,7 +256,7 @@ def exact_sketch_fn():
     return lambda stage, k, n: np.eye(n)
 
 
-def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=40,
+def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
              sketch_fn=None, accelerate=True):
     """PRISM A^{-1/p} (p in {2, 4}) with the auxiliary A^{1/p}.
     Scaling c = ||A||_F, stage 1 on A / c; for p = 4 stage 2 on stage 1's Y.
@@ -286,7 +286,7 @@ def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=40,
     return Z2 * c ** -0.25, Y2 * c ** 0.25, dict(status=status, stages=stages, c=c)
 
 
-def polar(G, d=2, lo=None, hi=None, tol=1e-6, max_iter=40, sketch_fn=None,
+def polar(G, d=2, lo=None, hi=None, tol=1e-6, max_iter=30, sketch_fn=None,
           accelerate=True):
     """PRISM polar factor of G (m x n).  Wide inputs are handled through G^T.
     R_k = I - X_k^T X_k, X_{k+1} = X_k g.  Returns (U, info)."""

@@ -3,6 +3,7 @@
 // in full on the caller's stream; iteration kernels skip themselves on the
 // device once their matrix has finished, so no call waits for the GPU.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -14,6 +15,9 @@
 struct pmx_context {
   int device;
   int num_cu;
+  int gemm_blocks_per_cu;  // persistent GEMM grid: blocks per CU (0: one block per tile)
+  int gemm_cfg;            // forced tile configuration (-1: by shape)
+  int gemm_map;            // tile order mode
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -249,9 +253,13 @@ T* at(void* ws, size_t off) {
 
 bool ptr_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-GemmParams gemm_base(int M, int N, int K, int batch) {
+GemmParams gemm_base(const pmx_context* h, int M, int N, int K, int batch) {
   GemmParams g;
   memset(&g, 0, sizeof(g));
+  g.max_blocks = h->gemm_blocks_per_cu > 0 ? h->num_cu * h->gemm_blocks_per_cu : 0;
+  g.cfg_id = h->gemm_cfg;
+  g.map_mode = h->gemm_map;
+  g.num_cu = h->num_cu;
   g.nprob = 1;
   g.batch = batch;
   g.M = M;
@@ -296,21 +304,26 @@ SketchJob make_sketch(const IterLayout& L, void* ws, const IterCfg& cfg, int n, 
 hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
                                    const pmx_matfn_opts& o, const IterCfg& cfg,
                                    const AlphaCoef& coef, int n, int batch, float* R,
-                                   float* R2) {
+                                   float* R2, bool bf16_power = false) {
   Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
   float* kbuf = at<float>(ws, L.kbuf);
   const int d = o.degree, pp = o.sketch_p;
   hipError_t e;
   if (d == 2) {
-    GemmParams g = gemm_base(n, n, n, batch);
+    GemmParams g = gemm_base(q.h, n, n, n, batch);
     g.prob[0].a = {R, n, L.buf_stride, nullptr, 0};
     g.prob[0].b = {R, n, L.buf_stride, nullptr, 0};
     g.prob[0].c = R2;
     g.prob[0].ldc = n;
     g.prob[0].stride_c = L.buf_stride;
     g.ctrl = ctrl;
-    set_vec(g);
-    e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
+    if (bf16_power) {
+      g.vec = (n % 4 == 0 && L.buf_stride % 4 == 0) ? 1 : 0;
+      e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_bf16(g, ROLE_POWER, q.s); });
+    } else {
+      set_vec(g);
+      e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
+    }
     if (e != hipSuccess) return e;
   }
   if (!o.accelerate) return hipSuccess;
@@ -386,7 +399,7 @@ pmx_status pmx_matfn_opts_default(pmx_matfn_opts* o) {
   o->struct_version = PMX_OPTS_VERSION;
   o->degree = 2;
   o->sketch_p = 8;
-  o->max_iter = 40;
+  o->max_iter = 30;
   o->accelerate = 1;
   o->alpha_lo = NAN;
   o->alpha_hi = NAN;
@@ -408,6 +421,13 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (!c) return PMX_ERR_HIP;
   c->device = device;
   c->num_cu = prop.multiProcessorCount;
+  // tuning knobs for experiments (environment, read once per handle)
+  c->gemm_blocks_per_cu = 0;
+  c->gemm_cfg = -1;
+  c->gemm_map = 2;
+  if (const char* e = getenv("PMX_GEMM_BLOCKS_PER_CU")) c->gemm_blocks_per_cu = atoi(e);
+  if (const char* e = getenv("PMX_GEMM_CFG")) c->gemm_cfg = atoi(e);
+  if (const char* e = getenv("PMX_GEMM_MAP")) c->gemm_map = atoi(e);
   *handle = c;
   return PMX_OK;
 }
@@ -459,8 +479,14 @@ static size_t polar_ws(int m, int n, int batch, const pmx_matfn_opts& o) {
   const int rows = std::max(m, n), cols = std::min(m, n);
   return iter_layout(rows, cols, batch, o, 2, 2, sizeof(float)).total;
 }
-static size_t apply_ws(int m, int n, int batch) {
-  return align_up(sizeof(float) * (size_t)m * n * batch);
+static size_t apply_ws(int m, int n, int batch, pmx_dtype dt) {
+  // fp32: T = L^{-1/4} G; bf16: G in fp32, T and P in fp32
+  const size_t one = align_up(sizeof(float) * (size_t)m * n * batch);
+  return dt == PMX_BF16 ? 3 * one : one;
+}
+static size_t stats_ws(int m, int n, int batch, pmx_dtype dt) {
+  // bf16 gradients are widened to fp32 once
+  return dt == PMX_BF16 ? align_up(sizeof(float) * (size_t)m * n * batch) : 0;
 }
 
 pmx_status pmx_workspace_size(pmx_handle h, pmx_op op, int m, int n, int batch,
@@ -472,11 +498,11 @@ pmx_status pmx_workspace_size(pmx_handle h, pmx_op op, int m, int n, int batch,
   switch (op) {
     case PMX_OP_STATS:
       if (m < 1 || m > kMaxN) return PMX_ERR_INVALID_VALUE;
-      *bytes = 0;
+      *bytes = stats_ws(m, n, batch, dtype);
       return PMX_OK;
     case PMX_OP_APPLY:
       if (m < 1 || m > kMaxN) return PMX_ERR_INVALID_VALUE;
-      *bytes = apply_ws(m, n, batch);
+      *bytes = apply_ws(m, n, batch, dtype);
       return PMX_OK;
     case PMX_OP_INV_ROOT:
       if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
@@ -503,8 +529,6 @@ pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dty
                                             int ldl, int64_t sl, float* R, int ldr,
                                             int64_t sr, float beta, float eps, int batch,
                                             void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!h || !G || m < 1 || n < 1 || m > kMaxN || n > kMaxN || batch < 1)
     return PMX_ERR_INVALID_VALUE;
   if (!L && !R) return PMX_ERR_INVALID_VALUE;
@@ -514,18 +538,37 @@ pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dty
   if (batch > 1 && sg < (int64_t)(m - 1) * ldg + n && sg != 0) return PMX_ERR_INVALID_VALUE;
   if (L && !batch_layout_ok(m, m, ldl, sl, batch)) return PMX_ERR_INVALID_VALUE;
   if (R && !batch_layout_ok(n, n, ldr, sr, batch)) return PMX_ERR_INVALID_VALUE;
-  if (dtype == PMX_BF16) return PMX_ERR_NOT_SUPPORTED;
-  const Extent eg = extent_of(G, m, n, ldg, sg, batch, 4);
+  const bool bf = dtype == PMX_BF16;
+  const size_t need = stats_ws(m, n, batch, dtype);
+  pmx_status wst = check_ws(ws, ws_bytes, need);
+  if (wst != PMX_OK) return wst;
+  const Extent eg = extent_of(G, m, n, ldg, sg, batch, bf ? 2 : 4);
   const Extent el = extent_of(L, m, m, ldl, sl, batch, 4);
   const Extent er = extent_of(R, n, n, ldr, sr, batch, 4);
-  if (overlap(eg, el) || overlap(eg, er) || overlap(el, er)) return PMX_ERR_ALIAS;
+  Extent ew;
+  ew.lo = (uintptr_t)ws;
+  ew.hi = ew.lo + need;
+  ew.valid = need > 0;
+  if (overlap(eg, el) || overlap(eg, er) || overlap(el, er) || overlap(ew, eg) ||
+      overlap(ew, el) || overlap(ew, er))
+    return PMX_ERR_ALIAS;
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
   Enq q{h, (hipStream_t)stream};
   const float* g = (const float*)G;
+  if (bf) {
+    // widen G to fp32 once (exact); products then run on the fp32 MFMA kernel
+    const int nb = sg == 0 ? 1 : batch;
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+      return launch_convert(G, true, ldg, sg, ws, false, n, (int64_t)m * n, m, n, nb, q.s);
+    }));
+    g = (const float*)ws;
+    ldg = n;
+    sg = sg == 0 ? 0 : (int64_t)m * n;
+  }
   const float omb = 1.f - beta;
   if (L) {
-    GemmParams p = gemm_base(m, m, n, batch);
+    GemmParams p = gemm_base(q.h, m, m, n, batch);
     p.prob[0].a = {g, ldg, sg, nullptr, 0};
     p.prob[0].b = {g, ldg, sg, nullptr, 0};
     p.prob[0].c = L;
@@ -538,7 +581,7 @@ pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dty
     PMX_TRY(q.run(PMX_KC_GEMM_STATS, [&] { return launch_gemm_f32(p, false, true, ROLE_STATS, q.s); }));
   }
   if (R) {
-    GemmParams p = gemm_base(n, n, m, batch);
+    GemmParams p = gemm_base(q.h, n, n, m, batch);
     p.prob[0].a = {g, ldg, sg, nullptr, 0};
     p.prob[0].b = {g, ldg, sg, nullptr, 0};
     p.prob[0].c = R;
@@ -630,7 +673,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
     for (int k = 0; k < o.max_iter; ++k) {
       PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b));
       const int cur = k & 1, nxt = cur ^ 1;
-      GemmParams u = gemm_base(n, n, n, batch);
+      GemmParams u = gemm_base(q.h, n, n, n, batch);
       u.ctrl = ctrl;
       u.degree = d;
       u.c0 = (float)taylor(0);
@@ -669,7 +712,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       }
       set_vec(u);
       PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
-      GemmParams r = gemm_base(n, n, n, batch);
+      GemmParams r = gemm_base(q.h, n, n, n, batch);
       r.ctrl = ctrl;
       r.prob[0].a = {Zb[nxt], n, Lw.buf_stride, nullptr, 0};
       r.prob[0].b = {Yb[nxt], n, Lw.buf_stride, nullptr, 0};
@@ -727,14 +770,14 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   if (ldg < n || sg < 0 || (batch > 1 && sg != 0 && sg < (int64_t)(m - 1) * ldg + n))
     return PMX_ERR_INVALID_VALUE;
   if (!batch_layout_ok(m, n, ldu, su, batch)) return PMX_ERR_INVALID_VALUE;
-  if (dtype == PMX_BF16) return PMX_ERR_NOT_SUPPORTED;
+  const bool bf = dtype == PMX_BF16;
   const int rows = std::max(m, n), cols = std::min(m, n);
   const bool tr = m < n;
   const IterLayout Lw = iter_layout(rows, cols, batch, o, 2, 2, sizeof(float));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
-  const Extent eg = extent_of(G, m, n, ldg, sg, batch, 4);
-  const Extent eu = extent_of(U, m, n, ldu, su, batch, 4);
+  const Extent eg = extent_of(G, m, n, ldg, sg, batch, bf ? 2 : 4);
+  const Extent eu = extent_of(U, m, n, ldu, su, batch, bf ? 2 : 4);
   Extent ew;
   ew.lo = (uintptr_t)ws;
   ew.hi = ew.lo + Lw.total;
@@ -759,7 +802,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
 
   PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
-    return launch_fro_scale(G, false, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, q.s);
+    return launch_fro_scale(G, bf, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
   PolarInitParams pi;
   pi.g = G;
@@ -771,10 +814,13 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   pi.cols = cols;
   pi.transpose = tr ? 1 : 0;
   pi.ctrl = ctrl;
-  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_init(pi, false, batch, q.s); }));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_init(pi, bf, batch, q.s); }));
+  // bf16 operands load 8 elements at a time: every bf16 leading dimension and
+  // stride must be a multiple of 8, every fp32 one a multiple of 4
+  const bool vec_bf = (cols % 8 == 0) && (Lw.buf_stride % 8 == 0);
 
   auto residual = [&](float* Xc, int products, int count, int k_next) {
-    GemmParams r = gemm_base(cols, cols, rows, batch);
+    GemmParams r = gemm_base(q.h, cols, cols, rows, batch);
     r.ctrl = ctrl;
     r.prob[0].a = {Xc, cols, Lw.buf_stride, nullptr, 0};
     r.prob[0].b = {Xc, cols, Lw.buf_stride, nullptr, 0};
@@ -787,14 +833,18 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     r.count_update = count;
     r.cfg = cfg;
     r.sketch = make_sketch(Lw, ws, cfg, cols, k_next, 0, acc && k_next < o.max_iter);
+    if (bf) {
+      r.vec = vec_bf ? 1 : 0;
+      return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_bf16(r, ROLE_RESID, q.s); });
+    }
     set_vec(r);
     return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
   };
   PMX_TRY(residual(Xb[0], 1, 0, 0));
   for (int k = 0; k < o.max_iter; ++k) {
-    PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b));
+    PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, bf));
     const int cur = k & 1, nxt = cur ^ 1;
-    GemmParams u = gemm_base(rows, cols, cols, batch);
+    GemmParams u = gemm_base(q.h, rows, cols, cols, batch);
     u.ctrl = ctrl;
     u.degree = d;
     u.c0 = (float)taylor(0);
@@ -804,8 +854,13 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     u.prob[0].c = Xb[nxt];
     u.prob[0].ldc = cols;
     u.prob[0].stride_c = Lw.buf_stride;
-    set_vec(u);
-    PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
+    if (bf) {
+      u.vec = vec_bf ? 1 : 0;
+      PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_bf16(u, ROLE_UPDATE, q.s); }));
+    } else {
+      set_vec(u);
+      PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
+    }
     PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1, k + 1));
   }
   PolarFinishParams fp;
@@ -819,7 +874,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   fp.cols = cols;
   fp.transpose = tr ? 1 : 0;
   fp.ctrl = ctrl;
-  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_finish(fp, false, batch, q.s); }));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_finish(fp, bf, batch, q.s); }));
   return PMX_OK;
 }
 
@@ -843,13 +898,13 @@ pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, i
   if (ldl < m || ldg < n || ldr < n || sl < 0 || sg < 0 || sr < 0)
     return PMX_ERR_INVALID_VALUE;
   if (!batch_layout_ok(m, n, ldp, sp, batch)) return PMX_ERR_INVALID_VALUE;
-  if (dtype == PMX_BF16) return PMX_ERR_NOT_SUPPORTED;
-  const size_t need = apply_ws(m, n, batch);
+  const bool bf = dtype == PMX_BF16;
+  const size_t need = apply_ws(m, n, batch, dtype);
   pmx_status st = check_ws(ws, ws_bytes, need);
   if (st != PMX_OK) return st;
-  const Extent ep = extent_of(P, m, n, ldp, sp, batch, 4);
+  const Extent ep = extent_of(P, m, n, ldp, sp, batch, bf ? 2 : 4);
   const Extent el = extent_of(Linv, m, m, ldl, sl, batch, 4);
-  const Extent eg = extent_of(G, m, n, ldg, sg, batch, 4);
+  const Extent eg = extent_of(G, m, n, ldg, sg, batch, bf ? 2 : 4);
   const Extent er = extent_of(Rinv, n, n, ldr, sr, batch, 4);
   Extent ew;
   ew.lo = (uintptr_t)ws;
@@ -861,24 +916,41 @@ pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, i
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
   Enq q{h, (hipStream_t)stream};
+  const size_t one = align_up(sizeof(float) * (size_t)m * n * batch);
   float* T = (float*)ws;
   const int64_t st_t = (int64_t)m * n;
-  GemmParams a = gemm_base(m, n, m, batch);
+  const float* gf = (const float*)G;
+  if (bf) {
+    float* Gw = at<float>(ws, one);
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+      return launch_convert(G, true, ldg, sg, Gw, false, n, st_t, m, n, batch, q.s);
+    }));
+    gf = Gw;
+    ldg = n;
+    sg = st_t;
+  }
+  GemmParams a = gemm_base(q.h, m, n, m, batch);
   a.prob[0].a = {Linv, ldl, sl, nullptr, 0};
-  a.prob[0].b = {(const float*)G, ldg, sg, nullptr, 0};
+  a.prob[0].b = {gf, ldg, sg, nullptr, 0};
   a.prob[0].c = T;
   a.prob[0].ldc = n;
   a.prob[0].stride_c = st_t;
   set_vec(a);
   PMX_TRY(q.run(PMX_KC_GEMM_APPLY, [&] { return launch_gemm_f32(a, false, false, ROLE_APPLY, q.s); }));
-  GemmParams b = gemm_base(m, n, n, batch);
+  GemmParams b = gemm_base(q.h, m, n, n, batch);
+  float* Pw = bf ? at<float>(ws, 2 * one) : (float*)P;
   b.prob[0].a = {T, n, st_t, nullptr, 0};
   b.prob[0].b = {Rinv, ldr, sr, nullptr, 0};
-  b.prob[0].c = (float*)P;
-  b.prob[0].ldc = ldp;
-  b.prob[0].stride_c = sp;
+  b.prob[0].c = Pw;
+  b.prob[0].ldc = bf ? n : ldp;
+  b.prob[0].stride_c = bf ? st_t : sp;
   set_vec(b);
   PMX_TRY(q.run(PMX_KC_GEMM_APPLY, [&] { return launch_gemm_f32(b, false, false, ROLE_APPLY, q.s); }));
+  if (bf) {
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+      return launch_convert(Pw, false, n, st_t, P, true, ldp, sp, m, n, batch, q.s);
+    }));
+  }
   return PMX_OK;
 }
 

@@ -6,26 +6,29 @@
 // (L^{-1/4} G R^{-1/4}) goes through this kernel.
 //
 // Design (CDNA4, 64-wide waves):
-//  * block tile 128 x 128, k-tile 16, 256 threads = 4 waves in a 2 x 2
-//    arrangement, each wave a 64 x 64 sub-tile made of 2 x 2
-//    v_mfma_f32_32x32x2_f32 accumulators (64 fp32 accumulator registers).
-//  * fp32 MFMA issues one 32x32x2 per 16 passes, so the kernel is bound by
-//    matrix-core issue, not by LDS or HBM (arithmetic intensity of a
-//    128 x 128 tile is 32 flop per byte of L2 traffic).
-//  * Within a k-tile the 16 k values are distributed over the MFMA's two
-//    k-lanes as k = 8 * (lane / 32) + step, so an operand stored with k
-//    contiguous ("KC", e.g. A not transposed) is read as two 16-byte LDS loads
-//    per lane, and an operand stored with m/n contiguous ("MC", e.g. B not
+//  * A block tile of BM x BN is split over WGM x WGN waves; every wave owns a
+//    (BM/WGM) x (BN/WGN) sub-tile made of 32 x 32 v_mfma_f32_32x32x2_f32
+//    accumulators.  fp32 MFMA issues one 32x32x2 per 16 passes, so the
+//    kernel is bound by matrix-core issue: a 128 x 128 tile already moves only
+//    1/32 byte of L2 traffic per flop.
+//  * Within a k-tile of BK values the k index is distributed over the MFMA's
+//    two k-lanes as k = (BK/2) * (lane / 32) + step, so an operand stored
+//    with k contiguous ("KC", e.g. A not transposed) is read as 16-byte LDS
+//    loads, and an operand stored with m/n contiguous ("MC", e.g. B not
 //    transposed) is staged without transposition and read with 4-byte loads
-//    along consecutive rows (conflict-free).  Both layouts are written to LDS
-//    with 16-byte stores straight from the 16-byte global loads.
+//    along consecutive rows.  Both layouts are written to LDS with 16-byte
+//    stores straight from 16-byte global loads.
 //  * LDS is double buffered with a register prefetch of the next k-tile:
 //    one barrier per k-tile.
+//  * Persistent grid: at most `max_blocks` blocks loop over (matrix, tile)
+//    items, so launches of matrices that have already converged dispatch
+//    few workgroups.  Items follow a grouped order (8 tile-rows per column
+//    sweep) for L2 reuse.
 //  * An operand may be the PRISM polynomial g = c0 I + c1 R + alpha R^2
 //    (or c0 I + alpha R for d = 1), formed while its tile is loaded from R and
 //    R^2, so g is never written to memory.
 //  * Epilogues by role: plain store; residual R = I - acc with a deterministic
-//    Frobenius reduction and the convergence decision (last block per matrix),
+//    Frobenius reduction and the convergence decision (last tile per matrix),
 //    while the blocks also generate the next iteration's Gaussian sketch;
 //    Shampoo EMA C = beta C + (1 - beta) acc + eps I in place.
 #include "pmx_internal.h"
@@ -35,17 +38,34 @@ namespace {
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_EMA = 2 };
 
-constexpr int BM = 128, BN = 128, BK = 16;
-constexpr int KC_LD = BK + 4;    // KC layout: [row][k], row stride 20 floats (80 B)
-constexpr int MC_LD = BM + 4;    // MC layout: [k][row], row stride 132 floats
-constexpr int NT = 256;
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int KC_FLOATS = BM * KC_LD;  // 2560
-constexpr int MC_FLOATS = BK * MC_LD;  // 2112
-constexpr int TILE_FLOATS = KC_FLOATS > MC_FLOATS ? KC_FLOATS : MC_FLOATS;
+// Tile configuration: block tile BM x BN x BK over WGM x WGN waves, at least
+// MINW waves resident per SIMD (bounds the registers per wave), STAGES LDS
+// buffers (2: double buffered, one barrier per k-tile; 1: single buffer with
+// the register prefetch written after a second barrier).
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int MINW_, int STAGES_ = 2>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, MINW = MINW_;
+  static constexpr int STAGES = STAGES_;
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  static constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 accumulators per wave
+  static constexpr int KH = BK / 2;                     // k values per MFMA k-lane
+  static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(BK % 16 == 0, "k tile");
+};
+
+// LDS floats of one operand tile of `rows` (m or n) x BK in layout KC or MC.
+template <class C, bool KCL, int ROWS>
+struct OpTile {
+  static constexpr int LD = KCL ? C::BK + 4 : ROWS + 4;
+  static constexpr int FLOATS = KCL ? ROWS * LD : C::BK * LD;
+  static constexpr int VEC = ROWS * C::BK / 4;  // float4 per tile
+  static constexpr int PER_THREAD = VEC / C::NT;
+  static_assert(VEC % C::NT == 0, "tile load split");
+};
 
 // Is the operand stored with k contiguous?  A (M x K view): not transposed.
 // B (K x N view): transposed.
@@ -60,28 +80,30 @@ struct PolyCtx {
   int degree;
 };
 
-// Global -> register prefetch of one 128 x 16 operand tile: two float4 per thread.
-// KC: storage rows are the tile's m/n rows, 16 k values = 4 float4 per row.
-// MC: storage rows are k, 128 m/n values = 32 float4 per row.
+// Global -> register prefetch of one ROWS x BK operand tile.
+// KC: storage rows are the tile's m/n rows (BK/4 float4 per row).
+// MC: storage rows are k (ROWS/4 float4 per row).
 // With `poly` the element (i, j) of the stored matrix is
 // c0 [i == j] + c1 R[i][j] + alpha R2[i][j] (d = 2) or c0 [i == j] + alpha R[i][j].
-template <bool KCL>
-__device__ __forceinline__ void load_tile(f32x4 (&r)[2], const float* __restrict__ base,
+template <class C, bool KCL, int ROWS, int NV>
+__device__ __forceinline__ void load_tile(f32x4 (&r)[NV],
+                                          const float* __restrict__ base,
                                           const float* __restrict__ base2, bool poly,
                                           const PolyCtx& pc, int64_t ld, int row0, int nrows,
                                           int k0, int K, bool vec) {
+  static_assert(NV == OpTile<C, KCL, ROWS>::PER_THREAD, "prefetch registers");
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = threadIdx.x + NT * i;
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + C::NT * i;
     int srow, scol, lim_row, lim_col;
     if (KCL) {
-      srow = row0 + (idx >> 2);
-      scol = k0 + ((idx & 3) << 2);
+      srow = row0 + idx / (C::BK / 4);
+      scol = k0 + (idx % (C::BK / 4)) * 4;
       lim_row = nrows;
       lim_col = K;
     } else {
-      srow = k0 + (idx >> 5);
-      scol = row0 + ((idx & 31) << 2);
+      srow = k0 + idx / (ROWS / 4);
+      scol = row0 + (idx % (ROWS / 4)) * 4;
       lim_row = K;
       lim_col = nrows;
     }
@@ -124,194 +146,311 @@ __device__ __forceinline__ void load_tile(f32x4 (&r)[2], const float* __restrict
   }
 }
 
-template <bool KCL>
-__device__ __forceinline__ void store_tile(float* __restrict__ lds, const f32x4 (&r)[2]) {
+template <class C, bool KCL, int ROWS, int NV>
+__device__ __forceinline__ void store_tile(float* __restrict__ lds, const f32x4 (&r)[NV]) {
+  using T = OpTile<C, KCL, ROWS>;
+  static_assert(NV == T::PER_THREAD, "prefetch registers");
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = threadIdx.x + NT * i;
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + C::NT * i;
     float* dst;
-    if (KCL) dst = lds + (idx >> 2) * KC_LD + ((idx & 3) << 2);
-    else dst = lds + (idx >> 5) * MC_LD + ((idx & 31) << 2);
+    if (KCL) dst = lds + (idx / (C::BK / 4)) * T::LD + (idx % (C::BK / 4)) * 4;
+    else dst = lds + (idx / (ROWS / 4)) * T::LD + (idx % (ROWS / 4)) * 4;
     *reinterpret_cast<f32x4*>(dst) = r[i];
   }
 }
 
-// Fragment of one 32-row (or 32-column) MFMA operand for the 8 k-steps of a
-// k-tile: lane l supplies row (l % 32) at k = 8 * (l / 32) + step.
-template <bool KCL>
+// Fragment of one 32-row (or 32-column) MFMA operand for 8 k-steps starting
+// at step s0: lane l supplies row (l % 32) at k = KH * (l / 32) + s0 + s.
+template <class C, bool KCL, int ROWS>
 __device__ __forceinline__ void read_frag(float (&f)[8], const float* __restrict__ lds,
-                                          int row_base) {
+                                          int row_base, int s0) {
+  using T = OpTile<C, KCL, ROWS>;
   const int lane = threadIdx.x & 63;
   const int row = row_base + (lane & 31);
-  const int kh = (lane >> 5) << 3;
+  const int kh = (lane >> 5) * C::KH + s0;
   if (KCL) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(lds + row * KC_LD + kh);
+    const f32x4* p = reinterpret_cast<const f32x4*>(lds + row * T::LD + kh);
     const f32x4 x0 = p[0], x1 = p[1];
     f[0] = x0[0]; f[1] = x0[1]; f[2] = x0[2]; f[3] = x0[3];
     f[4] = x1[0]; f[5] = x1[1]; f[6] = x1[2]; f[7] = x1[3];
   } else {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) f[s] = lds[(kh + s) * MC_LD + row];
+    for (int s = 0; s < 8; ++s) f[s] = lds[(kh + s) * T::LD + row];
   }
 }
 
-template <bool TA, bool TB, int ROLE>
-__global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmParams p) {
-  constexpr int EPI = ROLE == ROLE_RESID ? EPI_RESID : (ROLE == ROLE_STATS ? EPI_EMA : EPI_STORE);
-  const int z = blockIdx.z;
-  const int pi = z % p.nprob;
-  const int b = z / p.nprob;
-  if (p.ctrl) {
-    const int st = *(volatile int32_t*)&p.ctrl[b].status;
-    if (st != PMX_RUNNING) return;
+// Work item -> (matrix-problem z, tile m, tile n).  mode 1 additionally
+// permutes every full round of G items so that the blocks resident at the
+// same time on one XCD (workgroups go to the 8 XCDs round-robin by block
+// index) take neighbouring items; mode 2 keeps row-major tiles; modes 0 and
+// 1 order the tiles of a matrix in groups of 8 tile-rows per column sweep.
+struct TileCoord {
+  int z, tm, tn, tile;
+};
+
+__device__ __forceinline__ TileCoord map_item(int it, int G, int total, int tiles_m,
+                                              int tiles_n, int mode) {
+  int L = it;
+  if (mode == 1 && (G & 7) == 0) {
+    const int round = it / G;
+    if ((round + 1) * G <= total) {
+      const int bi = it - round * G;
+      L = round * G + (bi & 7) * (G >> 3) + (bi >> 3);
+    }
   }
-  const GemmProblem& pr = p.prob[pi];
-  const float* __restrict__ A = pr.a.ptr + (int64_t)b * pr.a.stride;
-  const float* __restrict__ B = pr.b.ptr + (int64_t)b * pr.b.stride;
-  float* __restrict__ C = pr.c + (int64_t)b * pr.stride_c;
+  const int tiles = tiles_m * tiles_n;
+  TileCoord c;
+  c.z = L / tiles;
+  const int t = L - c.z * tiles;
+  c.tile = t;
+  if (mode == 2) {
+    c.tm = t / tiles_n;
+    c.tn = t - c.tm * tiles_n;
+    return c;
+  }
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * GM;
+  const int gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int in_group = t - group * per_group;
+  c.tm = first_m + in_group % gsize;
+  c.tn = in_group / gsize;
+  return c;
+}
 
-  const int tile = blockIdx.x;
-  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
-  PolyCtx pc;
-  pc.c0 = p.c0;
-  pc.c1 = p.c1;
-  pc.degree = p.degree;
-  pc.alpha = (p.ctrl && (pr.a.poly || pr.b.poly)) ? (float)p.ctrl[b].alpha : 0.f;
-  if (EPI == EPI_RESID) sketch_share(p.sketch, b, tile, gridDim.x);
-  const int m0 = tm * BM, n0 = tn * BN;
-
+template <class C, bool TA, bool TB, int ROLE>
+__global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) {
+  constexpr int EPI = ROLE == ROLE_RESID ? EPI_RESID : (ROLE == ROLE_STATS ? EPI_EMA : EPI_STORE);
   constexpr bool AKC = Layout<true, TA>::kc;
   constexpr bool BKC = Layout<false, TB>::kc;
+  using TAo = OpTile<C, AKC, C::BM>;
+  using TBo = OpTile<C, BKC, C::BN>;
 
-  __shared__ __attribute__((aligned(16))) float smem[2][2][TILE_FLOATS];
+  __shared__ __attribute__((aligned(16))) float smem_a[C::STAGES][TAo::FLOATS];
+  __shared__ __attribute__((aligned(16))) float smem_b[C::STAGES][TBo::FLOATS];
+  __shared__ double red[C::NW];
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int wm = (wid >> 1) * 64, wn = (wid & 1) * 64;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
+  const int wm = (wid / C::WGN) * C::WTM, wn = (wid % C::WGN) * C::WTN;
   const bool vec = p.vec != 0;
-  const int nk = (p.K + BK - 1) / BK;
-  f32x4 ra[2], rb[2];
-  const float* __restrict__ A2 = pr.a.poly && pr.a.ptr2 ? pr.a.ptr2 + (int64_t)b * pr.a.stride : A;
-  const float* __restrict__ B2 = pr.b.poly && pr.b.ptr2 ? pr.b.ptr2 + (int64_t)b * pr.b.stride : B;
-  const bool apoly = pr.a.poly != 0, bpoly = pr.b.poly != 0;
-  load_tile<AKC>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, 0, p.K, vec);
-  load_tile<BKC>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, 0, p.K, vec);
-  store_tile<AKC>(smem[0][0], ra);
-  store_tile<BKC>(smem[0][1], rb);
-  __syncthreads();
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int total = tiles * p.batch * p.nprob;
+  const int G = gridDim.x;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_tile<AKC>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, (kt + 1) * BK, p.K, vec);
-      load_tile<BKC>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, (kt + 1) * BK, p.K, vec);
+  for (int it = blockIdx.x; it < total; it += G) {
+    const TileCoord tc = map_item(it, G, total, p.tiles_m, p.tiles_n, p.map_mode);
+    const int pi = tc.z % p.nprob;
+    const int b = tc.z / p.nprob;
+    if (p.ctrl) {
+      const int st = *(volatile int32_t*)&p.ctrl[b].status;
+      if (st != PMX_RUNNING) continue;
     }
-    float fa[2][8], fb[2][8];
+    const GemmProblem& pr = p.prob[pi];
+    const float* __restrict__ A = pr.a.ptr + (int64_t)b * pr.a.stride;
+    const float* __restrict__ B = pr.b.ptr + (int64_t)b * pr.b.stride;
+    float* __restrict__ Cm = pr.c + (int64_t)b * pr.stride_c;
+    const float* __restrict__ A2 = pr.a.poly && pr.a.ptr2 ? pr.a.ptr2 + (int64_t)b * pr.a.stride : A;
+    const float* __restrict__ B2 = pr.b.poly && pr.b.ptr2 ? pr.b.ptr2 + (int64_t)b * pr.b.stride : B;
+    const bool apoly = pr.a.poly != 0, bpoly = pr.b.poly != 0;
+    PolyCtx pc;
+    pc.c0 = p.c0;
+    pc.c1 = p.c1;
+    pc.degree = p.degree;
+    pc.alpha = (p.ctrl && (apoly || bpoly)) ? (float)p.ctrl[b].alpha : 0.f;
+    if (EPI == EPI_RESID) sketch_share(p.sketch, b, tc.tile, tiles);
+    const int m0 = tc.tm * C::BM, n0 = tc.tn * C::BN;
+
+    f32x16 acc[C::FM][C::FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) read_frag<AKC>(fa[i], smem[cur][0], wm + 32 * i);
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) read_frag<BKC>(fb[j], smem[cur][1], wn + 32 * j);
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s], acc[i][j], 0, 0, 0);
-    if (more) {
-      store_tile<AKC>(smem[cur ^ 1][0], ra);
-      store_tile<BKC>(smem[cur ^ 1][1], rb);
-    }
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = (p.K + C::BK - 1) / C::BK;
+    f32x4 ra[TAo::PER_THREAD], rb[TBo::PER_THREAD];
+    __syncthreads();  // the previous item's last LDS reads are done
+    load_tile<C, AKC, C::BM>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, 0, p.K, vec);
+    load_tile<C, BKC, C::BN>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, 0, p.K, vec);
+    store_tile<C, AKC, C::BM>(smem_a[0], ra);
+    store_tile<C, BKC, C::BN>(smem_b[0], rb);
     __syncthreads();
-  }
 
-  // Epilogue.  Lane l of a 32x32 accumulator holds column (l % 32) and rows
-  // 8 * (v / 4) + 4 * (l / 32) + (v % 4), v = 0..15.
-  const int hi = lane >> 5, col_in = lane & 31;
-  float fro = 0.f;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = C::STAGES == 2 ? (kt & 1) : 0;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        load_tile<C, AKC, C::BM>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, (kt + 1) * C::BK, p.K, vec);
+        load_tile<C, BKC, C::BN>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, (kt + 1) * C::BK, p.K, vec);
+      }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int s0 = 0; s0 < C::KH; s0 += 8) {
+        float fa[C::FM][8], fb[C::FN][8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn + 32 * j + col_in;
+        for (int i = 0; i < C::FM; ++i) read_frag<C, AKC, C::BM>(fa[i], smem_a[cur], wm + 32 * i, s0);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-        if (row < p.M && col < p.N) {
-          float* dst = C + (int64_t)row * pr.ldc + col;
-          float x = acc[i][j][v];
-          if (EPI == EPI_RESID) {
-            x = (row == col ? 1.f : 0.f) - x;
-            fro += x * x;
-          } else if (EPI == EPI_EMA) {
-            x = p.beta * *dst + p.omb * x + (row == col ? p.eps : 0.f);
-          }
-          *dst = x;
+        for (int j = 0; j < C::FN; ++j) read_frag<C, BKC, C::BN>(fb[j], smem_b[cur], wn + 32 * j, s0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s], acc[i][j], 0, 0, 0);
+      }
+      if (C::STAGES == 2) {
+        if (more) {
+          store_tile<C, AKC, C::BM>(smem_a[cur ^ 1], ra);
+          store_tile<C, BKC, C::BN>(smem_b[cur ^ 1], rb);
+        }
+        __syncthreads();
+      } else {
+        __syncthreads();
+        if (more) {
+          store_tile<C, AKC, C::BM>(smem_a[0], ra);
+          store_tile<C, BKC, C::BN>(smem_b[0], rb);
+          __syncthreads();
         }
       }
     }
 
-  if (EPI == EPI_RESID) {
-    __shared__ double red[NT / 64];
-    const double blocksum = block_sum<NT / 64>((double)fro, red);
-    double total;
-    const int nparts = p.tiles_m * p.tiles_n;
-    if (last_block_sum<NT / 64>(blocksum, p.partials + (int64_t)b * p.partial_stride,
-                                &p.ctrl[b].counter, nparts, tile, red, &total)) {
-      if (threadIdx.x == 0) {
-        Ctrl& c = p.ctrl[b];
-        if (p.count_update) c.iter += 1;
-        c.gemms += p.products;
-        decide(c, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, total);
+    // Epilogue.  Lane l of a 32x32 accumulator holds column (l % 32) and rows
+    // 8 * (v / 4) + 4 * (l / 32) + (v % 4), v = 0..15.
+    const int hi = lane >> 5, col_in = lane & 31;
+    float fro = 0.f;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int col = n0 + wn + 32 * j + col_in;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (row < p.M && col < p.N) {
+            float* dst = Cm + (int64_t)row * pr.ldc + col;
+            float x = acc[i][j][v];
+            if (EPI == EPI_RESID) {
+              x = (row == col ? 1.f : 0.f) - x;
+              fro += x * x;
+            } else if (EPI == EPI_EMA) {
+              x = p.beta * *dst + p.omb * x + (row == col ? p.eps : 0.f);
+            }
+            *dst = x;
+          }
+        }
+      }
+
+    if (EPI == EPI_RESID) {
+      const double blocksum = block_sum<C::NW>((double)fro, red);
+      double tot;
+      if (last_block_sum<C::NW>(blocksum, p.partials + (int64_t)b * p.partial_stride,
+                                &p.ctrl[b].counter, tiles, tc.tile, red, &tot)) {
+        if (threadIdx.x == 0) {
+          Ctrl& c = p.ctrl[b];
+          if (p.count_update) c.iter += 1;
+          c.gemms += p.products;
+          decide(c, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
+        }
       }
     }
   }
 }
 
-#define PMX_GEMM_LAUNCH(TA, TB, ROLE) \
-  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, ROLE>), grid, dim3(NT), 0, s, p)
+// Tile configurations.  0: 128 x 128 x 16, 2 x 2 waves (64 x 64 per wave);
+// 1: 256 x 128 x 16, 4 x 2 waves; 2: 128 x 256 x 16, 2 x 4 waves;
+// 3: 128 x 128 x 32, 2 x 2 waves; 4: 64 x 64 x 16, 2 x 2 waves (32 x 32 per
+// wave, for small matrices); 5: 128 x 64 x 16, 2 x 2 waves; 6: 256 x 128 x 16,
+// 2 x 2 waves (128 x 64 per wave); 7: 128 x 256 x 16, 2 x 2 waves (64 x 128);
+// 8: 128 x 128 x 64, single LDS buffer; 9: 128 x 128 x 32, double buffered.
+using C0 = Cfg<128, 128, 16, 2, 2, 3>;
+using C1 = Cfg<256, 128, 16, 4, 2, 2>;
+using C2 = Cfg<128, 256, 16, 2, 4, 2>;
+using C3 = Cfg<128, 128, 32, 2, 2, 2>;
+using C4 = Cfg<64, 64, 16, 2, 2, 4>;
+using C5 = Cfg<128, 64, 16, 2, 2, 4>;
+using C6 = Cfg<256, 128, 16, 2, 2, 2>;
+using C7 = Cfg<128, 256, 16, 2, 2, 2>;
+using C8 = Cfg<128, 128, 64, 2, 2, 1, 1>;
+using C9 = Cfg<128, 128, 32, 2, 2, 1, 2>;
+
+template <class C>
+int tiles_of(int M, int N) {
+  return ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+}
+
+template <class C, bool TA, bool TB>
+hipError_t launch_role(GemmParams p, int role, hipStream_t s) {
+  p.tiles_m = (p.M + C::BM - 1) / C::BM;
+  p.tiles_n = (p.N + C::BN - 1) / C::BN;
+  const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch * p.nprob;
+  int64_t g = total;
+  if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
+  const dim3 grid((unsigned)g), block(C::NT);
+  switch (role) {
+    case ROLE_POWER: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_POWER>), grid, block, 0, s, p); break;
+    case ROLE_UPDATE: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_UPDATE>), grid, block, 0, s, p); break;
+    case ROLE_RESID: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_RESID>), grid, block, 0, s, p); break;
+    case ROLE_STATS: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_STATS>), grid, block, 0, s, p); break;
+    case ROLE_APPLY: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_APPLY>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Roles instantiated per transpose combination: every NN role except the
+// statistics, G G^T (NT), G^T G and X^T X (TN).
+template <class C>
+hipError_t launch_cfg(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s) {
+  if (!ta && !tb) {
+    if (role == ROLE_STATS) return hipErrorInvalidValue;
+    return launch_role<C, false, false>(p, role, s);
+  }
+  if (!ta && tb) {
+    if (role != ROLE_STATS) return hipErrorInvalidValue;
+    return launch_role<C, false, true>(p, role, s);
+  }
+  if (ta && !tb) {
+    if (role != ROLE_STATS && role != ROLE_RESID) return hipErrorInvalidValue;
+    return launch_role<C, true, false>(p, role, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 }  // namespace
 
-int gemm_f32_tiles(int M, int N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+int gemm_f32_tiles(int M, int N) {
+  // upper bound over the configurations: the smallest tile (64 x 64)
+  return tiles_of<C4>(M, N);
+}
 
-// Instantiated combinations: every NN role, G G^T (NT) and G^T G / X^T X (TN).
-hipError_t launch_gemm_f32(const GemmParams& pin, bool ta, bool tb, int role, hipStream_t s) {
-  GemmParams p = pin;
-  p.tiles_m = (p.M + BM - 1) / BM;
-  p.tiles_n = (p.N + BN - 1) / BN;
-  dim3 grid(p.tiles_m * p.tiles_n, 1, p.batch * p.nprob);
-  if (!ta && !tb) {
-    switch (role) {
-      case ROLE_POWER: PMX_GEMM_LAUNCH(false, false, ROLE_POWER); break;
-      case ROLE_UPDATE: PMX_GEMM_LAUNCH(false, false, ROLE_UPDATE); break;
-      case ROLE_RESID: PMX_GEMM_LAUNCH(false, false, ROLE_RESID); break;
-      case ROLE_APPLY: PMX_GEMM_LAUNCH(false, false, ROLE_APPLY); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else if (!ta && tb) {
-    if (role != ROLE_STATS) return hipErrorInvalidValue;
-    PMX_GEMM_LAUNCH(false, true, ROLE_STATS);
-  } else if (ta && !tb) {
-    switch (role) {
-      case ROLE_STATS: PMX_GEMM_LAUNCH(true, false, ROLE_STATS); break;
-      case ROLE_RESID: PMX_GEMM_LAUNCH(true, false, ROLE_RESID); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    return hipErrorInvalidValue;
+// Configuration choice: p.cfg_id >= 0 forces one; otherwise the largest tile
+// that still gives every CU at least one tile of the launch.
+hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s) {
+  int id = p.cfg_id;
+  if (id < 0) {
+    const int64_t units = (int64_t)p.batch * p.nprob;
+    const int cu = p.num_cu > 0 ? p.num_cu : 256;
+    if ((int64_t)tiles_of<C0>(p.M, p.N) * units >= cu) id = 0;
+    else if ((int64_t)tiles_of<C5>(p.M, p.N) * units >= cu) id = 5;
+    else id = 4;
   }
-  return hipGetLastError();
+  switch (id) {
+    case 0: return launch_cfg<C0>(p, ta, tb, role, s);
+    case 1: return launch_cfg<C1>(p, ta, tb, role, s);
+    case 2: return launch_cfg<C2>(p, ta, tb, role, s);
+    case 3: return launch_cfg<C3>(p, ta, tb, role, s);
+    case 4: return launch_cfg<C4>(p, ta, tb, role, s);
+    case 5: return launch_cfg<C5>(p, ta, tb, role, s);
+    case 6: return launch_cfg<C6>(p, ta, tb, role, s);
+    case 7: return launch_cfg<C7>(p, ta, tb, role, s);
+    case 8: return launch_cfg<C8>(p, ta, tb, role, s);
+    case 9: return launch_cfg<C9>(p, ta, tb, role, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pmx

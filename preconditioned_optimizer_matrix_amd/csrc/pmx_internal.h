@@ -246,6 +246,10 @@ struct GemmParams {
   int M, N, K;
   int tiles_m, tiles_n;
   int vec;         // 1: every operand allows 16-byte loads
+  int max_blocks;  // persistent grid cap (0: one block per tile)
+  int cfg_id;      // tile configuration (-1: chosen from the shape)
+  int map_mode;    // tile order: 0 grouped, 1 grouped + XCD rounds, 2 row-major
+  int num_cu;
   Ctrl* ctrl;      // per-matrix control blocks; null = unconditional
   // polynomial operands
   int degree;

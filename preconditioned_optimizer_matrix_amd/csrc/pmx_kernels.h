@@ -122,6 +122,12 @@ hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hip
 hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s);
 int skinny_blocks(int n, int q);
 hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s);
+// Elementwise copy between fp32 and bf16 matrices (rows x cols, strided batch);
+// bf16 -> fp32 is exact, fp32 -> bf16 rounds to nearest even.
+hipError_t launch_convert(const void* src, bool src_bf16, int64_t lds, int64_t ss, void* dst,
+                          bool dst_bf16, int64_t ldd, int64_t sd, int rows, int cols, int batch,
+                          hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmParams& p, int role, hipStream_t s);
 hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t s);
 hipError_t launch_polar_finish(const PolarFinishParams& p, bool bf16, int batch, hipStream_t s);
 

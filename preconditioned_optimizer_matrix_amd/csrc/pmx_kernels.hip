@@ -292,39 +292,50 @@ __device__ double alpha_from_gram(const double* G, int J, double s, const AlphaC
 }
 
 // ---------------------------------------------------------------- skinny products
-// Recursive-halving reduction over a 64-lane wave of CNT values per lane:
-// at the step with offset O the lanes with bit O set keep the upper half of
-// their remaining values and add the partner's copy of it.  With CNT = 64,
-// lane l ends holding the wave-wide sum of value index l in acc[0].
+// Recursive-halving reduction over a 64-lane wave of CNT values per lane
+// (CNT a power of two <= 64): at the step with offset O the lanes with bit O
+// set keep the upper half of their remaining values and add the partner's
+// copy of it; once one value is left the remaining offsets add plainly.
+// Lane l ends with the wave-wide sum of value index l / (64 / CNT) in acc[0].
 template <int CNT, int O>
 __device__ __forceinline__ void halve_reduce(float* acc, int lane) {
-  if constexpr (CNT > 1 && O >= 1) {
-    constexpr int H = CNT / 2;
-    const bool upper = (lane & O) != 0;
+  if constexpr (O >= 1) {
+    if constexpr (CNT > 1) {
+      constexpr int H = CNT / 2;
+      const bool upper = (lane & O) != 0;
 #pragma unroll
-    for (int i = 0; i < H; ++i) {
-      const float send = upper ? acc[i] : acc[i + H];
-      const float keep = upper ? acc[i + H] : acc[i];
-      acc[i] = keep + __shfl_xor(send, O, 64);
+      for (int i = 0; i < H; ++i) {
+        const float send = upper ? acc[i] : acc[i + H];
+        const float keep = upper ? acc[i + H] : acc[i];
+        acc[i] = keep + __shfl_xor(send, O, 64);
+      }
+      halve_reduce<H, O / 2>(acc, lane);
+    } else {
+      acc[0] += __shfl_xor(acc[0], O, 64);
+      halve_reduce<1, O / 2>(acc, lane);
     }
-    halve_reduce<H, O / 2>(acc, lane);
   }
 }
 
 // out[:, oc : oc + q] = ||R||_F^-pow * Mat * in[:, ic : ic + q] for an n x n Mat
-// and an n x q block of the Krylov buffer (q <= Q).  HBM-bound on Mat: each
-// block streams 4 * (64 / Q) rows of Mat once; In is staged through LDS in
-// chunks of 256 rows and shared by those rows.  Each lane accumulates
-// (64 / Q) x Q partial sums; a recursive-halving exchange over the wave
-// leaves lane l with the complete sum for (row l / Q, column l % Q).
+// and an n x q block of the Krylov buffer (q <= Q).  HBM-bound on Mat, read
+// once with 16-byte loads: a block of 4 waves owns 8 rows (2 per wave), so
+// n = 4096 gives 512 blocks.  In is staged column-major through LDS in chunks
+// of 512 rows (conflict-free 16-byte reads) and shared by the block's rows.
+// Each lane accumulates 2 x Q partial sums over its columns; the wave's
+// recursive-halving reduction leaves the complete sums in the lanes.
 // GRAM (last Krylov pass): every block also adds its rows' share of the
 // J x J Gram of K_1..K_J in fp64; the last block to arrive reduces the
 // shares in block order and solves for alpha.
+constexpr int SK_RW = 2;             // rows per wave
+constexpr int SK_RB = 4 * SK_RW;     // rows per block
+constexpr int SK_CH = 512;           // In rows per LDS chunk
+constexpr int SK_LD = SK_CH + 4;     // column stride of the staged chunk
+
 template <int Q, bool GRAM>
 __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
-  constexpr int RW = 64 / Q;       // rows per wave
-  constexpr int RB = 4 * RW;       // rows per block
-  constexpr int LD = Q + 4;
+  constexpr int CNT = SK_RW * Q;        // partial sums per lane (16, 32 or 64)
+  constexpr int SHARE = 64 / CNT;       // lanes holding each final sum
   const int b = blockIdx.z;
   Ctrl* cb = p.ctrl + b;
   if (load_status(cb) != PMX_RUNNING) return;
@@ -335,52 +346,63 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   const double fro = cb->fro;
   const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
 
-  __shared__ __attribute__((aligned(16))) float in_lds[256 * LD];
+  __shared__ __attribute__((aligned(16))) float in_lds[Q * SK_LD];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int row0 = blockIdx.x * RB + wid * RW;
+  const int row0 = blockIdx.x * SK_RB + wid * SK_RW;
+  const bool vec = (job.mat_ld % 4 == 0) && ((((uintptr_t)mat) & 15) == 0);
 
-  float acc[RW * Q];
+  float acc[CNT];
 #pragma unroll
-  for (int i = 0; i < RW * Q; ++i) acc[i] = 0.f;
+  for (int i = 0; i < CNT; ++i) acc[i] = 0.f;
 
-  for (int j0 = 0; j0 < n; j0 += 256) {
+  for (int j0 = 0; j0 < n; j0 += SK_CH) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 256 * Q; idx += NT) {
-      const int r = idx / Q, c = idx - r * Q;
+    // stage In[j0 .. j0 + 512)[0 .. Q) column-major (zero beyond n and q)
+    for (int idx = threadIdx.x; idx < SK_CH * Q; idx += NT) {
+      const int c = idx / SK_CH, jj = idx - c * SK_CH;
       float v = 0.f;
-      if (j0 + r < n && c < p.q) v = kb[(int64_t)(j0 + r) * p.kld + job.in_col + c];
-      in_lds[r * LD + c] = v;
+      if (j0 + jj < n && c < p.q) v = kb[(int64_t)(j0 + jj) * p.kld + job.in_col + c];
+      in_lds[c * SK_LD + jj] = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int jj = lane + 64 * t;
+    for (int t = 0; t < SK_CH / 256; ++t) {
+      const int jj = 256 * t + 4 * lane;
       const int j = j0 + jj;
-      if (j < n) {
-        float m[RW];
+      if (j >= n) continue;
+      float4 m[SK_RW];
 #pragma unroll
-        for (int rr = 0; rr < RW; ++rr)
-          m[rr] = (row0 + rr < n) ? mat[(int64_t)(row0 + rr) * job.mat_ld + j] : 0.f;
-        const float4* src = reinterpret_cast<const float4*>(in_lds + jj * LD);
-#pragma unroll
-        for (int c4 = 0; c4 < Q / 4; ++c4) {
-          const float4 v = src[c4];
-#pragma unroll
-          for (int rr = 0; rr < RW; ++rr) {
-            acc[rr * Q + 4 * c4 + 0] += m[rr] * v.x;
-            acc[rr * Q + 4 * c4 + 1] += m[rr] * v.y;
-            acc[rr * Q + 4 * c4 + 2] += m[rr] * v.z;
-            acc[rr * Q + 4 * c4 + 3] += m[rr] * v.w;
+      for (int rr = 0; rr < SK_RW; ++rr) {
+        const int row = row0 + rr;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row < n) {
+          const float* src = mat + (int64_t)row * job.mat_ld + j;
+          if (vec && j + 3 < n) {
+            v = *reinterpret_cast<const float4*>(src);
+          } else {
+            v.x = src[0];
+            if (j + 1 < n) v.y = src[1];
+            if (j + 2 < n) v.z = src[2];
+            if (j + 3 < n) v.w = src[3];
           }
         }
+        m[rr] = v;
+      }
+#pragma unroll
+      for (int c = 0; c < Q; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(in_lds + c * SK_LD + jj);
+#pragma unroll
+        for (int rr = 0; rr < SK_RW; ++rr)
+          acc[rr * Q + c] += m[rr].x * x.x + m[rr].y * x.y + m[rr].z * x.z + m[rr].w * x.w;
       }
     }
   }
-  halve_reduce<64, 32>(acc, lane);
-  // lane l now holds value index l = rr * Q + c
-  const int rr = lane / Q, c = lane - rr * Q;
+  halve_reduce<CNT, 32>(acc, lane);
+  const int idx = lane / SHARE;
+  const int rr = idx / Q, c = idx - rr * Q;
   const int row = row0 + rr;
-  const bool valid = row < n && c < p.q;
+  const bool writer = (lane % SHARE) == 0;
+  const bool valid = writer && row < n && c < p.q;
   const float val = acc[0] * scale;
   if (valid) kb[(int64_t)row * p.kld + job.out_col + c] = val;
 
@@ -412,12 +434,15 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
     __syncthreads();
     if (!is_last) return;
     __threadfence();
-    if (threadIdx.x < ng) {
+    // every entry summed over the blocks' shares with a fixed thread
+    // assignment and reduction tree (deterministic)
+    for (int e = 0; e < ng; ++e) {
       double s = 0.0;
-      for (int i = 0; i < (int)gridDim.x; ++i)
-        s += __hip_atomic_load(&part[(int64_t)i * 16 + threadIdx.x], __ATOMIC_RELAXED,
+      for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
+        s += __hip_atomic_load(&part[(int64_t)i * 16 + e], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-      gsum[threadIdx.x] = s;
+      const double tot = block_sum<NT / 64>(s, red);
+      if (threadIdx.x == 0) gsum[e] = tot;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -453,6 +478,22 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
     else v = c1 * R[e] + alpha * R2[e];
     if (r == c) v += c0;
     G[e] = v;
+  }
+}
+
+// ---------------------------------------------------------------- conversion
+template <typename TI, typename TO>
+__global__ __launch_bounds__(NT) void convert_kernel(const TI* __restrict__ src, int64_t lds,
+                                                     int64_t ss, TO* __restrict__ dst,
+                                                     int64_t ldd, int64_t sd, int rows, int cols) {
+  const int b = blockIdx.y;
+  const TI* x = src + (int64_t)b * ss;
+  TO* y = dst + (int64_t)b * sd;
+  const int64_t total = (int64_t)rows * cols;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
+    y[(int64_t)r * ldd + c] = from_f32<TO>(to_f32(x[(int64_t)r * lds + c]));
   }
 }
 
@@ -548,8 +589,8 @@ hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hip
 }
 
 int skinny_blocks(int n, int q) {
-  const int rb = q <= 8 ? 32 : (q <= 16 ? 16 : 8);
-  return (n + rb - 1) / rb;
+  (void)q;
+  return (n + SK_RB - 1) / SK_RB;
 }
 
 hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
@@ -562,8 +603,8 @@ hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch,
     if (gram) hipLaunchKernelGGL((skinny_kernel<16, true>), grid, dim3(NT), 0, s, p);
     else hipLaunchKernelGGL((skinny_kernel<16, false>), grid, dim3(NT), 0, s, p);
   } else if (p.q <= 32) {
-    if (gram) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((skinny_kernel<32, false>), grid, dim3(NT), 0, s, p);
+    if (gram) hipLaunchKernelGGL((skinny_kernel<32, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((skinny_kernel<32, false>), grid, dim3(NT), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }
@@ -573,6 +614,21 @@ hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch,
 hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s) {
   dim3 grid(grid_for((int64_t)p.n * p.n, 2048), batch);
   hipLaunchKernelGGL(form_g_kernel, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert(const void* src, bool src_bf16, int64_t lds, int64_t ss, void* dst,
+                          bool dst_bf16, int64_t ldd, int64_t sd, int rows, int cols, int batch,
+                          hipStream_t s) {
+  dim3 grid(grid_for((int64_t)rows * cols, 4096), batch);
+  if (src_bf16 && !dst_bf16)
+    hipLaunchKernelGGL((convert_kernel<bf16_t, float>), grid, dim3(NT), 0, s,
+                       (const bf16_t*)src, lds, ss, (float*)dst, ldd, sd, rows, cols);
+  else if (!src_bf16 && dst_bf16)
+    hipLaunchKernelGGL((convert_kernel<float, bf16_t>), grid, dim3(NT), 0, s,
+                       (const float*)src, lds, ss, (bf16_t*)dst, ldd, sd, rows, cols);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -213,9 +213,13 @@ def parse_info(info_tensor):
     return np.frombuffer(raw, dtype=INFO_DTYPE)
 
 
-def shampoo_stats_update(G, L, R, beta, eps):
+def shampoo_stats_update(G, L, R, beta, eps, ws=None):
     """In place: L <- beta L + (1-beta) G G^T + eps I, R <- beta R + (1-beta) G^T G + eps I."""
     m, n, ldg, sg, batch = _mat(G)
+    if L is not None and L.dim() == 3:
+        batch = L.shape[0]
+    elif R is not None and R.dim() == 3:
+        batch = R.shape[0]
     if L is not None:
         _, _, ldl, sl, _ = _mat(L)
     else:
@@ -224,10 +228,14 @@ def shampoo_stats_update(G, L, R, beta, eps):
         _, _, ldr, sr, _ = _mat(R)
     else:
         ldr, sr = n, 0
+    dt = _dtype_code(G)
+    need = workspace_bytes(OP_STATS, m, n, batch, dt, None)
+    if need and (ws is None or ws.numel() < need):
+        ws = workspace(need, G.device)
     check(lib.pmx_shampoo_stats_update_batched(
-        handle(G.device.index), _ptr(G), _dtype_code(G), m, n, ldg, sg, _ptr(L), ldl, sl,
-        _ptr(R), ldr, sr, float(beta), float(eps), batch, None, 0, _stream(G)),
-        "shampoo_stats_update")
+        handle(G.device.index), _ptr(G), dt, m, n, ldg, sg, _ptr(L), ldl, sl,
+        _ptr(R), ldr, sr, float(beta), float(eps), batch, _ptr(ws) if need else None,
+        ws.numel() if need else 0, _stream(G)), "shampoo_stats_update")
     return L, R
 
 

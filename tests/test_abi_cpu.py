@@ -44,7 +44,7 @@ def test_host_only_calls():
     for code in range(6):
         assert pmx.lib.pmx_status_string(code)
     o = pmx.default_opts()
-    assert (o.degree, o.sketch_p, o.max_iter, o.accelerate) == (2, 8, 40, 1)
+    assert (o.degree, o.sketch_p, o.max_iter, o.accelerate) == (2, 8, 30, 1)
     assert math.isnan(o.alpha_lo) and math.isnan(o.alpha_hi)
     assert o.tol == pytest.approx(1e-6)
     assert pmx.lib.pmx_matfn_opts_default(None) == pmx.ERR_INVALID_VALUE

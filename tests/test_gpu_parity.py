@@ -69,7 +69,7 @@ def _run_root(env, A, p, **kw):
     return X.cpu().numpy(), XA.cpu().numpy(), pmx.parse_info(info)
 
 
-@pytest.mark.parametrize("n", [17, 64, 200])
+@pytest.mark.parametrize("n", [17, 64, 200, 517, 600])
 @pytest.mark.parametrize("p", [2, 4])
 def test_inv_root_matches_closed_form(env, n, p):
     _, pmx, _ = env
@@ -201,3 +201,72 @@ def test_argument_errors_enqueue_nothing(env):
     assert call(args(ws=ws.data_ptr() + 4)) == pmx.ERR_WORKSPACE
     assert call(args(ws=None)) == pmx.ERR_WORKSPACE
     torch.cuda.synchronize()
+
+
+def _bf16(torch, x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("m,n", [(256, 64), (64, 200), (300, 40), (130, 37)])
+def test_polar_bf16(env, m, n):
+    # bf16 iterates: orthogonality to the bf16 floor, U^T G close to the exact
+    # H = V Sigma V^T of the (bf16-valued) input, and U close to the exact factor
+    # for this well-conditioned Gaussian input
+    torch, pmx, dev = env
+    _say("polar bf16", m, n)
+    Gt = _bf16(torch, W.gaussian(m, n, 5 * m + n))
+    G = Gt.float().numpy().astype(np.float64)
+    U, info = pmx.polar(Gt.to(dev), opts=pmx.default_opts(tol=1e-2))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)[0]
+    assert U.dtype == torch.bfloat16
+    Un = U.float().cpu().numpy().astype(np.float64)
+    Up, H = cf.polar(G if m >= n else G.T)
+    if m < n:
+        Un_t, G_t = Un.T, G.T
+    else:
+        Un_t, G_t = Un, G
+    k = min(m, n)
+    assert int(inf["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+    assert np.linalg.norm(Un_t.T @ Un_t - np.eye(k)) / np.sqrt(k) < 1e-2
+    assert cf.rel_fro(Un_t.T @ G_t, H) < 3e-2
+    assert cf.rel_fro(Un_t, Up) < 3e-2
+
+
+def test_polar_bf16_iterations_follow_reference(env):
+    torch, pmx, dev = env
+    Gt = _bf16(torch, W.polar_batch(1, 512, 128, 9, smin=1e-2)[0][0])
+    _say("polar bf16 trace")
+    U, info = pmx.polar(Gt.to(dev), opts=pmx.default_opts(tol=1e-2, seed=3))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)[0]
+    _, ref = prism.polar(Gt.float().numpy().astype(np.float64), tol=1e-2,
+                         sketch_fn=prism.make_sketch_fn(3, b=0, p=8))
+    st = ref["stages"][0]
+    assert abs(int(inf["iters"][0]) - st.iters) <= 1
+    for kk in range(min(int(inf["iters"][0]), st.iters)):
+        if st.r[kk] >= 3e-2:
+            assert abs(inf["alpha"][0][kk] - st.alpha[kk]) < 2e-2, kk
+
+
+@pytest.mark.parametrize("m,n", [(64, 96), (33, 17)])
+def test_stats_and_apply_bf16(env, m, n):
+    torch, pmx, dev = env
+    _say("stats/apply bf16", m, n)
+    Gt = _bf16(torch, W.gaussian(m, n, m * n))
+    G = Gt.float().numpy().astype(np.float64)
+    L = torch.eye(m, device=dev) * 1e-2
+    R = torch.eye(n, device=dev) * 1e-2
+    pmx.shampoo_stats_update(Gt.to(dev), L, R, 0.9, 1e-3)
+    Lr, Rr = cf.stats_update(1e-2 * np.eye(m), 1e-2 * np.eye(n), G, 0.9, 1e-3)
+    torch.cuda.synchronize()
+    assert cf.rel_fro(L.cpu().numpy(), Lr) < 1e-5
+    assert cf.rel_fro(R.cpu().numpy(), Rr) < 1e-5
+    rng = np.random.default_rng(m)
+    Li = rng.standard_normal((m, m)).astype(np.float32)
+    Ri = rng.standard_normal((n, n)).astype(np.float32)
+    P = pmx.precond_apply(torch.from_numpy(Li).to(dev), Gt.to(dev), torch.from_numpy(Ri).to(dev))
+    torch.cuda.synchronize()
+    assert P.dtype == torch.bfloat16
+    # fp32 products, one bf16 rounding of the output (relative 2^-8)
+    assert cf.rel_fro(P.float().cpu().numpy(), cf.precond_apply(Li, G, Ri)) < 5e-3
