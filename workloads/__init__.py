@@ -144,3 +144,19 @@ def mp_square(n=10000, m=20000, seed=501, block=2000):
     A[np.diag_indices(n)] += 1e-4
     A = 0.5 * (A + A.T)
     return A.astype(np.float32)
+
+
+def mp_square_device(n=10000, m=20000, seed=501, device="cuda"):
+    """The 10^4 Marchenko-Pastur workload built on the GPU (torch, seeded):
+    W ~ N(0, 1) fp32 (n x m), A = W W^T / m + 1e-4 I formed in fp64, cast to
+    fp32.  Returns a torch fp32 tensor on `device`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    W = torch.randn(n, m, generator=g, device=device, dtype=torch.float32).double()
+    A = (W @ W.T) / m
+    del W
+    A.diagonal().add_(1e-4)
+    A = 0.5 * (A + A.T)
+    return A.float()
+
