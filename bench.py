@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--max-iter", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--workload", default="shampoo_1024x4096",
+                    choices=["shampoo_1024x4096", "spd_64", "blocks_64x512",
+                             "muon_32x4096x1024", "mp_10000"])
     return ap.parse_args()
 
 
@@ -66,12 +69,115 @@ def cpu_baseline(G, L0, R0, beta, eps):
                 step_s=round(t4 - t0, 2))
 
 
+def timed(torch, fn, steps, warmup):
+    """Mean ms of `fn` over `steps` calls after `warmup` calls (HIP events on
+    the current stream, synchronised on both sides)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def other_workload(args):
+    """Secondary workloads (one JSON line each; the headline is the Shampoo layer)."""
+    import torch
+
+    import workloads as W
+    from preconditioned_optimizer_matrix_amd import pmx
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    opts = pmx.default_opts(max_iter=args.max_iter)
+    taylor = pmx.default_opts(max_iter=60, accelerate=0)
+    out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None}
+    wl = args.workload
+    if wl == "spd_64":
+        c = W.spd_64()
+        A = torch.from_numpy(c["A"]).to(dev)
+        G = torch.from_numpy(c["G"]).to(dev)
+        res = {}
+        for name, fn in (("inv_sqrt_p2", lambda o: pmx.inv_root(A, 2, opts=o)),
+                         ("inv_root_p4", lambda o: pmx.inv_root(A, 4, opts=o)),
+                         ("polar_64x32", lambda o: pmx.polar(G, opts=o))):
+            ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
+            info = pmx.parse_info(fn(opts)[-1])[0]
+            tinfo = pmx.parse_info(fn(taylor)[-1])[0]
+            res[name] = {"us": round(ms * 1e3, 1), "gemms": int(info["gemms"]),
+                         "gemms_taylor": int(tinfo["gemms"]),
+                         "iters": [int(x) for x in info["iters"]]}
+        out.update(metric="us per matrix function (n=64)", value=res["inv_root_p4"]["us"],
+                   unit="us", dtype="f32", config={"workload": wl}, calls=res)
+    elif wl == "blocks_64x512":
+        c = W.blocks_64x512()
+        A = torch.from_numpy(c["A"]).to(dev)
+        ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 64, pmx.F32, opts), dev)
+        X = torch.empty_like(A)
+        info = pmx.new_info(64, dev)
+        fn = lambda o: pmx.inv_root(A, 4, opts=o, aux=False, out=X, info=info, ws=ws)
+        ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
+        inf = pmx.parse_info(info)
+        gemms = int(inf["gemms"].sum())
+        fn(taylor)
+        tg = int(pmx.parse_info(info)["gemms"].sum())
+        tf = gemms * 2.0 * 512 ** 3 / (ms * 1e-3) / 1e12
+        out.update(metric="ms per batched inverse-4th-root (64 x 512)", value=round(ms, 3),
+                   unit="ms", dtype="f32", config={"workload": wl},
+                   gemms_total=gemms, gemms_taylor_total=tg, mfma_tflops=round(tf, 2),
+                   mfma_frac=round(tf / PEAK_FP32_MFMA, 4))
+    elif wl == "muon_32x4096x1024":
+        c = W.muon_32x4096x1024()
+        G = torch.from_numpy(c["G_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        o = pmx.default_opts(max_iter=args.max_iter, tol=c["tol"])
+        ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_POLAR, 4096, 1024, 32, pmx.BF16, o), dev)
+        U = torch.empty_like(G)
+        info = pmx.new_info(32, dev)
+        fn = lambda oo: pmx.polar(G, opts=oo, out=U, info=info, ws=ws)
+        ms = timed(torch, lambda: fn(o), args.steps, args.warmup)
+        inf = pmx.parse_info(info)
+        it = int(inf["iters"][:, 0].max())
+        fn(pmx.default_opts(max_iter=60, tol=c["tol"], accelerate=0))
+        tit = int(pmx.parse_info(info)["iters"][:, 0].max())
+        # per update: X^T X (4096 x 1024 x 1024), R^2 (1024^3), X g (4096 x 1024 x 1024)
+        flops = 32 * (2.0 * 4096 * 1024 * 1024 * (2 * it + 1) + 2.0 * 1024 ** 3 * it)
+        tf = flops / (ms * 1e-3) / 1e12
+        out.update(metric="ms per batched polar factor (32 x 4096 x 1024, bf16)",
+                   value=round(ms, 3), unit="ms", dtype="bf16", config={"workload": wl},
+                   iters=it, iters_taylor=tit, gemms_per_matrix=int(inf["gemms"][0]),
+                   mfma_tflops=round(tf, 1), mfma_frac=round(tf / 2516.6, 4))
+    elif wl == "mp_10000":
+        A = W.mp_square_device(device=dev)
+        ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, 10000, 10000, 1, pmx.F32, opts), dev)
+        X, XA = torch.empty_like(A), torch.empty_like(A)
+        info = pmx.new_info(1, dev)
+        fn = lambda o: pmx.inv_root(A, 2, opts=o, out=X, out_aux=XA, info=info, ws=ws)
+        ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
+        inf = pmx.parse_info(info)[0]
+        gemms = int(inf["gemms"])
+        fn(taylor)
+        tg = int(pmx.parse_info(info)[0]["gemms"])
+        tf = gemms * 2.0 * 1e12 / (ms * 1e-3) / 1e12
+        out.update(metric="ms per square root (n=10^4, A^1/2 and A^-1/2)", value=round(ms, 2),
+                   unit="ms", dtype="f32", config={"workload": wl}, gemms=gemms,
+                   gemms_taylor=tg, gemm_ratio_taylor_over_prism=round(tg / gemms, 3),
+                   iters=int(inf["iters"][0]), mfma_tflops=round(tf, 2),
+                   mfma_frac=round(tf / PEAK_FP32_MFMA, 4))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: every GPU box here has one GPU, and the path "
               "has no multi-GPU implementation (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "shampoo_1024x4096":
+        return other_workload(args)
     import torch
 
     import workloads as W
@@ -128,6 +234,12 @@ def main():
         % (ms_step, r_ms, gemmsR, gemmsL, list(iR["iters"]), list(iL["iters"]),
            pmx.STATUS_NAMES[int(iR["status"])], pmx.STATUS_NAMES[int(iL["status"])]))
 
+    # ablation: the same R^-1/4 with the Taylor coefficient (classical Newton-Schulz)
+    infoT = pmx.new_info(1, dev)
+    pmx.inv_root(R, 4, opts=pmx.default_opts(max_iter=60, accelerate=0), aux=False,
+                 out=torch.empty_like(R), info=infoT, ws=wsR)
+    gemmsR_taylor = int(pmx.parse_info(infoT)[0]["gemms"])
+
     # property check at full size: || X^4 R e_j - e_j || on sampled columns (fp64)
     cols = torch.arange(0, n, n // 8, device=dev)
     E = torch.zeros(n, len(cols), dtype=torch.float64, device=dev)
@@ -177,7 +289,7 @@ def main():
                    "warmup_updates": 9, "degree": 2, "sketch_p": 8, "tol": 1e-6,
                    "max_iter": args.max_iter,
                    "step": "restore L,R; stats update; L^-1/4; R^-1/4; apply"},
-        "gemms_to_converge": {"R": gemmsR, "L": gemmsL},
+        "gemms_to_converge": {"R": gemmsR, "L": gemmsL, "R_taylor": gemmsR_taylor},
         "iters": {"R": [int(x) for x in iR["iters"]], "L": [int(x) for x in iL["iters"]]},
         "status": {"R": pmx.STATUS_NAMES[int(iR["status"])],
                    "L": pmx.STATUS_NAMES[int(iL["status"])]},

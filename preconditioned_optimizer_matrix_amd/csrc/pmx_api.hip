@@ -210,7 +210,7 @@ IterCfg make_cfg(const pmx_matfn_opts& o, int n, pmx_matfn_info* info) {
 
 // ------------------------------------------------------------------ workspace
 struct IterLayout {
-  size_t ctrl, partials, gram, bufs[6], kbuf, total;
+  size_t ctrl, partials, gram, bufs[10], kbuf, total;
   int64_t buf_stride, kstride, kld, pstride, gstride;
 };
 
@@ -231,7 +231,7 @@ IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, i
   const int64_t big = (int64_t)rows * cols, small = (int64_t)cols * cols;
   (void)big_elem;
   L.buf_stride = ((std::max(big, small) + 63) / 64) * 64;  // elements (fp32 slots)
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < 10; ++i) {
     L.bufs[i] = 0;
     if (i < nbig + nsmall) {
       L.bufs[i] = off;
@@ -304,12 +304,12 @@ SketchJob make_sketch(const IterLayout& L, void* ws, const IterCfg& cfg, int n, 
 hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
                                    const pmx_matfn_opts& o, const IterCfg& cfg,
                                    const AlphaCoef& coef, int n, int batch, float* R,
-                                   float* R2, bool bf16_power = false) {
+                                   float* R2, bool power = true) {
   Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
   float* kbuf = at<float>(ws, L.kbuf);
   const int d = o.degree, pp = o.sketch_p;
   hipError_t e;
-  if (d == 2) {
+  if (d == 2 && power) {
     GemmParams g = gemm_base(q.h, n, n, n, batch);
     g.prob[0].a = {R, n, L.buf_stride, nullptr, 0};
     g.prob[0].b = {R, n, L.buf_stride, nullptr, 0};
@@ -317,13 +317,8 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     g.prob[0].ldc = n;
     g.prob[0].stride_c = L.buf_stride;
     g.ctrl = ctrl;
-    if (bf16_power) {
-      g.vec = (n % 4 == 0 && L.buf_stride % 4 == 0) ? 1 : 0;
-      e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_bf16(g, ROLE_POWER, q.s); });
-    } else {
-      set_vec(g);
-      e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
-    }
+    set_vec(g);
+    e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
     if (e != hipSuccess) return e;
   }
   if (!o.accelerate) return hipSuccess;
@@ -475,9 +470,12 @@ pmx_status pmx_trace_collect(pmx_handle h, double* ms, int64_t* launches) {
 static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
   return iter_layout(n, n, batch, o, 4, 2, sizeof(float)).total;
 }
-static size_t polar_ws(int m, int n, int batch, const pmx_matfn_opts& o) {
+// fp32: X ping-pong, R, R^2.  bf16: X and X^T ping-pong, R, R^2 (fp32), and
+// the bf16 operands R, R^T, g^T.
+static int polar_bufs(pmx_dtype dt) { return dt == PMX_BF16 ? 9 : 4; }
+static size_t polar_ws(int m, int n, int batch, const pmx_matfn_opts& o, pmx_dtype dt) {
   const int rows = std::max(m, n), cols = std::min(m, n);
-  return iter_layout(rows, cols, batch, o, 2, 2, sizeof(float)).total;
+  return iter_layout(rows, cols, batch, o, polar_bufs(dt), 0, sizeof(float)).total;
 }
 static size_t apply_ws(int m, int n, int batch, pmx_dtype dt) {
   // fp32: T = L^{-1/4} G; bf16: G in fp32, T and P in fp32
@@ -511,7 +509,7 @@ pmx_status pmx_workspace_size(pmx_handle h, pmx_op op, int m, int n, int batch,
     case PMX_OP_POLAR:
       if (m < 1 || m > kMaxN) return PMX_ERR_INVALID_VALUE;
       if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
-      *bytes = polar_ws(m, n, batch, o);
+      *bytes = polar_ws(m, n, batch, o, dtype);
       return PMX_OK;
   }
   return PMX_ERR_INVALID_VALUE;
@@ -773,7 +771,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const bool bf = dtype == PMX_BF16;
   const int rows = std::max(m, n), cols = std::min(m, n);
   const bool tr = m < n;
-  const IterLayout Lw = iter_layout(rows, cols, batch, o, 2, 2, sizeof(float));
+  const IterLayout Lw = iter_layout(rows, cols, batch, o, polar_bufs(dtype), 0, sizeof(float));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
   const Extent eg = extent_of(G, m, n, ldg, sg, batch, bf ? 2 : 4);
@@ -799,6 +797,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const AlphaCoef coef = make_coef(o.degree);
   const int d = o.degree;
   const bool acc = o.accelerate != 0;
+  const int64_t bs = Lw.buf_stride;
 
   PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
@@ -809,64 +808,135 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   pi.ldg = ldg;
   pi.g_stride = sg;
   pi.x = Xb[0];
-  pi.x_stride = Lw.buf_stride;
+  pi.x_stride = bs;
   pi.rows = rows;
   pi.cols = cols;
   pi.transpose = tr ? 1 : 0;
   pi.ctrl = ctrl;
   PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_init(pi, bf, batch, q.s); }));
-  // bf16 operands load 8 elements at a time: every bf16 leading dimension and
-  // stride must be a multiple of 8, every fp32 one a multiple of 4
-  const bool vec_bf = (cols % 8 == 0) && (Lw.buf_stride % 8 == 0);
 
-  auto residual = [&](float* Xc, int products, int count, int k_next) {
-    GemmParams r = gemm_base(q.h, cols, cols, rows, batch);
-    r.ctrl = ctrl;
-    r.prob[0].a = {Xc, cols, Lw.buf_stride, nullptr, 0};
-    r.prob[0].b = {Xc, cols, Lw.buf_stride, nullptr, 0};
-    r.prob[0].c = Rb;
-    r.prob[0].ldc = cols;
-    r.prob[0].stride_c = Lw.buf_stride;
-    r.partials = partials;
-    r.partial_stride = Lw.pstride;
-    r.products = products;
-    r.count_update = count;
-    r.cfg = cfg;
-    r.sketch = make_sketch(Lw, ws, cfg, cols, k_next, 0, acc && k_next < o.max_iter);
-    if (bf) {
-      r.vec = vec_bf ? 1 : 0;
-      return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_bf16(r, ROLE_RESID, q.s); });
-    }
-    set_vec(r);
-    return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
-  };
-  PMX_TRY(residual(Xb[0], 1, 0, 0));
-  for (int k = 0; k < o.max_iter; ++k) {
-    PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, bf));
-    const int cur = k & 1, nxt = cur ^ 1;
-    GemmParams u = gemm_base(q.h, rows, cols, cols, batch);
-    u.ctrl = ctrl;
-    u.degree = d;
-    u.c0 = (float)taylor(0);
-    u.c1 = (float)taylor(1);
-    u.prob[0].a = {Xb[cur], cols, Lw.buf_stride, nullptr, 0};
-    u.prob[0].b = {Rb, cols, Lw.buf_stride, R2b, 1};
-    u.prob[0].c = Xb[nxt];
-    u.prob[0].ldc = cols;
-    u.prob[0].stride_c = Lw.buf_stride;
-    if (bf) {
-      u.vec = vec_bf ? 1 : 0;
-      PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_bf16(u, ROLE_UPDATE, q.s); }));
-    } else {
+  if (!bf) {
+    auto residual = [&](float* Xc, int products, int count, int k_next) {
+      GemmParams r = gemm_base(q.h, cols, cols, rows, batch);
+      r.ctrl = ctrl;
+      r.prob[0].a = {Xc, cols, bs, nullptr, 0};
+      r.prob[0].b = {Xc, cols, bs, nullptr, 0};
+      r.prob[0].c = Rb;
+      r.prob[0].ldc = cols;
+      r.prob[0].stride_c = bs;
+      r.partials = partials;
+      r.partial_stride = Lw.pstride;
+      r.products = products;
+      r.count_update = count;
+      r.cfg = cfg;
+      r.sketch = make_sketch(Lw, ws, cfg, cols, k_next, 0, acc && k_next < o.max_iter);
+      set_vec(r);
+      return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
+    };
+    PMX_TRY(residual(Xb[0], 1, 0, 0));
+    for (int k = 0; k < o.max_iter; ++k) {
+      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b));
+      const int cur = k & 1, nxt = cur ^ 1;
+      GemmParams u = gemm_base(q.h, rows, cols, cols, batch);
+      u.ctrl = ctrl;
+      u.degree = d;
+      u.c0 = (float)taylor(0);
+      u.c1 = (float)taylor(1);
+      u.prob[0].a = {Xb[cur], cols, bs, nullptr, 0};
+      u.prob[0].b = {Rb, cols, bs, R2b, 1};
+      u.prob[0].c = Xb[nxt];
+      u.prob[0].ldc = cols;
+      u.prob[0].stride_c = bs;
       set_vec(u);
       PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
+      PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1, k + 1));
     }
-    PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1, k + 1));
+  } else {
+    // bf16: every product is k-contiguous x k-contiguous (see pmx_gemm_bf16.hip)
+    float* Xt[2] = {at<float>(ws, Lw.bufs[4]), at<float>(ws, Lw.bufs[5])};
+    float* Rh = at<float>(ws, Lw.bufs[6]);   // R in bf16
+    float* Rht = at<float>(ws, Lw.bufs[7]);  // R^T in bf16
+    float* Gt = at<float>(ws, Lw.bufs[8]);   // g^T in bf16
+    const bool vec = (cols % 8 == 0) && (rows % 8 == 0) && (bs % 8 == 0);
+    auto xpose = [&](const void* a, bool a_bf16, const float* a2, int poly, int r_, int c_,
+                     void* out_t, void* out_n, Ctrl* gate) {
+      XposeParams x;
+      memset(&x, 0, sizeof(x));
+      x.a = a;
+      x.a2 = a2;
+      x.a_bf16 = a_bf16 ? 1 : 0;
+      x.lda = c_;
+      x.sa = bs;
+      x.out_t = (uint16_t*)out_t;
+      x.ldt = r_;
+      x.st = bs;
+      x.out_n = (uint16_t*)out_n;
+      x.ldn = c_;
+      x.sn = bs;
+      x.rows = r_;
+      x.cols = c_;
+      x.poly = poly;
+      x.degree = d;
+      x.c0 = (float)taylor(0);
+      x.c1 = (float)taylor(1);
+      x.ctrl = gate;
+      return q.run(PMX_KC_OTHER, [&] { return launch_xpose(x, batch, q.s); });
+    };
+    auto residual = [&](float* Xtc, int products, int count, int k_next) {
+      GemmParams r = gemm_base(q.h, cols, cols, rows, batch);
+      r.ctrl = ctrl;
+      r.prob[0].a = {Xtc, rows, bs, nullptr, 0};
+      r.prob[0].b = {Xtc, rows, bs, nullptr, 0};
+      r.prob[0].c = Rb;
+      r.prob[0].ldc = cols;
+      r.prob[0].stride_c = bs;
+      r.partials = partials;
+      r.partial_stride = Lw.pstride;
+      r.products = products;
+      r.count_update = count;
+      r.cfg = cfg;
+      r.sketch = make_sketch(Lw, ws, cfg, cols, k_next, 0, acc && k_next < o.max_iter);
+      r.vec = vec ? 1 : 0;
+      return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_bf16(r, ROLE_RESID, q.s); });
+    };
+    PMX_TRY(xpose(Xb[0], true, nullptr, 0, rows, cols, Xt[0], nullptr, ctrl));
+    PMX_TRY(residual(Xt[0], 1, 0, 0));
+    for (int k = 0; k < o.max_iter; ++k) {
+      if (d == 2) {
+        PMX_TRY(xpose(Rb, false, nullptr, 0, cols, cols, Rht, Rh, ctrl));
+        GemmParams g = gemm_base(q.h, cols, cols, cols, batch);
+        g.ctrl = ctrl;
+        g.prob[0].a = {Rh, cols, bs, nullptr, 0};
+        g.prob[0].b = {Rht, cols, bs, nullptr, 0};
+        g.prob[0].c = R2b;
+        g.prob[0].ldc = cols;
+        g.prob[0].stride_c = bs;
+        g.vec = vec ? 1 : 0;
+        PMX_TRY(q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_bf16(g, ROLE_POWER, q.s); }));
+      }
+      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, false));
+      PMX_TRY(xpose(Rb, false, R2b, 1, cols, cols, Gt, nullptr, ctrl));
+      const int cur = k & 1, nxt = cur ^ 1;
+      GemmParams u = gemm_base(q.h, rows, cols, cols, batch);
+      u.ctrl = ctrl;
+      u.nprob = 1;
+      u.prob[0].a = {Xb[cur], cols, bs, nullptr, 0};
+      u.prob[0].b = {Gt, cols, bs, nullptr, 0};
+      u.prob[0].c = Xb[nxt];
+      u.prob[0].ldc = cols;
+      u.prob[0].stride_c = bs;
+      u.prob[1].c = Xt[nxt];  // transposed copy of the new iterate
+      u.prob[1].ldc = rows;
+      u.prob[1].stride_c = bs;
+      u.vec = vec ? 1 : 0;
+      PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_bf16(u, ROLE_UPDATE, q.s); }));
+      PMX_TRY(residual(Xt[nxt], (d - 1) + 1 + 1, 1, k + 1));
+    }
   }
   PolarFinishParams fp;
   fp.xbuf[0] = Xb[0];
   fp.xbuf[1] = Xb[1];
-  fp.buf_stride = Lw.buf_stride;
+  fp.buf_stride = bs;
   fp.u = U;
   fp.ldu = ldu;
   fp.u_stride = su;

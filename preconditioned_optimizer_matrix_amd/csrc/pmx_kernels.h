@@ -91,6 +91,24 @@ struct FormGParams {
   Ctrl* ctrl;
 };
 
+// 64 x 64 tile transpose to bf16: out_t[j][i] = f(in[i][j]) (cols x rows) and
+// optionally out_n[i][j] = f(in[i][j]); f is the identity or, with `poly`, the
+// PRISM polynomial c0 [i == j] + c1 R + alpha R2 (d = 2) / c0 [i == j] + alpha R.
+struct XposeParams {
+  const void* a;
+  const float* a2;
+  int a_bf16;
+  int64_t lda, sa;
+  uint16_t* out_t;
+  int64_t ldt, st;
+  uint16_t* out_n;
+  int64_t ldn, sn;
+  int rows, cols;
+  int poly, degree;
+  float c0, c1;
+  Ctrl* ctrl;  // null: unconditional; else skipped when the matrix is not running
+};
+
 struct RootFinishParams {
   float* ybuf[2];
   float* zbuf[2];
@@ -128,6 +146,7 @@ hipError_t launch_convert(const void* src, bool src_bf16, int64_t lds, int64_t s
                           bool dst_bf16, int64_t ldd, int64_t sd, int rows, int cols, int batch,
                           hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, int role, hipStream_t s);
+hipError_t launch_xpose(const XposeParams& p, int batch, hipStream_t s);
 hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t s);
 hipError_t launch_polar_finish(const PolarFinishParams& p, bool bf16, int batch, hipStream_t s);
 

@@ -56,10 +56,8 @@ __global__ __launch_bounds__(NT) void fro_scale_kernel(const T* __restrict__ X, 
   const int b = blockIdx.y;
   const T* x = X + (int64_t)b * stride;
   double acc = 0.0;
-  const int64_t total = (int64_t)rows * cols;
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * NT) {
-    const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
+  for (int r = blockIdx.x; r < rows; r += gridDim.x)
+  for (int c = threadIdx.x; c < cols; c += NT) {
     const double v = (double)to_f32(x[(int64_t)r * ld + c]);
     acc += v * v;
   }
@@ -114,10 +112,9 @@ __global__ __launch_bounds__(NT) void sqrt_stage_init_kernel(StageInitParams p) 
   float* y0 = p.ybuf[0] + (int64_t)b * p.buf_stride;
   float* R = p.r + (int64_t)b * p.buf_stride;
   double acc = 0.0;
-  const int64_t total = (int64_t)n * n;
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * NT) {
-    const int r = (int)(e / n), c = (int)(e - (int64_t)r * n);
+  for (int r = blockIdx.x; r < n; r += gridDim.x)
+  for (int c = threadIdx.x; c < n; c += NT) {
+    const int64_t e = (int64_t)r * n + c;
     const float y = src[(int64_t)r * sld + c] * fs;
     y0[e] = y;
     const float rv = (r == c ? 1.f : 0.f) - y;
@@ -148,10 +145,9 @@ __global__ __launch_bounds__(NT) void polar_init_kernel(PolarInitParams p) {
   const T* g = reinterpret_cast<const T*>(p.g) + (int64_t)b * p.g_stride;
   T* x = reinterpret_cast<T*>(p.x) + (int64_t)b * p.x_stride;
   const float fs = (float)(1.0 / cb->c);
-  const int64_t total = (int64_t)p.rows * p.cols;  // X is rows x cols (rows >= cols)
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * NT) {
-    const int r = (int)(e / p.cols), c = (int)(e - (int64_t)r * p.cols);
+  for (int r = blockIdx.x; r < p.rows; r += gridDim.x)
+  for (int c = threadIdx.x; c < p.cols; c += NT) {
+    const int64_t e = (int64_t)r * p.cols + c;
     const float v = p.transpose ? to_f32(g[(int64_t)c * p.ldg + r]) : to_f32(g[(int64_t)r * p.ldg + c]);
     x[e] = from_f32<T>(v * fs);
   }
@@ -358,8 +354,9 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   for (int j0 = 0; j0 < n; j0 += SK_CH) {
     __syncthreads();
     // stage In[j0 .. j0 + 512)[0 .. Q) column-major (zero beyond n and q)
+    // consecutive threads read consecutive columns of one In row (coalesced)
     for (int idx = threadIdx.x; idx < SK_CH * Q; idx += NT) {
-      const int c = idx / SK_CH, jj = idx - c * SK_CH;
+      const int jj = idx / Q, c = idx - jj * Q;
       float v = 0.f;
       if (j0 + jj < n && c < p.q) v = kb[(int64_t)(j0 + jj) * p.kld + job.in_col + c];
       in_lds[c * SK_LD + jj] = v;
@@ -469,10 +466,9 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   const float* R2 = p.r2 ? p.r2 + (int64_t)b * p.stride : nullptr;
   float* G = p.dst + (int64_t)b * p.stride;
   const float c0 = p.c0, c1 = p.c1;
-  const int64_t total = (int64_t)n * n;
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * NT) {
-    const int r = (int)(e / n), c = (int)(e - (int64_t)r * n);
+  for (int r = blockIdx.x; r < n; r += gridDim.x)
+  for (int c = threadIdx.x; c < n; c += NT) {
+    const int64_t e = (int64_t)r * n + c;
     float v;
     if (p.degree == 1) v = alpha * R[e];
     else v = c1 * R[e] + alpha * R2[e];
@@ -489,11 +485,51 @@ __global__ __launch_bounds__(NT) void convert_kernel(const TI* __restrict__ src,
   const int b = blockIdx.y;
   const TI* x = src + (int64_t)b * ss;
   TO* y = dst + (int64_t)b * sd;
-  const int64_t total = (int64_t)rows * cols;
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * NT) {
-    const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
+  for (int r = blockIdx.x; r < rows; r += gridDim.x)
+  for (int c = threadIdx.x; c < cols; c += NT) {
     y[(int64_t)r * ldd + c] = from_f32<TO>(to_f32(x[(int64_t)r * lds + c]));
+  }
+}
+
+// ---------------------------------------------------------------- tile transpose
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) { return from_f32<bf16_t>(x).bits; }
+
+__global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
+  const int b = blockIdx.z;
+  float alpha = 0.f;
+  if (p.ctrl) {
+    if (load_status(p.ctrl + b) != PMX_RUNNING) return;
+    alpha = (float)p.ctrl[b].alpha;
+  }
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const float* af = reinterpret_cast<const float*>(p.a) + (int64_t)b * p.sa;
+  const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.a) + (int64_t)b * p.sa;
+  const float* a2 = p.a2 ? p.a2 + (int64_t)b * p.sa : nullptr;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = ty + 4 * i, gr = r0 + r, gc = c0 + tx;
+    float v = 0.f;
+    if (gr < p.rows && gc < p.cols) {
+      const int64_t off = (int64_t)gr * p.lda + gc;
+      v = p.a_bf16 ? __uint_as_float((uint32_t)ab[off] << 16) : af[off];
+      if (p.poly) {
+        float g = p.degree == 2 ? p.c1 * v + alpha * a2[off] : alpha * v;
+        if (gr == gc) g += p.c0;
+        v = g;
+      }
+      if (p.out_n) p.out_n[(int64_t)b * p.sn + (int64_t)gr * p.ldn + gc] = to_bf16_bits(v);
+    }
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+  if (!p.out_t) return;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int c = ty + 4 * i, gc = c0 + c, gr = r0 + tx;
+    if (gc < p.cols && gr < p.rows)
+      p.out_t[(int64_t)b * p.st + (int64_t)gc * p.ldt + gr] = to_bf16_bits(tile[tx][c]);
   }
 }
 
@@ -513,10 +549,9 @@ __global__ __launch_bounds__(NT) void root_finish_kernel(RootFinishParams p) {
   float* X = p.x + (int64_t)b * p.x_stride;
   float* XA = p.aux ? p.aux + (int64_t)b * p.aux_stride : nullptr;
   const int n = p.n;
-  const int64_t total = (int64_t)n * n;
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * NT) {
-    const int r = (int)(e / n), col = (int)(e - (int64_t)r * n);
+  for (int r = blockIdx.x; r < n; r += gridDim.x)
+  for (int col = threadIdx.x; col < n; col += NT) {
+    const int64_t e = (int64_t)r * n + col;
     float zx, ya;
     if (bad) {
       zx = NAN;
@@ -539,10 +574,9 @@ __global__ __launch_bounds__(NT) void polar_finish_kernel(PolarFinishParams p) {
   const int it = cb->iter;
   const T* X = reinterpret_cast<const T*>(p.xbuf[it & 1]) + (int64_t)b * p.buf_stride;
   T* U = reinterpret_cast<T*>(p.u) + (int64_t)b * p.u_stride;
-  const int64_t total = (int64_t)p.rows * p.cols;  // X is rows x cols
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * NT) {
-    const int r = (int)(e / p.cols), c = (int)(e - (int64_t)r * p.cols);
+  for (int r = blockIdx.x; r < p.rows; r += gridDim.x)
+  for (int c = threadIdx.x; c < p.cols; c += NT) {
+    const int64_t e = (int64_t)r * p.cols + c;
     const T v = bad ? from_f32<T>(NAN) : X[e];
     if (p.transpose) U[(int64_t)c * p.ldu + r] = v;
     else U[(int64_t)r * p.ldu + c] = v;
@@ -550,11 +584,10 @@ __global__ __launch_bounds__(NT) void polar_finish_kernel(PolarFinishParams p) {
 }
 
 // ---------------------------------------------------------------- launchers
-static int grid_for(int64_t elems, int cap) {
-  int64_t g = (elems + NT * 4 - 1) / (NT * 4);
-  if (g < 1) g = 1;
-  if (g > cap) g = cap;
-  return (int)g;
+// Row-parallel elementwise kernels: one block per row (grid-stride beyond cap).
+static int grid_rows(int rows, int cap) {
+  int g = rows < cap ? rows : cap;
+  return g < 1 ? 1 : g;
 }
 
 hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStream_t s) {
@@ -565,7 +598,7 @@ hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStr
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,
                             int64_t pstride, pmx_matfn_info* info, hipStream_t s) {
-  dim3 grid(grid_for((int64_t)rows * cols, kPartialsPerMatrix), batch);
+  dim3 grid(grid_rows(rows, kPartialsPerMatrix), batch);
   if (bf16)
     hipLaunchKernelGGL(fro_scale_kernel<bf16_t>, grid, dim3(NT), 0, s,
                        (const bf16_t*)x, rows, cols, ld, stride, ctrl, partials, pstride, info);
@@ -576,13 +609,13 @@ hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_
 }
 
 hipError_t launch_sqrt_stage_init(const StageInitParams& p, int batch, hipStream_t s) {
-  dim3 grid(grid_for((int64_t)p.n * p.n, kPartialsPerMatrix), batch);
+  dim3 grid(grid_rows(p.n, kPartialsPerMatrix), batch);
   hipLaunchKernelGGL(sqrt_stage_init_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hipStream_t s) {
-  dim3 grid(grid_for((int64_t)p.rows * p.cols, 2048), batch);
+  dim3 grid(grid_rows(p.rows, 2048), batch);
   if (bf16) hipLaunchKernelGGL(polar_init_kernel<bf16_t>, grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL(polar_init_kernel<float>, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
@@ -612,7 +645,7 @@ hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch,
 }
 
 hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s) {
-  dim3 grid(grid_for((int64_t)p.n * p.n, 2048), batch);
+  dim3 grid(grid_rows(p.n, 2048), batch);
   hipLaunchKernelGGL(form_g_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
@@ -620,7 +653,7 @@ hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s) {
 hipError_t launch_convert(const void* src, bool src_bf16, int64_t lds, int64_t ss, void* dst,
                           bool dst_bf16, int64_t ldd, int64_t sd, int rows, int cols, int batch,
                           hipStream_t s) {
-  dim3 grid(grid_for((int64_t)rows * cols, 4096), batch);
+  dim3 grid(grid_rows(rows, 4096), batch);
   if (src_bf16 && !dst_bf16)
     hipLaunchKernelGGL((convert_kernel<bf16_t, float>), grid, dim3(NT), 0, s,
                        (const bf16_t*)src, lds, ss, (float*)dst, ldd, sd, rows, cols);
@@ -632,14 +665,20 @@ hipError_t launch_convert(const void* src, bool src_bf16, int64_t lds, int64_t s
   return hipGetLastError();
 }
 
+hipError_t launch_xpose(const XposeParams& p, int batch, hipStream_t s) {
+  dim3 grid((p.cols + 63) / 64, (p.rows + 63) / 64, batch);
+  hipLaunchKernelGGL(xpose_kernel, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t s) {
-  dim3 grid(grid_for((int64_t)p.n * p.n, 2048), batch);
+  dim3 grid(grid_rows(p.n, 2048), batch);
   hipLaunchKernelGGL(root_finish_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_polar_finish(const PolarFinishParams& p, bool bf16, int batch, hipStream_t s) {
-  dim3 grid(grid_for((int64_t)p.rows * p.cols, 2048), batch);
+  dim3 grid(grid_rows(p.rows, 2048), batch);
   if (bf16) hipLaunchKernelGGL(polar_finish_kernel<bf16_t>, grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL(polar_finish_kernel<float>, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
