@@ -97,6 +97,17 @@ def other_workload(args):
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None}
     wl = args.workload
+
+    def traced(fn):
+        # one more call with the launch trace: per-class kernel ms and launches
+        if args.no_trace:
+            return None
+        pmx.trace_enable(True)
+        fn()
+        tr = pmx.trace_collect()
+        pmx.trace_enable(False)
+        return {k: [round(v[0], 3), v[1]] for k, v in tr.items()}
+
     if wl == "spd_64":
         c = W.spd_64()
         A = torch.from_numpy(c["A"]).to(dev)
@@ -123,6 +134,7 @@ def other_workload(args):
         ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
         inf = pmx.parse_info(info)
         gemms = int(inf["gemms"].sum())
+        out["kernel_trace_ms"] = traced(lambda: fn(opts))
         fn(taylor)
         tg = int(pmx.parse_info(info)["gemms"].sum())
         tf = gemms * 2.0 * 512 ** 3 / (ms * 1e-3) / 1e12
@@ -141,6 +153,7 @@ def other_workload(args):
         ms = timed(torch, lambda: fn(o), args.steps, args.warmup)
         inf = pmx.parse_info(info)
         it = int(inf["iters"][:, 0].max())
+        out["kernel_trace_ms"] = traced(lambda: fn(o))
         fn(pmx.default_opts(max_iter=60, tol=c["tol"], accelerate=0))
         tit = int(pmx.parse_info(info)["iters"][:, 0].max())
         # per update: X^T X (4096 x 1024 x 1024), R^2 (1024^3), X g (4096 x 1024 x 1024)
@@ -159,6 +172,7 @@ def other_workload(args):
         ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
         inf = pmx.parse_info(info)[0]
         gemms = int(inf["gemms"])
+        out["kernel_trace_ms"] = traced(lambda: fn(opts))
         fn(taylor)
         tg = int(pmx.parse_info(info)[0]["gemms"])
         tf = gemms * 2.0 * 1e12 / (ms * 1e-3) / 1e12

@@ -18,6 +18,8 @@ struct pmx_context {
   int gemm_blocks_per_cu;  // persistent GEMM grid: blocks per CU (0: one block per tile)
   int gemm_cfg;            // forced tile configuration (-1: by shape)
   int gemm_map;            // tile order mode
+  int bf16_cfg;            // bf16 GEMM tile (-1: by shape, 0 128^2, 1 256^2 x 8 waves, 2 x 4)
+  int bf16_map;            // bf16 GEMM: 1 deals whole matrices to XCDs, 0 plain order
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -268,6 +270,13 @@ GemmParams gemm_base(const pmx_context* h, int M, int N, int K, int batch) {
   return g;
 }
 
+GemmParams bf16_base(const pmx_context* h, int M, int N, int K, int batch) {
+  GemmParams g = gemm_base(h, M, N, K, batch);
+  g.cfg_id = h->bf16_cfg;
+  g.map_mode = h->bf16_map;
+  return g;
+}
+
 void set_vec(GemmParams& g) {
   bool v = true;
   for (int i = 0; i < g.nprob; ++i) {
@@ -423,6 +432,10 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_GEMM_BLOCKS_PER_CU")) c->gemm_blocks_per_cu = atoi(e);
   if (const char* e = getenv("PMX_GEMM_CFG")) c->gemm_cfg = atoi(e);
   if (const char* e = getenv("PMX_GEMM_MAP")) c->gemm_map = atoi(e);
+  c->bf16_cfg = -1;
+  c->bf16_map = 1;
+  if (const char* e = getenv("PMX_BF16_CFG")) c->bf16_cfg = atoi(e);
+  if (const char* e = getenv("PMX_BF16_MAP")) c->bf16_map = atoi(e);
   *handle = c;
   return PMX_OK;
 }
@@ -471,8 +484,8 @@ static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
   return iter_layout(n, n, batch, o, 4, 2, sizeof(float)).total;
 }
 // fp32: X ping-pong, R, R^2.  bf16: X and X^T ping-pong, R, R^2 (fp32), and
-// the bf16 operands R, R^T, g^T.
-static int polar_bufs(pmx_dtype dt) { return dt == PMX_BF16 ? 9 : 4; }
+// the bf16 operands R and g.
+static int polar_bufs(pmx_dtype dt) { return dt == PMX_BF16 ? 8 : 4; }
 static size_t polar_ws(int m, int n, int batch, const pmx_matfn_opts& o, pmx_dtype dt) {
   const int rows = std::max(m, n), cols = std::min(m, n);
   return iter_layout(rows, cols, batch, o, polar_bufs(dt), 0, sizeof(float)).total;
@@ -679,6 +692,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       if (k == 0) {
         // Z_1 = g Z_0 = g is written explicitly; Y_1 = Y_0 g reads it back.
         FormGParams fp;
+        memset(&fp, 0, sizeof(fp));
         fp.r = Rb;
         fp.r2 = (d == 2) ? R2b : nullptr;
         fp.dst = Zb[1];
@@ -803,19 +817,18 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(G, bf, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
-  PolarInitParams pi;
-  pi.g = G;
-  pi.ldg = ldg;
-  pi.g_stride = sg;
-  pi.x = Xb[0];
-  pi.x_stride = bs;
-  pi.rows = rows;
-  pi.cols = cols;
-  pi.transpose = tr ? 1 : 0;
-  pi.ctrl = ctrl;
-  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_init(pi, bf, batch, q.s); }));
-
   if (!bf) {
+    PolarInitParams pi;
+    pi.g = G;
+    pi.ldg = ldg;
+    pi.g_stride = sg;
+    pi.x = Xb[0];
+    pi.x_stride = bs;
+    pi.rows = rows;
+    pi.cols = cols;
+    pi.transpose = tr ? 1 : 0;
+    pi.ctrl = ctrl;
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_init(pi, false, batch, q.s); }));
     auto residual = [&](float* Xc, int products, int count, int k_next) {
       GemmParams r = gemm_base(q.h, cols, cols, rows, batch);
       r.ctrl = ctrl;
@@ -852,44 +865,25 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1, k + 1));
     }
   } else {
-    // bf16: every product is k-contiguous x k-contiguous (see pmx_gemm_bf16.hip)
+    // bf16: every product is k-contiguous x k-contiguous (pmx_gemm_bf16.hip).
+    // X and X^T are kept in bf16 (the update writes both); R is symmetric, so
+    // its bf16 copy Rh (written by the residual) is both operands of R^2, and
+    // the bf16 polynomial g is the update's second operand as it stands.
     float* Xt[2] = {at<float>(ws, Lw.bufs[4]), at<float>(ws, Lw.bufs[5])};
-    float* Rh = at<float>(ws, Lw.bufs[6]);   // R in bf16
-    float* Rht = at<float>(ws, Lw.bufs[7]);  // R^T in bf16
-    float* Gt = at<float>(ws, Lw.bufs[8]);   // g^T in bf16
+    float* Rh = at<float>(ws, Lw.bufs[6]);  // R in bf16
+    float* Gh = at<float>(ws, Lw.bufs[7]);  // g in bf16
     const bool vec = (cols % 8 == 0) && (rows % 8 == 0) && (bs % 8 == 0);
-    auto xpose = [&](const void* a, bool a_bf16, const float* a2, int poly, int r_, int c_,
-                     void* out_t, void* out_n, Ctrl* gate) {
-      XposeParams x;
-      memset(&x, 0, sizeof(x));
-      x.a = a;
-      x.a2 = a2;
-      x.a_bf16 = a_bf16 ? 1 : 0;
-      x.lda = c_;
-      x.sa = bs;
-      x.out_t = (uint16_t*)out_t;
-      x.ldt = r_;
-      x.st = bs;
-      x.out_n = (uint16_t*)out_n;
-      x.ldn = c_;
-      x.sn = bs;
-      x.rows = r_;
-      x.cols = c_;
-      x.poly = poly;
-      x.degree = d;
-      x.c0 = (float)taylor(0);
-      x.c1 = (float)taylor(1);
-      x.ctrl = gate;
-      return q.run(PMX_KC_OTHER, [&] { return launch_xpose(x, batch, q.s); });
-    };
     auto residual = [&](float* Xtc, int products, int count, int k_next) {
-      GemmParams r = gemm_base(q.h, cols, cols, rows, batch);
+      GemmParams r = bf16_base(q.h, cols, cols, rows, batch);
       r.ctrl = ctrl;
       r.prob[0].a = {Xtc, rows, bs, nullptr, 0};
       r.prob[0].b = {Xtc, rows, bs, nullptr, 0};
       r.prob[0].c = Rb;
       r.prob[0].ldc = cols;
       r.prob[0].stride_c = bs;
+      r.prob[1].c = (d == 2) ? Rh : nullptr;  // bf16 copy for the power R^2
+      r.prob[1].ldc = cols;
+      r.prob[1].stride_c = bs;
       r.partials = partials;
       r.partial_stride = Lw.pstride;
       r.products = products;
@@ -899,15 +893,33 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       r.vec = vec ? 1 : 0;
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_bf16(r, ROLE_RESID, q.s); });
     };
-    PMX_TRY(xpose(Xb[0], true, nullptr, 0, rows, cols, Xt[0], nullptr, ctrl));
+    {
+      // X_0 = G / ||G||_F and its transpose, in one pass over G
+      XposeParams x;
+      memset(&x, 0, sizeof(x));
+      x.a = G;
+      x.a_bf16 = 1;
+      x.lda = ldg;
+      x.sa = sg;
+      x.rows = m;
+      x.cols = n;
+      x.scale_inv_c = 1;
+      x.ctrl = ctrl;
+      x.out_n = (uint16_t*)(tr ? Xt[0] : Xb[0]);
+      x.ldn = n;
+      x.sn = bs;
+      x.out_t = (uint16_t*)(tr ? Xb[0] : Xt[0]);
+      x.ldt = m;
+      x.st = bs;
+      PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_xpose(x, batch, q.s); }));
+    }
     PMX_TRY(residual(Xt[0], 1, 0, 0));
     for (int k = 0; k < o.max_iter; ++k) {
       if (d == 2) {
-        PMX_TRY(xpose(Rb, false, nullptr, 0, cols, cols, Rht, Rh, ctrl));
-        GemmParams g = gemm_base(q.h, cols, cols, cols, batch);
+        GemmParams g = bf16_base(q.h, cols, cols, cols, batch);
         g.ctrl = ctrl;
         g.prob[0].a = {Rh, cols, bs, nullptr, 0};
-        g.prob[0].b = {Rht, cols, bs, nullptr, 0};
+        g.prob[0].b = {Rh, cols, bs, nullptr, 0};
         g.prob[0].c = R2b;
         g.prob[0].ldc = cols;
         g.prob[0].stride_c = bs;
@@ -915,13 +927,25 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
         PMX_TRY(q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_bf16(g, ROLE_POWER, q.s); }));
       }
       PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, false));
-      PMX_TRY(xpose(Rb, false, R2b, 1, cols, cols, Gt, nullptr, ctrl));
+      FormGParams fg;
+      memset(&fg, 0, sizeof(fg));
+      fg.r = Rb;
+      fg.r2 = (d == 2) ? R2b : nullptr;
+      fg.dst = Gh;
+      fg.dst_bf16 = 1;
+      fg.stride = bs;
+      fg.n = cols;
+      fg.degree = d;
+      fg.c0 = (float)taylor(0);
+      fg.c1 = (float)taylor(1);
+      fg.ctrl = ctrl;
+      PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fg, batch, q.s); }));
       const int cur = k & 1, nxt = cur ^ 1;
-      GemmParams u = gemm_base(q.h, rows, cols, cols, batch);
+      GemmParams u = bf16_base(q.h, rows, cols, cols, batch);
       u.ctrl = ctrl;
       u.nprob = 1;
       u.prob[0].a = {Xb[cur], cols, bs, nullptr, 0};
-      u.prob[0].b = {Gt, cols, bs, nullptr, 0};
+      u.prob[0].b = {Gh, cols, bs, nullptr, 0};
       u.prob[0].c = Xb[nxt];
       u.prob[0].ldc = cols;
       u.prob[0].stride_c = bs;
@@ -934,15 +958,25 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     }
   }
   PolarFinishParams fp;
-  fp.xbuf[0] = Xb[0];
-  fp.xbuf[1] = Xb[1];
+  memset(&fp, 0, sizeof(fp));
+  if (bf && tr) {
+    // U = X^T is the kept transposed iterate: a straight copy
+    fp.xbuf[0] = at<float>(ws, Lw.bufs[4]);
+    fp.xbuf[1] = at<float>(ws, Lw.bufs[5]);
+    fp.rows = cols;
+    fp.cols = rows;
+    fp.transpose = 0;
+  } else {
+    fp.xbuf[0] = Xb[0];
+    fp.xbuf[1] = Xb[1];
+    fp.rows = rows;
+    fp.cols = cols;
+    fp.transpose = tr ? 1 : 0;
+  }
   fp.buf_stride = bs;
   fp.u = U;
   fp.ldu = ldu;
   fp.u_stride = su;
-  fp.rows = rows;
-  fp.cols = cols;
-  fp.transpose = tr ? 1 : 0;
   fp.ctrl = ctrl;
   PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_finish(fp, bf, batch, q.s); }));
   return PMX_OK;

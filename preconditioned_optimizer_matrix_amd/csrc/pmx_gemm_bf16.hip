@@ -2,20 +2,24 @@
 // bf16 polar-factor iteration.  Every operand is stored with k contiguous:
 //   C[i][j] = sum_k A[i][k] * Bs[j][k]
 // (A is M x K, Bs is N x K, both row-major bf16).  The polar iteration keeps a
-// transposed copy X^T of its iterate and writes R, R^T and g^T in bf16 with a
-// tile-transpose kernel, so its three products all take this form:
-//   R  = I - X^T X : A = X^T, Bs = X^T
-//   R2 = R R       : A = R,   Bs = R^T
-//   X' = X g       : A = X,   Bs = g^T   (the epilogue also writes X'^T)
+// transposed copy X^T of its iterate; R and g are symmetric, so their bf16
+// copies serve as Bs unchanged and its three products all take this form:
+//   R  = I - X^T X : A = X^T, Bs = X^T   (the epilogue also writes R in bf16)
+//   R2 = R R       : A = R,   Bs = R
+//   X' = X g       : A = X,   Bs = g     (the epilogue also writes X'^T)
 //
 // Design (CDNA4):
 //  * v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) and 8 consecutive
 //    k values 8 (l / 32) .. +7 of a 16-wide k step: one 16-byte LDS read per
 //    fragment.  LDS rows are padded to 72 bf16 (144 bytes) so the 16-byte
 //    reads of 8 consecutive rows hit distinct banks.
-//  * Block tile 128 x 128 x 64, 4 waves (64 x 64 each, 2 x 2 accumulators),
-//    16-byte global loads straight into 16-byte LDS stores, LDS double
-//    buffered with a register prefetch, persistent grid over (matrix, tile).
+//  * Block tile 256 x 256 x 64 with 4 waves of 128 x 128 (4 x 4 accumulators
+//    in AGPRs, one block per CU: 8 fragment reads per 16 MFMAs), or
+//    128 x 128 x 64 with waves of 64 x 64 when the problem has fewer large
+//    tiles than compute units.  16-byte global loads into 16-byte LDS stores,
+//    LDS double buffered with a register prefetch of the next k tile, the
+//    fragments of the next 16-wide k step read while the current one
+//    multiplies; persistent grid over (matrix, tile).
 //  * fp32 -> bf16 rounding is round-to-nearest-even.
 #include "pmx_kernels.h"
 
@@ -27,10 +31,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
-constexpr int LDK = BK + 8;      // bf16 per LDS row (144 bytes)
-constexpr int TILE = 128 * LDK;  // bf16 per operand tile
-constexpr int CHUNKS = 128 * BK / 8 / NT;  // 16-byte chunks per thread per operand (4)
+// Block tile BM x BN x BK, waves of WM x WN (FM x FN accumulators of
+// 32 x 32), MINB blocks resident per CU.  LDS rows hold BK + 8 bf16: the row
+// pitch (144 or 80 bytes) is an odd multiple of 16 bytes modulo 128, so the
+// 16-byte fragment reads of 8 (or 16) consecutive rows hit distinct banks.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int MINB_>
+struct BCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, MINB = MINB_;
+  static constexpr int LDK = BK + 8;
+  static constexpr int CH = BK / 8;  // 16-byte chunks per LDS row
+  static constexpr int WAVES = (BM / WM) * (BN / WN);
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int CA = BM * CH / NT;  // 16-byte chunks per thread per k tile
+  static constexpr int CB = BN * CH / NT;
+  static constexpr int LDS = (BM + BN) * LDK;  // bf16 per stage
+  static_assert(CA * NT == BM * CH && CB * NT == BN * CH, "tile / thread mismatch");
+};
+using BSmall = BCfg<128, 128, 64, 64, 64, 2>;   // 4 waves of 64 x 64, 72 KB LDS
+using BLarge = BCfg<256, 256, 128, 64, 64, 1>;  // 8 waves of 128 x 64, 144 KB LDS
+using BLarge4 = BCfg<256, 256, 128, 128, 64, 1>;  // 4 waves of 128 x 128
+using BMid2 = BCfg<256, 128, 128, 64, 32, 2>;   // 4 waves of 128 x 64, 60 KB, 2 per CU
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
@@ -39,14 +60,16 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return u >> 16;
 }
 
-// One 128 x 64 operand tile: chunk idx -> (row idx / 8, k 8 (idx % 8)).
-__device__ __forceinline__ void load_chunks(u32x4 (&v)[CHUNKS], const uint16_t* base, int64_t ld,
+// One ROWS x BK operand tile: chunk idx -> (row idx / CH, k 8 (idx % CH)).
+template <class CF, int C>
+__device__ __forceinline__ void load_chunks(u32x4 (&v)[C], const uint16_t* base, int64_t ld,
                                             int row0, int nrows, int k0, int K, bool vec) {
+  constexpr int NT = CF::NT, CH = CF::CH;
 #pragma unroll
-  for (int i = 0; i < CHUNKS; ++i) {
+  for (int i = 0; i < C; ++i) {
     const int idx = threadIdx.x + NT * i;
-    const int row = row0 + (idx >> 3);
-    const int k = k0 + ((idx & 7) << 3);
+    const int row = row0 + idx / CH;
+    const int k = k0 + (idx % CH) * 8;
     u32x4 out = {0u, 0u, 0u, 0u};
     if (row < nrows) {
       const uint16_t* b = base + (int64_t)row * ld + k;
@@ -63,11 +86,12 @@ __device__ __forceinline__ void load_chunks(u32x4 (&v)[CHUNKS], const uint16_t* 
   }
 }
 
-__device__ __forceinline__ void store_chunks(uint16_t* lds, const u32x4 (&v)[CHUNKS]) {
+template <class CF, int C>
+__device__ __forceinline__ void store_chunks(uint16_t* lds, const u32x4 (&v)[C]) {
 #pragma unroll
-  for (int i = 0; i < CHUNKS; ++i) {
-    const int idx = threadIdx.x + NT * i;
-    *reinterpret_cast<u32x4*>(lds + (idx >> 3) * LDK + ((idx & 7) << 3)) = v[i];
+  for (int i = 0; i < C; ++i) {
+    const int idx = threadIdx.x + CF::NT * i;
+    *reinterpret_cast<u32x4*>(lds + (idx / CF::CH) * CF::LDK + (idx % CF::CH) * 8) = v[i];
   }
 }
 
@@ -88,24 +112,126 @@ __device__ __forceinline__ void item_tile(int it, int tiles_m, int tiles_n, int*
   *tn = in_group / gsize;
 }
 
-// ROLE_RESID: C fp32 = I - acc with the Frobenius reduction and decision;
-// ROLE_POWER: C fp32 = acc; ROLE_UPDATE: C bf16 = acc and, at ptr2 of the
-// output descriptor (prob[1].c), its transpose.
-template <int ROLE>
-__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmParams p) {
+// Main loop of a tile that lies wholly inside A and Bs (16-byte aligned rows,
+// K a multiple of 64): no bounds tests, so a k tile is one basic block and
+// its schedule is fixed with scheduling-group barriers.  Per k tile: the
+// fragments of the first 16-wide step and the next tile's global loads are
+// issued first; each step's MFMAs are interleaved one-for-one with the
+// fragment reads of the following step; the last step's MFMAs are interleaved
+// with the LDS stores of the next tile (into the other LDS buffer, which no
+// wave reads in this k tile).
+// Scheduling groups: MF MFMAs, each followed by up to PER instructions of
+// class MASK (0x100 LDS read, 0x200 LDS write) until OPS are placed.
+template <int MF, int OPS, int MASK, int PER>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (MF > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int k = OPS < PER ? OPS : PER;
+    if constexpr (k > 0) __builtin_amdgcn_sched_group_barrier(MASK, k, 0);
+    sched_interleave<MF - 1, OPS - k, MASK, PER>();
+  } else if constexpr (OPS > 0) {
+    __builtin_amdgcn_sched_group_barrier(MASK, OPS, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[C::FM][C::FN],
+                                              uint16_t (*smem)[C::LDS], const uint16_t* A,
+                                              int64_t lda, const uint16_t* B, int64_t ldb,
+                                              int m0, int n0, int nk, int lane, int wm, int wn) {
+  constexpr int NT = C::NT, FM = C::FM, FN = C::FN, CA = C::CA, CB = C::CB;
+  constexpr int BK = C::BK, LDK = C::LDK, CH = C::CH, STEPS = BK / 16;
+  constexpr int NF = FM + FN;  // fragment reads per step
+  constexpr int RS = NT / CH;  // rows covered by one chunk index step
+  constexpr int MF = FM * FN;  // MFMAs per step
+  const int t = threadIdx.x;
+  const uint16_t* ga = A + (int64_t)(m0 + t / CH) * lda + (t % CH) * 8;
+  const uint16_t* gb = B + (int64_t)(n0 + t / CH) * ldb + (t % CH) * 8;
+  const int64_t sta = (int64_t)RS * lda, stb = (int64_t)RS * ldb;
+  const int wofs = (t / CH) * LDK + (t % CH) * 8;
+  u32x4 va[CA], vb[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + i * sta);
+#pragma unroll
+  for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + i * stb);
+#pragma unroll
+  for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(smem[0] + wofs + i * RS * LDK) = va[i];
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+    *reinterpret_cast<u32x4*>(smem[0] + C::BM * LDK + wofs + i * RS * LDK) = vb[i];
+  __syncthreads();
+  const int ra = (wm + (lane & 31)) * LDK + (lane >> 5) * 8;
+  const int rb = (C::BM + wn + (lane & 31)) * LDK + (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t* sa = smem[kt & 1] + ra;
+    const uint16_t* sb = smem[kt & 1] + rb;
+    uint16_t* dst = smem[(kt & 1) ^ 1] + wofs;
+    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;  // the last tile reloads itself
+    bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(sa + 32 * i * LDK);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(sb + 32 * j * LDK);
+#pragma unroll
+    for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + kn + i * sta);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + kn + i * stb);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const int c = s & 1, n = c ^ 1;
+      if (s + 1 < STEPS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[n][i] = *reinterpret_cast<const bf16x8*>(sa + 32 * i * LDK + 16 * (s + 1));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[n][j] = *reinterpret_cast<const bf16x8*>(sb + 32 * j * LDK + 16 * (s + 1));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(dst + i * RS * LDK) = va[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(dst + C::BM * LDK + i * RS * LDK) = vb[i];
+    // schedule of the k tile
+    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);       // step 0 fragments
+    __builtin_amdgcn_sched_group_barrier(0x020, CA + CB, 0);  // next tile, global
+#pragma unroll
+    for (int s = 0; s + 1 < STEPS; ++s) sched_interleave<MF, NF, 0x100, (NF + MF - 1) / MF>();
+    sched_interleave<MF, CA + CB, 0x200, (CA + CB + MF - 1) / MF>();
+    __syncthreads();
+  }
+}
+
+// ROLE_RESID: C fp32 = I - acc with the Frobenius reduction and decision, and
+// a bf16 copy at prob[1].c when set; ROLE_POWER: C fp32 = acc; ROLE_UPDATE:
+// C bf16 = acc and its transpose at prob[1].c.
+template <class C, int ROLE>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p) {
   constexpr bool RESID = ROLE == ROLE_RESID;
   constexpr bool BF16_OUT = ROLE == ROLE_UPDATE;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
-  __shared__ double red[NT / 64];
+  constexpr int NT = C::NT, FM = C::FM, FN = C::FN;
+  constexpr int WGN = C::BN / C::WN;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][C::LDS];
+  __shared__ double red[C::WAVES];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = (wid >> 1) * 64, wn = (wid & 1) * 64;
+  const int wm = (wid / WGN) * C::WM, wn = (wid % WGN) * C::WN;
   const bool vec = p.vec != 0;
   const int tiles = p.tiles_m * p.tiles_n;
   const int total = tiles * p.batch;
   const GemmProblem& pr = p.prob[0];
 
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+  // Workgroups are dealt to the 8 XCDs round-robin; with one block per tile
+  // and 8 | total, XCD x takes the contiguous item range [x total / 8, ...),
+  // so each XCD's L2 serves whole matrices.
+  const bool xcd = p.map_mode != 0 && (int)gridDim.x == total && (total & 7) == 0;
+  for (int it0 = blockIdx.x; it0 < total; it0 += gridDim.x) {
+    const int it = xcd ? (it0 & 7) * (total >> 3) + (it0 >> 3) : it0;
     int b, tm, tn, tile;
     item_tile(it, p.tiles_m, p.tiles_n, &b, &tm, &tn, &tile);
     if (p.ctrl) {
@@ -115,54 +241,65 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmParams p) {
     const uint16_t* A = reinterpret_cast<const uint16_t*>(pr.a.ptr) + (int64_t)b * pr.a.stride;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(pr.b.ptr) + (int64_t)b * pr.b.stride;
     if (RESID) sketch_share(p.sketch, b, tile, tiles);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    u32x4 va[CHUNKS], vb[CHUNKS];
-    const int nk = (p.K + BK - 1) / BK;
+    const int nk = (p.K + C::BK - 1) / C::BK;
     __syncthreads();
-    load_chunks(va, A, pr.a.ld, m0, p.M, 0, p.K, vec);
-    load_chunks(vb, B, pr.b.ld, n0, p.N, 0, p.K, vec);
-    store_chunks(smem[0][0], va);
-    store_chunks(smem[0][1], vb);
+    if (vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && p.K % C::BK == 0) {
+      mainloop_fast<C>(acc, smem, A, pr.a.ld, B, pr.b.ld, m0, n0, nk, lane, wm, wn);
+    } else {
+    u32x4 va[C::CA], vb[C::CB];
+    load_chunks<C>(va, A, pr.a.ld, m0, p.M, 0, p.K, vec);
+    load_chunks<C>(vb, B, pr.b.ld, n0, p.N, 0, p.K, vec);
+    store_chunks<C>(smem[0], va);
+    store_chunks<C>(smem[0] + C::BM * C::LDK, vb);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       const bool more = kt + 1 < nk;
       if (more) {
-        load_chunks(va, A, pr.a.ld, m0, p.M, (kt + 1) * BK, p.K, vec);
-        load_chunks(vb, B, pr.b.ld, n0, p.N, (kt + 1) * BK, p.K, vec);
+        load_chunks<C>(va, A, pr.a.ld, m0, p.M, (kt + 1) * C::BK, p.K, vec);
+        load_chunks<C>(vb, B, pr.b.ld, n0, p.N, (kt + 1) * C::BK, p.K, vec);
       }
-      const uint16_t* sa = smem[cur][0];
-      const uint16_t* sb = smem[cur][1];
+      const uint16_t* sa = smem[cur] + (wm + (lane & 31)) * C::LDK + (lane >> 5) * 8;
+      const uint16_t* sb = smem[cur] + (C::BM + wn + (lane & 31)) * C::LDK + (lane >> 5) * 8;
+      // fragments of the next 16-wide k step are read while this one multiplies
+      bf16x8 fa[2][FM], fb[2][FN];
 #pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        const int kofs = s * 16 + (lane >> 5) * 8;
-        bf16x8 fa[2], fb[2];
+      for (int i = 0; i < FM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(sa + 32 * i * C::LDK);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          fa[i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 32 * i + (lane & 31)) * LDK + kofs);
+      for (int j = 0; j < FN; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(sb + 32 * j * C::LDK);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          fb[j] = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 * j + (lane & 31)) * LDK + kofs);
+      for (int s = 0; s < C::BK / 16; ++s) {
+        const int c = s & 1, n = c ^ 1;
+        if (s + 1 < C::BK / 16) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < FM; ++i)
+            fa[n][i] = *reinterpret_cast<const bf16x8*>(sa + 32 * i * C::LDK + 16 * (s + 1));
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j)
+            fb[n][j] = *reinterpret_cast<const bf16x8*>(sb + 32 * j * C::LDK + 16 * (s + 1));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
       }
       if (more) {
-        store_chunks(smem[cur ^ 1][0], va);
-        store_chunks(smem[cur ^ 1][1], vb);
+        store_chunks<C>(smem[cur ^ 1], va);
+        store_chunks<C>(smem[cur ^ 1] + C::BM * C::LDK, vb);
       }
       __syncthreads();
+    }
     }
 
     // Epilogue (same accumulator layout as the 32x32 fp32 MFMA: lane l holds
@@ -170,9 +307,9 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmParams p) {
     const int hi = lane >> 5, col_in = lane & 31;
     float fro = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < FN; ++j) {
         const int col = n0 + wn + 32 * j + col_in;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -186,12 +323,17 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmParams p) {
               x = (row == col ? 1.f : 0.f) - x;
               if (row < p.M && col < p.N) fro += x * x;
             }
+            h[r] = bf16_rne(x);
             if (row < p.M && col < p.N) {
               const int64_t o = (int64_t)b * pr.stride_c + (int64_t)row * pr.ldc + col;
-              if (BF16_OUT) reinterpret_cast<uint16_t*>(pr.c)[o] = (uint16_t)bf16_rne(x);
+              if (BF16_OUT) reinterpret_cast<uint16_t*>(pr.c)[o] = (uint16_t)h[r];
               else pr.c[o] = x;
+              if (RESID && p.prob[1].c) {
+                const GemmProblem& hp = p.prob[1];
+                reinterpret_cast<uint16_t*>(hp.c)[(int64_t)b * hp.stride_c +
+                                                  (int64_t)row * hp.ldc + col] = (uint16_t)h[r];
+              }
             }
-            h[r] = bf16_rne(x);
           }
           if (BF16_OUT && col < p.N) {
             // transposed copy: X'^T[col][row_base .. row_base + 3]
@@ -209,10 +351,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmParams p) {
         }
       }
     if (RESID) {
-      const double blocksum = block_sum<NT / 64>((double)fro, red);
+      const double blocksum = block_sum<C::WAVES>((double)fro, red);
       double tot;
-      if (last_block_sum<NT / 64>(blocksum, p.partials + (int64_t)b * p.partial_stride,
-                                  &p.ctrl[b].counter, tiles, tile, red, &tot)) {
+      if (last_block_sum<C::WAVES>(blocksum, p.partials + (int64_t)b * p.partial_stride,
+                                   &p.ctrl[b].counter, tiles, tile, red, &tot)) {
         if (threadIdx.x == 0) {
           Ctrl& c = p.ctrl[b];
           if (p.count_update) c.iter += 1;
@@ -224,26 +366,37 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmParams p) {
   }
 }
 
-}  // namespace
-
-// C = A Bs^T with A (M x K) and Bs (N x K) bf16, k contiguous.  Roles:
-// ROLE_RESID (C fp32 = I - A Bs^T, convergence), ROLE_POWER (C fp32),
-// ROLE_UPDATE (C bf16 and its transpose at prob[1].c / ldc / stride_c).
-hipError_t launch_gemm_bf16(const GemmParams& pin, int role, hipStream_t s) {
-  GemmParams p = pin;
-  p.tiles_m = (p.M + BM - 1) / BM;
-  p.tiles_n = (p.N + BN - 1) / BN;
+template <class C>
+hipError_t launch_cfg(GemmParams p, int role, hipStream_t s) {
+  p.tiles_m = (p.M + C::BM - 1) / C::BM;
+  p.tiles_n = (p.N + C::BN - 1) / C::BN;
   const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
   int64_t g = total;
   if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
-  const dim3 grid((unsigned)g), block(NT);
+  const dim3 grid((unsigned)g), block(C::NT);
   switch (role) {
-    case ROLE_RESID: hipLaunchKernelGGL((gemm_bf16_kernel<ROLE_RESID>), grid, block, 0, s, p); break;
-    case ROLE_POWER: hipLaunchKernelGGL((gemm_bf16_kernel<ROLE_POWER>), grid, block, 0, s, p); break;
-    case ROLE_UPDATE: hipLaunchKernelGGL((gemm_bf16_kernel<ROLE_UPDATE>), grid, block, 0, s, p); break;
+    case ROLE_RESID: hipLaunchKernelGGL((gemm_bf16_kernel<C, ROLE_RESID>), grid, block, 0, s, p); break;
+    case ROLE_POWER: hipLaunchKernelGGL((gemm_bf16_kernel<C, ROLE_POWER>), grid, block, 0, s, p); break;
+    case ROLE_UPDATE: hipLaunchKernelGGL((gemm_bf16_kernel<C, ROLE_UPDATE>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+// C = A Bs^T with A (M x K) and Bs (N x K) bf16, k contiguous.  Roles:
+// ROLE_RESID (C fp32 = I - A Bs^T, convergence, optional bf16 copy at
+// prob[1].c / ldc / stride_c), ROLE_POWER (C fp32),
+// ROLE_UPDATE (C bf16 and its transpose at prob[1].c / ldc / stride_c).
+hipError_t launch_gemm_bf16(const GemmParams& p, int role, hipStream_t s) {
+  // the large tile once it still gives every compute unit a tile
+  const int64_t large = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+  int cfg = p.cfg_id;
+  if (cfg < 0 || cfg > 3) cfg = (p.M >= 256 && p.N >= 256 && large >= p.num_cu) ? 1 : 0;
+  if (cfg == 2) return launch_cfg<BLarge4>(p, role, s);
+  if (cfg == 3) return launch_cfg<BMid2>(p, role, s);
+  return cfg == 1 ? launch_cfg<BLarge>(p, role, s) : launch_cfg<BSmall>(p, role, s);
 }
 
 }  // namespace pmx

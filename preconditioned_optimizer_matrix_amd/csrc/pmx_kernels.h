@@ -84,9 +84,11 @@ struct SkinnyParams {
 struct FormGParams {
   const float* r;
   const float* r2;       // R^2 (d = 2), may alias dst
-  float* dst;
-  int64_t stride;
+  void* dst;             // fp32, or bf16 with dst_bf16
+  int64_t stride;        // elements, shared by r, r2 and dst
   int n, degree;
+  int dst_bf16;
+  int vec;               // set by the launcher
   float c0, c1;
   Ctrl* ctrl;
 };
@@ -105,6 +107,7 @@ struct XposeParams {
   int64_t ldn, sn;
   int rows, cols;
   int poly, degree;
+  int scale_inv_c;  // multiply the input by 1 / ctrl.c first (needs ctrl)
   float c0, c1;
   Ctrl* ctrl;  // null: unconditional; else skipped when the matrix is not running
 };
@@ -122,12 +125,15 @@ struct RootFinishParams {
   Ctrl* ctrl;
 };
 
+// U from the final iterate X = xbuf[iter & 1] (rows x cols, ld cols): U = X,
+// or U = X^T with `transpose` (ld ldu either way); NaN when the call failed.
 struct PolarFinishParams {
   void* xbuf[2];
   int64_t buf_stride;
   void* u;
   int64_t ldu, u_stride;
   int rows, cols, transpose;
+  int vec;  // set by the launcher
   Ctrl* ctrl;
 };
 

@@ -51,15 +51,39 @@ __global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch) {
 template <typename T>
 __global__ __launch_bounds__(NT) void fro_scale_kernel(const T* __restrict__ X, int rows,
                                                        int cols, int64_t ld, int64_t stride,
-                                                       Ctrl* ctrl, double* partials,
+                                                       int vec, Ctrl* ctrl, double* partials,
                                                        int64_t pstride, pmx_matfn_info* info) {
   const int b = blockIdx.y;
   const T* x = X + (int64_t)b * stride;
   double acc = 0.0;
-  for (int r = blockIdx.x; r < rows; r += gridDim.x)
-  for (int c = threadIdx.x; c < cols; c += NT) {
-    const double v = (double)to_f32(x[(int64_t)r * ld + c]);
-    acc += v * v;
+  if (vec) {
+    // 16-byte loads: 8 bf16 or 4 fp32 per load (rows, ld and the base aligned)
+    constexpr int V = 16 / sizeof(T);
+    const int cv = cols / V;
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+      const uint4* row = reinterpret_cast<const uint4*>(x + (int64_t)r * ld);
+      for (int c = threadIdx.x; c < cv; c += NT) {
+        const uint4 w = row[c];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (sizeof(T) == 2) {
+            const double lo = (double)__uint_as_float(u[i] << 16);
+            const double hi = (double)__uint_as_float(u[i] & 0xFFFF0000u);
+            acc += lo * lo + hi * hi;
+          } else {
+            const double v = (double)__uint_as_float(u[i]);
+            acc += v * v;
+          }
+        }
+      }
+    }
+  } else {
+    for (int r = blockIdx.x; r < rows; r += gridDim.x)
+    for (int c = threadIdx.x; c < cols; c += NT) {
+      const double v = (double)to_f32(x[(int64_t)r * ld + c]);
+      acc += v * v;
+    }
   }
   __shared__ double red[NT / 64];
   const double bs = block_sum<NT / 64>(acc, red);
@@ -289,10 +313,11 @@ __device__ double alpha_from_gram(const double* G, int J, double s, const AlphaC
 
 // ---------------------------------------------------------------- skinny products
 // Recursive-halving reduction over a 64-lane wave of CNT values per lane
-// (CNT a power of two <= 64): at the step with offset O the lanes with bit O
-// set keep the upper half of their remaining values and add the partner's
-// copy of it; once one value is left the remaining offsets add plainly.
-// Lane l ends with the wave-wide sum of value index l / (64 / CNT) in acc[0].
+// (CNT a power of two): at the step with offset O the lanes with bit O set
+// keep the upper half of their remaining values and add the partner's copy of
+// it; once one value is left the remaining offsets add plainly.  Lane l ends
+// with the wave-wide sum of value index l / (64 / CNT) in acc[0] (CNT <= 64),
+// or of value indices (CNT / 64) l + i in acc[i] (CNT >= 64).
 template <int CNT, int O>
 __device__ __forceinline__ void halve_reduce(float* acc, int lane) {
   if constexpr (O >= 1) {
@@ -315,23 +340,25 @@ __device__ __forceinline__ void halve_reduce(float* acc, int lane) {
 
 // out[:, oc : oc + q] = ||R||_F^-pow * Mat * in[:, ic : ic + q] for an n x n Mat
 // and an n x q block of the Krylov buffer (q <= Q).  HBM-bound on Mat, read
-// once with 16-byte loads: a block of 4 waves owns 8 rows (2 per wave), so
-// n = 4096 gives 512 blocks.  In is staged column-major through LDS in chunks
-// of 512 rows (conflict-free 16-byte reads) and shared by the block's rows.
-// Each lane accumulates 2 x Q partial sums over its columns; the wave's
-// recursive-halving reduction leaves the complete sums in the lanes.
+// once with 16-byte loads: a block of 4 waves owns 4 RW rows (RW per wave);
+// RW = 2 keeps a single n = 4096 matrix at 512 blocks, RW = 8 serves batches,
+// where it cuts the LDS reads of In per byte of Mat by four.  In is staged
+// column-major through LDS in chunks of 512 rows (conflict-free 16-byte
+// reads) and shared by the block's rows.  Each lane accumulates RW x Q
+// partial sums over its columns; the wave's recursive-halving reduction leaves
+// the complete sums spread over the lanes.
 // GRAM (last Krylov pass): every block also adds its rows' share of the
 // J x J Gram of K_1..K_J in fp64; the last block to arrive reduces the
 // shares in block order and solves for alpha.
-constexpr int SK_RW = 2;             // rows per wave
-constexpr int SK_RB = 4 * SK_RW;     // rows per block
 constexpr int SK_CH = 512;           // In rows per LDS chunk
 constexpr int SK_LD = SK_CH + 4;     // column stride of the staged chunk
 
-template <int Q, bool GRAM>
+template <int Q, int RW, bool GRAM>
 __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
-  constexpr int CNT = SK_RW * Q;        // partial sums per lane (16, 32 or 64)
-  constexpr int SHARE = 64 / CNT;       // lanes holding each final sum
+  constexpr int CNT = RW * Q;                   // partial sums per lane
+  constexpr int NV = CNT > 64 ? CNT / 64 : 1;   // complete sums per lane
+  constexpr int SHARE = CNT < 64 ? 64 / CNT : 1;  // lanes holding each sum
+  constexpr int RB = 4 * RW;
   const int b = blockIdx.z;
   Ctrl* cb = p.ctrl + b;
   if (load_status(cb) != PMX_RUNNING) return;
@@ -344,8 +371,10 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
 
   __shared__ __attribute__((aligned(16))) float in_lds[Q * SK_LD];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int row0 = blockIdx.x * SK_RB + wid * SK_RW;
+  const int row0 = blockIdx.x * RB + wid * RW;
   const bool vec = (job.mat_ld % 4 == 0) && ((((uintptr_t)mat) & 15) == 0);
+  const bool in_vec = (p.kld % 4 == 0) && (job.in_col % 4 == 0) && (p.q == Q) &&
+                      ((((uintptr_t)kb) & 15) == 0);
 
   float acc[CNT];
 #pragma unroll
@@ -354,12 +383,25 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   for (int j0 = 0; j0 < n; j0 += SK_CH) {
     __syncthreads();
     // stage In[j0 .. j0 + 512)[0 .. Q) column-major (zero beyond n and q)
-    // consecutive threads read consecutive columns of one In row (coalesced)
-    for (int idx = threadIdx.x; idx < SK_CH * Q; idx += NT) {
-      const int jj = idx / Q, c = idx - jj * Q;
-      float v = 0.f;
-      if (j0 + jj < n && c < p.q) v = kb[(int64_t)(j0 + jj) * p.kld + job.in_col + c];
-      in_lds[c * SK_LD + jj] = v;
+    if (in_vec) {
+      // one 16-byte load per (row, 4 columns)
+      for (int idx = threadIdx.x; idx < SK_CH * (Q / 4); idx += NT) {
+        const int jj = idx / (Q / 4), c = 4 * (idx - jj * (Q / 4));
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j0 + jj < n)
+          v = *reinterpret_cast<const float4*>(kb + (int64_t)(j0 + jj) * p.kld + job.in_col + c);
+        in_lds[(c + 0) * SK_LD + jj] = v.x;
+        in_lds[(c + 1) * SK_LD + jj] = v.y;
+        in_lds[(c + 2) * SK_LD + jj] = v.z;
+        in_lds[(c + 3) * SK_LD + jj] = v.w;
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < SK_CH * Q; idx += NT) {
+        const int jj = idx / Q, c = idx - jj * Q;
+        float v = 0.f;
+        if (j0 + jj < n && c < p.q) v = kb[(int64_t)(j0 + jj) * p.kld + job.in_col + c];
+        in_lds[c * SK_LD + jj] = v;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -367,9 +409,9 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
       const int jj = 256 * t + 4 * lane;
       const int j = j0 + jj;
       if (j >= n) continue;
-      float4 m[SK_RW];
+      float4 m[RW];
 #pragma unroll
-      for (int rr = 0; rr < SK_RW; ++rr) {
+      for (int rr = 0; rr < RW; ++rr) {
         const int row = row0 + rr;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (row < n) {
@@ -389,41 +431,76 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
       for (int c = 0; c < Q; ++c) {
         const float4 x = *reinterpret_cast<const float4*>(in_lds + c * SK_LD + jj);
 #pragma unroll
-        for (int rr = 0; rr < SK_RW; ++rr)
+        for (int rr = 0; rr < RW; ++rr)
           acc[rr * Q + c] += m[rr].x * x.x + m[rr].y * x.y + m[rr].z * x.z + m[rr].w * x.w;
       }
     }
   }
   halve_reduce<CNT, 32>(acc, lane);
-  const int idx = lane / SHARE;
-  const int rr = idx / Q, c = idx - rr * Q;
-  const int row = row0 + rr;
-  const bool writer = (lane % SHARE) == 0;
-  const bool valid = writer && row < n && c < p.q;
-  const float val = acc[0] * scale;
-  if (valid) kb[(int64_t)row * p.kld + job.out_col + c] = val;
+  // lane l holds value indices NV l .. NV l + NV - 1 (CNT >= 64) or l / SHARE
+  bool valid[NV];
+  int vrow[NV], vcol[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = CNT >= 64 ? NV * lane + i : lane / SHARE;
+    const int rr = idx / Q, c = idx - rr * Q;
+    vrow[i] = row0 + rr;
+    vcol[i] = c;
+    valid[i] = (lane % SHARE) == 0 && vrow[i] < n && c < p.q;
+    acc[i] *= scale;
+    if (valid[i]) kb[(int64_t)vrow[i] * p.kld + job.out_col + c] = acc[i];
+  }
 
   if constexpr (GRAM) {
+    // the block's share of the Gram entries (a, bb), a <= bb < J <= 5
     const int J = 2 * p.cfg.degree + 1;
     const int pp = p.cfg.p;
-    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-    if (valid) {
-      for (int j = 1; j < J; ++j) v[j - 1] = (double)kb[(int64_t)row * p.kld + j * pp + c];
-      v[J - 1] = (double)val;
-    }
-    __shared__ double red[NT / 64];
-    __shared__ double gsum[15];
-    int t = 0;
-    for (int a = 0; a < J; ++a)
-      for (int bb = a; bb < J; ++bb, ++t) {
-        const double s = block_sum<NT / 64>(v[a] * v[bb], red);
-        if (threadIdx.x == 0) gsum[t] = s;
+    double g[15];
+#pragma unroll
+    for (int e = 0; e < 15; ++e) g[e] = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+      if (valid[i]) {
+#pragma unroll
+        for (int j = 1; j < 5; ++j)
+          if (j < J) v[j - 1] = (double)kb[(int64_t)vrow[i] * p.kld + j * pp + vcol[i]];
+#pragma unroll
+        for (int j = 0; j < 5; ++j)
+          if (j == J - 1) v[j] = (double)acc[i];
       }
-    const int ng = t;
+      int t = 0;
+#pragma unroll
+      for (int a = 0; a < 5; ++a)
+#pragma unroll
+        for (int bb = a; bb < 5; ++bb, ++t) g[t] += v[a] * v[bb];
+    }
+    // entries of (a, bb) with a <= bb < J, in row order, are packed first
+    __shared__ double wsum[4][15];
+    __shared__ double gsum[15];
+    {
+      int t = 0, o = 0;
+#pragma unroll
+      for (int a = 0; a < 5; ++a)
+#pragma unroll
+        for (int bb = a; bb < 5; ++bb, ++t) {
+          const double sv = wave_sum(g[t]);
+          if (a < J && bb < J) {
+            if (lane == 0) wsum[wid][o] = sv;
+            ++o;
+          }
+        }
+    }
+    const int ng = J * (J + 1) / 2;
+    __syncthreads();
     __shared__ int is_last;
     double* part = p.gram_partials + (int64_t)b * p.gram_stride;
+    if (threadIdx.x < ng)
+      part[(int64_t)blockIdx.x * 16 + threadIdx.x] =
+          ((wsum[0][threadIdx.x] + wsum[1][threadIdx.x]) + wsum[2][threadIdx.x]) +
+          wsum[3][threadIdx.x];
+    __syncthreads();
     if (threadIdx.x == 0) {
-      for (int i = 0; i < ng; ++i) part[(int64_t)blockIdx.x * 16 + i] = gsum[i];
       __threadfence();
       const uint32_t prev = atomicAdd(&cb->counter, 1u);
       is_last = (prev == gridDim.x - 1);
@@ -431,15 +508,15 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
     __syncthreads();
     if (!is_last) return;
     __threadfence();
-    // every entry summed over the blocks' shares with a fixed thread
-    // assignment and reduction tree (deterministic)
-    for (int e = 0; e < ng; ++e) {
-      double s = 0.0;
-      for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
-        s += __hip_atomic_load(&part[(int64_t)i * 16 + e], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      const double tot = block_sum<NT / 64>(s, red);
-      if (threadIdx.x == 0) gsum[e] = tot;
+    // every entry summed over the blocks' shares by one wave each, with a
+    // fixed lane assignment and reduction tree (deterministic)
+    for (int e = wid; e < ng; e += NT / 64) {
+      double sv = 0.0;
+      for (int i = lane; i < (int)gridDim.x; i += 64)
+        sv += __hip_atomic_load(&part[(int64_t)i * 16 + e], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      sv = wave_sum(sv);
+      if (lane == 0) gsum[e] = sv;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -464,16 +541,49 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   const int n = p.n;
   const float* R = p.r + (int64_t)b * p.stride;
   const float* R2 = p.r2 ? p.r2 + (int64_t)b * p.stride : nullptr;
-  float* G = p.dst + (int64_t)b * p.stride;
+  float* G = p.dst_bf16 ? nullptr : reinterpret_cast<float*>(p.dst) + (int64_t)b * p.stride;
+  uint16_t* Gh = p.dst_bf16 ? reinterpret_cast<uint16_t*>(p.dst) + (int64_t)b * p.stride : nullptr;
   const float c0 = p.c0, c1 = p.c1;
+  const bool d1 = p.degree == 1;
+  if (p.vec) {
+    // four columns per thread (n % 4 == 0, stride % 4 == 0)
+    const int nv = n / 4;
+    for (int r = blockIdx.x; r < n; r += gridDim.x)
+    for (int c4 = threadIdx.x; c4 < nv; c4 += NT) {
+      const int64_t e = (int64_t)r * n + 4 * c4;
+      const float4 x = *reinterpret_cast<const float4*>(R + e);
+      float4 v;
+      if (d1) {
+        v = make_float4(alpha * x.x, alpha * x.y, alpha * x.z, alpha * x.w);
+      } else {
+        const float4 y = *reinterpret_cast<const float4*>(R2 + e);
+        v = make_float4(c1 * x.x + alpha * y.x, c1 * x.y + alpha * y.y, c1 * x.z + alpha * y.z,
+                        c1 * x.w + alpha * y.w);
+      }
+      const int dc = r - 4 * c4;
+      if (dc == 0) v.x += c0;
+      if (dc == 1) v.y += c0;
+      if (dc == 2) v.z += c0;
+      if (dc == 3) v.w += c0;
+      if (Gh) {
+        const uint32_t h0 = from_f32<bf16_t>(v.x).bits, h1 = from_f32<bf16_t>(v.y).bits;
+        const uint32_t h2 = from_f32<bf16_t>(v.z).bits, h3 = from_f32<bf16_t>(v.w).bits;
+        *reinterpret_cast<uint2*>(Gh + e) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      } else {
+        *reinterpret_cast<float4*>(G + e) = v;
+      }
+    }
+    return;
+  }
   for (int r = blockIdx.x; r < n; r += gridDim.x)
   for (int c = threadIdx.x; c < n; c += NT) {
     const int64_t e = (int64_t)r * n + c;
     float v;
-    if (p.degree == 1) v = alpha * R[e];
+    if (d1) v = alpha * R[e];
     else v = c1 * R[e] + alpha * R2[e];
     if (r == c) v += c0;
-    G[e] = v;
+    if (Gh) Gh[e] = from_f32<bf16_t>(v).bits;
+    else G[e] = v;
   }
 }
 
@@ -496,10 +606,11 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) { return from_f32<bf16
 
 __global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
   const int b = blockIdx.z;
-  float alpha = 0.f;
+  float alpha = 0.f, scale = 1.f;
   if (p.ctrl) {
     if (load_status(p.ctrl + b) != PMX_RUNNING) return;
     alpha = (float)p.ctrl[b].alpha;
+    if (p.scale_inv_c) scale = (float)(1.0 / p.ctrl[b].c);
   }
   __shared__ float tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -514,6 +625,7 @@ __global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
     if (gr < p.rows && gc < p.cols) {
       const int64_t off = (int64_t)gr * p.lda + gc;
       v = p.a_bf16 ? __uint_as_float((uint32_t)ab[off] << 16) : af[off];
+      v *= scale;
       if (p.poly) {
         float g = p.degree == 2 ? p.c1 * v + alpha * a2[off] : alpha * v;
         if (gr == gc) g += p.c0;
@@ -574,6 +686,22 @@ __global__ __launch_bounds__(NT) void polar_finish_kernel(PolarFinishParams p) {
   const int it = cb->iter;
   const T* X = reinterpret_cast<const T*>(p.xbuf[it & 1]) + (int64_t)b * p.buf_stride;
   T* U = reinterpret_cast<T*>(p.u) + (int64_t)b * p.u_stride;
+  if (p.vec && !p.transpose) {
+    // straight copy, 16 bytes per thread (cols, ldu and the bases aligned)
+    constexpr int V = 16 / sizeof(T);
+    const int cv = p.cols / V;
+    uint4 nanv;
+    {
+      const uint32_t w = sizeof(T) == 2 ? 0x7FC07FC0u : 0x7FC00000u;
+      nanv = make_uint4(w, w, w, w);
+    }
+    for (int r = blockIdx.x; r < p.rows; r += gridDim.x) {
+      const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)r * p.cols);
+      uint4* dst = reinterpret_cast<uint4*>(U + (int64_t)r * p.ldu);
+      for (int c = threadIdx.x; c < cv; c += NT) dst[c] = bad ? nanv : src[c];
+    }
+    return;
+  }
   for (int r = blockIdx.x; r < p.rows; r += gridDim.x)
   for (int c = threadIdx.x; c < p.cols; c += NT) {
     const int64_t e = (int64_t)r * p.cols + c;
@@ -598,13 +726,18 @@ hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStr
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,
                             int64_t pstride, pmx_matfn_info* info, hipStream_t s) {
-  dim3 grid(grid_rows(rows, kPartialsPerMatrix), batch);
+  // about 2048 blocks in all, at most one per row and kPartialsPerMatrix per matrix
+  const int per = (2048 + batch - 1) / batch;
+  dim3 grid(grid_rows(rows, per < kPartialsPerMatrix ? per : kPartialsPerMatrix), batch);
+  const int V = bf16 ? 8 : 4;
+  const int vec = (cols % V == 0) && (ld % V == 0) && (batch == 1 || stride % V == 0) &&
+                  ((uintptr_t)x % 16 == 0);
   if (bf16)
-    hipLaunchKernelGGL(fro_scale_kernel<bf16_t>, grid, dim3(NT), 0, s,
-                       (const bf16_t*)x, rows, cols, ld, stride, ctrl, partials, pstride, info);
+    hipLaunchKernelGGL(fro_scale_kernel<bf16_t>, grid, dim3(NT), 0, s, (const bf16_t*)x, rows,
+                       cols, ld, stride, vec, ctrl, partials, pstride, info);
   else
     hipLaunchKernelGGL(fro_scale_kernel<float>, grid, dim3(NT), 0, s, (const float*)x, rows,
-                       cols, ld, stride, ctrl, partials, pstride, info);
+                       cols, ld, stride, vec, ctrl, partials, pstride, info);
   return hipGetLastError();
 }
 
@@ -621,31 +754,43 @@ hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hip
   return hipGetLastError();
 }
 
+// Blocks per matrix and job at RW = 2 (the most any launch uses).
 int skinny_blocks(int n, int q) {
   (void)q;
-  return (n + SK_RB - 1) / SK_RB;
+  return (n + 7) / 8;
+}
+
+template <int Q, int RW>
+static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
+  dim3 grid((p.n + 4 * RW - 1) / (4 * RW), njobs, batch);
+  if (gram) hipLaunchKernelGGL((skinny_kernel<Q, RW, true>), grid, dim3(NT), 0, s, p);
+  else hipLaunchKernelGGL((skinny_kernel<Q, RW, false>), grid, dim3(NT), 0, s, p);
 }
 
 hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
-  dim3 grid(skinny_blocks(p.n, p.q), njobs, batch);
   if (gram && njobs != 1) return hipErrorInvalidValue;
+  // eight rows per wave once that still leaves two blocks per compute unit
+  const bool wide = (int64_t)((p.n + 31) / 32) * njobs * batch >= 512;
   if (p.q <= 8) {
-    if (gram) hipLaunchKernelGGL((skinny_kernel<8, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((skinny_kernel<8, false>), grid, dim3(NT), 0, s, p);
+    if (wide) skinny_go<8, 8>(p, njobs, gram, batch, s);
+    else skinny_go<8, 2>(p, njobs, gram, batch, s);
   } else if (p.q <= 16) {
-    if (gram) hipLaunchKernelGGL((skinny_kernel<16, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((skinny_kernel<16, false>), grid, dim3(NT), 0, s, p);
+    if (wide) skinny_go<16, 8>(p, njobs, gram, batch, s);
+    else skinny_go<16, 2>(p, njobs, gram, batch, s);
   } else if (p.q <= 32) {
-    if (gram) hipLaunchKernelGGL((skinny_kernel<32, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((skinny_kernel<32, false>), grid, dim3(NT), 0, s, p);
+    skinny_go<32, 2>(p, njobs, gram, batch, s);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s) {
-  dim3 grid(grid_rows(p.n, 2048), batch);
+hipError_t launch_form_g(const FormGParams& pin, int batch, hipStream_t s) {
+  FormGParams p = pin;
+  p.vec = (p.n % 4 == 0) && (p.stride % 4 == 0) && ((uintptr_t)p.r % 16 == 0) &&
+          (!p.r2 || (uintptr_t)p.r2 % 16 == 0) && ((uintptr_t)p.dst % 16 == 0);
+  const int per = (4096 + batch - 1) / batch;
+  dim3 grid(grid_rows(p.n, per < 2048 ? per : 2048), batch);
   hipLaunchKernelGGL(form_g_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
@@ -677,8 +822,14 @@ hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_polar_finish(const PolarFinishParams& p, bool bf16, int batch, hipStream_t s) {
-  dim3 grid(grid_rows(p.rows, 2048), batch);
+hipError_t launch_polar_finish(const PolarFinishParams& pin, bool bf16, int batch, hipStream_t s) {
+  PolarFinishParams p = pin;
+  const int V = bf16 ? 8 : 4;
+  p.vec = (p.cols % V == 0) && (p.ldu % V == 0) && (p.buf_stride % V == 0) &&
+          (batch == 1 || p.u_stride % V == 0) && ((uintptr_t)p.u % 16 == 0) &&
+          ((uintptr_t)p.xbuf[0] % 16 == 0) && ((uintptr_t)p.xbuf[1] % 16 == 0);
+  const int per = (4096 + batch - 1) / batch;
+  dim3 grid(grid_rows(p.rows, per < 2048 ? per : 2048), batch);
   if (bf16) hipLaunchKernelGGL(polar_finish_kernel<bf16_t>, grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL(polar_finish_kernel<float>, grid, dim3(NT), 0, s, p);
   return hipGetLastError();

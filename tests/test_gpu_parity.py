@@ -233,6 +233,32 @@ def test_polar_bf16(env, m, n):
     assert cf.rel_fro(Un_t, Up) < 3e-2
 
 
+@pytest.mark.parametrize("m,n", [(640, 264), (300, 600)])
+def test_polar_bf16_batched_large_tiles(env, m, n):
+    # 64 matrices: enough 256 x 256 tiles for the large bf16 GEMM tile, with
+    # ragged edges (264 = 256 + 8, 300 = 256 + 44, 600 = 2 * 256 + 88) and
+    # whole interior tiles
+    torch, pmx, dev = env
+    _say("polar bf16 batched", m, n)
+    vals, bits, _ = W.polar_batch(64, max(m, n), min(m, n), 7 * m + n, smin=1e-2)
+    if m < n:
+        vals = np.ascontiguousarray(vals.transpose(0, 2, 1))
+        bits = np.ascontiguousarray(bits.transpose(0, 2, 1))
+    Gt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    U, info = pmx.polar(Gt.to(dev), opts=pmx.default_opts(tol=1e-2))
+    torch.cuda.synchronize()
+    infs = pmx.parse_info(info)
+    Un = U.float().cpu().numpy().astype(np.float64)
+    k = min(m, n)
+    for b in (0, 1, 31, 63):
+        assert int(infs[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), b
+        G = vals[b].astype(np.float64)
+        Up, _ = cf.polar(G if m >= n else G.T)
+        Ub = Un[b] if m >= n else Un[b].T
+        assert np.linalg.norm(Ub.T @ Ub - np.eye(k)) / np.sqrt(k) < 1e-2, b
+        assert cf.rel_fro(Ub, Up) < 3e-2, b
+
+
 def test_polar_bf16_iterations_follow_reference(env):
     torch, pmx, dev = env
     Gt = _bf16(torch, W.polar_batch(1, 512, 128, 9, smin=1e-2)[0][0])
