@@ -20,6 +20,7 @@ struct pmx_context {
   int gemm_map;            // tile order mode
   int bf16_cfg;            // bf16 GEMM tile (-1: by shape, 0 128^2, 1 256^2 x 8 waves, 2 x 4)
   int bf16_map;            // bf16 GEMM: 1 deals whole matrices to XCDs, 0 plain order
+  int skinny_variant;      // skinny products: 0 In through LDS, 1 In read directly
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -334,6 +335,7 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
   SkinnyParams kp;
   memset(&kp, 0, sizeof(kp));
   kp.kbuf = kbuf;
+  kp.variant = q.h->skinny_variant;
   kp.kld = L.kld;
   kp.kstride = L.kstride;
   kp.n = n;
@@ -436,6 +438,8 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   c->bf16_map = 1;
   if (const char* e = getenv("PMX_BF16_CFG")) c->bf16_cfg = atoi(e);
   if (const char* e = getenv("PMX_BF16_MAP")) c->bf16_map = atoi(e);
+  c->skinny_variant = 0;
+  if (const char* e = getenv("PMX_SKINNY")) c->skinny_variant = atoi(e);
   *handle = c;
   return PMX_OK;
 }

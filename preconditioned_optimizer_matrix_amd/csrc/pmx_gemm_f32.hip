@@ -180,6 +180,146 @@ __device__ __forceinline__ void read_frag(float (&f)[8], const float* __restrict
   }
 }
 
+// Main loop of a whole tile (every load in bounds, K a multiple of BK) with
+// A stored k-contiguous and B stored m/n-contiguous, the layout of every
+// square product of the iteration.  A k tile is one basic block whose
+// schedule is fixed with scheduling-group barriers: the A fragments of the
+// whole k tile and the first B fragments are read, the next tile's global
+// loads issued (with the polynomial formed as they arrive), and each k step's
+// MFMAs are interleaved with the B fragment reads of the following step; the
+// last step's MFMAs are interleaved with the LDS stores of the next tile
+// (into the other buffer, which no wave reads in this k tile).
+template <int MF, int OPS, int MASK, int PER>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (MF > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int k = OPS < PER ? OPS : PER;
+    if constexpr (k > 0) __builtin_amdgcn_sched_group_barrier(MASK, k, 0);
+    sched_interleave<MF - 1, OPS - k, MASK, PER>();
+  } else if constexpr (OPS > 0) {
+    __builtin_amdgcn_sched_group_barrier(MASK, OPS, 0);
+  }
+}
+
+template <class C, bool APOLY, bool BPOLY, int FM_, int FN_>
+__device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[FM_][FN_], float* smem_a0,
+                                              float* smem_b0, const float* __restrict__ A,
+                                              const float* __restrict__ A2, int64_t lda,
+                                              const float* __restrict__ B,
+                                              const float* __restrict__ B2, int64_t ldb,
+                                              const PolyCtx& pc, int m0, int n0, int nk,
+                                              int lane, int wm, int wn) {
+  using TA = OpTile<C, true, C::BM>;
+  using TB = OpTile<C, false, C::BN>;
+  constexpr int FM = C::FM, FN = C::FN, BK = C::BK, KH = C::KH;
+  constexpr int NA = TA::PER_THREAD, NB = TB::PER_THREAD;
+  constexpr int MF = FM * FN;
+  static_assert(KH == 8, "one A fragment read pair per k tile");
+  static_assert(FM_ == FM && FN_ == FN, "accumulator shape");
+  auto smem_a = [&](int st) { return smem_a0 + st * TA::FLOATS; };
+  auto smem_b = [&](int st) { return smem_b0 + st * TB::FLOATS; };
+  const int t = threadIdx.x;
+  // A (KC): item idx -> row idx / (BK / 4), k 4 (idx % (BK / 4))
+  // B (MC): item idx -> k idx / (BN / 4), column 4 (idx % (BN / 4))
+  int64_t aoff[NA], boff[NB];
+  int alds[NA], blds[NB], arow[NA], acol[NA], brow[NB], bcol[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int idx = t + C::NT * i;
+    arow[i] = idx / (BK / 4);
+    acol[i] = (idx % (BK / 4)) * 4;
+    aoff[i] = (int64_t)(m0 + arow[i]) * lda + acol[i];
+    alds[i] = arow[i] * TA::LD + acol[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int idx = t + C::NT * i;
+    brow[i] = idx / (C::BN / 4);
+    bcol[i] = (idx % (C::BN / 4)) * 4;
+    boff[i] = (int64_t)brow[i] * ldb + n0 + bcol[i];
+    blds[i] = brow[i] * TB::LD + bcol[i];
+  }
+  // polynomial element (i, j) of the stored matrix: c0 [i == j] + c1 R + alpha R2
+  auto poly4 = [&](f32x4 r1, f32x4 r2, int i, int j) {
+    f32x4 g;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      g[u] = pc.degree == 2 ? pc.c1 * r1[u] + pc.alpha * r2[u] : pc.alpha * r1[u];
+      if (i == j + u) g[u] += pc.c0;
+    }
+    return g;
+  };
+  f32x4 ra[NA], rb[NB], ra2[NA], rb2[NB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      ra[i] = *reinterpret_cast<const f32x4*>(A + aoff[i] + k0);
+      if (APOLY && pc.degree == 2) ra2[i] = *reinterpret_cast<const f32x4*>(A2 + aoff[i] + k0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      rb[i] = *reinterpret_cast<const f32x4*>(B + boff[i] + (int64_t)k0 * ldb);
+      if (BPOLY && pc.degree == 2)
+        rb2[i] = *reinterpret_cast<const f32x4*>(B2 + boff[i] + (int64_t)k0 * ldb);
+    }
+  };
+  auto lstore = [&](int stage, int k0) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const f32x4 v = APOLY ? poly4(ra[i], ra2[i], m0 + arow[i], k0 + acol[i]) : ra[i];
+      *reinterpret_cast<f32x4*>(smem_a(stage) + alds[i]) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const f32x4 v = BPOLY ? poly4(rb[i], rb2[i], k0 + brow[i], n0 + bcol[i]) : rb[i];
+      *reinterpret_cast<f32x4*>(smem_b(stage) + blds[i]) = v;
+    }
+  };
+  gload(0);
+  lstore(0, 0);
+  __syncthreads();
+  const int fa_ofs = (wm + (lane & 31)) * TA::LD + (lane >> 5) * KH;
+  const int fb_ofs = ((lane >> 5) * KH) * TB::LD + wn + (lane & 31);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;  // the last tile reloads itself
+    const float* sa = smem_a(cur) + fa_ofs;
+    const float* sb = smem_b(cur) + fb_ofs;
+    f32x4 fa[FM][2];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      fa[i][0] = *reinterpret_cast<const f32x4*>(sa + 32 * i * TA::LD);
+      fa[i][1] = *reinterpret_cast<const f32x4*>(sa + 32 * i * TA::LD + 4);
+    }
+    float fb[2][FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = sb[32 * j];
+    gload(kn);
+#pragma unroll
+    for (int s = 0; s < KH; ++s) {
+      const int c = s & 1, n = c ^ 1;
+      if (s + 1 < KH) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[n][j] = sb[(s + 1) * TB::LD + 32 * j];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s >> 2][s & 3], fb[c][j],
+                                                           acc[i][j], 0, 0, 0);
+    }
+    lstore(cur ^ 1, kn);
+    // schedule of the k tile
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM + FN, 0);  // A, first B fragments
+    __builtin_amdgcn_sched_group_barrier(0x020, (NA + NB) * ((APOLY || BPOLY) ? 2 : 1), 0);
+#pragma unroll
+    for (int s = 0; s + 1 < KH; ++s) sched_interleave<MF, FN, 0x100, (FN + MF - 1) / MF>();
+    sched_interleave<MF, NA + NB, 0x200, (NA + NB + MF - 1) / MF>();
+    __syncthreads();
+  }
+}
+
 // Work item -> (matrix-problem z, tile m, tile n).  mode 1 additionally
 // permutes every full round of G items so that the blocks resident at the
 // same time on one XCD (workgroups go to the 8 XCDs round-robin by block
@@ -272,8 +412,25 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int nk = (p.K + C::BK - 1) / C::BK;
-    f32x4 ra[TAo::PER_THREAD], rb[TBo::PER_THREAD];
     __syncthreads();  // the previous item's last LDS reads are done
+    if constexpr (AKC && !BKC && C::STAGES == 2 && C::KH == 8) {
+      if (vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && p.K % C::BK == 0 &&
+          !(apoly && bpoly) && !(apoly && A2 == A && pc.degree == 2) &&
+          !(bpoly && B2 == B && pc.degree == 2)) {
+        if (apoly)
+          mainloop_fast<C, true, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2, pr.b.ld, pc,
+                                        m0, n0, nk, lane, wm, wn);
+        else if (bpoly)
+          mainloop_fast<C, false, true>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2, pr.b.ld, pc,
+                                        m0, n0, nk, lane, wm, wn);
+        else
+          mainloop_fast<C, false, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2, pr.b.ld, pc,
+                                         m0, n0, nk, lane, wm, wn);
+        goto epilogue;
+      }
+    }
+    {
+    f32x4 ra[TAo::PER_THREAD], rb[TBo::PER_THREAD];
     load_tile<C, AKC, C::BM>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, 0, p.K, vec);
     load_tile<C, BKC, C::BN>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, 0, p.K, vec);
     store_tile<C, AKC, C::BM>(smem_a[0], ra);
@@ -317,7 +474,9 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
         }
       }
     }
+    }
 
+  epilogue:
     // Epilogue.  Lane l of a 32x32 accumulator holds column (l % 32) and rows
     // 8 * (v / 4) + 4 * (l / 32) + (v % 4), v = 0..15.
     const int hi = lane >> 5, col_in = lane & 31;

@@ -73,6 +73,7 @@ struct SkinnyParams {
   float* kbuf;
   int64_t kld, kstride;
   int n, q;
+  int variant;  // 0: In staged through LDS, 1: In read directly
   Ctrl* ctrl;
   // last pass only: Gram shares (16 doubles per block) and the alpha solve
   double* gram_partials;

@@ -353,89 +353,19 @@ __device__ __forceinline__ void halve_reduce(float* acc, int lane) {
 constexpr int SK_CH = 512;           // In rows per LDS chunk
 constexpr int SK_LD = SK_CH + 4;     // column stride of the staged chunk
 
+// Reduction, output and (GRAM) Gram share / alpha fit of a skinny product:
+// acc holds the lane's RW x Q partial sums for rows row0 .. row0 + RW - 1.
 template <int Q, int RW, bool GRAM>
-__global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
-  constexpr int CNT = RW * Q;                   // partial sums per lane
-  constexpr int NV = CNT > 64 ? CNT / 64 : 1;   // complete sums per lane
-  constexpr int SHARE = CNT < 64 ? 64 / CNT : 1;  // lanes holding each sum
-  constexpr int RB = 4 * RW;
-  const int b = blockIdx.z;
-  Ctrl* cb = p.ctrl + b;
-  if (load_status(cb) != PMX_RUNNING) return;
-  const SkinnyJob& job = p.job[blockIdx.y];
-  const int n = p.n;
-  const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
-  float* kb = p.kbuf + (int64_t)b * p.kstride;
-  const double fro = cb->fro;
-  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
-
-  __shared__ __attribute__((aligned(16))) float in_lds[Q * SK_LD];
+__device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const SkinnyParams& p,
+                                              const SkinnyJob& job, int b, int row0,
+                                              float scale, double fro) {
+  constexpr int CNT = RW * Q;
+  constexpr int NV = CNT > 64 ? CNT / 64 : 1;
+  constexpr int SHARE = CNT < 64 ? 64 / CNT : 1;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int row0 = blockIdx.x * RB + wid * RW;
-  const bool vec = (job.mat_ld % 4 == 0) && ((((uintptr_t)mat) & 15) == 0);
-  const bool in_vec = (p.kld % 4 == 0) && (job.in_col % 4 == 0) && (p.q == Q) &&
-                      ((((uintptr_t)kb) & 15) == 0);
-
-  float acc[CNT];
-#pragma unroll
-  for (int i = 0; i < CNT; ++i) acc[i] = 0.f;
-
-  for (int j0 = 0; j0 < n; j0 += SK_CH) {
-    __syncthreads();
-    // stage In[j0 .. j0 + 512)[0 .. Q) column-major (zero beyond n and q)
-    if (in_vec) {
-      // one 16-byte load per (row, 4 columns)
-      for (int idx = threadIdx.x; idx < SK_CH * (Q / 4); idx += NT) {
-        const int jj = idx / (Q / 4), c = 4 * (idx - jj * (Q / 4));
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j0 + jj < n)
-          v = *reinterpret_cast<const float4*>(kb + (int64_t)(j0 + jj) * p.kld + job.in_col + c);
-        in_lds[(c + 0) * SK_LD + jj] = v.x;
-        in_lds[(c + 1) * SK_LD + jj] = v.y;
-        in_lds[(c + 2) * SK_LD + jj] = v.z;
-        in_lds[(c + 3) * SK_LD + jj] = v.w;
-      }
-    } else {
-      for (int idx = threadIdx.x; idx < SK_CH * Q; idx += NT) {
-        const int jj = idx / Q, c = idx - jj * Q;
-        float v = 0.f;
-        if (j0 + jj < n && c < p.q) v = kb[(int64_t)(j0 + jj) * p.kld + job.in_col + c];
-        in_lds[c * SK_LD + jj] = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < SK_CH / 256; ++t) {
-      const int jj = 256 * t + 4 * lane;
-      const int j = j0 + jj;
-      if (j >= n) continue;
-      float4 m[RW];
-#pragma unroll
-      for (int rr = 0; rr < RW; ++rr) {
-        const int row = row0 + rr;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row < n) {
-          const float* src = mat + (int64_t)row * job.mat_ld + j;
-          if (vec && j + 3 < n) {
-            v = *reinterpret_cast<const float4*>(src);
-          } else {
-            v.x = src[0];
-            if (j + 1 < n) v.y = src[1];
-            if (j + 2 < n) v.z = src[2];
-            if (j + 3 < n) v.w = src[3];
-          }
-        }
-        m[rr] = v;
-      }
-#pragma unroll
-      for (int c = 0; c < Q; ++c) {
-        const float4 x = *reinterpret_cast<const float4*>(in_lds + c * SK_LD + jj);
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr)
-          acc[rr * Q + c] += m[rr].x * x.x + m[rr].y * x.y + m[rr].z * x.z + m[rr].w * x.w;
-      }
-    }
-  }
+  const int n = p.n;
+  Ctrl* cb = p.ctrl + b;
+  float* kb = p.kbuf + (int64_t)b * p.kstride;
   halve_reduce<CNT, 32>(acc, lane);
   // lane l holds value indices NV l .. NV l + NV - 1 (CNT >= 64) or l / SHARE
   bool valid[NV];
@@ -528,6 +458,283 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
       cb->counter = 0u;
     }
   }
+}
+
+template <int Q, int RW, bool GRAM>
+__global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
+  constexpr int CNT = RW * Q;  // partial sums per lane
+  constexpr int RB = 4 * RW;
+  const int b = blockIdx.z;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const SkinnyJob& job = p.job[blockIdx.y];
+  const int n = p.n;
+  const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
+  float* kb = p.kbuf + (int64_t)b * p.kstride;
+  const double fro = cb->fro;
+  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+
+  __shared__ __attribute__((aligned(16))) float in_lds[Q * SK_LD];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * RB + wid * RW;
+  const bool vec = (job.mat_ld % 4 == 0) && ((((uintptr_t)mat) & 15) == 0);
+  const bool in_vec = (p.kld % 4 == 0) && (job.in_col % 4 == 0) && (p.q == Q) &&
+                      ((((uintptr_t)kb) & 15) == 0);
+
+  float acc[CNT];
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) acc[i] = 0.f;
+
+  for (int j0 = 0; j0 < n; j0 += SK_CH) {
+    __syncthreads();
+    // stage In[j0 .. j0 + 512)[0 .. Q) column-major (zero beyond n and q)
+    if (in_vec) {
+      // one 16-byte load per (row, 4 columns)
+      for (int idx = threadIdx.x; idx < SK_CH * (Q / 4); idx += NT) {
+        const int jj = idx / (Q / 4), c = 4 * (idx - jj * (Q / 4));
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j0 + jj < n)
+          v = *reinterpret_cast<const float4*>(kb + (int64_t)(j0 + jj) * p.kld + job.in_col + c);
+        in_lds[(c + 0) * SK_LD + jj] = v.x;
+        in_lds[(c + 1) * SK_LD + jj] = v.y;
+        in_lds[(c + 2) * SK_LD + jj] = v.z;
+        in_lds[(c + 3) * SK_LD + jj] = v.w;
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < SK_CH * Q; idx += NT) {
+        const int jj = idx / Q, c = idx - jj * Q;
+        float v = 0.f;
+        if (j0 + jj < n && c < p.q) v = kb[(int64_t)(j0 + jj) * p.kld + job.in_col + c];
+        in_lds[c * SK_LD + jj] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < SK_CH / 256; ++t) {
+      const int jj = 256 * t + 4 * lane;
+      const int j = j0 + jj;
+      if (j >= n) continue;
+      float4 m[RW];
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr) {
+        const int row = row0 + rr;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row < n) {
+          const float* src = mat + (int64_t)row * job.mat_ld + j;
+          if (vec && j + 3 < n) {
+            v = *reinterpret_cast<const float4*>(src);
+          } else {
+            v.x = src[0];
+            if (j + 1 < n) v.y = src[1];
+            if (j + 2 < n) v.z = src[2];
+            if (j + 3 < n) v.w = src[3];
+          }
+        }
+        m[rr] = v;
+      }
+#pragma unroll
+      for (int c = 0; c < Q; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(in_lds + c * SK_LD + jj);
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr)
+          acc[rr * Q + c] += m[rr].x * x.x + m[rr].y * x.y + m[rr].z * x.z + m[rr].w * x.w;
+      }
+    }
+  }
+  skinny_finish<Q, RW, GRAM>(acc, p, job, b, row0, scale, fro);
+}
+
+// The same product software-pipelined: while chunk c (CH rows of In, CH
+// columns of Mat) is multiplied, the Mat loads and the In staging loads of
+// chunk c + 1 are in flight; In is double buffered in LDS, so there is one
+// barrier per chunk.
+template <int Q, int RW, int CH, bool GRAM>
+__global__ __launch_bounds__(NT) void skinny_pipe_kernel(SkinnyParams p) {
+  constexpr int CNT = RW * Q;
+  constexpr int RB = 4 * RW;
+  constexpr int T = CH / 256;            // 4-column steps per lane per chunk
+  constexpr int LD = CH + 4;             // column stride of a staged chunk
+  constexpr int IV = CH * Q / 4 / NT;    // 16-byte In loads per thread per chunk
+  static_assert(IV >= 1 && IV * NT * 4 == CH * Q, "chunk / thread mismatch");
+  const int b = blockIdx.z;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const SkinnyJob& job = p.job[blockIdx.y];
+  const int n = p.n;
+  const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
+  const float* __restrict__ in = p.kbuf + (int64_t)b * p.kstride + job.in_col;
+  const double fro = cb->fro;
+  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+  __shared__ __attribute__((aligned(16))) float in_lds[2][Q * LD];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * RB + wid * RW;
+  const bool vec = (job.mat_ld % 4 == 0) && ((((uintptr_t)mat) & 15) == 0) && (n % 4 == 0);
+  const bool in_vec = (p.kld % 4 == 0) && (job.in_col % 4 == 0) && (p.q == Q) &&
+                      ((((uintptr_t)p.kbuf) & 15) == 0) && (p.kstride % 4 == 0);
+
+  auto load_m = [&](float4 (&m)[T][RW], int j0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int j = j0 + 256 * t + 4 * lane;
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr) {
+        const int row = row0 + rr;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row < n && j < n) {
+          const float* src = mat + (int64_t)row * job.mat_ld + j;
+          if (vec) {
+            v = *reinterpret_cast<const float4*>(src);
+          } else {
+            v.x = src[0];
+            if (j + 1 < n) v.y = src[1];
+            if (j + 2 < n) v.z = src[2];
+            if (j + 3 < n) v.w = src[3];
+          }
+        }
+        m[t][rr] = v;
+      }
+    }
+  };
+  // In chunk rows j0 .. j0 + CH, thread item idx -> (row idx / (Q / 4), 4 columns)
+  auto load_in = [&](float4 (&iv)[IV], int j0) {
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      const int jj = idx / (Q / 4), c = 4 * (idx % (Q / 4));
+      const int j = j0 + jj;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < n) {
+        const float* src = in + (int64_t)j * p.kld + c;
+        if (in_vec) {
+          v = *reinterpret_cast<const float4*>(src);
+        } else {
+          if (c + 0 < p.q) v.x = src[0];
+          if (c + 1 < p.q) v.y = src[1];
+          if (c + 2 < p.q) v.z = src[2];
+          if (c + 3 < p.q) v.w = src[3];
+        }
+      }
+      iv[i] = v;
+    }
+  };
+  auto store_in = [&](float* lds, const float4 (&iv)[IV]) {
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      const int jj = idx / (Q / 4), c = 4 * (idx % (Q / 4));
+      lds[(c + 0) * LD + jj] = iv[i].x;
+      lds[(c + 1) * LD + jj] = iv[i].y;
+      lds[(c + 2) * LD + jj] = iv[i].z;
+      lds[(c + 3) * LD + jj] = iv[i].w;
+    }
+  };
+
+  float acc[CNT];
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) acc[i] = 0.f;
+  float4 m[T][RW], mn[T][RW], iv[IV];
+  load_m(m, 0);
+  load_in(iv, 0);
+  store_in(in_lds[0], iv);
+  __syncthreads();
+  const int nch = (n + CH - 1) / CH;
+  for (int c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    if (more) {
+      load_m(mn, (c + 1) * CH);
+      load_in(iv, (c + 1) * CH);
+    }
+    const float* lds = in_lds[c & 1];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int jj = 256 * t + 4 * lane;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const float4 x = *reinterpret_cast<const float4*>(lds + q * LD + jj);
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr)
+          acc[rr * Q + q] += m[t][rr].x * x.x + m[t][rr].y * x.y + m[t][rr].z * x.z + m[t][rr].w * x.w;
+      }
+    }
+    if (more) store_in(in_lds[(c + 1) & 1], iv);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) m[t][rr] = mn[t][rr];
+    }
+  }
+  skinny_finish<Q, RW, GRAM>(acc, p, job, b, row0, scale, fro);
+}
+
+// The same product without LDS: each lane reads the In rows of its four
+// columns directly (16-byte loads, L1/L2 resident: In is n x q) next to the
+// RW rows of Mat, so a block has no barriers and keeps its loads in flight.
+template <int Q, int RW, bool GRAM>
+__global__ __launch_bounds__(NT) void skinny_stream_kernel(SkinnyParams p) {
+  constexpr int CNT = RW * Q;
+  constexpr int RB = 4 * RW;
+  const int b = blockIdx.z;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const SkinnyJob& job = p.job[blockIdx.y];
+  const int n = p.n;
+  const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
+  const float* __restrict__ in = p.kbuf + (int64_t)b * p.kstride + job.in_col;
+  const double fro = cb->fro;
+  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * RB + wid * RW;
+  const bool vec = (job.mat_ld % 4 == 0) && ((((uintptr_t)mat) & 15) == 0) && (n % 4 == 0) &&
+                   (p.kld % 4 == 0) && (job.in_col % 4 == 0) && (p.q == Q) &&
+                   ((((uintptr_t)p.kbuf) & 15) == 0) && (p.kstride % 4 == 0);
+  float acc[CNT];
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) acc[i] = 0.f;
+  if (vec) {
+#pragma unroll 2
+    for (int j = 4 * lane; j < n; j += 256) {
+      float4 m[RW];
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr)
+        m[rr] = (row0 + rr < n)
+                    ? *reinterpret_cast<const float4*>(mat + (int64_t)(row0 + rr) * job.mat_ld + j)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 x[4][Q / 4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c4 = 0; c4 < Q / 4; ++c4)
+          x[u][c4] = *reinterpret_cast<const float4*>(in + (int64_t)(j + u) * p.kld + 4 * c4);
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+        for (int c4 = 0; c4 < Q / 4; ++c4) {
+          float* a = acc + rr * Q + 4 * c4;
+          a[0] += m[rr].x * x[0][c4].x + m[rr].y * x[1][c4].x + m[rr].z * x[2][c4].x + m[rr].w * x[3][c4].x;
+          a[1] += m[rr].x * x[0][c4].y + m[rr].y * x[1][c4].y + m[rr].z * x[2][c4].y + m[rr].w * x[3][c4].y;
+          a[2] += m[rr].x * x[0][c4].z + m[rr].y * x[1][c4].z + m[rr].z * x[2][c4].z + m[rr].w * x[3][c4].z;
+          a[3] += m[rr].x * x[0][c4].w + m[rr].y * x[1][c4].w + m[rr].z * x[2][c4].w + m[rr].w * x[3][c4].w;
+        }
+    }
+  } else {
+    for (int j = 4 * lane; j < n; j += 256) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j + u >= n) break;
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+          if (row0 + rr >= n) break;
+          const float mv = mat[(int64_t)(row0 + rr) * job.mat_ld + j + u];
+#pragma unroll
+          for (int c = 0; c < Q; ++c)
+            if (c < p.q) acc[rr * Q + c] += mv * in[(int64_t)(j + u) * p.kld + c];
+        }
+      }
+    }
+  }
+  skinny_finish<Q, RW, GRAM>(acc, p, job, b, row0, scale, fro);
 }
 
 // ---------------------------------------------------------------- polynomial
@@ -763,19 +970,31 @@ int skinny_blocks(int n, int q) {
 template <int Q, int RW>
 static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
   dim3 grid((p.n + 4 * RW - 1) / (4 * RW), njobs, batch);
+  if (p.variant == 1) {
+    if (gram) hipLaunchKernelGGL((skinny_stream_kernel<Q, RW, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((skinny_stream_kernel<Q, RW, false>), grid, dim3(NT), 0, s, p);
+    return;
+  }
+  if (p.variant == 2) {
+    constexpr int CH = (RW <= 2 && Q <= 8) ? 512 : 256;
+    if (gram) hipLaunchKernelGGL((skinny_pipe_kernel<Q, RW, CH, true>), grid, dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((skinny_pipe_kernel<Q, RW, CH, false>), grid, dim3(NT), 0, s, p);
+    return;
+  }
   if (gram) hipLaunchKernelGGL((skinny_kernel<Q, RW, true>), grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL((skinny_kernel<Q, RW, false>), grid, dim3(NT), 0, s, p);
 }
 
 hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
   if (gram && njobs != 1) return hipErrorInvalidValue;
-  // eight rows per wave once that still leaves two blocks per compute unit
+  // more rows per wave once that still leaves two blocks per compute unit
   const bool wide = (int64_t)((p.n + 31) / 32) * njobs * batch >= 512;
   if (p.q <= 8) {
     if (wide) skinny_go<8, 8>(p, njobs, gram, batch, s);
     else skinny_go<8, 2>(p, njobs, gram, batch, s);
   } else if (p.q <= 16) {
-    if (wide) skinny_go<16, 8>(p, njobs, gram, batch, s);
+    if (wide && p.variant != 0) skinny_go<16, 4>(p, njobs, gram, batch, s);
+    else if (wide) skinny_go<16, 8>(p, njobs, gram, batch, s);
     else skinny_go<16, 2>(p, njobs, gram, batch, s);
   } else if (p.q <= 32) {
     skinny_go<32, 2>(p, njobs, gram, batch, s);
