@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--max-iter", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy a 256 MiB fp32 buffer 4 times (a plain copy kernel of "
+                         "known traffic, for scaling HBM byte counters)")
     ap.add_argument("--workload", default="shampoo_1024x4096",
                     choices=["shampoo_1024x4096", "spd_64", "blocks_64x512",
                              "muon_32x4096x1024", "mp_10000"])
@@ -184,12 +187,45 @@ def other_workload(args):
     print(json.dumps(out), flush=True)
 
 
+def calibrate_copy():
+    """A plain device copy of known size: 4 launches, each reading and writing
+    256 MiB, so FETCH_SIZE / WRITE_SIZE per launch should read 262144 KiB."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": a.numel() * 4, "launches": 4}), flush=True)
+
+
+def update_traffic(n_launch):
+    """HBM bytes per update-GEMM launch measured with rocprofv3 counters
+    (profiles/update_gemm_traffic.json), or None when the GEMM source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "update_gemm_traffic.json")
+    src = os.path.join(ROOT, "preconditioned_optimizer_matrix_amd", "csrc", "pmx_gemm_f32.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256") != digest or rec.get("launches_per_step") != n_launch:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: every GPU box here has one GPU, and the path "
               "has no multi-GPU implementation (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        return calibrate_copy()
     if args.workload != "shampoo_1024x4096":
         return other_workload(args)
     import torch
@@ -268,25 +304,36 @@ def main():
     roofline = None
     trace = None
     if not args.no_trace:
-        # one more step with the launch trace: per-class kernel time and launches
+        # one more step with the launch trace: per-class kernel time and
+        # launches; the R^-1/4 call is collected on its own for the roofline of
+        # its update GEMM (the n = 4096 instantiation, one kernel).
         pmx.trace_enable(True)
-        step()
-        trace = pmx.trace_collect()
+        L.copy_(L9)
+        R.copy_(R9)
+        pmx.shampoo_stats_update(G, L, R, beta, eps)
+        pmx.inv_root(L, 4, opts=opts, aux=False, out=Li, info=infoL, ws=wsL)
+        tr_pre = pmx.trace_collect()
+        pmx.inv_root(R, 4, opts=opts, aux=False, out=Ri, info=infoR, ws=wsR)
+        tr_r = pmx.trace_collect()
+        pmx.precond_apply(Li, G, Ri, out=P, ws=wsA)
+        tr_post = pmx.trace_collect()
         pmx.trace_enable(False)
-        t_ms, launches = trace["gemm_update"]
-        iL2, iR2 = pmx.parse_info(infoL)[0], pmx.parse_info(infoR)[0]
-
-        def upd_products(info):
-            return sum(2 * int(it) - 1 for it in info["iters"] if int(it) > 0)
-
-        flops = (upd_products(iL2) * 2.0 * m ** 3 + upd_products(iR2) * 2.0 * n ** 3)
+        trace = {k: (tr_pre[k][0] + tr_r[k][0] + tr_post[k][0],
+                     tr_pre[k][1] + tr_r[k][1] + tr_post[k][1]) for k in tr_r}
+        t_ms, launches = tr_r["gemm_update"]
+        iR2 = pmx.parse_info(infoR)[0]
+        # update products of a stage with k iterations: 2 k - 1 (Z_1 = g is formed directly)
+        products = sum(2 * int(it) - 1 for it in iR2["iters"] if int(it) > 0)
+        flops = products * 2.0 * n ** 3
         avg_ms = t_ms / max(launches, 1)
         achieved = flops / launches / (avg_ms * 1e-3) / 1e12
-        roofline = dict(bound="mfma", kernel="gemm_f32_kernel<false,false,ROLE_UPDATE>",
+        roofline = dict(bound="mfma",
+                        kernel="gemm_f32_kernel<Cfg<128,128,16,2,2,3>,NN,ROLE_UPDATE> (n=4096)",
                         achieved=round(achieved, 2), peak=PEAK_FP32_MFMA, unit="TFLOP/s",
-                        frac=round(achieved / PEAK_FP32_MFMA, 4), traffic=None,
+                        frac=round(achieved / PEAK_FP32_MFMA, 4),
+                        traffic=update_traffic(int(launches)),
                         launches=int(launches), avg_launch_ms=round(avg_ms, 4),
-                        algorithmic_flops_per_launch=round(flops / launches, 1))
+                        products=products, algorithmic_flops_per_launch=round(flops / launches, 1))
         log("trace:", {k: (round(v[0], 3), v[1]) for k, v in trace.items()})
 
     cpu = None
