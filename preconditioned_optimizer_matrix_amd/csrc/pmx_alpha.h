@@ -1,0 +1,177 @@
+// The on-device alpha fit of a PRISM update (shared by the Krylov kernel and
+// the fused small-matrix kernel): from the Gram of the scaled Krylov blocks to
+// the argmin of the sketched quartic on [lo, hi].
+#pragma once
+
+#include "pmx_kernels.h"
+
+namespace pmx {
+
+// ---------------------------------------------------------------- alpha fit
+// Real roots of a x^2 + b x + c inside (lo, hi).
+__device__ inline int quad_roots_in(double a, double b, double c, double lo, double hi, double* out) {
+  int n = 0;
+  const double scale = fmax(fabs(a), fmax(fabs(b), fabs(c)));
+  if (scale == 0.0) return 0;
+  if (fabs(a) <= 1e-14 * scale) {
+    if (b != 0.0) {
+      const double x = -c / b;
+      if (x > lo && x < hi) out[n++] = x;
+    }
+    return n;
+  }
+  const double disc = b * b - 4.0 * a * c;
+  if (disc < 0.0) return 0;
+  const double sq = sqrt(disc);
+  const double q = -0.5 * (b + (b >= 0.0 ? sq : -sq));
+  const double x1 = q / a;
+  const double x2 = (q != 0.0) ? c / q : x1;
+  if (x1 > lo && x1 < hi) out[n++] = x1;
+  if (x2 > lo && x2 < hi && x2 != x1) out[n++] = x2;
+  return n;
+}
+
+// argmin over [lo, hi] of phi(a) = w0 + w1 a + w2 a^2 + w3 a^3 + w4 a^4.
+// phi' is a cubic; the roots of phi'' split [lo, hi] into pieces on which
+// phi' is monotone, and every sign change of phi' on a piece is refined to
+// full double precision by bracketed Newton steps.  Candidates are both ends and those critical
+// points; the smallest phi wins, ties to the smaller alpha.
+__device__ inline double argmin_quartic(const double (&w)[5], double lo, double hi) {
+  auto phi = [&](double a) { return w[0] + a * (w[1] + a * (w[2] + a * (w[3] + a * w[4]))); };
+  auto dphi = [&](double a) { return w[1] + a * (2.0 * w[2] + a * (3.0 * w[3] + a * 4.0 * w[4])); };
+  auto d2phi = [&](double a) { return 2.0 * w[2] + a * (6.0 * w[3] + a * 12.0 * w[4]); };
+  double brk[4];
+  int nb = 0;
+  brk[nb++] = lo;
+  double qr[2];
+  const int nq = quad_roots_in(12.0 * w[4], 6.0 * w[3], 2.0 * w[2], lo, hi, qr);
+  if (nq == 2 && qr[1] < qr[0]) {
+    const double t = qr[0];
+    qr[0] = qr[1];
+    qr[1] = t;
+  }
+  for (int i = 0; i < nq; ++i) brk[nb++] = qr[i];
+  brk[nb++] = hi;
+  double cand[6];
+  int nc = 0;
+  cand[nc++] = lo;
+  for (int i = 0; i + 1 < nb; ++i) {
+    double x0 = brk[i], x1 = brk[i + 1];
+    double f0 = dphi(x0);
+    const double f1 = dphi(x1);
+    if (f0 == 0.0) {
+      if (x0 > lo && x0 < hi) cand[nc++] = x0;
+      continue;
+    }
+    if ((f0 < 0.0) == (f1 < 0.0) || f1 == 0.0) continue;
+    // phi' is monotone on the piece: Newton steps on phi' kept inside the
+    // sign-change bracket (a bisection step whenever Newton would leave it)
+    // converge quadratically; stop at a step within 4 ulp or an exhausted
+    // bracket.
+    double x = 0.5 * (x0 + x1);
+    for (int it = 0; it < 100; ++it) {
+      const double fx = dphi(x);
+      if (fx == 0.0) break;
+      if ((fx < 0.0) == (f0 < 0.0)) {
+        x0 = x;
+        f0 = fx;
+      } else {
+        x1 = x;
+      }
+      const double d2 = d2phi(x);
+      if (d2 != 0.0) {
+        const double step = fx / d2;
+        if (fabs(step) <= 8.881784197001252e-16 * fabs(x)) {
+          x -= step;
+          break;
+        }
+      }
+      double xn = (d2 != 0.0) ? x - fx / d2 : 0.5 * (x0 + x1);
+      if (!(xn > x0 && xn < x1)) xn = 0.5 * (x0 + x1);
+      if (!(xn > x0 && xn < x1)) break;
+      x = xn;
+    }
+    if (x > lo && x < hi) cand[nc++] = x;
+  }
+  cand[nc++] = hi;
+  for (int i = 1; i < nc; ++i)
+    for (int j = i; j > 0 && cand[j] < cand[j - 1]; --j) {
+      const double t = cand[j];
+      cand[j] = cand[j - 1];
+      cand[j - 1] = t;
+    }
+  double best = cand[0], bv = phi(cand[0]);
+  for (int i = 1; i < nc; ++i) {
+    const double v = phi(cand[i]);
+    if (v < bv) {
+      bv = v;
+      best = cand[i];
+    }
+  }
+  return best;
+}
+
+// alpha from the Gram G (upper triangle, row-major, of the J x J Gram of the
+// scaled Krylov blocks K~_j = (R/s)^j S, j = 1..J, J = 2d + 1): the
+// coefficient vectors of r(xi; alpha) are rescaled by s^j to undo the Krylov
+// scaling, the quartic phi_S(alpha) = c(alpha)^T M c(alpha) is formed, and its
+// argmin on [lo, hi] is taken.  A degenerate or non-finite quartic gives c_d.
+template <int J>
+__device__ inline double alpha_from_gram_t(const double* G, double s, const AlphaCoef& co,
+                                           double lo, double hi) {
+  double av[3][J];
+  double sp = 1.0;
+#pragma unroll
+  for (int j = 1; j <= J; ++j) {
+    sp *= s;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) av[i][j - 1] = co.a[i][j] * sp;
+  }
+  // full J x J Gram from the packed upper triangle, then u_i = M a_i
+  double M[J][J];
+  {
+    int t = 0;
+#pragma unroll
+    for (int x = 0; x < J; ++x)
+#pragma unroll
+      for (int y = x; y < J; ++y, ++t) M[x][y] = M[y][x] = G[t];
+  }
+  double u[3][J];
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int x = 0; x < J; ++x) {
+      double v = 0.0;
+#pragma unroll
+      for (int y = 0; y < J; ++y) v += M[x][y] * av[i][y];
+      u[i][x] = v;
+    }
+  auto q = [&](int i1, int i2) {
+    double t = 0.0;
+#pragma unroll
+    for (int x = 0; x < J; ++x) t += av[i1][x] * u[i2][x];
+    return t;
+  };
+  double w[5];
+  w[0] = q(0, 0);
+  w[1] = q(0, 1) + q(1, 0);
+  w[2] = q(1, 1) + q(0, 2) + q(2, 0);
+  w[3] = q(1, 2) + q(2, 1);
+  w[4] = q(2, 2);
+  bool ok = true;
+  double mx = 0.0;
+#pragma unroll
+  for (int e = 0; e < 5; ++e) ok = ok && isfinite(w[e]);
+#pragma unroll
+  for (int e = 1; e < 5; ++e) mx = fmax(mx, fabs(w[e]));
+  if (!ok || mx <= 1e-300) return fmin(fmax(co.taylor_d, lo), hi);
+  if (hi <= lo) return lo;
+  return argmin_quartic(w, lo, hi);
+}
+
+__device__ inline double alpha_from_gram(const double* G, int J, double s, const AlphaCoef& co,
+                                         double lo, double hi) {
+  return J == 3 ? alpha_from_gram_t<3>(G, s, co, lo, hi) : alpha_from_gram_t<5>(G, s, co, lo, hi);
+}
+
+}  // namespace pmx

@@ -21,6 +21,7 @@ struct pmx_context {
   int bf16_cfg;            // bf16 GEMM tile (-1: by shape, 0 128^2, 1 256^2 x 8 waves, 2 x 4)
   int bf16_map;            // bf16 GEMM: 1 deals whole matrices to XCDs, 0 plain order
   int skinny_variant;      // skinny products: 0 In through LDS, 1 In read directly
+  int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -440,6 +441,8 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_BF16_MAP")) c->bf16_map = atoi(e);
   c->skinny_variant = 0;
   if (const char* e = getenv("PMX_SKINNY")) c->skinny_variant = atoi(e);
+  c->small_fused = 1;
+  if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
   *handle = c;
   return PMX_OK;
 }
@@ -663,11 +666,34 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   const int d = o.degree;
   const bool acc = o.accelerate != 0;
 
+  const int stages = (p == 4) ? 2 : 1;
+  if (n <= kSmallMaxN && h->small_fused) {
+    SmallRootParams sp;
+    memset(&sp, 0, sizeof(sp));
+    sp.a = A;
+    sp.lda = lda;
+    sp.a_stride = sa;
+    sp.x = X;
+    sp.ldx = ldx;
+    sp.x_stride = sx;
+    sp.aux = XA;
+    sp.ldaux = ldaux;
+    sp.aux_stride = saux;
+    sp.n = n;
+    sp.stages = stages;
+    sp.expo_x = -1.0 / p;
+    sp.expo_aux = 1.0 / p;
+    sp.c0 = (float)taylor(0);
+    sp.c1 = (float)taylor(1);
+    sp.cfg = cfg;
+    sp.coef = coef;
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_small_root(sp, batch, q.s); }));
+    return PMX_OK;
+  }
   PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
-  const int stages = (p == 4) ? 2 : 1;
   for (int stage = 0; stage < stages; ++stage) {
     StageInitParams ip;
     ip.a = A;
@@ -817,6 +843,25 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const bool acc = o.accelerate != 0;
   const int64_t bs = Lw.buf_stride;
 
+  if (!bf && rows <= kSmallMaxN && h->small_fused) {
+    SmallPolarParams sp;
+    memset(&sp, 0, sizeof(sp));
+    sp.g = (const float*)G;
+    sp.ldg = ldg;
+    sp.g_stride = sg;
+    sp.u = (float*)U;
+    sp.ldu = ldu;
+    sp.u_stride = su;
+    sp.rows = rows;
+    sp.cols = cols;
+    sp.transpose = tr ? 1 : 0;
+    sp.c0 = (float)taylor(0);
+    sp.c1 = (float)taylor(1);
+    sp.cfg = cfg;
+    sp.coef = coef;
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_small_polar(sp, batch, q.s); }));
+    return PMX_OK;
+  }
   PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(G, bf, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, q.s);

@@ -138,6 +138,38 @@ struct PolarFinishParams {
   Ctrl* ctrl;
 };
 
+// Fused small-matrix calls: one workgroup per matrix runs the whole iteration
+// with every matrix in LDS (order n <= kSmallMaxN; polar rows, cols <= it).
+constexpr int kSmallMaxN = 64;
+
+struct SmallRootParams {
+  const float* a;
+  int64_t lda, a_stride;
+  float* x;
+  int64_t ldx, x_stride;
+  float* aux;  // may be null
+  int64_t ldaux, aux_stride;
+  int n, stages;
+  double expo_x, expo_aux;  // X = c^expo_x Z, X_aux = c^expo_aux Y
+  float c0, c1;             // Taylor coefficients c_0, c_1
+  IterCfg cfg;
+  AlphaCoef coef;
+};
+
+struct SmallPolarParams {
+  const float* g;
+  int64_t ldg, g_stride;
+  float* u;
+  int64_t ldu, u_stride;
+  int rows, cols, transpose;  // the iterate is rows x cols (G^T when transpose)
+  float c0, c1;
+  IterCfg cfg;
+  AlphaCoef coef;
+};
+
+hipError_t launch_small_root(const SmallRootParams& p, int batch, hipStream_t s);
+hipError_t launch_small_polar(const SmallPolarParams& p, int batch, hipStream_t s);
+
 hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStream_t s);
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,

@@ -69,7 +69,7 @@ def _run_root(env, A, p, **kw):
     return X.cpu().numpy(), XA.cpu().numpy(), pmx.parse_info(info)
 
 
-@pytest.mark.parametrize("n", [17, 64, 200, 517, 600])
+@pytest.mark.parametrize("n", [17, 64, 65, 200, 517, 600])
 @pytest.mark.parametrize("p", [2, 4])
 def test_inv_root_matches_closed_form(env, n, p):
     _, pmx, _ = env
@@ -136,7 +136,27 @@ def test_inv_root_batched(env):
     assert len(set(int(i) for i in inf["iters"][:, 0])) > 1
 
 
-@pytest.mark.parametrize("m,n", [(64, 32), (33, 70), (150, 150), (300, 17)])
+def test_small_fused_batched(env):
+    # orders up to 64 run as one fused launch per call (one workgroup per
+    # matrix): a batch of mixed conditioning, ragged order 40, both roots
+    torch, pmx, dev = env
+    _say("small fused batch")
+    As = np.stack([W.spd_logu(40, 900 + b, 10.0 ** -(b % 4 + 1), 1.0)[0] for b in range(6)])
+    for p in (2, 4):
+        X, XA, info = pmx.inv_root(torch.from_numpy(As).to(dev), p)
+        torch.cuda.synchronize()
+        inf = pmx.parse_info(info)
+        Xn, XAn = X.cpu().numpy(), XA.cpu().numpy()
+        for b in range(6):
+            ref, ref_aux = cf.inv_root(As[b], p)
+            assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+            assert cf.rel_fro(Xn[b], ref) < 1e-4
+            assert cf.rel_fro(XAn[b], ref_aux) < 1e-4
+            assert int(inf[b]["stages"]) == (2 if p == 4 else 1)
+        assert len(set(int(i) for i in inf["iters"][:, 0])) > 1
+
+
+@pytest.mark.parametrize("m,n", [(64, 32), (32, 48), (33, 70), (150, 150), (300, 17)])
 def test_polar_fp32(env, m, n):
     torch, pmx, dev = env
     _say("polar", m, n)
