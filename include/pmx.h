@@ -43,7 +43,7 @@ extern "C" {
 
 #define PMX_VERSION_MAJOR 0
 #define PMX_VERSION_MINOR 1
-#define PMX_OPTS_VERSION 1
+#define PMX_OPTS_VERSION 2
 #define PMX_TRACE_LEN 64   /* alpha / residual trace entries kept per stage */
 #define PMX_MAX_SKETCH 16  /* largest supported sketch width p */
 
@@ -82,7 +82,7 @@ typedef enum {
  * Part II).  pmx_matfn_opts_default fills the defaults given per field.
  */
 typedef struct {
-  int32_t struct_version; /* must be PMX_OPTS_VERSION */
+  int32_t struct_version; /* PMX_OPTS_VERSION (2), or 1 for the 40-byte layout */
   int32_t degree;         /* d in {1, 2}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2 */
   int32_t sketch_p;       /* Gaussian sketch width p, 1..PMX_MAX_SKETCH; default 8 */
   int32_t max_iter;       /* updates per stage, 1..1000; default 30 */
@@ -91,6 +91,14 @@ typedef struct {
   float alpha_hi;         /*   d = 1: [1/2, 1], d = 2: [3/8, 1.47]          */
   float tol;              /* stop when ||R_k||_F / sqrt(n) <= tol; default 1e-6 */
   uint64_t seed;          /* key of the Philox4x32-10 sketch stream; default 0 */
+  int32_t fp64_iters;     /* inverse roots: the first fp64_iters updates of each
+                             stage run in fp64 (0..max_iter), the rest in fp32;
+                             for ill-conditioned inputs (kappa near 1e6) whose
+                             fp32 result misses 1e-4.  Ignored by the polar
+                             factor.  Default 0.  Added in struct_version 2: a
+                             version-1 struct (without it and `reserved`) is
+                             still accepted and means 0. */
+  int32_t reserved;       /* must be 0 */
 } pmx_matfn_opts;
 
 /*

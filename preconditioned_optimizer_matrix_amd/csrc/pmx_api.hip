@@ -3,6 +3,7 @@
 // in full on the caller's stream; iteration kernels skip themselves on the
 // device once their matrix has finished, so no call waits for the GPU.
 #include <math.h>
+#include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -177,9 +178,17 @@ bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out) {
   pmx_matfn_opts o;
   pmx_matfn_opts_default(&o);
   if (in) {
-    if (in->struct_version != PMX_OPTS_VERSION) return false;
-    o = *in;
+    if (in->struct_version == 1) {
+      // the 40-byte layout without fp64_iters / reserved
+      memcpy(&o, in, offsetof(pmx_matfn_opts, fp64_iters));
+      o.struct_version = PMX_OPTS_VERSION;
+    } else if (in->struct_version == PMX_OPTS_VERSION) {
+      o = *in;
+    } else {
+      return false;
+    }
   }
+  if (o.fp64_iters < 0 || o.fp64_iters > o.max_iter || o.reserved != 0) return false;
   if (o.degree != 1 && o.degree != 2) return false;
   if (o.sketch_p < 1 || o.sketch_p > PMX_MAX_SKETCH) return false;
   if (o.max_iter < 1 || o.max_iter > kMaxIter) return false;
@@ -214,14 +223,14 @@ IterCfg make_cfg(const pmx_matfn_opts& o, int n, pmx_matfn_info* info) {
 
 // ------------------------------------------------------------------ workspace
 struct IterLayout {
-  size_t ctrl, partials, gram, bufs[10], kbuf, total;
+  size_t ctrl, partials, gram, bufs[10], b64[6], kbuf, total;
   int64_t buf_stride, kstride, kld, pstride, gstride;
 };
 
 // Work buffers of the iterative functions: `nbig` matrices of rows x cols
 // (the iterates) and `nsmall` of cols x cols (R, R^2/g), per batch matrix.
 IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, int nbig,
-                       int nsmall, size_t big_elem) {
+                       int nsmall, size_t big_elem, int nf64 = 0) {
   IterLayout L;
   size_t off = 0;
   L.ctrl = off;
@@ -240,6 +249,13 @@ IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, i
     if (i < nbig + nsmall) {
       L.bufs[i] = off;
       off = align_up(off + sizeof(float) * (size_t)L.buf_stride * batch);
+    }
+  }
+  for (int i = 0; i < 6; ++i) {
+    L.b64[i] = 0;
+    if (i < nf64) {
+      L.b64[i] = off;
+      off = align_up(off + sizeof(double) * (size_t)L.buf_stride * batch);
     }
   }
   L.kld = (int64_t)(2 * o.degree + 2) * o.sketch_p;
@@ -412,6 +428,8 @@ pmx_status pmx_matfn_opts_default(pmx_matfn_opts* o) {
   o->alpha_hi = NAN;
   o->tol = 1e-6f;
   o->seed = 0;
+  o->fp64_iters = 0;
+  o->reserved = 0;
   return PMX_OK;
 }
 
@@ -487,8 +505,11 @@ pmx_status pmx_trace_collect(pmx_handle h, double* ms, int64_t* launches) {
   return st;
 }
 
+// fp32: Y and Z ping-pong, R, R^2; with fp64 leading updates also their fp64
+// counterparts (Y, Z ping-pong, R, R^2).
+static int inv_root_f64_bufs(const pmx_matfn_opts& o) { return o.fp64_iters > 0 ? 6 : 0; }
 static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
-  return iter_layout(n, n, batch, o, 4, 2, sizeof(float)).total;
+  return iter_layout(n, n, batch, o, 4, 2, sizeof(float), inv_root_f64_bufs(o)).total;
 }
 // fp32: X ping-pong, R, R^2.  bf16: X and X^T ping-pong, R, R^2 (fp32), and
 // the bf16 operands R and g.
@@ -636,7 +657,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
     return PMX_ERR_INVALID_VALUE;
   if (!batch_layout_ok(n, n, ldx, sx, batch)) return PMX_ERR_INVALID_VALUE;
   if (XA && !batch_layout_ok(n, n, ldaux, saux, batch)) return PMX_ERR_INVALID_VALUE;
-  const IterLayout Lw = iter_layout(n, n, batch, o, 4, 2, sizeof(float));
+  const IterLayout Lw = iter_layout(n, n, batch, o, 4, 2, sizeof(float), inv_root_f64_bufs(o));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
   const Extent ea = extent_of(A, n, n, lda, sa, batch, 4);
@@ -667,7 +688,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   const bool acc = o.accelerate != 0;
 
   const int stages = (p == 4) ? 2 : 1;
-  if (n <= kSmallMaxN && h->small_fused) {
+  if (n <= kSmallMaxN && h->small_fused && o.fp64_iters == 0) {
     SmallRootParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.a = A;
@@ -694,24 +715,135 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
+  const int k64 = std::min(o.fp64_iters, o.max_iter);
+  double* Y64[2] = {at<double>(ws, Lw.b64[0]), at<double>(ws, Lw.b64[1])};
+  double* Z64[2] = {at<double>(ws, Lw.b64[2]), at<double>(ws, Lw.b64[3])};
+  double* R64 = at<double>(ws, Lw.b64[4]);
+  double* R264 = at<double>(ws, Lw.b64[5]);
+  auto gemm64 = [&](int nprob) {
+    Gemm64Params g;
+    memset(&g, 0, sizeof(g));
+    g.nprob = nprob;
+    g.n = n;
+    g.batch = batch;
+    g.stride = Lw.buf_stride;
+    g.stride32 = Lw.buf_stride;
+    g.ctrl = ctrl;
+    g.degree = d;
+    g.c0 = taylor(0);
+    g.c1 = taylor(1);
+    return g;
+  };
+  auto plain64 = [](const double* m) { return Gemm64Operand{m, nullptr, 0}; };
   for (int stage = 0; stage < stages; ++stage) {
-    StageInitParams ip;
-    ip.a = A;
-    ip.lda = lda;
-    ip.a_stride = sa;
-    ip.ybuf[0] = Yb[0];
-    ip.ybuf[1] = Yb[1];
-    ip.r = Rb;
-    ip.buf_stride = Lw.buf_stride;
-    ip.n = n;
-    ip.stage = stage;
-    ip.ctrl = ctrl;
-    ip.partials = partials;
-    ip.partial_stride = Lw.pstride;
-    ip.cfg = cfg;
-    ip.sketch = make_sketch(Lw, ws, cfg, n, 0, stage, acc);
-    PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_sqrt_stage_init(ip, batch, q.s); }));
-    for (int k = 0; k < o.max_iter; ++k) {
+    if (k64 > 0) {
+      // leading updates in fp64 (same sequence as the fp32 loop below)
+      StageInit64Params ip;
+      memset(&ip, 0, sizeof(ip));
+      ip.a = A;
+      ip.lda = lda;
+      ip.a_stride = sa;
+      ip.ybuf32[0] = Yb[0];
+      ip.ybuf32[1] = Yb[1];
+      ip.stride32 = Lw.buf_stride;
+      ip.y64 = Y64[0];
+      ip.r64 = R64;
+      ip.r32 = Rb;
+      ip.stride = Lw.buf_stride;
+      ip.n = n;
+      ip.stage = stage;
+      ip.ctrl = ctrl;
+      ip.partials = partials;
+      ip.partial_stride = Lw.pstride;
+      ip.cfg = cfg;
+      ip.sketch = make_sketch(Lw, ws, cfg, n, 0, stage, acc);
+      PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_stage_init_f64(ip, batch, q.s); }));
+      const Gemm64Operand g64 = {R64, d == 2 ? R264 : nullptr, 1};
+      for (int k = 0; k < k64; ++k) {
+        if (d == 2) {
+          Gemm64Params g = gemm64(1);
+          g.prob[0].a = plain64(R64);
+          g.prob[0].b = plain64(R64);
+          g.prob[0].c = R264;
+          g.prob[0].c32 = R2b;
+          PMX_TRY(q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f64(g, ROLE_POWER, q.s); }));
+        }
+        PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b, false));
+        const int cur = k & 1, nxt = cur ^ 1;
+        Gemm64Params u = gemm64(k == 0 ? 1 : 2);
+        if (k == 0) {
+          FormG64Params fp;
+          memset(&fp, 0, sizeof(fp));
+          fp.r = R64;
+          fp.r2 = (d == 2) ? R264 : nullptr;
+          fp.dst = Z64[1];
+          fp.stride = Lw.buf_stride;
+          fp.n = n;
+          fp.degree = d;
+          fp.c0 = taylor(0);
+          fp.c1 = taylor(1);
+          fp.ctrl = ctrl;
+          PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g_f64(fp, batch, q.s); }));
+          u.prob[0].a = plain64(Y64[0]);
+          u.prob[0].b = plain64(Z64[1]);
+          u.prob[0].c = Y64[1];
+        } else {
+          u.prob[0].a = plain64(Y64[cur]);
+          u.prob[0].b = g64;
+          u.prob[0].c = Y64[nxt];
+          u.prob[1].a = g64;
+          u.prob[1].b = plain64(Z64[cur]);
+          u.prob[1].c = Z64[nxt];
+        }
+        PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f64(u, ROLE_UPDATE, q.s); }));
+        Gemm64Params r = gemm64(1);
+        r.prob[0].a = plain64(Z64[nxt]);
+        r.prob[0].b = plain64(Y64[nxt]);
+        r.prob[0].c = R64;
+        r.prob[0].c32 = Rb;
+        r.partials = partials;
+        r.partial_stride = Lw.pstride;
+        r.products = (d - 1) + 1 + (k > 0 ? 1 : 0) + 1;
+        r.count_update = 1;
+        r.cfg = cfg;
+        r.sketch = make_sketch(Lw, ws, cfg, n, k + 1, stage, acc && k + 1 < o.max_iter);
+        PMX_TRY(q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f64(r, ROLE_RESID, q.s); }));
+      }
+      Handover64Params hp;
+      memset(&hp, 0, sizeof(hp));
+      hp.y64[0] = Y64[0];
+      hp.y64[1] = Y64[1];
+      hp.z64[0] = Z64[0];
+      hp.z64[1] = Z64[1];
+      hp.y32[0] = Yb[0];
+      hp.y32[1] = Yb[1];
+      hp.z32[0] = Zb[0];
+      hp.z32[1] = Zb[1];
+      hp.stride = Lw.buf_stride;
+      hp.stride32 = Lw.buf_stride;
+      hp.n = n;
+      hp.stage = stage;
+      hp.ctrl = ctrl;
+      PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_handover_f64(hp, batch, q.s); }));
+    } else {
+      StageInitParams ip;
+      ip.a = A;
+      ip.lda = lda;
+      ip.a_stride = sa;
+      ip.ybuf[0] = Yb[0];
+      ip.ybuf[1] = Yb[1];
+      ip.r = Rb;
+      ip.buf_stride = Lw.buf_stride;
+      ip.n = n;
+      ip.stage = stage;
+      ip.ctrl = ctrl;
+      ip.partials = partials;
+      ip.partial_stride = Lw.pstride;
+      ip.cfg = cfg;
+      ip.sketch = make_sketch(Lw, ws, cfg, n, 0, stage, acc);
+      PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_sqrt_stage_init(ip, batch, q.s); }));
+    }
+    for (int k = k64; k < o.max_iter; ++k) {
       PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b));
       const int cur = k & 1, nxt = cur ^ 1;
       GemmParams u = gemm_base(q.h, n, n, n, batch);

@@ -170,6 +170,76 @@ struct SmallPolarParams {
 hipError_t launch_small_root(const SmallRootParams& p, int batch, hipStream_t s);
 hipError_t launch_small_polar(const SmallPolarParams& p, int batch, hipStream_t s);
 
+// fp64 leading updates of an inverse root (square n x n buffers, ld n).
+struct Gemm64Operand {
+  const double* p;
+  const double* p2;  // R^2 of a polynomial operand (d = 2)
+  int poly;          // 1: g = c0 I + c1 R + alpha R2 (d = 2) / c0 I + alpha R
+};
+
+struct Gemm64Problem {
+  Gemm64Operand a, b;
+  double* c;
+  float* c32;  // optional fp32 copy of C (stride32)
+};
+
+struct Gemm64Params {
+  Gemm64Problem prob[2];
+  int nprob, n, batch;
+  int64_t stride;    // doubles between the matrices of a batch
+  int64_t stride32;  // floats between the fp32 copies
+  Ctrl* ctrl;
+  int degree;
+  double c0, c1;
+  double* partials;  // ROLE_RESID: Frobenius partials, one per tile
+  int64_t partial_stride;
+  int products, count_update;
+  IterCfg cfg;
+  SketchJob sketch;
+};
+
+struct StageInit64Params {
+  const float* a;
+  int64_t lda, a_stride;
+  float* ybuf32[2];  // the previous stage's Y (stage 1)
+  int64_t stride32;
+  double* y64;
+  double* r64;
+  float* r32;
+  int64_t stride;
+  int n, stage;
+  Ctrl* ctrl;
+  double* partials;
+  int64_t partial_stride;
+  IterCfg cfg;
+  SketchJob sketch;
+};
+
+struct FormG64Params {
+  const double* r;
+  const double* r2;
+  double* dst;
+  int64_t stride;
+  int n, degree;
+  double c0, c1;
+  Ctrl* ctrl;
+};
+
+struct Handover64Params {
+  double* y64[2];
+  double* z64[2];
+  float* y32[2];
+  float* z32[2];
+  int64_t stride, stride32;
+  int n, stage;
+  Ctrl* ctrl;
+};
+
+hipError_t launch_gemm_f64(const Gemm64Params& p, int role, hipStream_t s);
+hipError_t launch_stage_init_f64(const StageInit64Params& p, int batch, hipStream_t s);
+hipError_t launch_form_g_f64(const FormG64Params& p, int batch, hipStream_t s);
+hipError_t launch_handover_f64(const Handover64Params& p, int batch, hipStream_t s);
+
 hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStream_t s);
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,

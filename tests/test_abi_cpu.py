@@ -29,8 +29,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     from preconditioned_optimizer_matrix_amd import pmx
-    # pmx_matfn_opts: 5 int32 + 3 float + uint64 (8-aligned) = 40 bytes
-    assert ctypes.sizeof(pmx.Opts) == 40
+    # pmx_matfn_opts: 5 int32 + 3 float + uint64 (8-aligned) + 2 int32 = 48 bytes
+    assert ctypes.sizeof(pmx.Opts) == 48
+    assert pmx.Opts.fp64_iters.offset == 40
     # pmx_matfn_info: 6 int32 + 3 float + 4 * 64 float
     assert ctypes.sizeof(pmx.Info) == 4 * (6 + 3 + 4 * pmx.TRACE_LEN)
     src = open(HEADER).read()
@@ -47,6 +48,7 @@ def test_host_only_calls():
     assert (o.degree, o.sketch_p, o.max_iter, o.accelerate) == (2, 8, 30, 1)
     assert math.isnan(o.alpha_lo) and math.isnan(o.alpha_hi)
     assert o.tol == pytest.approx(1e-6)
+    assert (o.fp64_iters, o.reserved, o.struct_version) == (0, 0, pmx.OPTS_VERSION)
     assert pmx.lib.pmx_matfn_opts_default(None) == pmx.ERR_INVALID_VALUE
 
 
@@ -80,6 +82,16 @@ def test_workspace_sizes_and_option_validation():
     assert ws(alpha_lo=0.4, alpha_hi=float("nan")) == pmx.ERR_INVALID_VALUE
     assert ws(struct_version=99) == pmx.ERR_INVALID_VALUE
     assert ws(alpha_lo=0.5, alpha_hi=0.5) == pmx.OK
+    assert ws(fp64_iters=-1) == pmx.ERR_INVALID_VALUE
+    assert ws(fp64_iters=31) == pmx.ERR_INVALID_VALUE  # more than max_iter
+    assert ws(reserved=1) == pmx.ERR_INVALID_VALUE
+    assert ws(fp64_iters=4) == pmx.OK
+    # the 40-byte version-1 layout is still accepted (fp64_iters = 0)
+    assert ws(struct_version=1, fp64_iters=7, reserved=5) == pmx.OK
+    # fp64 leading updates add six n x n fp64 buffers
+    o4 = pmx.default_opts(fp64_iters=4)
+    b4 = pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, o4)
+    assert b4 - b >= 6 * 8 * n * n
     sz = ctypes.c_size_t()
     assert pmx.lib.pmx_workspace_size(None, pmx.OP_INV_ROOT, 0, 0, 1, pmx.F32, None,
                                       ctypes.byref(sz)) == pmx.ERR_INVALID_VALUE

@@ -136,6 +136,40 @@ def test_inv_root_batched(env):
     assert len(set(int(i) for i in inf["iters"][:, 0])) > 1
 
 
+@pytest.mark.parametrize("p", [2, 4])
+def test_fp64_leading_updates(env, p):
+    # kappa = 1e6 power-law blocks (ragged n = 100 and n = 256): fp32 alone
+    # floors near 2e-4; with the first four updates of each stage in fp64 the
+    # result is within 1e-4 of the oracle
+    torch, pmx, dev = env
+    _say("fp64 leading updates", p)
+    for n, k64 in ((100, 4), (256, 4)):
+        As, _, _ = W.spd_power_batch(3, n, 1100 + n)
+        opts = pmx.default_opts(fp64_iters=k64)
+        X, XA, info = pmx.inv_root(torch.from_numpy(As).to(dev), p, opts=opts)
+        torch.cuda.synchronize()
+        inf = pmx.parse_info(info)
+        Xn, XAn = X.cpu().numpy(), XA.cpu().numpy()
+        for b in range(3):
+            ref, ref_aux = cf.inv_root(As[b], p)
+            assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), (n, b)
+            assert cf.rel_fro(Xn[b], ref) < 1e-4, (n, b, cf.rel_fro(Xn[b], ref))
+            assert cf.rel_fro(XAn[b], ref_aux) < 1e-4
+            assert int(inf[b]["iters"][0]) > k64  # the fp32 updates continued the stage
+    # a NaN input through the fp64 path
+    A = np.eye(80, dtype=np.float32)
+    A[3, 5] = np.nan
+    X, _, info = _run_root(env, A, 4, fp64_iters=2)
+    assert int(info[0]["status"]) == pmx.NONFINITE
+    assert np.all(np.isnan(X))
+    # a stage that converges inside the fp64 updates (well conditioned input)
+    A, _, _ = W.spd_logu(90, 4242, 0.5, 1.0)
+    X, XA, info = _run_root(env, A, p, fp64_iters=12)
+    ref, ref_aux = cf.inv_root(A, p)
+    assert int(info[0]["iters"][0]) < 12
+    assert cf.rel_fro(X, ref) < 1e-6 and cf.rel_fro(XA, ref_aux) < 1e-6
+
+
 def test_small_fused_batched(env):
     # orders up to 64 run as one fused launch per call (one workgroup per
     # matrix): a batch of mixed conditioning, ragged order 40, both roots

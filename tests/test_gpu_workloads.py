@@ -96,21 +96,29 @@ def test_shampoo_1024x4096(env):
 
 
 def test_blocks_64x512(env):
+    # kappa = 1e6: pure fp32 floors near 2e-4 against the oracle; with the
+    # first four updates of each stage in fp64 every block is within 1e-4
     torch, pmx, dev = env
     c = W.blocks_64x512()
     _say("blocks_64x512")
-    X, _, info = pmx.inv_root(torch.from_numpy(c["A"]).to(dev), 4, aux=False)
+    A = torch.from_numpy(c["A"]).to(dev)
+    X32, _, info32 = pmx.inv_root(A, 4, aux=False)
+    X64, _, info64 = pmx.inv_root(A, 4, aux=False, opts=pmx.default_opts(fp64_iters=4))
     torch.cuda.synchronize()
-    Xn = X.cpu().numpy()
-    inf = pmx.parse_info(info)
-    errs = []
+    X32n, X64n = X32.cpu().numpy(), X64.cpu().numpy()
+    i32, i64 = pmx.parse_info(info32), pmx.parse_info(info64)
+    e32, e64 = [], []
     for b in range(64):
         ref, _ = cf.inv_root(c["A"][b], 4)
-        errs.append(cf.rel_fro(Xn[b], ref))
-        assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
-    _say("blocks_64x512 rel err max %.2e median %.2e, iters %s" % (
-        max(errs), float(np.median(errs)), sorted(set(tuple(int(x) for x in i) for i in inf["iters"]))))
-    assert max(errs) < 5e-4
+        e32.append(cf.rel_fro(X32n[b], ref))
+        e64.append(cf.rel_fro(X64n[b], ref))
+        assert int(i32[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+        assert int(i64[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+    _say("blocks_64x512 rel err fp32 max %.2e, fp64 leading max %.2e median %.2e, iters %s" % (
+        max(e32), max(e64), float(np.median(e64)),
+        sorted(set(tuple(int(x) for x in i) for i in i64["iters"]))))
+    assert max(e64) < 1e-4
+    assert max(e32) < 5e-4
 
 
 def test_muon_32x4096x1024(env):
