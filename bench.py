@@ -207,19 +207,28 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_per_launch": a.numel() * 4, "launches": 4}), flush=True)
 
 
+def source_digest():
+    """SHA-256 over the sources that decide what the update GEMM launches read
+    and write: the GEMM kernel and the launch sequence."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("pmx_gemm_f32.hip", "pmx_api.hip"):
+        h.update(open(os.path.join(ROOT, "preconditioned_optimizer_matrix_amd", "csrc", f),
+                      "rb").read())
+    return h.hexdigest()
+
+
 def update_traffic(n_launch):
     """HBM bytes per update-GEMM launch measured with rocprofv3 counters
-    (profiles/update_gemm_traffic.json), or None when the GEMM source has
-    changed since the counters were taken."""
-    import hashlib
+    (profiles/update_gemm_traffic.json), or None when the GEMM kernel or its
+    launch sequence has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "update_gemm_traffic.json")
-    src = os.path.join(ROOT, "preconditioned_optimizer_matrix_amd", "csrc", "pmx_gemm_f32.hip")
     try:
         rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = source_digest()
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_source_sha256") != digest or rec.get("launches_per_step") != n_launch:
+    if rec.get("source_sha256") != digest or rec.get("launches_per_step") != n_launch:
         return None
     return rec.get("hbm_bytes_per_launch")
 

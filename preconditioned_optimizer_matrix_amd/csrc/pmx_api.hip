@@ -22,7 +22,9 @@ struct pmx_context {
   int bf16_cfg;            // bf16 GEMM tile (-1: by shape, 0 128^2, 1 256^2 x 8 waves, 2 x 4)
   int bf16_map;            // bf16 GEMM: 1 deals whole matrices to XCDs, 0 plain order
   int skinny_variant;      // skinny products: 0 In through LDS, 1 In read directly
+  int bf16_dma;            // bf16 GEMM: 1 uses direct global-to-LDS loads for whole tiles (measured slower; off)
   int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
+  int explicit_g;          // fp32 updates: 1 writes g once, 0 forms it in the operand loads
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -292,6 +294,7 @@ GemmParams bf16_base(const pmx_context* h, int M, int N, int K, int batch) {
   GemmParams g = gemm_base(h, M, N, K, batch);
   g.cfg_id = h->bf16_cfg;
   g.map_mode = h->bf16_map;
+  g.dma = h->bf16_dma;
   return g;
 }
 
@@ -459,6 +462,10 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_BF16_MAP")) c->bf16_map = atoi(e);
   c->skinny_variant = 0;
   if (const char* e = getenv("PMX_SKINNY")) c->skinny_variant = atoi(e);
+  c->bf16_dma = 0;
+  if (const char* e = getenv("PMX_BF16_DMA")) c->bf16_dma = atoi(e);
+  c->explicit_g = 1;
+  if (const char* e = getenv("PMX_EXPLICIT_G")) c->explicit_g = atoi(e);
   c->small_fused = 1;
   if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
   *handle = c;
@@ -870,6 +877,32 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         u.prob[0].c = Yb[1];
         u.prob[0].ldc = n;
         u.prob[0].stride_c = Lw.buf_stride;
+      } else if (h->explicit_g) {
+        // g written once (in place of R^2, which the Krylov passes have read),
+        // then Y_{k+1} = Y_k g and Z_{k+1} = g Z_k with plain operands
+        FormGParams fp;
+        memset(&fp, 0, sizeof(fp));
+        fp.r = Rb;
+        fp.r2 = (d == 2) ? R2b : nullptr;
+        fp.dst = R2b;
+        fp.stride = Lw.buf_stride;
+        fp.n = n;
+        fp.degree = d;
+        fp.c0 = (float)taylor(0);
+        fp.c1 = (float)taylor(1);
+        fp.ctrl = ctrl;
+        PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
+        u.nprob = 2;
+        u.prob[0].a = {Yb[cur], n, Lw.buf_stride, nullptr, 0};
+        u.prob[0].b = {R2b, n, Lw.buf_stride, nullptr, 0};
+        u.prob[0].c = Yb[nxt];
+        u.prob[0].ldc = n;
+        u.prob[0].stride_c = Lw.buf_stride;
+        u.prob[1].a = {R2b, n, Lw.buf_stride, nullptr, 0};
+        u.prob[1].b = {Zb[cur], n, Lw.buf_stride, nullptr, 0};
+        u.prob[1].c = Zb[nxt];
+        u.prob[1].ldc = n;
+        u.prob[1].stride_c = Lw.buf_stride;
       } else {
         // Y_{k+1} = Y_k g and Z_{k+1} = g Z_k, g = f_{d-1}(R) + alpha R^d formed on load
         u.nprob = 2;
@@ -1038,6 +1071,22 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       u.c1 = (float)taylor(1);
       u.prob[0].a = {Xb[cur], cols, bs, nullptr, 0};
       u.prob[0].b = {Rb, cols, bs, R2b, 1};
+      if (h->explicit_g) {
+        // g written once in place of R^2 (read by the Krylov passes already)
+        FormGParams fp;
+        memset(&fp, 0, sizeof(fp));
+        fp.r = Rb;
+        fp.r2 = (d == 2) ? R2b : nullptr;
+        fp.dst = R2b;
+        fp.stride = bs;
+        fp.n = cols;
+        fp.degree = d;
+        fp.c0 = (float)taylor(0);
+        fp.c1 = (float)taylor(1);
+        fp.ctrl = ctrl;
+        PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
+        u.prob[0].b = {R2b, cols, bs, nullptr, 0};
+      }
       u.prob[0].c = Xb[nxt];
       u.prob[0].ldc = cols;
       u.prob[0].stride_c = bs;

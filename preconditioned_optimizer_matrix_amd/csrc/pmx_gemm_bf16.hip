@@ -207,13 +207,82 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[C::FM][C::FN],
   }
 }
 
+// Epilogue of one tile by role (same accumulator layout as the 32x32 fp32
+// MFMA: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + (v % 4)).
+template <class C, int ROLE, int FM, int FN>
+__device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmParams& p,
+                                              const GemmProblem& pr, int b, int m0, int n0,
+                                              int tile, int tiles, int lane, int wm, int wn,
+                                              double* red) {
+  constexpr bool RESID = ROLE == ROLE_RESID;
+  constexpr bool BF16_OUT = ROLE == ROLE_UPDATE;
+  const int hi = lane >> 5, col_in = lane & 31;
+  float fro = 0.f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn + 32 * j + col_in;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row_base = m0 + wm + 32 * i + 8 * g + 4 * hi;
+        uint32_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = row_base + r;
+          float x = acc[i][j][4 * g + r];
+          if (RESID) {
+            x = (row == col ? 1.f : 0.f) - x;
+            if (row < p.M && col < p.N) fro += x * x;
+          }
+          h[r] = bf16_rne(x);
+          if (row < p.M && col < p.N) {
+            const int64_t o = (int64_t)b * pr.stride_c + (int64_t)row * pr.ldc + col;
+            if (BF16_OUT) reinterpret_cast<uint16_t*>(pr.c)[o] = (uint16_t)h[r];
+            else pr.c[o] = x;
+            if (RESID && p.prob[1].c) {
+              const GemmProblem& hp = p.prob[1];
+              reinterpret_cast<uint16_t*>(hp.c)[(int64_t)b * hp.stride_c +
+                                                (int64_t)row * hp.ldc + col] = (uint16_t)h[r];
+            }
+          }
+        }
+        if (BF16_OUT && col < p.N) {
+          // transposed copy: X'^T[col][row_base .. row_base + 3]
+          const GemmProblem& tp = p.prob[1];
+          uint16_t* T = reinterpret_cast<uint16_t*>(tp.c) + (int64_t)b * tp.stride_c +
+                        (int64_t)col * tp.ldc + row_base;
+          if (p.vec && row_base + 3 < p.M) {
+            *reinterpret_cast<u32x2*>(T) = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (row_base + r < p.M) T[r] = (uint16_t)h[r];
+          }
+        }
+      }
+    }
+  if (RESID) {
+    const double blocksum = block_sum<C::WAVES>((double)fro, red);
+    double tot;
+    if (last_block_sum<C::WAVES>(blocksum, p.partials + (int64_t)b * p.partial_stride,
+                                 &p.ctrl[b].counter, tiles, tile, red, &tot)) {
+      if (threadIdx.x == 0) {
+        Ctrl& c = p.ctrl[b];
+        if (p.count_update) c.iter += 1;
+        c.gemms += p.products;
+        decide(c, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
+      }
+    }
+  }
+}
+
 // ROLE_RESID: C fp32 = I - acc with the Frobenius reduction and decision, and
 // a bf16 copy at prob[1].c when set; ROLE_POWER: C fp32 = acc; ROLE_UPDATE:
 // C bf16 = acc and its transpose at prob[1].c.
 template <class C, int ROLE>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p) {
   constexpr bool RESID = ROLE == ROLE_RESID;
-  constexpr bool BF16_OUT = ROLE == ROLE_UPDATE;
   constexpr int NT = C::NT, FM = C::FM, FN = C::FN;
   constexpr int WGN = C::BN / C::WN;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][C::LDS];
@@ -302,68 +371,168 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
     }
     }
 
-    // Epilogue (same accumulator layout as the 32x32 fp32 MFMA: lane l holds
-    // column l % 32 and rows 8 (v / 4) + 4 (l / 32) + (v % 4)).
-    const int hi = lane >> 5, col_in = lane & 31;
-    float fro = 0.f;
+    bf16_epilogue<C, ROLE>(acc, p, pr, b, m0, n0, tile, tiles, lane, wm, wn, red);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole-tile variant with direct global-to-LDS loads (global_load_lds_dwordx4:
+// lane l of a wave writes its 16 bytes at the instruction's LDS base + 16 l).
+// 256 x 256 tiles, 8 waves of 128 x 64, k tiles of 32 in a ring of 4 LDS
+// stages (32 KB each), so three k tiles are in flight while one is
+// multiplied.  No padding is possible inside a wave's contiguous 1 KB, so
+// rows are XOR-swizzled instead: the 16-byte chunk kc of row R sits in slot
+// 4 R + (kc ^ f(R)), f(R) = ((R >> 1) ^ (R >> 3)) & 3, which keeps the
+// fragment reads of 16 consecutive rows on distinct banks.  Waits are
+// explicit (vmcnt plus a bare s_barrier, no memory fence): before the
+// barrier that starts k tile t + 1 a wave waits for its own loads of that
+// tile; after it, the stage of tile t is refilled with tile t + 4 and the
+// first fragments of tile t + 1 are read while the last MFMAs of tile t still
+// run.  Used when M and N are multiples of 256, K of 32 and rows are
+// 16-byte aligned.
+constexpr int DBK = 32, DNS = 4;
+constexpr int DOPB = 256 * DBK * 2;  // bytes per operand and stage
+constexpr int DSTB = 2 * DOPB;       // bytes per stage
+using BDma = BCfg<256, 256, 128, 64, 32, 1>;
+
+__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int ROLE>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmParams p) {
+  using C = BDma;
+  constexpr bool RESID = ROLE == ROLE_RESID;
+  constexpr int FM = C::FM, FN = C::FN;  // 4 x 2 accumulators per wave
+  __shared__ __attribute__((aligned(16))) unsigned char lds[DNS * DSTB];
+  __shared__ double red[C::WAVES];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = (wid >> 2) * 128, wn = (wid & 3) * 64;
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int total = tiles * p.batch;
+  const GemmProblem& pr = p.prob[0];
+  const int nk = p.K / DBK;
+  const int sw = dma_swz(lane & 31);
+  // this lane's DMA slots: instruction j covers slots (2 wid + j) 64 + lane
+  int rowj[2], kcj[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int slot = (2 * wid + j) * 64 + lane;
+    rowj[j] = slot >> 2;
+    kcj[j] = (slot & 3) ^ dma_swz(slot >> 2);
+  }
+  const bool xcd = p.map_mode != 0 && (int)gridDim.x == total && (total & 7) == 0;
+  for (int it0 = blockIdx.x; it0 < total; it0 += gridDim.x) {
+    const int it = xcd ? (it0 & 7) * (total >> 3) + (it0 >> 3) : it0;
+    int b, tm, tn, tile;
+    item_tile(it, p.tiles_m, p.tiles_n, &b, &tm, &tn, &tile);
+    if (p.ctrl) {
+      const int st = *(volatile int32_t*)&p.ctrl[b].status;
+      if (st != PMX_RUNNING) continue;
+    }
+    if (RESID) sketch_share(p.sketch, b, tile, tiles);
+    const int m0 = tm * 256, n0 = tn * 256;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(pr.a.ptr) + (int64_t)b * pr.a.stride;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(pr.b.ptr) + (int64_t)b * pr.b.stride;
+    const uint16_t* ga[2];
+    const uint16_t* gb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ga[j] = A + (int64_t)(m0 + rowj[j]) * pr.a.ld + 8 * kcj[j];
+      gb[j] = B + (int64_t)(n0 + rowj[j]) * pr.b.ld + 8 * kcj[j];
+    }
+    auto issue = [&](int t) {
+      const int tc = t < nk ? t : nk - 1;  // past the end: reload the last tile
+      unsigned char* st = lds + (t & (DNS - 1)) * DSTB;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(ga[j] + tc * DBK),
+                                         (lds_ptr_t)(st + (2 * wid + j) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(gb[j] + tc * DBK),
+                                         (lds_ptr_t)(st + DOPB + (2 * wid + j) * 1024), 16, 0, 0);
+    };
+    // fragment i of A / j of B, 16-wide k step s of the k tile in stage st
+    auto frag_a = [&](int st, int i, int s) {
+      const int r = wm + 32 * i + (lane & 31);
+      const int kc = 2 * s + (lane >> 5);
+      return *reinterpret_cast<const bf16x8*>(lds + st * DSTB + (r * 4 + (kc ^ sw)) * 16);
+    };
+    auto frag_b = [&](int st, int j, int s) {
+      const int r = wn + 32 * j + (lane & 31);
+      const int kc = 2 * s + (lane >> 5);
+      return *reinterpret_cast<const bf16x8*>(lds + st * DSTB + DOPB + (r * 4 + (kc ^ sw)) * 16);
+    };
+    f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn + 32 * j + col_in;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row_base = m0 + wm + 32 * i + 8 * g + 4 * hi;
-          uint32_t h[4];
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    // the previous item's LDS reads and this item's sketch stores are done
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    issue(0);
+    issue(1);
+    issue(2);
+    issue(3);
+    __builtin_amdgcn_s_waitcnt(0x3f7c);  // vmcnt(12): tile 0 has landed for this wave
+    __builtin_amdgcn_s_barrier();
+    bf16x8 fa[2][FM], fb[2][FN];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = row_base + r;
-            float x = acc[i][j][4 * g + r];
-            if (RESID) {
-              x = (row == col ? 1.f : 0.f) - x;
-              if (row < p.M && col < p.N) fro += x * x;
-            }
-            h[r] = bf16_rne(x);
-            if (row < p.M && col < p.N) {
-              const int64_t o = (int64_t)b * pr.stride_c + (int64_t)row * pr.ldc + col;
-              if (BF16_OUT) reinterpret_cast<uint16_t*>(pr.c)[o] = (uint16_t)h[r];
-              else pr.c[o] = x;
-              if (RESID && p.prob[1].c) {
-                const GemmProblem& hp = p.prob[1];
-                reinterpret_cast<uint16_t*>(hp.c)[(int64_t)b * hp.stride_c +
-                                                  (int64_t)row * hp.ldc + col] = (uint16_t)h[r];
-              }
-            }
-          }
-          if (BF16_OUT && col < p.N) {
-            // transposed copy: X'^T[col][row_base .. row_base + 3]
-            const GemmProblem& tp = p.prob[1];
-            uint16_t* T = reinterpret_cast<uint16_t*>(tp.c) + (int64_t)b * tp.stride_c +
-                          (int64_t)col * tp.ldc + row_base;
-            if (p.vec && row_base + 3 < p.M) {
-              *reinterpret_cast<u32x2*>(T) = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-            } else {
+    for (int i = 0; i < FM; ++i) fa[0][i] = frag_a(0, i, 0);
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (row_base + r < p.M) T[r] = (uint16_t)h[r];
-            }
-          }
-        }
-      }
-    if (RESID) {
-      const double blocksum = block_sum<C::WAVES>((double)fro, red);
-      double tot;
-      if (last_block_sum<C::WAVES>(blocksum, p.partials + (int64_t)b * p.partial_stride,
-                                   &p.ctrl[b].counter, tiles, tile, red, &tot)) {
-        if (threadIdx.x == 0) {
-          Ctrl& c = p.ctrl[b];
-          if (p.count_update) c.iter += 1;
-          c.gemms += p.products;
-          decide(c, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
-        }
-      }
+    for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(0, j, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & (DNS - 1), nst = (kt + 1) & (DNS - 1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[1][i] = frag_a(st, i, 1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[1][j] = frag_b(st, j, 1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][j], acc[i][j], 0, 0, 0);
+      // step 0: its 8 MFMAs interleaved with the 6 fragment reads of step 1
+      sched_interleave<FM * FN, FM + FN, 0x100, 1>();
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+      // tile kt + 1 landed for this wave, then for every wave; the stage of
+      // tile kt is free again
+      __builtin_amdgcn_s_waitcnt(0x3f78);  // vmcnt(8)
+      __builtin_amdgcn_s_barrier();
+      issue(kt + 4);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[0][i] = frag_a(nst, i, 0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(nst, j, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the trailing reloads are done
+    bf16_epilogue<C, ROLE>(acc, p, pr, b, m0, n0, tile, tiles, lane, wm, wn, red);
   }
+}
+
+hipError_t launch_dma(GemmParams p, int role, hipStream_t s) {
+  p.tiles_m = p.M / 256;
+  p.tiles_n = p.N / 256;
+  const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
+  int64_t g = total;
+  if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
+  const dim3 grid((unsigned)g), block(512);
+  switch (role) {
+    case ROLE_RESID: hipLaunchKernelGGL(gemm_bf16_dma_kernel<ROLE_RESID>, grid, block, 0, s, p); break;
+    case ROLE_POWER: hipLaunchKernelGGL(gemm_bf16_dma_kernel<ROLE_POWER>, grid, block, 0, s, p); break;
+    case ROLE_UPDATE: hipLaunchKernelGGL(gemm_bf16_dma_kernel<ROLE_UPDATE>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <class C>
@@ -396,6 +565,9 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int role, hipStream_t s) {
   if (cfg < 0 || cfg > 3) cfg = (p.M >= 256 && p.N >= 256 && large >= p.num_cu) ? 1 : 0;
   if (cfg == 2) return launch_cfg<BLarge4>(p, role, s);
   if (cfg == 3) return launch_cfg<BMid2>(p, role, s);
+  if (cfg == 1 && p.dma && p.vec && p.M % 256 == 0 && p.N % 256 == 0 && p.K % DBK == 0 &&
+      p.K >= DBK && ((uintptr_t)p.prob[0].a.ptr & 15) == 0 && ((uintptr_t)p.prob[0].b.ptr & 15) == 0)
+    return launch_dma(p, role, s);
   return cfg == 1 ? launch_cfg<BLarge>(p, role, s) : launch_cfg<BSmall>(p, role, s);
 }
 

@@ -249,6 +249,7 @@ struct GemmParams {
   int max_blocks;  // persistent grid cap (0: one block per tile)
   int cfg_id;      // tile configuration (-1: chosen from the shape)
   int map_mode;    // tile order: 0 grouped, 1 grouped + XCD rounds, 2 row-major
+  int dma;         // bf16: whole-tile variant with direct global-to-LDS loads
   int num_cu;
   Ctrl* ctrl;      // per-matrix control blocks; null = unconditional
   // polynomial operands
