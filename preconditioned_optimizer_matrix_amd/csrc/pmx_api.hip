@@ -24,7 +24,6 @@ struct pmx_context {
   int skinny_variant;      // skinny products: 0 In through LDS, 1 In read directly
   int bf16_dma;            // bf16 GEMM: 1 uses direct global-to-LDS loads for whole tiles (measured slower; off)
   int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
-  int explicit_g;          // fp32 updates: 1 writes g once, 0 forms it in the operand loads
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -464,8 +463,6 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_SKINNY")) c->skinny_variant = atoi(e);
   c->bf16_dma = 0;
   if (const char* e = getenv("PMX_BF16_DMA")) c->bf16_dma = atoi(e);
-  c->explicit_g = 1;
-  if (const char* e = getenv("PMX_EXPLICIT_G")) c->explicit_g = atoi(e);
   c->small_fused = 1;
   if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
   *handle = c;
@@ -858,6 +855,9 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       u.degree = d;
       u.c0 = (float)taylor(0);
       u.c1 = (float)taylor(1);
+      // the sketch of update k + 1 is generated with g (after the Krylov
+      // passes of update k have read S_k)
+      const SketchJob next_sketch = make_sketch(Lw, ws, cfg, n, k + 1, stage, acc && k + 1 < o.max_iter);
       if (k == 0) {
         // Z_1 = g Z_0 = g is written explicitly; Y_1 = Y_0 g reads it back.
         FormGParams fp;
@@ -871,15 +871,16 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         fp.c0 = (float)taylor(0);
         fp.c1 = (float)taylor(1);
         fp.ctrl = ctrl;
+        fp.sketch = next_sketch;
         PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
         u.prob[0].a = {Yb[0], n, Lw.buf_stride, nullptr, 0};
         u.prob[0].b = {Zb[1], n, Lw.buf_stride, nullptr, 0};
         u.prob[0].c = Yb[1];
         u.prob[0].ldc = n;
         u.prob[0].stride_c = Lw.buf_stride;
-      } else if (h->explicit_g) {
+      } else {
         // g written once (in place of R^2, which the Krylov passes have read),
-        // then Y_{k+1} = Y_k g and Z_{k+1} = g Z_k with plain operands
+        // then Y_{k+1} = Y_k g and Z_{k+1} = g Z_k
         FormGParams fp;
         memset(&fp, 0, sizeof(fp));
         fp.r = Rb;
@@ -891,6 +892,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         fp.c0 = (float)taylor(0);
         fp.c1 = (float)taylor(1);
         fp.ctrl = ctrl;
+        fp.sketch = next_sketch;
         PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
         u.nprob = 2;
         u.prob[0].a = {Yb[cur], n, Lw.buf_stride, nullptr, 0};
@@ -899,19 +901,6 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         u.prob[0].ldc = n;
         u.prob[0].stride_c = Lw.buf_stride;
         u.prob[1].a = {R2b, n, Lw.buf_stride, nullptr, 0};
-        u.prob[1].b = {Zb[cur], n, Lw.buf_stride, nullptr, 0};
-        u.prob[1].c = Zb[nxt];
-        u.prob[1].ldc = n;
-        u.prob[1].stride_c = Lw.buf_stride;
-      } else {
-        // Y_{k+1} = Y_k g and Z_{k+1} = g Z_k, g = f_{d-1}(R) + alpha R^d formed on load
-        u.nprob = 2;
-        u.prob[0].a = {Yb[cur], n, Lw.buf_stride, nullptr, 0};
-        u.prob[0].b = {Rb, n, Lw.buf_stride, R2b, 1};
-        u.prob[0].c = Yb[nxt];
-        u.prob[0].ldc = n;
-        u.prob[0].stride_c = Lw.buf_stride;
-        u.prob[1].a = {Rb, n, Lw.buf_stride, R2b, 1};
         u.prob[1].b = {Zb[cur], n, Lw.buf_stride, nullptr, 0};
         u.prob[1].c = Zb[nxt];
         u.prob[1].ldc = n;
@@ -931,7 +920,6 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       r.products = (d - 1) + 1 + (k > 0 ? 1 : 0) + 1;
       r.count_update = 1;
       r.cfg = cfg;
-      r.sketch = make_sketch(Lw, ws, cfg, n, k + 1, stage, acc && k + 1 < o.max_iter);
       set_vec(r);
       PMX_TRY(q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, false, false, ROLE_RESID, q.s); }));
     }
@@ -1042,8 +1030,9 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     pi.cols = cols;
     pi.transpose = tr ? 1 : 0;
     pi.ctrl = ctrl;
+    pi.sketch = make_sketch(Lw, ws, cfg, cols, 0, 0, acc);
     PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_init(pi, false, batch, q.s); }));
-    auto residual = [&](float* Xc, int products, int count, int k_next) {
+    auto residual = [&](float* Xc, int products, int count) {
       GemmParams r = gemm_base(q.h, cols, cols, rows, batch);
       r.ctrl = ctrl;
       r.prob[0].a = {Xc, cols, bs, nullptr, 0};
@@ -1056,11 +1045,10 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       r.products = products;
       r.count_update = count;
       r.cfg = cfg;
-      r.sketch = make_sketch(Lw, ws, cfg, cols, k_next, 0, acc && k_next < o.max_iter);
       set_vec(r);
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
     };
-    PMX_TRY(residual(Xb[0], 1, 0, 0));
+    PMX_TRY(residual(Xb[0], 1, 0));
     for (int k = 0; k < o.max_iter; ++k) {
       PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b));
       const int cur = k & 1, nxt = cur ^ 1;
@@ -1071,8 +1059,9 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       u.c1 = (float)taylor(1);
       u.prob[0].a = {Xb[cur], cols, bs, nullptr, 0};
       u.prob[0].b = {Rb, cols, bs, R2b, 1};
-      if (h->explicit_g) {
-        // g written once in place of R^2 (read by the Krylov passes already)
+      {
+        // g written once in place of R^2 (read by the Krylov passes already),
+        // with the sketch of the next update
         FormGParams fp;
         memset(&fp, 0, sizeof(fp));
         fp.r = Rb;
@@ -1084,6 +1073,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
         fp.c0 = (float)taylor(0);
         fp.c1 = (float)taylor(1);
         fp.ctrl = ctrl;
+        fp.sketch = make_sketch(Lw, ws, cfg, cols, k + 1, 0, acc && k + 1 < o.max_iter);
         PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
         u.prob[0].b = {R2b, cols, bs, nullptr, 0};
       }
@@ -1092,7 +1082,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       u.prob[0].stride_c = bs;
       set_vec(u);
       PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
-      PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1, k + 1));
+      PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1));
     }
   } else {
     // bf16: every product is k-contiguous x k-contiguous (pmx_gemm_bf16.hip).
@@ -1103,7 +1093,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     float* Rh = at<float>(ws, Lw.bufs[6]);  // R in bf16
     float* Gh = at<float>(ws, Lw.bufs[7]);  // g in bf16
     const bool vec = (cols % 8 == 0) && (rows % 8 == 0) && (bs % 8 == 0);
-    auto residual = [&](float* Xtc, int products, int count, int k_next) {
+    auto residual = [&](float* Xtc, int products, int count) {
       GemmParams r = bf16_base(q.h, cols, cols, rows, batch);
       r.ctrl = ctrl;
       r.prob[0].a = {Xtc, rows, bs, nullptr, 0};
@@ -1119,7 +1109,6 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       r.products = products;
       r.count_update = count;
       r.cfg = cfg;
-      r.sketch = make_sketch(Lw, ws, cfg, cols, k_next, 0, acc && k_next < o.max_iter);
       r.vec = vec ? 1 : 0;
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_bf16(r, ROLE_RESID, q.s); });
     };
@@ -1141,9 +1130,10 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       x.out_t = (uint16_t*)(tr ? Xb[0] : Xt[0]);
       x.ldt = m;
       x.st = bs;
+      x.sketch = make_sketch(Lw, ws, cfg, cols, 0, 0, acc);
       PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_xpose(x, batch, q.s); }));
     }
-    PMX_TRY(residual(Xt[0], 1, 0, 0));
+    PMX_TRY(residual(Xt[0], 1, 0));
     for (int k = 0; k < o.max_iter; ++k) {
       if (d == 2) {
         GemmParams g = bf16_base(q.h, cols, cols, cols, batch);
@@ -1169,6 +1159,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       fg.c0 = (float)taylor(0);
       fg.c1 = (float)taylor(1);
       fg.ctrl = ctrl;
+      fg.sketch = make_sketch(Lw, ws, cfg, cols, k + 1, 0, acc && k + 1 < o.max_iter);
       PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fg, batch, q.s); }));
       const int cur = k & 1, nxt = cur ^ 1;
       GemmParams u = bf16_base(q.h, rows, cols, cols, batch);
@@ -1184,7 +1175,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       u.prob[1].stride_c = bs;
       u.vec = vec ? 1 : 0;
       PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_bf16(u, ROLE_UPDATE, q.s); }));
-      PMX_TRY(residual(Xt[nxt], (d - 1) + 1 + 1, 1, k + 1));
+      PMX_TRY(residual(Xt[nxt], (d - 1) + 1 + 1, 1));
     }
   }
   PolarFinishParams fp;

@@ -282,8 +282,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
 // C bf16 = acc and its transpose at prob[1].c.
 template <class C, int ROLE>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p) {
-  constexpr bool RESID = ROLE == ROLE_RESID;
-  constexpr int NT = C::NT, FM = C::FM, FN = C::FN;
+  constexpr int FM = C::FM, FN = C::FN;
   constexpr int WGN = C::BN / C::WN;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][C::LDS];
   __shared__ double red[C::WAVES];
@@ -309,7 +308,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
     }
     const uint16_t* A = reinterpret_cast<const uint16_t*>(pr.a.ptr) + (int64_t)b * pr.a.stride;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(pr.b.ptr) + (int64_t)b * pr.b.stride;
-    if (RESID) sketch_share(p.sketch, b, tile, tiles);
     const int m0 = tm * C::BM, n0 = tn * C::BN;
 
     f32x16 acc[FM][FN];
@@ -402,7 +400,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 template <int ROLE>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmParams p) {
   using C = BDma;
-  constexpr bool RESID = ROLE == ROLE_RESID;
   constexpr int FM = C::FM, FN = C::FN;  // 4 x 2 accumulators per wave
   __shared__ __attribute__((aligned(16))) unsigned char lds[DNS * DSTB];
   __shared__ double red[C::WAVES];
@@ -430,7 +427,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmParams p) {
       const int st = *(volatile int32_t*)&p.ctrl[b].status;
       if (st != PMX_RUNNING) continue;
     }
-    if (RESID) sketch_share(p.sketch, b, tile, tiles);
     const int m0 = tm * 256, n0 = tn * 256;
     const uint16_t* A = reinterpret_cast<const uint16_t*>(pr.a.ptr) + (int64_t)b * pr.a.stride;
     const uint16_t* B = reinterpret_cast<const uint16_t*>(pr.b.ptr) + (int64_t)b * pr.b.stride;
@@ -471,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmParams p) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    // the previous item's LDS reads and this item's sketch stores are done
+    // the previous item's LDS reads are done
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     issue(0);

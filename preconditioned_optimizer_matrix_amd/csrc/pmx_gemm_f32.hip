@@ -28,8 +28,7 @@
 //    (or c0 I + alpha R for d = 1), formed while its tile is loaded from R and
 //    R^2, so g is never written to memory.
 //  * Epilogues by role: plain store; residual R = I - acc with a deterministic
-//    Frobenius reduction and the convergence decision (last tile per matrix),
-//    while the blocks also generate the next iteration's Gaussian sketch;
+//    Frobenius reduction and the convergence decision (last tile per matrix);
 //    Shampoo EMA C = beta C + (1 - beta) acc + eps I in place.
 #include "pmx_internal.h"
 
@@ -400,7 +399,6 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
     pc.c1 = p.c1;
     pc.degree = p.degree;
     pc.alpha = (p.ctrl && (apoly || bpoly)) ? (float)p.ctrl[b].alpha : 0.f;
-    if (EPI == EPI_RESID) sketch_share(p.sketch, b, tc.tile, tiles);
     const int m0 = tc.tm * C::BM, n0 = tc.tn * C::BN;
 
     f32x16 acc[C::FM][C::FN];

@@ -263,7 +263,6 @@ struct GemmParams {
   int products;          // dense products to add to ctrl.gemms on completion
   int count_update;      // 1: this residual ends an update (iter += 1)
   IterCfg cfg;
-  SketchJob sketch;      // sketch of the next iteration, generated on the side
 };
 
 hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s);

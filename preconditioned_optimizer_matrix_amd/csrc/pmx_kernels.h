@@ -53,6 +53,7 @@ struct PolarInitParams {
   int64_t x_stride;
   int rows, cols, transpose;
   Ctrl* ctrl;
+  SketchJob sketch;      // the first sketch, generated on the side
 };
 
 struct SkinnyJob {
@@ -92,6 +93,7 @@ struct FormGParams {
   int vec;               // set by the launcher
   float c0, c1;
   Ctrl* ctrl;
+  SketchJob sketch;      // the next iteration's sketch, generated on the side
 };
 
 // 64 x 64 tile transpose to bf16: out_t[j][i] = f(in[i][j]) (cols x rows) and
@@ -111,6 +113,7 @@ struct XposeParams {
   int scale_inv_c;  // multiply the input by 1 / ctrl.c first (needs ctrl)
   float c0, c1;
   Ctrl* ctrl;  // null: unconditional; else skipped when the matrix is not running
+  SketchJob sketch;  // a sketch generated on the side (needs ctrl)
 };
 
 struct RootFinishParams {

@@ -167,6 +167,7 @@ __global__ __launch_bounds__(NT) void polar_init_kernel(PolarInitParams p) {
   const int b = blockIdx.y;
   Ctrl* cb = p.ctrl + b;
   if (load_status(cb) != PMX_RUNNING) return;
+  sketch_share(p.sketch, b, blockIdx.x, gridDim.x);
   const T* g = reinterpret_cast<const T*>(p.g) + (int64_t)b * p.g_stride;
   T* x = reinterpret_cast<T*>(p.x) + (int64_t)b * p.x_stride;
   const float fs = (float)(1.0 / cb->c);
@@ -611,6 +612,7 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   const int b = blockIdx.y;
   const Ctrl* cb = p.ctrl + b;
   if (load_status(cb) != PMX_RUNNING) return;
+  sketch_share(p.sketch, b, blockIdx.x, gridDim.x);
   const float alpha = (float)cb->alpha;
   const int n = p.n;
   const float* R = p.r + (int64_t)b * p.stride;
@@ -685,6 +687,7 @@ __global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
     if (load_status(p.ctrl + b) != PMX_RUNNING) return;
     alpha = (float)p.ctrl[b].alpha;
     if (p.scale_inv_c) scale = (float)(1.0 / p.ctrl[b].c);
+    sketch_share(p.sketch, b, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   }
   __shared__ float tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
