@@ -303,6 +303,9 @@ void set_vec(GemmParams& g) {
     const GemmProblem& p = g.prob[i];
     v = v && ptr_aligned16(p.a.ptr) && ptr_aligned16(p.b.ptr) && (p.a.ld % 4 == 0) &&
         (p.b.ld % 4 == 0) && (p.a.stride % 4 == 0) && (p.b.stride % 4 == 0);
+    // a symmetric output's mirrored stores are 16-byte stores into C
+    if (g.sym)
+      v = v && ptr_aligned16(p.c) && (p.ldc % 4 == 0) && (p.stride_c % 4 == 0);
   }
   g.vec = v ? 1 : 0;
 }
@@ -346,6 +349,7 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     g.prob[0].ldc = n;
     g.prob[0].stride_c = L.buf_stride;
     g.ctrl = ctrl;
+    g.sym = 1;  // R symmetric, so R^2 is: upper-triangle tiles, mirrored
     set_vec(g);
     e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
     if (e != hipSuccess) return e;
@@ -920,6 +924,10 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       r.products = (d - 1) + 1 + (k > 0 ? 1 : 0) + 1;
       r.count_update = 1;
       r.cfg = cfg;
+      // Z Y is a polynomial in A, symmetric in exact arithmetic: its upper
+      // triangle is kept and mirrored, so R and every g formed from it stay
+      // exactly symmetric
+      r.sym = 1;
       set_vec(r);
       PMX_TRY(q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, false, false, ROLE_RESID, q.s); }));
     }
@@ -1045,6 +1053,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       r.products = products;
       r.count_update = count;
       r.cfg = cfg;
+      r.sym = 1;  // X^T X: upper-triangle tiles, mirrored
       set_vec(r);
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
     };

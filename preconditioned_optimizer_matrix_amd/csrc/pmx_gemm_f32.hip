@@ -30,6 +30,9 @@
 //  * Epilogues by role: plain store; residual R = I - acc with a deterministic
 //    Frobenius reduction and the convergence decision (last tile per matrix);
 //    Shampoo EMA C = beta C + (1 - beta) acc + eps I in place.
+//  * Symmetric outputs (R^2, the residual, Gram products): with `sym` only the
+//    tiles on and above the diagonal are computed and each off-diagonal tile
+//    is also stored transposed, about half the products' work.
 #include "pmx_internal.h"
 
 namespace pmx {
@@ -359,6 +362,23 @@ __device__ __forceinline__ TileCoord map_item(int it, int G, int total, int tile
   return c;
 }
 
+// Item -> (matrix-problem z, tile) over the T (T + 1) / 2 tiles (tm <= tn) of
+// the upper triangle, row by row.
+__device__ __forceinline__ TileCoord map_item_sym(int it, int tiles, int T) {
+  TileCoord c;
+  c.z = it / tiles;
+  int t = it - c.z * tiles;
+  c.tile = t;
+  int tm = 0;
+  while (t >= T - tm) {
+    t -= T - tm;
+    ++tm;
+  }
+  c.tm = tm;
+  c.tn = tm + t;
+  return c;
+}
+
 template <class C, bool TA, bool TB, int ROLE>
 __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) {
   constexpr int EPI = ROLE == ROLE_RESID ? EPI_RESID : (ROLE == ROLE_STATS ? EPI_EMA : EPI_STORE);
@@ -375,12 +395,16 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
   const int wid = threadIdx.x >> 6;
   const int wm = (wid / C::WGN) * C::WTM, wn = (wid % C::WGN) * C::WTN;
   const bool vec = p.vec != 0;
-  const int tiles = p.tiles_m * p.tiles_n;
+  // symmetric output (C = C^T in exact arithmetic): the upper-triangle tiles
+  // only, each off-diagonal one also stored transposed
+  const bool sym = p.sym != 0;
+  const int tiles = sym ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   const int total = tiles * p.batch * p.nprob;
   const int G = gridDim.x;
 
   for (int it = blockIdx.x; it < total; it += G) {
-    const TileCoord tc = map_item(it, G, total, p.tiles_m, p.tiles_n, p.map_mode);
+    const TileCoord tc = sym ? map_item_sym(it, tiles, p.tiles_m)
+                             : map_item(it, G, total, p.tiles_m, p.tiles_n, p.map_mode);
     const int pi = tc.z % p.nprob;
     const int b = tc.z / p.nprob;
     if (p.ctrl) {
@@ -478,6 +502,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
     // Epilogue.  Lane l of a 32x32 accumulator holds column (l % 32) and rows
     // 8 * (v / 4) + 4 * (l / 32) + (v % 4), v = 0..15.
     const int hi = lane >> 5, col_in = lane & 31;
+    const bool mirror = sym && tc.tm != tc.tn;
     float fro = 0.f;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -485,21 +510,39 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
       for (int j = 0; j < C::FN; ++j) {
         const int col = n0 + wn + 32 * j + col_in;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (row < p.M && col < p.N) {
-            float* dst = Cm + (int64_t)row * pr.ldc + col;
-            float x = acc[i][j][v];
-            if (EPI == EPI_RESID) {
-              x = (row == col ? 1.f : 0.f) - x;
-              fro += x * x;
-            } else if (EPI == EPI_EMA) {
-              x = p.beta * *dst + p.omb * x + (row == col ? p.eps : 0.f);
+        for (int g = 0; g < 4; ++g) {
+          const int row_base = m0 + wm + 32 * i + 8 * g + 4 * hi;
+          float xs[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = row_base + r;
+            float x = acc[i][j][4 * g + r];
+            if (row < p.M && col < p.N) {
+              float* dst = Cm + (int64_t)row * pr.ldc + col;
+              if (EPI == EPI_RESID) {
+                x = (row == col ? 1.f : 0.f) - x;
+                fro += x * x;
+              } else if (EPI == EPI_EMA) {
+                x = p.beta * *dst + p.omb * x + (row == col ? p.eps : 0.f);
+              }
+              *dst = x;
             }
-            *dst = x;
+            xs[r] = x;
+          }
+          if (mirror && col < p.N) {
+            // C[col][row_base .. row_base + 3]: four consecutive elements
+            float* dst = Cm + (int64_t)col * pr.ldc + row_base;
+            if (vec && row_base + 3 < p.M) {
+              *reinterpret_cast<f32x4*>(dst) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (row_base + r < p.M) dst[r] = xs[r];
+            }
           }
         }
       }
+    if (mirror) fro *= 2.f;  // the tile stands for itself and its transpose
 
     if (EPI == EPI_RESID) {
       const double blocksum = block_sum<C::NW>((double)fro, red);
@@ -543,7 +586,10 @@ template <class C, bool TA, bool TB>
 hipError_t launch_role(GemmParams p, int role, hipStream_t s) {
   p.tiles_m = (p.M + C::BM - 1) / C::BM;
   p.tiles_n = (p.N + C::BN - 1) / C::BN;
-  const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch * p.nprob;
+  if (p.sym && (C::BM != C::BN || p.M != p.N)) return hipErrorInvalidValue;
+  const int64_t tiles = p.sym ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2
+                              : (int64_t)p.tiles_m * p.tiles_n;
+  const int64_t total = tiles * p.batch * p.nprob;
   int64_t g = total;
   if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
   const dim3 grid((unsigned)g), block(C::NT);
@@ -585,10 +631,16 @@ int gemm_f32_tiles(int M, int N) {
 }
 
 // Configuration choice: p.cfg_id >= 0 forces one; otherwise the largest tile
-// that still gives every CU at least one tile of the launch.
+// that still gives every CU at least one tile of the launch (square tiles for
+// symmetric outputs).
 hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s) {
   int id = p.cfg_id;
-  if (id < 0) {
+  if (p.sym) {
+    // square tiles only: the 128 x 128 tile once the triangle still gives
+    // every CU a tile, else 64 x 64
+    const int64_t t0 = (p.M + 127) / 128;
+    id = (t0 * (t0 + 1) / 2 * p.batch * p.nprob >= (p.num_cu > 0 ? p.num_cu : 256)) ? 0 : 4;
+  } else if (id < 0) {
     const int64_t units = (int64_t)p.batch * p.nprob;
     const int cu = p.num_cu > 0 ? p.num_cu : 256;
     if ((int64_t)tiles_of<C0>(p.M, p.N) * units >= cu) id = 0;

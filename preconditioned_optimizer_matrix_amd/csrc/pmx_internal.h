@@ -245,11 +245,12 @@ struct GemmParams {
   int batch;
   int M, N, K;
   int tiles_m, tiles_n;
-  int vec;         // 1: every operand allows 16-byte loads
+  int vec;         // 1: every operand allows 16-byte loads (and C 16-byte stores when sym)
   int max_blocks;  // persistent grid cap (0: one block per tile)
   int cfg_id;      // tile configuration (-1: chosen from the shape)
   int map_mode;    // tile order: 0 grouped, 1 grouped + XCD rounds, 2 row-major
   int dma;         // bf16: whole-tile variant with direct global-to-LDS loads
+  int sym;         // fp32: output symmetric, upper-triangle tiles mirrored (M == N)
   int num_cu;
   Ctrl* ctrl;      // per-matrix control blocks; null = unconditional
   // polynomial operands
