@@ -72,6 +72,22 @@ def cpu_baseline(G, L0, R0, beta, eps):
                 step_s=round(t4 - t0, 2))
 
 
+def root_exec_flops(n, batch, iters):
+    """Launched tile arithmetic of one fp32 inverse-root sequence of order n
+    (batch matrices per launch), from the update counts of its stages: a stage
+    of k updates runs 2 k - 1 full update products and 2 k + 1 symmetric ones
+    (k + 1 residuals I - Z Y, k powers R^2) over the upper-triangle tiles."""
+    bm = 128
+    T = -(-n // bm)
+    if T * (T + 1) // 2 * batch < 256:
+        bm = 64
+        T = -(-n // bm)
+    tf = -(-n // 128)
+    full = tf * tf * 2.0 * 128 * 128 * n if tf * tf * batch >= 256 else 2.0 * n ** 3
+    sym = T * (T + 1) // 2 * 2.0 * bm * bm * n
+    return sum((2 * int(k) - 1) * full + (2 * int(k) + 1) * sym for k in iters if int(k) > 0)
+
+
 def timed(torch, fn, steps, warmup):
     """Mean ms of `fn` over `steps` calls after `warmup` calls (HIP events on
     the current stream, synchronised on both sides)."""
@@ -138,13 +154,15 @@ def other_workload(args):
         info = pmx.new_info(64, dev)
         fn = lambda o: pmx.inv_root(A, 4, opts=o, aux=False, out=X, info=info, ws=ws)
         ms32 = timed(torch, lambda: fn(opts), args.steps, args.warmup)
-        gemms = int(pmx.parse_info(info)["gemms"].sum())
+        inf32 = pmx.parse_info(info)
+        gemms = int(inf32["gemms"].sum())
+        flops32 = sum(root_exec_flops(512, 64, inf32["iters"][b]) for b in range(64))
         ms = timed(torch, lambda: fn(o64), args.steps, args.warmup)
         gemms64 = int(pmx.parse_info(info)["gemms"].sum())
         out["kernel_trace_ms"] = traced(lambda: fn(o64))
         fn(taylor)
         tg = int(pmx.parse_info(info)["gemms"].sum())
-        tf = gemms * 2.0 * 512 ** 3 / (ms32 * 1e-3) / 1e12
+        tf = flops32 / (ms32 * 1e-3) / 1e12
         out.update(metric="ms per batched inverse-4th-root (64 x 512)", value=round(ms, 3),
                    unit="ms", dtype="f64 leading 4 updates per stage, then f32",
                    config={"workload": wl, "fp64_iters": 4},
@@ -184,7 +202,7 @@ def other_workload(args):
         out["kernel_trace_ms"] = traced(lambda: fn(opts))
         fn(taylor)
         tg = int(pmx.parse_info(info)[0]["gemms"])
-        tf = gemms * 2.0 * 1e12 / (ms * 1e-3) / 1e12
+        tf = root_exec_flops(10000, 1, inf["iters"]) / (ms * 1e-3) / 1e12
         out.update(metric="ms per square root (n=10^4, A^1/2 and A^-1/2)", value=round(ms, 2),
                    unit="ms", dtype="f32", config={"workload": wl}, gemms=gemms,
                    gemms_taylor=tg, gemm_ratio_taylor_over_prism=round(tg / gemms, 3),
@@ -294,7 +312,8 @@ def main():
     r_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ev]))
     iL, iR = pmx.parse_info(infoL)[0], pmx.parse_info(infoR)[0]
     gemmsR, gemmsL = int(iR["gemms"]), int(iL["gemms"])
-    tflops_r = gemmsR * 2.0 * n ** 3 / (r_ms * 1e-3) / 1e12
+    tflops_r = root_exec_flops(n, 1, iR["iters"]) / (r_ms * 1e-3) / 1e12
+    dense_tflops_r = gemmsR * 2.0 * n ** 3 / (r_ms * 1e-3) / 1e12
     log("step %.3f ms, R^-1/4 %.3f ms, gemms R %d L %d, iters R %s L %s, status R %s L %s"
         % (ms_step, r_ms, gemmsR, gemmsL, list(iR["iters"]), list(iL["iters"]),
            pmx.STATUS_NAMES[int(iR["status"])], pmx.STATUS_NAMES[int(iL["status"])]))
@@ -371,6 +390,7 @@ def main():
                    "L": pmx.STATUS_NAMES[int(iL["status"])]},
         "mfma_tflops_r_root": round(tflops_r, 2),
         "mfma_frac_r_root": round(tflops_r / PEAK_FP32_MFMA, 4),
+        "dense_equiv_tflops_r_root": round(dense_tflops_r, 2),
         "property_x4r_minus_i": prop,
         "roofline": roofline,
         "cpu_baseline": cpu,

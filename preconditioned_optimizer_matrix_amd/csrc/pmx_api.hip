@@ -24,6 +24,7 @@ struct pmx_context {
   int skinny_variant;      // skinny products: 0 In through LDS, 1 In read directly
   int bf16_dma;            // bf16 GEMM: 1 uses direct global-to-LDS loads for whole tiles (measured slower; off)
   int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
+  int split_k;             // 1: split-k tail for the fp32 products of the iterations
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -224,8 +225,8 @@ IterCfg make_cfg(const pmx_matfn_opts& o, int n, pmx_matfn_info* info) {
 
 // ------------------------------------------------------------------ workspace
 struct IterLayout {
-  size_t ctrl, partials, gram, bufs[10], b64[6], kbuf, total;
-  int64_t buf_stride, kstride, kld, pstride, gstride;
+  size_t ctrl, partials, gram, bufs[10], b64[6], kbuf, skc, skp, total;
+  int64_t buf_stride, kstride, kld, pstride, gstride, skcap;
 };
 
 // Work buffers of the iterative functions: `nbig` matrices of rows x cols
@@ -263,6 +264,13 @@ IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, i
   L.kstride = (((int64_t)cols * L.kld + 63) / 64) * 64;
   L.kbuf = off;
   off = align_up(off + sizeof(float) * (size_t)L.kstride * batch);
+  // split-k tail of the fp32 products: counters and two partial-tile slots
+  // per worker (128 x 128 tiles from order 512 on, else 64 x 64)
+  L.skc = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)kSplitMaxWorkers);
+  L.skcap = (int64_t)2 * kSplitMaxWorkers * (cols >= 512 ? 128 * 128 : 64 * 64);
+  L.skp = off;
+  off = align_up(off + sizeof(float) * (size_t)L.skcap);
   L.total = off;
   return L;
 }
@@ -295,6 +303,15 @@ GemmParams bf16_base(const pmx_context* h, int M, int N, int K, int batch) {
   g.map_mode = h->bf16_map;
   g.dma = h->bf16_dma;
   return g;
+}
+
+// The split-k tail buffers of an iterative call's workspace.
+void use_split(GemmParams& g, void* ws, const IterLayout& L) {
+  if (!g.sk_part && g.cfg_id < 0) {
+    g.sk_part = at<float>(ws, L.skp);
+    g.sk_cnt = at<uint32_t>(ws, L.skc);
+    g.sk_cap = L.skcap;
+  }
 }
 
 void set_vec(GemmParams& g) {
@@ -350,6 +367,7 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     g.prob[0].stride_c = L.buf_stride;
     g.ctrl = ctrl;
     g.sym = 1;  // R symmetric, so R^2 is: upper-triangle tiles, mirrored
+    if (q.h->split_k) use_split(g, ws, L);
     set_vec(g);
     e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
     if (e != hipSuccess) return e;
@@ -469,6 +487,8 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_BF16_DMA")) c->bf16_dma = atoi(e);
   c->small_fused = 1;
   if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
+  c->split_k = 1;
+  if (const char* e = getenv("PMX_SPLITK")) c->split_k = atoi(e);
   *handle = c;
   return PMX_OK;
 }
@@ -719,7 +739,9 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
     PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_small_root(sp, batch, q.s); }));
     return PMX_OK;
   }
-  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+    return launch_ctrl_reset(ctrl, info, batch, at<uint32_t>(ws, Lw.skc), kSplitMaxWorkers, q.s);
+  }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
@@ -910,6 +932,11 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         u.prob[1].ldc = n;
         u.prob[1].stride_c = Lw.buf_stride;
       }
+      // Y g and g Z are left whole: the full products keep Y_k = A Z_k^T as
+      // computed, which keeps Z Y symmetric by structure; mirroring their
+      // upper triangles would mix Y g with g Y and lose that (measurably
+      // less accurate on ill-conditioned inputs)
+      if (q.h->split_k) use_split(u, ws, Lw);
       set_vec(u);
       PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
       GemmParams r = gemm_base(q.h, n, n, n, batch);
@@ -924,10 +951,10 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       r.products = (d - 1) + 1 + (k > 0 ? 1 : 0) + 1;
       r.count_update = 1;
       r.cfg = cfg;
-      // Z Y is a polynomial in A, symmetric in exact arithmetic: its upper
-      // triangle is kept and mirrored, so R and every g formed from it stay
-      // exactly symmetric
+      // Z Y = Z A Z^T is symmetric by structure: its upper triangle is kept
+      // and mirrored, so R and every g formed from it stay exactly symmetric
       r.sym = 1;
+      if (q.h->split_k) use_split(r, ws, Lw);
       set_vec(r);
       PMX_TRY(q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, false, false, ROLE_RESID, q.s); }));
     }
@@ -1023,7 +1050,9 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_small_polar(sp, batch, q.s); }));
     return PMX_OK;
   }
-  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_ctrl_reset(ctrl, info, batch, q.s); }));
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+    return launch_ctrl_reset(ctrl, info, batch, at<uint32_t>(ws, Lw.skc), kSplitMaxWorkers, q.s);
+  }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(G, bf, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
@@ -1054,6 +1083,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       r.count_update = count;
       r.cfg = cfg;
       r.sym = 1;  // X^T X: upper-triangle tiles, mirrored
+      if (q.h->split_k) use_split(r, ws, Lw);
       set_vec(r);
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
     };
@@ -1089,6 +1119,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       u.prob[0].c = Xb[nxt];
       u.prob[0].ldc = cols;
       u.prob[0].stride_c = bs;
+      if (q.h->split_k) use_split(u, ws, Lw);
       set_vec(u);
       PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
       PMX_TRY(residual(Xb[nxt], (d - 1) + 1 + 1, 1));

@@ -30,9 +30,12 @@
 //  * Epilogues by role: plain store; residual R = I - acc with a deterministic
 //    Frobenius reduction and the convergence decision (last tile per matrix);
 //    Shampoo EMA C = beta C + (1 - beta) acc + eps I in place.
-//  * Symmetric outputs (R^2, the residual, Gram products): with `sym` only the
-//    tiles on and above the diagonal are computed and each off-diagonal tile
-//    is also stored transposed, about half the products' work.
+//  * Symmetric outputs (R^2, the residuals Z A Z^T and X^T X): with `sym` only
+//    the tiles on and above the diagonal are computed and each off-diagonal
+//    tile is also stored transposed, about half the products' work.
+#include <algorithm>
+#include <type_traits>
+
 #include "pmx_internal.h"
 
 namespace pmx {
@@ -209,8 +212,8 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[FM_][FN_], float* sm
                                               const float* __restrict__ A2, int64_t lda,
                                               const float* __restrict__ B,
                                               const float* __restrict__ B2, int64_t ldb,
-                                              const PolyCtx& pc, int m0, int n0, int nk,
-                                              int lane, int wm, int wn) {
+                                              const PolyCtx& pc, int m0, int n0, int kb,
+                                              int nk, int lane, int wm, int wn) {
   using TA = OpTile<C, true, C::BM>;
   using TB = OpTile<C, false, C::BN>;
   constexpr int FM = C::FM, FN = C::FN, BK = C::BK, KH = C::KH;
@@ -277,14 +280,14 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[FM_][FN_], float* sm
       *reinterpret_cast<f32x4*>(smem_b(stage) + blds[i]) = v;
     }
   };
-  gload(0);
-  lstore(0, 0);
+  gload(kb * BK);
+  lstore(0, kb * BK);
   __syncthreads();
   const int fa_ofs = (wm + (lane & 31)) * TA::LD + (lane >> 5) * KH;
   const int fb_ofs = ((lane >> 5) * KH) * TB::LD + wn + (lane & 31);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;  // the last tile reloads itself
+    const int kn = (kb + (kt + 1 < nk ? kt + 1 : kt)) * BK;  // the last tile reloads itself
     const float* sa = smem_a(cur) + fa_ofs;
     const float* sb = smem_b(cur) + fb_ofs;
     f32x4 fa[FM][2];
@@ -379,17 +382,40 @@ __device__ __forceinline__ TileCoord map_item_sym(int it, int tiles, int T) {
   return c;
 }
 
-template <class C, bool TA, bool TB, int ROLE>
+// Split-k tail ("stream-k").  When a launch's tiles do not divide evenly
+// over the compute units, the last sk_rem items are not given out whole:
+// their k tiles, laid end to end, are cut into sk_workers equal spans, one per
+// extra block.  A span's partial accumulators go to a slot of sk_part; the
+// block that completes a tile's last span (per-tile arrival counter in
+// sk_cnt) adds the tile's slots in k order, so the sum does not depend on the
+// order of arrival, resets the counter and runs the epilogue.  The host makes
+// spans no longer than a tile, so a worker touches at most two tiles and
+// owns slots 2 w and 2 w + 1.
+__device__ __forceinline__ int64_t span_start(int w, int64_t U, int W) {
+  return (int64_t)w * U / W;
+}
+
+// the worker whose span holds k-tile unit u (span_start(w) <= u < span_start(w + 1))
+__device__ __forceinline__ int span_owner(int64_t u, int64_t U, int W) {
+  int w = (int)(u * W / U);
+  while (w + 1 < W && span_start(w + 1, U, W) <= u) ++w;
+  while (w > 0 && span_start(w, U, W) > u) --w;
+  return w;
+}
+
+template <class C, bool TA, bool TB, int ROLE, bool SPLIT>
 __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) {
   constexpr int EPI = ROLE == ROLE_RESID ? EPI_RESID : (ROLE == ROLE_STATS ? EPI_EMA : EPI_STORE);
   constexpr bool AKC = Layout<true, TA>::kc;
   constexpr bool BKC = Layout<false, TB>::kc;
   using TAo = OpTile<C, AKC, C::BM>;
   using TBo = OpTile<C, BKC, C::BN>;
+  constexpr int TILE = C::BM * C::BN;
 
   __shared__ __attribute__((aligned(16))) float smem_a[C::STAGES][TAo::FLOATS];
   __shared__ __attribute__((aligned(16))) float smem_b[C::STAGES][TBo::FLOATS];
   __shared__ double red[C::NW];
+  __shared__ int sk_first, sk_pieces;
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -400,21 +426,29 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
   const bool sym = p.sym != 0;
   const int tiles = sym ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   const int total = tiles * p.batch * p.nprob;
-  const int G = gridDim.x;
+  const int nk = (p.K + C::BK - 1) / C::BK;
+  constexpr bool split = SPLIT;  // launched with sk_part set
+  const int dp = split ? p.sk_dp : total;  // items computed whole
+  const int G = split ? (int)gridDim.x - p.sk_workers : (int)gridDim.x;
 
-  for (int it = blockIdx.x; it < total; it += G) {
-    const TileCoord tc = sym ? map_item_sym(it, tiles, p.tiles_m)
-                             : map_item(it, G, total, p.tiles_m, p.tiles_n, p.map_mode);
+  f32x16 acc[C::FM][C::FN];
+
+  auto coord = [&](int it) __attribute__((always_inline)) {
+    return sym ? map_item_sym(it, tiles, p.tiles_m)
+               : map_item(it, G > 0 ? G : 1, total, p.tiles_m, p.tiles_n, p.map_mode);
+  };
+  auto running = [&](const TileCoord& tc) __attribute__((always_inline)) {
+    return !p.ctrl ||
+           *(volatile int32_t*)&p.ctrl[tc.z / p.nprob].status == PMX_RUNNING;
+  };
+
+  // acc = the product over k tiles [kb, ke) of the tile tc
+  auto compute = [&](const TileCoord& tc, int kb, int ke) __attribute__((always_inline)) {
     const int pi = tc.z % p.nprob;
     const int b = tc.z / p.nprob;
-    if (p.ctrl) {
-      const int st = *(volatile int32_t*)&p.ctrl[b].status;
-      if (st != PMX_RUNNING) continue;
-    }
     const GemmProblem& pr = p.prob[pi];
     const float* __restrict__ A = pr.a.ptr + (int64_t)b * pr.a.stride;
     const float* __restrict__ B = pr.b.ptr + (int64_t)b * pr.b.stride;
-    float* __restrict__ Cm = pr.c + (int64_t)b * pr.stride_c;
     const float* __restrict__ A2 = pr.a.poly && pr.a.ptr2 ? pr.a.ptr2 + (int64_t)b * pr.a.stride : A;
     const float* __restrict__ B2 = pr.b.poly && pr.b.ptr2 ? pr.b.ptr2 + (int64_t)b * pr.b.stride : B;
     const bool apoly = pr.a.poly != 0, bpoly = pr.b.poly != 0;
@@ -424,44 +458,45 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
     pc.degree = p.degree;
     pc.alpha = (p.ctrl && (apoly || bpoly)) ? (float)p.ctrl[b].alpha : 0.f;
     const int m0 = tc.tm * C::BM, n0 = tc.tn * C::BN;
-
-    f32x16 acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    const int nk = (p.K + C::BK - 1) / C::BK;
     __syncthreads();  // the previous item's last LDS reads are done
+    if constexpr (SPLIT) {
+      // launched only for whole tiles of plain NN operands
+      mainloop_fast<C, false, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2,
+                                     pr.b.ld, pc, m0, n0, kb, ke - kb, lane, wm, wn);
+      return;
+    }
     if constexpr (AKC && !BKC && C::STAGES == 2 && C::KH == 8) {
       if (vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && p.K % C::BK == 0 &&
           !(apoly && bpoly) && !(apoly && A2 == A && pc.degree == 2) &&
           !(bpoly && B2 == B && pc.degree == 2)) {
         if (apoly)
-          mainloop_fast<C, true, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2, pr.b.ld, pc,
-                                        m0, n0, nk, lane, wm, wn);
+          mainloop_fast<C, true, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B,
+                                        B2, pr.b.ld, pc, m0, n0, kb, ke - kb, lane, wm, wn);
         else if (bpoly)
-          mainloop_fast<C, false, true>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2, pr.b.ld, pc,
-                                        m0, n0, nk, lane, wm, wn);
+          mainloop_fast<C, false, true>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B,
+                                        B2, pr.b.ld, pc, m0, n0, kb, ke - kb, lane, wm, wn);
         else
-          mainloop_fast<C, false, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2, pr.b.ld, pc,
-                                         m0, n0, nk, lane, wm, wn);
-        goto epilogue;
+          mainloop_fast<C, false, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B,
+                                         B2, pr.b.ld, pc, m0, n0, kb, ke - kb, lane, wm, wn);
+        return;
       }
     }
-    {
     f32x4 ra[TAo::PER_THREAD], rb[TBo::PER_THREAD];
-    load_tile<C, AKC, C::BM>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, 0, p.K, vec);
-    load_tile<C, BKC, C::BN>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, 0, p.K, vec);
+    load_tile<C, AKC, C::BM>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, kb * C::BK, p.K, vec);
+    load_tile<C, BKC, C::BN>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, kb * C::BK, p.K, vec);
     store_tile<C, AKC, C::BM>(smem_a[0], ra);
     store_tile<C, BKC, C::BN>(smem_b[0], rb);
     __syncthreads();
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = C::STAGES == 2 ? (kt & 1) : 0;
-      const bool more = kt + 1 < nk;
+    for (int kt = kb; kt < ke; ++kt) {
+      const int cur = C::STAGES == 2 ? ((kt - kb) & 1) : 0;
+      const bool more = kt + 1 < ke;
       if (more) {
         load_tile<C, AKC, C::BM>(ra, A, A2, apoly, pc, pr.a.ld, m0, p.M, (kt + 1) * C::BK, p.K, vec);
         load_tile<C, BKC, C::BN>(rb, B, B2, bpoly, pc, pr.b.ld, n0, p.N, (kt + 1) * C::BK, p.K, vec);
@@ -496,11 +531,16 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
         }
       }
     }
-    }
+  };
 
-  epilogue:
-    // Epilogue.  Lane l of a 32x32 accumulator holds column (l % 32) and rows
-    // 8 * (v / 4) + 4 * (l / 32) + (v % 4), v = 0..15.
+  // Epilogue of the tile tc from acc.  Lane l of a 32x32 accumulator holds
+  // column (l % 32) and rows 8 * (v / 4) + 4 * (l / 32) + (v % 4), v = 0..15.
+  auto epilogue = [&](const TileCoord& tc) __attribute__((always_inline)) {
+    const int pi = tc.z % p.nprob;
+    const int b = tc.z / p.nprob;
+    const GemmProblem& pr = p.prob[pi];
+    float* __restrict__ Cm = pr.c + (int64_t)b * pr.stride_c;
+    const int m0 = tc.tm * C::BM, n0 = tc.tn * C::BN;
     const int hi = lane >> 5, col_in = lane & 31;
     const bool mirror = sym && tc.tm != tc.tn;
     float fro = 0.f;
@@ -557,6 +597,100 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
         }
       }
     }
+  };
+
+  if constexpr (!split) {
+    for (int it = blockIdx.x; it < total; it += G) {
+      const TileCoord tc = coord(it);
+      if (!running(tc)) continue;
+      compute(tc, 0, nk);
+      epilogue(tc);
+    }
+  } else {
+    // Blocks below G take whole items it = blockIdx.x, + G, ... < dp; split-k
+    // worker w takes the k-tile units [span_start(w), span_start(w + 1)) of
+    // the tail, piece by piece (piece j of its span fills slot 2 w + j).
+    const bool worker = (int)blockIdx.x >= G;
+    const int W = p.sk_workers;
+    const int w = (int)blockIdx.x - G;
+    const int64_t U = (int64_t)p.sk_rem * nk;
+    int64_t u = worker ? span_start(w, U, W) : 0;
+    const int64_t u1 = worker ? span_start(w + 1, U, W) : 0;
+    int it = blockIdx.x;
+    for (int piece = 0;; ++piece) {
+      int t, kb, ke;
+      if (!worker) {
+        if (it >= dp) break;
+        t = it;
+        kb = 0;
+        ke = nk;
+        it += G;
+      } else {
+        if (u >= u1) break;
+        const int tt = (int)(u / nk);
+        kb = (int)(u - (int64_t)tt * nk);
+        ke = (int)((int64_t)nk < kb + (u1 - u) ? (int64_t)nk : kb + (u1 - u));
+        u += ke - kb;
+        t = dp + tt;
+      }
+      const TileCoord tc = coord(t);
+      if (!running(tc)) continue;
+      compute(tc, kb, ke);
+      if (kb != 0 || ke != nk) {
+        t -= dp;  // tail tile index
+        {
+          f32x4* slot = reinterpret_cast<f32x4*>(p.sk_part + (int64_t)(2 * w + piece) * TILE);
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                slot[((i * C::FN + j) * 4 + g) * C::NT + threadIdx.x] =
+                    f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                          acc[i][j][4 * g + 3]};
+        }
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          const int wa = span_owner((int64_t)t * nk, U, W);
+          const int wb = span_owner((int64_t)t * nk + nk - 1, U, W);
+          const uint32_t prev = atomicAdd(&p.sk_cnt[t], 1u);
+          sk_first = wa;
+          sk_pieces = prev == (uint32_t)(wb - wa) ? wb - wa + 1 : 0;
+        }
+        __syncthreads();
+        const int npc = sk_pieces, wa = sk_first;
+        if (npc == 0) continue;
+        // the last span of the tile: its slots in k order
+        __threadfence();
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        for (int q = 0; q < npc; ++q) {
+          const int wq = wa + q;
+          // the tile is the first (slot 2 wq) or the second (2 wq + 1) of wq's span
+          const int first = (int)(span_start(wq, U, W) / nk);
+          const f32x4* slot = reinterpret_cast<const f32x4*>(
+              p.sk_part + (int64_t)(2 * wq + (t == first ? 0 : 1)) * TILE);
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 x = slot[((i * C::FN + j) * 4 + g) * C::NT + threadIdx.x];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][4 * g + r] += x[r];
+              }
+        }
+        if (threadIdx.x == 0) p.sk_cnt[t] = 0u;
+      }
+      epilogue(tc);
+    }
   }
 }
 
@@ -582,25 +716,55 @@ int tiles_of(int M, int N) {
   return ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
 }
 
-template <class C, bool TA, bool TB>
-hipError_t launch_role(GemmParams p, int role, hipStream_t s) {
+// Split-k variants: the iteration roles (R^2, updates, residuals) on the
+// configurations the automatic choice takes.
+template <class C, bool TA, bool TB, int ROLE>
+constexpr bool kSplitVariant =
+    !TA && !TB && (ROLE == ROLE_POWER || ROLE == ROLE_UPDATE || ROLE == ROLE_RESID) &&
+    (std::is_same<C, C0>::value || std::is_same<C, C4>::value || std::is_same<C, C5>::value);
+
+template <class C, bool TA, bool TB, int ROLE>
+hipError_t launch_role(GemmParams p, hipStream_t s) {
   p.tiles_m = (p.M + C::BM - 1) / C::BM;
   p.tiles_n = (p.N + C::BN - 1) / C::BN;
   if (p.sym && (C::BM != C::BN || p.M != p.N)) return hipErrorInvalidValue;
   const int64_t tiles = p.sym ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2
                               : (int64_t)p.tiles_m * p.tiles_n;
   const int64_t total = tiles * p.batch * p.nprob;
-  int64_t g = total;
-  if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
-  const dim3 grid((unsigned)g), block(C::NT);
-  switch (role) {
-    case ROLE_POWER: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_POWER>), grid, block, 0, s, p); break;
-    case ROLE_UPDATE: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_UPDATE>), grid, block, 0, s, p); break;
-    case ROLE_RESID: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_RESID>), grid, block, 0, s, p); break;
-    case ROLE_STATS: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_STATS>), grid, block, 0, s, p); break;
-    case ROLE_APPLY: hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE_APPLY>), grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
+  // split-k tail when the items leave the last round of the compute units
+  // part-filled: the remainder's k tiles are spread over one extra block per
+  // CU (at least two k tiles each, so every span is shorter than a tile)
+  float* const skp = p.sk_part;
+  p.sk_part = nullptr;
+  p.sk_dp = (int)total;
+  p.sk_rem = p.sk_workers = 0;
+  if (kSplitVariant<C, TA, TB, ROLE>) {
+    const int cu = p.num_cu > 0 ? p.num_cu : 256;
+    const int64_t nk = (p.K + C::BK - 1) / C::BK;
+    const int64_t rem = total % cu;
+    const int64_t W = std::min<int64_t>(std::min(cu, kSplitMaxWorkers), rem * nk / 2);
+    // split variants run whole tiles of plain operands only
+    bool whole = p.vec && p.M % C::BM == 0 && p.N % C::BN == 0 && p.K % C::BK == 0;
+    for (int i = 0; i < p.nprob; ++i) whole = whole && !p.prob[i].a.poly && !p.prob[i].b.poly;
+    if (whole && skp && p.sk_cnt && rem > 0 && nk >= 4 && W >= rem &&
+        2 * W * C::BM * C::BN <= p.sk_cap) {
+      p.sk_part = skp;
+      p.sk_dp = (int)(total - rem);
+      p.sk_rem = (int)rem;
+      p.sk_workers = (int)W;
+    }
   }
+  int64_t g = p.sk_dp;
+  if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
+  const dim3 grid((unsigned)(g + p.sk_workers)), block(C::NT);
+  if (grid.x == 0) return hipSuccess;
+  if constexpr (kSplitVariant<C, TA, TB, ROLE>) {
+    if (p.sk_part) {
+      hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, true>), grid, block, 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -609,16 +773,22 @@ hipError_t launch_role(GemmParams p, int role, hipStream_t s) {
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s) {
   if (!ta && !tb) {
-    if (role == ROLE_STATS) return hipErrorInvalidValue;
-    return launch_role<C, false, false>(p, role, s);
+    switch (role) {
+      case ROLE_POWER: return launch_role<C, false, false, ROLE_POWER>(p, s);
+      case ROLE_UPDATE: return launch_role<C, false, false, ROLE_UPDATE>(p, s);
+      case ROLE_RESID: return launch_role<C, false, false, ROLE_RESID>(p, s);
+      case ROLE_APPLY: return launch_role<C, false, false, ROLE_APPLY>(p, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   if (!ta && tb) {
     if (role != ROLE_STATS) return hipErrorInvalidValue;
-    return launch_role<C, false, true>(p, role, s);
+    return launch_role<C, false, true, ROLE_STATS>(p, s);
   }
   if (ta && !tb) {
-    if (role != ROLE_STATS && role != ROLE_RESID) return hipErrorInvalidValue;
-    return launch_role<C, true, false>(p, role, s);
+    if (role == ROLE_STATS) return launch_role<C, true, false, ROLE_STATS>(p, s);
+    if (role == ROLE_RESID) return launch_role<C, true, false, ROLE_RESID>(p, s);
+    return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

@@ -239,6 +239,9 @@ struct GemmProblem {
   int64_t stride_c;
 };
 
+// Most split-k workers (and per-tile counters) of one fp32 GEMM launch.
+constexpr int kSplitMaxWorkers = 256;
+
 struct GemmParams {
   GemmProblem prob[2];
   int nprob;       // problems per launch (the two updates Y g and g Z share one)
@@ -264,6 +267,13 @@ struct GemmParams {
   int products;          // dense products to add to ctrl.gemms on completion
   int count_update;      // 1: this residual ends an update (iter += 1)
   IterCfg cfg;
+  // fp32 split-k tail (null sk_part: every item whole).  The caller provides
+  // sk_cap floats of partial-tile slots and kSplitMaxWorkers zeroed per-tile
+  // counters (each launch leaves them zero); the launcher fills in the split.
+  float* sk_part;
+  uint32_t* sk_cnt;
+  int64_t sk_cap;
+  int sk_dp, sk_rem, sk_workers;
 };
 
 hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s);

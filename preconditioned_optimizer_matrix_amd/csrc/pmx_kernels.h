@@ -243,7 +243,9 @@ hipError_t launch_stage_init_f64(const StageInit64Params& p, int batch, hipStrea
 hipError_t launch_form_g_f64(const FormG64Params& p, int batch, hipStream_t s);
 hipError_t launch_handover_f64(const Handover64Params& p, int batch, hipStream_t s);
 
-hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStream_t s);
+// Resets the control blocks and infos of a call and zeroes nzero words at zero.
+hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, uint32_t* zero,
+                             int nzero, hipStream_t s);
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,
                             int64_t pstride, pmx_matfn_info* info, hipStream_t s);

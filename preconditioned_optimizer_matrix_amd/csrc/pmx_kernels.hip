@@ -19,8 +19,10 @@ __device__ __forceinline__ int32_t load_status(const Ctrl* c) {
 }  // namespace
 
 // ---------------------------------------------------------------- control
-__global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch) {
+__global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch, uint32_t* zero,
+                                  int nzero) {
   const int b = blockIdx.x;
+  for (int i = b * blockDim.x + threadIdx.x; i < nzero; i += gridDim.x * blockDim.x) zero[i] = 0u;
   if (b >= batch) return;
   if (threadIdx.x == 0) {
     Ctrl c;
@@ -795,8 +797,10 @@ static int grid_rows(int rows, int cap) {
   return g < 1 ? 1 : g;
 }
 
-hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(ctrl_reset_kernel, dim3(batch), dim3(NT), 0, s, ctrl, info, batch);
+hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, uint32_t* zero,
+                             int nzero, hipStream_t s) {
+  hipLaunchKernelGGL(ctrl_reset_kernel, dim3(batch), dim3(NT), 0, s, ctrl, info, batch, zero,
+                     nzero);
   return hipGetLastError();
 }
 

@@ -57,8 +57,10 @@ def test_workspace_sizes_and_option_validation():
     o = pmx.default_opts()
     n = 4096
     b = pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, o)
-    # six n x n fp32 work matrices dominate
-    assert 6 * 4 * n * n <= b < 6 * 4 * n * n + (1 << 20)
+    # six n x n fp32 work matrices, then the split-k slots (two 128 x 128
+    # fp32 tiles for each of 256 workers)
+    sk = 2 * 256 * 128 * 128 * 4
+    assert 6 * 4 * n * n + sk <= b < 6 * 4 * n * n + sk + (1 << 20)
     bb = pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 64, pmx.F32, o)
     assert bb >= 64 * 6 * 4 * 512 * 512
     assert pmx.workspace_bytes(pmx.OP_STATS, 1024, 4096, 1, pmx.F32, None) == 0
