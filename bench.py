@@ -37,6 +37,11 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 256 MiB fp32 buffer 4 times (a plain copy kernel of "
                          "known traffic, for scaling HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only write the update GEMM's HBM traffic record from four "
+                         "rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of "
+                         "'--steps 1 --warmup 0 --no-cpu-baseline --no-trace', then of "
+                         "--calibrate-copy)")
     ap.add_argument("--workload", default="shampoo_1024x4096",
                     choices=["shampoo_1024x4096", "spd_64", "blocks_64x512",
                              "muon_32x4096x1024", "mp_10000"])
@@ -211,6 +216,68 @@ def other_workload(args):
     print(json.dumps(out), flush=True)
 
 
+UPDATE_KERNEL = ("gemm_f32_kernel<pmx::(anonymous namespace)::Cfg<128, 128, 16, 2, 2, 3, 2>, "
+                 "false, false, 1, false>")
+
+
+def write_traffic(dirs):
+    """profiles/update_gemm_traffic.json from rocprofv3 counter folders: the
+    first 60 dispatches of the n = 4096 update GEMM (the first step's R^-1/4
+    call, early exits included), each counter scaled by what it reads for the
+    plain 256 MiB copy of calibrate_copy()."""
+    import csv
+    import glob
+
+    def per_dispatch(d, pick):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        vals = {}
+        for r in csv.DictReader(open(f)):
+            if pick(r["Kernel_Name"]):
+                k = int(r["Dispatch_Id"])
+                vals[k] = vals.get(k, 0.0) + float(r["Counter_Value"])
+        return [vals[k] for k in sorted(vals)]
+
+    upd = lambda name: UPDATE_KERNEL in name
+    cpy = lambda name: "copyBuffer" in name
+    n_launch = 60
+    fetch = per_dispatch(dirs[0], upd)[:n_launch]
+    write = per_dispatch(dirs[1], upd)[:n_launch]
+    cf = per_dispatch(dirs[2], cpy)
+    cw = per_dispatch(dirs[3], cpy)
+    true_kib = 256 * 1024.0
+    fs, ws = true_kib / np.mean(cf), true_kib / np.mean(cw)
+    f_raw, w_raw = float(np.mean(fetch)), float(np.mean(write))
+    rec = {
+        "kernel": "gemm_f32_kernel<Cfg<128,128,16,2,2,3>,NN,ROLE_UPDATE> (n=4096 updates of R^-1/4)",
+        "source_sha256": source_digest(),
+        "source_files": ["preconditioned_optimizer_matrix_amd/csrc/pmx_gemm_f32.hip",
+                         "preconditioned_optimizer_matrix_amd/csrc/pmx_api.hip"],
+        "launches_per_step": n_launch,
+        "fetch_kib_per_launch_raw": round(f_raw, 1),
+        "write_kib_per_launch_raw": round(w_raw, 1),
+        "copy_kib_true": true_kib,
+        "copy_fetch_kib_raw": round(float(np.mean(cf)), 1),
+        "copy_write_kib_raw": round(float(np.mean(cw)), 1),
+        "fetch_scale": round(fs, 5),
+        "write_scale": round(ws, 5),
+        "hbm_bytes_per_launch": int(round((f_raw * fs + w_raw * ws) * 1024)),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --calibrate-copy",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --calibrate-copy",
+            "python3 bench.py --traffic-from <four dirs>",
+        ],
+        "reduction": "per counter: mean over the first 60 dispatches of the kernel (the first "
+                     "step's R^-1/4 call, early exits included); copy: mean over the 4 "
+                     "__amd_rocclr_copyBuffer dispatches of 256 MiB",
+    }
+    path = os.path.join(ROOT, "profiles", "update_gemm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec), flush=True)
+
+
 def calibrate_copy():
     """A plain device copy of known size: 4 launches, each reading and writing
     256 MiB, so FETCH_SIZE / WRITE_SIZE per launch should read 262144 KiB."""
@@ -259,6 +326,8 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.traffic_from:
+        return write_traffic(args.traffic_from)
     if args.workload != "shampoo_1024x4096":
         return other_workload(args)
     import torch
