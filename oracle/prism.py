@@ -27,8 +27,8 @@ implements; every one is listed in the design notes):
     phi_S(alpha) = || r(R_k; alpha) S ||_F^2, a quartic in alpha whose
     coefficients come from the Gram matrix of K_j = R_k^j S;
   * alpha_k = argmin of phi_S over [lo, hi] (candidates: both ends and the real
-    critical points inside); default [lo, hi] = [1/2, 1] for d = 1 and
-    [3/8, 1.47] for d = 2 (see oracle.interval);
+    critical points inside); default [lo, hi] = [1/2, 1] for d = 1,
+    [3/8, 1.47] for d = 2 and [5/16, 2.46] for d = 3 (see oracle.interval);
   * stopping: r_k = ||R_k||_F / sqrt(n) <= tol; stagnation when r_{k-1} < 1e-2
     and r_k > 0.9 r_{k-1}; divergence when r_k > 2; max_iter updates at most.
 """
@@ -55,12 +55,16 @@ def taylor_coeff(j):
 
 def default_interval(d):
     """[lo, hi] for the adaptive coefficient ([PRISM synthesis] Part II.1 gives
-    [1/2, 1] for d = 1; for d = 2 the same rule, see oracle.interval)."""
+    [1/2, 1] for d = 1; for d = 2 and d = 3 the same rule, see oracle.interval:
+    lo = c_d and hi = the rule's bound (1.4722, 2.4686) rounded down to two
+    decimals)."""
     if d == 1:
         return 0.5, 1.0
     if d == 2:
         return 0.375, 1.47
-    raise ValueError("degree must be 1 or 2")
+    if d == 3:
+        return 0.3125, 2.46
+    raise ValueError("degree must be 1, 2 or 3")
 
 
 def map_coeffs(d):

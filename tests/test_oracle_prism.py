@@ -16,7 +16,7 @@ def test_taylor_coefficients_binomial_series():
         assert prism.taylor_coeff(j) == pytest.approx(binom(-0.5, j) * (-1) ** j, rel=1e-15)
 
 
-@pytest.mark.parametrize("d", [1, 2])
+@pytest.mark.parametrize("d", [1, 2, 3])
 def test_residual_map_direct_evaluation(d):
     # r(xi; alpha) = 1 - (1 - xi) (f_{d-1}(xi) + alpha xi^d)^2, evaluated directly
     rng = np.random.default_rng(d)
@@ -33,20 +33,22 @@ def test_residual_map_direct_evaluation(d):
 def _textbook_ns(Y0, d, iters):
     """Classical coupled Newton-Schulz (Higham's coupled iteration):
     d = 1: M = (3I - ZY)/2;  d = 2: M = (15I - 10 ZY + 3 (ZY)^2)/8;
-    Y <- Y M, Z <- M Z."""
+    d = 3: M = (35I - 35 ZY + 21 (ZY)^2 - 5 (ZY)^3)/16;  Y <- Y M, Z <- M Z."""
     n = Y0.shape[0]
     Y, Z = Y0.copy(), np.eye(n)
     for _ in range(iters):
         T = Z @ Y
         if d == 1:
             M = (3 * np.eye(n) - T) / 2
-        else:
+        elif d == 2:
             M = (15 * np.eye(n) - 10 * T + 3 * T @ T) / 8
+        else:
+            M = (35 * np.eye(n) - 35 * T + 21 * T @ T - 5 * T @ T @ T) / 16
         Y, Z = Y @ M, M @ Z
     return Y, Z
 
 
-@pytest.mark.parametrize("d", [1, 2])
+@pytest.mark.parametrize("d", [1, 2, 3])
 def test_taylor_interval_is_classical_newton_schulz(d):
     A, _, _ = W.spd_logu(16, 3, 1e-2, 1.0)
     A = A.astype(np.float64)
@@ -64,7 +66,7 @@ def test_taylor_interval_is_classical_newton_schulz(d):
     np.testing.assert_allclose(Y2, Yt, atol=1e-13)
 
 
-@pytest.mark.parametrize("d", [1, 2])
+@pytest.mark.parametrize("d", [1, 2, 3])
 def test_exact_objective_equals_explicit_next_residual(d):
     # with S = I, fit_alpha minimises ||I - Z_{k+1} Y_{k+1}||_F^2 computed by
     # actually performing the update for every alpha on a grid
@@ -92,7 +94,7 @@ def test_exact_objective_equals_explicit_next_residual(d):
         Y, Z = Y @ g, g @ Z
 
 
-@pytest.mark.parametrize("d", [1, 2])
+@pytest.mark.parametrize("d", [1, 2, 3])
 def test_sketched_alpha_brute_force_grid(d):
     A, _, _ = W.spd_logu(40, 8, 1e-3, 1.0)
     A = A.astype(np.float64)
@@ -116,7 +118,7 @@ def test_sketched_alpha_brute_force_grid(d):
 
 def test_alpha_stays_in_interval_and_degenerate_cases():
     rng = np.random.default_rng(5)
-    for d in (1, 2):
+    for d in (1, 2, 3):
         lo, hi = prism.default_interval(d)
         for _ in range(200):
             B = rng.standard_normal((2 * d + 2, 2 * d + 2)) * 10.0 ** rng.uniform(-8, 2)
@@ -150,7 +152,7 @@ def test_eigenbasis_route_gives_same_alpha():
             assert abs(a_mat - a_eig) < 1e-7
 
 
-@pytest.mark.parametrize("d", [1, 2])
+@pytest.mark.parametrize("d", [1, 2, 3])
 def test_eigen_model_iteration_counts_match_matrix_iteration(d):
     c = W.spd_64()
     Q, lam = c["Q"], c["lam"]
@@ -221,6 +223,34 @@ def test_interval_rule_reproduces_page_interval():
     assert 1.4715 < u2 < 1.4730
     assert prism.default_interval(2)[1] <= u2
     assert prism.default_interval(1) == (0.5, 1.0)
+
+
+def test_interval_rule_degree_three():
+    # d = 3 (the Taylor coefficient 5/16 and the same rule): about 2.4686
+    u3 = interval.upper_bound(3, iters=24, samples=60)
+    assert 2.4680 < u3 < 2.4692
+    lo, hi = prism.default_interval(3)
+    assert lo == prism.taylor_coeff(3) == 5 / 16
+    assert hi <= u3 and interval.admissible(hi, 3)
+    assert not interval.admissible(2.6, 3)
+
+
+@pytest.mark.parametrize("p", [2, 4])
+def test_degree_three_roots_and_polar_converge(p):
+    c = W.spd_64()
+    A = c["A"].astype(np.float64)
+    X, Xa, info = prism.inv_root(A, p=p, d=3, sketch_fn=prism.make_sketch_fn(3), tol=1e-9)
+    Xr, Xar = cf.inv_root(A, p)
+    assert info["status"] == prism.CONVERGED
+    assert cf.rel_fro(X, Xr) < 1e-9 and cf.rel_fro(Xa, Xar) < 1e-9
+    for st in info["stages"]:
+        assert st.gemms == em.products_sqrt_stage(st.iters, 3)
+    if p == 2:
+        G = W.gaussian(64, 32, 102).astype(np.float64)
+        U, pinfo = prism.polar(G, d=3, sketch_fn=prism.make_sketch_fn(3), tol=1e-10)
+        assert pinfo["status"] == prism.CONVERGED
+        assert cf.rel_fro(U, cf.polar(G)[0]) < 1e-9
+        assert pinfo["stages"][0].gemms == em.products_polar(pinfo["stages"][0].iters, 3)
 
 
 def test_status_codes():
