@@ -83,12 +83,15 @@ typedef enum {
  */
 typedef struct {
   int32_t struct_version; /* PMX_OPTS_VERSION (2), or 1 for the 40-byte layout */
-  int32_t degree;         /* d in {1, 2}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2 */
+  int32_t degree;         /* d in {1, 2, 3}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2;
+                             d = 3 runs on the fp32 paths only (the bf16 polar
+                             factor and fp64_iters > 0 return NOT_SUPPORTED) */
   int32_t sketch_p;       /* Gaussian sketch width p, 1..PMX_MAX_SKETCH; default 8 */
   int32_t max_iter;       /* updates per stage, 1..1000; default 30 */
   int32_t accelerate;     /* 1: fitted alpha (PRISM); 0: alpha = Taylor c_d; default 1 */
   float alpha_lo;         /* alpha interval; NaN selects the default:       */
-  float alpha_hi;         /*   d = 1: [1/2, 1], d = 2: [3/8, 1.47]          */
+  float alpha_hi;         /*   d = 1: [1/2, 1], d = 2: [3/8, 1.47],         */
+                          /*   d = 3: [5/16, 2.46]                          */
   float tol;              /* stop when ||R_k||_F / sqrt(n) <= tol; default 1e-6 */
   uint64_t seed;          /* key of the Philox4x32-10 sketch stream; default 0 */
   int32_t fp64_iters;     /* inverse roots: the first fp64_iters updates of each
@@ -230,14 +233,14 @@ pmx_status pmx_precond_apply_batched(pmx_handle handle, const float* Linv, int l
  * kernel symbol family of the library.
  */
 typedef enum {
-  PMX_KC_GEMM_POWER = 0,   /* R^2 = R R */
-  PMX_KC_GEMM_UPDATE = 1,  /* Y g and g Z (one launch), X g; g formed in the operand load */
+  PMX_KC_GEMM_POWER = 0,   /* R^2 = R R (and R^3 = R^2 R for d = 3) */
+  PMX_KC_GEMM_UPDATE = 1,  /* Y g and g Z (one launch), X g */
   PMX_KC_GEMM_RESID = 2,   /* I - Z Y, I - X^T X, Frobenius norm, convergence decision */
   PMX_KC_GEMM_STATS = 3,   /* G G^T, G^T G with the EMA epilogue */
   PMX_KC_GEMM_APPLY = 4,   /* L^{-1/4} G, then (L^{-1/4} G) R^{-1/4} */
   PMX_KC_SKINNY = 5,       /* Krylov passes R^j S */
   PMX_KC_SKINNY_ALPHA = 6, /* last Krylov pass with the Gram and the alpha solve */
-  PMX_KC_OTHER = 7,        /* control reset, scaling, stage set-up, first g, outputs */
+  PMX_KC_OTHER = 7,        /* control reset, scaling, stage set-up, g, outputs */
   PMX_KC_COUNT = 8
 } pmx_kernel_class;
 

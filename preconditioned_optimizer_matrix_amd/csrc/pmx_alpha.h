@@ -171,7 +171,9 @@ __device__ inline double alpha_from_gram_t(const double* G, double s, const Alph
 
 __device__ inline double alpha_from_gram(const double* G, int J, double s, const AlphaCoef& co,
                                          double lo, double hi) {
-  return J == 3 ? alpha_from_gram_t<3>(G, s, co, lo, hi) : alpha_from_gram_t<5>(G, s, co, lo, hi);
+  if (J == 3) return alpha_from_gram_t<3>(G, s, co, lo, hi);
+  if (J == 5) return alpha_from_gram_t<5>(G, s, co, lo, hi);
+  return alpha_from_gram_t<7>(G, s, co, lo, hi);
 }
 
 }  // namespace pmx

@@ -166,7 +166,7 @@ AlphaCoef make_coef(int d) {
   Poly A2 = pmul(om, x2d);
   for (int i = 0; i < 8; ++i) A2.c[i] = -A2.c[i];
   AlphaCoef co;
-  for (int j = 0; j < 6; ++j) {
+  for (int j = 0; j < 8; ++j) {
     co.a[0][j] = A0.c[j];
     co.a[1][j] = A1.c[j];
     co.a[2][j] = A2.c[j];
@@ -191,14 +191,17 @@ bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out) {
     }
   }
   if (o.fp64_iters < 0 || o.fp64_iters > o.max_iter || o.reserved != 0) return false;
-  if (o.degree != 1 && o.degree != 2) return false;
+  if (o.degree < 1 || o.degree > 3) return false;
   if (o.sketch_p < 1 || o.sketch_p > PMX_MAX_SKETCH) return false;
   if (o.max_iter < 1 || o.max_iter > kMaxIter) return false;
   if (o.accelerate != 0 && o.accelerate != 1) return false;
   if (isnan(o.alpha_lo) != isnan(o.alpha_hi)) return false;
   if (isnan(o.alpha_lo)) {
-    o.alpha_lo = o.degree == 1 ? 0.5f : 0.375f;
-    o.alpha_hi = o.degree == 1 ? 1.0f : 1.47f;
+    // lo = c_d; hi = the interval rule's bound rounded down (1, 1.4722, 2.4686)
+    static const float lo_d[4] = {0.f, 0.5f, 0.375f, 0.3125f};
+    static const float hi_d[4] = {0.f, 1.0f, 1.47f, 2.46f};
+    o.alpha_lo = lo_d[o.degree];
+    o.alpha_hi = hi_d[o.degree];
   }
   if (!isfinite(o.alpha_lo) || !isfinite(o.alpha_hi) || o.alpha_lo > o.alpha_hi) return false;
   if (!isfinite(o.tol) || o.tol < 0.f) return false;
@@ -240,7 +243,7 @@ IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, i
   L.pstride = std::max<int64_t>(kPartialsPerMatrix, gemm_f32_tiles(cols, cols));
   L.partials = off;
   off = align_up(off + sizeof(double) * (size_t)L.pstride * batch);
-  L.gstride = (int64_t)16 * (skinny_blocks(cols, 1) + 1);
+  L.gstride = (int64_t)kGramShare * (skinny_blocks(cols, 1) + 1);
   L.gram = off;
   off = align_up(off + sizeof(double) * (size_t)L.gstride * batch);
   const int64_t big = (int64_t)rows * cols, small = (int64_t)cols * cols;
@@ -349,16 +352,18 @@ SketchJob make_sketch(const IterLayout& L, void* ws, const IterCfg& cfg, int n, 
 // already in the Krylov buffer (generated by the kernel that produced R_k).
 //   d = 2: K1 = R S / s, K2 = R^2 S / s^2; [K3 | K4] = R^2 [K1 | K2] / s^2;
 //          K5 = R^2 K3 / s^2 (+ Gram, alpha)
+//   d = 3: as d = 2, then [K5 | K6] = R^2 [K3 | K4] / s^2 and
+//          K7 = R^2 K5 / s^2 (+ Gram, alpha); R^3 = R^2 R is formed for g
 //   d = 1: K_j = R K_{j-1} / s, j = 1..3 (+ Gram, alpha on the last pass)
 hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
                                    const pmx_matfn_opts& o, const IterCfg& cfg,
                                    const AlphaCoef& coef, int n, int batch, float* R,
-                                   float* R2, bool power = true) {
+                                   float* R2, float* R3, bool power = true) {
   Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
   float* kbuf = at<float>(ws, L.kbuf);
   const int d = o.degree, pp = o.sketch_p;
   hipError_t e;
-  if (d == 2 && power) {
+  if (d >= 2 && power) {
     GemmParams g = gemm_base(q.h, n, n, n, batch);
     g.prob[0].a = {R, n, L.buf_stride, nullptr, 0};
     g.prob[0].b = {R, n, L.buf_stride, nullptr, 0};
@@ -371,6 +376,14 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     set_vec(g);
     e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
     if (e != hipSuccess) return e;
+    if (d == 3) {
+      // R^3 = R^2 R: symmetric by structure, so its upper triangle is kept and
+      // mirrored and g stays exactly symmetric
+      g.prob[0].a = {R2, n, L.buf_stride, nullptr, 0};
+      g.prob[0].c = R3;
+      e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
+      if (e != hipSuccess) return e;
+    }
   }
   if (!o.accelerate) return hipSuccess;
   SkinnyParams kp;
@@ -399,7 +412,7 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     return q.run(gram ? PMX_KC_SKINNY_ALPHA : PMX_KC_SKINNY,
                  [&] { return launch_skinny(kp, njobs, gram, batch, q.s); });
   };
-  if (d == 2) {
+  if (d >= 2) {
     kp.q = pp;
     kp.job[0] = job(R, 0, pp, 1);
     kp.job[1] = job(R2, 0, 2 * pp, 2);
@@ -407,8 +420,12 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     kp.q = 2 * pp;
     kp.job[0] = job(R2, pp, 3 * pp, 2);
     if ((e = pass(1, false)) != hipSuccess) return e;
+    if (d == 3) {
+      kp.job[0] = job(R2, 3 * pp, 5 * pp, 2);
+      if ((e = pass(1, false)) != hipSuccess) return e;
+    }
     kp.q = pp;
-    kp.job[0] = job(R2, 3 * pp, 5 * pp, 2);
+    kp.job[0] = job(R2, (2 * d - 1) * pp, (2 * d + 1) * pp, 2);
     return pass(1, true);
   }
   kp.q = pp;
@@ -536,15 +553,19 @@ pmx_status pmx_trace_collect(pmx_handle h, double* ms, int64_t* launches) {
 // fp32: Y and Z ping-pong, R, R^2; with fp64 leading updates also their fp64
 // counterparts (Y, Z ping-pong, R, R^2).
 static int inv_root_f64_bufs(const pmx_matfn_opts& o) { return o.fp64_iters > 0 ? 6 : 0; }
+// n x n residual buffers: R, R^2 (g is written over R^2), and R^3 for d = 3.
+static int small_bufs(const pmx_matfn_opts& o) { return o.degree == 3 ? 3 : 2; }
 static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
-  return iter_layout(n, n, batch, o, 4, 2, sizeof(float), inv_root_f64_bufs(o)).total;
+  return iter_layout(n, n, batch, o, 4, small_bufs(o), sizeof(float), inv_root_f64_bufs(o)).total;
 }
-// fp32: X ping-pong, R, R^2.  bf16: X and X^T ping-pong, R, R^2 (fp32), and
-// the bf16 operands R and g.
-static int polar_bufs(pmx_dtype dt) { return dt == PMX_BF16 ? 8 : 4; }
+// fp32: X ping-pong, R, R^2 (and R^3 for d = 3).  bf16: X and X^T
+// ping-pong, R, R^2 (fp32), and the bf16 operands R and g.
+static int polar_bufs(pmx_dtype dt, const pmx_matfn_opts& o) {
+  return dt == PMX_BF16 ? 8 : (o.degree == 3 ? 5 : 4);
+}
 static size_t polar_ws(int m, int n, int batch, const pmx_matfn_opts& o, pmx_dtype dt) {
   const int rows = std::max(m, n), cols = std::min(m, n);
-  return iter_layout(rows, cols, batch, o, polar_bufs(dt), 0, sizeof(float)).total;
+  return iter_layout(rows, cols, batch, o, polar_bufs(dt, o), 0, sizeof(float)).total;
 }
 static size_t apply_ws(int m, int n, int batch, pmx_dtype dt) {
   // fp32: T = L^{-1/4} G; bf16: G in fp32, T and P in fp32
@@ -685,7 +706,10 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
     return PMX_ERR_INVALID_VALUE;
   if (!batch_layout_ok(n, n, ldx, sx, batch)) return PMX_ERR_INVALID_VALUE;
   if (XA && !batch_layout_ok(n, n, ldaux, saux, batch)) return PMX_ERR_INVALID_VALUE;
-  const IterLayout Lw = iter_layout(n, n, batch, o, 4, 2, sizeof(float), inv_root_f64_bufs(o));
+  // d = 3 runs the fp32 updates only
+  if (o.degree == 3 && o.fp64_iters > 0) return PMX_ERR_NOT_SUPPORTED;
+  const IterLayout Lw =
+      iter_layout(n, n, batch, o, 4, small_bufs(o), sizeof(float), inv_root_f64_bufs(o));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
   const Extent ea = extent_of(A, n, n, lda, sa, batch, 4);
@@ -710,13 +734,14 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   float* Zb[2] = {at<float>(ws, Lw.bufs[2]), at<float>(ws, Lw.bufs[3])};
   float* Rb = at<float>(ws, Lw.bufs[4]);
   float* R2b = at<float>(ws, Lw.bufs[5]);
+  float* R3b = o.degree == 3 ? at<float>(ws, Lw.bufs[6]) : nullptr;
   const IterCfg cfg = make_cfg(o, n, info);
   const AlphaCoef coef = make_coef(o.degree);
   const int d = o.degree;
   const bool acc = o.accelerate != 0;
 
   const int stages = (p == 4) ? 2 : 1;
-  if (n <= kSmallMaxN && h->small_fused && o.fp64_iters == 0) {
+  if (n <= kSmallMaxN && h->small_fused && o.fp64_iters == 0 && o.degree <= 2) {
     SmallRootParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.a = A;
@@ -798,7 +823,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
           g.prob[0].c32 = R2b;
           PMX_TRY(q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f64(g, ROLE_POWER, q.s); }));
         }
-        PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b, false));
+        PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b, nullptr, false));
         const int cur = k & 1, nxt = cur ^ 1;
         Gemm64Params u = gemm64(k == 0 ? 1 : 2);
         if (k == 0) {
@@ -874,7 +899,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_sqrt_stage_init(ip, batch, q.s); }));
     }
     for (int k = k64; k < o.max_iter; ++k) {
-      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b));
+      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b, R3b));
       const int cur = k & 1, nxt = cur ^ 1;
       GemmParams u = gemm_base(q.h, n, n, n, batch);
       u.ctrl = ctrl;
@@ -889,7 +914,9 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         FormGParams fp;
         memset(&fp, 0, sizeof(fp));
         fp.r = Rb;
-        fp.r2 = (d == 2) ? R2b : nullptr;
+        fp.r2 = (d >= 2) ? R2b : nullptr;
+        fp.r3 = R3b;
+        fp.c2 = (float)taylor(2);
         fp.dst = Zb[1];
         fp.stride = Lw.buf_stride;
         fp.n = n;
@@ -910,7 +937,9 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         FormGParams fp;
         memset(&fp, 0, sizeof(fp));
         fp.r = Rb;
-        fp.r2 = (d == 2) ? R2b : nullptr;
+        fp.r2 = (d >= 2) ? R2b : nullptr;
+        fp.r3 = R3b;
+        fp.c2 = (float)taylor(2);
         fp.dst = R2b;
         fp.stride = Lw.buf_stride;
         fp.n = n;
@@ -1003,7 +1032,8 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const bool bf = dtype == PMX_BF16;
   const int rows = std::max(m, n), cols = std::min(m, n);
   const bool tr = m < n;
-  const IterLayout Lw = iter_layout(rows, cols, batch, o, polar_bufs(dtype), 0, sizeof(float));
+  if (bf && o.degree == 3) return PMX_ERR_NOT_SUPPORTED;  // d = 3: fp32 only
+  const IterLayout Lw = iter_layout(rows, cols, batch, o, polar_bufs(dtype, o), 0, sizeof(float));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
   const Extent eg = extent_of(G, m, n, ldg, sg, batch, bf ? 2 : 4);
@@ -1025,13 +1055,14 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   float* Xb[2] = {at<float>(ws, Lw.bufs[0]), at<float>(ws, Lw.bufs[1])};
   float* Rb = at<float>(ws, Lw.bufs[2]);
   float* R2b = at<float>(ws, Lw.bufs[3]);
+  float* R3b = (!bf && o.degree == 3) ? at<float>(ws, Lw.bufs[4]) : nullptr;
   const IterCfg cfg = make_cfg(o, cols, info);
   const AlphaCoef coef = make_coef(o.degree);
   const int d = o.degree;
   const bool acc = o.accelerate != 0;
   const int64_t bs = Lw.buf_stride;
 
-  if (!bf && rows <= kSmallMaxN && h->small_fused) {
+  if (!bf && rows <= kSmallMaxN && h->small_fused && o.degree <= 2) {
     SmallPolarParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.g = (const float*)G;
@@ -1089,7 +1120,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     };
     PMX_TRY(residual(Xb[0], 1, 0));
     for (int k = 0; k < o.max_iter; ++k) {
-      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b));
+      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, R3b));
       const int cur = k & 1, nxt = cur ^ 1;
       GemmParams u = gemm_base(q.h, rows, cols, cols, batch);
       u.ctrl = ctrl;
@@ -1104,7 +1135,9 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
         FormGParams fp;
         memset(&fp, 0, sizeof(fp));
         fp.r = Rb;
-        fp.r2 = (d == 2) ? R2b : nullptr;
+        fp.r2 = (d >= 2) ? R2b : nullptr;
+        fp.r3 = R3b;
+        fp.c2 = (float)taylor(2);
         fp.dst = R2b;
         fp.stride = bs;
         fp.n = cols;
@@ -1186,7 +1219,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
         g.vec = vec ? 1 : 0;
         PMX_TRY(q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_bf16(g, ROLE_POWER, q.s); }));
       }
-      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, false));
+      PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, nullptr, false));
       FormGParams fg;
       memset(&fg, 0, sizeof(fg));
       fg.r = Rb;

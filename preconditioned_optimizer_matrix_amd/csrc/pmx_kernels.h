@@ -8,6 +8,8 @@ namespace pmx {
 // Partial-sum slots reserved per matrix for the elementwise reductions and
 // for the residual GEMM (one slot per output tile).
 constexpr int kPartialsPerMatrix = 1024;
+// Gram share slots per skinny block (J (J + 1) / 2 <= 28 entries, J <= 7).
+constexpr int kGramShare = 32;
 
 // bf16 storage type: raw bits, converted explicitly (round to nearest even).
 struct bf16_t {
@@ -65,7 +67,7 @@ struct SkinnyJob {
 
 // Coefficient vectors of r(xi; alpha) = sum_j (a0_j + alpha a1_j + alpha^2 a2_j) xi^j.
 struct AlphaCoef {
-  double a[3][6];
+  double a[3][8];  // coefficients of xi^0 .. xi^{2d+1}, d <= 3
   double taylor_d;
 };
 
@@ -85,13 +87,14 @@ struct SkinnyParams {
 
 struct FormGParams {
   const float* r;
-  const float* r2;       // R^2 (d = 2), may alias dst
+  const float* r2;       // R^2 (d >= 2), may alias dst
+  const float* r3;       // R^3 (d = 3), may alias dst
   void* dst;             // fp32, or bf16 with dst_bf16
   int64_t stride;        // elements, shared by r, r2 and dst
   int n, degree;
   int dst_bf16;
   int vec;               // set by the launcher
-  float c0, c1;
+  float c0, c1, c2;      // Taylor coefficients c_0 .. c_{d-1} (c2 for d = 3)
   Ctrl* ctrl;
   SketchJob sketch;      // the next iteration's sketch, generated on the side
 };

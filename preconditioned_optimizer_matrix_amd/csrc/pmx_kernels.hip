@@ -217,15 +217,15 @@ __device__ __forceinline__ void halve_reduce(float* acc, int lane) {
 // reads) and shared by the block's rows.  Each lane accumulates RW x Q
 // partial sums over its columns; the wave's recursive-halving reduction leaves
 // the complete sums spread over the lanes.
-// GRAM (last Krylov pass): every block also adds its rows' share of the
+// GJ > 0 (last Krylov pass, J <= GJ Krylov blocks): every block also adds its rows' share of the
 // J x J Gram of K_1..K_J in fp64; the last block to arrive reduces the
 // shares in block order and solves for alpha.
 constexpr int SK_CH = 512;           // In rows per LDS chunk
 constexpr int SK_LD = SK_CH + 4;     // column stride of the staged chunk
 
-// Reduction, output and (GRAM) Gram share / alpha fit of a skinny product:
+// Reduction, output and (GJ > 0) Gram share / alpha fit of a skinny product:
 // acc holds the lane's RW x Q partial sums for rows row0 .. row0 + RW - 1.
-template <int Q, int RW, bool GRAM>
+template <int Q, int RW, int GJ>
 __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const SkinnyParams& p,
                                               const SkinnyJob& job, int b, int row0,
                                               float scale, double fro) {
@@ -251,39 +251,42 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     if (valid[i]) kb[(int64_t)vrow[i] * p.kld + job.out_col + c] = acc[i];
   }
 
-  if constexpr (GRAM) {
-    // the block's share of the Gram entries (a, bb), a <= bb < J <= 5
+  if constexpr (GJ > 0) {
+    // the block's share of the Gram entries (a, bb), a <= bb < J <= GJ
+    constexpr int NE = GJ * (GJ + 1) / 2;
     const int J = 2 * p.cfg.degree + 1;
     const int pp = p.cfg.p;
-    double g[15];
+    double g[NE];
 #pragma unroll
-    for (int e = 0; e < 15; ++e) g[e] = 0.0;
+    for (int e = 0; e < NE; ++e) g[e] = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+      double v[GJ];
+#pragma unroll
+      for (int j = 0; j < GJ; ++j) v[j] = 0.0;
       if (valid[i]) {
 #pragma unroll
-        for (int j = 1; j < 5; ++j)
+        for (int j = 1; j < GJ; ++j)
           if (j < J) v[j - 1] = (double)kb[(int64_t)vrow[i] * p.kld + j * pp + vcol[i]];
 #pragma unroll
-        for (int j = 0; j < 5; ++j)
+        for (int j = 0; j < GJ; ++j)
           if (j == J - 1) v[j] = (double)acc[i];
       }
       int t = 0;
 #pragma unroll
-      for (int a = 0; a < 5; ++a)
+      for (int a = 0; a < GJ; ++a)
 #pragma unroll
-        for (int bb = a; bb < 5; ++bb, ++t) g[t] += v[a] * v[bb];
+        for (int bb = a; bb < GJ; ++bb, ++t) g[t] += v[a] * v[bb];
     }
     // entries of (a, bb) with a <= bb < J, in row order, are packed first
-    __shared__ double wsum[4][15];
-    __shared__ double gsum[15];
+    __shared__ double wsum[4][NE];
+    __shared__ double gsum[NE];
     {
       int t = 0, o = 0;
 #pragma unroll
-      for (int a = 0; a < 5; ++a)
+      for (int a = 0; a < GJ; ++a)
 #pragma unroll
-        for (int bb = a; bb < 5; ++bb, ++t) {
+        for (int bb = a; bb < GJ; ++bb, ++t) {
           const double sv = wave_sum(g[t]);
           if (a < J && bb < J) {
             if (lane == 0) wsum[wid][o] = sv;
@@ -296,7 +299,7 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     __shared__ int is_last;
     double* part = p.gram_partials + (int64_t)b * p.gram_stride;
     if (threadIdx.x < ng)
-      part[(int64_t)blockIdx.x * 16 + threadIdx.x] =
+      part[(int64_t)blockIdx.x * kGramShare + threadIdx.x] =
           ((wsum[0][threadIdx.x] + wsum[1][threadIdx.x]) + wsum[2][threadIdx.x]) +
           wsum[3][threadIdx.x];
     __syncthreads();
@@ -313,7 +316,7 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     for (int e = wid; e < ng; e += NT / 64) {
       double sv = 0.0;
       for (int i = lane; i < (int)gridDim.x; i += 64)
-        sv += __hip_atomic_load(&part[(int64_t)i * 16 + e], __ATOMIC_RELAXED,
+        sv += __hip_atomic_load(&part[(int64_t)i * kGramShare + e], __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
       sv = wave_sum(sv);
       if (lane == 0) gsum[e] = sv;
@@ -330,7 +333,7 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
   }
 }
 
-template <int Q, int RW, bool GRAM>
+template <int Q, int RW, int GJ>
 __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   constexpr int CNT = RW * Q;  // partial sums per lane
   constexpr int RB = 4 * RW;
@@ -411,14 +414,14 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
       }
     }
   }
-  skinny_finish<Q, RW, GRAM>(acc, p, job, b, row0, scale, fro);
+  skinny_finish<Q, RW, GJ>(acc, p, job, b, row0, scale, fro);
 }
 
 // The same product software-pipelined: while chunk c (CH rows of In, CH
 // columns of Mat) is multiplied, the Mat loads and the In staging loads of
 // chunk c + 1 are in flight; In is double buffered in LDS, so there is one
 // barrier per chunk.
-template <int Q, int RW, int CH, bool GRAM>
+template <int Q, int RW, int CH, int GJ>
 __global__ __launch_bounds__(NT) void skinny_pipe_kernel(SkinnyParams p) {
   constexpr int CNT = RW * Q;
   constexpr int RB = 4 * RW;
@@ -535,13 +538,13 @@ __global__ __launch_bounds__(NT) void skinny_pipe_kernel(SkinnyParams p) {
         for (int rr = 0; rr < RW; ++rr) m[t][rr] = mn[t][rr];
     }
   }
-  skinny_finish<Q, RW, GRAM>(acc, p, job, b, row0, scale, fro);
+  skinny_finish<Q, RW, GJ>(acc, p, job, b, row0, scale, fro);
 }
 
 // The same product without LDS: each lane reads the In rows of its four
 // columns directly (16-byte loads, L1/L2 resident: In is n x q) next to the
 // RW rows of Mat, so a block has no barriers and keeps its loads in flight.
-template <int Q, int RW, bool GRAM>
+template <int Q, int RW, int GJ>
 __global__ __launch_bounds__(NT) void skinny_stream_kernel(SkinnyParams p) {
   constexpr int CNT = RW * Q;
   constexpr int RB = 4 * RW;
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(NT) void skinny_stream_kernel(SkinnyParams p) {
       }
     }
   }
-  skinny_finish<Q, RW, GRAM>(acc, p, job, b, row0, scale, fro);
+  skinny_finish<Q, RW, GJ>(acc, p, job, b, row0, scale, fro);
 }
 
 // ---------------------------------------------------------------- polynomial
@@ -621,8 +624,9 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   const float* R2 = p.r2 ? p.r2 + (int64_t)b * p.stride : nullptr;
   float* G = p.dst_bf16 ? nullptr : reinterpret_cast<float*>(p.dst) + (int64_t)b * p.stride;
   uint16_t* Gh = p.dst_bf16 ? reinterpret_cast<uint16_t*>(p.dst) + (int64_t)b * p.stride : nullptr;
-  const float c0 = p.c0, c1 = p.c1;
-  const bool d1 = p.degree == 1;
+  const float* R3 = p.r3 ? p.r3 + (int64_t)b * p.stride : nullptr;
+  const float c0 = p.c0, c1 = p.c1, c2 = p.c2;
+  const bool d1 = p.degree == 1, d3 = p.degree == 3;
   if (p.vec) {
     // four columns per thread (n % 4 == 0, stride % 4 == 0)
     const int nv = n / 4;
@@ -633,6 +637,11 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
       float4 v;
       if (d1) {
         v = make_float4(alpha * x.x, alpha * x.y, alpha * x.z, alpha * x.w);
+      } else if (d3) {
+        const float4 y = *reinterpret_cast<const float4*>(R2 + e);
+        const float4 z = *reinterpret_cast<const float4*>(R3 + e);
+        v = make_float4(c1 * x.x + c2 * y.x + alpha * z.x, c1 * x.y + c2 * y.y + alpha * z.y,
+                        c1 * x.z + c2 * y.z + alpha * z.z, c1 * x.w + c2 * y.w + alpha * z.w);
       } else {
         const float4 y = *reinterpret_cast<const float4*>(R2 + e);
         v = make_float4(c1 * x.x + alpha * y.x, c1 * x.y + alpha * y.y, c1 * x.z + alpha * y.z,
@@ -658,6 +667,7 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
     const int64_t e = (int64_t)r * n + c;
     float v;
     if (d1) v = alpha * R[e];
+    else if (d3) v = c1 * R[e] + c2 * R2[e] + alpha * R3[e];
     else v = c1 * R[e] + alpha * R2[e];
     if (r == c) v += c0;
     if (Gh) Gh[e] = from_f32<bf16_t>(v).bits;
@@ -841,26 +851,32 @@ int skinny_blocks(int n, int q) {
   return (n + 7) / 8;
 }
 
-template <int Q, int RW>
-static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
+template <int Q, int RW, int GJ>
+static void skinny_go_j(const SkinnyParams& p, int njobs, int batch, hipStream_t s) {
   dim3 grid((p.n + 4 * RW - 1) / (4 * RW), njobs, batch);
   if (p.variant == 1) {
-    if (gram) hipLaunchKernelGGL((skinny_stream_kernel<Q, RW, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((skinny_stream_kernel<Q, RW, false>), grid, dim3(NT), 0, s, p);
-    return;
-  }
-  if (p.variant == 2) {
+    hipLaunchKernelGGL((skinny_stream_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
+  } else if (p.variant == 2) {
     constexpr int CH = (RW <= 2 && Q <= 8) ? 512 : 256;
-    if (gram) hipLaunchKernelGGL((skinny_pipe_kernel<Q, RW, CH, true>), grid, dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((skinny_pipe_kernel<Q, RW, CH, false>), grid, dim3(NT), 0, s, p);
-    return;
+    hipLaunchKernelGGL((skinny_pipe_kernel<Q, RW, CH, GJ>), grid, dim3(NT), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((skinny_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
   }
-  if (gram) hipLaunchKernelGGL((skinny_kernel<Q, RW, true>), grid, dim3(NT), 0, s, p);
-  else hipLaunchKernelGGL((skinny_kernel<Q, RW, false>), grid, dim3(NT), 0, s, p);
+}
+
+// Gram variants: J = 2d + 1 Krylov blocks, at most 5 (d <= 2) or 7 (d = 3);
+// the Gram pass is always a single q = p job (p <= PMX_MAX_SKETCH = 16).
+template <int Q, int RW>
+static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
+  if (!gram) skinny_go_j<Q, RW, 0>(p, njobs, batch, s);
+  else if constexpr (Q <= 16) {
+    if (p.cfg.degree == 3) skinny_go_j<Q, RW, 7>(p, njobs, batch, s);
+    else skinny_go_j<Q, RW, 5>(p, njobs, batch, s);
+  }
 }
 
 hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
-  if (gram && njobs != 1) return hipErrorInvalidValue;
+  if (gram && (njobs != 1 || p.q > 16)) return hipErrorInvalidValue;
   // more rows per wave once that still leaves two blocks per compute unit
   const bool wide = (int64_t)((p.n + 31) / 32) * njobs * batch >= 512;
   if (p.q <= 8) {
@@ -880,8 +896,10 @@ hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch,
 
 hipError_t launch_form_g(const FormGParams& pin, int batch, hipStream_t s) {
   FormGParams p = pin;
+  if (p.degree == 3 && (!p.r2 || !p.r3)) return hipErrorInvalidValue;
   p.vec = (p.n % 4 == 0) && (p.stride % 4 == 0) && ((uintptr_t)p.r % 16 == 0) &&
-          (!p.r2 || (uintptr_t)p.r2 % 16 == 0) && ((uintptr_t)p.dst % 16 == 0);
+          (!p.r2 || (uintptr_t)p.r2 % 16 == 0) && (!p.r3 || (uintptr_t)p.r3 % 16 == 0) &&
+          ((uintptr_t)p.dst % 16 == 0);
   const int per = (4096 + batch - 1) / batch;
   dim3 grid(grid_rows(p.n, per < 2048 ? per : 2048), batch);
   hipLaunchKernelGGL(form_g_kernel, grid, dim3(NT), 0, s, p);

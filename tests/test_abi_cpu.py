@@ -75,7 +75,13 @@ def test_workspace_sizes_and_option_validation():
                                           ctypes.byref(oo), ctypes.byref(sz))
 
     assert ws() == pmx.OK
-    assert ws(degree=3) == pmx.ERR_INVALID_VALUE
+    assert ws(degree=3) == pmx.OK
+    assert ws(degree=4) == pmx.ERR_INVALID_VALUE
+    assert ws(degree=0) == pmx.ERR_INVALID_VALUE
+    # d = 3 adds the n x n buffer of R^3
+    b2 = pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 1, pmx.F32, pmx.default_opts())
+    b3 = pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 1, pmx.F32, pmx.default_opts(degree=3))
+    assert b3 - b2 >= 4 * 512 * 512
     assert ws(sketch_p=0) == pmx.ERR_INVALID_VALUE
     assert ws(sketch_p=pmx.MAX_SKETCH + 1) == pmx.ERR_INVALID_VALUE
     assert ws(max_iter=0) == pmx.ERR_INVALID_VALUE

@@ -106,7 +106,7 @@ def test_inv_root_iterations_and_alpha_follow_reference(env, p):
     assert abs(int(inf["gemms"]) - total_ref) <= 4 * len(ref["stages"])
 
 
-@pytest.mark.parametrize("d", [1, 2])
+@pytest.mark.parametrize("d", [1, 2, 3])
 def test_taylor_and_degree_variants(env, d):
     _, pmx, _ = env
     A, _, _ = W.spd_logu(80, 3, 1e-2, 1.0)
@@ -119,6 +119,56 @@ def test_taylor_and_degree_variants(env, d):
         _, _, r = prism.inv_root(A.astype(np.float64), p=2, d=d, accelerate=bool(acc),
                                  sketch_fn=prism.make_sketch_fn(0))
         assert abs(int(info[0]["iters"][0]) - r["stages"][0].iters) <= 1
+
+
+@pytest.mark.parametrize("p", [2, 4])
+def test_degree_three(env, p):
+    # d = 3: g = 1 + R/2 + 3R^2/8 + alpha R^3 with alpha in [5/16, 2.46]; R^3 is a
+    # fourth (symmetric) product per update and the alpha fit uses K_1..K_7
+    torch, pmx, dev = env
+    for n in (64, 100, 256, 517):
+        _say("degree 3 root", p, n)
+        A, _, _ = W.spd_logu(n, 3000 + n)
+        X, XA, info = _run_root(env, A, p, degree=3, seed=4)
+        ref, ref_aux = cf.inv_root(A, p)
+        assert int(info[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), n
+        assert cf.rel_fro(X, ref) < 1e-4 and cf.rel_fro(XA, ref_aux) < 1e-4, n
+    # alpha traces and iteration counts against the oracle with the same sketches
+    A, _, _ = W.spd_logu(96, 77)
+    _say("degree 3 alpha trace", p)
+    X, XA, info = _run_root(env, A, p, degree=3, seed=5)
+    _, _, ref = prism.inv_root(A.astype(np.float64), p=p, d=3,
+                               sketch_fn=prism.make_sketch_fn(5, b=0, p=8))
+    inf = info[0]
+    for s, st in enumerate(ref["stages"]):
+        it = int(inf["iters"][s])
+        assert abs(it - st.iters) <= 1, (s, it, st.iters)
+        for k in range(min(it, st.iters)):
+            if st.r[k] >= 1e-3:
+                assert abs(inf["alpha"][s][k] - st.alpha[k]) < 1e-3, (s, k)
+                assert inf["rtrace"][s][k] == pytest.approx(st.r[k], rel=1e-3)
+    # batched, mixed conditioning
+    As = np.stack([W.spd_logu(200, 40 + b, 10.0 ** -(b + 1), 1.0)[0] for b in range(3)])
+    Xb, _, infb = pmx.inv_root(torch.from_numpy(As).to(dev), p, opts=pmx.default_opts(degree=3))
+    torch.cuda.synchronize()
+    for b in range(3):
+        assert cf.rel_fro(Xb[b].cpu().numpy(), cf.inv_root(As[b], p)[0]) < 1e-4, b
+    if p == 2:
+        # fp32 polar factor with d = 3
+        for m, n in ((64, 32), (150, 150), (300, 17)):
+            _say("degree 3 polar", m, n)
+            G = W.gaussian(m, n, m + 7 * n)
+            U, pinfo = pmx.polar(torch.from_numpy(G).to(dev), opts=pmx.default_opts(degree=3))
+            torch.cuda.synchronize()
+            assert int(pmx.parse_info(pinfo)[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+            assert cf.rel_fro(U.cpu().numpy(), cf.polar(G)[0]) < 1e-4
+        # d = 3 is an fp32 path: the bf16 polar and the fp64 leading updates refuse it
+        Gb = _bf16(torch, W.gaussian(64, 32, 5)).to(dev)
+        with pytest.raises(pmx.PmxError):
+            pmx.polar(Gb, opts=pmx.default_opts(degree=3))
+        with pytest.raises(pmx.PmxError):
+            pmx.inv_root(torch.from_numpy(A).to(dev), 2, opts=pmx.default_opts(degree=3, fp64_iters=2))
+        torch.cuda.synchronize()
 
 
 def test_inv_root_batched(env):
