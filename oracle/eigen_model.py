@@ -38,13 +38,18 @@ def argmin_alpha(xi, w, d, lo, hi, npts=2001):
     return best
 
 
-def run(xi0, d, lo, hi, tol, max_iter, weights_fn=None, accelerate=True):
+def run(xi0, d, lo, hi, tol, max_iter, weights_fn=None, accelerate=True, degree_max=None,
+        adapt_ratio=0.3, intervals=None):
     """Iterate the scalar map on the residual spectrum xi0 (eigenvalues of R_0).
     weights_fn(k) returns the weights w_i for iteration k (None: exact, w = 1).
-    Returns dict(iters, status, r, alpha)."""
+    degree_max > d: after an update whose contraction of the weighted
+    residual, sqrt(sum w r(xi)^2 / sum w xi^2), exceeds adapt_ratio the degree
+    rises by one (intervals[d] gives the interval of each raised degree).
+    Returns dict(iters, status, r, alpha, degree)."""
     xi = np.asarray(xi0, np.float64).copy()
     n = xi.size
-    rs, alphas = [], []
+    rs, alphas, degrees = [], [], []
+    dmax = d if degree_max is None else degree_max
     k = 0
     while True:
         r = sqrt(float(np.sum(xi * xi)) / n)
@@ -61,15 +66,22 @@ def run(xi0, d, lo, hi, tol, max_iter, weights_fn=None, accelerate=True):
         if k >= max_iter:
             status = MAXITER
             break
+        w = np.ones(n) if weights_fn is None else weights_fn(k)
         if accelerate:
-            w = np.ones(n) if weights_fn is None else weights_fn(k)
             alpha = argmin_alpha(xi, w, d, lo, hi)
         else:
             alpha = taylor_coeff(d)
         alphas.append(alpha)
-        xi = residual_map(xi, alpha, d)
+        degrees.append(d)
+        nxt = residual_map(xi, alpha, d)
+        if accelerate and d < dmax:
+            q = sqrt(float(np.sum(w * nxt * nxt)) / float(np.sum(w * xi * xi)))
+            if q > adapt_ratio:
+                d += 1
+                lo, hi = intervals[d]
+        xi = nxt
         k += 1
-    return dict(iters=k, status=status, r=rs, alpha=alphas)
+    return dict(iters=k, status=status, r=rs, alpha=alphas, degree=degrees)
 
 
 def products_sqrt_stage(iters, d):

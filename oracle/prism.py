@@ -30,7 +30,13 @@ implements; every one is listed in the design notes):
     critical points inside); default [lo, hi] = [1/2, 1] for d = 1,
     [3/8, 1.47] for d = 2 and [5/16, 2.46] for d = 3 (see oracle.interval);
   * stopping: r_k = ||R_k||_F / sqrt(n) <= tol; stagnation when r_{k-1} < 1e-2
-    and r_k > 0.9 r_{k-1}; divergence when r_k > 2; max_iter updates at most.
+    and r_k > 0.9 r_{k-1}; divergence when r_k > 2; max_iter updates at most;
+  * adaptive degree ([PRISM summary], methodology step 3: the degree is raised
+    only when the sketched residual shows it is needed): a stage starts at
+    degree d; after alpha_k is fitted, the sketch predicts the contraction of
+    the update, q_k = sqrt(phi_S(alpha_k)) / ||R_k S||_F (phi_S(alpha_k) is the
+    sketched ||R_{k+1} S||_F^2); when q_k > adapt_ratio and d < degree_max the
+    following updates of the stage use d + 1.  The update k itself keeps d.
 """
 from math import comb, sqrt
 
@@ -156,13 +162,25 @@ def krylov_gram(R, S, d):
     return M
 
 
+def predicted_contraction(M, d, alpha):
+    """q = sqrt(phi_S(alpha)) / ||R S||_F from the Gram matrix of K_0..K_{2d+1}
+    (M[1, 1] = ||R S||_F^2): the sketch's estimate of ||R_{k+1}|| / ||R_k||."""
+    w = quartic(M, d)
+    phi = w[0] + alpha * (w[1] + alpha * (w[2] + alpha * (w[3] + alpha * w[4])))
+    m11 = float(M[1, 1])
+    return sqrt(max(phi, 0.0) / m11) if m11 > 0.0 else 0.0
+
+
 class StageTrace:
-    """Per-stage record: r_k at the start of every iteration, alpha_k used by
-    every update, number of updates, dense and sketch products, status."""
+    """Per-stage record: r_k at the start of every iteration, alpha_k and the
+    degree used by every update, number of updates, dense and sketch products,
+    status."""
 
     def __init__(self):
         self.r = []
         self.alpha = []
+        self.degree = []
+        self.q = []
         self.iters = 0
         self.gemms = 0
         self.sketch_products = 0
@@ -204,16 +222,38 @@ def _alpha_for(R, d, lo, hi, accelerate, sketch_fn, stage, k, trace):
         return taylor_coeff(d)
     S = sketch_fn(stage, k, R.shape[0])
     trace.sketch_products += 2 * d + 1
-    return fit_alpha(krylov_gram(R, S, d), d, lo, hi)
+    M = krylov_gram(R, S, d)
+    alpha = fit_alpha(M, d, lo, hi)
+    trace.q.append(predicted_contraction(M, d, alpha))
+    return alpha
+
+
+class DegreeRule:
+    """Degree of each update of a stage: fixed at d, or (degree_max > d)
+    raised by one after an update whose predicted contraction exceeds
+    adapt_ratio.  Intervals: the given [lo, hi] for the starting degree, the
+    default interval of every raised degree."""
+
+    def __init__(self, d, lo, hi, degree_max=None, adapt_ratio=0.3):
+        self.d = d
+        self.dmax = d if degree_max is None else max(d, degree_max)
+        self.ratio = adapt_ratio
+        self.lo0, self.hi0 = (lo, hi) if lo is not None and hi is not None else default_interval(d)
+
+    def interval(self, d):
+        return (self.lo0, self.hi0) if d == self.d else default_interval(d)
+
+    def next(self, d, q):
+        return d + 1 if (d < self.dmax and q > self.ratio) else d
 
 
 def coupled_sqrt_stage(Y0, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
-                       sketch_fn=None, stage=0, accelerate=True):
+                       sketch_fn=None, stage=0, accelerate=True, degree_max=None,
+                       adapt_ratio=0.3):
     """One coupled Newton-Schulz square-root stage from Y_0 (Z_0 = I).
     Y_0 must have its spectrum in (0, 1].  Returns (Y, Z, StageTrace)
-    with Y -> Y_0^{1/2}, Z -> Y_0^{-1/2}."""
-    if lo is None or hi is None:
-        lo, hi = default_interval(d)
+    with Y -> Y_0^{1/2}, Z -> Y_0^{-1/2}.  degree_max > d: adaptive degree."""
+    rule = DegreeRule(d, lo, hi, degree_max, adapt_ratio)
     Y0 = np.asarray(Y0, np.float64)
     n = Y0.shape[0]
     I = np.eye(n)
@@ -229,9 +269,13 @@ def coupled_sqrt_stage(Y0, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
         if st is not None:
             tr.status = st
             break
+        lo, hi = rule.interval(d)
         alpha = _alpha_for(R, d, lo, hi, accelerate, sketch_fn, stage, k, tr)
         tr.alpha.append(alpha)
+        tr.degree.append(d)
         g = _poly_g(R, alpha, d, tr)
+        if accelerate:
+            d = rule.next(d, tr.q[-1])
         Y = Y @ g
         tr.gemms += 1
         if k == 0:
@@ -261,7 +305,7 @@ def exact_sketch_fn():
 
 
 def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
-             sketch_fn=None, accelerate=True):
+             sketch_fn=None, accelerate=True, degree_max=None, adapt_ratio=0.3):
     """PRISM A^{-1/p} (p in {2, 4}) with the auxiliary A^{1/p}.
     Scaling c = ||A||_F, stage 1 on A / c; for p = 4 stage 2 on stage 1's Y.
     Returns (X, X_aux, info) with info = dict(status, stages=[StageTrace...], c)."""
@@ -275,7 +319,8 @@ def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
         t = StageTrace()
         t.status = NONFINITE
         return nan, nan, dict(status=NONFINITE, stages=[t], c=c)
-    Y, Z, t1 = coupled_sqrt_stage(A / c, d, lo, hi, tol, max_iter, sketch_fn, 0, accelerate)
+    Y, Z, t1 = coupled_sqrt_stage(A / c, d, lo, hi, tol, max_iter, sketch_fn, 0, accelerate,
+                                  degree_max, adapt_ratio)
     stages = [t1]
     status = t1.status
     if p == 2:
@@ -284,22 +329,23 @@ def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
         raise ValueError("p must be 2 or 4")
     if status in (NONFINITE, DIVERGED):
         return Z * np.nan, Y * np.nan, dict(status=status, stages=stages, c=c)
-    Y2, Z2, t2 = coupled_sqrt_stage(Y, d, lo, hi, tol, max_iter, sketch_fn, 1, accelerate)
+    Y2, Z2, t2 = coupled_sqrt_stage(Y, d, lo, hi, tol, max_iter, sketch_fn, 1, accelerate,
+                                    degree_max, adapt_ratio)
     stages.append(t2)
     status = _worst(status, t2.status)
     return Z2 * c ** -0.25, Y2 * c ** 0.25, dict(status=status, stages=stages, c=c)
 
 
 def polar(G, d=2, lo=None, hi=None, tol=1e-6, max_iter=30, sketch_fn=None,
-          accelerate=True):
+          accelerate=True, degree_max=None, adapt_ratio=0.3):
     """PRISM polar factor of G (m x n).  Wide inputs are handled through G^T.
     R_k = I - X_k^T X_k, X_{k+1} = X_k g.  Returns (U, info)."""
     G = np.asarray(G, np.float64)
     if G.shape[0] < G.shape[1]:
-        U, info = polar(G.T, d, lo, hi, tol, max_iter, sketch_fn, accelerate)
+        U, info = polar(G.T, d, lo, hi, tol, max_iter, sketch_fn, accelerate, degree_max,
+                        adapt_ratio)
         return U.T, info
-    if lo is None or hi is None:
-        lo, hi = default_interval(d)
+    rule = DegreeRule(d, lo, hi, degree_max, adapt_ratio)
     if sketch_fn is None:
         sketch_fn = make_sketch_fn(0)
     m, n = G.shape
@@ -320,9 +366,13 @@ def polar(G, d=2, lo=None, hi=None, tol=1e-6, max_iter=30, sketch_fn=None,
         if st is not None:
             tr.status = st
             break
+        lo, hi = rule.interval(d)
         alpha = _alpha_for(R, d, lo, hi, accelerate, sketch_fn, 0, k, tr)
         tr.alpha.append(alpha)
+        tr.degree.append(d)
         g = _poly_g(R, alpha, d, tr)
+        if accelerate:
+            d = rule.next(d, tr.q[-1])
         X = X @ g
         tr.gemms += 1
         R = I - X.T @ X

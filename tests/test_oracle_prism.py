@@ -274,3 +274,69 @@ def test_status_codes():
     U, info = prism.polar(G, max_iter=30)
     assert info["status"] in (prism.MAXITER, prism.STAGNATED)
     np.testing.assert_allclose(U, cf.polar(G)[0], atol=1e-6)
+
+
+def test_predicted_contraction_is_the_sketched_next_residual():
+    # q = sqrt(phi_S(alpha)) / ||R S|| equals ||r(R; alpha) S|| / ||R S|| with
+    # r(R; alpha) = I - (I - R) g(R)^2 formed explicitly
+    A, _, _ = W.spd_logu(30, 12, 1e-3, 1.0)
+    R = np.eye(30) - A.astype(np.float64) / np.linalg.norm(A)
+    S = philox.sketch(9, 0, 0, 0, 30, 8)
+    for d in (1, 2, 3):
+        lo, hi = prism.default_interval(d)
+        M = prism.krylov_gram(R, S, d)
+        alpha = prism.fit_alpha(M, d, lo, hi)
+        g = sum(prism.taylor_coeff(j) * np.linalg.matrix_power(R, j) for j in range(d))
+        g = g + alpha * np.linalg.matrix_power(R, d)
+        rR = np.eye(30) - (np.eye(30) - R) @ g @ g
+        q = np.linalg.norm(rR @ S) / np.linalg.norm(R @ S)
+        assert prism.predicted_contraction(M, d, alpha) == pytest.approx(q, rel=1e-9)
+
+
+@pytest.mark.parametrize("ratio", [0.3, 0.6])
+def test_adaptive_degree_matches_eigen_model(ratio):
+    # exact sketch (S = I): the matrix iteration's degree schedule, alphas and
+    # iteration count equal the scalar model's, whose contraction is computed
+    # from the residual spectrum directly
+    c = W.spd_64()
+    Q, lam = c["Q"], c["lam"]
+    A = W.spd_from_spectrum(Q, lam)
+    _, _, info = prism.inv_root(A, p=2, d=2, degree_max=3, adapt_ratio=ratio,
+                                sketch_fn=prism.exact_sketch_fn())
+    st = info["stages"][0]
+    lo, hi = prism.default_interval(2)
+    model = em.run(1 - lam / np.linalg.norm(lam), 2, lo, hi, 1e-6, 100, degree_max=3,
+                   adapt_ratio=ratio, intervals={3: prism.default_interval(3)})
+    assert st.degree == model["degree"]
+    assert st.iters == model["iters"]
+    np.testing.assert_allclose(st.alpha, model["alpha"], atol=1e-7)
+    assert 3 in st.degree
+    # dense products: per update (d - 1) powers, Y g, g Z (not at k = 0), Z Y
+    assert st.gemms == sum(d - 1 + 2 for d in st.degree) + len(st.degree) - 1
+
+
+def test_adaptive_degree_limits():
+    A, _, _ = W.spd_logu(40, 6, 1e-4, 1.0)
+    A = A.astype(np.float64)
+    fn = prism.make_sketch_fn(2)
+    _, _, fixed = prism.inv_root(A, p=2, d=2, sketch_fn=fn)
+    _, _, never = prism.inv_root(A, p=2, d=2, degree_max=3, adapt_ratio=np.inf, sketch_fn=fn)
+    _, _, always = prism.inv_root(A, p=2, d=2, degree_max=3, adapt_ratio=-1.0, sketch_fn=fn)
+    f, nv, al = fixed["stages"][0], never["stages"][0], always["stages"][0]
+    assert nv.iters == f.iters and nv.alpha == f.alpha and set(nv.degree) == {2}
+    assert al.degree[0] == 2 and set(al.degree[1:]) == {3}
+
+
+@pytest.mark.parametrize("p", [2, 4])
+def test_adaptive_degree_converges_to_closed_form(p):
+    A, _, _ = W.spd_logu(48, 17, 1e-5, 1.0)
+    A = A.astype(np.float64)
+    X, Xa, info = prism.inv_root(A, p=p, d=2, degree_max=3, sketch_fn=prism.make_sketch_fn(4),
+                                 tol=1e-9)
+    Xr, Xar = cf.inv_root(A, p)
+    assert info["status"] == prism.CONVERGED
+    assert cf.rel_fro(X, Xr) < 1e-9 and cf.rel_fro(Xa, Xar) < 1e-9
+    G = W.gaussian(64, 40, 5).astype(np.float64)
+    U, pinfo = prism.polar(G, d=2, degree_max=3, sketch_fn=prism.make_sketch_fn(4), tol=1e-10)
+    assert pinfo["status"] == prism.CONVERGED
+    assert cf.rel_fro(U, cf.polar(G)[0]) < 1e-9
