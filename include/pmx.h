@@ -43,7 +43,7 @@ extern "C" {
 
 #define PMX_VERSION_MAJOR 0
 #define PMX_VERSION_MINOR 1
-#define PMX_OPTS_VERSION 2
+#define PMX_OPTS_VERSION 3
 #define PMX_TRACE_LEN 64   /* alpha / residual trace entries kept per stage */
 #define PMX_MAX_SKETCH 16  /* largest supported sketch width p */
 
@@ -82,7 +82,9 @@ typedef enum {
  * Part II).  pmx_matfn_opts_default fills the defaults given per field.
  */
 typedef struct {
-  int32_t struct_version; /* PMX_OPTS_VERSION (2), or 1 for the 40-byte layout */
+  int32_t struct_version; /* PMX_OPTS_VERSION (3); 2 (48-byte layout, ending at
+                             degree_max) and 1 (40 bytes, ending at seed) are
+                             accepted with the later fields at their defaults */
   int32_t degree;         /* d in {1, 2, 3}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2;
                              d = 3 runs on the fp32 paths only (the bf16 polar
                              factor and fp64_iters > 0 return NOT_SUPPORTED) */
@@ -98,9 +100,18 @@ typedef struct {
                              stage run in fp64 (0..max_iter), the rest in fp32;
                              for ill-conditioned inputs (kappa near 1e6) whose
                              fp32 result misses 1e-4.  Ignored by the polar
-                             factor.  Default 0.  Added in struct_version 2: a
-                             version-1 struct (without it and `reserved`) is
-                             still accepted and means 0. */
+                             factor.  Default 0.  Added in struct_version 2. */
+  int32_t degree_max;     /* adaptive degree ([PRISM summary], methodology step
+                             3): 0 (default) or `degree` keeps d fixed; 3 with
+                             degree = 2 starts every stage at d = 2 and uses
+                             d = 3 for the rest of the stage after an update
+                             whose sketched contraction
+                             sqrt(phi_S(alpha_k)) / ||R_k S||_F exceeds
+                             adapt_ratio.  Needs accelerate = 1 and
+                             fp64_iters = 0; fp32 paths only (the bf16 polar
+                             factor returns NOT_SUPPORTED).  Added in version 3
+                             (it takes the place of version 2's zero `reserved`). */
+  float adapt_ratio;      /* the contraction threshold above; default 0.3 */
   int32_t reserved;       /* must be 0 */
 } pmx_matfn_opts;
 

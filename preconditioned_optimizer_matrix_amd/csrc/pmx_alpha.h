@@ -118,7 +118,7 @@ __device__ inline double argmin_quartic(const double (&w)[5], double lo, double 
 // argmin on [lo, hi] is taken.  A degenerate or non-finite quartic gives c_d.
 template <int J>
 __device__ inline double alpha_from_gram_t(const double* G, double s, const AlphaCoef& co,
-                                           double lo, double hi) {
+                                           double lo, double hi, double* phi_out) {
   double av[3][J];
   double sp = 1.0;
 #pragma unroll
@@ -164,16 +164,20 @@ __device__ inline double alpha_from_gram_t(const double* G, double s, const Alph
   for (int e = 0; e < 5; ++e) ok = ok && isfinite(w[e]);
 #pragma unroll
   for (int e = 1; e < 5; ++e) mx = fmax(mx, fabs(w[e]));
-  if (!ok || mx <= 1e-300) return fmin(fmax(co.taylor_d, lo), hi);
-  if (hi <= lo) return lo;
-  return argmin_quartic(w, lo, hi);
+  double a;
+  if (!ok || mx <= 1e-300) a = fmin(fmax(co.taylor_d, lo), hi);
+  else if (hi <= lo) a = lo;
+  else a = argmin_quartic(w, lo, hi);
+  // phi_S at the chosen alpha (the sketched ||R_{k+1} S||_F^2)
+  if (phi_out) *phi_out = w[0] + a * (w[1] + a * (w[2] + a * (w[3] + a * w[4])));
+  return a;
 }
 
 __device__ inline double alpha_from_gram(const double* G, int J, double s, const AlphaCoef& co,
-                                         double lo, double hi) {
-  if (J == 3) return alpha_from_gram_t<3>(G, s, co, lo, hi);
-  if (J == 5) return alpha_from_gram_t<5>(G, s, co, lo, hi);
-  return alpha_from_gram_t<7>(G, s, co, lo, hi);
+                                         double lo, double hi, double* phi_out = nullptr) {
+  if (J == 3) return alpha_from_gram_t<3>(G, s, co, lo, hi, phi_out);
+  if (J == 5) return alpha_from_gram_t<5>(G, s, co, lo, hi, phi_out);
+  return alpha_from_gram_t<7>(G, s, co, lo, hi, phi_out);
 }
 
 }  // namespace pmx

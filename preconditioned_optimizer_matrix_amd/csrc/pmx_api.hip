@@ -181,17 +181,25 @@ bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out) {
   pmx_matfn_opts_default(&o);
   if (in) {
     if (in->struct_version == 1) {
-      // the 40-byte layout without fp64_iters / reserved
+      // the 40-byte layout, ending at seed
       memcpy(&o, in, offsetof(pmx_matfn_opts, fp64_iters));
-      o.struct_version = PMX_OPTS_VERSION;
+    } else if (in->struct_version == 2) {
+      // the 48-byte layout, ending at degree_max (version 2's zero `reserved`)
+      memcpy(&o, in, offsetof(pmx_matfn_opts, adapt_ratio));
     } else if (in->struct_version == PMX_OPTS_VERSION) {
       o = *in;
     } else {
       return false;
     }
+    o.struct_version = PMX_OPTS_VERSION;
   }
   if (o.fp64_iters < 0 || o.fp64_iters > o.max_iter || o.reserved != 0) return false;
   if (o.degree < 1 || o.degree > 3) return false;
+  // adaptive degree: 2 -> 3 only, with the fitted alpha and fp32 updates
+  if (o.degree_max != 0 && o.degree_max != o.degree &&
+      !(o.degree == 2 && o.degree_max == 3 && o.accelerate == 1 && o.fp64_iters == 0))
+    return false;
+  if (!isfinite(o.adapt_ratio)) return false;
   if (o.sketch_p < 1 || o.sketch_p > PMX_MAX_SKETCH) return false;
   if (o.max_iter < 1 || o.max_iter > kMaxIter) return false;
   if (o.accelerate != 0 && o.accelerate != 1) return false;
@@ -220,6 +228,8 @@ IterCfg make_cfg(const pmx_matfn_opts& o, int n, pmx_matfn_info* info) {
   c.hi = o.alpha_hi;
   c.tol = o.tol;
   c.taylor_d = (float)taylor(o.degree);
+  c.degree_max = std::max(o.degree, o.degree_max);
+  c.adapt_ratio = o.adapt_ratio;
   c.seed_lo = (uint32_t)(o.seed & 0xFFFFFFFFull);
   c.seed_hi = (uint32_t)(o.seed >> 32);
   c.info = info;
@@ -263,7 +273,7 @@ IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, i
       off = align_up(off + sizeof(double) * (size_t)L.buf_stride * batch);
     }
   }
-  L.kld = (int64_t)(2 * o.degree + 2) * o.sketch_p;
+  L.kld = (int64_t)(2 * std::max(o.degree, o.degree_max) + 2) * o.sketch_p;
   L.kstride = (((int64_t)cols * L.kld + 63) / 64) * 64;
   L.kbuf = off;
   off = align_up(off + sizeof(float) * (size_t)L.kstride * batch);
@@ -354,6 +364,9 @@ SketchJob make_sketch(const IterLayout& L, void* ws, const IterCfg& cfg, int n, 
 //          K5 = R^2 K3 / s^2 (+ Gram, alpha)
 //   d = 3: as d = 2, then [K5 | K6] = R^2 [K3 | K4] / s^2 and
 //          K7 = R^2 K5 / s^2 (+ Gram, alpha); R^3 = R^2 R is formed for g
+//   adaptive degree (2, raised to 3): the d = 3 sequence for every matrix,
+//          R^3 only for the matrices at d = 3, and the Gram pass uses
+//          K_1..K_5 or K_1..K_7 by each matrix's current degree
 //   d = 1: K_j = R K_{j-1} / s, j = 1..3 (+ Gram, alpha on the last pass)
 hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
                                    const pmx_matfn_opts& o, const IterCfg& cfg,
@@ -362,6 +375,7 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
   Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
   float* kbuf = at<float>(ws, L.kbuf);
   const int d = o.degree, pp = o.sketch_p;
+  const int dmax = cfg.degree_max;  // d = 3, or the adaptive degree's ceiling
   hipError_t e;
   if (d >= 2 && power) {
     GemmParams g = gemm_base(q.h, n, n, n, batch);
@@ -376,11 +390,12 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     set_vec(g);
     e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
     if (e != hipSuccess) return e;
-    if (d == 3) {
+    if (dmax == 3) {
       // R^3 = R^2 R: symmetric by structure, so its upper triangle is kept and
       // mirrored and g stays exactly symmetric
       g.prob[0].a = {R2, n, L.buf_stride, nullptr, 0};
       g.prob[0].c = R3;
+      g.min_degree = 3;  // under the adaptive degree, the matrices at d = 3 only
       e = q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
       if (e != hipSuccess) return e;
     }
@@ -398,6 +413,11 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
   kp.gram_stride = L.gstride;
   kp.cfg = cfg;
   kp.coef = coef;
+  if (dmax > d) {
+    kp.coef_up = make_coef(dmax);
+    kp.lo_up = 0.3125f;  // the default interval of d = 3
+    kp.hi_up = 2.46f;
+  }
   auto job = [&](const float* m, int ic, int oc, int pw) {
     SkinnyJob j;
     j.mat = m;
@@ -420,12 +440,12 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
     kp.q = 2 * pp;
     kp.job[0] = job(R2, pp, 3 * pp, 2);
     if ((e = pass(1, false)) != hipSuccess) return e;
-    if (d == 3) {
+    if (dmax == 3) {
       kp.job[0] = job(R2, 3 * pp, 5 * pp, 2);
       if ((e = pass(1, false)) != hipSuccess) return e;
     }
     kp.q = pp;
-    kp.job[0] = job(R2, (2 * d - 1) * pp, (2 * d + 1) * pp, 2);
+    kp.job[0] = job(R2, (2 * dmax - 1) * pp, (2 * dmax + 1) * pp, 2);
     return pass(1, true);
   }
   kp.q = pp;
@@ -470,6 +490,8 @@ pmx_status pmx_matfn_opts_default(pmx_matfn_opts* o) {
   o->tol = 1e-6f;
   o->seed = 0;
   o->fp64_iters = 0;
+  o->degree_max = 0;
+  o->adapt_ratio = 0.3f;
   o->reserved = 0;
   return PMX_OK;
 }
@@ -554,14 +576,16 @@ pmx_status pmx_trace_collect(pmx_handle h, double* ms, int64_t* launches) {
 // counterparts (Y, Z ping-pong, R, R^2).
 static int inv_root_f64_bufs(const pmx_matfn_opts& o) { return o.fp64_iters > 0 ? 6 : 0; }
 // n x n residual buffers: R, R^2 (g is written over R^2), and R^3 for d = 3.
-static int small_bufs(const pmx_matfn_opts& o) { return o.degree == 3 ? 3 : 2; }
+static int small_bufs(const pmx_matfn_opts& o) {
+  return std::max(o.degree, o.degree_max) == 3 ? 3 : 2;
+}
 static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
   return iter_layout(n, n, batch, o, 4, small_bufs(o), sizeof(float), inv_root_f64_bufs(o)).total;
 }
 // fp32: X ping-pong, R, R^2 (and R^3 for d = 3).  bf16: X and X^T
 // ping-pong, R, R^2 (fp32), and the bf16 operands R and g.
 static int polar_bufs(pmx_dtype dt, const pmx_matfn_opts& o) {
-  return dt == PMX_BF16 ? 8 : (o.degree == 3 ? 5 : 4);
+  return dt == PMX_BF16 ? 8 : (std::max(o.degree, o.degree_max) == 3 ? 5 : 4);
 }
 static size_t polar_ws(int m, int n, int batch, const pmx_matfn_opts& o, pmx_dtype dt) {
   const int rows = std::max(m, n), cols = std::min(m, n);
@@ -734,14 +758,15 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   float* Zb[2] = {at<float>(ws, Lw.bufs[2]), at<float>(ws, Lw.bufs[3])};
   float* Rb = at<float>(ws, Lw.bufs[4]);
   float* R2b = at<float>(ws, Lw.bufs[5]);
-  float* R3b = o.degree == 3 ? at<float>(ws, Lw.bufs[6]) : nullptr;
+  float* R3b = small_bufs(o) == 3 ? at<float>(ws, Lw.bufs[6]) : nullptr;
   const IterCfg cfg = make_cfg(o, n, info);
   const AlphaCoef coef = make_coef(o.degree);
   const int d = o.degree;
   const bool acc = o.accelerate != 0;
 
   const int stages = (p == 4) ? 2 : 1;
-  if (n <= kSmallMaxN && h->small_fused && o.fp64_iters == 0 && o.degree <= 2) {
+  if (n <= kSmallMaxN && h->small_fused && o.fp64_iters == 0 &&
+      std::max(o.degree, o.degree_max) <= 2) {
     SmallRootParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.a = A;
@@ -765,7 +790,8 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
     return PMX_OK;
   }
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
-    return launch_ctrl_reset(ctrl, info, batch, at<uint32_t>(ws, Lw.skc), kSplitMaxWorkers, q.s);
+    return launch_ctrl_reset(ctrl, info, batch, o.degree, at<uint32_t>(ws, Lw.skc),
+                             kSplitMaxWorkers, q.s);
   }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, q.s);
@@ -917,6 +943,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         fp.r2 = (d >= 2) ? R2b : nullptr;
         fp.r3 = R3b;
         fp.c2 = (float)taylor(2);
+        fp.adaptive = cfg.degree_max > d;
         fp.dst = Zb[1];
         fp.stride = Lw.buf_stride;
         fp.n = n;
@@ -940,6 +967,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         fp.r2 = (d >= 2) ? R2b : nullptr;
         fp.r3 = R3b;
         fp.c2 = (float)taylor(2);
+        fp.adaptive = cfg.degree_max > d;
         fp.dst = R2b;
         fp.stride = Lw.buf_stride;
         fp.n = n;
@@ -1032,7 +1060,8 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const bool bf = dtype == PMX_BF16;
   const int rows = std::max(m, n), cols = std::min(m, n);
   const bool tr = m < n;
-  if (bf && o.degree == 3) return PMX_ERR_NOT_SUPPORTED;  // d = 3: fp32 only
+  // d = 3 and the adaptive degree: fp32 only
+  if (bf && std::max(o.degree, o.degree_max) == 3) return PMX_ERR_NOT_SUPPORTED;
   const IterLayout Lw = iter_layout(rows, cols, batch, o, polar_bufs(dtype, o), 0, sizeof(float));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
@@ -1055,14 +1084,14 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   float* Xb[2] = {at<float>(ws, Lw.bufs[0]), at<float>(ws, Lw.bufs[1])};
   float* Rb = at<float>(ws, Lw.bufs[2]);
   float* R2b = at<float>(ws, Lw.bufs[3]);
-  float* R3b = (!bf && o.degree == 3) ? at<float>(ws, Lw.bufs[4]) : nullptr;
+  float* R3b = (!bf && polar_bufs(dtype, o) == 5) ? at<float>(ws, Lw.bufs[4]) : nullptr;
   const IterCfg cfg = make_cfg(o, cols, info);
   const AlphaCoef coef = make_coef(o.degree);
   const int d = o.degree;
   const bool acc = o.accelerate != 0;
   const int64_t bs = Lw.buf_stride;
 
-  if (!bf && rows <= kSmallMaxN && h->small_fused && o.degree <= 2) {
+  if (!bf && rows <= kSmallMaxN && h->small_fused && std::max(o.degree, o.degree_max) <= 2) {
     SmallPolarParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.g = (const float*)G;
@@ -1082,7 +1111,8 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     return PMX_OK;
   }
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
-    return launch_ctrl_reset(ctrl, info, batch, at<uint32_t>(ws, Lw.skc), kSplitMaxWorkers, q.s);
+    return launch_ctrl_reset(ctrl, info, batch, o.degree, at<uint32_t>(ws, Lw.skc),
+                             kSplitMaxWorkers, q.s);
   }));
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(G, bf, m, n, ldg, sg, batch, ctrl, partials, Lw.pstride, info, q.s);
@@ -1138,6 +1168,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
         fp.r2 = (d >= 2) ? R2b : nullptr;
         fp.r3 = R3b;
         fp.c2 = (float)taylor(2);
+        fp.adaptive = cfg.degree_max > d;
         fp.dst = R2b;
         fp.stride = bs;
         fp.n = cols;

@@ -438,8 +438,10 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
                : map_item(it, G > 0 ? G : 1, total, p.tiles_m, p.tiles_n, p.map_mode);
   };
   auto running = [&](const TileCoord& tc) __attribute__((always_inline)) {
-    return !p.ctrl ||
-           *(volatile int32_t*)&p.ctrl[tc.z / p.nprob].status == PMX_RUNNING;
+    if (!p.ctrl) return true;
+    const Ctrl* c = p.ctrl + tc.z / p.nprob;
+    return *(const volatile int32_t*)&c->status == PMX_RUNNING &&
+           (p.min_degree == 0 || *(const volatile int32_t*)&c->degree >= p.min_degree);
   };
 
   // acc = the product over k tiles [kb, ke) of the tile tc
@@ -592,7 +594,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
         if (threadIdx.x == 0) {
           Ctrl& c = p.ctrl[b];
           if (p.count_update) c.iter += 1;
-          c.gemms += p.products;
+          // p.products counts the powers of the configured degree
+          c.gemms += p.products + (c.degree - p.cfg.degree);
           decide(c, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
         }
       }

@@ -175,6 +175,7 @@ __global__ __launch_bounds__(NT) void stage_init_f64_kernel(StageInit64Params p)
       cb->iter = 0;
       cb->r_prev = 0.0;
       cb->status = PMX_RUNNING;
+      cb->degree_next = p.cfg.degree;
       decide(*cb, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
     }
   }

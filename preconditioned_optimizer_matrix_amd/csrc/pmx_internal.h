@@ -27,6 +27,8 @@ struct Ctrl {
   int32_t gemms;
   int32_t sketch_products;
   uint32_t counter;  // arrival counter of the last-block reductions
+  int32_t degree;      // d of the current update (fixed, or the adaptive degree)
+  int32_t degree_next; // d of the next update, taken over by decide()
   int32_t pad;
 };
 
@@ -39,6 +41,8 @@ struct IterCfg {
   int accelerate;
   float lo, hi, tol;
   float taylor_d;  // c_d, the coefficient used when accelerate == 0
+  int degree_max;  // > degree: adaptive degree (raised up to degree_max)
+  float adapt_ratio;
   uint32_t seed_lo, seed_hi;
   pmx_matfn_info* info;  // may be null
 };
@@ -73,6 +77,7 @@ __device__ __forceinline__ void decide(Ctrl& c, const IterCfg& cfg, pmx_matfn_in
   else if (k >= cfg.max_iter) st = PMX_MAXITER;
   if (info && k < PMX_TRACE_LEN) info->rtrace[s][k] = (float)r;
   c.r_prev = r;
+  c.degree = c.degree_next;  // a raise decided by the last alpha fit starts here
   c.fro = sqrt(fro2);
   if (st == PMX_RUNNING && !cfg.accelerate) {
     c.alpha = cfg.taylor_d;
@@ -267,6 +272,9 @@ struct GemmParams {
   int products;          // dense products to add to ctrl.gemms on completion
   int count_update;      // 1: this residual ends an update (iter += 1)
   IterCfg cfg;
+  // matrices whose current degree is below min_degree skip the launch
+  // (R^3 under the adaptive degree); 0: none
+  int min_degree;
   // fp32 split-k tail (null sk_part: every item whole).  The caller provides
   // sk_cap floats of partial-tile slots and kSplitMaxWorkers zeroed per-tile
   // counters (each launch leaves them zero); the launcher fills in the split.

@@ -78,11 +78,15 @@ struct SkinnyParams {
   int n, q;
   int variant;  // 0: In staged through LDS, 1: In read directly
   Ctrl* ctrl;
-  // last pass only: Gram shares (16 doubles per block) and the alpha solve
+  // last pass only: Gram shares (kGramShare doubles per block) and the alpha
+  // solve; a matrix at degree d uses K_1..K_{2d+1} (the pass writes one of
+  // them, the others are read back), coef and [cfg.lo, cfg.hi] at the
+  // configured degree, coef_up and [lo_up, hi_up] at the raised one
   double* gram_partials;
   int64_t gram_stride;
   IterCfg cfg;
-  AlphaCoef coef;
+  AlphaCoef coef, coef_up;
+  float lo_up, hi_up;
 };
 
 struct FormGParams {
@@ -95,6 +99,7 @@ struct FormGParams {
   int dst_bf16;
   int vec;               // set by the launcher
   float c0, c1, c2;      // Taylor coefficients c_0 .. c_{d-1} (c2 for d = 3)
+  int adaptive;          // 1: each matrix's degree from its control block
   Ctrl* ctrl;
   SketchJob sketch;      // the next iteration's sketch, generated on the side
 };
@@ -247,8 +252,8 @@ hipError_t launch_form_g_f64(const FormG64Params& p, int batch, hipStream_t s);
 hipError_t launch_handover_f64(const Handover64Params& p, int batch, hipStream_t s);
 
 // Resets the control blocks and infos of a call and zeroes nzero words at zero.
-hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, uint32_t* zero,
-                             int nzero, hipStream_t s);
+hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, int degree,
+                             uint32_t* zero, int nzero, hipStream_t s);
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,
                             int64_t pstride, pmx_matfn_info* info, hipStream_t s);

@@ -19,8 +19,8 @@ __device__ __forceinline__ int32_t load_status(const Ctrl* c) {
 }  // namespace
 
 // ---------------------------------------------------------------- control
-__global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch, uint32_t* zero,
-                                  int nzero) {
+__global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch, int degree,
+                                  uint32_t* zero, int nzero) {
   const int b = blockIdx.x;
   for (int i = b * blockDim.x + threadIdx.x; i < nzero; i += gridDim.x * blockDim.x) zero[i] = 0u;
   if (b >= batch) return;
@@ -37,6 +37,8 @@ __global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch, u
     c.gemms = 0;
     c.sketch_products = 0;
     c.counter = 0u;
+    c.degree = degree;
+    c.degree_next = degree;
     c.pad = 0;
     ctrl[b] = c;
   }
@@ -158,6 +160,7 @@ __global__ __launch_bounds__(NT) void sqrt_stage_init_kernel(StageInitParams p) 
       cb->iter = 0;
       cb->r_prev = 0.0;
       cb->status = PMX_RUNNING;
+      cb->degree_next = p.cfg.degree;  // every stage starts at the configured degree
       decide(*cb, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
     }
   }
@@ -252,10 +255,14 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
   }
 
   if constexpr (GJ > 0) {
-    // the block's share of the Gram entries (a, bb), a <= bb < J <= GJ
+    // the block's share of the Gram entries (a, bb), a <= bb < J <= GJ, of
+    // K_1..K_J, J = 2 d + 1 for the matrix's current degree d; this pass
+    // writes K_jo, the others are read back
+    const int deg = *(const volatile int32_t*)&cb->degree;
     constexpr int NE = GJ * (GJ + 1) / 2;
-    const int J = 2 * p.cfg.degree + 1;
+    const int J = 2 * deg + 1;
     const int pp = p.cfg.p;
+    const int jo = job.out_col / pp;
     double g[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) g[e] = 0.0;
@@ -266,11 +273,10 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
       for (int j = 0; j < GJ; ++j) v[j] = 0.0;
       if (valid[i]) {
 #pragma unroll
-        for (int j = 1; j < GJ; ++j)
-          if (j < J) v[j - 1] = (double)kb[(int64_t)vrow[i] * p.kld + j * pp + vcol[i]];
-#pragma unroll
-        for (int j = 0; j < GJ; ++j)
-          if (j == J - 1) v[j] = (double)acc[i];
+        for (int j = 1; j <= GJ; ++j)
+          if (j <= J)
+            v[j - 1] = j == jo ? (double)acc[i]
+                               : (double)kb[(int64_t)vrow[i] * p.kld + j * pp + vcol[i]];
       }
       int t = 0;
 #pragma unroll
@@ -323,8 +329,18 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      const double alpha = alpha_from_gram(gsum, J, fro, p.coef, p.cfg.lo, p.cfg.hi);
+      double phi = 0.0;
+      const bool up = deg > p.cfg.degree;
+      const double alpha = alpha_from_gram(gsum, J, fro, up ? p.coef_up : p.coef,
+                                           up ? p.lo_up : p.cfg.lo, up ? p.hi_up : p.cfg.hi, &phi);
       cb->alpha = alpha;
+      // adaptive degree: the sketch predicts ||R_{k+1} S|| / ||R_k S|| =
+      // sqrt(phi_S(alpha)) / ||R S|| (gsum[0] = ||K_1||^2 of the scaled K_1 = R S / s)
+      if (deg < p.cfg.degree_max) {
+        const double m11 = gsum[0] * fro * fro;
+        const double q = m11 > 0.0 ? sqrt(fmax(phi, 0.0) / m11) : 0.0;
+        if (q > (double)p.cfg.adapt_ratio) cb->degree_next = deg + 1;
+      }
       cb->sketch_products += J;
       const int k = cb->iter;
       if (p.cfg.info && k < PMX_TRACE_LEN) p.cfg.info[b].alpha[cb->stage][k] = (float)alpha;
@@ -626,7 +642,8 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   uint16_t* Gh = p.dst_bf16 ? reinterpret_cast<uint16_t*>(p.dst) + (int64_t)b * p.stride : nullptr;
   const float* R3 = p.r3 ? p.r3 + (int64_t)b * p.stride : nullptr;
   const float c0 = p.c0, c1 = p.c1, c2 = p.c2;
-  const bool d1 = p.degree == 1, d3 = p.degree == 3;
+  const int deg = p.adaptive ? *(const volatile int32_t*)&cb->degree : p.degree;
+  const bool d1 = deg == 1, d3 = deg == 3;
   if (p.vec) {
     // four columns per thread (n % 4 == 0, stride % 4 == 0)
     const int nv = n / 4;
@@ -807,10 +824,10 @@ static int grid_rows(int rows, int cap) {
   return g < 1 ? 1 : g;
 }
 
-hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, uint32_t* zero,
-                             int nzero, hipStream_t s) {
-  hipLaunchKernelGGL(ctrl_reset_kernel, dim3(batch), dim3(NT), 0, s, ctrl, info, batch, zero,
-                     nzero);
+hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, int degree,
+                             uint32_t* zero, int nzero, hipStream_t s) {
+  hipLaunchKernelGGL(ctrl_reset_kernel, dim3(batch), dim3(NT), 0, s, ctrl, info, batch, degree,
+                     zero, nzero);
   return hipGetLastError();
 }
 
@@ -870,7 +887,7 @@ template <int Q, int RW>
 static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
   if (!gram) skinny_go_j<Q, RW, 0>(p, njobs, batch, s);
   else if constexpr (Q <= 16) {
-    if (p.cfg.degree == 3) skinny_go_j<Q, RW, 7>(p, njobs, batch, s);
+    if (p.cfg.degree_max == 3) skinny_go_j<Q, RW, 7>(p, njobs, batch, s);
     else skinny_go_j<Q, RW, 5>(p, njobs, batch, s);
   }
 }
@@ -896,7 +913,7 @@ hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch,
 
 hipError_t launch_form_g(const FormGParams& pin, int batch, hipStream_t s) {
   FormGParams p = pin;
-  if (p.degree == 3 && (!p.r2 || !p.r3)) return hipErrorInvalidValue;
+  if ((p.degree == 3 || p.adaptive) && (!p.r2 || !p.r3)) return hipErrorInvalidValue;
   p.vec = (p.n % 4 == 0) && (p.stride % 4 == 0) && ((uintptr_t)p.r % 16 == 0) &&
           (!p.r2 || (uintptr_t)p.r2 % 16 == 0) && (!p.r3 || (uintptr_t)p.r3 % 16 == 0) &&
           ((uintptr_t)p.dst % 16 == 0);

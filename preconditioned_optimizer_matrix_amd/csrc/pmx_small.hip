@@ -244,7 +244,7 @@ __device__ void small_fill(float* M, int n, float diag) {
 // Control block and info at the start of a call (the reset of the
 // multi-kernel path), then c = ||src||_F; status NONFINITE when c is not a
 // positive finite number.
-__device__ void small_start(SmallShared& sh, pmx_matfn_info* info, double fro2) {
+__device__ void small_start(SmallShared& sh, pmx_matfn_info* info, double fro2, int degree) {
   if (threadIdx.x == 0) {
     Ctrl c;
     c.c = sqrt(fro2);
@@ -258,6 +258,8 @@ __device__ void small_start(SmallShared& sh, pmx_matfn_info* info, double fro2) 
     c.gemms = 0;
     c.sketch_products = 0;
     c.counter = 0u;
+    c.degree = degree;
+    c.degree_next = degree;
     c.pad = 0;
     if (!(c.c > 0.0) || !isfinite(c.c)) {
       c.status = PMX_NONFINITE;
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(SNT, 1) void small_root_kernel(SmallRootParams p) {
     Y[i * SLD + j] = v;
     acc += (double)v * (double)v;
   }
-  small_start(sh, cfg.info, block_total(acc, sh));
+  small_start(sh, cfg.info, block_total(acc, sh), cfg.degree);
   const bool accel = cfg.accelerate != 0;
   const int d = cfg.degree;
   for (int stage = 0; stage < p.stages; ++stage) {
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
     X[i * SLD + j] = v;
     acc += (double)v * (double)v;
   }
-  small_start(sh, cfg.info, block_total(acc, sh));
+  small_start(sh, cfg.info, block_total(acc, sh), cfg.degree);
   const bool accel = cfg.accelerate != 0;
   const int d = cfg.degree;
   if (small_status(sh) == PMX_RUNNING) {

@@ -18,7 +18,7 @@ OK, ERR_INVALID_VALUE, ERR_NOT_SUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = ra
 RUNNING, CONVERGED, MAXITER, STAGNATED, NONFINITE, DIVERGED = -1, 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 OP_STATS, OP_INV_ROOT, OP_POLAR, OP_APPLY = range(4)
-OPTS_VERSION = 2
+OPTS_VERSION = 3
 TRACE_LEN = 64
 MAX_SKETCH = 16
 STATUS_NAMES = {RUNNING: "RUNNING", CONVERGED: "CONVERGED", MAXITER: "MAXITER",
@@ -45,6 +45,7 @@ class Opts(ctypes.Structure):
                 ("accelerate", ctypes.c_int32), ("alpha_lo", ctypes.c_float),
                 ("alpha_hi", ctypes.c_float), ("tol", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("fp64_iters", ctypes.c_int32),
+                ("degree_max", ctypes.c_int32), ("adapt_ratio", ctypes.c_float),
                 ("reserved", ctypes.c_int32)]
 
 

@@ -29,9 +29,11 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     from preconditioned_optimizer_matrix_amd import pmx
-    # pmx_matfn_opts: 5 int32 + 3 float + uint64 (8-aligned) + 2 int32 = 48 bytes
-    assert ctypes.sizeof(pmx.Opts) == 48
+    # pmx_matfn_opts: 5 int32 + 3 float + uint64 (8-aligned) + 2 int32 + float
+    # + int32 = 56 bytes (version 2 ended at degree_max, version 1 at seed)
+    assert ctypes.sizeof(pmx.Opts) == 56
     assert pmx.Opts.fp64_iters.offset == 40
+    assert pmx.Opts.degree_max.offset == 44 and pmx.Opts.adapt_ratio.offset == 48
     # pmx_matfn_info: 6 int32 + 3 float + 4 * 64 float
     assert ctypes.sizeof(pmx.Info) == 4 * (6 + 3 + 4 * pmx.TRACE_LEN)
     src = open(HEADER).read()
@@ -49,6 +51,7 @@ def test_host_only_calls():
     assert math.isnan(o.alpha_lo) and math.isnan(o.alpha_hi)
     assert o.tol == pytest.approx(1e-6)
     assert (o.fp64_iters, o.reserved, o.struct_version) == (0, 0, pmx.OPTS_VERSION)
+    assert o.degree_max == 0 and o.adapt_ratio == pytest.approx(0.3)
     assert pmx.lib.pmx_matfn_opts_default(None) == pmx.ERR_INVALID_VALUE
 
 
@@ -96,6 +99,16 @@ def test_workspace_sizes_and_option_validation():
     assert ws(fp64_iters=4) == pmx.OK
     # the 40-byte version-1 layout is still accepted (fp64_iters = 0)
     assert ws(struct_version=1, fp64_iters=7, reserved=5) == pmx.OK
+    # version 2 (48 bytes): the fields after degree_max are not read
+    assert ws(struct_version=2, adapt_ratio=float("nan"), reserved=5) == pmx.OK
+    # adaptive degree: 2 -> 3 with the fitted alpha and fp32 updates only
+    assert ws(degree_max=3) == pmx.OK
+    assert ws(degree_max=2) == pmx.OK
+    assert ws(degree=1, degree_max=3) == pmx.ERR_INVALID_VALUE
+    assert ws(degree_max=3, accelerate=0) == pmx.ERR_INVALID_VALUE
+    assert ws(degree_max=3, fp64_iters=2) == pmx.ERR_INVALID_VALUE
+    assert ws(degree_max=4) == pmx.ERR_INVALID_VALUE
+    assert ws(degree_max=3, adapt_ratio=float("inf")) == pmx.ERR_INVALID_VALUE
     # fp64 leading updates add six n x n fp64 buffers
     o4 = pmx.default_opts(fp64_iters=4)
     b4 = pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, o4)

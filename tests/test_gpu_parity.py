@@ -171,6 +171,57 @@ def test_degree_three(env, p):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("p", [2, 4])
+def test_adaptive_degree(env, p):
+    # degree 2 raised to 3 per matrix after an update whose sketched
+    # contraction exceeds adapt_ratio (0.3)
+    torch, pmx, dev = env
+    for n in (100, 256, 517):
+        _say("adaptive degree root", p, n)
+        # (at kappa = 1e4 and n = 517 an fp32 emulation of the fixed d = 2
+        # iteration already floors near 1.1e-4 for A^{1/4}, so kappa = 1e3 here)
+        A, _, _ = W.spd_logu(n, 5000 + n, 1e-3, 1.0)
+        X, XA, info = _run_root(env, A, p, degree_max=3, seed=6)
+        ref, ref_aux = cf.inv_root(A, p)
+        assert int(info[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), n
+        assert cf.rel_fro(X, ref) < 1e-4 and cf.rel_fro(XA, ref_aux) < 1e-4, n
+    # same sketches as the oracle: iteration counts, alphas and products
+    A, _, _ = W.spd_logu(96, 77)
+    _say("adaptive degree alpha trace", p)
+    X, XA, info = _run_root(env, A, p, degree_max=3, seed=5)
+    _, _, ref = prism.inv_root(A.astype(np.float64), p=p, d=2, degree_max=3,
+                               sketch_fn=prism.make_sketch_fn(5, b=0, p=8))
+    inf = info[0]
+    assert any(3 in st.degree for st in ref["stages"])
+    for s, st in enumerate(ref["stages"]):
+        it = int(inf["iters"][s])
+        assert abs(it - st.iters) <= 1, (s, it, st.iters)
+        for k in range(min(it, st.iters)):
+            if st.r[k] >= 1e-3:
+                assert abs(inf["alpha"][s][k] - st.alpha[k]) < 1e-3, (s, k)
+    total_ref = sum(st.gemms for st in ref["stages"])
+    assert abs(int(inf["gemms"]) - total_ref) <= 5 * len(ref["stages"])
+    # batched, mixed conditioning: each matrix keeps its own degree
+    As = np.stack([W.spd_logu(200, 60 + b, 10.0 ** -(b + 1), 1.0)[0] for b in range(3)])
+    Xb, _, infb = pmx.inv_root(torch.from_numpy(As).to(dev), p,
+                               opts=pmx.default_opts(degree_max=3))
+    torch.cuda.synchronize()
+    for b in range(3):
+        assert cf.rel_fro(Xb[b].cpu().numpy(), cf.inv_root(As[b], p)[0]) < 1e-4, b
+    if p == 2:
+        for m, n in ((150, 150), (300, 17), (96, 200)):
+            _say("adaptive degree polar", m, n)
+            G = W.gaussian(m, n, 3 * m + n)
+            U, pinfo = pmx.polar(torch.from_numpy(G).to(dev), opts=pmx.default_opts(degree_max=3))
+            torch.cuda.synchronize()
+            assert int(pmx.parse_info(pinfo)[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+            assert cf.rel_fro(U.cpu().numpy(), cf.polar(G)[0]) < 1e-4
+        with pytest.raises(pmx.PmxError):
+            pmx.polar(_bf16(torch, W.gaussian(64, 32, 5)).to(dev),
+                      opts=pmx.default_opts(degree_max=3))
+        torch.cuda.synchronize()
+
+
 def test_inv_root_batched(env):
     torch, pmx, dev = env
     _say("batched inv_root")
