@@ -21,6 +21,9 @@ Modules
                   on a Gaussian sketch, coupled square root, chained inverse 4th
                   root, polar factor), used to pin alpha traces, iteration and
                   product counts.
+  inv_newton   -- the coupled inverse Newton iteration for A^{-1/p} with the
+                  PRISM coefficient (residual map 1 - (1 - xi) g^p, an objective
+                  of degree 2p in alpha).
   interval     -- the [lo, hi] interval rule for the adaptive coefficient.
   eigen_model  -- the same iteration on a known spectrum (scalar map), an
                   independent route to iteration counts and alpha.

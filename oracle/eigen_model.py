@@ -20,11 +20,13 @@ from .prism import (CONVERGED, DIVERGE_LEVEL, DIVERGED, MAXITER, STAG_FACTOR,
                     STAG_LEVEL, STAGNATED, residual_map, taylor_coeff)
 
 
-def argmin_alpha(xi, w, d, lo, hi, npts=2001):
+def argmin_alpha(xi, w, d, lo, hi, npts=2001, rmap=None):
     """argmin over [lo, hi] of sum_i w_i r(xi_i; alpha)^2."""
     xi = np.asarray(xi, np.float64)
     w = np.asarray(w, np.float64)
-    obj = lambda a: float(np.sum(w * residual_map(xi, a, d) ** 2))
+    if rmap is None:
+        rmap = residual_map
+    obj = lambda a: float(np.sum(w * rmap(xi, a, d) ** 2))
     grid = np.linspace(lo, hi, npts)
     vals = np.array([obj(a) for a in grid])
     i = int(np.argmin(vals))
@@ -39,13 +41,19 @@ def argmin_alpha(xi, w, d, lo, hi, npts=2001):
 
 
 def run(xi0, d, lo, hi, tol, max_iter, weights_fn=None, accelerate=True, degree_max=None,
-        adapt_ratio=0.3, intervals=None):
+        adapt_ratio=0.3, intervals=None, rmap=None, taylor=None):
     """Iterate the scalar map on the residual spectrum xi0 (eigenvalues of R_0).
     weights_fn(k) returns the weights w_i for iteration k (None: exact, w = 1).
     degree_max > d: after an update whose contraction of the weighted
     residual, sqrt(sum w r(xi)^2 / sum w xi^2), exceeds adapt_ratio the degree
     rises by one (intervals[d] gives the interval of each raised degree).
+    rmap(xi, alpha, d) replaces the square-root family's residual map and
+    taylor(d) its Taylor coefficient (another iteration family).
     Returns dict(iters, status, r, alpha, degree)."""
+    if rmap is None:
+        rmap = residual_map
+    if taylor is None:
+        taylor = taylor_coeff
     xi = np.asarray(xi0, np.float64).copy()
     n = xi.size
     rs, alphas, degrees = [], [], []
@@ -68,12 +76,12 @@ def run(xi0, d, lo, hi, tol, max_iter, weights_fn=None, accelerate=True, degree_
             break
         w = np.ones(n) if weights_fn is None else weights_fn(k)
         if accelerate:
-            alpha = argmin_alpha(xi, w, d, lo, hi)
+            alpha = argmin_alpha(xi, w, d, lo, hi, rmap=rmap)
         else:
-            alpha = taylor_coeff(d)
+            alpha = taylor(d)
         alphas.append(alpha)
         degrees.append(d)
-        nxt = residual_map(xi, alpha, d)
+        nxt = rmap(xi, alpha, d)
         if accelerate and d < dmax:
             q = sqrt(float(np.sum(w * nxt * nxt)) / float(np.sum(w * xi * xi)))
             if q > adapt_ratio:

@@ -29,27 +29,32 @@ def _extreme(f, lo, hi, npts=4001):
     return min(float(res.fun), float(v.min()))
 
 
-def admissible(alpha, d, tol=1e-9):
-    """Conditions (i) and (ii) for one alpha."""
+def admissible(alpha, d, tol=1e-9, rmap=None):
+    """Conditions (i) and (ii) for one alpha.  rmap(xi, alpha) is the residual
+    map (default: the square-root / polar family's r of degree d)."""
+    if rmap is None:
+        rmap = lambda x, a: residual_map(x, a, d)
     xs = np.linspace(1e-6, 1.0, 20001)
-    r = residual_map(xs, alpha, d)
+    r = rmap(xs, alpha)
     if np.any(np.abs(r) > xs * (1 + tol)):
         return False
-    f = lambda x: residual_map(x, alpha, d)
+    f = lambda x: rmap(x, alpha)
     m = min(0.0, _extreme(f, 0.0, 1.0))
     lo_img = _extreme(f, m, 1.0)
-    hi_img = -_extreme(lambda x: -residual_map(x, alpha, d), m, 1.0)
+    hi_img = -_extreme(lambda x: -rmap(x, alpha), m, 1.0)
     return lo_img >= m - tol and hi_img <= 1.0 + tol
 
 
-def upper_bound(d, top=3.0, iters=30, samples=100):
-    """Largest u (bisection to ~3e-9 relative) with every alpha' in [c_d, u]
-    admissible (checked on ``samples`` equally spaced alpha')."""
-    lo = taylor_coeff(d)
+def upper_bound(d, top=3.0, iters=30, samples=100, rmap=None, lo=None):
+    """Largest u (bisection to ~3e-9 relative) with every alpha' in [lo, u]
+    admissible (checked on ``samples`` equally spaced alpha'); lo defaults to
+    the square-root family's Taylor coefficient c_d."""
+    if lo is None:
+        lo = taylor_coeff(d)
     a, b = lo, top
     for _ in range(iters):
         mid = 0.5 * (a + b)
-        if all(admissible(x, d) for x in np.linspace(lo, mid, samples)):
+        if all(admissible(x, d, rmap=rmap) for x in np.linspace(lo, mid, samples)):
             a = mid
         else:
             b = mid
