@@ -37,6 +37,9 @@ def parse():
                          "(the bf16 polar factor always runs d = 2)")
     ap.add_argument("--degree-max", type=int, default=0,
                     help="3 with --degree 2: adaptive degree (fp32 paths)")
+    ap.add_argument("--method", type=int, default=0,
+                    help="inverse roots: 0 coupled Newton-Schulz (chained for p = 4), "
+                         "1 coupled inverse Newton")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -82,12 +85,12 @@ def cpu_baseline(G, L0, R0, beta, eps):
                 step_s=round(t4 - t0, 2))
 
 
-def root_exec_flops(n, batch, iters, gemms):
+def root_exec_flops(n, batch, iters, gemms, method=0):
     """Launched tile arithmetic of one fp32 inverse-root sequence of order n
     (batch matrices per launch) from its update counts and dense products: a
-    stage of k updates runs 2 k - 1 full update products; the rest (residuals
-    I - Z Y and the powers of R) are symmetric and run the upper-triangle
-    tiles only."""
+    stage of k updates runs 2 k - 1 full update products (Y g, g Z; the
+    inverse Newton iteration k - 1, X g); the rest (residuals, powers of R and
+    g, g^p M) are symmetric and run the upper-triangle tiles only."""
     bm = 128
     T = -(-n // bm)
     if T * (T + 1) // 2 * batch < 256:
@@ -96,7 +99,7 @@ def root_exec_flops(n, batch, iters, gemms):
     tf = -(-n // 128)
     full = tf * tf * 2.0 * 128 * 128 * n if tf * tf * batch >= 256 else 2.0 * n ** 3
     sym = T * (T + 1) // 2 * 2.0 * bm * bm * n
-    nfull = sum(2 * int(k) - 1 for k in iters if int(k) > 0)
+    nfull = sum((2 * int(k) - 1) if method == 0 else (int(k) - 1) for k in iters if int(k) > 0)
     return nfull * full + (int(gemms) - nfull) * sym
 
 
@@ -124,8 +127,8 @@ def other_workload(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     opts = pmx.default_opts(max_iter=args.max_iter, degree=args.degree,
-                            degree_max=args.degree_max)
-    taylor = pmx.default_opts(max_iter=60, accelerate=0, degree=args.degree)
+                            degree_max=args.degree_max, method=args.method)
+    taylor = pmx.default_opts(max_iter=60, accelerate=0, degree=args.degree, method=args.method)
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None}
     wl = args.workload
@@ -169,7 +172,7 @@ def other_workload(args):
         ms32 = timed(torch, lambda: fn(opts), args.steps, args.warmup)
         inf32 = pmx.parse_info(info)
         gemms = int(inf32["gemms"].sum())
-        flops32 = sum(root_exec_flops(512, 64, inf32["iters"][b], inf32["gemms"][b])
+        flops32 = sum(root_exec_flops(512, 64, inf32["iters"][b], inf32["gemms"][b], args.method)
                       for b in range(64))
         ms = timed(torch, lambda: fn(o64), args.steps, args.warmup)
         gemms64 = int(pmx.parse_info(info)["gemms"].sum())
@@ -216,7 +219,7 @@ def other_workload(args):
         out["kernel_trace_ms"] = traced(lambda: fn(opts))
         fn(taylor)
         tg = int(pmx.parse_info(info)[0]["gemms"])
-        tf = root_exec_flops(10000, 1, inf["iters"], inf["gemms"]) / (ms * 1e-3) / 1e12
+        tf = root_exec_flops(10000, 1, inf["iters"], inf["gemms"], args.method) / (ms * 1e-3) / 1e12
         out.update(metric="ms per square root (n=10^4, A^1/2 and A^-1/2)", value=round(ms, 2),
                    unit="ms", dtype="f32", config={"workload": wl}, gemms=gemms,
                    gemms_taylor=tg, gemm_ratio_taylor_over_prism=round(tg / gemms, 3),
@@ -357,7 +360,7 @@ def main():
     L9, R9 = L.clone(), R.clone()
     G = Gs[-1]
     opts = pmx.default_opts(max_iter=args.max_iter, degree=args.degree,
-                            degree_max=args.degree_max)
+                            degree_max=args.degree_max, method=args.method)
     wsL = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, m, m, 1, pmx.F32, opts), dev)
     wsR = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, opts), dev)
     wsA = pmx.workspace(pmx.workspace_bytes(pmx.OP_APPLY, m, n, 1, pmx.F32, None), dev)
@@ -391,7 +394,7 @@ def main():
     r_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ev]))
     iL, iR = pmx.parse_info(infoL)[0], pmx.parse_info(infoR)[0]
     gemmsR, gemmsL = int(iR["gemms"]), int(iL["gemms"])
-    tflops_r = root_exec_flops(n, 1, iR["iters"], iR["gemms"]) / (r_ms * 1e-3) / 1e12
+    tflops_r = root_exec_flops(n, 1, iR["iters"], iR["gemms"], args.method) / (r_ms * 1e-3) / 1e12
     dense_tflops_r = gemmsR * 2.0 * n ** 3 / (r_ms * 1e-3) / 1e12
     log("step %.3f ms, R^-1/4 %.3f ms, gemms R %d L %d, iters R %s L %s, status R %s L %s"
         % (ms_step, r_ms, gemmsR, gemmsL, list(iR["iters"]), list(iL["iters"]),
@@ -416,7 +419,7 @@ def main():
 
     roofline = None
     trace = None
-    if not args.no_trace:
+    if not args.no_trace and args.method == 0:
         # one more step with the launch trace: per-class kernel time and
         # launches; the R^-1/4 call is collected on its own for the roofline of
         # its update GEMM (the n = 4096 instantiation, one kernel).
@@ -461,7 +464,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "shampoo_1024x4096", "m": m, "n": n, "beta": beta, "eps": eps,
                    "warmup_updates": 9, "degree": args.degree,
-                   "degree_max": args.degree_max, "sketch_p": 8, "tol": 1e-6,
+                   "degree_max": args.degree_max, "method": args.method, "sketch_p": 8,
+                   "tol": 1e-6,
                    "max_iter": args.max_iter,
                    "step": "restore L,R; stats update; L^-1/4; R^-1/4; apply"},
         "gemms_to_converge": {"R": gemmsR, "L": gemmsL, "R_taylor": gemmsR_taylor},

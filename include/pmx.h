@@ -44,6 +44,8 @@ extern "C" {
 #define PMX_VERSION_MAJOR 0
 #define PMX_VERSION_MINOR 1
 #define PMX_OPTS_VERSION 3
+#define PMX_METHOD_NEWTON_SCHULZ 0
+#define PMX_METHOD_INVERSE_NEWTON 1
 #define PMX_TRACE_LEN 64   /* alpha / residual trace entries kept per stage */
 #define PMX_MAX_SKETCH 16  /* largest supported sketch width p */
 
@@ -112,7 +114,20 @@ typedef struct {
                              factor returns NOT_SUPPORTED).  Added in version 3
                              (it takes the place of version 2's zero `reserved`). */
   float adapt_ratio;      /* the contraction threshold above; default 0.3 */
-  int32_t reserved;       /* must be 0 */
+  int32_t method;         /* inverse roots: PMX_METHOD_NEWTON_SCHULZ (0, default):
+                             coupled Newton-Schulz square roots, chained for
+                             p = 4; PMX_METHOD_INVERSE_NEWTON (1): the coupled
+                             inverse Newton iteration X <- X g, M <- g^p M with
+                             R = I - M and g = f_{d-1}(R) + alpha R^d, f the
+                             Taylor polynomial of (1 - xi)^{-1/p} ([PRISM
+                             synthesis], key contributions: inverse Newton
+                             methods); alpha minimises a degree-2p sketched
+                             objective over [1/4, 1/2] (d = 1) or [5/32, 0.60]
+                             (d = 2) for p = 4, the square-root family's
+                             intervals for p = 2.  d in {1, 2}, fp32 updates
+                             only (fp64_iters = 0, no adaptive degree); X_aux =
+                             A X^{p-1} is formed after the iteration.  Ignored
+                             by the polar factor.  Added in version 3. */
 } pmx_matfn_opts;
 
 /*

@@ -173,6 +173,153 @@ __device__ inline double alpha_from_gram_t(const double* G, double s, const Alph
   return a;
 }
 
+// ------------------------------------------------- inverse Newton objective
+// Real roots inside (lo, hi), ascending, of c[0] + c[1] x + ... + c[D] x^D.
+// The roots of the derivative split [lo, hi] into pieces on which the
+// polynomial is monotone; every sign change on a piece is refined by the same
+// bracketed Newton steps as argmin_quartic.  At most D roots.
+template <int D>
+__device__ inline int poly_roots_in(const double* c, double lo, double hi, double* out) {
+  if constexpr (D == 1) {
+    if (c[1] == 0.0) return 0;
+    const double x = -c[0] / c[1];
+    if (x > lo && x < hi) {
+      out[0] = x;
+      return 1;
+    }
+    return 0;
+  } else {
+    double dc[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) dc[i] = (double)(i + 1) * c[i + 1];
+    double brk[D + 1];
+    int nb = 0;
+    brk[nb++] = lo;
+    double crit[D];
+    const int nc = poly_roots_in<D - 1>(dc, lo, hi, crit);
+    for (int i = 0; i < nc; ++i) brk[nb++] = crit[i];
+    brk[nb++] = hi;
+    auto P = [&](double x) {
+      double v = c[D];
+      for (int i = D - 1; i >= 0; --i) v = v * x + c[i];
+      return v;
+    };
+    auto dP = [&](double x) {
+      double v = dc[D - 1];
+      for (int i = D - 2; i >= 0; --i) v = v * x + dc[i];
+      return v;
+    };
+    int n = 0;
+    for (int i = 0; i + 1 < nb; ++i) {
+      double x0 = brk[i], x1 = brk[i + 1];
+      double f0 = P(x0);
+      const double f1 = P(x1);
+      if (f0 == 0.0) {
+        if (x0 > lo && x0 < hi && (n == 0 || out[n - 1] != x0)) out[n++] = x0;
+        continue;
+      }
+      if ((f0 < 0.0) == (f1 < 0.0) || f1 == 0.0) continue;
+      double x = 0.5 * (x0 + x1);
+      for (int it = 0; it < 100; ++it) {
+        const double fx = P(x);
+        if (fx == 0.0) break;
+        if ((fx < 0.0) == (f0 < 0.0)) {
+          x0 = x;
+          f0 = fx;
+        } else {
+          x1 = x;
+        }
+        const double d1 = dP(x);
+        if (d1 != 0.0) {
+          const double step = fx / d1;
+          if (fabs(step) <= 8.881784197001252e-16 * fabs(x)) {
+            x -= step;
+            break;
+          }
+        }
+        double xn = (d1 != 0.0) ? x - fx / d1 : 0.5 * (x0 + x1);
+        if (!(xn > x0 && xn < x1)) xn = 0.5 * (x0 + x1);
+        if (!(xn > x0 && xn < x1)) break;
+        x = xn;
+      }
+      if (x > lo && x < hi) out[n++] = x;
+    }
+    return n;
+  }
+}
+
+// alpha for the inverse Newton family from the Gram G (packed upper
+// triangle of the J x J Gram of the scaled K~_j = (R/s)^j S, j = 1..J): the
+// objective c(alpha)^T M c(alpha), c(alpha) = sum_{i <= NP - 1} alpha^i a_i,
+// has degree 2 (NP - 1); its argmin over [lo, hi] among both ends and the
+// critical points inside (ties to the smaller alpha).  A degenerate or
+// non-finite objective gives the Taylor coefficient.
+template <int J, int NP>
+__device__ inline double alpha_from_gram_newton(const double* G, double s,
+                                                const AlphaCoefN& co, double lo, double hi,
+                                                double* phi_out) {
+  constexpr int W = 2 * (NP - 1);  // degree of the objective
+  double av[NP][J];
+  double sp = 1.0;
+  for (int j = 1; j <= J; ++j) {
+    sp *= s;
+    for (int i = 0; i < NP; ++i) av[i][j - 1] = co.a[i][j] * sp;
+  }
+  double M[J][J];
+  {
+    int t = 0;
+    for (int x = 0; x < J; ++x)
+      for (int y = x; y < J; ++y, ++t) M[x][y] = M[y][x] = G[t];
+  }
+  double w[W + 1];
+  for (int e = 0; e <= W; ++e) w[e] = 0.0;
+  for (int i1 = 0; i1 < NP; ++i1) {
+    double u[J];
+    for (int x = 0; x < J; ++x) {
+      double v = 0.0;
+      for (int y = 0; y < J; ++y) v += M[x][y] * av[i1][y];
+      u[x] = v;
+    }
+    for (int i2 = 0; i2 < NP; ++i2) {
+      double t = 0.0;
+      for (int x = 0; x < J; ++x) t += av[i2][x] * u[x];
+      w[i1 + i2] += t;
+    }
+  }
+  auto phi = [&](double a) {
+    double v = w[W];
+    for (int e = W - 1; e >= 0; --e) v = v * a + w[e];
+    return v;
+  };
+  bool ok = true;
+  double mx = 0.0;
+  for (int e = 0; e <= W; ++e) ok = ok && isfinite(w[e]);
+  for (int e = 1; e <= W; ++e) mx = fmax(mx, fabs(w[e]));
+  double best;
+  if (!ok || mx <= 1e-300) {
+    best = fmin(fmax(co.taylor_d, lo), hi);
+  } else if (hi <= lo) {
+    best = lo;
+  } else {
+    double dw[W];
+    for (int e = 0; e < W; ++e) dw[e] = (double)(e + 1) * w[e + 1];
+    double crit[W];
+    const int nc = poly_roots_in<W - 1>(dw, lo, hi, crit);
+    best = lo;
+    double bv = phi(lo);
+    for (int i = 0; i < nc; ++i) {  // ascending: strict improvement keeps the smaller
+      const double v = phi(crit[i]);
+      if (v < bv) {
+        bv = v;
+        best = crit[i];
+      }
+    }
+    if (phi(hi) < bv) best = hi;
+  }
+  if (phi_out) *phi_out = phi(best);
+  return best;
+}
+
 __device__ inline double alpha_from_gram(const double* G, int J, double s, const AlphaCoef& co,
                                          double lo, double hi, double* phi_out = nullptr) {
   if (J == 3) return alpha_from_gram_t<3>(G, s, co, lo, hi, phi_out);

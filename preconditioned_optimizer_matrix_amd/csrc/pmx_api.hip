@@ -175,8 +175,10 @@ AlphaCoef make_coef(int d) {
   return co;
 }
 
-// Effective options after defaults; returns false if invalid.
-bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out) {
+// Effective options after defaults; returns false if invalid.  root_p: the
+// root order of an inverse-root call (selects the inverse Newton iteration's
+// default interval for p = 4), 0 otherwise.
+bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out, int root_p = 0) {
   pmx_matfn_opts o;
   pmx_matfn_opts_default(&o);
   if (in) {
@@ -193,7 +195,12 @@ bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out) {
     }
     o.struct_version = PMX_OPTS_VERSION;
   }
-  if (o.fp64_iters < 0 || o.fp64_iters > o.max_iter || o.reserved != 0) return false;
+  if (o.fp64_iters < 0 || o.fp64_iters > o.max_iter) return false;
+  if (o.method != PMX_METHOD_NEWTON_SCHULZ && o.method != PMX_METHOD_INVERSE_NEWTON) return false;
+  // the inverse Newton iteration: d <= 2, fixed degree, fp32 updates
+  if (o.method == PMX_METHOD_INVERSE_NEWTON &&
+      (o.degree > 2 || (o.degree_max != 0 && o.degree_max != o.degree) || o.fp64_iters != 0))
+    return false;
   if (o.degree < 1 || o.degree > 3) return false;
   // adaptive degree: 2 -> 3 only, with the fitted alpha and fp32 updates
   if (o.degree_max != 0 && o.degree_max != o.degree &&
@@ -210,6 +217,11 @@ bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out) {
     static const float hi_d[4] = {0.f, 1.0f, 1.47f, 2.46f};
     o.alpha_lo = lo_d[o.degree];
     o.alpha_hi = hi_d[o.degree];
+    if (o.method == PMX_METHOD_INVERSE_NEWTON && root_p == 4) {
+      // the fourth-root map's rule: lo = b_d (1/4, 5/32), hi 1/2 and 0.6039 -> 0.60
+      o.alpha_lo = o.degree == 1 ? 0.25f : 0.15625f;
+      o.alpha_hi = o.degree == 1 ? 0.5f : 0.60f;
+    }
   }
   if (!isfinite(o.alpha_lo) || !isfinite(o.alpha_hi) || o.alpha_lo > o.alpha_hi) return false;
   if (!isfinite(o.tol) || o.tol < 0.f) return false;
@@ -273,7 +285,11 @@ IterLayout iter_layout(int rows, int cols, int batch, const pmx_matfn_opts& o, i
       off = align_up(off + sizeof(double) * (size_t)L.buf_stride * batch);
     }
   }
-  L.kld = (int64_t)(2 * std::max(o.degree, o.degree_max) + 2) * o.sketch_p;
+  // Krylov blocks K_0..K_J: J = 2d + 1, or 4d + 1 for the inverse Newton
+  // iteration (sized for p = 4)
+  const int J = o.method == PMX_METHOD_INVERSE_NEWTON ? 4 * o.degree + 1
+                                                      : 2 * std::max(o.degree, o.degree_max) + 1;
+  L.kld = (int64_t)(J + 1) * o.sketch_p;
   L.kstride = (((int64_t)cols * L.kld + 63) / 64) * 64;
   L.kbuf = off;
   off = align_up(off + sizeof(float) * (size_t)L.kstride * batch);
@@ -456,6 +472,266 @@ hipError_t enqueue_power_and_alpha(Enq& q, void* ws, const IterLayout& L,
   return hipSuccess;
 }
 
+// Coefficients a_0..a_p of the inverse Newton residual map
+// r(xi; alpha) = 1 - (1 - xi) (f + alpha xi^d)^p = sum_i alpha^i a_i(xi),
+// f the Taylor polynomial of (1 - xi)^{-1/p} to degree d - 1:
+//   a_0 = 1 - (1 - xi) f^p,  a_i = -binom(p, i) (1 - xi) f^{p-i} xi^{d i}.
+double root_coeff(int j, int p) {
+  double c = 1.0;
+  for (int i = 0; i < j; ++i) c *= (1.0 / p + i) / (i + 1);
+  return c;
+}
+
+AlphaCoefN make_coef_newton(int d, int p) {
+  Poly f, om;
+  for (int j = 0; j < d; ++j) f.c[j] = root_coeff(j, p);
+  om.c[0] = 1.0;
+  om.c[1] = -1.0;
+  AlphaCoefN co;
+  memset(&co, 0, sizeof(co));
+  for (int i = 0; i <= p; ++i) {
+    // (1 - xi) f^{p-i} xi^{d i}, in 10 coefficients (p d + 1 <= 9)
+    double acc[16] = {0.0};
+    double fp[16] = {0.0};
+    fp[0] = 1.0;
+    for (int t = 0; t < p - i; ++t) {
+      double nx[16] = {0.0};
+      for (int u = 0; u < 16; ++u)
+        for (int v = 0; v < 8 && u + v < 16; ++v) nx[u + v] += fp[u] * f.c[v];
+      memcpy(fp, nx, sizeof(fp));
+    }
+    for (int u = 0; u + 1 < 16; ++u) {
+      acc[u] += fp[u];
+      acc[u + 1] -= fp[u];
+    }
+    double binom = 1.0;
+    for (int t = 0; t < i; ++t) binom = binom * (p - t) / (t + 1);
+    for (int u = 0; u < 10; ++u) {
+      const int src = u - d * i;
+      co.a[i][u] = (src >= 0 && src < 16) ? -binom * acc[src] : 0.0;
+    }
+    if (i == 0) co.a[0][0] += 1.0;
+  }
+  co.taylor_d = root_coeff(d, p);
+  return co;
+}
+
+// The PRISM coupled inverse Newton iteration for A^{-1/p}, fp32 (the
+// iteration and its readings are documented with PMX_METHOD_INVERSE_NEWTON):
+//   M_0 = A / c, X_0 = I, R_0 = I - M_0;  per update k:
+//   R^2 (d = 2, triangle); Krylov passes K_1..K_{p d + 1} and alpha;
+//   g = f(R) + alpha R^d written over R^2 (and into X_1 at k = 0);
+//   g^2, g^4 (p = 4) (triangle); X_{k+1} = X_k g (k >= 1);
+//   R_{k+1} = I - g^p M_k with M_{k+1} = g^p M_k kept (triangle, convergence).
+// The outputs: X = c^{-1/p} X_k, then X_aux = A X^{p-1} from X.
+pmx_status enqueue_inverse_newton(Enq& q, void* ws, const IterLayout& L, const pmx_matfn_opts& o,
+                                  const IterCfg& cfg, const float* A, int lda, int64_t sa, int n,
+                                  int p, float* X, int ldx, int64_t sx, float* XA, int ldaux,
+                                  int64_t saux, int batch) {
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  float* Xb[2] = {at<float>(ws, L.bufs[0]), at<float>(ws, L.bufs[1])};
+  float* Mb[2] = {at<float>(ws, L.bufs[2]), at<float>(ws, L.bufs[3])};
+  float* Rb = at<float>(ws, L.bufs[4]);
+  float* Pb = at<float>(ws, L.bufs[5]);
+  float* Tb = at<float>(ws, L.bufs[6]);
+  float* Ub = at<float>(ws, L.bufs[7]);
+  const int64_t bs = L.buf_stride;
+  const int d = o.degree;
+  const bool acc = o.accelerate != 0;
+  const int J = p * d + 1;
+  IterCfg c = cfg;
+  c.taylor_d = (float)root_coeff(d, p);  // alpha without the sketch fit
+  {
+    StageInitParams ip;
+    memset(&ip, 0, sizeof(ip));
+    ip.a = A;
+    ip.lda = lda;
+    ip.a_stride = sa;
+    ip.ybuf[0] = Mb[0];
+    ip.ybuf[1] = Mb[1];
+    ip.r = Rb;
+    ip.buf_stride = bs;
+    ip.n = n;
+    ip.stage = 0;
+    ip.ctrl = ctrl;
+    ip.partials = at<double>(ws, L.partials);
+    ip.partial_stride = L.pstride;
+    ip.cfg = c;
+    ip.sketch = make_sketch(L, ws, c, n, 0, 0, acc);
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_sqrt_stage_init(ip, batch, q.s); }));
+  }
+  auto sym_product = [&](const float* a, const float* b, float* out) {
+    GemmParams g = gemm_base(q.h, n, n, n, batch);
+    g.prob[0].a = {a, n, bs, nullptr, 0};
+    g.prob[0].b = {b, n, bs, nullptr, 0};
+    g.prob[0].c = out;
+    g.prob[0].ldc = n;
+    g.prob[0].stride_c = bs;
+    g.ctrl = ctrl;
+    g.sym = 1;
+    if (q.h->split_k) use_split(g, ws, L);
+    set_vec(g);
+    return q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
+  };
+  for (int k = 0; k < o.max_iter; ++k) {
+    const int cur = k & 1, nxt = cur ^ 1;
+    if (d == 2) PMX_TRY(sym_product(Rb, Rb, Pb));
+    if (acc) {
+      SkinnyParams kp;
+      memset(&kp, 0, sizeof(kp));
+      kp.kbuf = at<float>(ws, L.kbuf);
+      kp.variant = q.h->skinny_variant;
+      kp.kld = L.kld;
+      kp.kstride = L.kstride;
+      kp.n = n;
+      kp.ctrl = ctrl;
+      kp.gram_partials = at<double>(ws, L.gram);
+      kp.gram_stride = L.gstride;
+      kp.cfg = c;
+      kp.coef = make_coef(d);
+      kp.gram_j = J;
+      if (p == 4) {
+        kp.newton_p = 4;
+        kp.coef_n = make_coef_newton(d, 4);
+      }
+      const int pp = o.sketch_p;
+      auto job = [&](const float* m, int ic, int oc, int pw) {
+        SkinnyJob j;
+        j.mat = m;
+        j.mat_ld = n;
+        j.mat_stride = bs;
+        j.in_col = ic;
+        j.out_col = oc;
+        j.pow = pw;
+        return j;
+      };
+      auto pass = [&](int njobs, bool gram) {
+        return q.run(gram ? PMX_KC_SKINNY_ALPHA : PMX_KC_SKINNY,
+                     [&] { return launch_skinny(kp, njobs, gram, batch, q.s); });
+      };
+      if (d == 2) {
+        // K_1 = R S, K_2 = R^2 S; pairs [K_{t+1} | K_{t+2}] = R^2 [K_{t-1} | K_t];
+        // the last block K_J = R^2 K_{J-2} with the Gram and alpha (J odd)
+        kp.q = pp;
+        kp.job[0] = job(Rb, 0, pp, 1);
+        kp.job[1] = job(Pb, 0, 2 * pp, 2);
+        PMX_TRY(pass(2, false));
+        int t = 2;
+        while (J - t >= 3) {
+          kp.q = 2 * pp;
+          kp.job[0] = job(Pb, (t - 1) * pp, (t + 1) * pp, 2);
+          PMX_TRY(pass(1, false));
+          t += 2;
+        }
+        kp.q = pp;
+        kp.job[0] = job(Pb, (J - 2) * pp, J * pp, 2);
+        PMX_TRY(pass(1, true));
+      } else {
+        kp.q = pp;
+        for (int j = 1; j <= J; ++j) {
+          kp.job[0] = job(Rb, (j - 1) * pp, j * pp, 1);
+          PMX_TRY(pass(1, j == J));
+        }
+      }
+    }
+    {
+      FormGParams fp;
+      memset(&fp, 0, sizeof(fp));
+      fp.r = Rb;
+      fp.r2 = d == 2 ? Pb : nullptr;
+      fp.dst = Pb;
+      fp.dst2 = k == 0 ? Xb[1] : nullptr;  // X_1 = X_0 g = g
+      fp.stride = bs;
+      fp.n = n;
+      fp.degree = d;
+      fp.c0 = (float)root_coeff(0, p);
+      fp.c1 = (float)root_coeff(1, p);
+      fp.ctrl = ctrl;
+      fp.sketch = make_sketch(L, ws, c, n, k + 1, 0, acc && k + 1 < o.max_iter);
+      PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
+    }
+    PMX_TRY(sym_product(Pb, Pb, Tb));                // g^2
+    const float* gp = Tb;
+    if (p == 4) {
+      PMX_TRY(sym_product(Tb, Tb, Ub));              // g^4
+      gp = Ub;
+    }
+    if (k > 0) {
+      GemmParams u = gemm_base(q.h, n, n, n, batch);
+      u.ctrl = ctrl;
+      u.prob[0].a = {Xb[cur], n, bs, nullptr, 0};
+      u.prob[0].b = {Pb, n, bs, nullptr, 0};
+      u.prob[0].c = Xb[nxt];
+      u.prob[0].ldc = n;
+      u.prob[0].stride_c = bs;
+      if (q.h->split_k) use_split(u, ws, L);
+      set_vec(u);
+      PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f32(u, false, false, ROLE_UPDATE, q.s); }));
+    }
+    {
+      // R_{k+1} = I - g^p M_k, and M_{k+1} = g^p M_k kept (symmetric by
+      // construction: g^p and M_k are polynomials in A)
+      GemmParams r = gemm_base(q.h, n, n, n, batch);
+      r.ctrl = ctrl;
+      r.prob[0].a = {gp, n, bs, nullptr, 0};
+      r.prob[0].b = {Mb[cur], n, bs, nullptr, 0};
+      r.prob[0].c = Rb;
+      r.prob[0].ldc = n;
+      r.prob[0].stride_c = bs;
+      r.prob[1].c = Mb[nxt];
+      r.prob[1].ldc = n;
+      r.prob[1].stride_c = bs;
+      r.resid_keep = 1;
+      r.partials = at<double>(ws, L.partials);
+      r.partial_stride = L.pstride;
+      r.products = (d - 1) + (p == 4 ? 2 : 1) + (k > 0 ? 1 : 0) + 1;
+      r.count_update = 1;
+      r.cfg = c;
+      r.sym = 1;
+      if (q.h->split_k) use_split(r, ws, L);
+      set_vec(r);
+      PMX_TRY(q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, false, false, ROLE_RESID, q.s); }));
+    }
+  }
+  RootFinishParams fp;
+  memset(&fp, 0, sizeof(fp));
+  fp.ybuf[0] = Xb[0];
+  fp.ybuf[1] = Xb[1];
+  fp.zbuf[0] = Xb[0];
+  fp.zbuf[1] = Xb[1];
+  fp.buf_stride = bs;
+  fp.x = X;
+  fp.ldx = ldx;
+  fp.x_stride = sx;
+  fp.n = n;
+  fp.expo_x = -1.0 / p;
+  fp.ctrl = ctrl;
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_root_finish(fp, batch, q.s); }));
+  if (XA) {
+    // A^{1/p} = A X^{p-1} from the scaled output (no gating: a failed matrix
+    // has X = NaN and its auxiliary output follows)
+    auto product = [&](const float* a, int64_t la, int64_t sta, const float* b, int64_t lb,
+                       int64_t stb, float* out, int64_t lo_, int64_t sto) {
+      GemmParams g = gemm_base(q.h, n, n, n, batch);
+      g.prob[0].a = {a, la, sta, nullptr, 0};
+      g.prob[0].b = {b, lb, stb, nullptr, 0};
+      g.prob[0].c = out;
+      g.prob[0].ldc = lo_;
+      g.prob[0].stride_c = sto;
+      set_vec(g);
+      return q.run(PMX_KC_OTHER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
+    };
+    if (p == 2) {
+      PMX_TRY(product(A, lda, sa, X, ldx, sx, XA, ldaux, saux));
+    } else {
+      PMX_TRY(product(X, ldx, sx, X, ldx, sx, Tb, n, bs));       // X^2
+      PMX_TRY(product(Tb, n, bs, X, ldx, sx, Ub, n, bs));        // X^3
+      PMX_TRY(product(A, lda, sa, Ub, n, bs, XA, ldaux, saux));  // A X^3
+    }
+  }
+  return PMX_OK;
+}
+
 }  // namespace
 }  // namespace pmx
 
@@ -492,7 +768,7 @@ pmx_status pmx_matfn_opts_default(pmx_matfn_opts* o) {
   o->fp64_iters = 0;
   o->degree_max = 0;
   o->adapt_ratio = 0.3f;
-  o->reserved = 0;
+  o->method = PMX_METHOD_NEWTON_SCHULZ;
   return PMX_OK;
 }
 
@@ -576,7 +852,10 @@ pmx_status pmx_trace_collect(pmx_handle h, double* ms, int64_t* launches) {
 // counterparts (Y, Z ping-pong, R, R^2).
 static int inv_root_f64_bufs(const pmx_matfn_opts& o) { return o.fp64_iters > 0 ? 6 : 0; }
 // n x n residual buffers: R, R^2 (g is written over R^2), and R^3 for d = 3.
+// Inverse Newton: the four big buffers are X and M ping-pong, then R, R^2 / g,
+// g^2 and g^4.
 static int small_bufs(const pmx_matfn_opts& o) {
+  if (o.method == PMX_METHOD_INVERSE_NEWTON) return 4;
   return std::max(o.degree, o.degree_max) == 3 ? 3 : 2;
 }
 static size_t inv_root_ws(int n, int batch, const pmx_matfn_opts& o) {
@@ -725,7 +1004,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   if (!h || !A || !X || n < 1 || n > kMaxN || batch < 1) return PMX_ERR_INVALID_VALUE;
   if (p != 2 && p != 4) return PMX_ERR_INVALID_VALUE;
   pmx_matfn_opts o;
-  if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
+  if (!resolve_opts(opts, &o, p)) return PMX_ERR_INVALID_VALUE;
   if (lda < n || sa < 0 || (batch > 1 && sa != 0 && sa < (int64_t)(n - 1) * lda + n))
     return PMX_ERR_INVALID_VALUE;
   if (!batch_layout_ok(n, n, ldx, sx, batch)) return PMX_ERR_INVALID_VALUE;
@@ -766,7 +1045,7 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
 
   const int stages = (p == 4) ? 2 : 1;
   if (n <= kSmallMaxN && h->small_fused && o.fp64_iters == 0 &&
-      std::max(o.degree, o.degree_max) <= 2) {
+      std::max(o.degree, o.degree_max) <= 2 && o.method == PMX_METHOD_NEWTON_SCHULZ) {
     SmallRootParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.a = A;
@@ -796,6 +1075,9 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
+  if (o.method == PMX_METHOD_INVERSE_NEWTON)
+    return enqueue_inverse_newton(q, ws, Lw, o, cfg, A, lda, sa, n, p, X, ldx, sx, XA, ldaux,
+                                  saux, batch);
   const int k64 = std::min(o.fp64_iters, o.max_iter);
   double* Y64[2] = {at<double>(ws, Lw.b64[0]), at<double>(ws, Lw.b64[1])};
   double* Z64[2] = {at<double>(ws, Lw.b64[2]), at<double>(ws, Lw.b64[3])};

@@ -545,6 +545,10 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
     const int m0 = tc.tm * C::BM, n0 = tc.tn * C::BN;
     const int hi = lane >> 5, col_in = lane & 31;
     const bool mirror = sym && tc.tm != tc.tn;
+    // resid_keep: the product itself is also stored, at prob[1].c (ld and
+    // batch stride of prob[1])
+    float* __restrict__ Kp = (EPI == EPI_RESID && p.resid_keep)
+                                 ? p.prob[1].c + (int64_t)b * p.prob[1].stride_c : nullptr;
     float fro = 0.f;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -562,6 +566,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
             if (row < p.M && col < p.N) {
               float* dst = Cm + (int64_t)row * pr.ldc + col;
               if (EPI == EPI_RESID) {
+                if (Kp) Kp[(int64_t)row * p.prob[1].ldc + col] = x;
                 x = (row == col ? 1.f : 0.f) - x;
                 fro += x * x;
               } else if (EPI == EPI_EMA) {
@@ -580,6 +585,13 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 if (row_base + r < p.M) dst[r] = xs[r];
+            }
+            if (Kp) {
+              // the kept product: I - x on the (off-diagonal) mirrored block
+              float* kd = Kp + (int64_t)col * p.prob[1].ldc + row_base;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (row_base + r < p.M) kd[r] = -xs[r];
             }
           }
         }

@@ -271,6 +271,7 @@ struct GemmParams {
   int64_t partial_stride;
   int products;          // dense products to add to ctrl.gemms on completion
   int count_update;      // 1: this residual ends an update (iter += 1)
+  int resid_keep;        // 1: the residual also stores the product at prob[1].c
   IterCfg cfg;
   // matrices whose current degree is below min_degree skip the launch
   // (R^3 under the adaptive degree); 0: none

@@ -8,8 +8,8 @@ namespace pmx {
 // Partial-sum slots reserved per matrix for the elementwise reductions and
 // for the residual GEMM (one slot per output tile).
 constexpr int kPartialsPerMatrix = 1024;
-// Gram share slots per skinny block (J (J + 1) / 2 <= 28 entries, J <= 7).
-constexpr int kGramShare = 32;
+// Gram share slots per skinny block (J (J + 1) / 2 <= 45 entries, J <= 9).
+constexpr int kGramShare = 48;
 
 // bf16 storage type: raw bits, converted explicitly (round to nearest even).
 struct bf16_t {
@@ -71,6 +71,13 @@ struct AlphaCoef {
   double taylor_d;
 };
 
+// Coefficient vectors a_0..a_p (powers xi^0 .. xi^{p d + 1}, p d + 1 <= 9) of
+// the inverse Newton residual map r(xi; alpha) = sum_i alpha^i a_i(xi).
+struct AlphaCoefN {
+  double a[5][10];
+  double taylor_d;
+};
+
 struct SkinnyParams {
   SkinnyJob job[2];
   float* kbuf;
@@ -87,6 +94,10 @@ struct SkinnyParams {
   IterCfg cfg;
   AlphaCoef coef, coef_up;
   float lo_up, hi_up;
+  // inverse Newton (newton_p = p > 0): J = gram_j Krylov blocks and the
+  // objective of degree 2p built from coef_n
+  int newton_p, gram_j;
+  AlphaCoefN coef_n;
 };
 
 struct FormGParams {
@@ -94,6 +105,7 @@ struct FormGParams {
   const float* r2;       // R^2 (d >= 2), may alias dst
   const float* r3;       // R^3 (d = 3), may alias dst
   void* dst;             // fp32, or bf16 with dst_bf16
+  float* dst2;           // optional second fp32 copy (same layout)
   int64_t stride;        // elements, shared by r, r2 and dst
   int n, degree;
   int dst_bf16;

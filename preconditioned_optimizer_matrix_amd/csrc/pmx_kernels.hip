@@ -220,13 +220,13 @@ __device__ __forceinline__ void halve_reduce(float* acc, int lane) {
 // reads) and shared by the block's rows.  Each lane accumulates RW x Q
 // partial sums over its columns; the wave's recursive-halving reduction leaves
 // the complete sums spread over the lanes.
-// GJ > 0 (last Krylov pass, J <= GJ Krylov blocks): every block also adds its rows' share of the
+// GJ != 0 (last Krylov pass, J <= |GJ| Krylov blocks): every block also adds its rows' share of the
 // J x J Gram of K_1..K_J in fp64; the last block to arrive reduces the
 // shares in block order and solves for alpha.
 constexpr int SK_CH = 512;           // In rows per LDS chunk
 constexpr int SK_LD = SK_CH + 4;     // column stride of the staged chunk
 
-// Reduction, output and (GJ > 0) Gram share / alpha fit of a skinny product:
+// Reduction, output and (GJ != 0) Gram share / alpha fit of a skinny product:
 // acc holds the lane's RW x Q partial sums for rows row0 .. row0 + RW - 1.
 template <int Q, int RW, int GJ>
 __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const SkinnyParams& p,
@@ -254,13 +254,17 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     if (valid[i]) kb[(int64_t)vrow[i] * p.kld + job.out_col + c] = acc[i];
   }
 
-  if constexpr (GJ > 0) {
-    // the block's share of the Gram entries (a, bb), a <= bb < J <= GJ, of
-    // K_1..K_J, J = 2 d + 1 for the matrix's current degree d; this pass
-    // writes K_jo, the others are read back
+  if constexpr (GJ != 0) {
+    // the block's share of the Gram entries (a, bb), a <= bb < J <= |GJ|, of
+    // K_1..K_J, J = 2 d + 1 for the matrix's current degree d (gram_j when
+    // set); this pass writes K_jo, the others are read back.  GJ < 0: the
+    // inverse Newton objective (a separate instantiation: its solver's
+    // registers would lower the occupancy of every Gram pass)
+    constexpr bool NEWTON = GJ < 0;
+    constexpr int GA = NEWTON ? -GJ : GJ;
     const int deg = *(const volatile int32_t*)&cb->degree;
-    constexpr int NE = GJ * (GJ + 1) / 2;
-    const int J = 2 * deg + 1;
+    constexpr int NE = GA * (GA + 1) / 2;
+    const int J = p.gram_j ? p.gram_j : 2 * deg + 1;
     const int pp = p.cfg.p;
     const int jo = job.out_col / pp;
     double g[NE];
@@ -268,21 +272,21 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     for (int e = 0; e < NE; ++e) g[e] = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      double v[GJ];
+      double v[GA];
 #pragma unroll
-      for (int j = 0; j < GJ; ++j) v[j] = 0.0;
+      for (int j = 0; j < GA; ++j) v[j] = 0.0;
       if (valid[i]) {
 #pragma unroll
-        for (int j = 1; j <= GJ; ++j)
+        for (int j = 1; j <= GA; ++j)
           if (j <= J)
             v[j - 1] = j == jo ? (double)acc[i]
                                : (double)kb[(int64_t)vrow[i] * p.kld + j * pp + vcol[i]];
       }
       int t = 0;
 #pragma unroll
-      for (int a = 0; a < GJ; ++a)
+      for (int a = 0; a < GA; ++a)
 #pragma unroll
-        for (int bb = a; bb < GJ; ++bb, ++t) g[t] += v[a] * v[bb];
+        for (int bb = a; bb < GA; ++bb, ++t) g[t] += v[a] * v[bb];
     }
     // entries of (a, bb) with a <= bb < J, in row order, are packed first
     __shared__ double wsum[4][NE];
@@ -290,9 +294,9 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     {
       int t = 0, o = 0;
 #pragma unroll
-      for (int a = 0; a < GJ; ++a)
+      for (int a = 0; a < GA; ++a)
 #pragma unroll
-        for (int bb = a; bb < GJ; ++bb, ++t) {
+        for (int bb = a; bb < GA; ++bb, ++t) {
           const double sv = wave_sum(g[t]);
           if (a < J && bb < J) {
             if (lane == 0) wsum[wid][o] = sv;
@@ -331,8 +335,16 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     if (threadIdx.x == 0) {
       double phi = 0.0;
       const bool up = deg > p.cfg.degree;
-      const double alpha = alpha_from_gram(gsum, J, fro, up ? p.coef_up : p.coef,
-                                           up ? p.lo_up : p.cfg.lo, up ? p.hi_up : p.cfg.hi, &phi);
+      double alpha;
+      if constexpr (NEWTON) {
+        if (GA >= 9 && J == 9)
+          alpha = alpha_from_gram_newton<9, 5>(gsum, fro, p.coef_n, p.cfg.lo, p.cfg.hi, &phi);
+        else
+          alpha = alpha_from_gram_newton<5, 5>(gsum, fro, p.coef_n, p.cfg.lo, p.cfg.hi, &phi);
+      } else {
+        alpha = alpha_from_gram(gsum, J, fro, up ? p.coef_up : p.coef,
+                                up ? p.lo_up : p.cfg.lo, up ? p.hi_up : p.cfg.hi, &phi);
+      }
       cb->alpha = alpha;
       // adaptive degree: the sketch predicts ||R_{k+1} S|| / ||R_k S|| =
       // sqrt(phi_S(alpha)) / ||R S|| (gsum[0] = ||K_1||^2 of the scaled K_1 = R S / s)
@@ -640,6 +652,7 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   const float* R2 = p.r2 ? p.r2 + (int64_t)b * p.stride : nullptr;
   float* G = p.dst_bf16 ? nullptr : reinterpret_cast<float*>(p.dst) + (int64_t)b * p.stride;
   uint16_t* Gh = p.dst_bf16 ? reinterpret_cast<uint16_t*>(p.dst) + (int64_t)b * p.stride : nullptr;
+  float* G2 = p.dst2 ? p.dst2 + (int64_t)b * p.stride : nullptr;
   const float* R3 = p.r3 ? p.r3 + (int64_t)b * p.stride : nullptr;
   const float c0 = p.c0, c1 = p.c1, c2 = p.c2;
   const int deg = p.adaptive ? *(const volatile int32_t*)&cb->degree : p.degree;
@@ -676,6 +689,7 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
       } else {
         *reinterpret_cast<float4*>(G + e) = v;
       }
+      if (G2) *reinterpret_cast<float4*>(G2 + e) = v;
     }
     return;
   }
@@ -689,6 +703,7 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
     if (r == c) v += c0;
     if (Gh) Gh[e] = from_f32<bf16_t>(v).bits;
     else G[e] = v;
+    if (G2) G2[e] = v;
   }
 }
 
@@ -871,6 +886,10 @@ int skinny_blocks(int n, int q) {
 template <int Q, int RW, int GJ>
 static void skinny_go_j(const SkinnyParams& p, int njobs, int batch, hipStream_t s) {
   dim3 grid((p.n + 4 * RW - 1) / (4 * RW), njobs, batch);
+  if constexpr (GJ < 0) {
+    hipLaunchKernelGGL((skinny_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
+    return;
+  }
   if (p.variant == 1) {
     hipLaunchKernelGGL((skinny_stream_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
   } else if (p.variant == 2) {
@@ -882,13 +901,20 @@ static void skinny_go_j(const SkinnyParams& p, int njobs, int batch, hipStream_t
 }
 
 // Gram variants: J = 2d + 1 Krylov blocks, at most 5 (d <= 2) or 7 (d = 3);
-// the Gram pass is always a single q = p job (p <= PMX_MAX_SKETCH = 16).
+// the inverse Newton objective for p = 4 (J = 5 or 9) has variants of its
+// own.  The Gram pass is a single q = p job (p <= PMX_MAX_SKETCH = 16).
 template <int Q, int RW>
 static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
   if (!gram) skinny_go_j<Q, RW, 0>(p, njobs, batch, s);
   else if constexpr (Q <= 16) {
-    if (p.cfg.degree_max == 3) skinny_go_j<Q, RW, 7>(p, njobs, batch, s);
-    else skinny_go_j<Q, RW, 5>(p, njobs, batch, s);
+    if (p.newton_p == 4) {
+      if (p.gram_j > 5) skinny_go_j<Q, RW, -9>(p, njobs, batch, s);
+      else skinny_go_j<Q, RW, -5>(p, njobs, batch, s);
+    } else if (p.cfg.degree_max == 3 || p.gram_j > 5) {
+      skinny_go_j<Q, RW, 7>(p, njobs, batch, s);
+    } else {
+      skinny_go_j<Q, RW, 5>(p, njobs, batch, s);
+    }
   }
 }
 
@@ -916,7 +942,7 @@ hipError_t launch_form_g(const FormGParams& pin, int batch, hipStream_t s) {
   if ((p.degree == 3 || p.adaptive) && (!p.r2 || !p.r3)) return hipErrorInvalidValue;
   p.vec = (p.n % 4 == 0) && (p.stride % 4 == 0) && ((uintptr_t)p.r % 16 == 0) &&
           (!p.r2 || (uintptr_t)p.r2 % 16 == 0) && (!p.r3 || (uintptr_t)p.r3 % 16 == 0) &&
-          ((uintptr_t)p.dst % 16 == 0);
+          ((uintptr_t)p.dst % 16 == 0) && ((uintptr_t)p.dst2 % 16 == 0);
   const int per = (4096 + batch - 1) / batch;
   dim3 grid(grid_rows(p.n, per < 2048 ? per : 2048), batch);
   hipLaunchKernelGGL(form_g_kernel, grid, dim3(NT), 0, s, p);

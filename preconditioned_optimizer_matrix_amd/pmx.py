@@ -19,6 +19,7 @@ RUNNING, CONVERGED, MAXITER, STAGNATED, NONFINITE, DIVERGED = -1, 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 OP_STATS, OP_INV_ROOT, OP_POLAR, OP_APPLY = range(4)
 OPTS_VERSION = 3
+METHOD_NEWTON_SCHULZ, METHOD_INVERSE_NEWTON = 0, 1
 TRACE_LEN = 64
 MAX_SKETCH = 16
 STATUS_NAMES = {RUNNING: "RUNNING", CONVERGED: "CONVERGED", MAXITER: "MAXITER",
@@ -46,7 +47,7 @@ class Opts(ctypes.Structure):
                 ("alpha_hi", ctypes.c_float), ("tol", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("fp64_iters", ctypes.c_int32),
                 ("degree_max", ctypes.c_int32), ("adapt_ratio", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("method", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):

@@ -50,7 +50,7 @@ def test_host_only_calls():
     assert (o.degree, o.sketch_p, o.max_iter, o.accelerate) == (2, 8, 30, 1)
     assert math.isnan(o.alpha_lo) and math.isnan(o.alpha_hi)
     assert o.tol == pytest.approx(1e-6)
-    assert (o.fp64_iters, o.reserved, o.struct_version) == (0, 0, pmx.OPTS_VERSION)
+    assert (o.fp64_iters, o.method, o.struct_version) == (0, 0, pmx.OPTS_VERSION)
     assert o.degree_max == 0 and o.adapt_ratio == pytest.approx(0.3)
     assert pmx.lib.pmx_matfn_opts_default(None) == pmx.ERR_INVALID_VALUE
 
@@ -95,12 +95,16 @@ def test_workspace_sizes_and_option_validation():
     assert ws(alpha_lo=0.5, alpha_hi=0.5) == pmx.OK
     assert ws(fp64_iters=-1) == pmx.ERR_INVALID_VALUE
     assert ws(fp64_iters=31) == pmx.ERR_INVALID_VALUE  # more than max_iter
-    assert ws(reserved=1) == pmx.ERR_INVALID_VALUE
+    assert ws(method=2) == pmx.ERR_INVALID_VALUE
+    assert ws(method=1) == pmx.OK
+    assert ws(method=1, degree=3) == pmx.ERR_INVALID_VALUE
+    assert ws(method=1, fp64_iters=2) == pmx.ERR_INVALID_VALUE
+    assert ws(method=1, degree_max=3) == pmx.ERR_INVALID_VALUE
     assert ws(fp64_iters=4) == pmx.OK
     # the 40-byte version-1 layout is still accepted (fp64_iters = 0)
-    assert ws(struct_version=1, fp64_iters=7, reserved=5) == pmx.OK
+    assert ws(struct_version=1, fp64_iters=7, method=5) == pmx.OK
     # version 2 (48 bytes): the fields after degree_max are not read
-    assert ws(struct_version=2, adapt_ratio=float("nan"), reserved=5) == pmx.OK
+    assert ws(struct_version=2, adapt_ratio=float("nan"), method=5) == pmx.OK
     # adaptive degree: 2 -> 3 with the fitted alpha and fp32 updates only
     assert ws(degree_max=3) == pmx.OK
     assert ws(degree_max=2) == pmx.OK

@@ -10,6 +10,7 @@ import pytest
 
 import workloads as W
 from oracle import closed_form as cf
+from oracle import inv_newton as inw
 from oracle import prism
 
 pytestmark = pytest.mark.gpu
@@ -220,6 +221,53 @@ def test_adaptive_degree(env, p):
             pmx.polar(_bf16(torch, W.gaussian(64, 32, 5)).to(dev),
                       opts=pmx.default_opts(degree_max=3))
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("p", [2, 4])
+def test_inverse_newton(env, p):
+    # method 1: X <- X g, M <- g^p M with the PRISM alpha (degree-2p objective)
+    torch, pmx, dev = env
+    M1 = pmx.METHOD_INVERSE_NEWTON
+    for d in (1, 2):
+        for n in (64, 100, 256, 517):
+            _say("inverse newton", p, d, n)
+            A, _, _ = W.spd_logu(n, 7000 + n, 1e-3, 1.0)
+            X, XA, info = _run_root(env, A, p, method=M1, degree=d, seed=2, max_iter=40)
+            ref, ref_aux = cf.inv_root(A, p)
+            assert int(info[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), (d, n)
+            assert cf.rel_fro(X, ref) < 1e-4 and cf.rel_fro(XA, ref_aux) < 1e-4, (d, n)
+        # iteration counts, alphas and products against the oracle (same sketches)
+        A, _, _ = W.spd_logu(96, 77)
+        _say("inverse newton alpha trace", p, d)
+        X, XA, info = _run_root(env, A, p, method=M1, degree=d, seed=5, max_iter=40)
+        _, _, ref = inw.inv_root(A.astype(np.float64), p=p, d=d, max_iter=40,
+                                 sketch_fn=prism.make_sketch_fn(5, b=0, p=8))
+        inf, st = info[0], ref["stages"][0]
+        it = int(inf["iters"][0])
+        assert abs(it - st.iters) <= 1, (it, st.iters)
+        for k in range(min(it, st.iters)):
+            if st.r[k] >= 1e-3:
+                assert abs(inf["alpha"][0][k] - st.alpha[k]) < 1e-3, (d, k)
+                assert inf["rtrace"][0][k] == pytest.approx(st.r[k], rel=1e-3)
+        per = (d - 1) + (1 if p == 2 else 2) + 1
+        assert abs(int(inf["gemms"]) - st.gemms) <= per + 1
+    # the Taylor coefficient with d = 1 is the classical coupled inverse Newton
+    A, _, _ = W.spd_logu(80, 3, 1e-2, 1.0)
+    X, _, info = _run_root(env, A, p, method=M1, degree=1, accelerate=0, max_iter=60)
+    _, _, r = inw.inv_root(A.astype(np.float64), p=p, d=1, accelerate=False, max_iter=60)
+    assert cf.rel_fro(X, cf.inv_root(A, p)[0]) < 1e-4
+    assert abs(int(info[0]["iters"][0]) - r["stages"][0].iters) <= 1
+    # batched, and a non-finite input
+    As = np.stack([W.spd_logu(200, 80 + b, 10.0 ** -(b + 1), 1.0)[0] for b in range(3)])
+    As[2, 5, 7] = np.nan
+    Xb, _, infb = pmx.inv_root(torch.from_numpy(As).to(dev), p,
+                               opts=pmx.default_opts(method=M1))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(infb)
+    for b in range(2):
+        assert cf.rel_fro(Xb[b].cpu().numpy(), cf.inv_root(As[b], p)[0]) < 1e-4, b
+    assert int(inf[2]["status"]) == pmx.NONFINITE
+    assert np.all(np.isnan(Xb[2].cpu().numpy()))
 
 
 def test_inv_root_batched(env):
