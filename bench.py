@@ -410,12 +410,34 @@ def main():
     cols = torch.arange(0, n, n // 8, device=dev)
     E = torch.zeros(n, len(cols), dtype=torch.float64, device=dev)
     E[cols, torch.arange(len(cols), device=dev)] = 1.0
-    V = R.double() @ E
-    Xd = Ri.double()
-    for _ in range(4):
-        V = Xd @ V
-    prop = float((V - E).norm(dim=0).max())
+
+    def prop_of(Xr):
+        V = R.double() @ E
+        Xd = Xr.double()
+        for _ in range(4):
+            V = Xd @ V
+        return float((V - E).norm(dim=0).max())
+
+    prop = prop_of(Ri)
     log("max_j ||R^{-1/4}^4 R e_j - e_j|| over 8 sampled columns: %.2e" % prop)
+
+    # the other inverse-root family on the same R: the coupled inverse Newton
+    # iteration (method 1), timed the same way
+    newton = None
+    if args.method == 0:
+        oN = pmx.default_opts(max_iter=args.max_iter, method=1)
+        wsN = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, oN), dev)
+        infoN = pmx.new_info(1, dev)
+        XN = torch.empty_like(R)
+        fnN = lambda: pmx.inv_root(R, 4, opts=oN, aux=False, out=XN, info=infoN, ws=wsN)
+        msN = timed(torch, fnN, args.steps, args.warmup)
+        iN = pmx.parse_info(infoN)[0]
+        newton = dict(ms=round(msN, 3), gemms=int(iN["gemms"]), iters=int(iN["iters"][0]),
+                      status=pmx.STATUS_NAMES[int(iN["status"])],
+                      tflops_launched=round(root_exec_flops(n, 1, iN["iters"], iN["gemms"], 1)
+                                            / (msN * 1e-3) / 1e12, 2),
+                      property_x4r_minus_i=prop_of(XN))
+        log("inverse Newton R^-1/4:", newton)
 
     roofline = None
     trace = None
@@ -476,6 +498,7 @@ def main():
         "mfma_frac_r_root": round(tflops_r / PEAK_FP32_MFMA, 4),
         "dense_equiv_tflops_r_root": round(dense_tflops_r, 2),
         "property_x4r_minus_i": prop,
+        "inverse_newton_r_root": newton,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
