@@ -76,7 +76,8 @@ typedef enum {
   PMX_OP_STATS = 0,
   PMX_OP_INV_ROOT = 1,
   PMX_OP_POLAR = 2,
-  PMX_OP_APPLY = 3
+  PMX_OP_APPLY = 3,
+  PMX_OP_POLAR_VARBATCH = 4  /* batch = number of blocks; m, n ignored */
 } pmx_op;
 
 /*
@@ -234,6 +235,36 @@ pmx_status pmx_matfn_polar_batched(pmx_handle handle, const void* G, pmx_dtype d
                                    int ldu, int64_t stride_u, int batch,
                                    const pmx_matfn_opts* opts, pmx_matfn_info* info_dev,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Polar factors of many small blocks of different shapes in one launch (the
+ * per-block orthogonalisation of block-diagonal preconditioners; [PRISM
+ * synthesis] Part I, sign/polar functions).  Each block is iterated as in
+ * pmx_matfn_polar, fp32 arithmetic throughout (bf16 blocks are widened on
+ * load and rounded to nearest even on store), one workgroup per block with
+ * the whole iteration in LDS.
+ *   blocks: HOST array of `count` descriptors; every one is checked before
+ *           anything is enqueued (1 <= m, n <= PMX_VARBATCH_MAX_DIM, ldg >= n,
+ *           ldu >= n, non-null pointers, output not overlapping its input),
+ *           then copied into the workspace on `stream`; the array may be
+ *           reused once the call returns.
+ *   info_dev: `count` pmx_matfn_info (may be NULL), in block order.
+ *   opts: degree 1 or 2 (fixed), fp32 iterates; method and fp64_iters are
+ *         ignored.  Workspace: pmx_workspace_size(PMX_OP_POLAR_VARBATCH, batch
+ *         = count).  dtype applies to every block.
+ */
+#define PMX_VARBATCH_MAX_DIM 64
+typedef struct {
+  const void* g; /* device pointer: the m x n block, row-major, leading dimension ldg */
+  void* u;       /* device pointer: its polar factor, m x n, leading dimension ldu */
+  int32_t m, n;
+  int32_t ldg, ldu;
+} pmx_polar_block;
+
+pmx_status pmx_matfn_polar_varbatch(pmx_handle handle, const pmx_polar_block* blocks, int count,
+                                    pmx_dtype dtype, const pmx_matfn_opts* opts,
+                                    pmx_matfn_info* info_dev, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * Preconditioned step ([Shampoo blog] sections 2.1 and 2.3, step 4):

@@ -904,6 +904,10 @@ pmx_status pmx_workspace_size(pmx_handle h, pmx_op op, int m, int n, int batch,
       if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
       *bytes = polar_ws(m, n, batch, o, dtype);
       return PMX_OK;
+    case PMX_OP_POLAR_VARBATCH:
+      // the device copy of the block descriptors
+      *bytes = align_up(sizeof(pmx_polar_block) * (size_t)batch);
+      return PMX_OK;
   }
   return PMX_ERR_INVALID_VALUE;
 }
@@ -1586,6 +1590,57 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   fp.u_stride = su;
   fp.ctrl = ctrl;
   PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_polar_finish(fp, bf, batch, q.s); }));
+  return PMX_OK;
+}
+
+// ------------------------------------------------------------------ variable-size polar
+pmx_status pmx_matfn_polar_varbatch(pmx_handle h, const pmx_polar_block* blocks, int count,
+                                    pmx_dtype dtype, const pmx_matfn_opts* opts,
+                                    pmx_matfn_info* info, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (!h || !blocks || count < 1) return PMX_ERR_INVALID_VALUE;
+  if (dtype != PMX_F32 && dtype != PMX_BF16) return PMX_ERR_INVALID_VALUE;
+  pmx_matfn_opts o;
+  if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
+  if (std::max(o.degree, o.degree_max) > 2) return PMX_ERR_NOT_SUPPORTED;
+  const int esz = dtype == PMX_BF16 ? 2 : 4;
+  const size_t need = align_up(sizeof(pmx_polar_block) * (size_t)count);
+  pmx_status st = check_ws(ws, ws_bytes, need);
+  if (st != PMX_OK) return st;
+  Extent ew;
+  ew.lo = (uintptr_t)ws;
+  ew.hi = ew.lo + need;
+  ew.valid = true;
+  const Extent ei =
+      extent_of(info, 1, (int)sizeof(pmx_matfn_info), 0, sizeof(pmx_matfn_info), count, 1);
+  if (overlap(ei, ew)) return PMX_ERR_ALIAS;
+  for (int i = 0; i < count; ++i) {
+    const pmx_polar_block& bl = blocks[i];
+    if (!bl.g || !bl.u || bl.m < 1 || bl.n < 1 || bl.m > PMX_VARBATCH_MAX_DIM ||
+        bl.n > PMX_VARBATCH_MAX_DIM || bl.ldg < bl.n || bl.ldu < bl.n)
+      return PMX_ERR_INVALID_VALUE;
+    const Extent eg = extent_of(bl.g, bl.m, bl.n, bl.ldg, 0, 1, esz);
+    const Extent eu = extent_of(bl.u, bl.m, bl.n, bl.ldu, 0, 1, esz);
+    if (overlap(eg, eu) || overlap(eu, ew) || overlap(eg, ew) || overlap(eu, ei))
+      return PMX_ERR_ALIAS;
+  }
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return PMX_ERR_HIP;
+  Enq q{h, (hipStream_t)stream};
+  // descriptors to the device on the call's stream (staged from host memory
+  // before the copy call returns)
+  if (hipMemcpyAsync(ws, blocks, sizeof(pmx_polar_block) * (size_t)count, hipMemcpyHostToDevice,
+                     q.s) != hipSuccess)
+    return PMX_ERR_HIP;
+  SmallPolarParams sp;
+  memset(&sp, 0, sizeof(sp));
+  sp.blocks = reinterpret_cast<const pmx_polar_block*>(ws);
+  sp.bf16 = dtype == PMX_BF16;
+  sp.c0 = (float)taylor(0);
+  sp.c1 = (float)taylor(1);
+  sp.cfg = make_cfg(o, PMX_VARBATCH_MAX_DIM, info);
+  sp.coef = make_coef(o.degree);
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_small_polar(sp, count, q.s); }));
   return PMX_OK;
 }
 

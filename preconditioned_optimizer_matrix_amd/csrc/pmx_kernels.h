@@ -188,6 +188,10 @@ struct SmallPolarParams {
   float c0, c1;
   IterCfg cfg;
   AlphaCoef coef;
+  // variable shapes: block b is blocks[b] (its own pointers, shape and
+  // leading dimensions; g, u, rows, cols and transpose above are unused)
+  const pmx_polar_block* blocks;
+  int bf16;  // elements of G and U are bf16 (fp32 inside)
 };
 
 hipError_t launch_small_root(const SmallRootParams& p, int batch, hipStream_t s);

@@ -392,10 +392,28 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SmallShared& sh = *reinterpret_cast<SmallShared*>(smem_raw);
   const int b = blockIdx.x;
-  const int rows = p.rows, cols = p.cols;  // the iterate X is rows x cols, rows >= cols
+  // the iterate X is rows x cols, rows >= cols (G^T when transpose)
+  int rows = p.rows, cols = p.cols, transpose = p.transpose;
+  const void* G = p.g + (int64_t)b * p.g_stride;
+  void* Uo = p.u + (int64_t)b * p.u_stride;
+  int64_t ldg = p.ldg, ldu = p.ldu;
+  if (p.blocks) {
+    const pmx_polar_block blk = p.blocks[b];
+    transpose = blk.m < blk.n;
+    rows = transpose ? blk.n : blk.m;
+    cols = transpose ? blk.m : blk.n;
+    G = blk.g;
+    Uo = blk.u;
+    ldg = blk.ldg;
+    ldu = blk.ldu;
+  }
+  auto load = [&](int64_t e) {
+    return p.bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(G)[e] << 16)
+                  : reinterpret_cast<const float*>(G)[e];
+  };
   IterCfg cfg = p.cfg;
+  cfg.n = cols;  // r_k = ||R_k||_F / sqrt(cols), per block
   if (cfg.info) cfg.info += b;
-  const float* G = p.g + (int64_t)b * p.g_stride;
   float* X = sh.m[0];
   float* Xn = sh.m[1];
   float* R = sh.m[4];
@@ -404,8 +422,7 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
   for (int e = threadIdx.x; e < SN * SN; e += SNT) {
     const int i = e >> 6, j = e & 63;
     float v = 0.f;
-    if (i < rows && j < cols)
-      v = p.transpose ? G[(int64_t)j * p.ldg + i] : G[(int64_t)i * p.ldg + j];
+    if (i < rows && j < cols) v = transpose ? load((int64_t)j * ldg + i) : load((int64_t)i * ldg + j);
     X[i * SLD + j] = v;
     acc += (double)v * (double)v;
   }
@@ -449,12 +466,15 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
   }
   const int st = sh.c.status_all;
   const bool bad = (st == PMX_NONFINITE || st == PMX_DIVERGED);
-  float* U = p.u + (int64_t)b * p.u_stride;
   for (int e = threadIdx.x; e < rows * cols; e += SNT) {
     const int i = e / cols, j = e - (e / cols) * cols;
     const float v = bad ? NAN : X[i * SLD + j];
-    if (p.transpose) U[(int64_t)j * p.ldu + i] = v;
-    else U[(int64_t)i * p.ldu + j] = v;
+    const int64_t o = transpose ? (int64_t)j * ldu + i : (int64_t)i * ldu + j;
+    if (p.bf16) {
+      reinterpret_cast<uint16_t*>(Uo)[o] = from_f32<bf16_t>(v).bits;  // nearest even
+    } else {
+      reinterpret_cast<float*>(Uo)[o] = v;
+    }
   }
 }
 

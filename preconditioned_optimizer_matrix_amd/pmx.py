@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libpmx.so")
 OK, ERR_INVALID_VALUE, ERR_NOT_SUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(6)
 RUNNING, CONVERGED, MAXITER, STAGNATED, NONFINITE, DIVERGED = -1, 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-OP_STATS, OP_INV_ROOT, OP_POLAR, OP_APPLY = range(4)
+OP_STATS, OP_INV_ROOT, OP_POLAR, OP_APPLY, OP_POLAR_VARBATCH = range(5)
+VARBATCH_MAX_DIM = 64
 OPTS_VERSION = 3
 METHOD_NEWTON_SCHULZ, METHOD_INVERSE_NEWTON = 0, 1
 TRACE_LEN = 64
@@ -30,7 +31,7 @@ EXPORTS = [
     "pmx_matfn_opts_default", "pmx_workspace_size",
     "pmx_shampoo_stats_update", "pmx_shampoo_stats_update_batched",
     "pmx_matfn_inv_root", "pmx_matfn_inv_root_batched",
-    "pmx_matfn_polar", "pmx_matfn_polar_batched",
+    "pmx_matfn_polar", "pmx_matfn_polar_batched", "pmx_matfn_polar_varbatch",
     "pmx_precond_apply", "pmx_precond_apply_batched",
     "pmx_trace_enable", "pmx_trace_collect",
 ]
@@ -48,6 +49,11 @@ class Opts(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("fp64_iters", ctypes.c_int32),
                 ("degree_max", ctypes.c_int32), ("adapt_ratio", ctypes.c_float),
                 ("method", ctypes.c_int32)]
+
+
+class PolarBlock(ctypes.Structure):
+    _fields_ = [("g", ctypes.c_void_p), ("u", ctypes.c_void_p), ("m", ctypes.c_int32),
+                ("n", ctypes.c_int32), ("ldg", ctypes.c_int32), ("ldu", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):
@@ -96,6 +102,8 @@ def _load():
         "pmx_matfn_polar_batched": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _i32,
                                            _i64, _i32, ctypes.POINTER(Opts), _vp, _vp, _sz,
                                            _vp]),
+        "pmx_matfn_polar_varbatch": (_i32, [_vp, ctypes.POINTER(PolarBlock), _i32, _i32,
+                                            ctypes.POINTER(Opts), _vp, _vp, _sz, _vp]),
         "pmx_precond_apply": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _i32,
                                      _vp, _i32, _vp, _sz, _vp]),
         "pmx_precond_apply_batched": (_i32, [_vp, _vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32,
@@ -289,6 +297,33 @@ def polar(G, opts=None, out=None, info=None, ws=None):
         handle(G.device.index), _ptr(G), dt, m, n, ldg, sg, _ptr(U), ldu, su, batch,
         ctypes.byref(opts), _ptr(info), _ptr(ws), ws.numel(), _stream(G)), "matfn_polar")
     return U, info
+
+
+def polar_varbatch(Gs, opts=None, outs=None, info=None, ws=None):
+    """Polar factors of a list of 2-D blocks of different shapes (each at most
+    VARBATCH_MAX_DIM on a side, one dtype), in one launch; returns
+    (list of U, info_tensor)."""
+    torch = _torch()
+    if opts is None:
+        opts = default_opts()
+    Us = outs if outs is not None else [torch.empty_like(g, memory_format=torch.contiguous_format)
+                                        for g in Gs]
+    count = len(Gs)
+    arr = (PolarBlock * count)()
+    for i, (g, u) in enumerate(zip(Gs, Us)):
+        m, n, ldg, _, _ = _mat(g)
+        _, _, ldu, _, _ = _mat(u)
+        arr[i] = PolarBlock(_ptr(g), _ptr(u), m, n, ldg, ldu)
+    dev = Gs[0].device
+    if info is None:
+        info = new_info(count, dev)
+    need = workspace_bytes(OP_POLAR_VARBATCH, 1, 1, count, _dtype_code(Gs[0]), opts)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, dev)
+    check(lib.pmx_matfn_polar_varbatch(handle(dev.index), arr, count, _dtype_code(Gs[0]),
+                                       ctypes.byref(opts), _ptr(info), _ptr(ws), ws.numel(),
+                                       _stream(Gs[0])), "matfn_polar_varbatch")
+    return Us, info
 
 
 def precond_apply(Linv, G, Rinv, out=None, ws=None):

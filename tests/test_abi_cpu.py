@@ -67,6 +67,9 @@ def test_workspace_sizes_and_option_validation():
     bb = pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 64, pmx.F32, o)
     assert bb >= 64 * 6 * 4 * 512 * 512
     assert pmx.workspace_bytes(pmx.OP_STATS, 1024, 4096, 1, pmx.F32, None) == 0
+    # variable-size polar: the descriptors (32 bytes each), 256-byte aligned
+    assert ctypes.sizeof(pmx.PolarBlock) == 32
+    assert pmx.workspace_bytes(pmx.OP_POLAR_VARBATCH, 1, 1, 100, pmx.F32, None) == 3328
     assert pmx.workspace_bytes(pmx.OP_APPLY, 1024, 4096, 1, pmx.F32, None) >= 4 * 1024 * 4096
     pb = pmx.workspace_bytes(pmx.OP_POLAR, 4096, 1024, 1, pmx.F32, o)
     assert pb >= 2 * 4 * 4096 * 1024 + 2 * 4 * 1024 * 1024

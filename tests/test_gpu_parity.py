@@ -270,6 +270,49 @@ def test_inverse_newton(env, p):
     assert np.all(np.isnan(Xb[2].cpu().numpy()))
 
 
+def test_polar_varbatch(env):
+    # many small blocks of different shapes (tall, wide, square, 1 x 1, the
+    # 64 limit) in one fused launch, against the SVD polar factor and, for a
+    # few blocks, the oracle's iteration with the block's own sketch stream
+    torch, pmx, dev = env
+    rng = np.random.default_rng(44)
+    shapes = [(1, 1), (64, 64), (64, 1), (1, 64), (3, 5), (40, 17), (17, 40)]
+    shapes += [tuple(int(x) for x in rng.integers(1, 65, 2)) for _ in range(33)]
+    Gs = [W.gaussian(m, n, 100 + i) for i, (m, n) in enumerate(shapes)]
+    _say("polar varbatch fp32", len(Gs))
+    Us, info = pmx.polar_varbatch([torch.from_numpy(g).to(dev) for g in Gs],
+                                  opts=pmx.default_opts(seed=9))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)
+    for i, (g, u) in enumerate(zip(Gs, Us)):
+        assert int(inf[i]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), (i, shapes[i])
+        assert cf.rel_fro(u.cpu().numpy(), cf.polar(g)[0]) < 1e-4, (i, shapes[i])
+    for i in (1, 5, 6):
+        _, ref = prism.polar(Gs[i].astype(np.float64), sketch_fn=prism.make_sketch_fn(9, b=i, p=8))
+        st = ref["stages"][0]
+        assert abs(int(inf[i]["iters"][0]) - st.iters) <= 1
+        for k in range(min(int(inf[i]["iters"][0]), st.iters)):
+            if st.r[k] >= 1e-3:
+                assert abs(inf[i]["alpha"][0][k] - st.alpha[k]) < 1e-3, (i, k)
+    # bf16 blocks: fp32 inside, the factor rounded once on store
+    Gb = [_bf16(torch, g).to(dev) for g in Gs[:12]]
+    Ub, _ = pmx.polar_varbatch(Gb)
+    torch.cuda.synchronize()
+    for g, u in zip(Gb, Ub):
+        gq = g.float().cpu().numpy()
+        assert cf.rel_fro(u.float().cpu().numpy(), cf.polar(gq)[0]) < 1e-2
+    # argument errors: a block above the limit, an output overlapping its input
+    big = torch.zeros(65, 8, device=dev)
+    with pytest.raises(pmx.PmxError):
+        pmx.polar_varbatch([torch.from_numpy(Gs[0]).to(dev), big])
+    g0 = torch.from_numpy(Gs[5]).to(dev)
+    with pytest.raises(pmx.PmxError):
+        pmx.polar_varbatch([g0], outs=[g0])
+    with pytest.raises(pmx.PmxError):
+        pmx.polar_varbatch([g0], opts=pmx.default_opts(degree=3))
+    torch.cuda.synchronize()
+
+
 def test_inv_root_batched(env):
     torch, pmx, dev = env
     _say("batched inv_root")
