@@ -24,6 +24,9 @@ Modules
   inv_newton   -- the coupled inverse Newton iteration for A^{-1/p} with the
                   PRISM coefficient (residual map 1 - (1 - xi) g^p, an objective
                   of degree 2p in alpha).
+  shampoo_step -- a whole Shampoo step over a model's layers (block-diagonal
+                  statistics, roots every k steps, momentum, adaptive rate,
+                  convolution reshape), from the closed forms.
   interval     -- the [lo, hi] interval rule for the adaptive coefficient.
   eigen_model  -- the same iteration on a known spectrum (scalar map), an
                   independent route to iteration counts and alpha.
