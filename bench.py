@@ -52,7 +52,8 @@ def parse():
                          "--calibrate-copy)")
     ap.add_argument("--workload", default="shampoo_1024x4096",
                     choices=["shampoo_1024x4096", "spd_64", "blocks_64x512",
-                             "muon_32x4096x1024", "mp_10000"])
+                             "muon_32x4096x1024", "mp_10000", "varblocks_4096",
+                             "model_step"])
     return ap.parse_args()
 
 
@@ -159,6 +160,56 @@ def other_workload(args):
                          "iters": [int(x) for x in info["iters"]]}
         out.update(metric="us per matrix function (n=64)", value=res["inv_root_p4"]["us"],
                    unit="us", dtype="f32", config={"workload": wl}, calls=res)
+    elif wl == "model_step":
+        # a whole Shampoo step over a synthetic model: four 1024 x 4096 and
+        # four 4096 x 1024 dense layers and two 256 x 128 x 3 x 3 convolution
+        # kernels, blocks of 1024, gradients N(0, 1e-2) (seed 701); roots
+        # every step and every 10 steps (momentum 0.9)
+        shapes = [(1024, 4096)] * 4 + [(4096, 1024)] * 4 + [(256, 128, 3, 3)] * 2
+        rng = np.random.default_rng(701)
+        Ws = [torch.from_numpy(rng.standard_normal(s).astype(np.float32)).to(dev) for s in shapes]
+        Gs = [torch.from_numpy((0.1 * rng.standard_normal(s)).astype(np.float32)).to(dev)
+              for s in shapes]
+        res = {}
+        for every in (1, 10):
+            cfg = pmx.shampoo_config(block=1024, root_every=every, momentum=0.9,
+                                     root_opts=pmx.default_opts(max_iter=args.max_iter,
+                                                                method=args.method))
+            plan = pmx.ShampooPlan(shapes, dev, cfg)
+            t = [0]
+
+            def one():
+                plan.step(Ws, Gs, t[0])
+                t[0] += 1
+            n_steps = max(args.steps, every)
+            ms = timed(torch, one, n_steps, max(args.warmup, 1))
+            res["root_every_%d" % every] = round(ms, 3)
+            del plan
+        params = sum(int(np.prod(s)) for s in shapes)
+        out.update(metric="ms per Shampoo step over a 10-layer model (blocks of 1024)",
+                   value=res["root_every_1"], unit="ms", dtype="f32",
+                   config={"workload": wl, "layers": [list(s) for s in shapes], "block": 1024,
+                           "momentum": 0.9, "method": args.method},
+                   ms_per_step=res, parameters=params)
+    elif wl == "varblocks_4096":
+        # 4096 Gaussian blocks with sides uniform in [8, 64] (seed 601), fp32,
+        # polar factors in one variable-size call
+        Gs = [torch.from_numpy(g).to(dev) for g in W.irregular_blocks(4096, 601)]
+        Us = [torch.empty_like(g) for g in Gs]
+        info = pmx.new_info(len(Gs), dev)
+        ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_POLAR_VARBATCH, 1, 1, len(Gs)), dev)
+        fn = lambda o: pmx.polar_varbatch(Gs, opts=o, outs=Us, info=info, ws=ws)
+        ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
+        inf = pmx.parse_info(info)
+        flops = sum(2.0 * max(g.shape) * min(g.shape) ** 2 * (2 * int(i) + 1) +
+                    2.0 * min(g.shape) ** 3 * int(i) for g, i in zip(Gs, inf["iters"][:, 0]))
+        out.update(metric="ms per variable-size batched polar (4096 blocks, sides 8..64)",
+                   value=round(ms, 3), unit="ms", dtype="f32", config={"workload": wl},
+                   blocks_per_s=round(len(Gs) / (ms * 1e-3), 1),
+                   iters_mean=round(float(inf["iters"][:, 0].mean()), 2),
+                   status_counts={pmx.STATUS_NAMES[int(k)]: int(v) for k, v in
+                                  zip(*np.unique(inf["status"], return_counts=True))},
+                   tflops=round(flops / (ms * 1e-3) / 1e12, 2))
     elif wl == "blocks_64x512":
         # fp32 throughout, and with the first four updates of each stage in
         # fp64 (the setting that meets 1e-4 at kappa = 1e6); value is the latter

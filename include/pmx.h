@@ -283,6 +283,64 @@ pmx_status pmx_precond_apply_batched(pmx_handle handle, const float* Linv, int l
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * A whole Shampoo optimizer step over the layers of a model ([Shampoo blog]
+ * sections 2.3 and 6.3 for the step, 3.2 for the block-diagonal
+ * approximation, 5.1 for the adaptive learning rate, 5.2 for momentum, 5.3
+ * for convolution kernels):
+ *   every layer's gradient is viewed as a matrix (a c_out x c_in x kh x kw
+ *   kernel as the (c_out kh kw) x c_in matrix K'[(o kh + y) kw + x][i] =
+ *   K[o][i][y][x]) and cut into blocks of at most block x block; each block
+ *   is a parameter of its own with statistics L, R, momentum M and roots;
+ *   per step t (counted by the caller from 0):
+ *     L <- beta L + (1 - beta) G G^T + eps I,  R likewise       (every block)
+ *     L^{-1/4}, R^{-1/4} recomputed when t % root_every == 0 (kept otherwise)
+ *     P = L^{-1/4} G R^{-1/4},  M <- momentum M + P  (M = P when momentum = 0)
+ *     W <- W - eta_t M,  eta_t = lr, or with adaptive_lr
+ *     eta_t = lr / sqrt(1 + sum_{i <= t} ||G_i||_F^2) (the sum over all layers).
+ * Blocks of equal shape are processed as one batch in every call above; the
+ * plan groups them once.  All device memory is the caller's: `state`
+ * (statistics, roots, momentum, the running gradient norm; kept between
+ * steps, set up by pmx_shampoo_plan_init) and `workspace` (per step).
+ */
+typedef struct {
+  int32_t struct_version;   /* 1 */
+  int32_t block;            /* largest block side, 1..PMX_MAX_N; default 1024 */
+  int32_t root_every;       /* >= 1; default 1 */
+  int32_t adaptive_lr;      /* 0 or 1; default 0 */
+  float beta, eps;          /* defaults 0.95, 1e-6 */
+  float lr, momentum;       /* defaults 1e-3, 0 */
+  pmx_matfn_opts root_opts; /* options of the inverse 4th roots (defaults) */
+} pmx_shampoo_config;
+
+typedef struct {
+  int32_t dims;     /* 2: shape[0] x shape[1] row-major; 4: c_out x c_in x kh x kw */
+  int32_t shape[4];
+} pmx_layer;
+
+typedef struct pmx_shampoo_plan_t* pmx_shampoo_plan;
+
+/* Fill `cfg` with the defaults above. */
+pmx_status pmx_shampoo_config_default(pmx_shampoo_config* cfg);
+/* Block and group the layers (host only; no device memory). */
+pmx_status pmx_shampoo_plan_create(pmx_handle handle, const pmx_shampoo_config* cfg,
+                                   const pmx_layer* layers, int nlayers,
+                                   pmx_shampoo_plan* plan);
+pmx_status pmx_shampoo_plan_destroy(pmx_shampoo_plan plan);
+/* Bytes of the persistent state and of the per-step workspace. */
+pmx_status pmx_shampoo_plan_sizes(pmx_shampoo_plan plan, size_t* state_bytes,
+                                  size_t* workspace_bytes);
+/* Enqueue the state's set-up on `stream`: L = R = eps I, M = 0, the running
+ * norm 0, and the block tables. */
+pmx_status pmx_shampoo_plan_init(pmx_shampoo_plan plan, void* state, size_t state_bytes,
+                                 void* stream);
+/* One step: W[l] and G[l] are device pointers to layer l's weight and
+ * gradient (fp32, the layer's natural layout); the HOST arrays W and G may be
+ * reused once the call returns (they are copied into the workspace). */
+pmx_status pmx_shampoo_plan_step(pmx_shampoo_plan plan, float* const* W, const float* const* G,
+                                 int64_t step, void* state, size_t state_bytes, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Launch trace for benchmarking.  While enabled, every kernel that a call on
  * this handle enqueues is bracketed by a pair of HIP events recorded on the
  * call's stream (host-side event objects owned by the handle; no device

@@ -733,6 +733,9 @@ pmx_status enqueue_inverse_newton(Enq& q, void* ws, const IterLayout& L, const p
 }
 
 }  // namespace
+
+int handle_device(pmx_handle h) { return h ? h->device : -1; }
+
 }  // namespace pmx
 
 using namespace pmx;

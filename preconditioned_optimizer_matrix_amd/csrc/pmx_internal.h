@@ -286,6 +286,9 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s);
+
+// The HIP device a handle is bound to (-1 for a null handle).
+int handle_device(pmx_handle h);
 int gemm_f32_tiles(int M, int N);
 
 }  // namespace pmx

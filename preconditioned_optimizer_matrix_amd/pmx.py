@@ -34,6 +34,8 @@ EXPORTS = [
     "pmx_matfn_polar", "pmx_matfn_polar_batched", "pmx_matfn_polar_varbatch",
     "pmx_precond_apply", "pmx_precond_apply_batched",
     "pmx_trace_enable", "pmx_trace_collect",
+    "pmx_shampoo_config_default", "pmx_shampoo_plan_create", "pmx_shampoo_plan_destroy",
+    "pmx_shampoo_plan_sizes", "pmx_shampoo_plan_init", "pmx_shampoo_plan_step",
 ]
 
 # kernel classes of the launch trace (pmx_kernel_class)
@@ -49,6 +51,17 @@ class Opts(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("fp64_iters", ctypes.c_int32),
                 ("degree_max", ctypes.c_int32), ("adapt_ratio", ctypes.c_float),
                 ("method", ctypes.c_int32)]
+
+
+class ShampooConfig(ctypes.Structure):
+    _fields_ = [("struct_version", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("root_every", ctypes.c_int32), ("adaptive_lr", ctypes.c_int32),
+                ("beta", ctypes.c_float), ("eps", ctypes.c_float), ("lr", ctypes.c_float),
+                ("momentum", ctypes.c_float), ("root_opts", Opts)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("dims", ctypes.c_int32), ("shape", ctypes.c_int32 * 4)]
 
 
 class PolarBlock(ctypes.Structure):
@@ -110,6 +123,16 @@ def _load():
                                              _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32, _vp,
                                              _sz, _vp]),
         "pmx_trace_enable": (_i32, [_vp, _i32]),
+        "pmx_shampoo_config_default": (_i32, [ctypes.POINTER(ShampooConfig)]),
+        "pmx_shampoo_plan_create": (_i32, [_vp, ctypes.POINTER(ShampooConfig),
+                                           ctypes.POINTER(Layer), _i32,
+                                           ctypes.POINTER(ctypes.c_void_p)]),
+        "pmx_shampoo_plan_destroy": (_i32, [_vp]),
+        "pmx_shampoo_plan_sizes": (_i32, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+        "pmx_shampoo_plan_init": (_i32, [_vp, _vp, _sz, _vp]),
+        "pmx_shampoo_plan_step": (_i32, [_vp, ctypes.POINTER(ctypes.c_void_p),
+                                         ctypes.POINTER(ctypes.c_void_p), _i64, _vp, _sz, _vp,
+                                         _sz, _vp]),
         "pmx_trace_collect": (_i32, [_vp, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]),
     }
@@ -169,6 +192,11 @@ def handle(device=None):
 def _stream(t):
     torch = _torch()
     return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _stream_of(device):
+    torch = _torch()
+    return _vp(torch.cuda.current_stream(device).cuda_stream)
 
 
 def _dtype_code(t):
@@ -324,6 +352,73 @@ def polar_varbatch(Gs, opts=None, outs=None, info=None, ws=None):
                                        ctypes.byref(opts), _ptr(info), _ptr(ws), ws.numel(),
                                        _stream(Gs[0])), "matfn_polar_varbatch")
     return Us, info
+
+
+def shampoo_config(root_opts=None, **kw):
+    """pmx_shampoo_config with the library defaults, fields overridden by kw."""
+    c = ShampooConfig()
+    check(lib.pmx_shampoo_config_default(ctypes.byref(c)), "shampoo_config_default")
+    for k, v in kw.items():
+        if not hasattr(c, k):
+            raise KeyError(k)
+        setattr(c, k, v)
+    if root_opts is not None:
+        c.root_opts = root_opts
+    return c
+
+
+def _layer(shape):
+    ly = Layer()
+    ly.dims = len(shape)
+    if ly.dims not in (2, 4):
+        # passed on: the library rejects it (PMX_ERR_INVALID_VALUE)
+        return ly
+    for i, v in enumerate(shape[:4]):
+        ly.shape[i] = int(v)
+    return ly
+
+
+class ShampooPlan:
+    """A whole Shampoo step over a list of layer shapes (2-D or 4-D), with its
+    device state and workspace (torch tensors on `device`)."""
+
+    def __init__(self, shapes, device, config=None):
+        torch = _torch()
+        self.device = torch.device(device)
+        self.config = config if config is not None else shampoo_config()
+        arr = (Layer * len(shapes))(*[_layer(s) for s in shapes])
+        self.nlayers = len(shapes)
+        plan = ctypes.c_void_p()
+        check(lib.pmx_shampoo_plan_create(handle(self.device.index), ctypes.byref(self.config),
+                                          arr, len(shapes), ctypes.byref(plan)),
+              "shampoo_plan_create")
+        self.plan = plan
+        sb, wb = _sz(), _sz()
+        check(lib.pmx_shampoo_plan_sizes(plan, ctypes.byref(sb), ctypes.byref(wb)),
+              "shampoo_plan_sizes")
+        self.state = workspace(sb.value, self.device)
+        self.ws = workspace(wb.value, self.device)
+        check(lib.pmx_shampoo_plan_init(plan, _ptr(self.state), self.state.numel(),
+                                        _stream_of(self.device)), "shampoo_plan_init")
+
+    def step(self, Ws, Gs, t):
+        if len(Ws) != self.nlayers or len(Gs) != self.nlayers:
+            raise ValueError("one weight and one gradient per layer")
+        for w, g in zip(Ws, Gs):
+            if w.dtype != _torch().float32 or g.dtype != _torch().float32:
+                raise TypeError("fp32 weights and gradients")
+            if not (w.is_contiguous() and g.is_contiguous()):
+                raise ValueError("contiguous weights and gradients")
+        wp = (ctypes.c_void_p * self.nlayers)(*[w.data_ptr() for w in Ws])
+        gp = (ctypes.c_void_p * self.nlayers)(*[g.data_ptr() for g in Gs])
+        check(lib.pmx_shampoo_plan_step(self.plan, wp, gp, int(t), _ptr(self.state),
+                                        self.state.numel(), _ptr(self.ws), self.ws.numel(),
+                                        _stream_of(self.device)), "shampoo_plan_step")
+
+    def __del__(self):
+        if getattr(self, "plan", None) is not None and lib is not None:
+            lib.pmx_shampoo_plan_destroy(self.plan)
+            self.plan = None
 
 
 def precond_apply(Linv, G, Rinv, out=None, ws=None):

@@ -152,3 +152,15 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "numpy.linalg" not in txt and "np.linalg" not in txt, f
+
+
+def test_shampoo_plan_host_side():
+    # plan creation, grouping and sizes need no GPU (a null handle is refused)
+    from preconditioned_optimizer_matrix_amd import pmx
+    c = pmx.shampoo_config()
+    assert (c.block, c.root_every, c.adaptive_lr) == (1024, 1, 0)
+    assert c.beta == pytest.approx(0.95) and c.root_opts.degree == 2
+    arr = (pmx.Layer * 1)(pmx._layer((8, 8)))
+    plan = ctypes.c_void_p()
+    assert pmx.lib.pmx_shampoo_plan_create(None, ctypes.byref(c), arr, 1,
+                                           ctypes.byref(plan)) == pmx.ERR_INVALID_VALUE

@@ -542,3 +542,38 @@ def test_stats_and_apply_bf16(env, m, n):
     assert P.dtype == torch.bfloat16
     # fp32 products, one bf16 rounding of the output (relative 2^-8)
     assert cf.rel_fro(P.float().cpu().numpy(), cf.precond_apply(Li, G, Ri)) < 5e-3
+
+
+def test_shampoo_plan_step(env):
+    # a small model: two dense layers cut into blocks of 48 (ragged edges), a
+    # convolution kernel, roots every 2 steps, momentum and the adaptive rate;
+    # the weights after four steps against the fp64 reference
+    from oracle import shampoo_step as ss
+    torch, pmx, dev = env
+    shapes = [(100, 70), (48, 130), (16, 8, 3, 3)]
+    rng = np.random.default_rng(5)
+    W0 = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    Gs = [[(0.1 * rng.standard_normal(s)).astype(np.float32) for s in shapes] for _ in range(4)]
+    for momentum, adaptive in ((0.0, 0), (0.9, 1)):
+        _say("shampoo plan step", momentum, adaptive)
+        cfg = pmx.shampoo_config(block=48, root_every=2, beta=0.9, eps=1e-3, lr=0.05,
+                                 momentum=momentum, adaptive_lr=adaptive)
+        plan = pmx.ShampooPlan(shapes, dev, cfg)
+        Wd = [torch.from_numpy(w.copy()).to(dev) for w in W0]
+        st = ss.ShampooState(shapes, block=48, eps=1e-3)
+        Wr = [w.astype(np.float64) for w in W0]
+        for t in range(4):
+            plan.step(Wd, [torch.from_numpy(g).to(dev) for g in Gs[t]], t)
+            Wr = ss.step(st, Wr, Gs[t], t, 0.9, 1e-3, 0.05, momentum=momentum, root_every=2,
+                         adaptive_lr=bool(adaptive))
+        torch.cuda.synchronize()
+        for l in range(len(shapes)):
+            dW = Wd[l].cpu().numpy().astype(np.float64) - W0[l]
+            dWr = Wr[l] - W0[l]
+            assert cf.rel_fro(dW, dWr) < 1e-4, (l, cf.rel_fro(dW, dWr))
+        del plan
+    # argument errors
+    with pytest.raises(pmx.PmxError):
+        pmx.ShampooPlan([(4, 4, 4)], dev)
+    with pytest.raises(pmx.PmxError):
+        pmx.ShampooPlan([(8, 8)], dev, pmx.shampoo_config(block=0))

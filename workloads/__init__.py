@@ -86,6 +86,17 @@ def gaussian(m, n, seed, std=1.0):
     return (np.random.default_rng(seed).standard_normal((m, n)) * std).astype(np.float32)
 
 
+def irregular_blocks(count, seed, lo=8, hi=64):
+    """`count` Gaussian blocks (fp32) whose sides are drawn uniformly from
+    [lo, hi], one generator per block: the many small irregular blocks of a
+    block-diagonal preconditioner's per-block orthogonalisation."""
+    out = []
+    for rng in rngs(seed, count):
+        m, n = (int(x) for x in rng.integers(lo, hi + 1, 2))
+        out.append(rng.standard_normal((m, n)).astype(np.float32))
+    return out
+
+
 def polar_batch(batch, m, n, seed, smin=1e-4, smax=1.0, bf16=True):
     """Batch of m x n matrices U diag(sigma) V^T, sigma geometric over [smin, smax].
     Returns (values_f32 [batch, m, n], bits_u16 or None, sigma)."""
