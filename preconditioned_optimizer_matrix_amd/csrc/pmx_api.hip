@@ -25,6 +25,8 @@ struct pmx_context {
   int bf16_dma;            // bf16 GEMM: 1 uses direct global-to-LDS loads for whole tiles (measured slower; off)
   int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
   int split_k;             // 1: split-k tail for the fp32 products of the iterations
+  int bf16_sym;            // 1: bf16 X^T X and R^2 run upper-triangle tiles, mirrored
+  int bf16_sym_small;      // 1: ... with 128 x 128 tiles
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -807,6 +809,12 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
   c->split_k = 1;
   if (const char* e = getenv("PMX_SPLITK")) c->split_k = atoi(e);
+  // measured slower for the 32 x 4096 x 1024 polar (320 triangle tiles of 256^2
+  // still take two rounds of the compute units, and the mirrored stores cost)
+  c->bf16_sym = 0;
+  if (const char* e = getenv("PMX_BF16_SYM")) c->bf16_sym = atoi(e);
+  c->bf16_sym_small = 0;
+  if (const char* e = getenv("PMX_BF16_SYM_SMALL")) c->bf16_sym_small = atoi(e);
   *handle = c;
   return PMX_OK;
 }
@@ -1503,6 +1511,8 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       r.count_update = count;
       r.cfg = cfg;
       r.vec = vec ? 1 : 0;
+      r.sym = q.h->bf16_sym;  // X^T X: upper-triangle tiles, mirrored
+      r.sym_small = q.h->bf16_sym_small;
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_bf16(r, ROLE_RESID, q.s); });
     };
     {
@@ -1537,6 +1547,8 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
         g.prob[0].ldc = cols;
         g.prob[0].stride_c = bs;
         g.vec = vec ? 1 : 0;
+        g.sym = q.h->bf16_sym;  // R^2 with R exactly symmetric: triangle, mirrored
+        g.sym_small = q.h->bf16_sym_small;
         PMX_TRY(q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_bf16(g, ROLE_POWER, q.s); }));
       }
       PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, nullptr, false));

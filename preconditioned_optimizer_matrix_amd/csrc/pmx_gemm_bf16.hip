@@ -95,6 +95,23 @@ __device__ __forceinline__ void store_chunks(uint16_t* lds, const u32x4 (&v)[C])
   }
 }
 
+// Symmetric outputs: the T (T + 1) / 2 tiles tm <= tn of the upper triangle,
+// row by row.
+__device__ __forceinline__ void item_tile_sym(int it, int T, int* z, int* tm, int* tn,
+                                              int* tile) {
+  const int tiles = T * (T + 1) / 2;
+  *z = it / tiles;
+  int t = it - *z * tiles;
+  *tile = t;
+  int m = 0;
+  while (t >= T - m) {
+    t -= T - m;
+    ++m;
+  }
+  *tm = m;
+  *tn = m + t;
+}
+
 // Tiles of a matrix in groups of 8 tile-rows per column sweep.
 __device__ __forceinline__ void item_tile(int it, int tiles_m, int tiles_n, int* z, int* tm,
                                           int* tn, int* tile) {
@@ -213,7 +230,7 @@ template <class C, int ROLE, int FM, int FN>
 __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmParams& p,
                                               const GemmProblem& pr, int b, int m0, int n0,
                                               int tile, int tiles, int lane, int wm, int wn,
-                                              double* red) {
+                                              double* red, bool mirror) {
   constexpr bool RESID = ROLE == ROLE_RESID;
   constexpr bool BF16_OUT = ROLE == ROLE_UPDATE;
   const int hi = lane >> 5, col_in = lane & 31;
@@ -247,6 +264,29 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
             }
           }
         }
+        if (!BF16_OUT && mirror && col < p.N) {
+          // symmetric output: the tile's transpose C[col][row_base .. + 3]
+          // (off-diagonal tiles only), and of the bf16 copy of a residual
+          float xs[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = row_base + r;
+            const float a = acc[i][j][4 * g + r];
+            xs[r] = RESID ? ((row == col ? 1.f : 0.f) - a) : a;
+          }
+          float* Ct = pr.c + (int64_t)b * pr.stride_c + (int64_t)col * pr.ldc + row_base;
+          uint16_t* Ht = (RESID && p.prob[1].c)
+                             ? reinterpret_cast<uint16_t*>(p.prob[1].c) +
+                                   (int64_t)b * p.prob[1].stride_c +
+                                   (int64_t)col * p.prob[1].ldc + row_base
+                             : nullptr;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (row_base + r < p.M) {
+              Ct[r] = xs[r];
+              if (Ht) Ht[r] = (uint16_t)h[r];
+            }
+        }
         if (BF16_OUT && col < p.N) {
           // transposed copy: X'^T[col][row_base .. row_base + 3]
           const GemmProblem& tp = p.prob[1];
@@ -262,6 +302,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
         }
       }
     }
+  if (mirror) fro *= 2.f;  // the tile stands for itself and its transpose
   if (RESID) {
     const double blocksum = block_sum<C::WAVES>((double)fro, red);
     double tot;
@@ -290,7 +331,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = (wid / WGN) * C::WM, wn = (wid % WGN) * C::WN;
   const bool vec = p.vec != 0;
-  const int tiles = p.tiles_m * p.tiles_n;
+  const bool sym = p.sym != 0;  // upper-triangle tiles only, mirrored on store
+  const int tiles = sym ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   const int total = tiles * p.batch;
   const GemmProblem& pr = p.prob[0];
 
@@ -301,7 +343,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
   for (int it0 = blockIdx.x; it0 < total; it0 += gridDim.x) {
     const int it = xcd ? (it0 & 7) * (total >> 3) + (it0 >> 3) : it0;
     int b, tm, tn, tile;
-    item_tile(it, p.tiles_m, p.tiles_n, &b, &tm, &tn, &tile);
+    if (sym) item_tile_sym(it, p.tiles_m, &b, &tm, &tn, &tile);
+    else item_tile(it, p.tiles_m, p.tiles_n, &b, &tm, &tn, &tile);
     if (p.ctrl) {
       const int st = *(volatile int32_t*)&p.ctrl[b].status;
       if (st != PMX_RUNNING) continue;
@@ -369,7 +412,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
     }
     }
 
-    bf16_epilogue<C, ROLE>(acc, p, pr, b, m0, n0, tile, tiles, lane, wm, wn, red);
+    bf16_epilogue<C, ROLE>(acc, p, pr, b, m0, n0, tile, tiles, lane, wm, wn, red,
+                           sym && tm != tn);
   }
 }
 
@@ -511,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmParams p) {
       for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(nst, j, 0);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the trailing reloads are done
-    bf16_epilogue<C, ROLE>(acc, p, pr, b, m0, n0, tile, tiles, lane, wm, wn, red);
+    bf16_epilogue<C, ROLE>(acc, p, pr, b, m0, n0, tile, tiles, lane, wm, wn, red, false);
   }
 }
 
@@ -535,7 +579,9 @@ template <class C>
 hipError_t launch_cfg(GemmParams p, int role, hipStream_t s) {
   p.tiles_m = (p.M + C::BM - 1) / C::BM;
   p.tiles_n = (p.N + C::BN - 1) / C::BN;
-  const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
+  if (p.sym && (C::BM != C::BN || p.M != p.N || role == ROLE_UPDATE)) return hipErrorInvalidValue;
+  const int64_t total = (p.sym ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2
+                               : (int64_t)p.tiles_m * p.tiles_n) * p.batch;
   int64_t g = total;
   if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
   const dim3 grid((unsigned)g), block(C::NT);
@@ -559,6 +605,13 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int role, hipStream_t s) {
   const int64_t large = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
   int cfg = p.cfg_id;
   if (cfg < 0 || cfg > 3) cfg = (p.M >= 256 && p.N >= 256 && large >= p.num_cu) ? 1 : 0;
+  if (p.sym) {
+    // square tiles (the 256 x 256 tile, or 128 x 128 when forced with 0)
+    if (cfg == 2 || cfg == 3) cfg = 1;
+    if (cfg == 1 && p.sym_small) cfg = 0;
+    if (cfg == 1) return launch_cfg<BLarge>(p, role, s);
+    return launch_cfg<BSmall>(p, role, s);
+  }
   if (cfg == 2) return launch_cfg<BLarge4>(p, role, s);
   if (cfg == 3) return launch_cfg<BMid2>(p, role, s);
   if (cfg == 1 && p.dma && p.vec && p.M % 256 == 0 && p.N % 256 == 0 && p.K % DBK == 0 &&

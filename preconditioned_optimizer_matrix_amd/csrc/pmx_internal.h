@@ -258,7 +258,8 @@ struct GemmParams {
   int cfg_id;      // tile configuration (-1: chosen from the shape)
   int map_mode;    // tile order: 0 grouped, 1 grouped + XCD rounds, 2 row-major
   int dma;         // bf16: whole-tile variant with direct global-to-LDS loads
-  int sym;         // fp32: output symmetric, upper-triangle tiles mirrored (M == N)
+  int sym;         // output symmetric, upper-triangle tiles mirrored (M == N)
+  int sym_small;   // bf16 symmetric launches: 128 x 128 tiles instead of 256 x 256
   int num_cu;
   Ctrl* ctrl;      // per-matrix control blocks; null = unconditional
   // polynomial operands
