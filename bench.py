@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--method", type=int, default=0,
                     help="inverse roots: 0 coupled Newton-Schulz (chained for p = 4), "
                          "1 coupled inverse Newton")
+    ap.add_argument("--host-poll", type=int, default=2,
+                    help="updates per host-polled convergence point (0: enqueue all "
+                         "max_iter updates; the surplus ones exit on the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -127,6 +130,7 @@ def other_workload(args):
     from preconditioned_optimizer_matrix_amd import pmx
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    pmx.set_host_poll(args.host_poll)
     opts = pmx.default_opts(max_iter=args.max_iter, degree=args.degree,
                             degree_max=args.degree_max, method=args.method)
     taylor = pmx.default_opts(max_iter=60, accelerate=0, degree=args.degree, method=args.method)
@@ -276,6 +280,7 @@ def other_workload(args):
                    gemms_taylor=tg, gemm_ratio_taylor_over_prism=round(tg / gemms, 3),
                    iters=int(inf["iters"][0]), mfma_tflops=round(tf, 2),
                    mfma_frac=round(tf / PEAK_FP32_MFMA, 4))
+    out["config"]["host_poll"] = args.host_poll
     print(json.dumps(out), flush=True)
 
 
@@ -400,6 +405,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    pmx.set_host_poll(args.host_poll)
     cfg = W.shampoo_1024x4096()
     m, n = cfg["Gs"][0].shape
     beta, eps = cfg["beta"], cfg["eps"]
@@ -539,7 +545,7 @@ def main():
                    "warmup_updates": 9, "degree": args.degree,
                    "degree_max": args.degree_max, "method": args.method, "sketch_p": 8,
                    "tol": 1e-6,
-                   "max_iter": args.max_iter,
+                   "max_iter": args.max_iter, "host_poll": args.host_poll,
                    "step": "restore L,R; stats update; L^-1/4; R^-1/4; apply"},
         "gemms_to_converge": {"R": gemmsR, "L": gemmsL, "R_taylor": gemmsR_taylor},
         "iters": {"R": [int(x) for x in iR["iters"]], "L": [int(x) for x in iL["iters"]]},

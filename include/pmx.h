@@ -359,6 +359,26 @@ typedef enum {
   PMX_KC_COUNT = 8
 } pmx_kernel_class;
 
+/* Convergence polling by the host (off by default: chunk = 0).  A
+ * matrix-function call normally enqueues all max_iter updates of a stage up
+ * front; the updates after convergence exit on the device but still pay for
+ * their launches (a few microseconds each).  With chunk > 0 the fp32 update
+ * loops of pmx_matfn_inv_root* and pmx_matfn_polar* (and the Shampoo plan's
+ * roots) publish, after every `chunk` updates, whether any matrix of the
+ * batch is still iterating: a one-block kernel writes it to pinned host
+ * memory behind an event.  The host reads each published value one chunk
+ * later, so one chunk stays queued and the device does not wait for the
+ * host, and it stops enqueuing updates once a value says that none is
+ * iterating.  Results and info are the same as with chunk = 0 (the updates
+ * left out are those that would have exited at once); at most 2 chunk - 1
+ * updates a stage are enqueued past convergence.  The calling thread blocks
+ * on those events, so a call returns only once the device is at most a
+ * chunk behind it.  Polling is skipped while the stream is being captured.
+ * The first enable allocates 8 bytes of pinned host memory and two events,
+ * freed by pmx_destroy.  Returns PMX_ERR_INVALID_VALUE for chunk outside
+ * [0, 1000], PMX_ERR_HIP when the pinned memory or events cannot be made. */
+pmx_status pmx_set_host_poll(pmx_handle handle, int chunk);
+
 /* Enable (1) or disable (0) the launch trace; enabling discards old records. */
 pmx_status pmx_trace_enable(pmx_handle handle, int enable);
 /* Wait for the recorded events, write per kernel class the summed

@@ -27,6 +27,12 @@ struct pmx_context {
   int split_k;             // 1: split-k tail for the fp32 products of the iterations
   int bf16_sym;            // 1: bf16 X^T X and R^2 run upper-triangle tiles, mirrored
   int bf16_sym_small;      // 1: ... with 128 x 128 tiles
+  // host-polled convergence (pmx_set_host_poll): updates per published point,
+  // two pinned host flags (device-mapped) and the events behind them
+  int poll_chunk = 0;
+  int32_t* poll_host = nullptr;
+  int32_t* poll_dev = nullptr;
+  hipEvent_t poll_ev[2] = {nullptr, nullptr};
   // launch trace (benchmarking): event pairs recorded around every launch
   bool trace = false;
   struct Rec {
@@ -122,6 +128,45 @@ struct Enq {
       h->recs.push_back({cls, a, b});
     }
     return e;
+  }
+};
+
+// Host-polled convergence of one update loop (pmx_set_host_poll).  At the
+// top of update i (i > 0, i a multiple of the chunk) a one-block kernel
+// publishes whether any matrix is still iterating, followed by an event; the
+// value published one point earlier is then read after its event, so one
+// chunk stays queued while the host waits.  When that value is 0 every later
+// update of the loop would exit on the device at once, so the loop stops.
+struct Poller {
+  Enq& q;
+  const Ctrl* ctrl;
+  int batch;
+  int chunk = 0;
+  int points = 0;
+  Poller(Enq& q_, const Ctrl* c, int b) : q(q_), ctrl(c), batch(b) {
+    chunk = q.h ? q.h->poll_chunk : 0;
+    if (chunk > 0) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(q.s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        chunk = 0;
+    }
+  }
+  hipError_t step(int i, bool* stop) {
+    *stop = false;
+    if (chunk <= 0 || i == 0 || i % chunk != 0) return hipSuccess;
+    pmx_context* h = q.h;
+    volatile int32_t* flag = h->poll_host;
+    const int slot = points & 1;
+    flag[slot] = -1;
+    hipError_t e = q.run(PMX_KC_OTHER, [&] {
+      return launch_publish_running(ctrl, batch, h->poll_dev + slot, q.s);
+    });
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(h->poll_ev[slot], q.s)) != hipSuccess) return e;
+    if (++points < 2) return hipSuccess;
+    if ((e = hipEventSynchronize(h->poll_ev[slot ^ 1])) != hipSuccess) return e;
+    *stop = flag[slot ^ 1] == 0;
+    return hipSuccess;
   }
 };
 
@@ -575,7 +620,11 @@ pmx_status enqueue_inverse_newton(Enq& q, void* ws, const IterLayout& L, const p
     set_vec(g);
     return q.run(PMX_KC_GEMM_POWER, [&] { return launch_gemm_f32(g, false, false, ROLE_POWER, q.s); });
   };
+  Poller poll(q, ctrl, batch);
   for (int k = 0; k < o.max_iter; ++k) {
+    bool stop = false;
+    PMX_TRY(poll.step(k, &stop));
+    if (stop) break;
     const int cur = k & 1, nxt = cur ^ 1;
     if (d == 2) PMX_TRY(sym_product(Rb, Rb, Pb));
     if (acc) {
@@ -822,7 +871,37 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
 pmx_status pmx_destroy(pmx_handle h) {
   if (!h) return PMX_ERR_INVALID_VALUE;
   for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+  for (hipEvent_t e : h->poll_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (h->poll_host) (void)hipHostFree(h->poll_host);
   delete h;
+  return PMX_OK;
+}
+
+pmx_status pmx_set_host_poll(pmx_handle h, int chunk) {
+  if (!h || chunk < 0 || chunk > kMaxIter) return PMX_ERR_INVALID_VALUE;
+  if (chunk > 0 && !h->poll_host) {
+    DeviceGuard dg(h->device);
+    if (!dg.ok) return PMX_ERR_HIP;
+    void* p = nullptr;
+    if (hipHostMalloc(&p, 2 * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) !=
+        hipSuccess)
+      return PMX_ERR_HIP;
+    void* d = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess ||
+        hipEventCreateWithFlags(&e0, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&e1, hipEventDisableTiming) != hipSuccess) {
+      if (e0) (void)hipEventDestroy(e0);
+      (void)hipHostFree(p);
+      return PMX_ERR_HIP;
+    }
+    h->poll_host = (int32_t*)p;
+    h->poll_dev = (int32_t*)d;
+    h->poll_ev[0] = e0;
+    h->poll_ev[1] = e1;
+  }
+  h->poll_chunk = chunk;
   return PMX_OK;
 }
 
@@ -1221,7 +1300,11 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       ip.sketch = make_sketch(Lw, ws, cfg, n, 0, stage, acc);
       PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_sqrt_stage_init(ip, batch, q.s); }));
     }
+    Poller poll(q, ctrl, batch);
     for (int k = k64; k < o.max_iter; ++k) {
+      bool stop = false;
+      PMX_TRY(poll.step(k - k64, &stop));
+      if (stop) break;
       PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b, R3b));
       const int cur = k & 1, nxt = cur ^ 1;
       GemmParams u = gemm_base(q.h, n, n, n, batch);
@@ -1446,7 +1529,11 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
     };
     PMX_TRY(residual(Xb[0], 1, 0));
+    Poller poll(q, ctrl, batch);
     for (int k = 0; k < o.max_iter; ++k) {
+      bool stop = false;
+      PMX_TRY(poll.step(k, &stop));
+      if (stop) break;
       PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, cols, batch, Rb, R2b, R3b));
       const int cur = k & 1, nxt = cur ^ 1;
       GemmParams u = gemm_base(q.h, rows, cols, cols, batch);
@@ -1537,7 +1624,11 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_xpose(x, batch, q.s); }));
     }
     PMX_TRY(residual(Xt[0], 1, 0));
+    Poller poll(q, ctrl, batch);
     for (int k = 0; k < o.max_iter; ++k) {
+      bool stop = false;
+      PMX_TRY(poll.step(k, &stop));
+      if (stop) break;
       if (d == 2) {
         GemmParams g = bf16_base(q.h, cols, cols, cols, batch);
         g.ctrl = ctrl;

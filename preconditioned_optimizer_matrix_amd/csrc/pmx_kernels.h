@@ -84,6 +84,7 @@ struct SkinnyParams {
   int64_t kld, kstride;
   int n, q;
   int variant;  // 0: In staged through LDS, 1: In read directly
+  int mfma;     // set by the launcher: the matrix-core form
   Ctrl* ctrl;
   // last pass only: Gram shares (kGramShare doubles per block) and the alpha
   // solve; a matrix at degree d uses K_1..K_{2d+1} (the pass writes one of
@@ -277,6 +278,10 @@ hipError_t launch_sqrt_stage_init(const StageInitParams& p, int batch, hipStream
 hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hipStream_t s);
 hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s);
 int skinny_blocks(int n, int q);
+// dst (pinned host memory, device-mapped) = 1 if any of ctrl[0 .. batch) is
+// still PMX_RUNNING, else 0; one block, a system-scope store.
+hipError_t launch_publish_running(const Ctrl* ctrl, int batch, int32_t* dst, hipStream_t s);
+
 hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s);
 // Elementwise copy between fp32 and bf16 matrices (rows x cols, strided batch);
 // bf16 -> fp32 is exact, fp32 -> bf16 rounds to nearest even.

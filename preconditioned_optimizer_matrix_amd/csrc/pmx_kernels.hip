@@ -228,7 +228,7 @@ constexpr int SK_LD = SK_CH + 4;     // column stride of the staged chunk
 
 // Reduction, output and (GJ != 0) Gram share / alpha fit of a skinny product:
 // acc holds the lane's RW x Q partial sums for rows row0 .. row0 + RW - 1.
-template <int Q, int RW, int GJ>
+template <int Q, int RW, int GJ, int NW = NT / 64>
 __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const SkinnyParams& p,
                                               const SkinnyJob& job, int b, int row0,
                                               float scale, double fro) {
@@ -289,7 +289,7 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
         for (int bb = a; bb < GA; ++bb, ++t) g[t] += v[a] * v[bb];
     }
     // entries of (a, bb) with a <= bb < J, in row order, are packed first
-    __shared__ double wsum[4][NE];
+    __shared__ double wsum[NW][NE];
     __shared__ double gsum[NE];
     {
       int t = 0, o = 0;
@@ -310,8 +310,11 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     double* part = p.gram_partials + (int64_t)b * p.gram_stride;
     if (threadIdx.x < ng)
       part[(int64_t)blockIdx.x * kGramShare + threadIdx.x] =
-          ((wsum[0][threadIdx.x] + wsum[1][threadIdx.x]) + wsum[2][threadIdx.x]) +
-          wsum[3][threadIdx.x];
+          [&] {
+            double t = wsum[0][threadIdx.x];
+            for (int w = 1; w < NW; ++w) t += wsum[w][threadIdx.x];
+            return t;
+          }();
     __syncthreads();
     if (threadIdx.x == 0) {
       __threadfence();
@@ -323,7 +326,7 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     __threadfence();
     // every entry summed over the blocks' shares by one wave each, with a
     // fixed lane assignment and reduction tree (deterministic)
-    for (int e = wid; e < ng; e += NT / 64) {
+    for (int e = wid; e < ng; e += NW) {
       double sv = 0.0;
       for (int i = lane; i < (int)gridDim.x; i += 64)
         sv += __hip_atomic_load(&part[(int64_t)i * kGramShare + e], __ATOMIC_RELAXED,
@@ -359,6 +362,79 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
       cb->counter = 0u;
     }
   }
+}
+
+// The same product on the matrix cores, for 16-byte-aligned Mat (n % 4 == 0):
+// a block owns 16 rows of Mat and its W waves split the columns into W equal
+// slices.  Each wave runs v_mfma_f32_16x16x4_f32 along its slice with 16 x 4
+// tiles of Mat as A and the matching 4 x 16 tiles of In as B (columns >= q
+// are zero), so one value of In read from L2 serves 16 rows and nothing is
+// staged in LDS (the LDS-staged forms above read Q values of In a value of
+// Mat).  Lane l holds A[l % 16][k] and B[k][l % 16] for the k-slot l / 16; a
+// float4 load of Mat feeds four products.  The W partial 16 x 16 tiles are
+// summed through LDS in wave order; wave w then finishes rows w 16/W ..
+// (w + 1) 16/W - 1.
+typedef float sk_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int Q, int W, int GJ>
+__global__ __launch_bounds__(W * 64) void skinny_mfma_kernel(SkinnyParams p) {
+  constexpr int RW = 16 / W;  // rows finished by each wave
+  constexpr int UN = 4;       // 16-column steps with loads in flight together
+  const int b = blockIdx.z;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const SkinnyJob& job = p.job[blockIdx.y];
+  const int n = p.n;
+  const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
+  float* kb = p.kbuf + (int64_t)b * p.kstride;
+  const double fro = cb->fro;
+  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = lane & 15, slot = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const bool rok = row0 + r < n;
+  const float* arow = mat + (int64_t)(rok ? row0 + r : 0) * job.mat_ld;
+  const bool cok = r < p.q;
+  const float* xcol = kb + job.in_col + (cok ? r : 0);
+  const int kper = (n + 16 * W - 1) / (16 * W) * 16;  // a multiple of 16
+  const int kbeg = wid * kper;
+  const int kend = n < kbeg + kper ? n : kbeg + kper;  // a multiple of 4
+  sk_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kbeg; k0 < kend; k0 += 16 * UN) {
+    float4 a[UN];
+    float x[UN][4];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int k = k0 + 16 * u + 4 * slot;
+      const bool kok = k < kend;  // then k + 3 < kend as well
+      a[u] = rok && kok ? *reinterpret_cast<const float4*>(arow + k)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[u][i] = cok && kok ? xcol[(int64_t)(k + i) * p.kld] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].x, x[u][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].y, x[u][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].z, x[u][2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u].w, x[u][3], c, 0, 0, 0);
+    }
+  }
+  // lane l holds D[4 (l / 16) + v][l % 16], v = 0 .. 3
+  __shared__ float red[W][16][17];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wid][4 * slot + v][r] = c[v];
+  __syncthreads();
+  float tot = 0.f;
+  if (lane < RW * Q) {
+    const int rr = wid * RW + lane / Q, cc = lane - (lane / Q) * Q;
+    for (int w = 0; w < W; ++w) tot += red[w][rr][cc];
+  }
+  // value (i / Q, i % Q) sits in lane i alone; the finish sums over lanes
+  float acc[RW * Q];
+#pragma unroll
+  for (int i = 0; i < RW * Q; ++i) acc[i] = lane == i ? tot : 0.f;
+  skinny_finish<Q, RW, GJ, W>(acc, p, job, b, row0 + wid * RW, scale, fro);
 }
 
 template <int Q, int RW, int GJ>
@@ -885,6 +961,18 @@ int skinny_blocks(int n, int q) {
 
 template <int Q, int RW, int GJ>
 static void skinny_go_j(const SkinnyParams& p, int njobs, int batch, hipStream_t s) {
+  if constexpr (Q == 8 || Q == 16) {
+    if (p.mfma) {
+      // 16 waves a block (8 for the 9-entry Newton objective, whose solver
+      // needs more than 128 registers a lane)
+      dim3 g((p.n + 15) / 16, njobs, batch);
+      if constexpr (GJ != -9)
+        hipLaunchKernelGGL((skinny_mfma_kernel<Q, 16, GJ>), g, dim3(1024), 0, s, p);
+      else
+        hipLaunchKernelGGL((skinny_mfma_kernel<Q, 8, GJ>), g, dim3(512), 0, s, p);
+      return;
+    }
+  }
   dim3 grid((p.n + 4 * RW - 1) / (4 * RW), njobs, batch);
   if constexpr (GJ < 0) {
     hipLaunchKernelGGL((skinny_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
@@ -918,8 +1006,22 @@ static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hi
   }
 }
 
-hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
+hipError_t launch_skinny(const SkinnyParams& pin, int njobs, bool gram, int batch,
+                         hipStream_t s) {
+  SkinnyParams p = pin;
   if (gram && (njobs != 1 || p.q > 16)) return hipErrorInvalidValue;
+  // the matrix-core form: any q <= 16 with 16-byte-aligned rows of Mat, for
+  // launches of at most 1024 blocks of 16 rows (single or few large
+  // matrices); larger batches of small matrices keep the LDS-staged forms,
+  // which measured faster there (their Gram shares cost less a row)
+  {
+    const int64_t blocks = (int64_t)((p.n + 15) / 16) * njobs * batch;
+    bool ok = p.variant == 0 && p.q <= 16 && p.n % 4 == 0 && blocks <= 1024;
+    for (int j = 0; j < njobs; ++j)
+      ok = ok && p.job[j].mat_ld % 4 == 0 && ((uintptr_t)p.job[j].mat & 15) == 0 &&
+           p.job[j].mat_stride % 4 == 0;
+    p.mfma = ok ? 1 : 0;
+  }
   // more rows per wave once that still leaves two blocks per compute unit
   const bool wide = (int64_t)((p.n + 31) / 32) * njobs * batch >= 512;
   if (p.q <= 8) {
@@ -934,6 +1036,23 @@ hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch,
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// One flag for the host: is any matrix of the batch still iterating?
+__global__ __launch_bounds__(NT) void publish_running_kernel(const Ctrl* ctrl, int batch,
+                                                             int32_t* dst) {
+  __shared__ int32_t any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  for (int b = threadIdx.x; b < batch; b += NT)
+    if (load_status(ctrl + b) == PMX_RUNNING) any = 1;
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(dst, any, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_publish_running(const Ctrl* ctrl, int batch, int32_t* dst, hipStream_t s) {
+  hipLaunchKernelGGL(publish_running_kernel, dim3(1), dim3(NT), 0, s, ctrl, batch, dst);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ EXPORTS = [
     "pmx_matfn_inv_root", "pmx_matfn_inv_root_batched",
     "pmx_matfn_polar", "pmx_matfn_polar_batched", "pmx_matfn_polar_varbatch",
     "pmx_precond_apply", "pmx_precond_apply_batched",
-    "pmx_trace_enable", "pmx_trace_collect",
+    "pmx_trace_enable", "pmx_trace_collect", "pmx_set_host_poll",
     "pmx_shampoo_config_default", "pmx_shampoo_plan_create", "pmx_shampoo_plan_destroy",
     "pmx_shampoo_plan_sizes", "pmx_shampoo_plan_init", "pmx_shampoo_plan_step",
 ]
@@ -123,6 +123,7 @@ def _load():
                                              _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32, _vp,
                                              _sz, _vp]),
         "pmx_trace_enable": (_i32, [_vp, _i32]),
+        "pmx_set_host_poll": (_i32, [_vp, _i32]),
         "pmx_shampoo_config_default": (_i32, [ctypes.POINTER(ShampooConfig)]),
         "pmx_shampoo_plan_create": (_i32, [_vp, ctypes.POINTER(ShampooConfig),
                                            ctypes.POINTER(Layer), _i32,
@@ -438,6 +439,15 @@ def precond_apply(Linv, G, Rinv, out=None, ws=None):
         ldr, sr, _ptr(P), ldp, sp, batch, _ptr(ws), ws.numel(), _stream(G)),
         "precond_apply")
     return P
+
+
+def set_host_poll(chunk, device=None):
+    """Host-polled convergence for this device's handle: after every `chunk`
+    updates the iteration loops publish whether any matrix still iterates and
+    stop enqueuing once none does (0 turns it off: all max_iter updates are
+    enqueued and the surplus ones exit on the device).  Same results either
+    way; the calling thread waits on the published points."""
+    check(lib.pmx_set_host_poll(handle(device), int(chunk)), "set_host_poll")
 
 
 def trace_enable(enable=True, device=None):
