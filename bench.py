@@ -48,11 +48,13 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 256 MiB fp32 buffer 4 times (a plain copy kernel of "
                          "known traffic, for scaling HBM byte counters)")
-    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+    ap.add_argument("--traffic-from", nargs=5,
+                    metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "BENCH_JSON"),
                     help="only write the update GEMM's HBM traffic record from four "
                          "rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of "
-                         "'--steps 1 --warmup 0 --no-cpu-baseline --no-trace', then of "
-                         "--calibrate-copy)")
+                         "'--steps 1 --warmup 0 --no-cpu-baseline --no-trace --host-poll 0', "
+                         "then of --calibrate-copy) and the JSON line that profiled bench "
+                         "run printed (for its R^-1/4 update counts)")
     ap.add_argument("--workload", default="shampoo_1024x4096",
                     choices=["shampoo_1024x4096", "spd_64", "blocks_64x512",
                              "muon_32x4096x1024", "mp_10000", "varblocks_4096",
@@ -289,10 +291,13 @@ UPDATE_KERNEL = ("gemm_f32_kernel<pmx::(anonymous namespace)::Cfg<128, 128, 16, 
 
 
 def write_traffic(dirs):
-    """profiles/update_gemm_traffic.json from rocprofv3 counter folders: the
-    first 60 dispatches of the n = 4096 update GEMM (the first step's R^-1/4
-    call, early exits included), each counter scaled by what it reads for the
-    plain 256 MiB copy of calibrate_copy()."""
+    """profiles/update_gemm_traffic.json from rocprofv3 counter folders: HBM
+    bytes per update product of the n = 4096 update GEMM, summed over the
+    first 60 dispatches (the first step's R^-1/4 call without host polling:
+    30 updates a stage, early exits included) and divided by that call's
+    products (2 k - 1 a stage of k updates, from the profiled run's JSON
+    line); each counter scaled by what it reads for the plain 256 MiB copy of
+    calibrate_copy()."""
     import csv
     import glob
 
@@ -310,35 +315,39 @@ def write_traffic(dirs):
     n_launch = 60
     fetch = per_dispatch(dirs[0], upd)[:n_launch]
     write = per_dispatch(dirs[1], upd)[:n_launch]
+    run = json.loads(open(dirs[4]).read().strip().splitlines()[-1])
+    products = sum(2 * int(k) - 1 for k in run["iters"]["R"] if int(k) > 0)
     cf = per_dispatch(dirs[2], cpy)
     cw = per_dispatch(dirs[3], cpy)
     true_kib = 256 * 1024.0
     fs, ws = true_kib / np.mean(cf), true_kib / np.mean(cw)
-    f_raw, w_raw = float(np.mean(fetch)), float(np.mean(write))
+    f_raw, w_raw = float(np.sum(fetch)), float(np.sum(write))
     rec = {
         "kernel": "gemm_f32_kernel<Cfg<128,128,16,2,2,3>,NN,ROLE_UPDATE> (n=4096 updates of R^-1/4)",
         "source_sha256": source_digest(),
         "source_files": ["preconditioned_optimizer_matrix_amd/csrc/pmx_gemm_f32.hip",
                          "preconditioned_optimizer_matrix_amd/csrc/pmx_api.hip"],
-        "launches_per_step": n_launch,
-        "fetch_kib_per_launch_raw": round(f_raw, 1),
-        "write_kib_per_launch_raw": round(w_raw, 1),
+        "dispatches": n_launch,
+        "products": products,
+        "fetch_kib_raw": round(f_raw, 1),
+        "write_kib_raw": round(w_raw, 1),
         "copy_kib_true": true_kib,
         "copy_fetch_kib_raw": round(float(np.mean(cf)), 1),
         "copy_write_kib_raw": round(float(np.mean(cw)), 1),
         "fetch_scale": round(fs, 5),
         "write_scale": round(ws, 5),
-        "hbm_bytes_per_launch": int(round((f_raw * fs + w_raw * ws) * 1024)),
+        "hbm_bytes_per_product": int(round((f_raw * fs + w_raw * ws) * 1024 / products)),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace --host-poll 0 > <json>",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace --host-poll 0",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --calibrate-copy",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --calibrate-copy",
-            "python3 bench.py --traffic-from <four dirs>",
+            "python3 bench.py --traffic-from <four dirs> <json>",
         ],
-        "reduction": "per counter: mean over the first 60 dispatches of the kernel (the first "
-                     "step's R^-1/4 call, early exits included); copy: mean over the 4 "
-                     "__amd_rocclr_copyBuffer dispatches of 256 MiB",
+        "reduction": "per counter: sum over the first 60 dispatches of the kernel (the first "
+                     "step's R^-1/4 call, early exits included) over that call's update "
+                     "products; copy: mean over the 4 __amd_rocclr_copyBuffer dispatches "
+                     "of 256 MiB",
     }
     path = os.path.join(ROOT, "profiles", "update_gemm_traffic.json")
     with open(path, "w") as fh:
@@ -371,19 +380,21 @@ def source_digest():
     return h.hexdigest()
 
 
-def update_traffic(n_launch):
-    """HBM bytes per update-GEMM launch measured with rocprofv3 counters
-    (profiles/update_gemm_traffic.json), or None when the GEMM kernel or its
-    launch sequence has changed since the counters were taken."""
+def update_traffic(products, launches):
+    """HBM bytes per update-GEMM launch of a call with `products` update
+    products in `launches` launches, from the bytes per product measured with
+    rocprofv3 counters (profiles/update_gemm_traffic.json; the early exits
+    move no matrix data), or None when the GEMM kernel or its launch sequence
+    has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "update_gemm_traffic.json")
     try:
         rec = json.load(open(path))
         digest = source_digest()
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != digest or rec.get("launches_per_step") != n_launch:
+    if rec.get("source_sha256") != digest or "hbm_bytes_per_product" not in rec:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(round(rec["hbm_bytes_per_product"] * products / max(launches, 1)))
 
 
 def main():
@@ -526,7 +537,7 @@ def main():
                         kernel="gemm_f32_kernel<Cfg<128,128,16,2,2,3>,NN,ROLE_UPDATE> (n=4096)",
                         achieved=round(achieved, 2), peak=PEAK_FP32_MFMA, unit="TFLOP/s",
                         frac=round(achieved / PEAK_FP32_MFMA, 4),
-                        traffic=update_traffic(int(launches)),
+                        traffic=update_traffic(products, int(launches)),
                         launches=int(launches), avg_launch_ms=round(avg_ms, 4),
                         products=products, algorithmic_flops_per_launch=round(flops / launches, 1))
         log("trace:", {k: (round(v[0], 3), v[1]) for k, v in trace.items()})
