@@ -135,8 +135,9 @@ def krylov_gram(R, S, J):
 
 
 def inv_root(A, p=4, d=2, lo=None, hi=None, tol=1e-6, max_iter=30, sketch_fn=None,
-             accelerate=True):
-    """A^{-1/p} and A^{1/p} by the PRISM coupled inverse Newton iteration.
+             accelerate=True, scale="frobenius"):
+    """A^{-1/p} and A^{1/p} by the PRISM coupled inverse Newton iteration, on
+    A / c with c from prism.input_scale.
     Returns (X, X_aux, info) with info = dict(status, stages=[StageTrace], c)."""
     A = np.asarray(A, np.float64)
     n = A.shape[0]
@@ -145,7 +146,7 @@ def inv_root(A, p=4, d=2, lo=None, hi=None, tol=1e-6, max_iter=30, sketch_fn=Non
     if sketch_fn is None:
         sketch_fn = prism.make_sketch_fn(0)
     tr = prism.StageTrace()
-    c = float(np.linalg.norm(A))
+    c = prism.input_scale(A, scale, sketch_fn)
     if not np.isfinite(c) or c == 0.0:
         tr.status = prism.NONFINITE
         nan = np.full((n, n), np.nan)

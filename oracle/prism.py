@@ -304,15 +304,54 @@ def exact_sketch_fn():
     return lambda stage, k, n: np.eye(n)
 
 
+# The power estimate of the input scale (an option; the pages leave the
+# scaling open): the start block is the sketch of stage POWER_STAGE, k = 0.
+POWER_STAGE, POWER_PASSES, POWER_FACTOR = 2, 4, 2.0
+
+
+def power_scale(A, c, V0, passes=POWER_PASSES, factor=POWER_FACTOR):
+    """c * min(1, factor * mu) with mu = max_j ||K_t[:, j]|| / ||K_{t-1}[:, j]||,
+    K_0 = V0 and K_t = (A / c) K_{t-1} for t = 1..passes.  Every ratio is at
+    most the spectral norm of A / c (||M x|| <= ||M||_2 ||x||), so the result
+    never exceeds c and stays at most factor * lambda_max; zero or non-finite
+    ratios leave c unchanged."""
+    M = np.asarray(A, np.float64) / c
+    prev, K = None, np.asarray(V0, np.float64)
+    for _ in range(passes):
+        prev, K = K, M @ K
+    n0 = np.linalg.norm(prev, axis=0)
+    n1 = np.linalg.norm(K, axis=0)
+    ok = (n0 > 0) & np.isfinite(n0) & np.isfinite(n1)
+    if not np.any(ok):
+        return c
+    mu = float(np.max(n1[ok] / n0[ok]))
+    if not (mu > 0.0) or not np.isfinite(mu):
+        return c
+    return c * min(1.0, factor * mu)
+
+
+def input_scale(A, scale, sketch_fn):
+    """The scale c of Y_0 = A / c: ||A||_F ("frobenius") or its power estimate
+    ("power", start block sketch_fn(POWER_STAGE, 0, n))."""
+    c = float(np.linalg.norm(A))
+    if scale == "power" and np.isfinite(c) and c > 0.0:
+        c = power_scale(A, c, sketch_fn(POWER_STAGE, 0, A.shape[0]))
+    elif scale not in ("frobenius", "power"):
+        raise ValueError("scale must be 'frobenius' or 'power'")
+    return c
+
+
 def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
-             sketch_fn=None, accelerate=True, degree_max=None, adapt_ratio=0.3):
+             sketch_fn=None, accelerate=True, degree_max=None, adapt_ratio=0.3,
+             scale="frobenius"):
     """PRISM A^{-1/p} (p in {2, 4}) with the auxiliary A^{1/p}.
-    Scaling c = ||A||_F, stage 1 on A / c; for p = 4 stage 2 on stage 1's Y.
+    Scaling c = ||A||_F (or its power estimate, input_scale), stage 1 on
+    A / c; for p = 4 stage 2 on stage 1's Y.
     Returns (X, X_aux, info) with info = dict(status, stages=[StageTrace...], c)."""
     A = np.asarray(A, np.float64)
     if sketch_fn is None:
         sketch_fn = make_sketch_fn(0)
-    c = float(np.linalg.norm(A))
+    c = input_scale(A, scale, sketch_fn)
     if not np.isfinite(c) or c == 0.0:
         n = A.shape[0]
         nan = np.full((n, n), np.nan)
