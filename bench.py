@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--method", type=int, default=0,
                     help="inverse roots: 0 coupled Newton-Schulz (chained for p = 4), "
                          "1 coupled inverse Newton")
+    ap.add_argument("--scale", choices=["frobenius", "power"], default="power",
+                    help="input scale of the inverse roots: the power estimate of the "
+                         "top eigenvalue (opts.scale_mode 1), or ||A||_F (the library's "
+                         "default, also reported beside the headline)")
     ap.add_argument("--host-poll", type=int, default=2,
                     help="updates per host-polled convergence point (0: enqueue all "
                          "max_iter updates; the surplus ones exit on the device)")
@@ -60,6 +64,9 @@ def parse():
                              "muon_32x4096x1024", "mp_10000", "varblocks_4096",
                              "model_step"])
     return ap.parse_args()
+
+
+SCALE_MODES = {"frobenius": 0, "power": 1}
 
 
 def log(*a):
@@ -133,12 +140,19 @@ def other_workload(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pmx.set_host_poll(args.host_poll)
+    wl = args.workload
+    # the power scale applies to the inverse roots of order above 64 (order 64
+    # runs the fused single-launch kernel, which scales by ||A||_F; the polar
+    # factor takes only the Frobenius scale)
+    scale = args.scale if wl in ("blocks_64x512", "mp_10000", "model_step") else "frobenius"
+    args.scale = scale
     opts = pmx.default_opts(max_iter=args.max_iter, degree=args.degree,
-                            degree_max=args.degree_max, method=args.method)
-    taylor = pmx.default_opts(max_iter=60, accelerate=0, degree=args.degree, method=args.method)
+                            degree_max=args.degree_max, method=args.method,
+                            scale_mode=SCALE_MODES[scale])
+    taylor = pmx.default_opts(max_iter=60, accelerate=0, degree=args.degree, method=args.method,
+                              scale_mode=SCALE_MODES[scale])
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None}
-    wl = args.workload
 
     def traced(fn):
         # one more call with the launch trace: per-class kernel ms and launches
@@ -180,7 +194,8 @@ def other_workload(args):
         for every in (1, 10):
             cfg = pmx.shampoo_config(block=1024, root_every=every, momentum=0.9,
                                      root_opts=pmx.default_opts(max_iter=args.max_iter,
-                                                                method=args.method))
+                                                                method=args.method,
+                                                                scale_mode=SCALE_MODES[args.scale]))
             plan = pmx.ShampooPlan(shapes, dev, cfg)
             t = [0]
 
@@ -221,7 +236,8 @@ def other_workload(args):
         # fp64 (the setting that meets 1e-4 at kappa = 1e6); value is the latter
         c = W.blocks_64x512()
         A = torch.from_numpy(c["A"]).to(dev)
-        o64 = pmx.default_opts(max_iter=args.max_iter, fp64_iters=4)
+        o64 = pmx.default_opts(max_iter=args.max_iter, fp64_iters=4,
+                               scale_mode=SCALE_MODES[args.scale])
         ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 64, pmx.F32, o64), dev)
         X = torch.empty_like(A)
         info = pmx.new_info(64, dev)
@@ -283,6 +299,7 @@ def other_workload(args):
                    iters=int(inf["iters"][0]), mfma_tflops=round(tf, 2),
                    mfma_frac=round(tf / PEAK_FP32_MFMA, 4))
     out["config"]["host_poll"] = args.host_poll
+    out["config"]["scale"] = args.scale
     print(json.dumps(out), flush=True)
 
 
@@ -428,7 +445,8 @@ def main():
     L9, R9 = L.clone(), R.clone()
     G = Gs[-1]
     opts = pmx.default_opts(max_iter=args.max_iter, degree=args.degree,
-                            degree_max=args.degree_max, method=args.method)
+                            degree_max=args.degree_max, method=args.method,
+                            scale_mode=SCALE_MODES[args.scale])
     wsL = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, m, m, 1, pmx.F32, opts), dev)
     wsR = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, opts), dev)
     wsA = pmx.workspace(pmx.workspace_bytes(pmx.OP_APPLY, m, n, 1, pmx.F32, None), dev)
@@ -470,7 +488,8 @@ def main():
 
     # ablation: the same R^-1/4 with the Taylor coefficient (classical Newton-Schulz)
     infoT = pmx.new_info(1, dev)
-    pmx.inv_root(R, 4, opts=pmx.default_opts(max_iter=60, accelerate=0), aux=False,
+    pmx.inv_root(R, 4, opts=pmx.default_opts(max_iter=60, accelerate=0,
+                                             scale_mode=SCALE_MODES[args.scale]), aux=False,
                  out=torch.empty_like(R), info=infoT, ws=wsR)
     gemmsR_taylor = int(pmx.parse_info(infoT)[0]["gemms"])
 
@@ -493,7 +512,8 @@ def main():
     # iteration (method 1), timed the same way
     newton = None
     if args.method == 0:
-        oN = pmx.default_opts(max_iter=args.max_iter, method=1)
+        oN = pmx.default_opts(max_iter=args.max_iter, method=1,
+                              scale_mode=SCALE_MODES[args.scale])
         wsN = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, 1, pmx.F32, oN), dev)
         infoN = pmx.new_info(1, dev)
         XN = torch.empty_like(R)
@@ -506,6 +526,23 @@ def main():
                                             / (msN * 1e-3) / 1e12, 2),
                       property_x4r_minus_i=prop_of(XN))
         log("inverse Newton R^-1/4:", newton)
+
+    # the same R^-1/4 with the other input scale, timed the same way
+    other_scale = None
+    if args.method == 0:
+        alt = "frobenius" if args.scale == "power" else "power"
+        oS = pmx.default_opts(max_iter=args.max_iter, degree=args.degree,
+                              degree_max=args.degree_max, scale_mode=SCALE_MODES[alt])
+        infoS = pmx.new_info(1, dev)
+        XS = torch.empty_like(R)
+        fnS = lambda: pmx.inv_root(R, 4, opts=oS, aux=False, out=XS, info=infoS, ws=wsR)
+        msS = timed(torch, fnS, args.steps, args.warmup)
+        iS = pmx.parse_info(infoS)[0]
+        other_scale = dict(scale=alt, ms=round(msS, 3), gemms=int(iS["gemms"]),
+                           iters=[int(x) for x in iS["iters"]],
+                           status=pmx.STATUS_NAMES[int(iS["status"])],
+                           property_x4r_minus_i=prop_of(XS))
+        log("R^-1/4 with the %s scale:" % alt, other_scale)
 
     roofline = None
     trace = None
@@ -557,6 +594,7 @@ def main():
                    "degree_max": args.degree_max, "method": args.method, "sketch_p": 8,
                    "tol": 1e-6,
                    "max_iter": args.max_iter, "host_poll": args.host_poll,
+                   "scale": args.scale,
                    "step": "restore L,R; stats update; L^-1/4; R^-1/4; apply"},
         "gemms_to_converge": {"R": gemmsR, "L": gemmsL, "R_taylor": gemmsR_taylor},
         "iters": {"R": [int(x) for x in iR["iters"]], "L": [int(x) for x in iL["iters"]]},
@@ -567,6 +605,7 @@ def main():
         "dense_equiv_tflops_r_root": round(dense_tflops_r, 2),
         "property_x4r_minus_i": prop,
         "inverse_newton_r_root": newton,
+        "r_root_other_scale": other_scale,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

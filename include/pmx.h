@@ -43,9 +43,11 @@ extern "C" {
 
 #define PMX_VERSION_MAJOR 0
 #define PMX_VERSION_MINOR 1
-#define PMX_OPTS_VERSION 3
+#define PMX_OPTS_VERSION 4
 #define PMX_METHOD_NEWTON_SCHULZ 0
 #define PMX_METHOD_INVERSE_NEWTON 1
+#define PMX_SCALE_FROBENIUS 0
+#define PMX_SCALE_POWER 1
 #define PMX_TRACE_LEN 64   /* alpha / residual trace entries kept per stage */
 #define PMX_MAX_SKETCH 16  /* largest supported sketch width p */
 
@@ -85,9 +87,10 @@ typedef enum {
  * Part II).  pmx_matfn_opts_default fills the defaults given per field.
  */
 typedef struct {
-  int32_t struct_version; /* PMX_OPTS_VERSION (3); 2 (48-byte layout, ending at
-                             degree_max) and 1 (40 bytes, ending at seed) are
-                             accepted with the later fields at their defaults */
+  int32_t struct_version; /* PMX_OPTS_VERSION (4); 3 (56-byte layout, ending at
+                             method), 2 (48 bytes, ending at degree_max) and 1
+                             (40 bytes, ending at seed) are accepted with the
+                             later fields at their defaults */
   int32_t degree;         /* d in {1, 2, 3}: g(xi) = f_{d-1}(xi) + alpha xi^d; default 2;
                              d = 3 runs on the fp32 paths only (the bf16 polar
                              factor and fp64_iters > 0 return NOT_SUPPORTED) */
@@ -129,6 +132,21 @@ typedef struct {
                              only (fp64_iters = 0, no adaptive degree); X_aux =
                              A X^{p-1} is formed after the iteration.  Ignored
                              by the polar factor.  Added in version 3. */
+  int32_t scale_mode;     /* inverse roots: the input scale c of Y_0 = A / c.
+                             PMX_SCALE_FROBENIUS (0, default): c = ||A||_F, an
+                             upper bound of the spectral norm.
+                             PMX_SCALE_POWER (1): c = ||A||_F min(1, 2 mu),
+                             mu = max_j ||K_8[:, j]|| / ||K_7[:, j]|| over the
+                             p columns of K_t = (A / ||A||_F)^t V_0 (eight
+                             skinny passes from a Gaussian block V_0 drawn as a
+                             sketch of stage 2), a lower bound of
+                             lambda_max / ||A||_F; so c stays within 2 lambda_max
+                             of the top eigenvalue and never exceeds ||A||_F.
+                             Flat spectra of large order (Shampoo statistics)
+                             start much closer to convergence.  The pages leave
+                             the scaling open.  The polar factor returns
+                             NOT_SUPPORTED for 1.  Added in version 4. */
+  int32_t reserved;       /* 0 */
 } pmx_matfn_opts;
 
 /*

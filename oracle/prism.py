@@ -306,7 +306,7 @@ def exact_sketch_fn():
 
 # The power estimate of the input scale (an option; the pages leave the
 # scaling open): the start block is the sketch of stage POWER_STAGE, k = 0.
-POWER_STAGE, POWER_PASSES, POWER_FACTOR = 2, 4, 2.0
+POWER_STAGE, POWER_PASSES, POWER_FACTOR = 2, 8, 2.0
 
 
 def power_scale(A, c, V0, passes=POWER_PASSES, factor=POWER_FACTOR):

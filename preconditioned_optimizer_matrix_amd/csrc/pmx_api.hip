@@ -235,6 +235,9 @@ bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out, int root_p = 0)
     } else if (in->struct_version == 2) {
       // the 48-byte layout, ending at degree_max (version 2's zero `reserved`)
       memcpy(&o, in, offsetof(pmx_matfn_opts, adapt_ratio));
+    } else if (in->struct_version == 3) {
+      // the 56-byte layout, ending at method
+      memcpy(&o, in, offsetof(pmx_matfn_opts, scale_mode));
     } else if (in->struct_version == PMX_OPTS_VERSION) {
       o = *in;
     } else {
@@ -272,6 +275,8 @@ bool resolve_opts(const pmx_matfn_opts* in, pmx_matfn_opts* out, int root_p = 0)
   }
   if (!isfinite(o.alpha_lo) || !isfinite(o.alpha_hi) || o.alpha_lo > o.alpha_hi) return false;
   if (!isfinite(o.tol) || o.tol < 0.f) return false;
+  if (o.scale_mode != PMX_SCALE_FROBENIUS && o.scale_mode != PMX_SCALE_POWER) return false;
+  if (o.reserved != 0) return false;
   *out = o;
   return true;
 }
@@ -418,6 +423,49 @@ SketchJob make_sketch(const IterLayout& L, void* ws, const IterCfg& cfg, int n, 
   sj.seed_lo = cfg.seed_lo;
   sj.seed_hi = cfg.seed_hi;
   return sj;
+}
+
+// The power estimate of the input scale (scale_mode 1): V_0 = the sketch of
+// stage kPowerStage, kPowerPasses skinny passes K_t = (A / c) K_{t-1} that
+// alternate between the column blocks [0, p) and [p, 2p) of the Krylov
+// buffer, and the update of c from the last two blocks.  The stage set-up
+// that follows takes Y_0 = A / c with the new c, and the outputs use it.
+hipError_t enqueue_power_scale(Enq& q, void* ws, const IterLayout& L, const IterCfg& cfg,
+                               const float* A, int lda, int64_t sa, int n, int batch) {
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  float* kbuf = at<float>(ws, L.kbuf);
+  const int pp = cfg.p;
+  const SketchJob sj = make_sketch(L, ws, cfg, n, 0, kPowerStage, true);
+  hipError_t e = q.run(PMX_KC_OTHER, [&] { return launch_sketch(sj, ctrl, batch, q.s); });
+  if (e != hipSuccess) return e;
+  SkinnyParams kp;
+  memset(&kp, 0, sizeof(kp));
+  kp.kbuf = kbuf;
+  kp.variant = q.h->skinny_variant;
+  kp.kld = L.kld;
+  kp.kstride = L.kstride;
+  kp.n = n;
+  kp.q = pp;
+  kp.ctrl = ctrl;
+  kp.gram_partials = at<double>(ws, L.gram);
+  kp.gram_stride = L.gstride;
+  kp.cfg = cfg;
+  for (int t = 0; t < kPowerPasses; ++t) {
+    SkinnyJob& j = kp.job[0];
+    j.mat = A;
+    j.mat_ld = lda;
+    j.mat_stride = sa;
+    j.in_col = (t & 1) ? pp : 0;
+    j.out_col = (t & 1) ? 0 : pp;
+    j.pow = 1;
+    e = q.run(PMX_KC_SKINNY, [&] { return launch_skinny(kp, 1, false, batch, q.s); });
+    if (e != hipSuccess) return e;
+  }
+  const int last = (kPowerPasses & 1) ? pp : 0;
+  return q.run(PMX_KC_OTHER, [&] {
+    return launch_power_scale(ctrl, kbuf, L.kld, L.kstride, n, pp, pp - last, last,
+                              kPowerFactor, cfg.info, batch, q.s);
+  });
 }
 
 // The power R^2 (d = 2) and the alpha fit of one PRISM update, shared by the
@@ -823,6 +871,8 @@ pmx_status pmx_matfn_opts_default(pmx_matfn_opts* o) {
   o->degree_max = 0;
   o->adapt_ratio = 0.3f;
   o->method = PMX_METHOD_NEWTON_SCHULZ;
+  o->scale_mode = PMX_SCALE_FROBENIUS;
+  o->reserved = 0;
   return PMX_OK;
 }
 
@@ -1139,7 +1189,8 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
 
   const int stages = (p == 4) ? 2 : 1;
   if (n <= kSmallMaxN && h->small_fused && o.fp64_iters == 0 &&
-      std::max(o.degree, o.degree_max) <= 2 && o.method == PMX_METHOD_NEWTON_SCHULZ) {
+      std::max(o.degree, o.degree_max) <= 2 && o.method == PMX_METHOD_NEWTON_SCHULZ &&
+      o.scale_mode == PMX_SCALE_FROBENIUS) {
     SmallRootParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.a = A;
@@ -1169,6 +1220,8 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
   PMX_TRY(q.run(PMX_KC_OTHER, [&] {
     return launch_fro_scale(A, false, n, n, lda, sa, batch, ctrl, partials, Lw.pstride, info, q.s);
   }));
+  if (o.scale_mode == PMX_SCALE_POWER)
+    PMX_TRY(enqueue_power_scale(q, ws, Lw, cfg, A, lda, sa, n, batch));
   if (o.method == PMX_METHOD_INVERSE_NEWTON)
     return enqueue_inverse_newton(q, ws, Lw, o, cfg, A, lda, sa, n, p, X, ldx, sx, XA, ldaux,
                                   saux, batch);
@@ -1442,6 +1495,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const bool tr = m < n;
   // d = 3 and the adaptive degree: fp32 only
   if (bf && std::max(o.degree, o.degree_max) == 3) return PMX_ERR_NOT_SUPPORTED;
+  if (o.scale_mode != PMX_SCALE_FROBENIUS) return PMX_ERR_NOT_SUPPORTED;
   const IterLayout Lw = iter_layout(rows, cols, batch, o, polar_bufs(dtype, o), 0, sizeof(float));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
@@ -1709,6 +1763,7 @@ pmx_status pmx_matfn_polar_varbatch(pmx_handle h, const pmx_polar_block* blocks,
   pmx_matfn_opts o;
   if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
   if (std::max(o.degree, o.degree_max) > 2) return PMX_ERR_NOT_SUPPORTED;
+  if (o.scale_mode != PMX_SCALE_FROBENIUS) return PMX_ERR_NOT_SUPPORTED;
   const int esz = dtype == PMX_BF16 ? 2 : 4;
   const size_t need = align_up(sizeof(pmx_polar_block) * (size_t)count);
   pmx_status st = check_ws(ws, ws_bytes, need);

@@ -278,6 +278,24 @@ hipError_t launch_sqrt_stage_init(const StageInitParams& p, int batch, hipStream
 hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hipStream_t s);
 hipError_t launch_skinny(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s);
 int skinny_blocks(int n, int q);
+// The power estimate of the input scale (inverse roots, scale_mode 1):
+// launch_sketch writes the start block V_0 (the sketch of `sj`, columns
+// [0, p) of the Krylov buffer) of every running matrix; after the skinny
+// passes K_t = (A / c) K_{t-1}, launch_power_scale sets
+// c <- c min(1, factor max_j ||K_t[:, j]|| / ||K_{t-1}[:, j]||) from the
+// column blocks at col_last (K_t) and col_prev (K_{t-1}).
+constexpr int kPowerStage = 2;   // sketch stream of V_0 (stages 0, 1 are the iteration's)
+// t = 8: an isolated top eigenvalue over a bulk below lambda_max / 2 gains
+// 2^16 over the bulk in the squared column norms, more than the 1 / n weight
+// it starts with for every order up to 32768, so mu >= lambda_max / 2 and c
+// stays above the spectrum
+constexpr int kPowerPasses = 8;
+constexpr double kPowerFactor = 2.0;
+hipError_t launch_sketch(const SketchJob& sj, const Ctrl* ctrl, int batch, hipStream_t s);
+hipError_t launch_power_scale(Ctrl* ctrl, const float* kbuf, int64_t kld, int64_t kstride,
+                              int n, int p, int col_prev, int col_last, double factor,
+                              pmx_matfn_info* info, int batch, hipStream_t s);
+
 // dst (pinned host memory, device-mapped) = 1 if any of ctrl[0 .. batch) is
 // still PMX_RUNNING, else 0; one block, a system-scope store.
 hipError_t launch_publish_running(const Ctrl* ctrl, int batch, int32_t* dst, hipStream_t s);

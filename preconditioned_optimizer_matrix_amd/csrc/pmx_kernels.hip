@@ -99,6 +99,7 @@ __global__ __launch_bounds__(NT) void fro_scale_kernel(const T* __restrict__ X, 
       Ctrl& c = ctrl[b];
       const double s = sqrt(tot);
       c.c = s;
+      c.fro = s;  // the Krylov scaling of a power estimate on A / c
       if (info) info[b].scale = (float)s;
       if (!(s > 0.0) || !isfinite(s)) {
         c.status = PMX_NONFINITE;
@@ -1036,6 +1037,60 @@ hipError_t launch_skinny(const SkinnyParams& pin, int njobs, bool gram, int batc
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- power scale
+__global__ __launch_bounds__(NT) void sketch_kernel(SketchJob sj, const Ctrl* ctrl) {
+  const int b = blockIdx.y;
+  if (load_status(ctrl + b) != PMX_RUNNING) return;
+  sketch_share(sj, b, blockIdx.x, gridDim.x);
+}
+
+// One block per matrix: per column j the fp64 norms of K_{t-1}[:, j] and
+// K_t[:, j] (fixed-order block sums), mu = the largest ratio, a lower bound
+// of the spectral norm of A / c; c shrinks by min(1, factor mu).
+__global__ __launch_bounds__(NT) void power_scale_kernel(Ctrl* ctrl, const float* kbuf,
+                                                         int64_t kld, int64_t kstride, int n,
+                                                         int p, int col_prev, int col_last,
+                                                         double factor, pmx_matfn_info* info) {
+  const int b = blockIdx.x;
+  Ctrl* cb = ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const float* k = kbuf + (int64_t)b * kstride;
+  __shared__ double red[NT / 64];
+  double mu = 0.0;
+  for (int j = 0; j < p; ++j) {
+    double s0 = 0.0, s1 = 0.0;
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const double a = (double)k[(int64_t)i * kld + col_prev + j];
+      const double c = (double)k[(int64_t)i * kld + col_last + j];
+      s0 += a * a;
+      s1 += c * c;
+    }
+    s0 = block_sum<NT / 64>(s0, red);
+    s1 = block_sum<NT / 64>(s1, red);
+    if (s0 > 0.0 && isfinite(s0) && isfinite(s1)) mu = fmax(mu, sqrt(s1 / s0));
+  }
+  if (threadIdx.x == 0 && mu > 0.0 && isfinite(mu)) {
+    cb->c *= fmin(1.0, factor * mu);
+    if (info) info[b].scale = (float)cb->c;
+  }
+}
+
+hipError_t launch_sketch(const SketchJob& sj, const Ctrl* ctrl, int batch, hipStream_t s) {
+  const int64_t calls = ((int64_t)sj.n * sj.p + 3) / 4;
+  int blocks = (int)((calls + NT - 1) / NT);
+  blocks = blocks < 1 ? 1 : (blocks > 64 ? 64 : blocks);
+  hipLaunchKernelGGL(sketch_kernel, dim3(blocks, batch), dim3(NT), 0, s, sj, ctrl);
+  return hipGetLastError();
+}
+
+hipError_t launch_power_scale(Ctrl* ctrl, const float* kbuf, int64_t kld, int64_t kstride,
+                              int n, int p, int col_prev, int col_last, double factor,
+                              pmx_matfn_info* info, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(power_scale_kernel, dim3(batch), dim3(NT), 0, s, ctrl, kbuf, kld, kstride,
+                     n, p, col_prev, col_last, factor, info);
   return hipGetLastError();
 }
 

@@ -19,8 +19,9 @@ RUNNING, CONVERGED, MAXITER, STAGNATED, NONFINITE, DIVERGED = -1, 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 OP_STATS, OP_INV_ROOT, OP_POLAR, OP_APPLY, OP_POLAR_VARBATCH = range(5)
 VARBATCH_MAX_DIM = 64
-OPTS_VERSION = 3
+OPTS_VERSION = 4
 METHOD_NEWTON_SCHULZ, METHOD_INVERSE_NEWTON = 0, 1
+SCALE_FROBENIUS, SCALE_POWER = 0, 1
 TRACE_LEN = 64
 MAX_SKETCH = 16
 STATUS_NAMES = {RUNNING: "RUNNING", CONVERGED: "CONVERGED", MAXITER: "MAXITER",
@@ -50,7 +51,8 @@ class Opts(ctypes.Structure):
                 ("alpha_hi", ctypes.c_float), ("tol", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("fp64_iters", ctypes.c_int32),
                 ("degree_max", ctypes.c_int32), ("adapt_ratio", ctypes.c_float),
-                ("method", ctypes.c_int32)]
+                ("method", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class ShampooConfig(ctypes.Structure):

@@ -30,8 +30,10 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header():
     from preconditioned_optimizer_matrix_amd import pmx
     # pmx_matfn_opts: 5 int32 + 3 float + uint64 (8-aligned) + 2 int32 + float
-    # + int32 = 56 bytes (version 2 ended at degree_max, version 1 at seed)
-    assert ctypes.sizeof(pmx.Opts) == 56
+    # + 3 int32 + reserved = 64 bytes (version 3 ended at method, version 2 at
+    # degree_max, version 1 at seed)
+    assert ctypes.sizeof(pmx.Opts) == 64
+    assert pmx.Opts.method.offset == 52 and pmx.Opts.scale_mode.offset == 56
     assert pmx.Opts.fp64_iters.offset == 40
     assert pmx.Opts.degree_max.offset == 44 and pmx.Opts.adapt_ratio.offset == 48
     # pmx_matfn_info: 6 int32 + 3 float + 4 * 64 float
@@ -51,6 +53,7 @@ def test_host_only_calls():
     assert math.isnan(o.alpha_lo) and math.isnan(o.alpha_hi)
     assert o.tol == pytest.approx(1e-6)
     assert (o.fp64_iters, o.method, o.struct_version) == (0, 0, pmx.OPTS_VERSION)
+    assert (o.scale_mode, o.reserved) == (pmx.SCALE_FROBENIUS, 0)
     assert o.degree_max == 0 and o.adapt_ratio == pytest.approx(0.3)
     assert pmx.lib.pmx_matfn_opts_default(None) == pmx.ERR_INVALID_VALUE
 
@@ -108,6 +111,14 @@ def test_workspace_sizes_and_option_validation():
     assert ws(struct_version=1, fp64_iters=7, method=5) == pmx.OK
     # version 2 (48 bytes): the fields after degree_max are not read
     assert ws(struct_version=2, adapt_ratio=float("nan"), method=5) == pmx.OK
+    # version 3 (56 bytes): scale_mode and reserved are not read
+    assert ws(struct_version=3, scale_mode=7, reserved=3) == pmx.OK
+    # the input scale: Frobenius or the power estimate
+    assert ws(scale_mode=pmx.SCALE_POWER) == pmx.OK
+    assert ws(scale_mode=pmx.SCALE_POWER, method=1) == pmx.OK
+    assert ws(scale_mode=2) == pmx.ERR_INVALID_VALUE
+    assert ws(scale_mode=-1) == pmx.ERR_INVALID_VALUE
+    assert ws(reserved=1) == pmx.ERR_INVALID_VALUE
     # adaptive degree: 2 -> 3 with the fitted alpha and fp32 updates only
     assert ws(degree_max=3) == pmx.OK
     assert ws(degree_max=2) == pmx.OK

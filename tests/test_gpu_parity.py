@@ -270,6 +270,49 @@ def test_inverse_newton(env, p):
     assert np.all(np.isnan(Xb[2].cpu().numpy()))
 
 
+def test_power_scale(env):
+    # scale_mode 1: c = ||A||_F min(1, 2 mu) from four power passes; the scale,
+    # the iteration counts and the roots against the oracle with the same
+    # start block (the sketch of stage 2)
+    torch, pmx, dev = env
+    P = pmx.SCALE_POWER
+    for n, lo in ((64, 0.5), (200, 0.5), (517, 0.2), (1024, 0.5)):
+        for p in (2, 4):
+            _say("power scale", n, p)
+            A, _, _ = W.spd_logu(n, 9000 + n, lo, 1.0)
+            X, XA, info = _run_root(env, A, p, seed=4, scale_mode=P)
+            _, _, ref_info = prism.inv_root(A.astype(np.float64), p,
+                                            sketch_fn=prism.make_sketch_fn(4, b=0, p=8),
+                                            scale="power")
+            ref, ref_aux = cf.inv_root(A, p)
+            assert int(info[0]["status"]) == pmx.CONVERGED, (n, p)
+            assert cf.rel_fro(X, ref) < 1e-4 and cf.rel_fro(XA, ref_aux) < 1e-4, (n, p)
+            assert float(info[0]["scale"]) == pytest.approx(ref_info["c"], rel=1e-5), (n, p)
+            for s_, st in enumerate(ref_info["stages"]):
+                assert abs(int(info[0]["iters"][s_]) - st.iters) <= 1, (n, p, s_)
+            # never more updates than the Frobenius scale
+            _, _, inf_f = _run_root(env, A, p, seed=4)
+            assert int(info[0]["iters"].sum()) <= int(inf_f[0]["iters"].sum()), (n, p)
+    # batched, a shared start block stream per matrix; the inverse Newton
+    # iteration and fp64 leading updates take the same scale
+    As = np.stack([W.spd_logu(300, 70 + b, 10.0 ** -b, 1.0)[0] for b in range(3)])
+    for kw in ({}, {"method": pmx.METHOD_INVERSE_NEWTON}, {"fp64_iters": 2}):
+        _say("power scale batched", kw)
+        Xb, _, infb = pmx.inv_root(torch.from_numpy(As).to(dev), 4,
+                                   opts=pmx.default_opts(scale_mode=P, seed=9, **kw))
+        torch.cuda.synchronize()
+        inf = pmx.parse_info(infb)
+        for b in range(3):
+            c_ref = prism.input_scale(As[b].astype(np.float64), "power",
+                                      prism.make_sketch_fn(9, b=b, p=8))
+            assert float(inf[b]["scale"]) == pytest.approx(c_ref, rel=1e-5), (kw, b)
+            assert cf.rel_fro(Xb[b].cpu().numpy(), cf.inv_root(As[b], 4)[0]) < 1e-4, (kw, b)
+    # the polar factor does not take it
+    with pytest.raises(pmx.PmxError):
+        pmx.polar(torch.from_numpy(W.gaussian(64, 32, 1)).to(dev),
+                  opts=pmx.default_opts(scale_mode=P))
+
+
 def test_polar_varbatch(env):
     # many small blocks of different shapes (tall, wide, square, 1 x 1, the
     # 64 limit) in one fused launch, against the SVD polar factor and, for a

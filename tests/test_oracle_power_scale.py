@@ -1,7 +1,7 @@
 """Pins of the oracle's power estimate of the input scale (oracle.prism.power_scale).
 
 The pages leave the scaling of Y_0 = A / c open; the option estimates the top
-eigenvalue with a few block power passes and sets c = ||A||_F min(1, 2 mu).
+eigenvalue with eight block power passes and sets c = ||A||_F min(1, 2 mu).
 Pinned here against values that do not come from the function itself: a
 brute-force per-eigenvalue formula on diagonal matrices, the closed forms for
 a scaled identity and a rank-one matrix, the norm bounds that hold for any
@@ -72,9 +72,26 @@ def test_bounds_on_random_spd(seed):
     # mu <= ||A / cF||_2, so c <= 2 lambda_max, and c <= cF always
     assert c <= cF * (1 + 1e-15)
     assert c <= 2.0 * lmax * (1 + 1e-12)
-    # four passes from eight Gaussian columns reach at least half of lambda_max
-    # here, so c is an upper bound of the spectrum
+    # eight passes from eight Gaussian columns reach at least half of
+    # lambda_max here, so c is an upper bound of the spectrum
     assert c >= lmax
+
+
+def test_isolated_top_eigenvalue():
+    # one eigenvalue 1 over a bulk of 0.45 at n = 4096: the start block puts a
+    # weight of about 1/n on the top direction, and eight passes raise it by
+    # (1/0.45)^16 ~ 3.5e5 against the bulk, so mu reaches the top and
+    # c = 2 mu ||A||_F covers it (four passes would stop near the bulk)
+    n = 4096
+    lam = np.full(n, 0.45)
+    lam[1234] = 1.0
+    cF = float(np.linalg.norm(lam))
+    V = prism.make_sketch_fn(0)(prism.POWER_STAGE, 0, n)
+    c8 = prism.power_scale(np.diag(lam), cF, V)
+    assert c8 == pytest.approx(_brute_diag(lam, cF, V, 8, 2.0), rel=1e-12)
+    assert 1.0 <= c8 <= 2.0
+    c4 = prism.power_scale(np.diag(lam), cF, V, passes=4)
+    assert c4 < c8
 
 
 def test_roots_and_iterations():
