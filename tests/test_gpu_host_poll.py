@@ -29,7 +29,8 @@ def _say(*a):
 
 def _calls(env):
     """Every fp32 update loop of the library (coupled roots with one and two
-    stages, the inverse Newton method, fp32 and bf16 polar), batched so that
+    stages, with the Frobenius and the estimated scale, the inverse Newton
+    method, fp32 and bf16 polar), batched so that
     the matrices converge at different updates; orders above the fused
     small-matrix path."""
     torch, pmx, dev = env
@@ -42,6 +43,9 @@ def _calls(env):
         out += [X, XA, info]
     X, XA, info = pmx.inv_root(torch.from_numpy(As).to(dev), 4,
                                opts=pmx.default_opts(method=pmx.METHOD_INVERSE_NEWTON))
+    out += [X, XA, info]
+    X, XA, info = pmx.inv_root(torch.from_numpy(As).to(dev), 4,
+                               opts=pmx.default_opts(scale_mode=pmx.SCALE_POWER))
     out += [X, XA, info]
     for G in (torch.from_numpy(Gs), Gb):
         U, info = pmx.polar(G.to(dev))

@@ -93,6 +93,28 @@ def test_shampoo_1024x4096(env):
     for info in (iL, iR):
         assert int(pmx.parse_info(info)[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
     assert eL < 1e-4 and eR < 1e-4 and eP < 1e-4
+    # the launch configuration bench.py times: the power-estimated scale with
+    # host polling at chunk 2; same tolerance, its scale against the oracle's
+    # estimate from the same start block, fewer updates
+    _say("shampoo_1024x4096: roots, power scale, host polling")
+    po = pmx.default_opts(scale_mode=pmx.SCALE_POWER)
+    pmx.set_host_poll(2)
+    try:
+        Lp, _, iLp = pmx.inv_root(L, 4, aux=False, opts=po)
+        Rp, _, iRp = pmx.inv_root(R, 4, aux=False, opts=po)
+        torch.cuda.synchronize()
+    finally:
+        pmx.set_host_poll(0)
+    ePL = cf.rel_fro(Lp.cpu().numpy(), Lref)
+    ePR = cf.rel_fro(Rp.cpu().numpy(), Rref)
+    _say("power scale errors L %.2e R %.2e" % (ePL, ePR))
+    assert ePL < 1e-4 and ePR < 1e-4
+    for M, info, info_f in ((Lg, iLp, iL), (Rg, iRp, iR)):
+        inf, inf_f = pmx.parse_info(info)[0], pmx.parse_info(info_f)[0]
+        assert int(inf["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+        c_ref = prism.input_scale(M.astype(np.float64), "power", prism.make_sketch_fn(0))
+        assert float(inf["scale"]) == pytest.approx(c_ref, rel=1e-5)
+        assert int(inf["iters"].sum()) < int(inf_f["iters"].sum())
 
 
 def test_blocks_64x512(env):
