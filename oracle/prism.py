@@ -375,14 +375,28 @@ def inv_root(A, p=2, d=2, lo=None, hi=None, tol=1e-6, max_iter=30,
     return Z2 * c ** -0.25, Y2 * c ** 0.25, dict(status=status, stages=stages, c=c)
 
 
+def polar_power_scale(R0, V0, passes=POWER_PASSES, factor=POWER_FACTOR):
+    """s with s^2 = min(1, factor mu), mu the largest column growth ratio of
+    K_t = (I - R0) K_{t-1} = X0^T X0 K_{t-1} from K_0 = V0 (power_scale on
+    X0^T X0 with c = 1): X0 / s has its top singular value at most 1 once mu
+    reaches half of the top eigenvalue of X0^T X0."""
+    M = np.eye(R0.shape[0]) - np.asarray(R0, np.float64)
+    return sqrt(power_scale(M, 1.0, V0, passes, factor))
+
+
 def polar(G, d=2, lo=None, hi=None, tol=1e-6, max_iter=30, sketch_fn=None,
-          accelerate=True, degree_max=None, adapt_ratio=0.3):
+          accelerate=True, degree_max=None, adapt_ratio=0.3, scale="frobenius"):
     """PRISM polar factor of G (m x n).  Wide inputs are handled through G^T.
-    R_k = I - X_k^T X_k, X_{k+1} = X_k g.  Returns (U, info)."""
+    R_k = I - X_k^T X_k, X_{k+1} = X_k g.  X_0 = G / c with c = ||G||_F; with
+    scale="power" X_0 is then divided by s = polar_power_scale(R_0, V_0)
+    (V_0 the sketch of stage POWER_STAGE), c becomes c s and R_0 is formed
+    again.  Returns (U, info)."""
     G = np.asarray(G, np.float64)
+    if scale not in ("frobenius", "power"):
+        raise ValueError("scale must be 'frobenius' or 'power'")
     if G.shape[0] < G.shape[1]:
         U, info = polar(G.T, d, lo, hi, tol, max_iter, sketch_fn, accelerate, degree_max,
-                        adapt_ratio)
+                        adapt_ratio, scale)
         return U.T, info
     rule = DegreeRule(d, lo, hi, degree_max, adapt_ratio)
     if sketch_fn is None:
@@ -397,6 +411,12 @@ def polar(G, d=2, lo=None, hi=None, tol=1e-6, max_iter=30, sketch_fn=None,
     X = G / c
     R = I - X.T @ X
     tr.gemms += 1
+    if scale == "power":
+        sc = polar_power_scale(R, sketch_fn(POWER_STAGE, 0, n))
+        if sc < 1.0:
+            X = X / sc
+            R = I - X.T @ X
+            c *= sc
     k = 0
     while True:
         r = float(np.linalg.norm(R) / sqrt(n))

@@ -124,3 +124,40 @@ def test_roots_and_iterations():
     assert inf["status"] == prism.CONVERGED and inf["c"] < inf_f["c"]
     with pytest.raises(ValueError):
         prism.inv_root(A, 2, scale="spectral")
+
+
+def test_polar_scale():
+    # G with orthogonal columns of norm a: X_0^T X_0 = I / n, every ratio is
+    # 1 / n, s^2 = 2 / n, so X_0 / s has singular values 1 / sqrt(2)
+    n = 32
+    Q = np.linalg.qr(np.random.default_rng(8).standard_normal((128, n)))[0]
+    G = 3.0 * Q
+    X0 = G / np.linalg.norm(G)
+    R0 = np.eye(n) - X0.T @ X0
+    V = prism.make_sketch_fn(1)(prism.POWER_STAGE, 0, n)
+    s = prism.polar_power_scale(R0, V)
+    assert s == pytest.approx(np.sqrt(2.0 / n), rel=1e-12)
+    assert np.linalg.svd(X0 / s, compute_uv=False) == pytest.approx(np.full(n, 2 ** -0.5),
+                                                                    rel=1e-12)
+    # the scale shrinks c only, the factor matches the SVD, fewer updates on a
+    # spread spectrum (the Muon workload's geometric singular values)
+    rng = np.random.default_rng(9)
+    U0 = np.linalg.qr(rng.standard_normal((512, 256)))[0]
+    V0 = np.linalg.qr(rng.standard_normal((256, 256)))[0]
+    G = (U0 * np.geomspace(1e-3, 1.0, 256)) @ V0.T
+    sk = prism.make_sketch_fn(2)
+    Up, ip = prism.polar(G, sketch_fn=sk, tol=1e-12, max_iter=60, scale="power")
+    assert cf.rel_fro(Up, cf.polar(G)[0]) < 1e-9
+    _, ip = prism.polar(G, sketch_fn=sk, tol=1e-2, scale="power")
+    _, i_f = prism.polar(G, sketch_fn=sk, tol=1e-2)
+    assert ip["c"] < i_f["c"]
+    assert ip["stages"][0].iters < i_f["stages"][0].iters
+    # s never exceeds 1 (X_0^T X_0 has eigenvalues at most 1)
+    for seed in range(3):
+        Gr = np.random.default_rng(seed).standard_normal((96, 40))
+        X0 = Gr / np.linalg.norm(Gr)
+        V40 = prism.make_sketch_fn(seed)(prism.POWER_STAGE, 0, 40)
+        assert prism.polar_power_scale(np.eye(40) - X0.T @ X0, V40) <= 1.0
+    # wide inputs go through G^T with the same scale
+    Uw, iw = prism.polar(G.T, sketch_fn=sk, tol=1e-12, max_iter=60, scale="power")
+    assert cf.rel_fro(Uw, cf.polar(G.T)[0]) < 1e-9 and iw["c"] == pytest.approx(ip["c"])
