@@ -141,8 +141,8 @@ def other_workload(args):
     torch.cuda.set_device(dev)
     pmx.set_host_poll(args.host_poll)
     wl = args.workload
-    # the power scale applies to the inverse roots of order above 64 (order 64
-    # runs the fused single-launch kernel, which scales by ||A||_F; the polar
+    # the power scale applies to the fp32 calls above order 64 (order 64 runs
+    # the fused single-launch kernel, which scales by ||A||_F; the bf16 polar
     # factor takes only the Frobenius scale)
     scale = args.scale if wl in ("blocks_64x512", "mp_10000", "model_step") else "frobenius"
     args.scale = scale
@@ -262,7 +262,7 @@ def other_workload(args):
     elif wl == "muon_32x4096x1024":
         c = W.muon_32x4096x1024()
         G = torch.from_numpy(c["G_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
-        o = pmx.default_opts(max_iter=args.max_iter, tol=c["tol"])
+        o = pmx.default_opts(max_iter=args.max_iter, tol=c["tol"], scale_mode=SCALE_MODES[scale])
         ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_POLAR, 4096, 1024, 32, pmx.BF16, o), dev)
         U = torch.empty_like(G)
         info = pmx.new_info(32, dev)
@@ -271,7 +271,7 @@ def other_workload(args):
         inf = pmx.parse_info(info)
         it = int(inf["iters"][:, 0].max())
         out["kernel_trace_ms"] = traced(lambda: fn(o))
-        fn(pmx.default_opts(max_iter=60, tol=c["tol"], accelerate=0))
+        fn(pmx.default_opts(max_iter=60, tol=c["tol"], accelerate=0, scale_mode=SCALE_MODES[scale]))
         tit = int(pmx.parse_info(info)["iters"][:, 0].max())
         # per update: X^T X (4096 x 1024 x 1024), R^2 (1024^3), X g (4096 x 1024 x 1024)
         flops = 32 * (2.0 * 4096 * 1024 * 1024 * (2 * it + 1) + 2.0 * 1024 ** 3 * it)

@@ -132,7 +132,7 @@ typedef struct {
                              only (fp64_iters = 0, no adaptive degree); X_aux =
                              A X^{p-1} is formed after the iteration.  Ignored
                              by the polar factor.  Added in version 3. */
-  int32_t scale_mode;     /* inverse roots: the input scale c of Y_0 = A / c.
+  int32_t scale_mode;     /* the input scale c of Y_0 = A / c (inverse roots).
                              PMX_SCALE_FROBENIUS (0, default): c = ||A||_F, an
                              upper bound of the spectral norm.
                              PMX_SCALE_POWER (1): c = ||A||_F min(1, 2 mu),
@@ -143,9 +143,17 @@ typedef struct {
                              lambda_max / ||A||_F; so c stays within 2 lambda_max
                              of the top eigenvalue and never exceeds ||A||_F.
                              Flat spectra of large order (Shampoo statistics)
-                             start much closer to convergence.  The pages leave
-                             the scaling open.  The polar factor returns
-                             NOT_SUPPORTED for 1.  Added in version 4. */
+                             start much closer to convergence.  The fp32
+                             polar factor with 1: X_0 = G / ||G||_F is divided
+                             by s, s^2 = min(1, 2 mu) from the same passes on
+                             X_0^T X_0 = I - R_0, R_0 is rewritten for X_0 / s
+                             and 1 / s is folded into the first g.  The bf16
+                             polar factor and the variable-size one return
+                             NOT_SUPPORTED for 1 (bf16 rounding of X, amplified
+                             while the top singular values overshoot under the
+                             largest alpha, made the iteration diverge).
+                             Order-64 calls with 1 leave the fused kernel.  The
+                             pages leave the scaling open.  Added in version 4. */
   int32_t reserved;       /* 0 */
 } pmx_matfn_opts;
 

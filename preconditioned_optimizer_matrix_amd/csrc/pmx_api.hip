@@ -464,7 +464,61 @@ hipError_t enqueue_power_scale(Enq& q, void* ws, const IterLayout& L, const Iter
   const int last = (kPowerPasses & 1) ? pp : 0;
   return q.run(PMX_KC_OTHER, [&] {
     return launch_power_scale(ctrl, kbuf, L.kld, L.kstride, n, pp, pp - last, last,
-                              kPowerFactor, cfg.info, batch, q.s);
+                              kPowerFactor, 0, cfg.info, batch, q.s);
+  });
+}
+
+// The estimated scale of the polar factor (scale_mode 1), after the first
+// residual R_0 = I - X_0^T X_0: V_0 (the sketch of stage kPowerStage) in the
+// Krylov columns [2p, 3p) -- [0, p) holds S_0 --, kPowerPasses complement
+// passes K_t = K_{t-1} - R_0 K_{t-1} = X_0^T X_0 K_{t-1} between [2p, 3p) and
+// [3p, 4p), s^2 = min(1, 2 mu), then R_0 <- I - (I - R_0) / s^2 in place
+// (and its bf16 copy rh) with the decision on r_0 again.  X_0 itself is not
+// touched: the first update multiplies by g / s (form_g's first_scale).
+hipError_t enqueue_polar_scale(Enq& q, void* ws, const IterLayout& L, const IterCfg& cfg,
+                               float* R, uint16_t* rh, int n, int batch) {
+  Ctrl* ctrl = at<Ctrl>(ws, L.ctrl);
+  float* kbuf = at<float>(ws, L.kbuf);
+  const int pp = cfg.p;
+  const int c0 = 2 * pp, c1 = 3 * pp;
+  if ((int64_t)4 * pp > L.kld) return hipErrorInvalidValue;
+  SketchJob sj = make_sketch(L, ws, cfg, n, 0, kPowerStage, true);
+  sj.col = c0;
+  hipError_t e = q.run(PMX_KC_OTHER, [&] { return launch_sketch(sj, ctrl, batch, q.s); });
+  if (e != hipSuccess) return e;
+  SkinnyParams kp;
+  memset(&kp, 0, sizeof(kp));
+  kp.kbuf = kbuf;
+  kp.variant = q.h->skinny_variant;
+  kp.kld = L.kld;
+  kp.kstride = L.kstride;
+  kp.n = n;
+  kp.q = pp;
+  kp.ctrl = ctrl;
+  kp.gram_partials = at<double>(ws, L.gram);
+  kp.gram_stride = L.gstride;
+  kp.cfg = cfg;
+  for (int t = 0; t < kPowerPasses; ++t) {
+    SkinnyJob& j = kp.job[0];
+    j.mat = R;
+    j.mat_ld = n;
+    j.mat_stride = L.buf_stride;
+    j.in_col = (t & 1) ? c1 : c0;
+    j.out_col = (t & 1) ? c0 : c1;
+    j.pow = 0;
+    e = q.run(PMX_KC_SKINNY, [&] { return launch_skinny(kp, 1, false, batch, q.s); });
+    if (e != hipSuccess) return e;
+  }
+  const int last = (kPowerPasses & 1) ? c1 : c0;
+  const int prev = (kPowerPasses & 1) ? c0 : c1;
+  e = q.run(PMX_KC_OTHER, [&] {
+    return launch_power_scale(ctrl, kbuf, L.kld, L.kstride, n, pp, prev, last, kPowerFactor, 1,
+                              cfg.info, batch, q.s);
+  });
+  if (e != hipSuccess) return e;
+  return q.run(PMX_KC_OTHER, [&] {
+    return launch_polar_rescale(ctrl, R, rh, L.buf_stride, n, at<double>(ws, L.partials),
+                                L.pstride, cfg, batch, q.s);
   });
 }
 
@@ -1495,7 +1549,13 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const bool tr = m < n;
   // d = 3 and the adaptive degree: fp32 only
   if (bf && std::max(o.degree, o.degree_max) == 3) return PMX_ERR_NOT_SUPPORTED;
-  if (o.scale_mode != PMX_SCALE_FROBENIUS) return PMX_ERR_NOT_SUPPORTED;
+  const bool pscale = o.scale_mode == PMX_SCALE_POWER;
+  // the estimated scale is fp32 only: with X in bf16 it diverged on one of the
+  // 32 Muon matrices (the top eigenvalues of R sit in the overshoot band near
+  // xi = -0.25 from the first update on, where r(xi; alpha) at the upper alpha
+  // bound expands perturbations about 1.8x per update, and bf16 rounding of X
+  // is large enough to be driven past it)
+  if (bf && pscale) return PMX_ERR_NOT_SUPPORTED;
   const IterLayout Lw = iter_layout(rows, cols, batch, o, polar_bufs(dtype, o), 0, sizeof(float));
   pmx_status st = check_ws(ws, ws_bytes, Lw.total);
   if (st != PMX_OK) return st;
@@ -1525,7 +1585,8 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
   const bool acc = o.accelerate != 0;
   const int64_t bs = Lw.buf_stride;
 
-  if (!bf && rows <= kSmallMaxN && h->small_fused && std::max(o.degree, o.degree_max) <= 2) {
+  if (!bf && rows <= kSmallMaxN && h->small_fused && std::max(o.degree, o.degree_max) <= 2 &&
+      !pscale) {
     SmallPolarParams sp;
     memset(&sp, 0, sizeof(sp));
     sp.g = (const float*)G;
@@ -1583,6 +1644,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       return q.run(PMX_KC_GEMM_RESID, [&] { return launch_gemm_f32(r, true, false, ROLE_RESID, q.s); });
     };
     PMX_TRY(residual(Xb[0], 1, 0));
+    if (pscale) PMX_TRY(enqueue_polar_scale(q, ws, Lw, cfg, Rb, nullptr, cols, batch));
     Poller poll(q, ctrl, batch);
     for (int k = 0; k < o.max_iter; ++k) {
       bool stop = false;
@@ -1614,6 +1676,7 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
         fp.c0 = (float)taylor(0);
         fp.c1 = (float)taylor(1);
         fp.ctrl = ctrl;
+        fp.first_scale = pscale && k == 0;
         fp.sketch = make_sketch(Lw, ws, cfg, cols, k + 1, 0, acc && k + 1 < o.max_iter);
         PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g(fp, batch, q.s); }));
         u.prob[0].b = {R2b, cols, bs, nullptr, 0};

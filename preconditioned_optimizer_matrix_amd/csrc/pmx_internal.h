@@ -20,6 +20,7 @@ struct Ctrl {
   double r_prev;     // r_{k-1}
   double fro;        // ||R_k||_F of the current residual (Krylov scaling)
   double alpha;      // alpha_k of the current update
+  double inv_s;      // polar factor, estimated scale: 1 / s folded into the first g (0: none)
   int32_t status;    // PMX_RUNNING while the current stage iterates
   int32_t status_all;// worst outcome of the finished stages
   int32_t iter;      // updates done in the current stage
@@ -174,6 +175,7 @@ struct SketchJob {
   int64_t kld, kstride;
   int n, p, k, stage;
   uint32_t seed_lo, seed_hi;
+  int col;          // first column of the block written (0: the sketch S_k)
 };
 
 // Philox calls [q0, q1) of the sketch of matrix b: element e = i p + j takes
@@ -199,7 +201,7 @@ __device__ __forceinline__ void sketch_calls(const SketchJob& sj, int b, int64_t
       const int64_t e = q * 4 + w;
       if (e < total) {
         const int i = (int)(e / sj.p), j = (int)(e - (int64_t)i * sj.p);
-        kb[(int64_t)i * sj.kld + j] = (float)z[w];
+        kb[(int64_t)i * sj.kld + sj.col + j] = (float)z[w];
       }
     }
   }

@@ -62,7 +62,8 @@ struct SkinnyJob {
   const float* mat;
   int64_t mat_ld, mat_stride;
   int in_col, out_col;
-  int pow;               // output scaled by ||R||_F^-pow
+  int pow;               // output scaled by ||R||_F^-pow; 0: the complement
+                         // in - Mat in, unscaled
 };
 
 // Coefficient vectors of r(xi; alpha) = sum_j (a0_j + alpha a1_j + alpha^2 a2_j) xi^j.
@@ -113,6 +114,7 @@ struct FormGParams {
   int vec;               // set by the launcher
   float c0, c1, c2;      // Taylor coefficients c_0 .. c_{d-1} (c2 for d = 3)
   int adaptive;          // 1: each matrix's degree from its control block
+  int first_scale;       // 1: g times the control block's inv_s (polar, estimated scale)
   Ctrl* ctrl;
   SketchJob sketch;      // the next iteration's sketch, generated on the side
 };
@@ -292,9 +294,18 @@ constexpr int kPowerStage = 2;   // sketch stream of V_0 (stages 0, 1 are the it
 constexpr int kPowerPasses = 8;
 constexpr double kPowerFactor = 2.0;
 hipError_t launch_sketch(const SketchJob& sj, const Ctrl* ctrl, int batch, hipStream_t s);
+// polar = 0: c <- c min(1, factor mu); polar = 1 (mu estimates the top
+// eigenvalue of X_0^T X_0): s = sqrt(min(1, factor mu)), inv_s = 1 / s and
+// c <- c s.
 hipError_t launch_power_scale(Ctrl* ctrl, const float* kbuf, int64_t kld, int64_t kstride,
                               int n, int p, int col_prev, int col_last, double factor,
-                              pmx_matfn_info* info, int batch, hipStream_t s);
+                              int polar, pmx_matfn_info* info, int batch, hipStream_t s);
+// Polar factor with the estimated scale: R_0 <- I - (I - R_0) inv_s^2 (fp32
+// R and, when rh is set, its bf16 copy) for the matrices with inv_s > 1, and
+// the decision on r_0 again from the new ||R_0||_F (same stage, k = 0).
+hipError_t launch_polar_rescale(Ctrl* ctrl, float* r, uint16_t* rh, int64_t stride, int n,
+                                double* partials, int64_t pstride, IterCfg cfg, int batch,
+                                hipStream_t s);
 
 // dst (pinned host memory, device-mapped) = 1 if any of ctrl[0 .. batch) is
 // still PMX_RUNNING, else 0; one block, a system-scope store.

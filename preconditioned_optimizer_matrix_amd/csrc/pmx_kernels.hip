@@ -30,6 +30,7 @@ __global__ void ctrl_reset_kernel(Ctrl* ctrl, pmx_matfn_info* info, int batch, i
     c.r_prev = 0.0;
     c.fro = 0.0;
     c.alpha = 0.0;
+    c.inv_s = 0.0;
     c.status = PMX_RUNNING;
     c.status_all = PMX_CONVERGED;
     c.iter = 0;
@@ -229,6 +230,11 @@ constexpr int SK_LD = SK_CH + 4;     // column stride of the staged chunk
 
 // Reduction, output and (GJ != 0) Gram share / alpha fit of a skinny product:
 // acc holds the lane's RW x Q partial sums for rows row0 .. row0 + RW - 1.
+// The output factor of a skinny product: ||R||_F^-pow, 1 for the complement.
+__device__ __forceinline__ float skinny_scale(int pow, double fro) {
+  return (float)(pow == 1 ? 1.0 / fro : pow == 2 ? 1.0 / (fro * fro) : 1.0);
+}
+
 template <int Q, int RW, int GJ, int NW = NT / 64>
 __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const SkinnyParams& p,
                                               const SkinnyJob& job, int b, int row0,
@@ -252,6 +258,7 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     vcol[i] = c;
     valid[i] = (lane % SHARE) == 0 && vrow[i] < n && c < p.q;
     acc[i] *= scale;
+    if (job.pow == 0 && valid[i]) acc[i] = kb[(int64_t)vrow[i] * p.kld + job.in_col + c] - acc[i];
     if (valid[i]) kb[(int64_t)vrow[i] * p.kld + job.out_col + c] = acc[i];
   }
 
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(W * 64) void skinny_mfma_kernel(SkinnyParams p) {
   const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
   float* kb = p.kbuf + (int64_t)b * p.kstride;
   const double fro = cb->fro;
-  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+  const float scale = skinny_scale(job.pow, fro);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r = lane & 15, slot = lane >> 4;
   const int row0 = blockIdx.x * 16;
@@ -450,7 +457,7 @@ __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
   float* kb = p.kbuf + (int64_t)b * p.kstride;
   const double fro = cb->fro;
-  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+  const float scale = skinny_scale(job.pow, fro);
 
   __shared__ __attribute__((aligned(16))) float in_lds[Q * SK_LD];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(NT) void skinny_pipe_kernel(SkinnyParams p) {
   const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
   const float* __restrict__ in = p.kbuf + (int64_t)b * p.kstride + job.in_col;
   const double fro = cb->fro;
-  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+  const float scale = skinny_scale(job.pow, fro);
   __shared__ __attribute__((aligned(16))) float in_lds[2][Q * LD];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int row0 = blockIdx.x * RB + wid * RW;
@@ -661,7 +668,7 @@ __global__ __launch_bounds__(NT) void skinny_stream_kernel(SkinnyParams p) {
   const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
   const float* __restrict__ in = p.kbuf + (int64_t)b * p.kstride + job.in_col;
   const double fro = cb->fro;
-  const float scale = (float)(job.pow == 1 ? 1.0 / fro : 1.0 / (fro * fro));
+  const float scale = skinny_scale(job.pow, fro);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int row0 = blockIdx.x * RB + wid * RW;
   const bool vec = (job.mat_ld % 4 == 0) && ((((uintptr_t)mat) & 15) == 0) && (n % 4 == 0) &&
@@ -723,7 +730,9 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   const Ctrl* cb = p.ctrl + b;
   if (load_status(cb) != PMX_RUNNING) return;
   sketch_share(p.sketch, b, blockIdx.x, gridDim.x);
-  const float alpha = (float)cb->alpha;
+  // the estimated scale of the polar factor: g / s in the first update
+  const float fs = p.first_scale && cb->inv_s > 0.0 ? (float)cb->inv_s : 1.f;
+  const float alpha = fs * (float)cb->alpha;
   const int n = p.n;
   const float* R = p.r + (int64_t)b * p.stride;
   const float* R2 = p.r2 ? p.r2 + (int64_t)b * p.stride : nullptr;
@@ -731,7 +740,7 @@ __global__ __launch_bounds__(NT) void form_g_kernel(FormGParams p) {
   uint16_t* Gh = p.dst_bf16 ? reinterpret_cast<uint16_t*>(p.dst) + (int64_t)b * p.stride : nullptr;
   float* G2 = p.dst2 ? p.dst2 + (int64_t)b * p.stride : nullptr;
   const float* R3 = p.r3 ? p.r3 + (int64_t)b * p.stride : nullptr;
-  const float c0 = p.c0, c1 = p.c1, c2 = p.c2;
+  const float c0 = fs * p.c0, c1 = fs * p.c1, c2 = fs * p.c2;
   const int deg = p.adaptive ? *(const volatile int32_t*)&cb->degree : p.degree;
   const bool d1 = deg == 1, d3 = deg == 3;
   if (p.vec) {
@@ -1053,7 +1062,8 @@ __global__ __launch_bounds__(NT) void sketch_kernel(SketchJob sj, const Ctrl* ct
 __global__ __launch_bounds__(NT) void power_scale_kernel(Ctrl* ctrl, const float* kbuf,
                                                          int64_t kld, int64_t kstride, int n,
                                                          int p, int col_prev, int col_last,
-                                                         double factor, pmx_matfn_info* info) {
+                                                         double factor, int polar,
+                                                         pmx_matfn_info* info) {
   const int b = blockIdx.x;
   Ctrl* cb = ctrl + b;
   if (load_status(cb) != PMX_RUNNING) return;
@@ -1073,8 +1083,46 @@ __global__ __launch_bounds__(NT) void power_scale_kernel(Ctrl* ctrl, const float
     if (s0 > 0.0 && isfinite(s0) && isfinite(s1)) mu = fmax(mu, sqrt(s1 / s0));
   }
   if (threadIdx.x == 0 && mu > 0.0 && isfinite(mu)) {
-    cb->c *= fmin(1.0, factor * mu);
+    const double f = fmin(1.0, factor * mu);
+    if (polar) {
+      const double sc = sqrt(f);
+      cb->inv_s = 1.0 / sc;
+      cb->c *= sc;
+    } else {
+      cb->c *= f;
+    }
     if (info) info[b].scale = (float)cb->c;
+  }
+}
+
+__global__ __launch_bounds__(NT) void polar_rescale_kernel(Ctrl* ctrl, float* r, uint16_t* rh,
+                                                           int64_t stride, int n,
+                                                           double* partials, int64_t pstride,
+                                                           IterCfg cfg) {
+  const int b = blockIdx.y;
+  Ctrl* cb = ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const double is = cb->inv_s;
+  if (!(is > 1.0)) return;  // uniform over the matrix's blocks
+  const float f = (float)(is * is);
+  float* R = r + (int64_t)b * stride;
+  uint16_t* H = rh ? rh + (int64_t)b * stride : nullptr;
+  double acc = 0.0;
+  for (int i = blockIdx.x; i < n; i += gridDim.x)
+    for (int j = threadIdx.x; j < n; j += NT) {
+      const int64_t e = (int64_t)i * n + j;
+      const float id = i == j ? 1.f : 0.f;
+      const float v = id - (id - R[e]) * f;
+      R[e] = v;
+      if (H) H[e] = from_f32<bf16_t>(v).bits;
+      acc += (double)v * (double)v;
+    }
+  __shared__ double red[NT / 64];
+  const double bs = block_sum<NT / 64>(acc, red);
+  double tot;
+  if (last_block_sum<NT / 64>(bs, partials + (int64_t)b * pstride, &cb->counter, gridDim.x,
+                              blockIdx.x, red, &tot)) {
+    if (threadIdx.x == 0) decide(*cb, cfg, cfg.info ? cfg.info + b : nullptr, tot);
   }
 }
 
@@ -1088,9 +1136,18 @@ hipError_t launch_sketch(const SketchJob& sj, const Ctrl* ctrl, int batch, hipSt
 
 hipError_t launch_power_scale(Ctrl* ctrl, const float* kbuf, int64_t kld, int64_t kstride,
                               int n, int p, int col_prev, int col_last, double factor,
-                              pmx_matfn_info* info, int batch, hipStream_t s) {
+                              int polar, pmx_matfn_info* info, int batch, hipStream_t s) {
   hipLaunchKernelGGL(power_scale_kernel, dim3(batch), dim3(NT), 0, s, ctrl, kbuf, kld, kstride,
-                     n, p, col_prev, col_last, factor, info);
+                     n, p, col_prev, col_last, factor, polar, info);
+  return hipGetLastError();
+}
+
+hipError_t launch_polar_rescale(Ctrl* ctrl, float* r, uint16_t* rh, int64_t stride, int n,
+                                double* partials, int64_t pstride, IterCfg cfg, int batch,
+                                hipStream_t s) {
+  dim3 grid(grid_rows(n, kPartialsPerMatrix), batch);
+  hipLaunchKernelGGL(polar_rescale_kernel, grid, dim3(NT), 0, s, ctrl, r, rh, stride, n,
+                     partials, pstride, cfg);
   return hipGetLastError();
 }
 

@@ -251,6 +251,7 @@ __device__ void small_start(SmallShared& sh, pmx_matfn_info* info, double fro2, 
     c.r_prev = 0.0;
     c.fro = 0.0;
     c.alpha = 0.0;
+    c.inv_s = 0.0;
     c.status = PMX_RUNNING;
     c.status_all = PMX_CONVERGED;
     c.iter = 0;

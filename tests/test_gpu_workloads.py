@@ -149,26 +149,38 @@ def test_muon_32x4096x1024(env):
     c = W.muon_32x4096x1024()
     bits = torch.from_numpy(c["G_bits"].view(np.int16)).view(torch.bfloat16)
     G = bits.to(dev)
-    _say("muon_32x4096x1024: polar")
-    U, info = pmx.polar(G, opts=pmx.default_opts(tol=c["tol"]))
-    torch.cuda.synchronize()
-    inf = pmx.parse_info(info)
-    Un = U.float().cpu().numpy()
     sigma = c["sigma"]
-    worst_o = worst_h = 0.0
+    Hs = []
     for b in range(32):
         rng = W.rngs(401, 32)[b]
         _ = W.random_orthogonal(rng, 4096, 1024)
         V = W.random_orthogonal(rng, 1024)
-        H = (V * sigma) @ V.T
-        Ub = Un[b].astype(np.float64)
-        o = np.linalg.norm(Ub.T @ Ub - np.eye(1024)) / np.sqrt(1024)
-        h = cf.rel_fro(Ub.T @ c["G"][b].astype(np.float64), H)
-        worst_o, worst_h = max(worst_o, o), max(worst_h, h)
-        assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
-    _say("muon: worst orthogonality %.2e, worst H error %.2e, iters %s" % (
-        worst_o, worst_h, sorted(set(int(i) for i in inf["iters"][:, 0]))))
-    assert worst_o <= 1e-2 and worst_h <= 3e-2
+        Hs.append((V * sigma) @ V.T)
+    # enqueue-ahead, then host polling (bench.py's setting): the same
+    # properties and update counts
+    iters = {}
+    for name, kw, poll in (("enqueue-ahead", {}, 0), ("host polling", {}, 2)):
+        _say("muon_32x4096x1024: polar, %s" % name)
+        pmx.set_host_poll(poll)
+        try:
+            U, info = pmx.polar(G, opts=pmx.default_opts(tol=c["tol"], **kw))
+            torch.cuda.synchronize()
+        finally:
+            pmx.set_host_poll(0)
+        inf = pmx.parse_info(info)
+        Un = U.float().cpu().numpy()
+        worst_o = worst_h = 0.0
+        for b in range(32):
+            Ub = Un[b].astype(np.float64)
+            o = np.linalg.norm(Ub.T @ Ub - np.eye(1024)) / np.sqrt(1024)
+            h = cf.rel_fro(Ub.T @ c["G"][b].astype(np.float64), Hs[b])
+            worst_o, worst_h = max(worst_o, o), max(worst_h, h)
+            assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+        iters[name] = inf["iters"][:, 0].astype(int)
+        _say("muon %s: worst orthogonality %.2e, worst H error %.2e, iters %s" % (
+            name, worst_o, worst_h, sorted(set(int(i) for i in iters[name]))))
+        assert worst_o <= 1e-2 and worst_h <= 3e-2
+    assert np.all(iters["host polling"] == iters["enqueue-ahead"])
 
 
 def test_mp_square(env):
