@@ -313,6 +313,39 @@ def test_power_scale(env):
                            opts=pmx.default_opts(scale_mode=P))
 
 
+def _spd_from(lam, seed):
+    n = lam.size
+    Q = W.random_orthogonal(np.random.default_rng(seed), n)
+    return ((Q * lam) @ Q.T).astype(np.float32)
+
+
+def test_power_scale_spectra(env):
+    # spectra that stress the estimate: an isolated top eigenvalue over a bulk
+    # just below half of it (the estimate's worst case), two clusters, a
+    # single large eigenvalue, geometric decay; every one converges to the
+    # eigendecomposition result with the estimated scale, in both iterations
+    torch, pmx, dev = env
+    P = pmx.SCALE_POWER
+    for n in (512, 1000):
+        cases = {
+            "isolated top": np.concatenate([[1.0], np.full(n - 1, 0.45)]),
+            "two clusters": np.concatenate([np.full(n // 2, 1.0), np.full(n - n // 2, 0.05)]),
+            "one large": np.concatenate([[50.0], np.linspace(0.5, 1.0, n - 1)]),
+            "geometric 1e-3": np.geomspace(1e-3, 1.0, n),
+            "flat": np.linspace(0.8, 1.0, n),
+        }
+        for k, (name, lam) in enumerate(cases.items()):
+            A = _spd_from(lam, 100 * n + k)
+            for method in (pmx.METHOD_NEWTON_SCHULZ, pmx.METHOD_INVERSE_NEWTON):
+                _say("power scale spectrum", n, name, method)
+                X, XA, info = _run_root(env, A, 4, scale_mode=P, method=method, max_iter=40)
+                ref, ref_aux = cf.inv_root(A, 4)
+                assert int(info[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), (n, name, method)
+                assert cf.rel_fro(X, ref) < 1e-4 and cf.rel_fro(XA, ref_aux) < 1e-4, (n, name, method)
+                # the scale covers the spectrum and never exceeds ||A||_F
+                assert float(lam.max()) <= float(info[0]["scale"]) <= float(np.linalg.norm(lam)) * 1.0001
+
+
 def _spread(m, n, seed, lo):
     # m x n with singular values geomspace(lo, 1) and random singular vectors
     rng = np.random.default_rng(seed)
