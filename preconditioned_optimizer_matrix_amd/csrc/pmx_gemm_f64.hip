@@ -223,7 +223,6 @@ __global__ __launch_bounds__(NT) void handover_f64_kernel(Handover64Params p) {
   }
 }
 
-static int rows_grid(int n, int cap) { return n < cap ? (n < 1 ? 1 : n) : cap; }
 
 }  // namespace
 
@@ -240,19 +239,19 @@ hipError_t launch_gemm_f64(const Gemm64Params& p, int role, hipStream_t s) {
 }
 
 hipError_t launch_stage_init_f64(const StageInit64Params& p, int batch, hipStream_t s) {
-  dim3 grid(rows_grid(p.n, kPartialsPerMatrix), batch);
+  dim3 grid(blocks_per_matrix(p.n, batch, 1024, kPartialsPerMatrix), batch);
   hipLaunchKernelGGL(stage_init_f64_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_form_g_f64(const FormG64Params& p, int batch, hipStream_t s) {
-  dim3 grid(rows_grid(p.n, 2048), batch);
+  dim3 grid(blocks_per_matrix(p.n, batch, 4096, 2048), batch);
   hipLaunchKernelGGL(form_g_f64_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_handover_f64(const Handover64Params& p, int batch, hipStream_t s) {
-  dim3 grid(rows_grid(p.n, 2048), batch);
+  dim3 grid(blocks_per_matrix(p.n, batch, 4096, 2048), batch);
   hipLaunchKernelGGL(handover_f64_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }

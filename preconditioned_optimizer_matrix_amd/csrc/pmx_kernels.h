@@ -8,6 +8,18 @@ namespace pmx {
 // Partial-sum slots reserved per matrix for the elementwise reductions and
 // for the residual GEMM (one slot per output tile).
 constexpr int kPartialsPerMatrix = 1024;
+
+// Blocks per matrix of a row-looping kernel over a batch: about `total`
+// blocks in all, at most `cap` and at most one per row.  Kernels that end in a
+// last-block reduction take total = 1024: every block pays a device-wide fence
+// before its arrival, so one block per row of a large batch (32768 blocks for
+// 64 matrices of order 512) spent over a millisecond in fences.
+inline int blocks_per_matrix(int rows, int batch, int total, int cap) {
+  int per = (total + batch - 1) / batch;
+  if (per > cap) per = cap;
+  if (per > rows) per = rows;
+  return per < 1 ? 1 : per;
+}
 // Gram share slots per skinny block (J (J + 1) / 2 <= 45 entries, J <= 9).
 constexpr int kGramShare = 48;
 

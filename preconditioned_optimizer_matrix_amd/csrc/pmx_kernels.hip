@@ -935,9 +935,7 @@ hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, int de
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,
                             int64_t pstride, pmx_matfn_info* info, hipStream_t s) {
-  // about 2048 blocks in all, at most one per row and kPartialsPerMatrix per matrix
-  const int per = (2048 + batch - 1) / batch;
-  dim3 grid(grid_rows(rows, per < kPartialsPerMatrix ? per : kPartialsPerMatrix), batch);
+  dim3 grid(blocks_per_matrix(rows, batch, 1024, kPartialsPerMatrix), batch);
   const int V = bf16 ? 8 : 4;
   const int vec = (cols % V == 0) && (ld % V == 0) && (batch == 1 || stride % V == 0) &&
                   ((uintptr_t)x % 16 == 0);
@@ -951,13 +949,13 @@ hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_
 }
 
 hipError_t launch_sqrt_stage_init(const StageInitParams& p, int batch, hipStream_t s) {
-  dim3 grid(grid_rows(p.n, kPartialsPerMatrix), batch);
+  dim3 grid(blocks_per_matrix(p.n, batch, 1024, kPartialsPerMatrix), batch);
   hipLaunchKernelGGL(sqrt_stage_init_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_polar_init(const PolarInitParams& p, bool bf16, int batch, hipStream_t s) {
-  dim3 grid(grid_rows(p.rows, 2048), batch);
+  dim3 grid(blocks_per_matrix(p.rows, batch, 4096, 2048), batch);
   if (bf16) hipLaunchKernelGGL(polar_init_kernel<bf16_t>, grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL(polar_init_kernel<float>, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
@@ -1145,7 +1143,7 @@ hipError_t launch_power_scale(Ctrl* ctrl, const float* kbuf, int64_t kld, int64_
 hipError_t launch_polar_rescale(Ctrl* ctrl, float* r, uint16_t* rh, int64_t stride, int n,
                                 double* partials, int64_t pstride, IterCfg cfg, int batch,
                                 hipStream_t s) {
-  dim3 grid(grid_rows(n, kPartialsPerMatrix), batch);
+  dim3 grid(blocks_per_matrix(n, batch, 1024, kPartialsPerMatrix), batch);
   hipLaunchKernelGGL(polar_rescale_kernel, grid, dim3(NT), 0, s, ctrl, r, rh, stride, n,
                      partials, pstride, cfg);
   return hipGetLastError();
@@ -1202,7 +1200,7 @@ hipError_t launch_xpose(const XposeParams& p, int batch, hipStream_t s) {
 }
 
 hipError_t launch_root_finish(const RootFinishParams& p, int batch, hipStream_t s) {
-  dim3 grid(grid_rows(p.n, 2048), batch);
+  dim3 grid(blocks_per_matrix(p.n, batch, 4096, 2048), batch);
   hipLaunchKernelGGL(root_finish_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
