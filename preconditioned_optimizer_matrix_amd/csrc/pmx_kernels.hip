@@ -263,13 +263,11 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
   }
 
   if constexpr (GJ != 0) {
-    // the block's share of the Gram entries (a, bb), a <= bb < J <= |GJ|, of
+    // the block's share of the Gram entries (a, bb), a <= bb < J <= GJ, of
     // K_1..K_J, J = 2 d + 1 for the matrix's current degree d (gram_j when
-    // set); this pass writes K_jo, the others are read back.  GJ < 0: the
-    // inverse Newton objective (a separate instantiation: its solver's
-    // registers would lower the occupancy of every Gram pass)
-    constexpr bool NEWTON = GJ < 0;
-    constexpr int GA = NEWTON ? -GJ : GJ;
+    // set: 9 for the inverse Newton objective with p = 4); this pass writes
+    // K_jo, the others are read back.  gram_alpha_kernel sums the shares.
+    constexpr int GA = GJ;
     const int deg = *(const volatile int32_t*)&cb->degree;
     constexpr int NE = GA * (GA + 1) / 2;
     const int J = p.gram_j ? p.gram_j : 2 * deg + 1;
@@ -314,7 +312,6 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     }
     const int ng = J * (J + 1) / 2;
     __syncthreads();
-    __shared__ int is_last;
     double* part = p.gram_partials + (int64_t)b * p.gram_stride;
     if (threadIdx.x < ng)
       part[(int64_t)blockIdx.x * kGramShare + threadIdx.x] =
@@ -323,53 +320,57 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
             for (int w = 1; w < NW; ++w) t += wsum[w][threadIdx.x];
             return t;
           }();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __threadfence();
-      const uint32_t prev = atomicAdd(&cb->counter, 1u);
-      is_last = (prev == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    // every entry summed over the blocks' shares by one wave each, with a
-    // fixed lane assignment and reduction tree (deterministic)
-    for (int e = wid; e < ng; e += NW) {
-      double sv = 0.0;
-      for (int i = lane; i < (int)gridDim.x; i += 64)
-        sv += __hip_atomic_load(&part[(int64_t)i * kGramShare + e], __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-      sv = wave_sum(sv);
-      if (lane == 0) gsum[e] = sv;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double phi = 0.0;
-      const bool up = deg > p.cfg.degree;
-      double alpha;
-      if constexpr (NEWTON) {
-        if (GA >= 9 && J == 9)
-          alpha = alpha_from_gram_newton<9, 5>(gsum, fro, p.coef_n, p.cfg.lo, p.cfg.hi, &phi);
-        else
-          alpha = alpha_from_gram_newton<5, 5>(gsum, fro, p.coef_n, p.cfg.lo, p.cfg.hi, &phi);
-      } else {
-        alpha = alpha_from_gram(gsum, J, fro, up ? p.coef_up : p.coef,
-                                up ? p.lo_up : p.cfg.lo, up ? p.hi_up : p.cfg.hi, &phi);
-      }
-      cb->alpha = alpha;
-      // adaptive degree: the sketch predicts ||R_{k+1} S|| / ||R_k S|| =
-      // sqrt(phi_S(alpha)) / ||R S|| (gsum[0] = ||K_1||^2 of the scaled K_1 = R S / s)
-      if (deg < p.cfg.degree_max) {
-        const double m11 = gsum[0] * fro * fro;
-        const double q = m11 > 0.0 ? sqrt(fmax(phi, 0.0) / m11) : 0.0;
-        if (q > (double)p.cfg.adapt_ratio) cb->degree_next = deg + 1;
-      }
-      cb->sketch_products += J;
-      const int k = cb->iter;
-      if (p.cfg.info && k < PMX_TRACE_LEN) p.cfg.info[b].alpha[cb->stage][k] = (float)alpha;
-      cb->counter = 0u;
-    }
   }
+}
+
+// After a Gram pass (the kernel boundary orders the shares before this): one
+// block per matrix sums the pass's `nblocks` shares of every Gram entry, one
+// wave per entry with a fixed lane assignment and reduction tree
+// (deterministic), and solves for alpha: the square-root / polar family's
+// quartic, or the inverse Newton objective (newton_p = 4).  Then the adaptive
+// degree's decision, the product count and the alpha trace.
+__global__ __launch_bounds__(NT) void gram_alpha_kernel(SkinnyParams p, int nblocks) {
+  const int b = blockIdx.x;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int deg = *(const volatile int32_t*)&cb->degree;
+  const int J = p.gram_j ? p.gram_j : 2 * deg + 1;
+  const int ng = J * (J + 1) / 2;
+  const double fro = cb->fro;
+  const double* part = p.gram_partials + (int64_t)b * p.gram_stride;
+  __shared__ double gsum[kGramShare];
+  for (int e = wid; e < ng; e += NT / 64) {
+    double sv = 0.0;
+    for (int i = lane; i < nblocks; i += 64) sv += part[(int64_t)i * kGramShare + e];
+    sv = wave_sum(sv);
+    if (lane == 0) gsum[e] = sv;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  double phi = 0.0;
+  const bool up = deg > p.cfg.degree;
+  double alpha;
+  if (p.newton_p == 4) {
+    if (J == 9)
+      alpha = alpha_from_gram_newton<9, 5>(gsum, fro, p.coef_n, p.cfg.lo, p.cfg.hi, &phi);
+    else
+      alpha = alpha_from_gram_newton<5, 5>(gsum, fro, p.coef_n, p.cfg.lo, p.cfg.hi, &phi);
+  } else {
+    alpha = alpha_from_gram(gsum, J, fro, up ? p.coef_up : p.coef, up ? p.lo_up : p.cfg.lo,
+                            up ? p.hi_up : p.cfg.hi, &phi);
+  }
+  cb->alpha = alpha;
+  // adaptive degree: the sketch predicts ||R_{k+1} S|| / ||R_k S|| =
+  // sqrt(phi_S(alpha)) / ||R S|| (gsum[0] = ||K_1||^2 of the scaled K_1 = R S / s)
+  if (deg < p.cfg.degree_max) {
+    const double m11 = gsum[0] * fro * fro;
+    const double q = m11 > 0.0 ? sqrt(fmax(phi, 0.0) / m11) : 0.0;
+    if (q > (double)p.cfg.adapt_ratio) cb->degree_next = deg + 1;
+  }
+  cb->sketch_products += J;
+  const int k = cb->iter;
+  if (p.cfg.info && k < PMX_TRACE_LEN) p.cfg.info[b].alpha[cb->stage][k] = (float)alpha;
 }
 
 // The same product on the matrix cores, for 16-byte-aligned Mat (n % 4 == 0):
@@ -967,24 +968,21 @@ int skinny_blocks(int n, int q) {
   return (n + 7) / 8;
 }
 
+// Launches one skinny pass; returns its blocks per matrix and job.
 template <int Q, int RW, int GJ>
-static void skinny_go_j(const SkinnyParams& p, int njobs, int batch, hipStream_t s) {
+static int skinny_go_j(const SkinnyParams& p, int njobs, int batch, hipStream_t s) {
   if constexpr (Q == 8 || Q == 16) {
     if (p.mfma) {
-      // 16 waves a block (8 for the 9-entry Newton objective, whose solver
-      // needs more than 128 registers a lane)
+      // 16 waves a block
       dim3 g((p.n + 15) / 16, njobs, batch);
-      if constexpr (GJ != -9)
-        hipLaunchKernelGGL((skinny_mfma_kernel<Q, 16, GJ>), g, dim3(1024), 0, s, p);
-      else
-        hipLaunchKernelGGL((skinny_mfma_kernel<Q, 8, GJ>), g, dim3(512), 0, s, p);
-      return;
+      hipLaunchKernelGGL((skinny_mfma_kernel<Q, 16, GJ>), g, dim3(1024), 0, s, p);
+      return (int)g.x;
     }
   }
   dim3 grid((p.n + 4 * RW - 1) / (4 * RW), njobs, batch);
-  if constexpr (GJ < 0) {
+  if constexpr (GJ == 9) {
     hipLaunchKernelGGL((skinny_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
-    return;
+    return (int)grid.x;
   }
   if (p.variant == 1) {
     hipLaunchKernelGGL((skinny_stream_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
@@ -994,23 +992,22 @@ static void skinny_go_j(const SkinnyParams& p, int njobs, int batch, hipStream_t
   } else {
     hipLaunchKernelGGL((skinny_kernel<Q, RW, GJ>), grid, dim3(NT), 0, s, p);
   }
+  return (int)grid.x;
 }
 
-// Gram variants: J = 2d + 1 Krylov blocks, at most 5 (d <= 2) or 7 (d = 3);
-// the inverse Newton objective for p = 4 (J = 5 or 9) has variants of its
-// own.  The Gram pass is a single q = p job (p <= PMX_MAX_SKETCH = 16).
+// Gram variants: J = 2d + 1 Krylov blocks, at most 5 (d <= 2) or 7 (d = 3),
+// or 9 (the inverse Newton objective for p = 4, d = 2).  The Gram pass is a
+// single q = p job (p <= PMX_MAX_SKETCH = 16), followed by gram_alpha_kernel.
 template <int Q, int RW>
 static void skinny_go(const SkinnyParams& p, int njobs, bool gram, int batch, hipStream_t s) {
-  if (!gram) skinny_go_j<Q, RW, 0>(p, njobs, batch, s);
-  else if constexpr (Q <= 16) {
-    if (p.newton_p == 4) {
-      if (p.gram_j > 5) skinny_go_j<Q, RW, -9>(p, njobs, batch, s);
-      else skinny_go_j<Q, RW, -5>(p, njobs, batch, s);
-    } else if (p.cfg.degree_max == 3 || p.gram_j > 5) {
-      skinny_go_j<Q, RW, 7>(p, njobs, batch, s);
-    } else {
-      skinny_go_j<Q, RW, 5>(p, njobs, batch, s);
-    }
+  if (!gram) {
+    skinny_go_j<Q, RW, 0>(p, njobs, batch, s);
+  } else if constexpr (Q <= 16) {
+    int blocks;
+    if (p.gram_j > 7) blocks = skinny_go_j<Q, RW, 9>(p, njobs, batch, s);
+    else if (p.cfg.degree_max == 3 || p.gram_j > 5) blocks = skinny_go_j<Q, RW, 7>(p, njobs, batch, s);
+    else blocks = skinny_go_j<Q, RW, 5>(p, njobs, batch, s);
+    hipLaunchKernelGGL(gram_alpha_kernel, dim3(batch), dim3(NT), 0, s, p, blocks);
   }
 }
 
