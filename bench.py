@@ -280,6 +280,22 @@ def other_workload(args):
                    value=round(ms, 3), unit="ms", dtype="bf16", config={"workload": wl},
                    iters=it, iters_taylor=tit, gemms_per_matrix=int(inf["gemms"][0]),
                    mfma_tflops=round(tf, 1), mfma_frac=round(tf / 2516.6, 4))
+        # each product on its own, from the traced call: algorithmic flops of
+        # the launches that ran (X g and R^2 once per update, I - X^T X once
+        # more) over the class's event-to-event time, which also holds the few
+        # early-exit launches after convergence
+        tr = out["kernel_trace_ms"]
+        if tr:
+            per = {"gemm_update": (it, 2.0 * 4096 * 1024 * 1024),
+                   "gemm_resid": (it + 1, 2.0 * 1024 * 1024 * 4096),
+                   "gemm_power": (it, 2.0 * 1024 ** 3)}
+            prod = {}
+            for k, (cnt, fl) in per.items():
+                t = tr.get(k, [0.0, 0])[0]
+                if t > 0:
+                    pf = 32 * fl * cnt / (t * 1e-3) / 1e15
+                    prod[k] = {"pflops": round(pf, 3), "frac": round(pf * 1e3 / 2516.6, 4)}
+            out["bf16_products"] = prod
     elif wl == "mp_10000":
         A = W.mp_square_device(device=dev)
         ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, 10000, 10000, 1, pmx.F32, opts), dev)
