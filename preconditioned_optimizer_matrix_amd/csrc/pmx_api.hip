@@ -150,6 +150,12 @@ struct Poller {
       if (hipStreamIsCapturing(q.s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
         chunk = 0;
     }
+    // a previous loop may have stopped with its newest publish kernel still
+    // queued (possibly on another stream): let it land before the flags are
+    // reused, so no stale value is read for this loop's points
+    if (chunk > 0)
+      for (hipEvent_t e : q.h->poll_ev)
+        if (hipEventSynchronize(e) != hipSuccess) chunk = 0;
   }
   hipError_t step(int i, bool* stop) {
     *stop = false;

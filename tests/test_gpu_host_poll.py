@@ -88,3 +88,29 @@ def test_host_poll_arguments(env):
     with pytest.raises(pmx.PmxError):
         pmx.set_host_poll(1001)
     pmx.set_host_poll(0)
+
+
+def test_host_poll_across_streams(env):
+    # consecutive polled calls on different streams, no synchronisation in
+    # between: each loop first lets the previous loop's last publish land, so
+    # no stale flag ends a loop early
+    torch, pmx, dev = env
+    As = [np.stack([W.spd_logu(256, 900 + 10 * i + b, 10.0 ** -(b + 1), 1.0)[0] for b in range(2)])
+          for i in range(3)]
+
+    def run(streams):
+        outs = []
+        for i, A in enumerate(As):
+            with torch.cuda.stream(streams[i % len(streams)]):
+                X, _, info = pmx.inv_root(torch.from_numpy(A).to(dev), 4, aux=False)
+            outs.append((X, info))
+        torch.cuda.synchronize()
+        return [(X.cpu().numpy().tobytes(), info.cpu().numpy().tobytes()) for X, info in outs]
+
+    base = run([torch.cuda.current_stream()])
+    pmx.set_host_poll(1)
+    try:
+        got = run([torch.cuda.Stream(), torch.cuda.Stream()])
+    finally:
+        pmx.set_host_poll(0)
+    assert got == base
