@@ -536,6 +536,24 @@ def test_status_codes(env):
     assert int(info[0]["status"]) == pmx.NONFINITE
     _, _, info = _run_root(env, np.zeros((5, 5), np.float32), 2)
     assert int(info[0]["status"]) == pmx.NONFINITE
+    # the same with the estimated scale (orders above the fused kernel's 64):
+    # the power passes skip a non-finite or zero input, and an indefinite
+    # input still diverges
+    P = pmx.SCALE_POWER
+    big = np.diag(np.concatenate([[1.0, 0.5, -0.3], np.full(97, 0.2)])).astype(np.float32)
+    X, _, info = _run_root(env, big, 2, scale_mode=P)
+    assert int(info[0]["status"]) == pmx.DIVERGED and np.all(np.isnan(X))
+    Anan = np.eye(100, dtype=np.float32)
+    Anan[3, 7] = np.nan
+    _, _, info = _run_root(env, Anan, 4, scale_mode=P)
+    assert int(info[0]["status"]) == pmx.NONFINITE
+    _, _, info = _run_root(env, np.zeros((100, 100), np.float32), 4, scale_mode=P)
+    assert int(info[0]["status"]) == pmx.NONFINITE
+    X, XA, info = _run_root(env, 3.0 * np.eye(100, dtype=np.float32), 4, scale_mode=P)
+    assert int(info[0]["status"]) == pmx.CONVERGED
+    assert np.allclose(X, 3.0 ** -0.25 * np.eye(100), atol=1e-6)
+    # the estimate of a I is c = 2 a (every column grows by exactly a / ||A||_F)
+    assert float(info[0]["scale"]) == pytest.approx(6.0, rel=1e-6)
     A64 = W.spd_64()["A"]
     _, _, info = _run_root(env, A64, 2, max_iter=1)
     assert int(info[0]["status"]) == pmx.MAXITER and int(info[0]["iters"][0]) == 1
