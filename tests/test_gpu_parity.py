@@ -271,7 +271,7 @@ def test_inverse_newton(env, p):
 
 
 def test_power_scale(env):
-    # scale_mode 1: c = ||A||_F min(1, 2 mu) from four power passes; the scale,
+    # scale_mode 1: c = ||A||_F min(1, 2 mu) from eight power passes; the scale,
     # the iteration counts and the roots against the oracle with the same
     # start block (the sketch of stage 2)
     torch, pmx, dev = env

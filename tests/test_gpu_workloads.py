@@ -141,6 +141,29 @@ def test_blocks_64x512(env):
         sorted(set(tuple(int(x) for x in i) for i in i64["iters"]))))
     assert max(e64) < 1e-4
     assert max(e32) < 5e-4
+    # the timed launch: estimated scale, fp64 leading updates, host polling
+    _say("blocks_64x512: estimated scale, host polling")
+    pmx.set_host_poll(2)
+    try:
+        Xp, _, infop = pmx.inv_root(A, 4, aux=False,
+                                    opts=pmx.default_opts(fp64_iters=4, scale_mode=pmx.SCALE_POWER))
+        torch.cuda.synchronize()
+    finally:
+        pmx.set_host_poll(0)
+    Xpn, ip = Xp.cpu().numpy(), pmx.parse_info(infop)
+    ep = []
+    for b in range(64):
+        ref, _ = cf.inv_root(c["A"][b], 4)
+        ep.append(cf.rel_fro(Xpn[b], ref))
+        assert int(ip[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+        if b % 16 == 0:
+            c_ref = prism.input_scale(c["A"][b].astype(np.float64), "power",
+                                      prism.make_sketch_fn(0, b))
+            assert float(ip[b]["scale"]) == pytest.approx(c_ref, rel=1e-4), b
+    _say("blocks_64x512 estimated scale: max rel err %.2e, updates %d (Frobenius %d)" % (
+        max(ep), int(ip["iters"].sum()), int(i64["iters"].sum())))
+    assert max(ep) < 1e-4
+    assert int(ip["iters"].sum()) <= int(i64["iters"].sum())
 
 
 def test_muon_32x4096x1024(env):
@@ -204,3 +227,23 @@ def test_mp_square(env):
          % (int(inf["iters"][0]), int(inf["gemms"]), sq, inv))
     assert int(inf["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
     assert sq < 1e-4 and inv < 1e-4
+    _say("mp_10000: estimated scale, host polling")
+    pmx.set_host_poll(2)
+    try:
+        Xp, XAp, infop = pmx.inv_root(A, 2, opts=pmx.default_opts(scale_mode=pmx.SCALE_POWER))
+        torch.cuda.synchronize()
+    finally:
+        pmx.set_host_poll(0)
+    ip = pmx.parse_info(infop)[0]
+    Xd, XAd = Xp.double(), XAp.double()
+    sq = float(torch.linalg.norm(XAd @ XAd - Ad) / torch.linalg.norm(Ad))
+    inv = float(torch.linalg.norm(XAd @ Xd - torch.eye(10000, device=dev, dtype=torch.float64)) / 100.0)
+    del Xd, XAd
+    c_ref = prism.input_scale(A.cpu().numpy().astype(np.float64), "power", prism.make_sketch_fn(0))
+    _say("mp_10000 estimated scale: iters %d (Frobenius %d), c %.6e (oracle %.6e), "
+         "||S^2 - A||/||A|| %.2e, ||S S^-1 - I||/sqrt(n) %.2e"
+         % (int(ip["iters"][0]), int(inf["iters"][0]), float(ip["scale"]), c_ref, sq, inv))
+    assert int(ip["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+    assert float(ip["scale"]) == pytest.approx(c_ref, rel=1e-4)
+    assert sq < 1e-4 and inv < 1e-4
+    assert int(ip["iters"][0]) <= int(inf["iters"][0])
