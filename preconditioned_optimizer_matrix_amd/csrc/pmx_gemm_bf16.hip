@@ -13,10 +13,10 @@
 //    k values 8 (l / 32) .. +7 of a 16-wide k step: one 16-byte LDS read per
 //    fragment.  LDS rows are padded to 72 bf16 (144 bytes) so the 16-byte
 //    reads of 8 consecutive rows hit distinct banks.
-//  * Block tile 256 x 256 x 64 with 4 waves of 128 x 128 (4 x 4 accumulators
-//    in AGPRs, one block per CU: 8 fragment reads per 16 MFMAs), or
-//    128 x 128 x 64 with waves of 64 x 64 when the problem has fewer large
-//    tiles than compute units.  16-byte global loads into 16-byte LDS stores,
+//  * Block tile 256 x 256 x 64 with 8 waves of 128 x 64 (4 x 2 accumulators,
+//    one block per CU: 6 fragment reads per 8 MFMAs), or 128 x 128 x 64 with
+//    4 waves of 64 x 64 when the problem has fewer large tiles than compute
+//    units.  16-byte global loads into 16-byte LDS stores,
 //    LDS double buffered with a register prefetch of the next k tile, the
 //    fragments of the next 16-wide k step read while the current one
 //    multiplies; persistent grid over (matrix, tile).
