@@ -437,6 +437,39 @@ def test_polar_varbatch(env):
     torch.cuda.synchronize()
 
 
+def test_rank_deficient_statistics(env):
+    # Shampoo's first step: one 48 x 80 gradient on eps I statistics leaves
+    # 32 eigenvalues of R at the damping (kappa = 2.3e4).  The pure fp32
+    # chain floors near 2e-4 on R^{-1/4} there (a float32 emulation of the
+    # same iteration lands at 2.1e-4); with the fp64 leading updates the
+    # root and the preconditioned step are within 1e-4.  Pure fp32 bounds:
+    # the measured floors with margin, so a loss of accuracy shows.
+    torch, pmx, dev = env
+    Gs = W.gaussian(48, 80, 7)
+    Lr, Rr = cf.stats_update(1e-3 * np.eye(48), 1e-3 * np.eye(80), Gs, 0.9, 1e-4)
+    lam = np.linalg.eigvalsh(Rr)
+    assert lam[31] < 1.1e-3 and lam[32] > 0.4  # the 32-fold eigenvalue at the damping
+    Lx, Rx = cf.inv_root(Lr, 4)[0], cf.inv_root(Rr, 4)[0]
+    Pr = cf.precond_apply(Lx, Gs, Rx)
+    G = torch.from_numpy(Gs).to(dev)
+    for kw, root_bound, apply_bound in (({}, 4e-4, 8e-4), ({"fp64_iters": 4}, 1e-4, 1e-4)):
+        _say("rank-deficient statistics", kw)
+        o = pmx.default_opts(**kw)
+        Li, _, il = pmx.inv_root(torch.from_numpy(Lr.astype(np.float32)).to(dev), 4, aux=False,
+                                 opts=o)
+        Ri, _, ir = pmx.inv_root(torch.from_numpy(Rr.astype(np.float32)).to(dev), 4, aux=False,
+                                 opts=o)
+        P = pmx.precond_apply(Li, G, Ri)
+        torch.cuda.synchronize()
+        eL = cf.rel_fro(Li.cpu().numpy(), Lx)
+        eR = cf.rel_fro(Ri.cpu().numpy(), Rx)
+        eP = cf.rel_fro(P.cpu().numpy(), Pr)
+        _say("  L^-1/4 %.2e, R^-1/4 %.2e, P %.2e" % (eL, eR, eP))
+        for info in (il, ir):
+            assert int(pmx.parse_info(info)[0]["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+        assert eL < 1e-4 and eR < root_bound and eP < apply_bound, kw
+
+
 def test_inv_root_batched(env):
     torch, pmx, dev = env
     _say("batched inv_root")
