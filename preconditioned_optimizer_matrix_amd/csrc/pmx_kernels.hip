@@ -62,27 +62,43 @@ __global__ __launch_bounds__(NT) void fro_scale_kernel(const T* __restrict__ X, 
   const int b = blockIdx.y;
   const T* x = X + (int64_t)b * stride;
   double acc = 0.0;
-  if (vec) {
+  // sum of squares of the 4 fp32 or 8 bf16 values of a 16-byte load
+  auto sumsq = [](const uint4 w) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    double a = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (sizeof(T) == 2) {
+        const double lo = (double)__uint_as_float(u[i] << 16);
+        const double hi = (double)__uint_as_float(u[i] & 0xFFFF0000u);
+        a += lo * lo + hi * hi;
+      } else {
+        const double v = (double)__uint_as_float(u[i]);
+        a += v * v;
+      }
+    }
+    return a;
+  };
+  constexpr int V = 16 / sizeof(T);
+  if (vec && ld == cols) {
+    // contiguous rows: one stream of 16-byte loads over the whole matrix,
+    // four in flight per thread (a row of 1024 bf16 is only 128 loads, so
+    // row-by-row left half of the block idle and one load in flight)
+    const uint4* v4 = reinterpret_cast<const uint4*>(x);
+    const int64_t nv = (int64_t)rows * cols / V;
+    const int64_t step = (int64_t)gridDim.x * NT;
+    int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+    for (; i + 3 * step < nv; i += 4 * step) {
+      const uint4 w0 = v4[i], w1 = v4[i + step], w2 = v4[i + 2 * step], w3 = v4[i + 3 * step];
+      acc += sumsq(w0) + sumsq(w1) + sumsq(w2) + sumsq(w3);
+    }
+    for (; i < nv; i += step) acc += sumsq(v4[i]);
+  } else if (vec) {
     // 16-byte loads: 8 bf16 or 4 fp32 per load (rows, ld and the base aligned)
-    constexpr int V = 16 / sizeof(T);
     const int cv = cols / V;
     for (int r = blockIdx.x; r < rows; r += gridDim.x) {
       const uint4* row = reinterpret_cast<const uint4*>(x + (int64_t)r * ld);
-      for (int c = threadIdx.x; c < cv; c += NT) {
-        const uint4 w = row[c];
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (sizeof(T) == 2) {
-            const double lo = (double)__uint_as_float(u[i] << 16);
-            const double hi = (double)__uint_as_float(u[i] & 0xFFFF0000u);
-            acc += lo * lo + hi * hi;
-          } else {
-            const double v = (double)__uint_as_float(u[i]);
-            acc += v * v;
-          }
-        }
-      }
+      for (int c = threadIdx.x; c < cv; c += NT) acc += sumsq(row[c]);
     }
   } else {
     for (int r = blockIdx.x; r < rows; r += gridDim.x)
@@ -878,7 +894,7 @@ __global__ __launch_bounds__(NT) void root_finish_kernel(RootFinishParams p) {
       ya = NAN;
     } else {
       zx = ((it == 0) ? (r == col ? 1.f : 0.f) : Z[e]) * sx;
-      ya = Y[e] * sa;
+      ya = XA ? Y[e] * sa : 0.f;  // Y is read only for the auxiliary output
     }
     X[(int64_t)r * p.ldx + col] = zx;
     if (XA) XA[(int64_t)r * p.ldaux + col] = ya;
@@ -936,7 +952,11 @@ hipError_t launch_ctrl_reset(Ctrl* ctrl, pmx_matfn_info* info, int batch, int de
 hipError_t launch_fro_scale(const void* x, bool bf16, int rows, int cols, int64_t ld,
                             int64_t stride, int batch, Ctrl* ctrl, double* partials,
                             int64_t pstride, pmx_matfn_info* info, hipStream_t s) {
-  dim3 grid(blocks_per_matrix(rows, batch, 1024, kPartialsPerMatrix), batch);
+  // about one block per CU over the whole batch: every block pays a fenced
+  // arrival in the last-block reduction, so 1024 blocks took 154 us for the
+  // 32 Muon matrices (268 MB) and 42 us for one fp32 4096^2 matrix, 256
+  // blocks 82 and 19 us, 64 blocks 208 and 29 us
+  dim3 grid(blocks_per_matrix(rows, batch, 256, kPartialsPerMatrix), batch);
   const int V = bf16 ? 8 : 4;
   const int vec = (cols % V == 0) && (ld % V == 0) && (batch == 1 || stride % V == 0) &&
                   ((uintptr_t)x % 16 == 0);
