@@ -149,6 +149,7 @@ struct XposeParams {
   float c0, c1;
   Ctrl* ctrl;  // null: unconditional; else skipped when the matrix is not running
   SketchJob sketch;  // a sketch generated on the side (needs ctrl)
+  int vec4;  // set by the launcher: bf16 input, no polynomial, 8-byte access in groups of 4
 };
 
 struct RootFinishParams {

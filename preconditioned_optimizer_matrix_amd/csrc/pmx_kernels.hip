@@ -860,6 +860,10 @@ __global__ __launch_bounds__(NT) void convert_kernel(const TI* __restrict__ src,
 
 // ---------------------------------------------------------------- tile transpose
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) { return from_f32<bf16_t>(x).bits; }
+// two values rounded to bf16, the first in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
+}
 
 __global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
   const int b = blockIdx.z;
@@ -872,6 +876,41 @@ __global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
   }
   __shared__ float tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (p.vec4) {
+    // bf16 input without a polynomial: each thread moves four consecutive
+    // bf16 (8 bytes) per access, both reading rows and writing the
+    // transposed rows (rows and cols multiples of 4)
+    const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.a) + (int64_t)b * p.sa;
+    const int q = threadIdx.x & 15, rr = threadIdx.x >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rr + 16 * i, gr = r0 + r, gc = c0 + 4 * q;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (gr < p.rows && gc < p.cols) {
+        const uint2 w = *reinterpret_cast<const uint2*>(ab + (int64_t)gr * p.lda + gc);
+        v[0] = __uint_as_float(w.x << 16) * scale;
+        v[1] = __uint_as_float(w.x & 0xFFFF0000u) * scale;
+        v[2] = __uint_as_float(w.y << 16) * scale;
+        v[3] = __uint_as_float(w.y & 0xFFFF0000u) * scale;
+        if (p.out_n)
+          *reinterpret_cast<uint2*>(p.out_n + (int64_t)b * p.sn + (int64_t)gr * p.ldn + gc) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tile[r][4 * q + j] = v[j];
+    }
+    __syncthreads();
+    if (!p.out_t) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = rr + 16 * i, gc = c0 + c, gr = r0 + 4 * q;
+      if (gc < p.cols && gr < p.rows)
+        *reinterpret_cast<uint2*>(p.out_t + (int64_t)b * p.st + (int64_t)gc * p.ldt + gr) =
+            make_uint2(pack_bf16x2(tile[4 * q][c], tile[4 * q + 1][c]),
+                       pack_bf16x2(tile[4 * q + 2][c], tile[4 * q + 3][c]));
+    }
+    return;
+  }
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const float* af = reinterpret_cast<const float*>(p.a) + (int64_t)b * p.sa;
   const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.a) + (int64_t)b * p.sa;
@@ -1246,7 +1285,13 @@ hipError_t launch_convert(const void* src, bool src_bf16, int64_t lds, int64_t s
   return hipGetLastError();
 }
 
-hipError_t launch_xpose(const XposeParams& p, int batch, hipStream_t s) {
+hipError_t launch_xpose(const XposeParams& pin, int batch, hipStream_t s) {
+  XposeParams p = pin;
+  auto al8 = [](const void* q) { return ((uintptr_t)q & 7u) == 0; };
+  p.vec4 = p.a_bf16 && !p.poly && p.rows % 4 == 0 && p.cols % 4 == 0 && p.lda % 4 == 0 &&
+           (batch == 1 || p.sa % 4 == 0) && al8(p.a) &&
+           (!p.out_n || (p.ldn % 4 == 0 && (batch == 1 || p.sn % 4 == 0) && al8(p.out_n))) &&
+           (!p.out_t || (p.ldt % 4 == 0 && (batch == 1 || p.st % 4 == 0) && al8(p.out_t)));
   dim3 grid((p.cols + 63) / 64, (p.rows + 63) / 64, batch);
   hipLaunchKernelGGL(xpose_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
