@@ -958,6 +958,33 @@ __global__ __launch_bounds__(NT) void root_finish_kernel(RootFinishParams p) {
   float* X = p.x + (int64_t)b * p.x_stride;
   float* XA = p.aux ? p.aux + (int64_t)b * p.aux_stride : nullptr;
   const int n = p.n;
+  const bool flat = !bad && it > 0 && p.ldx == n && (!XA || p.ldaux == n) && n % 4 == 0 &&
+                    ((uintptr_t)Z & 15) == 0 && ((uintptr_t)Y & 15) == 0 &&
+                    ((uintptr_t)X & 15) == 0 && ((uintptr_t)XA & 15) == 0;
+  if (flat) {
+    // contiguous outputs: one stream of 16-byte accesses, four loads in
+    // flight per thread
+    const float4* z4 = reinterpret_cast<const float4*>(Z);
+    const float4* y4 = reinterpret_cast<const float4*>(Y);
+    float4* x4 = reinterpret_cast<float4*>(X);
+    float4* a4 = reinterpret_cast<float4*>(XA);
+    const int64_t nv = (int64_t)n * n / 4;
+    const int64_t step = (int64_t)gridDim.x * NT;
+    auto sc = [](float4 v, float f) { return make_float4(v.x * f, v.y * f, v.z * f, v.w * f); };
+    int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+    for (; i + 3 * step < nv; i += 4 * step) {
+      const float4 z0 = z4[i], z1 = z4[i + step], z2 = z4[i + 2 * step], z3 = z4[i + 3 * step];
+      x4[i] = sc(z0, sx);
+      x4[i + step] = sc(z1, sx);
+      x4[i + 2 * step] = sc(z2, sx);
+      x4[i + 3 * step] = sc(z3, sx);
+    }
+    for (; i < nv; i += step) x4[i] = sc(z4[i], sx);
+    if (XA) {
+      for (i = (int64_t)blockIdx.x * NT + threadIdx.x; i < nv; i += step) a4[i] = sc(y4[i], sa);
+    }
+    return;
+  }
   for (int r = blockIdx.x; r < n; r += gridDim.x)
   for (int col = threadIdx.x; col < n; col += NT) {
     const int64_t e = (int64_t)r * n + col;
