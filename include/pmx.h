@@ -278,6 +278,9 @@ pmx_status pmx_matfn_polar_batched(pmx_handle handle, const void* G, pmx_dtype d
  *   opts: degree 1 or 2 (fixed), fp32 iterates; method and fp64_iters are
  *         ignored.  Workspace: pmx_workspace_size(PMX_OP_POLAR_VARBATCH, batch
  *         = count).  dtype applies to every block.
+ * Returns PMX_ERR_NOT_SUPPORTED, enqueuing nothing, while `stream` is being
+ * captured into a HIP graph: the descriptor copy reads host memory that a
+ * replay could not rely on.
  */
 #define PMX_VARBATCH_MAX_DIM 64
 typedef struct {
@@ -356,15 +359,42 @@ pmx_status pmx_shampoo_plan_destroy(pmx_shampoo_plan plan);
 pmx_status pmx_shampoo_plan_sizes(pmx_shampoo_plan plan, size_t* state_bytes,
                                   size_t* workspace_bytes);
 /* Enqueue the state's set-up on `stream`: L = R = eps I, M = 0, the running
- * norm 0, and the block tables. */
+ * norm 0, and the block tables.  Not capturable (PMX_ERR_NOT_SUPPORTED while
+ * `stream` is being captured into a HIP graph). */
 pmx_status pmx_shampoo_plan_init(pmx_shampoo_plan plan, void* state, size_t state_bytes,
                                  void* stream);
 /* One step: W[l] and G[l] are device pointers to layer l's weight and
  * gradient (fp32, the layer's natural layout); the HOST arrays W and G may be
- * reused once the call returns (they are copied into the workspace). */
+ * reused once the call returns (they are copied into the workspace).  Not
+ * capturable: PMX_ERR_NOT_SUPPORTED, enqueuing nothing, while `stream` is
+ * being captured into a HIP graph (a replay would copy from host memory that
+ * no longer holds the table). */
 pmx_status pmx_shampoo_plan_step(pmx_shampoo_plan plan, float* const* W, const float* const* G,
                                  int64_t step, void* state, size_t state_bytes, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * The Gaussian sketch S_k that the alpha fit of the iterations draws
+ * ([PRISM synthesis] Part II, "Randomized Sketching": a Gaussian oblivious
+ * subspace embedding, S with i.i.d. N(0, 1) entries, fresh per update).  The
+ * generator is Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key
+ * (seed mod 2^32, seed >> 32); the counter layout is this library's: element
+ * e = i p + j of S (n x p) for matrix `matrix` of a batch, stage `stage`
+ * (0 and 1: the two stages of the chained inverse 4th root, 0 for a square
+ * root or polar factor; 2: the start block of the estimated input scale) and
+ * update k is word e % 4 of the call with counter (e / 4, k, stage, matrix).
+ * Uniforms u = ((x >> 8) + 1/2) 2^-24; Box-Muller in fp64 on the word pairs
+ * (0, 1) and (2, 3): z0 = sqrt(-2 ln u0) cos(2 pi u1), z1 = ... sin(2 pi u1),
+ * likewise z2, z3 from (u2, u3); S[e] = z_{e % 4} rounded to fp32.
+ *   S:     device, n x p fp32, row stride lds >= p (written).
+ *   words: device, n x p uint32 (row stride p) receiving the raw Philox
+ *          words behind S, or NULL.  Must not overlap S (PMX_ERR_ALIAS).
+ * n in [1, 32768], p in [1, PMX_MAX_SKETCH], matrix, stage, k >= 0, else
+ * PMX_ERR_INVALID_VALUE with nothing enqueued.  The iterations generate
+ * their sketches with the same device code.
+ */
+pmx_status pmx_sketch_gaussian(pmx_handle handle, uint64_t seed, int matrix, int stage, int k,
+                               int n, int p, float* S, int lds, uint32_t* words, void* stream);
 
 /*
  * Launch trace for benchmarking.  While enabled, every kernel that a call on

@@ -1857,6 +1857,11 @@ pmx_status pmx_matfn_polar_varbatch(pmx_handle h, const pmx_polar_block* blocks,
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
   Enq q{h, (hipStream_t)stream};
+  // the descriptor copy below reads the caller's host array, which may be
+  // gone when a captured graph is replayed: refuse capture
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(q.s, &cs) != hipSuccess) return PMX_ERR_HIP;
+  if (cs != hipStreamCaptureStatusNone) return PMX_ERR_NOT_SUPPORTED;
   // descriptors to the device on the call's stream (staged from host memory
   // before the copy call returns)
   if (hipMemcpyAsync(ws, blocks, sizeof(pmx_polar_block) * (size_t)count, hipMemcpyHostToDevice,
@@ -1882,7 +1887,9 @@ pmx_status pmx_matfn_polar(pmx_handle h, const void* G, pmx_dtype dtype, int m, 
 }
 
 // ------------------------------------------------------------------ apply
-pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, int64_t sl,
+// The preconditioned step with the workspace `ws` (caller's, or the
+// library's scratch for the allocation-free entry point).
+static pmx_status precond_apply_impl(pmx_handle h, const float* Linv, int ldl, int64_t sl,
                                      const void* G, pmx_dtype dtype, int m, int n, int ldg,
                                      int64_t sg, const float* Rinv, int ldr, int64_t sr,
                                      void* P, int ldp, int64_t sp, int batch, void* ws,
@@ -1950,11 +1957,39 @@ pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, i
   return PMX_OK;
 }
 
+pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, int64_t sl,
+                                     const void* G, pmx_dtype dtype, int m, int n, int ldg,
+                                     int64_t sg, const float* Rinv, int ldr, int64_t sr,
+                                     void* P, int ldp, int64_t sp, int batch, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return precond_apply_impl(h, Linv, ldl, sl, G, dtype, m, n, ldg, sg, Rinv, ldr, sr, P, ldp, sp,
+                            batch, ws, ws_bytes, stream);
+}
+
 pmx_status pmx_precond_apply(pmx_handle h, const float* Linv, int ldl, const void* G,
                              pmx_dtype dtype, int m, int n, int ldg, const float* Rinv, int ldr,
                              void* P, int ldp, void* ws, size_t ws_bytes, void* stream) {
   return pmx_precond_apply_batched(h, Linv, ldl, 0, G, dtype, m, n, ldg, 0, Rinv, ldr, 0, P,
                                    ldp, 0, 1, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ sketch
+pmx_status pmx_sketch_gaussian(pmx_handle h, uint64_t seed, int matrix, int stage, int k, int n,
+                               int p, float* S, int lds, uint32_t* words, void* stream) {
+  if (!h || !S || n <= 0 || n > kMaxN || p < 1 || p > PMX_MAX_SKETCH || lds < p || matrix < 0 ||
+      stage < 0 || k < 0)
+    return PMX_ERR_INVALID_VALUE;
+  if (words) {
+    const Extent es = extent_of(S, n, p, lds, 0, 1, sizeof(float));
+    const Extent ew = extent_of(words, n, p, p, 0, 1, sizeof(uint32_t));
+    if (overlap(es, ew)) return PMX_ERR_ALIAS;
+  }
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return PMX_ERR_HIP;
+  Enq q{h, (hipStream_t)stream};
+  return from_hip(q.run(PMX_KC_OTHER, [&] {
+    return launch_sketch_export(seed, matrix, stage, k, n, p, S, lds, words, q.s);
+  }));
 }
 
 }  // extern "C"

@@ -178,24 +178,34 @@ struct SketchJob {
   int col;          // first column of the block written (0: the sketch S_k)
 };
 
+// The four standard normals of one Philox call's output words c[0..3]:
+// uniforms ((x >> 8) + 1/2) 2^-24, Box-Muller on the word pairs (0,1) and
+// (2,3), evaluated in fp64.
+__device__ __forceinline__ void philox_normals(const uint32_t (&c)[4], double (&z)[4]) {
+  double u[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) u[w] = ((double)(c[w] >> 8) + 0.5) * 0x1p-24;
+  const double r01 = sqrt(-2.0 * log(u[0])), r23 = sqrt(-2.0 * log(u[2]));
+  double s01, c01, s23, c23;
+  sincos(2.0 * M_PI * u[1], &s01, &c01);
+  sincos(2.0 * M_PI * u[3], &s23, &c23);
+  z[0] = r01 * c01;
+  z[1] = r01 * s01;
+  z[2] = r23 * c23;
+  z[3] = r23 * s23;
+}
+
 // Philox calls [q0, q1) of the sketch of matrix b: element e = i p + j takes
-// word e % 4 of the call with counter (e / 4, k, stage, b); uniforms
-// ((x >> 8) + 1/2) 2^-24, Box-Muller on the word pairs (0,1) and (2,3),
-// evaluated in fp64 and rounded to fp32.  One call per thread.
+// word e % 4 of the call with counter (e / 4, k, stage, b), key = seed; its
+// normal (philox_normals) is rounded to fp32.  One call per thread.
 __device__ __forceinline__ void sketch_calls(const SketchJob& sj, int b, int64_t q0, int64_t q1) {
   const int64_t total = (int64_t)sj.n * sj.p;
   float* kb = sj.kbuf + (int64_t)b * sj.kstride;
   for (int64_t q = q0 + threadIdx.x; q < q1; q += blockDim.x) {
     uint32_t c[4] = {(uint32_t)q, (uint32_t)sj.k, (uint32_t)sj.stage, (uint32_t)b};
     philox4x32_10(c, sj.seed_lo, sj.seed_hi);
-    double u[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) u[w] = ((double)(c[w] >> 8) + 0.5) * 0x1p-24;
-    const double r01 = sqrt(-2.0 * log(u[0])), r23 = sqrt(-2.0 * log(u[2]));
-    double s01, c01, s23, c23;
-    sincos(2.0 * M_PI * u[1], &s01, &c01);
-    sincos(2.0 * M_PI * u[3], &s23, &c23);
-    const double z[4] = {r01 * c01, r01 * s01, r23 * c23, r23 * s23};
+    double z[4];
+    philox_normals(c, z);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int64_t e = q * 4 + w;

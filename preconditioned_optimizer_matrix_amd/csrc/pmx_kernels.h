@@ -307,6 +307,10 @@ constexpr int kPowerStage = 2;   // sketch stream of V_0 (stages 0, 1 are the it
 constexpr int kPowerPasses = 8;
 constexpr double kPowerFactor = 2.0;
 hipError_t launch_sketch(const SketchJob& sj, const Ctrl* ctrl, int batch, hipStream_t s);
+// pmx_sketch_gaussian: the sketch of (matrix b, stage, iteration k) into S
+// (n x p, row stride lds) and optionally its raw Philox words (n x p, dense).
+hipError_t launch_sketch_export(uint64_t seed, int b, int stage, int k, int n, int p, float* S,
+                                int64_t lds, uint32_t* words, hipStream_t s);
 // polar = 0: c <- c min(1, factor mu); polar = 1 (mu estimates the top
 // eigenvalue of X_0^T X_0): s = sqrt(min(1, factor mu)), inv_s = 1 / s and
 // c <- c s.

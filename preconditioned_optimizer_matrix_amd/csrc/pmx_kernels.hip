@@ -1243,6 +1243,43 @@ __global__ __launch_bounds__(NT) void polar_rescale_kernel(Ctrl* ctrl, float* r,
   }
 }
 
+// The sketch of one (matrix, stage, iteration) as the iterations draw it,
+// written to a caller's n x p matrix (row stride lds) and, when `words` is
+// set, the Philox output word behind every element (n x p, row stride p).
+__global__ __launch_bounds__(NT) void sketch_export_kernel(uint32_t seed_lo, uint32_t seed_hi,
+                                                           int b, int stage, int k, int n, int p,
+                                                           float* S, int64_t lds,
+                                                           uint32_t* words) {
+  const int64_t total = (int64_t)n * p, calls = (total + 3) / 4;
+  for (int64_t q = (int64_t)blockIdx.x * NT + threadIdx.x; q < calls;
+       q += (int64_t)gridDim.x * NT) {
+    uint32_t c[4] = {(uint32_t)q, (uint32_t)k, (uint32_t)stage, (uint32_t)b};
+    philox4x32_10(c, seed_lo, seed_hi);
+    double z[4];
+    philox_normals(c, z);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int64_t e = q * 4 + w;
+      if (e < total) {
+        const int64_t i = e / p, j = e - i * p;
+        S[i * lds + j] = (float)z[w];
+        if (words) words[e] = c[w];
+      }
+    }
+  }
+}
+
+hipError_t launch_sketch_export(uint64_t seed, int b, int stage, int k, int n, int p, float* S,
+                                int64_t lds, uint32_t* words, hipStream_t s) {
+  const int64_t calls = ((int64_t)n * p + 3) / 4;
+  int64_t blocks = (calls + NT - 1) / NT;
+  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+  hipLaunchKernelGGL(sketch_export_kernel, dim3((unsigned)blocks), dim3(NT), 0, s,
+                     (uint32_t)(seed & 0xFFFFFFFFull), (uint32_t)(seed >> 32), b, stage, k, n, p,
+                     S, lds, words);
+  return hipGetLastError();
+}
+
 hipError_t launch_sketch(const SketchJob& sj, const Ctrl* ctrl, int batch, hipStream_t s) {
   const int64_t calls = ((int64_t)sj.n * sj.p + 3) / 4;
   int blocks = (int)((calls + NT - 1) / NT);

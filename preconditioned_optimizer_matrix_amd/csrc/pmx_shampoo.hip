@@ -180,6 +180,13 @@ struct Guard {
   }
 };
 
+// True while `s` is being captured into a graph (or its status is unknown).
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+}
+
+
 template <typename T>
 T* at_(void* base, size_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
@@ -378,6 +385,8 @@ pmx_status pmx_shampoo_plan_init(pmx_shampoo_plan P, void* state, size_t state_b
   Guard dg(P->device);
   if (!dg.ok) return PMX_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
+  // the block tables are copied from the plan's host memory: not captured
+  if (capturing(s)) return PMX_ERR_NOT_SUPPORTED;
   auto fill = [&](size_t off, int64_t count, int64_t n, float v) {
     if (count == 0) return hipSuccess;
     const int64_t blocks = std::min<int64_t>((count + ST - 1) / ST, 65536);
@@ -416,6 +425,9 @@ pmx_status pmx_shampoo_plan_step(pmx_shampoo_plan P, float* const* W, const floa
   Guard dg(P->device);
   if (!dg.ok) return PMX_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
+  // the pointer table below is copied from host memory that is gone once the
+  // call returns, so a captured graph could not replay it: refuse capture
+  if (capturing(s)) return PMX_ERR_NOT_SUPPORTED;
   const pmx_shampoo_config& c = P->cfg;
   // the step's layer pointers (W then G)
   std::vector<const void*> ptrs(2 * (size_t)nl);

@@ -104,14 +104,8 @@ __device__ void small_sketch(SmallShared& sh, int n, int p, int k, int stage, in
   for (int q = threadIdx.x; q < calls; q += SNT) {
     uint32_t c[4] = {(uint32_t)q, (uint32_t)k, (uint32_t)stage, (uint32_t)b};
     philox4x32_10(c, seed_lo, seed_hi);
-    double u[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) u[w] = ((double)(c[w] >> 8) + 0.5) * 0x1p-24;
-    const double r01 = sqrt(-2.0 * log(u[0])), r23 = sqrt(-2.0 * log(u[2]));
-    double s01, c01, s23, c23;
-    sincos(2.0 * M_PI * u[1], &s01, &c01);
-    sincos(2.0 * M_PI * u[3], &s23, &c23);
-    const double z[4] = {r01 * c01, r01 * s01, r23 * c23, r23 * s23};
+    double z[4];
+    philox_normals(c, z);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int e = q * 4 + w;

@@ -37,6 +37,7 @@ EXPORTS = [
     "pmx_trace_enable", "pmx_trace_collect", "pmx_set_host_poll",
     "pmx_shampoo_config_default", "pmx_shampoo_plan_create", "pmx_shampoo_plan_destroy",
     "pmx_shampoo_plan_sizes", "pmx_shampoo_plan_init", "pmx_shampoo_plan_step",
+    "pmx_sketch_gaussian",
 ]
 
 # kernel classes of the launch trace (pmx_kernel_class)
@@ -136,6 +137,8 @@ def _load():
         "pmx_shampoo_plan_step": (_i32, [_vp, ctypes.POINTER(ctypes.c_void_p),
                                          ctypes.POINTER(ctypes.c_void_p), _i64, _vp, _sz, _vp,
                                          _sz, _vp]),
+        "pmx_sketch_gaussian": (_i32, [_vp, ctypes.c_uint64, _i32, _i32, _i32, _i32, _i32, _vp,
+                                       _i32, _vp, _vp]),
         "pmx_trace_collect": (_i32, [_vp, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]),
     }
@@ -441,6 +444,20 @@ def precond_apply(Linv, G, Rinv, out=None, ws=None):
         ldr, sr, _ptr(P), ldp, sp, batch, _ptr(ws), ws.numel(), _stream(G)),
         "precond_apply")
     return P
+
+
+def sketch_gaussian(seed, matrix, stage, k, n, p, device=None, words=True):
+    """The iterations' Gaussian sketch S_k (n x p fp32) of (matrix, stage, k)
+    and, if words, the raw Philox words behind it (n x p int32 tensor holding
+    the uint32 bits); returns (S, words or None)."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else int(device))
+    S = torch.empty((n, p), dtype=torch.float32, device=dev)
+    Wd = torch.empty((n, p), dtype=torch.int32, device=dev) if words else None
+    check(lib.pmx_sketch_gaussian(handle(dev.index), ctypes.c_uint64(int(seed)), int(matrix),
+                                  int(stage), int(k), int(n), int(p), _ptr(S), int(p), _ptr(Wd),
+                                  _stream_of(dev)), "sketch_gaussian")
+    return S, Wd
 
 
 def set_host_poll(chunk, device=None):
