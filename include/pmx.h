@@ -312,6 +312,29 @@ pmx_status pmx_precond_apply_batched(pmx_handle handle, const float* Linv, int l
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * pmx_precond_apply_batched without a workspace argument, for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.  It runs the same kernels
+ * and gives the same result; the intermediate L^{-1/4} G (and, for bf16, the
+ * widened G and the fp32 P) lives in a scratch array inside the library, one
+ * copy per device of PMX_NOALLOC_SCRATCH_BYTES, held until the process ends
+ * (its address is resolved by pmx_create).  The call itself allocates
+ * nothing.  Limit: pmx_workspace_size(PMX_OP_APPLY, m, n, batch, dtype)
+ * must not exceed PMX_NOALLOC_SCRATCH_BYTES (fp32: m n batch <= 8 Mi
+ * elements; bf16: <= 2.6 Mi), else PMX_ERR_WORKSPACE with nothing enqueued.
+ * Every call on a device shares that device's scratch: calls that may
+ * overlap in time on one device (different streams without ordering, or
+ * different threads) race and must be ordered by the caller.  Other
+ * arguments and errors as in pmx_precond_apply_batched.
+ */
+#define PMX_NOALLOC_SCRATCH_BYTES (32u << 20)
+pmx_status pmx_precond_apply_noalloc(pmx_handle handle, const float* Linv, int ldl,
+                                     int64_t stride_l, const void* G, pmx_dtype dtype, int m,
+                                     int n, int ldg, int64_t stride_g, const float* Rinv,
+                                     int ldr, int64_t stride_r, void* P, int ldp,
+                                     int64_t stride_p, int batch, void* stream);
+
+/*
  * A whole Shampoo optimizer step over the layers of a model ([Shampoo blog]
  * sections 2.3 and 6.3 for the step, 3.2 for the block-diagonal
  * approximation, 5.1 for the adaptive learning rate, 5.2 for momentum, 5.3

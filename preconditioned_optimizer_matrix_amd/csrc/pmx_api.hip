@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -60,6 +61,36 @@ constexpr int kMaxN = 32768;
 constexpr int kMaxIter = 1000;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Library-owned scratch of pmx_precond_apply_noalloc: one copy per device,
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a host-side stand-in): pmx_create resolves
+// the device address once per device with hipGetSymbolAddress, and the entry
+// point passes that address.
+constexpr size_t kScratchBytes = (size_t)PMX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (the caller made `device` current).
+hipError_t resolve_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr || ((uintptr_t)ptr % kAlign) != 0) return hipErrorInvalidSymbol;
+  g_scratch_ptr[device] = ptr;
+  return hipSuccess;
+}
+
+void* scratch_of(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 // Current-device guard: make the handle's device current for the call and
 // restore the caller's device afterwards.
@@ -974,6 +1005,14 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_BF16_SYM")) c->bf16_sym = atoi(e);
   c->bf16_sym_small = 0;
   if (const char* e = getenv("PMX_BF16_SYM_SMALL")) c->bf16_sym_small = atoi(e);
+  {
+    // the scratch of pmx_precond_apply_noalloc, resolved once per device
+    DeviceGuard dg(device);
+    if (!dg.ok || resolve_scratch(device) != hipSuccess) {
+      delete c;
+      return PMX_ERR_HIP;
+    }
+  }
   *handle = c;
   return PMX_OK;
 }
@@ -1964,6 +2003,20 @@ pmx_status pmx_precond_apply_batched(pmx_handle h, const float* Linv, int ldl, i
                                      size_t ws_bytes, void* stream) {
   return precond_apply_impl(h, Linv, ldl, sl, G, dtype, m, n, ldg, sg, Rinv, ldr, sr, P, ldp, sp,
                             batch, ws, ws_bytes, stream);
+}
+
+pmx_status pmx_precond_apply_noalloc(pmx_handle h, const float* Linv, int ldl, int64_t sl,
+                                     const void* G, pmx_dtype dtype, int m, int n, int ldg,
+                                     int64_t sg, const float* Rinv, int ldr, int64_t sr,
+                                     void* P, int ldp, int64_t sp, int batch, void* stream) {
+  if (!h || m < 1 || n < 1 || m > kMaxN || n > kMaxN || batch < 1) return PMX_ERR_INVALID_VALUE;
+  if (dtype != PMX_F32 && dtype != PMX_BF16) return PMX_ERR_INVALID_VALUE;
+  const size_t need = apply_ws(m, n, batch, dtype);
+  if (need > kScratchBytes) return PMX_ERR_WORKSPACE;
+  void* ws = scratch_of(h->device);
+  if (!ws) return PMX_ERR_HIP;
+  return precond_apply_impl(h, Linv, ldl, sl, G, dtype, m, n, ldg, sg, Rinv, ldr, sr, P, ldp, sp,
+                            batch, ws, kScratchBytes, stream);
 }
 
 pmx_status pmx_precond_apply(pmx_handle h, const float* Linv, int ldl, const void* G,

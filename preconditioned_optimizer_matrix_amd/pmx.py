@@ -37,7 +37,7 @@ EXPORTS = [
     "pmx_trace_enable", "pmx_trace_collect", "pmx_set_host_poll",
     "pmx_shampoo_config_default", "pmx_shampoo_plan_create", "pmx_shampoo_plan_destroy",
     "pmx_shampoo_plan_sizes", "pmx_shampoo_plan_init", "pmx_shampoo_plan_step",
-    "pmx_sketch_gaussian",
+    "pmx_sketch_gaussian", "pmx_precond_apply_noalloc",
 ]
 
 # kernel classes of the launch trace (pmx_kernel_class)
@@ -125,6 +125,9 @@ def _load():
         "pmx_precond_apply_batched": (_i32, [_vp, _vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32,
                                              _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32, _vp,
                                              _sz, _vp]),
+        "pmx_precond_apply_noalloc": (_i32, [_vp, _vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32,
+                                             _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32,
+                                             _vp]),
         "pmx_trace_enable": (_i32, [_vp, _i32]),
         "pmx_set_host_poll": (_i32, [_vp, _i32]),
         "pmx_shampoo_config_default": (_i32, [ctypes.POINTER(ShampooConfig)]),
@@ -458,6 +461,24 @@ def sketch_gaussian(seed, matrix, stage, k, n, p, device=None, words=True):
                                   int(stage), int(k), int(n), int(p), _ptr(S), int(p), _ptr(Wd),
                                   _stream_of(dev)), "sketch_gaussian")
     return S, Wd
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def precond_apply_noalloc(Linv, G, Rinv, out=None):
+    """P = Linv G Rinv through the allocation-free entry point (the library's
+    scratch holds the intermediate; no workspace)."""
+    torch = _torch()
+    m, n, ldg, sg, batch = _mat(G)
+    _, _, ldl, sl, _ = _mat(Linv)
+    _, _, ldr, sr, _ = _mat(Rinv)
+    P = out if out is not None else torch.empty_like(G, memory_format=torch.contiguous_format)
+    _, _, ldp, sp, _ = _mat(P)
+    check(lib.pmx_precond_apply_noalloc(
+        handle(G.device.index), _ptr(Linv), ldl, sl, _ptr(G), _dtype_code(G), m, n, ldg, sg,
+        _ptr(Rinv), ldr, sr, _ptr(P), ldp, sp, batch, _stream(G)), "precond_apply_noalloc")
+    return P
 
 
 def set_host_poll(chunk, device=None):
