@@ -48,6 +48,9 @@ def parse():
                     help="updates per host-polled convergence point (0: enqueue all "
                          "max_iter updates; the surplus ones exit on the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other workloads (n = 64 roots, 64 x 512 blocks, 10^4 "
+                         "square root, 32 Muon matrices) in the default run")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 256 MiB fp32 buffer 4 times (a plain copy kernel of "
@@ -59,6 +62,10 @@ def parse():
                          "'--steps 1 --warmup 0 --no-cpu-baseline --no-trace --host-poll 0', "
                          "then of --calibrate-copy) and the JSON line that profiled bench "
                          "run printed (for its R^-1/4 update counts)")
+    ap.add_argument("--sweep", choices=["sketch", "sigma"],
+                    help="only a measurement sweep: the sketch width p on three "
+                         "workloads, or sigma_min of the polar factor (PRISM against "
+                         "the Taylor coefficient)")
     ap.add_argument("--workload", default="shampoo_1024x4096",
                     choices=["shampoo_1024x4096", "spd_64", "blocks_64x512",
                              "muon_32x4096x1024", "mp_10000", "varblocks_4096",
@@ -134,13 +141,26 @@ def timed(torch, fn, steps, warmup):
 def other_workload(args):
     """Secondary workloads (one JSON line each; the headline is the Shampoo layer)."""
     import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out = measure(args.workload, args)
+    print(json.dumps(out), flush=True)
+
+
+def measure(wl, args, inputs=None):
+    """One secondary workload's measurement as a dict (the JSON line of
+    `--workload wl`).  `inputs` may hold the workload's host arrays, made
+    beforehand (the default run builds the Muon matrices on a host thread
+    while the GPU measures the others)."""
+    import copy
+
+    import torch
 
     import workloads as W
     from preconditioned_optimizer_matrix_amd import pmx
+    args = copy.copy(args)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     pmx.set_host_poll(args.host_poll)
-    wl = args.workload
     # the power scale applies to the fp32 calls above order 64 (order 64 runs
     # the fused single-launch kernel, which scales by ||A||_F; the bf16 polar
     # factor takes only the Frobenius scale)
@@ -175,9 +195,16 @@ def other_workload(args):
             ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
             info = pmx.parse_info(fn(opts)[-1])[0]
             tinfo = pmx.parse_info(fn(taylor)[-1])[0]
+            # one workgroup (one compute unit) runs each call: the matrix-core
+            # bound is that CU's share of the fp32 MFMA peak
+            fl = int(info["gemms"]) * 2.0 * 64 * (64 if name != "polar_64x32" else 32) ** 2
+            tf = fl / (ms * 1e-3) / 1e12
             res[name] = {"us": round(ms * 1e3, 1), "gemms": int(info["gemms"]),
                          "gemms_taylor": int(tinfo["gemms"]),
-                         "iters": [int(x) for x in info["iters"]]}
+                         "iters": [int(x) for x in info["iters"]],
+                         "roofline": {"bound": "latency (one CU)", "achieved": round(tf, 4),
+                                      "peak": round(PEAK_FP32_MFMA / 256, 4), "unit": "TFLOP/s",
+                                      "frac": round(tf / (PEAK_FP32_MFMA / 256), 4)}}
         out.update(metric="us per matrix function (n=64)", value=res["inv_root_p4"]["us"],
                    unit="us", dtype="f32", config={"workload": wl}, calls=res)
     elif wl == "model_step":
@@ -260,7 +287,7 @@ def other_workload(args):
                    gemms_taylor_total=tg, mfma_tflops_fp32_only=round(tf, 2),
                    mfma_frac_fp32_only=round(tf / PEAK_FP32_MFMA, 4))
     elif wl == "muon_32x4096x1024":
-        c = W.muon_32x4096x1024()
+        c = inputs if inputs is not None else W.muon_32x4096x1024()
         G = torch.from_numpy(c["G_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
         o = pmx.default_opts(max_iter=args.max_iter, tol=c["tol"], scale_mode=SCALE_MODES[scale])
         ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_POLAR, 4096, 1024, 32, pmx.BF16, o), dev)
@@ -316,7 +343,98 @@ def other_workload(args):
                    mfma_frac=round(tf / PEAK_FP32_MFMA, 4))
     out["config"]["host_poll"] = args.host_poll
     out["config"]["scale"] = args.scale
-    print(json.dumps(out), flush=True)
+    return out
+
+
+def sweep_sketch(args):
+    """Sketch width p in {2, 4, 8, 16} on the 4096 statistics root (R^-1/4 of
+    the Shampoo layer after ten updates), the 64 x 512 power-law blocks
+    (A^-1/4, fp32) and the 10^4 square root: updates, dense products, skinny
+    sketch products, ms and the first stage's alpha trace.  Library scale
+    (||A||_F), host polling at chunk 2 (same results as enqueue-ahead)."""
+    import torch
+
+    import workloads as W
+    from preconditioned_optimizer_matrix_amd import pmx
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pmx.set_host_poll(2)
+    cfg = W.shampoo_1024x4096()
+    R = torch.from_numpy(cfg["R0"]).to(dev)
+    L = torch.from_numpy(cfg["L0"]).to(dev)
+    for g in cfg["Gs"]:
+        pmx.shampoo_stats_update(torch.from_numpy(g).to(dev), L, R, cfg["beta"], cfg["eps"])
+    del L
+    blocks = torch.from_numpy(W.blocks_64x512()["A"]).to(dev)
+    mp = W.mp_square_device(device=dev)
+    cases = (("shampoo_R_4096", R, 4, 1), ("blocks_64x512", blocks, 4, 64),
+             ("mp_10000", mp, 2, 1))
+    rows = []
+    for name, A, root, batch in cases:
+        n = A.shape[-1]
+        for sp in (2, 4, 8, 16):
+            o = pmx.default_opts(sketch_p=sp, max_iter=args.max_iter)
+            ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_INV_ROOT, n, n, batch, pmx.F32, o), dev)
+            X = torch.empty_like(A)
+            info = pmx.new_info(batch, dev)
+            fn = lambda: pmx.inv_root(A, root, opts=o, aux=False, out=X, info=info, ws=ws)
+            steps = 3 if n >= 10000 else args.steps
+            ms = timed(torch, fn, steps, 1)
+            inf = pmx.parse_info(info)
+            it = inf["iters"]
+            row = dict(workload=name, p=sp, ms=round(ms, 3),
+                       iters=[int(x) for x in it.max(axis=0)],
+                       updates_total=int(it.sum()), gemms_total=int(inf["gemms"].sum()),
+                       sketch_products_total=int(inf["sketch_products"].sum()),
+                       status=sorted(set(pmx.STATUS_NAMES[int(x)] for x in inf["status"])),
+                       alpha_stage1=[round(float(a), 4) for a in inf["alpha"][0][0][:int(it[0][0])]])
+            log(json.dumps(row))
+            rows.append(row)
+            del ws
+            torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "sketch_p", "host_poll": 2, "scale": "frobenius", "rows": rows}),
+          flush=True)
+
+
+def sweep_sigma(args):
+    """Polar factors of 8 fp32 matrices 2048 x 512 with singular values in
+    [sigma_min, 1] for sigma_min = 1e-1 .. 1e-5, log-uniform ("geometric") or
+    the Marchenko-Pastur shape of a 2048 x 512 Gaussian's singular values
+    mapped onto the interval ("mp"): PRISM (fitted alpha) against the Taylor
+    coefficient (alpha = c_d), tol 1e-5 on ||I - X^T X||_F / sqrt(n)."""
+    import torch
+
+    import workloads as W
+    from preconditioned_optimizer_matrix_amd import pmx
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pmx.set_host_poll(2)
+    m, n, batch = 2048, 512, 8
+    shape = W.mp_shape(m, n, 811)
+    rows = []
+    for fam in ("geometric", "mp"):
+        for k, smin in enumerate((1e-1, 1e-2, 1e-3, 1e-4, 1e-5)):
+            sig = np.geomspace(smin, 1.0, n) if fam == "geometric" else smin + (1 - smin) * shape
+            G = torch.from_numpy(W.polar_spectrum_batch(batch, m, n, 820 + k, sig)).to(dev)
+            row = dict(spectrum=fam, sigma_min=smin)
+            for meth, acc in (("prism", 1), ("taylor", 0)):
+                o = pmx.default_opts(tol=1e-5, max_iter=100, accelerate=acc)
+                ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_POLAR, m, n, batch, pmx.F32, o), dev)
+                U = torch.empty_like(G)
+                info = pmx.new_info(batch, dev)
+                fn = lambda: pmx.polar(G, opts=o, out=U, info=info, ws=ws)
+                ms = timed(torch, fn, args.steps, 1)
+                inf = pmx.parse_info(info)
+                row[meth] = dict(ms=round(ms, 3), iters_max=int(inf["iters"][:, 0].max()),
+                                 gemms_per_matrix=int(inf["gemms"].max()),
+                                 status=sorted(set(pmx.STATUS_NAMES[int(x)]
+                                                   for x in inf["status"])))
+            row["gemm_ratio_taylor_over_prism"] = round(
+                row["taylor"]["gemms_per_matrix"] / max(row["prism"]["gemms_per_matrix"], 1), 3)
+            log(json.dumps(row))
+            rows.append(row)
+    print(json.dumps({"sweep": "sigma_min", "shape": [batch, m, n], "dtype": "f32",
+                      "tol": 1e-5, "rows": rows}), flush=True)
 
 
 UPDATE_KERNEL = ("gemm_f32_kernel<pmx::(anonymous namespace)::Cfg<128, 128, 16, 2, 2, 3, 2>, "
@@ -440,6 +558,10 @@ def main():
         return calibrate_copy()
     if args.traffic_from:
         return write_traffic(args.traffic_from)
+    if args.sweep == "sketch":
+        return sweep_sketch(args)
+    if args.sweep == "sigma":
+        return sweep_sigma(args)
     if args.workload != "shampoo_1024x4096":
         return other_workload(args)
     import torch
@@ -449,6 +571,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # the Muon workload's host arrays (QR of 64 Gaussians, ~20 s of LAPACK)
+    # are built on a host thread while the GPU measures the rest
+    muon = {}
+    th = None
+    if not args.no_secondary:
+        import threading
+        th = threading.Thread(target=lambda: muon.update(W.muon_32x4096x1024()), daemon=True)
+        th.start()
     pmx.set_host_poll(args.host_poll)
     cfg = W.shampoo_1024x4096()
     m, n = cfg["Gs"][0].shape
@@ -595,6 +725,63 @@ def main():
                         products=products, algorithmic_flops_per_launch=round(flops / launches, 1))
         log("trace:", {k: (round(v[0], 3), v[1]) for k, v in trace.items()})
 
+    # the library's defaults: Frobenius scale, every update enqueued up front
+    # (the surplus ones exit on the device), the host never waits
+    pmx.set_host_poll(0)
+    oD = pmx.default_opts()
+    infoD = pmx.new_info(1, dev)
+    XD = torch.empty_like(R)
+    fnD = lambda: pmx.inv_root(R, 4, opts=oD, aux=False, out=XD, info=infoD, ws=wsR)
+    msD = timed(torch, fnD, args.steps, args.warmup)
+    iD = pmx.parse_info(infoD)[0]
+    lib_default = dict(scale="frobenius", host_poll=0, ms=round(msD, 3), gemms=int(iD["gemms"]),
+                       iters=[int(x) for x in iD["iters"]],
+                       status=pmx.STATUS_NAMES[int(iD["status"])],
+                       mfma_tflops=round(root_exec_flops(n, 1, iD["iters"], iD["gemms"])
+                                         / (msD * 1e-3) / 1e12, 2),
+                       property_x4r_minus_i=prop_of(XD))
+    log("R^-1/4 with the library defaults:", lib_default)
+    pmx.set_host_poll(args.host_poll)
+
+    secondary = None
+    if not args.no_secondary:
+        secondary = {}
+        keep = {
+            "spd_64": lambda r: {"us": {k: v["us"] for k, v in r["calls"].items()},
+                                 "gemms": {k: v["gemms"] for k, v in r["calls"].items()},
+                                 "gemms_taylor": {k: v["gemms_taylor"] for k, v in r["calls"].items()},
+                                 "roofline": r["calls"]["inv_root_p4"]["roofline"]},
+            "blocks_64x512": lambda r: {
+                "ms_fp64_leading": r["value"], "ms_fp32_only": r["fp32_only_ms"],
+                "gemms_total": r["gemms_total"], "gemms_taylor_total": r["gemms_taylor_total"],
+                "roofline": {"bound": "mfma", "achieved": r["mfma_tflops_fp32_only"],
+                             "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
+                             "frac": r["mfma_frac_fp32_only"], "of": "fp32-only call"}},
+            "mp_10000": lambda r: {
+                "ms": r["value"], "gemms": r["gemms"], "gemms_taylor": r["gemms_taylor"],
+                "gemm_ratio_taylor_over_prism": r["gemm_ratio_taylor_over_prism"],
+                "iters": r["iters"],
+                "roofline": {"bound": "mfma", "achieved": r["mfma_tflops"],
+                             "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s", "frac": r["mfma_frac"]}},
+            "muon_32x4096x1024": lambda r: {
+                "ms": r["value"], "iters": r["iters"], "iters_taylor": r["iters_taylor"],
+                "gemms_per_matrix": r["gemms_per_matrix"],
+                "roofline": {"bound": "mfma", "achieved": r["mfma_tflops"], "peak": 2516.6,
+                             "unit": "TFLOP/s", "frac": r["mfma_frac"], "of": "whole call"},
+                "bf16_products": r.get("bf16_products")},
+        }
+        for wl in ("spd_64", "blocks_64x512", "mp_10000", "muon_32x4096x1024"):
+            t0 = time.perf_counter()
+            if wl == "muon_32x4096x1024":
+                th.join()
+            r = measure(wl, args, inputs=muon if wl == "muon_32x4096x1024" else None)
+            secondary[wl] = dict(keep[wl](r), metric=r["metric"], unit=r["unit"],
+                                 dtype=r["dtype"], host_poll=r["config"]["host_poll"],
+                                 scale=r["config"]["scale"])
+            log("%s (%.1f s): %s" % (wl, time.perf_counter() - t0, json.dumps(secondary[wl])))
+            torch.cuda.empty_cache()
+        muon.clear()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg["Gs"][-1], L9.cpu().numpy(), R9.cpu().numpy(), beta, eps)
@@ -620,8 +807,10 @@ def main():
         "mfma_frac_r_root": round(tflops_r / PEAK_FP32_MFMA, 4),
         "dense_equiv_tflops_r_root": round(dense_tflops_r, 2),
         "property_x4r_minus_i": prop,
+        "library_default_r_root": lib_default,
         "inverse_newton_r_root": newton,
         "r_root_other_scale": other_scale,
+        "secondary": secondary,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -204,9 +204,14 @@ pmx_status pmx_workspace_size(pmx_handle handle, pmx_op op, int m, int n, int ba
  * Shampoo statistics update ([Shampoo blog] sections 2.2 and 2.3, step 2):
  *   L <- beta L + (1 - beta) G G^T + eps I   (m x m)
  *   R <- beta R + (1 - beta) G^T G + eps I   (n x n)
- * in place on L and R (full symmetric storage, fp32).  G is m x n with
- * element type `dtype` (fp32 or bf16; products accumulate in fp32).
- * Either L or R may be NULL to skip that side.  Requires 0 <= beta <= 1.
+ * in place on L and R (full storage, fp32).  G is m x n with element type
+ * `dtype` (fp32 or bf16; products accumulate in fp32).  The Grams G G^T and
+ * G^T G are computed once per pair of symmetric positions (upper-triangle
+ * tiles, mirrored); each stored element takes the EMA of its own old value,
+ * so L and R need not be exactly symmetric on entry.  The workspace
+ * (pmx_workspace_size(PMX_OP_STATS, m, n, batch, dtype)) holds G^T in fp32
+ * (and G widened to fp32 for bf16), plus the split-k partial tiles.  Either
+ * L or R may be NULL to skip that side.  Requires 0 <= beta <= 1.
  */
 pmx_status pmx_shampoo_stats_update(pmx_handle handle, const void* G, pmx_dtype dtype,
                                     int m, int n, int ldg, float* L, int ldl, float* R,

@@ -28,6 +28,7 @@ struct pmx_context {
   int split_k;             // 1: split-k tail for the fp32 products of the iterations
   int bf16_sym;            // 1: bf16 X^T X and R^2 run upper-triangle tiles, mirrored
   int bf16_sym_small;      // 1: ... with 128 x 128 tiles
+  int f64_tile;            // fp64 GEMM block tile (0: by the launch's size, else 64 or 128)
   // host-polled convergence (pmx_set_host_poll): updates per published point,
   // two pinned host flags (device-mapped) and the events behind them
   int poll_chunk = 0;
@@ -1005,6 +1006,9 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_BF16_SYM")) c->bf16_sym = atoi(e);
   c->bf16_sym_small = 0;
   if (const char* e = getenv("PMX_BF16_SYM_SMALL")) c->bf16_sym_small = atoi(e);
+  c->f64_tile = 0;
+  if (const char* e = getenv("PMX_F64_TILE")) c->f64_tile = atoi(e);
+  if (c->f64_tile != 64 && c->f64_tile != 128) c->f64_tile = 0;
   {
     // the scratch of pmx_precond_apply_noalloc, resolved once per device
     DeviceGuard dg(device);
@@ -1114,9 +1118,30 @@ static size_t apply_ws(int m, int n, int batch, pmx_dtype dt) {
   const size_t one = align_up(sizeof(float) * (size_t)m * n * batch);
   return dt == PMX_BF16 ? 3 * one : one;
 }
+// Statistics: G^T in fp32 (and G widened to fp32 for bf16 gradients), then
+// the split-k counters and partial-tile slots of the two triangle products.
+struct StatsLayout {
+  size_t gt, gn, skc, skp, total;
+  int64_t skcap;
+};
+static StatsLayout stats_layout(int m, int n, int batch, pmx_dtype dt) {
+  StatsLayout L;
+  const size_t one = align_up(sizeof(float) * (size_t)m * n * batch);
+  size_t off = 0;
+  L.gt = off;
+  off += one;
+  L.gn = off;
+  if (dt == PMX_BF16) off += one;
+  L.skc = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)kSplitMaxWorkers);
+  L.skcap = (int64_t)2 * kSplitMaxWorkers * (std::max(m, n) >= 512 ? 128 * 128 : 64 * 64);
+  L.skp = off;
+  off = align_up(off + sizeof(float) * (size_t)L.skcap);
+  L.total = off;
+  return L;
+}
 static size_t stats_ws(int m, int n, int batch, pmx_dtype dt) {
-  // bf16 gradients are widened to fp32 once
-  return dt == PMX_BF16 ? align_up(sizeof(float) * (size_t)m * n * batch) : 0;
+  return stats_layout(m, n, batch, dt).total;
 }
 
 pmx_status pmx_workspace_size(pmx_handle h, pmx_op op, int m, int n, int batch,
@@ -1189,44 +1214,42 @@ pmx_status pmx_shampoo_stats_update_batched(pmx_handle h, const void* G, pmx_dty
   DeviceGuard dg(h->device);
   if (!dg.ok) return PMX_ERR_HIP;
   Enq q{h, (hipStream_t)stream};
-  const float* g = (const float*)G;
-  if (bf) {
-    // widen G to fp32 once (exact); products then run on the fp32 MFMA kernel
-    const int nb = sg == 0 ? 1 : batch;
-    PMX_TRY(q.run(PMX_KC_OTHER, [&] {
-      return launch_convert(G, true, ldg, sg, ws, false, n, (int64_t)m * n, m, n, nb, q.s);
-    }));
-    g = (const float*)ws;
-    ldg = n;
-    sg = sg == 0 ? 0 : (int64_t)m * n;
-  }
+  // G^T (and G in fp32 for bf16 gradients) once, so that both Grams are
+  // NN products; they run as upper-triangle tiles, mirrored (SYRK)
+  const int nb = sg == 0 ? 1 : batch;
+  const StatsLayout SL = stats_layout(m, n, nb, dtype);
+  const int64_t plane = (int64_t)m * n;
+  float* gt = at<float>(ws, SL.gt);
+  float* gn = bf ? at<float>(ws, SL.gn) : nullptr;
+  uint32_t* skc = at<uint32_t>(ws, SL.skc);
+  PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+    return launch_stats_operands(G, bf, ldg, sg, m, n, nb, gt, gn, skc, kSplitMaxWorkers, q.s);
+  }));
+  const float* g = bf ? gn : (const float*)G;
+  const int64_t ldgf = bf ? n : ldg;
+  const int64_t sgf = sg == 0 ? 0 : (bf ? plane : sg);
+  const int64_t sgt = sg == 0 ? 0 : plane;
   const float omb = 1.f - beta;
-  if (L) {
-    GemmParams p = gemm_base(q.h, m, m, n, batch);
-    p.prob[0].a = {g, ldg, sg, nullptr, 0};
-    p.prob[0].b = {g, ldg, sg, nullptr, 0};
-    p.prob[0].c = L;
-    p.prob[0].ldc = ldl;
-    p.prob[0].stride_c = sl;
+  auto stats = [&](int dim, int k, GemmOperand a, GemmOperand b, float* C, int ldc, int64_t sc) {
+    GemmParams p = gemm_base(q.h, dim, dim, k, batch);
+    p.prob[0].a = a;
+    p.prob[0].b = b;
+    p.prob[0].c = C;
+    p.prob[0].ldc = ldc;
+    p.prob[0].stride_c = sc;
     p.beta = beta;
     p.omb = omb;
     p.eps = eps;
+    p.sym = 1;
+    p.sk_part = at<float>(ws, SL.skp);
+    p.sk_cnt = skc;
+    p.sk_cap = SL.skcap;
     set_vec(p);
-    PMX_TRY(q.run(PMX_KC_GEMM_STATS, [&] { return launch_gemm_f32(p, false, true, ROLE_STATS, q.s); }));
-  }
-  if (R) {
-    GemmParams p = gemm_base(q.h, n, n, m, batch);
-    p.prob[0].a = {g, ldg, sg, nullptr, 0};
-    p.prob[0].b = {g, ldg, sg, nullptr, 0};
-    p.prob[0].c = R;
-    p.prob[0].ldc = ldr;
-    p.prob[0].stride_c = sr;
-    p.beta = beta;
-    p.omb = omb;
-    p.eps = eps;
-    set_vec(p);
-    PMX_TRY(q.run(PMX_KC_GEMM_STATS, [&] { return launch_gemm_f32(p, true, false, ROLE_STATS, q.s); }));
-  }
+    return q.run(PMX_KC_GEMM_STATS, [&] { return launch_gemm_f32(p, false, false, ROLE_STATS, q.s); });
+  };
+  // L = G G^T: A = G (m x n), B = G^T (n x m);  R = G^T G: A = G^T, B = G
+  if (L) PMX_TRY(stats(m, n, {g, ldgf, sgf, nullptr, 0}, {gt, m, sgt, nullptr, 0}, L, ldl, sl));
+  if (R) PMX_TRY(stats(n, m, {gt, m, sgt, nullptr, 0}, {g, ldgf, sgf, nullptr, 0}, R, ldr, sr));
   return PMX_OK;
 }
 
@@ -1341,9 +1364,11 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
     g.degree = d;
     g.c0 = taylor(0);
     g.c1 = taylor(1);
+    g.num_cu = q.h->num_cu;
+    g.tile = q.h->f64_tile;
     return g;
   };
-  auto plain64 = [](const double* m) { return Gemm64Operand{m, nullptr, 0}; };
+  auto plain64 = [](const double* m) { return Gemm64Operand{m}; };
   for (int stage = 0; stage < stages; ++stage) {
     if (k64 > 0) {
       // leading updates in fp64 (same sequence as the fp32 loop below)
@@ -1367,10 +1392,10 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
       ip.cfg = cfg;
       ip.sketch = make_sketch(Lw, ws, cfg, n, 0, stage, acc);
       PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_stage_init_f64(ip, batch, q.s); }));
-      const Gemm64Operand g64 = {R64, d == 2 ? R264 : nullptr, 1};
       for (int k = 0; k < k64; ++k) {
         if (d == 2) {
           Gemm64Params g = gemm64(1);
+          g.sym = 1;
           g.prob[0].a = plain64(R64);
           g.prob[0].b = plain64(R64);
           g.prob[0].c = R264;
@@ -1380,32 +1405,35 @@ pmx_status pmx_matfn_inv_root_batched(pmx_handle h, const float* A, int n, int l
         PMX_TRY(enqueue_power_and_alpha(q, ws, Lw, o, cfg, coef, n, batch, Rb, R2b, nullptr, false));
         const int cur = k & 1, nxt = cur ^ 1;
         Gemm64Params u = gemm64(k == 0 ? 1 : 2);
+        // g = f_{d-1}(R) + alpha R^d in fp64: into Z_1 at k = 0, else over
+        // R^2 (the Krylov passes have read its fp32 copy)
+        FormG64Params fp;
+        memset(&fp, 0, sizeof(fp));
+        fp.r = R64;
+        fp.r2 = (d == 2) ? R264 : nullptr;
+        fp.dst = k == 0 ? Z64[1] : R264;
+        fp.stride = Lw.buf_stride;
+        fp.n = n;
+        fp.degree = d;
+        fp.c0 = taylor(0);
+        fp.c1 = taylor(1);
+        fp.ctrl = ctrl;
+        PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g_f64(fp, batch, q.s); }));
         if (k == 0) {
-          FormG64Params fp;
-          memset(&fp, 0, sizeof(fp));
-          fp.r = R64;
-          fp.r2 = (d == 2) ? R264 : nullptr;
-          fp.dst = Z64[1];
-          fp.stride = Lw.buf_stride;
-          fp.n = n;
-          fp.degree = d;
-          fp.c0 = taylor(0);
-          fp.c1 = taylor(1);
-          fp.ctrl = ctrl;
-          PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_form_g_f64(fp, batch, q.s); }));
           u.prob[0].a = plain64(Y64[0]);
           u.prob[0].b = plain64(Z64[1]);
           u.prob[0].c = Y64[1];
         } else {
           u.prob[0].a = plain64(Y64[cur]);
-          u.prob[0].b = g64;
+          u.prob[0].b = plain64(R264);
           u.prob[0].c = Y64[nxt];
-          u.prob[1].a = g64;
+          u.prob[1].a = plain64(R264);
           u.prob[1].b = plain64(Z64[cur]);
           u.prob[1].c = Z64[nxt];
         }
         PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_f64(u, ROLE_UPDATE, q.s); }));
         Gemm64Params r = gemm64(1);
+        r.sym = 1;
         r.prob[0].a = plain64(Z64[nxt]);
         r.prob[0].b = plain64(Y64[nxt]);
         r.prob[0].c = R64;

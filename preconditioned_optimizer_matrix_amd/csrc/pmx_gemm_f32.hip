@@ -30,9 +30,11 @@
 //  * Epilogues by role: plain store; residual R = I - acc with a deterministic
 //    Frobenius reduction and the convergence decision (last tile per matrix);
 //    Shampoo EMA C = beta C + (1 - beta) acc + eps I in place.
-//  * Symmetric outputs (R^2, the residuals Z A Z^T and X^T X): with `sym` only
-//    the tiles on and above the diagonal are computed and each off-diagonal
-//    tile is also stored transposed, about half the products' work.
+//  * Symmetric products (R^2, the residuals Z A Z^T and X^T X, the statistics
+//    Grams G G^T and G^T G): with `sym` only the tiles on and above the
+//    diagonal are computed and each off-diagonal tile is also stored
+//    transposed, about half the products' work.  The statistics' EMA reads
+//    the mirrored elements' own old values, so L and R need not be symmetric.
 #include <algorithm>
 #include <type_traits>
 
@@ -579,6 +581,24 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
           if (mirror && col < p.N) {
             // C[col][row_base .. row_base + 3]: four consecutive elements
             float* dst = Cm + (int64_t)col * pr.ldc + row_base;
+            if (EPI == EPI_EMA) {
+              // the mirrored elements keep their own old values (the caller's
+              // statistics need not be symmetric); off the diagonal: no eps
+              float old[4] = {0.f, 0.f, 0.f, 0.f};
+              if (vec && row_base + 3 < p.M) {
+                const f32x4 o = *reinterpret_cast<const f32x4*>(dst);
+                old[0] = o[0];
+                old[1] = o[1];
+                old[2] = o[2];
+                old[3] = o[3];
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (row_base + r < p.M) old[r] = dst[r];
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) xs[r] = p.beta * old[r] + p.omb * acc[i][j][4 * g + r];
+            }
             if (vec && row_base + 3 < p.M) {
               *reinterpret_cast<f32x4*>(dst) = f32x4{xs[0], xs[1], xs[2], xs[3]};
             } else {
@@ -735,7 +755,8 @@ int tiles_of(int M, int N) {
 // configurations the automatic choice takes.
 template <class C, bool TA, bool TB, int ROLE>
 constexpr bool kSplitVariant =
-    !TA && !TB && (ROLE == ROLE_POWER || ROLE == ROLE_UPDATE || ROLE == ROLE_RESID) &&
+    !TA && !TB &&
+    (ROLE == ROLE_POWER || ROLE == ROLE_UPDATE || ROLE == ROLE_RESID || ROLE == ROLE_STATS) &&
     (std::is_same<C, C0>::value || std::is_same<C, C4>::value || std::is_same<C, C5>::value);
 
 template <class C, bool TA, bool TB, int ROLE>
@@ -761,11 +782,14 @@ hipError_t launch_role(GemmParams p, hipStream_t s) {
     // split variants run whole tiles of plain operands only
     bool whole = p.vec && p.M % C::BM == 0 && p.N % C::BN == 0 && p.K % C::BK == 0;
     for (int i = 0; i < p.nprob; ++i) whole = whole && !p.prob[i].a.poly && !p.prob[i].b.poly;
-    // only as the tail of at least one whole round: a launch with fewer items
-    // than CUs runs faster unsplit (measured on the 1024^2 triangles, 136
-    // tiles: 45 -> 21 us; every span pays the cross-XCD fences of the fix-up)
-    if (whole && skp && p.sk_cnt && rem > 0 && total >= cu && nk >= 4 && W >= rem &&
-        2 * W * C::BM * C::BN <= p.sk_cap) {
+    // only as the tail of at least one whole round, or over long k: a launch
+    // with fewer items than CUs runs faster unsplit when k is short (measured
+    // on the 1024^2 triangles with k = 1024, 136 tiles: 45 -> 21 us; every
+    // span pays the cross-XCD fences of the fix-up), while with k >= 2048
+    // (the statistics G G^T of a 1024 x 4096 gradient) the spans are long
+    // enough to pay for them
+    if (whole && skp && p.sk_cnt && rem > 0 && (total >= cu || nk >= 128) && nk >= 4 &&
+        W >= rem && 2 * W * C::BM * C::BN <= p.sk_cap) {
       p.sk_part = skp;
       p.sk_dp = (int)(total - rem);
       p.sk_rem = (int)rem;
@@ -786,8 +810,9 @@ hipError_t launch_role(GemmParams p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Roles instantiated per transpose combination: every NN role except the
-// statistics, G G^T (NT), G^T G and X^T X (TN).
+// Roles instantiated per transpose combination: every role in NN (the
+// statistics take G and a transposed copy of G, so G G^T and G^T G are NN
+// products too), and the residual I - X^T X of the fp32 polar factor in TN.
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s) {
   if (!ta && !tb) {
@@ -795,19 +820,12 @@ hipError_t launch_cfg(const GemmParams& p, bool ta, bool tb, int role, hipStream
       case ROLE_POWER: return launch_role<C, false, false, ROLE_POWER>(p, s);
       case ROLE_UPDATE: return launch_role<C, false, false, ROLE_UPDATE>(p, s);
       case ROLE_RESID: return launch_role<C, false, false, ROLE_RESID>(p, s);
+      case ROLE_STATS: return launch_role<C, false, false, ROLE_STATS>(p, s);
       case ROLE_APPLY: return launch_role<C, false, false, ROLE_APPLY>(p, s);
       default: return hipErrorInvalidValue;
     }
   }
-  if (!ta && tb) {
-    if (role != ROLE_STATS) return hipErrorInvalidValue;
-    return launch_role<C, false, true, ROLE_STATS>(p, s);
-  }
-  if (ta && !tb) {
-    if (role == ROLE_STATS) return launch_role<C, true, false, ROLE_STATS>(p, s);
-    if (role == ROLE_RESID) return launch_role<C, true, false, ROLE_RESID>(p, s);
-    return hipErrorInvalidValue;
-  }
+  if (ta && !tb && role == ROLE_RESID) return launch_role<C, true, false, ROLE_RESID>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -8,37 +8,53 @@
 // epilogue with the Frobenius reduction and the decision, fp32 copies of R
 // and R^2 for the Krylov kernels.
 //
-// GEMM: 64 x 64 tiles, 256 threads with 4 x 4 fp64 accumulators each, k tiles
-// of 16 staged through LDS (A transposed so both operands are read along
-// rows), fp64 FMA on the vector ALUs (the gfx950 fp64 vector and matrix rates
-// are equal).
+// GEMM on the fp64 matrix cores (v_mfma_f64_16x16x4_f64): block tiles of
+// BT x BT (64 by default, 128 on request), 256 threads in 2 x 2
+// waves of (BT/2)^2, each wave holding (BT/32)^2 16 x 16 accumulators; k
+// tiles of 16 staged through LDS with both operands stored k-major (A is
+// transposed on the LDS store), double buffered with a register prefetch of
+// the next k tile: one barrier per k tile.  The symmetric products (R^2 and
+// the residual I - Z Y, Z Y = Z A Z^T) run the upper-triangle tiles only and
+// store each off-diagonal tile twice.
 #include "pmx_kernels.h"
 
 namespace pmx {
 namespace {
 
-constexpr int TN = 64, TK = 16, NT = 256;
+constexpr int TK = 16, NT = 256;
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int32_t load_status(const Ctrl* c) {
   return *(const volatile int32_t*)&c->status;
 }
 
-// element (i, j) of a plain or polynomial operand
-__device__ __forceinline__ double operand(const Gemm64Operand& o, int64_t off, int i, int j,
-                                          double c0, double c1, double alpha, int degree) {
-  if (!o.poly) return o.p[off];
-  const double r = o.p[off];
-  double g = degree == 2 ? c1 * r + alpha * o.p2[off] : alpha * r;
-  if (i == j) g += c0;
-  return g;
+// (tile row, tile column) of tile t: full grids row-major, symmetric
+// launches the upper triangle row by row
+__device__ __forceinline__ void tile_of(int t, int T, bool sym, int& tm, int& tn) {
+  if (!sym) {
+    tm = t / T;
+    tn = t - tm * T;
+    return;
+  }
+  int r = 0;
+  while (t >= T - r) {
+    t -= T - r;
+    ++r;
+  }
+  tm = r;
+  tn = r + t;
 }
 
-template <int ROLE>
+template <int BT, int ROLE>
 __global__ __launch_bounds__(NT) void gemm_f64_kernel(Gemm64Params p) {
   constexpr bool RESID = ROLE == ROLE_RESID;
+  constexpr int WT = BT / 2, F = WT / 16, LDT = BT + 2;
+  constexpr int PER = BT * TK / NT;  // elements of each operand tile per thread
   const int n = p.n;
-  const int tiles_1d = (n + TN - 1) / TN;
-  const int tiles = tiles_1d * tiles_1d;
+  const int T = (n + BT - 1) / BT;
+  const bool sym = p.sym != 0;
+  const int tiles = sym ? T * (T + 1) / 2 : T * T;
   const int pi = blockIdx.y;  // problem
   const int b = blockIdx.z;
   const int tile = blockIdx.x;
@@ -47,70 +63,97 @@ __global__ __launch_bounds__(NT) void gemm_f64_kernel(Gemm64Params p) {
   const Gemm64Problem& pr = p.prob[pi];
   const int64_t base = (int64_t)b * p.stride;
   if (RESID) sketch_share(p.sketch, b, tile, tiles);
-  const double alpha = cb->alpha;
-  const int m0 = (tile / tiles_1d) * TN, n0 = (tile % tiles_1d) * TN;
-  __shared__ double As[TK][TN + 1];  // As[k][i] = A[m0 + i][k0 + k]
-  __shared__ double Bs[TK][TN + 1];  // Bs[k][j] = B[k0 + k][n0 + j]
+  int tm, tn;
+  tile_of(tile, T, sym, tm, tn);
+  const int m0 = tm * BT, n0 = tn * BT;
+  __shared__ double As[2][TK][LDT];  // As[k][i] = A[m0 + i][k0 + k]
+  __shared__ double Bs[2][TK][LDT];  // Bs[k][j] = B[k0 + k][n0 + j]
   __shared__ double red[NT / 64];
-  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  double acc[4][4];
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int wm = (wid >> 1) * WT, wn = (wid & 1) * WT;
+  const double* __restrict__ A = pr.a.p + base;
+  const double* __restrict__ B = pr.b.p + base;
+  f64x4 acc[F][F];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < F; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
-  for (int k0 = 0; k0 < n; k0 += TK) {
-    // A tile 64 x 16 and B tile 16 x 64: four elements of each per thread
+    for (int v = 0; v < F; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+  double ra[PER], rb[PER];
+  // A: element e = t + NT q -> row e / TK, k e % TK (16 lanes per 128-byte
+  // row); B: k e / BT, column e % BT
+  auto load = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = t + NT * q;
-      const int ai = idx >> 4, ak = idx & 15;  // A: row ai, k ak
-      const int gi = m0 + ai, gk = k0 + ak;
-      double av = 0.0;
-      if (gi < n && gk < n)
-        av = operand(pr.a, base + (int64_t)gi * n + gk, gi, gk, p.c0, p.c1, alpha, p.degree);
-      As[ak][ai] = av;
-      const int bk = idx >> 6, bj = idx & 63;  // B: k bk, column bj
-      const int hk = k0 + bk, hj = n0 + bj;
-      double bv = 0.0;
-      if (hk < n && hj < n)
-        bv = operand(pr.b, base + (int64_t)hk * n + hj, hk, hj, p.c0, p.c1, alpha, p.degree);
-      Bs[bk][bj] = bv;
+    for (int q = 0; q < PER; ++q) {
+      const int e = t + NT * q;
+      const int ai = e / TK, ak = e % TK, gi = m0 + ai, gk = k0 + ak;
+      ra[q] = (gi < n && gk < n) ? A[(int64_t)gi * n + gk] : 0.0;
+      const int bk = e / BT, bj = e % BT, hk = k0 + bk, hj = n0 + bj;
+      rb[q] = (hk < n && hj < n) ? B[(int64_t)hk * n + hj] : 0.0;
     }
-    __syncthreads();
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < TK; ++k) {
-      double a[4], bb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = As[k][ty * 4 + u];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) bb[v] = Bs[k][tx * 4 + v];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], bb[v], acc[u][v]);
+    for (int q = 0; q < PER; ++q) {
+      const int e = t + NT * q;
+      As[buf][e % TK][e / TK] = ra[q];
+      Bs[buf][e / BT][e % BT] = rb[q];
     }
+  };
+  const int nk = (n + TK - 1) / TK;
+  load(0);
+  store(0);
+  __syncthreads();
+  const int li = lane & 15, lk = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * TK);
+#pragma unroll
+    for (int ks = 0; ks < TK; ks += 4) {
+      double fa[F], fb[F];
+#pragma unroll
+      for (int u = 0; u < F; ++u) fa[u] = As[cur][ks + lk][wm + 16 * u + li];
+#pragma unroll
+      for (int v = 0; v < F; ++v) fb[v] = Bs[cur][ks + lk][wn + 16 * v + li];
+#pragma unroll
+      for (int u = 0; u < F; ++u)
+#pragma unroll
+        for (int v = 0; v < F; ++v)
+          acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[u], fb[v], acc[u][v], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(cur ^ 1);
     __syncthreads();
   }
+  // lane l of a 16 x 16 fp64 accumulator holds column l % 16 and rows
+  // l / 16 + 4 r, r = 0 .. 3 (checked on the device; the fp32 16 x 16 MFMA
+  // holds rows 4 (l / 16) + r instead)
+  const bool mirror = sym && tm != tn;
+  float* c32 = pr.c32 ? pr.c32 + (int64_t)b * p.stride32 : nullptr;
+  double* C = pr.c + base;
   double fro = 0.0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = m0 + ty * 4 + u;
+  for (int u = 0; u < F; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = n0 + tx * 4 + v;
-      if (i < n && j < n) {
-        double x = acc[u][v];
-        if (RESID) {
-          x = (i == j ? 1.0 : 0.0) - x;
-          fro += x * x;
+    for (int v = 0; v < F; ++v) {
+      const int j = n0 + wn + 16 * v + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = m0 + wm + 16 * u + lk + 4 * r;
+        double x = acc[u][v][r];
+        if (RESID) x = (i == j ? 1.0 : 0.0) - x;
+        if (i < n && j < n) {
+          if (RESID) fro += x * x;
+          C[(int64_t)i * n + j] = x;
+          if (c32) c32[(int64_t)i * n + j] = (float)x;
+          if (mirror) {
+            // the transposed tile: C[j][i]
+            C[(int64_t)j * n + i] = x;
+            if (c32) c32[(int64_t)j * n + i] = (float)x;
+          }
         }
-        const int64_t o = base + (int64_t)i * n + j;
-        pr.c[o] = x;
-        if (pr.c32) pr.c32[(int64_t)b * p.stride32 + (int64_t)i * n + j] = (float)x;
       }
     }
-  }
   if (RESID) {
+    if (mirror) fro *= 2.0;  // the tile stands for itself and its transpose
     const double bs = block_sum<NT / 64>(fro, red);
     double tot;
     if (last_block_sum<NT / 64>(bs, p.partials + (int64_t)b * p.partial_stride, &cb->counter,
@@ -226,16 +269,25 @@ __global__ __launch_bounds__(NT) void handover_f64_kernel(Handover64Params p) {
 
 }  // namespace
 
-hipError_t launch_gemm_f64(const Gemm64Params& p, int role, hipStream_t s) {
-  const int t1 = (p.n + TN - 1) / TN;
-  const dim3 grid(t1 * t1, p.nprob, p.batch);
+template <int BT>
+hipError_t launch_gemm_f64_bt(const Gemm64Params& p, int role, hipStream_t s) {
+  const int T = (p.n + BT - 1) / BT;
+  const dim3 grid(p.sym ? T * (T + 1) / 2 : T * T, p.nprob, p.batch);
   switch (role) {
-    case ROLE_POWER: hipLaunchKernelGGL(gemm_f64_kernel<ROLE_POWER>, grid, dim3(NT), 0, s, p); break;
-    case ROLE_UPDATE: hipLaunchKernelGGL(gemm_f64_kernel<ROLE_UPDATE>, grid, dim3(NT), 0, s, p); break;
-    case ROLE_RESID: hipLaunchKernelGGL(gemm_f64_kernel<ROLE_RESID>, grid, dim3(NT), 0, s, p); break;
+    case ROLE_POWER: hipLaunchKernelGGL((gemm_f64_kernel<BT, ROLE_POWER>), grid, dim3(NT), 0, s, p); break;
+    case ROLE_UPDATE: hipLaunchKernelGGL((gemm_f64_kernel<BT, ROLE_UPDATE>), grid, dim3(NT), 0, s, p); break;
+    case ROLE_RESID: hipLaunchKernelGGL((gemm_f64_kernel<BT, ROLE_RESID>), grid, dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_f64(const Gemm64Params& p, int role, hipStream_t s) {
+  // 64 x 64 tiles by default: four blocks per CU fit in registers (the
+  // 128 x 128 tile holds one), and on the 64 x 512^2 blocks the fp64 leading
+  // updates took 20.2 ms against 21.9 ms with 128 x 128 tiles
+  const int bt = p.tile > 0 ? p.tile : 64;
+  return bt == 128 ? launch_gemm_f64_bt<128>(p, role, s) : launch_gemm_f64_bt<64>(p, role, s);
 }
 
 hipError_t launch_stage_init_f64(const StageInit64Params& p, int batch, hipStream_t s) {

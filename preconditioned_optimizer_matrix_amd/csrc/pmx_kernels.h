@@ -216,8 +216,6 @@ hipError_t launch_small_polar(const SmallPolarParams& p, int batch, hipStream_t 
 // fp64 leading updates of an inverse root (square n x n buffers, ld n).
 struct Gemm64Operand {
   const double* p;
-  const double* p2;  // R^2 of a polynomial operand (d = 2)
-  int poly;          // 1: g = c0 I + c1 R + alpha R2 (d = 2) / c0 I + alpha R
 };
 
 struct Gemm64Problem {
@@ -229,6 +227,9 @@ struct Gemm64Problem {
 struct Gemm64Params {
   Gemm64Problem prob[2];
   int nprob, n, batch;
+  int sym;     // symmetric product (R^2, I - Z Y): upper-triangle tiles, mirrored
+  int tile;    // block tile 64 or 128 (0: by the launch's size)
+  int num_cu;
   int64_t stride;    // doubles between the matrices of a batch
   int64_t stride32;  // floats between the fp32 copies
   Ctrl* ctrl;
@@ -329,6 +330,11 @@ hipError_t launch_polar_rescale(Ctrl* ctrl, float* r, uint16_t* rh, int64_t stri
 hipError_t launch_publish_running(const Ctrl* ctrl, int batch, int32_t* dst, hipStream_t s);
 
 hipError_t launch_form_g(const FormGParams& p, int batch, hipStream_t s);
+// Statistics operands: G^T (cols x rows fp32, dense) and, when gn is set, G
+// widened to fp32 (rows x cols, dense), per batch matrix; zeroes zero[0, nzero).
+hipError_t launch_stats_operands(const void* g, bool bf16, int64_t ld, int64_t sg, int rows,
+                                 int cols, int batch, float* gt, float* gn, uint32_t* zero,
+                                 int nzero, hipStream_t s);
 // Elementwise copy between fp32 and bf16 matrices (rows x cols, strided batch);
 // bf16 -> fp32 is exact, fp32 -> bf16 rounds to nearest even.
 hipError_t launch_convert(const void* src, bool src_bf16, int64_t lds, int64_t ss, void* dst,

@@ -858,6 +858,57 @@ __global__ __launch_bounds__(NT) void convert_kernel(const TI* __restrict__ src,
   }
 }
 
+// ---------------------------------------------------------------- statistics operands
+// The operands of the statistics products in the layout of the scheduled
+// GEMM loop (A with k contiguous, B with n contiguous): G^T (cols x rows,
+// fp32, row stride rows) and, for bf16 gradients, G widened to fp32 (rows x
+// cols, row stride cols).  64 x 64 tiles through LDS; block (0, 0, 0) also
+// zeroes the split-k arrival counters of the products that follow.
+template <typename T>
+__global__ __launch_bounds__(NT) void stats_operands_kernel(const T* __restrict__ g, int64_t ld,
+                                                            int64_t sg, int rows, int cols,
+                                                            float* __restrict__ gt,
+                                                            float* __restrict__ gn,
+                                                            uint32_t* zero, int nzero) {
+  const int b = blockIdx.z;
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0 && b == 0)
+    for (int i = threadIdx.x; i < nzero; i += NT) zero[i] = 0u;
+  __shared__ float tile[64][65];
+  const T* x = g + (int64_t)b * sg;
+  const int64_t plane = (int64_t)rows * cols;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = ty + 4 * i, gr = r0 + r, gc = c0 + tx;
+    float v = 0.f;
+    if (gr < rows && gc < cols) {
+      v = to_f32(x[(int64_t)gr * ld + gc]);
+      if (gn) gn[(int64_t)b * plane + (int64_t)gr * cols + gc] = v;
+    }
+    tile[r][tx] = v;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int c = ty + 4 * i, gc = c0 + c, gr = r0 + tx;
+    if (gc < cols && gr < rows) gt[(int64_t)b * plane + (int64_t)gc * rows + gr] = tile[tx][c];
+  }
+}
+
+hipError_t launch_stats_operands(const void* g, bool bf16, int64_t ld, int64_t sg, int rows,
+                                 int cols, int batch, float* gt, float* gn, uint32_t* zero,
+                                 int nzero, hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
+  if (bf16)
+    hipLaunchKernelGGL(stats_operands_kernel<bf16_t>, grid, dim3(NT), 0, s, (const bf16_t*)g, ld,
+                       sg, rows, cols, gt, gn, zero, nzero);
+  else
+    hipLaunchKernelGGL(stats_operands_kernel<float>, grid, dim3(NT), 0, s, (const float*)g, ld,
+                       sg, rows, cols, gt, gn, zero, nzero);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- tile transpose
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) { return from_f32<bf16_t>(x).bits; }
 // two values rounded to bf16, the first in the low half

@@ -353,6 +353,8 @@ pmx_status pmx_shampoo_plan_create(pmx_handle h, const pmx_shampoo_config* cfg,
         (lib = std::max(lib, b), pmx_workspace_size(nullptr, PMX_OP_INV_ROOT, g.cols, g.cols,
                                                      g.count, PMX_F32, ro, &b)) != PMX_OK ||
         (lib = std::max(lib, b), pmx_workspace_size(nullptr, PMX_OP_APPLY, g.rows, g.cols,
+                                                     g.count, PMX_F32, nullptr, &b)) != PMX_OK ||
+        (lib = std::max(lib, b), pmx_workspace_size(nullptr, PMX_OP_STATS, g.rows, g.cols,
                                                      g.count, PMX_F32, nullptr, &b)) != PMX_OK) {
       delete P;
       return PMX_ERR_INVALID_VALUE;

@@ -69,7 +69,11 @@ def test_workspace_sizes_and_option_validation():
     assert 6 * 4 * n * n + sk <= b < 6 * 4 * n * n + sk + (1 << 20)
     bb = pmx.workspace_bytes(pmx.OP_INV_ROOT, 512, 512, 64, pmx.F32, o)
     assert bb >= 64 * 6 * 4 * 512 * 512
-    assert pmx.workspace_bytes(pmx.OP_STATS, 1024, 4096, 1, pmx.F32, None) == 0
+    # statistics: G^T in fp32 (bf16: and G widened), counters, split-k slots
+    st = pmx.workspace_bytes(pmx.OP_STATS, 1024, 4096, 1, pmx.F32, None)
+    assert 4 * 1024 * 4096 + sk <= st < 4 * 1024 * 4096 + sk + (1 << 20)
+    stb = pmx.workspace_bytes(pmx.OP_STATS, 1024, 4096, 1, pmx.BF16, None)
+    assert stb - st == 4 * 1024 * 4096
     # variable-size polar: the descriptors (32 bytes each), 256-byte aligned
     assert ctypes.sizeof(pmx.PolarBlock) == 32
     assert pmx.workspace_bytes(pmx.OP_POLAR_VARBATCH, 1, 1, 100, pmx.F32, None) == 3328

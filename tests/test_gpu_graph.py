@@ -88,3 +88,36 @@ def test_capture_inv_root_and_polar(env):
         pmx.set_host_poll(0)
     _say("graph: replays")
     _replays(torch, dev, g, [X, XA, info, U, pinfo], refs)
+
+
+def test_capture_refused_where_host_tables_are_copied(env):
+    """The variable-size polar call and the whole Shampoo step copy a host
+    table to the device on the call's stream; a replay could not rely on
+    that host memory, so both refuse capture (PMX_ERR_NOT_SUPPORTED) and
+    enqueue nothing."""
+    torch, pmx, dev = env
+    Gs = [torch.from_numpy(W.gaussian(12, 7, 5)).to(dev)]
+    plan = pmx.ShampooPlan([(48, 80)], dev, pmx.shampoo_config(block=64))
+    Wt = torch.zeros(48, 80, device=dev)
+    Gt = torch.from_numpy(W.gaussian(48, 80, 6)).to(dev)
+    torch.cuda.synchronize()
+    codes = []
+    g = torch.cuda.CUDAGraph()
+    x = torch.zeros(4, device=dev)
+    with torch.cuda.graph(g):
+        for fn in (lambda: pmx.polar_varbatch(Gs), lambda: plan.step([Wt], [Gt], 0)):
+            try:
+                fn()
+                codes.append(pmx.OK)
+            except pmx.PmxError as e:
+                codes.append(e.code)
+        x.add_(1.0)
+    _say("capture refused with codes", codes)
+    assert codes == [pmx.ERR_NOT_SUPPORTED, pmx.ERR_NOT_SUPPORTED]
+    g.replay()
+    torch.cuda.synchronize()
+    assert float(x.sum()) == 4.0
+    # outside capture both run
+    pmx.polar_varbatch(Gs)
+    plan.step([Wt], [Gt], 0)
+    torch.cuda.synchronize()

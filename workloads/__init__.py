@@ -115,6 +115,27 @@ def polar_batch(batch, m, n, seed, smin=1e-4, smax=1.0, bf16=True):
     return vals, bits, sigma
 
 
+def polar_spectrum_batch(batch, m, n, seed, sigma):
+    """Batch of m x n fp32 matrices U diag(sigma) V^T with U, V from the QR of
+    seeded Gaussians and the given singular values (length n)."""
+    sigma = np.asarray(sigma, np.float64)
+    vals = np.empty((batch, m, n), np.float32)
+    for b, rng in enumerate(rngs(seed, batch)):
+        U = random_orthogonal(rng, m, n)
+        V = random_orthogonal(rng, n)
+        vals[b] = ((U * sigma) @ V.T).astype(np.float32)
+    return vals
+
+
+def mp_shape(m, n, seed):
+    """The singular values of an m x n Gaussian (the square roots of a
+    Marchenko-Pastur spectrum of ratio n / m), ascending, mapped affinely onto
+    [0, 1]: the heavy-tailed shape of the spectrum sweeps."""
+    s = np.linalg.svd(np.random.default_rng(seed).standard_normal((m, n)), compute_uv=False)
+    s = np.sort(s)
+    return (s - s[0]) / (s[-1] - s[0])
+
+
 # ---------------------------------------------------------------- headline workloads
 
 def spd_64():
