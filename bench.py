@@ -623,7 +623,8 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-    r_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ev]))
+    r_steps = [a.elapsed_time(b) for a, b in r_ev]
+    r_ms = float(np.mean(r_steps))
     iL, iR = pmx.parse_info(infoL)[0], pmx.parse_info(infoR)[0]
     gemmsR, gemmsL = int(iR["gemms"]), int(iL["gemms"])
     tflops_r = root_exec_flops(n, 1, iR["iters"], iR["gemms"], args.method) / (r_ms * 1e-3) / 1e12
@@ -799,6 +800,7 @@ def main():
                    "max_iter": args.max_iter, "host_poll": args.host_poll,
                    "scale": args.scale,
                    "step": "restore L,R; stats update; L^-1/4; R^-1/4; apply"},
+        "r_ms_per_step": [round(x, 3) for x in r_steps],
         "gemms_to_converge": {"R": gemmsR, "L": gemmsL, "R_taylor": gemmsR_taylor},
         "iters": {"R": [int(x) for x in iR["iters"]], "L": [int(x) for x in iL["iters"]]},
         "status": {"R": pmx.STATUS_NAMES[int(iR["status"])],

@@ -71,16 +71,22 @@ typedef enum {
   PMX_DIVERGED = 4   /* r_k > 2: input not positive definite */
 } pmx_numeric;
 
-typedef enum { PMX_F32 = 0, PMX_BF16 = 1 } pmx_dtype;
+/* Element types.  The argument types pmx_dtype and pmx_op are plain 32-bit
+ * integers (not enum types), so that any value a caller passes is a valid
+ * value of the parameter and is rejected with PMX_ERR_INVALID_VALUE. */
+typedef int32_t pmx_dtype;
+enum { PMX_F32 = 0, PMX_BF16 = 1 };
 
 /* Operation codes for pmx_workspace_size. */
-typedef enum {
+typedef int32_t pmx_op;
+enum {
   PMX_OP_STATS = 0,
   PMX_OP_INV_ROOT = 1,
   PMX_OP_POLAR = 2,
   PMX_OP_APPLY = 3,
-  PMX_OP_POLAR_VARBATCH = 4  /* batch = number of blocks; m, n ignored */
-} pmx_op;
+  PMX_OP_POLAR_VARBATCH = 4  /* batch = number of blocks, all of sides <= PMX_VARBATCH_MAX_DIM;
+                                m, n ignored */
+};
 
 /*
  * Options of the iterative matrix functions ([PRISM synthesis] Part I and
@@ -268,26 +274,34 @@ pmx_status pmx_matfn_polar_batched(pmx_handle handle, const void* G, pmx_dtype d
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Polar factors of many small blocks of different shapes in one launch (the
+ * Polar factors of many blocks of different shapes in one call (the
  * per-block orthogonalisation of block-diagonal preconditioners; [PRISM
  * synthesis] Part I, sign/polar functions).  Each block is iterated as in
- * pmx_matfn_polar, fp32 arithmetic throughout (bf16 blocks are widened on
- * load and rounded to nearest even on store), one workgroup per block with
- * the whole iteration in LDS.
+ * pmx_matfn_polar with fp32 arithmetic throughout (bf16 blocks are widened
+ * on load and rounded to nearest even on store).  Blocks with both sides at
+ * most PMX_VARBATCH_MAX_DIM run one workgroup per block with the whole
+ * iteration in LDS, all in one launch; larger blocks (sides up to
+ * PMX_VARBATCH_MAX_SIDE) are grouped by shape, gathered into a packed fp32
+ * batch in the workspace, iterated by the batched fp32 polar factor and
+ * scattered back (a large block's sketch stream is that of its position in
+ * its shape group, stage 0).
  *   blocks: HOST array of `count` descriptors; every one is checked before
- *           anything is enqueued (1 <= m, n <= PMX_VARBATCH_MAX_DIM, ldg >= n,
+ *           anything is enqueued (1 <= m, n <= PMX_VARBATCH_MAX_SIDE, ldg >= n,
  *           ldu >= n, non-null pointers, output not overlapping its input),
  *           then copied into the workspace on `stream`; the array may be
  *           reused once the call returns.
  *   info_dev: `count` pmx_matfn_info (may be NULL), in block order.
- *   opts: degree 1 or 2 (fixed), fp32 iterates; method and fp64_iters are
- *         ignored.  Workspace: pmx_workspace_size(PMX_OP_POLAR_VARBATCH, batch
- *         = count).  dtype applies to every block.
+ *   opts: degree 1 or 2 (fixed), fp32 iterates, the Frobenius scale; method
+ *         and fp64_iters are ignored.  dtype applies to every block.
+ *   workspace: pmx_polar_varbatch_workspace_size(blocks, count, ...); when no
+ *         block exceeds PMX_VARBATCH_MAX_DIM this equals
+ *         pmx_workspace_size(PMX_OP_POLAR_VARBATCH, batch = count).
  * Returns PMX_ERR_NOT_SUPPORTED, enqueuing nothing, while `stream` is being
  * captured into a HIP graph: the descriptor copy reads host memory that a
  * replay could not rely on.
  */
 #define PMX_VARBATCH_MAX_DIM 64
+#define PMX_VARBATCH_MAX_SIDE 8192
 typedef struct {
   const void* g; /* device pointer: the m x n block, row-major, leading dimension ldg */
   void* u;       /* device pointer: its polar factor, m x n, leading dimension ldu */
@@ -299,6 +313,12 @@ pmx_status pmx_matfn_polar_varbatch(pmx_handle handle, const pmx_polar_block* bl
                                     pmx_dtype dtype, const pmx_matfn_opts* opts,
                                     pmx_matfn_info* info_dev, void* workspace,
                                     size_t workspace_bytes, void* stream);
+/* Workspace bytes of pmx_matfn_polar_varbatch for these blocks (host array;
+ * only the shapes are read).  PMX_ERR_INVALID_VALUE for a shape out of
+ * range, a NULL array or count < 1; opts may be NULL for the defaults. */
+pmx_status pmx_polar_varbatch_workspace_size(const pmx_polar_block* blocks, int count,
+                                             pmx_dtype dtype, const pmx_matfn_opts* opts,
+                                             size_t* bytes);
 
 /*
  * Preconditioned step ([Shampoo blog] sections 2.1 and 2.3, step 4):

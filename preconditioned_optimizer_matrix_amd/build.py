@@ -72,5 +72,58 @@ def build(verbose=True):
     return LIB
 
 
+# Host sanitizers for the C++ runtime: the translation units that carry the
+# host logic (argument checks, workspace carving, alias checks, descriptor
+# tables) are rebuilt with AddressSanitizer and UndefinedBehaviorSanitizer on
+# their host pass only (-Xarch_host before every -fsanitize=; the GPU code is
+# compiled as usual) and linked with the other objects into libpmx_san.so.
+# Load it with the clang ASan runtime preloaded (asan_runtime()).
+SAN_LIB = os.path.join(HERE, "libpmx_san.so")
+SAN_SOURCES = ("pmx_api.hip", "pmx_shampoo.hip")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime():
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang ASan runtime not found")
+    return hits[-1]
+
+
+def build_sanitized(verbose=True):
+    san = os.path.join(BUILD, "san")
+    os.makedirs(san, exist_ok=True)
+    objs = []
+    for src in sources():
+        base = os.path.basename(src)
+        if base in SAN_SOURCES:
+            obj = os.path.join(san, base + ".o")
+            cmd = [hipcc()] + COMMON + SAN_FLAGS + ["-c", src, "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
+        else:
+            obj = os.path.join(BUILD, base + ".o")
+            if not os.path.exists(obj):
+                obj, _ = _compile(src)
+        objs.append(obj)
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan",
+           "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "--sanitize":
+        build_sanitized()
+    else:
+        build()

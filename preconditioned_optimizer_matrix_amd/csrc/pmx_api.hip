@@ -1890,6 +1890,67 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
 }
 
 // ------------------------------------------------------------------ variable-size polar
+// The plan of a variable-size polar call: the descriptor table (every
+// block, in order; the fused kernel skips the large ones), then the indices
+// of the blocks above kSmallMaxN grouped by shape, then one scratch area
+// reused by every shape group in turn: the packed fp32 input and output, the
+// group's info records and the batched polar factor's workspace.
+struct VarGroup {
+  int m, n, first, count;  // shape; idx[first, first + count)
+};
+struct VarPlan {
+  std::vector<int32_t> idx;
+  std::vector<VarGroup> groups;
+  size_t table = 0, idx_off = 0, scratch = 0, total = 0;
+  bool small = false;  // any block for the fused kernel
+};
+
+static size_t var_group_bytes(const VarGroup& g, const pmx_matfn_opts& o) {
+  const size_t mat = align_up(sizeof(float) * (size_t)g.m * g.n * g.count);
+  return 2 * mat + align_up(sizeof(pmx_matfn_info) * (size_t)g.count) +
+         polar_ws(g.m, g.n, g.count, o, PMX_F32);
+}
+
+static bool var_plan(const pmx_polar_block* blocks, int count, const pmx_matfn_opts& o,
+                     VarPlan* P) {
+  std::vector<std::pair<std::pair<int, int>, int32_t>> big;
+  for (int i = 0; i < count; ++i) {
+    const pmx_polar_block& bl = blocks[i];
+    if (bl.m < 1 || bl.n < 1 || bl.m > PMX_VARBATCH_MAX_SIDE || bl.n > PMX_VARBATCH_MAX_SIDE)
+      return false;
+    if (bl.m > kSmallMaxN || bl.n > kSmallMaxN) big.push_back({{bl.m, bl.n}, (int32_t)i});
+    else P->small = true;
+  }
+  std::stable_sort(big.begin(), big.end(),
+                   [](const auto& x, const auto& y) { return x.first < y.first; });
+  for (size_t i = 0; i < big.size(); ++i) {
+    if (i == 0 || big[i].first != big[i - 1].first)
+      P->groups.push_back({big[i].first.first, big[i].first.second, (int)i, 0});
+    P->groups.back().count += 1;
+    P->idx.push_back(big[i].second);
+  }
+  P->table = align_up(sizeof(pmx_polar_block) * (size_t)count);
+  P->idx_off = P->table;
+  P->scratch = P->idx_off + (P->idx.empty() ? 0 : align_up(sizeof(int32_t) * P->idx.size()));
+  size_t g = 0;
+  for (const VarGroup& gr : P->groups) g = std::max(g, var_group_bytes(gr, o));
+  P->total = P->scratch + g;
+  return true;
+}
+
+pmx_status pmx_polar_varbatch_workspace_size(const pmx_polar_block* blocks, int count,
+                                             pmx_dtype dtype, const pmx_matfn_opts* opts,
+                                             size_t* bytes) {
+  if (!blocks || count < 1 || !bytes) return PMX_ERR_INVALID_VALUE;
+  if (dtype != PMX_F32 && dtype != PMX_BF16) return PMX_ERR_INVALID_VALUE;
+  pmx_matfn_opts o;
+  if (!resolve_opts(opts, &o)) return PMX_ERR_INVALID_VALUE;
+  VarPlan P;
+  if (!var_plan(blocks, count, o, &P)) return PMX_ERR_INVALID_VALUE;
+  *bytes = P.total;
+  return PMX_OK;
+}
+
 pmx_status pmx_matfn_polar_varbatch(pmx_handle h, const pmx_polar_block* blocks, int count,
                                     pmx_dtype dtype, const pmx_matfn_opts* opts,
                                     pmx_matfn_info* info, void* ws, size_t ws_bytes,
@@ -1901,7 +1962,9 @@ pmx_status pmx_matfn_polar_varbatch(pmx_handle h, const pmx_polar_block* blocks,
   if (std::max(o.degree, o.degree_max) > 2) return PMX_ERR_NOT_SUPPORTED;
   if (o.scale_mode != PMX_SCALE_FROBENIUS) return PMX_ERR_NOT_SUPPORTED;
   const int esz = dtype == PMX_BF16 ? 2 : 4;
-  const size_t need = align_up(sizeof(pmx_polar_block) * (size_t)count);
+  VarPlan P;
+  if (!var_plan(blocks, count, o, &P)) return PMX_ERR_INVALID_VALUE;
+  const size_t need = P.total;
   pmx_status st = check_ws(ws, ws_bytes, need);
   if (st != PMX_OK) return st;
   Extent ew;
@@ -1913,9 +1976,7 @@ pmx_status pmx_matfn_polar_varbatch(pmx_handle h, const pmx_polar_block* blocks,
   if (overlap(ei, ew)) return PMX_ERR_ALIAS;
   for (int i = 0; i < count; ++i) {
     const pmx_polar_block& bl = blocks[i];
-    if (!bl.g || !bl.u || bl.m < 1 || bl.n < 1 || bl.m > PMX_VARBATCH_MAX_DIM ||
-        bl.n > PMX_VARBATCH_MAX_DIM || bl.ldg < bl.n || bl.ldu < bl.n)
-      return PMX_ERR_INVALID_VALUE;
+    if (!bl.g || !bl.u || bl.ldg < bl.n || bl.ldu < bl.n) return PMX_ERR_INVALID_VALUE;
     const Extent eg = extent_of(bl.g, bl.m, bl.n, bl.ldg, 0, 1, esz);
     const Extent eu = extent_of(bl.u, bl.m, bl.n, bl.ldu, 0, 1, esz);
     if (overlap(eg, eu) || overlap(eu, ew) || overlap(eg, ew) || overlap(eu, ei))
@@ -1929,20 +1990,49 @@ pmx_status pmx_matfn_polar_varbatch(pmx_handle h, const pmx_polar_block* blocks,
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(q.s, &cs) != hipSuccess) return PMX_ERR_HIP;
   if (cs != hipStreamCaptureStatusNone) return PMX_ERR_NOT_SUPPORTED;
-  // descriptors to the device on the call's stream (staged from host memory
-  // before the copy call returns)
+  // descriptors and the grouped indices to the device on the call's stream,
+  // staged from host memory before the copy calls return
   if (hipMemcpyAsync(ws, blocks, sizeof(pmx_polar_block) * (size_t)count, hipMemcpyHostToDevice,
                      q.s) != hipSuccess)
     return PMX_ERR_HIP;
-  SmallPolarParams sp;
-  memset(&sp, 0, sizeof(sp));
-  sp.blocks = reinterpret_cast<const pmx_polar_block*>(ws);
-  sp.bf16 = dtype == PMX_BF16;
-  sp.c0 = (float)taylor(0);
-  sp.c1 = (float)taylor(1);
-  sp.cfg = make_cfg(o, PMX_VARBATCH_MAX_DIM, info);
-  sp.coef = make_coef(o.degree);
-  PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_small_polar(sp, count, q.s); }));
+  if (!P.idx.empty() && hipMemcpyAsync(at<void>(ws, P.idx_off), P.idx.data(),
+                                       sizeof(int32_t) * P.idx.size(), hipMemcpyHostToDevice,
+                                       q.s) != hipSuccess)
+    return PMX_ERR_HIP;
+  const pmx_polar_block* table = reinterpret_cast<const pmx_polar_block*>(ws);
+  if (P.small) {
+    SmallPolarParams sp;
+    memset(&sp, 0, sizeof(sp));
+    sp.blocks = table;
+    sp.bf16 = dtype == PMX_BF16;
+    sp.c0 = (float)taylor(0);
+    sp.c1 = (float)taylor(1);
+    sp.cfg = make_cfg(o, PMX_VARBATCH_MAX_DIM, info);
+    sp.coef = make_coef(o.degree);
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_small_polar(sp, count, q.s); }));
+  }
+  // the large blocks, one shape group at a time through the batched fp32 path
+  const int32_t* idx = at<int32_t>(ws, P.idx_off);
+  for (const VarGroup& g : P.groups) {
+    const size_t mat = align_up(sizeof(float) * (size_t)g.m * g.n * g.count);
+    float* in = at<float>(ws, P.scratch);
+    float* out = at<float>(ws, P.scratch + mat);
+    pmx_matfn_info* ginfo = at<pmx_matfn_info>(ws, P.scratch + 2 * mat);
+    const size_t woff = P.scratch + 2 * mat + align_up(sizeof(pmx_matfn_info) * (size_t)g.count);
+    const size_t wbytes = polar_ws(g.m, g.n, g.count, o, PMX_F32);
+    const int32_t* gi = idx + g.first;
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+      return launch_varbatch_gather(table, gi, dtype == PMX_BF16, in, g.m, g.n, g.count, q.s);
+    }));
+    const int64_t plane = (int64_t)g.m * g.n;
+    st = pmx_matfn_polar_batched(h, in, PMX_F32, g.m, g.n, g.n, plane, out, g.n, plane, g.count,
+                                 &o, info ? ginfo : nullptr, at<void>(ws, woff), wbytes, stream);
+    if (st != PMX_OK) return st;
+    PMX_TRY(q.run(PMX_KC_OTHER, [&] {
+      return launch_varbatch_scatter(table, gi, dtype == PMX_BF16, out, g.m, g.n, g.count,
+                                     info ? ginfo : nullptr, info, q.s);
+    }));
+  }
   return PMX_OK;
 }
 

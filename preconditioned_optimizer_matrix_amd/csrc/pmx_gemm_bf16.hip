@@ -342,23 +342,15 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
   }
   if (mirror) fro *= 2.f;  // the tile stands for itself and its transpose
   if (RESID) {
+    // the tile's Frobenius share; resid_decide_kernel sums them
     const double blocksum = block_sum<C::WAVES>((double)fro, red);
-    double tot;
-    if (last_block_sum<C::WAVES>(blocksum, p.partials + (int64_t)b * p.partial_stride,
-                                 &p.ctrl[b].counter, tiles, tile, red, &tot)) {
-      if (threadIdx.x == 0) {
-        Ctrl& c = p.ctrl[b];
-        if (p.count_update) c.iter += 1;
-        c.gemms += p.products;
-        decide(c, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
-      }
-    }
+    if (threadIdx.x == 0) p.partials[(int64_t)b * p.partial_stride + tile] = blocksum;
   }
 }
 
-// ROLE_RESID: C fp32 = I - acc with the Frobenius reduction and decision, and
-// a bf16 copy at prob[1].c when set; ROLE_POWER: C fp32 = acc; ROLE_UPDATE:
-// C bf16 = acc and its transpose at prob[1].c.
+// ROLE_RESID: C fp32 = I - acc with the Frobenius share for the decision,
+// and a bf16 copy at prob[1].c when set; ROLE_POWER: C fp32 = acc;
+// ROLE_UPDATE: C bf16 = acc and its transpose at prob[1].c.
 template <class C, int ROLE>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p) {
   constexpr int FM = C::FM, FN = C::FN;
@@ -598,6 +590,21 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_dma_kernel(GemmParams p) {
   }
 }
 
+// After a residual launch: the decision kernel over its `tiles` shares per matrix.
+hipError_t after_resid(const GemmParams& p, int role, int tiles, hipStream_t s) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || role != ROLE_RESID) return e;
+  ResidDecide d;
+  d.ctrl = p.ctrl;
+  d.partials = p.partials;
+  d.partial_stride = p.partial_stride;
+  d.tiles = tiles;
+  d.products = p.products;
+  d.count_update = p.count_update;
+  d.cfg = p.cfg;
+  return launch_resid_decide(d, p.batch, s);
+}
+
 hipError_t launch_dma(GemmParams p, int role, hipStream_t s) {
   p.tiles_m = p.M / 256;
   p.tiles_n = p.N / 256;
@@ -611,7 +618,7 @@ hipError_t launch_dma(GemmParams p, int role, hipStream_t s) {
     case ROLE_UPDATE: hipLaunchKernelGGL(gemm_bf16_dma_kernel<ROLE_UPDATE>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return after_resid(p, role, (int)(total / p.batch), s);
 }
 
 template <class C>
@@ -630,7 +637,7 @@ hipError_t launch_cfg(GemmParams p, int role, hipStream_t s) {
     case ROLE_UPDATE: hipLaunchKernelGGL((gemm_bf16_kernel<C, ROLE_UPDATE>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return after_resid(p, role, (int)(total / p.batch), s);
 }
 
 }  // namespace

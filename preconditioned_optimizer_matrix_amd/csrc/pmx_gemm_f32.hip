@@ -619,18 +619,9 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
     if (mirror) fro *= 2.f;  // the tile stands for itself and its transpose
 
     if (EPI == EPI_RESID) {
+      // the tile's Frobenius share; resid_decide_kernel sums them
       const double blocksum = block_sum<C::NW>((double)fro, red);
-      double tot;
-      if (last_block_sum<C::NW>(blocksum, p.partials + (int64_t)b * p.partial_stride,
-                                &p.ctrl[b].counter, tiles, tc.tile, red, &tot)) {
-        if (threadIdx.x == 0) {
-          Ctrl& c = p.ctrl[b];
-          if (p.count_update) c.iter += 1;
-          // p.products counts the powers of the configured degree
-          c.gemms += p.products + (c.degree - p.cfg.degree);
-          decide(c, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
-        }
-      }
+      if (threadIdx.x == 0) p.partials[(int64_t)b * p.partial_stride + tc.tile] = blocksum;
     }
   };
 
@@ -800,14 +791,25 @@ hipError_t launch_role(GemmParams p, hipStream_t s) {
   if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
   const dim3 grid((unsigned)(g + p.sk_workers)), block(C::NT);
   if (grid.x == 0) return hipSuccess;
+  bool launched = false;
   if constexpr (kSplitVariant<C, TA, TB, ROLE>) {
     if (p.sk_part) {
       hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, true>), grid, block, 0, s, p);
-      return hipGetLastError();
+      launched = true;
     }
   }
-  hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  if (!launched) hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, false>), grid, block, 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ROLE != ROLE_RESID) return e;
+  ResidDecide d;
+  d.ctrl = p.ctrl;
+  d.partials = p.partials;
+  d.partial_stride = p.partial_stride;
+  d.tiles = (int)tiles;
+  d.products = p.products;
+  d.count_update = p.count_update;
+  d.cfg = p.cfg;
+  return launch_resid_decide(d, p.batch, s);
 }
 
 // Roles instantiated per transpose combination: every role in NN (the
@@ -843,9 +845,14 @@ hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipS
   int id = p.cfg_id;
   if (p.sym) {
     // square tiles only: the 128 x 128 tile once the triangle still gives
-    // every CU a tile, else 64 x 64
+    // every CU a tile, or when the split-k tail will spread a long k (>= 2048)
+    // over the CUs anyway; else 64 x 64
     const int64_t t0 = (p.M + 127) / 128;
-    id = (t0 * (t0 + 1) / 2 * p.batch * p.nprob >= (p.num_cu > 0 ? p.num_cu : 256)) ? 0 : 4;
+    const bool long_split = p.sk_part && p.sk_cnt && p.vec && p.M % 128 == 0 &&
+                            p.K % 16 == 0 && p.K >= 2048 && !p.prob[0].a.poly &&
+                            !p.prob[0].b.poly;
+    id = (long_split || t0 * (t0 + 1) / 2 * p.batch * p.nprob >= (p.num_cu > 0 ? p.num_cu : 256))
+             ? 0 : 4;
   } else if (id < 0) {
     const int64_t units = (int64_t)p.batch * p.nprob;
     const int cu = p.num_cu > 0 ? p.num_cu : 256;

@@ -153,17 +153,10 @@ __global__ __launch_bounds__(NT) void gemm_f64_kernel(Gemm64Params p) {
       }
     }
   if (RESID) {
+    // the tile's Frobenius share; resid_decide_kernel sums them
     if (mirror) fro *= 2.0;  // the tile stands for itself and its transpose
     const double bs = block_sum<NT / 64>(fro, red);
-    double tot;
-    if (last_block_sum<NT / 64>(bs, p.partials + (int64_t)b * p.partial_stride, &cb->counter,
-                                tiles, tile, red, &tot)) {
-      if (threadIdx.x == 0) {
-        if (p.count_update) cb->iter += 1;
-        cb->gemms += p.products;
-        decide(*cb, p.cfg, p.cfg.info ? p.cfg.info + b : nullptr, tot);
-      }
-    }
+    if (threadIdx.x == 0) p.partials[(int64_t)b * p.partial_stride + tile] = bs;
   }
 }
 
@@ -279,7 +272,17 @@ hipError_t launch_gemm_f64_bt(const Gemm64Params& p, int role, hipStream_t s) {
     case ROLE_RESID: hipLaunchKernelGGL((gemm_f64_kernel<BT, ROLE_RESID>), grid, dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || role != ROLE_RESID) return e;
+  ResidDecide d;
+  d.ctrl = p.ctrl;
+  d.partials = p.partials;
+  d.partial_stride = p.partial_stride;
+  d.tiles = (int)grid.x;
+  d.products = p.products;
+  d.count_update = p.count_update;
+  d.cfg = p.cfg;
+  return launch_resid_decide(d, p.batch, s);
 }
 
 hipError_t launch_gemm_f64(const Gemm64Params& p, int role, hipStream_t s) {

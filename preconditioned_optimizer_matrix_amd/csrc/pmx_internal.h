@@ -299,6 +299,25 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s);
+// The convergence decision after a residual product: the product's blocks
+// only store their tile's Frobenius share (partials[b][tile], no fence, no
+// arrival counter); this kernel, launched right behind it by the GEMM
+// launchers, sums the `tiles` shares of every running matrix in tile order
+// (fixed order: deterministic), counts the products and the update and runs
+// decide().  (A fenced last-block arrival in every tile of the product wrote
+// back each XCD's L2 per tile: 65-190 us per launch on batches of small
+// matrices.)
+struct ResidDecide {
+  Ctrl* ctrl;
+  const double* partials;
+  int64_t partial_stride;
+  int tiles;         // shares per matrix
+  int products;      // dense products to add to ctrl.gemms
+  int count_update;  // 1: this residual ends an update (iter += 1)
+  IterCfg cfg;
+};
+hipError_t launch_resid_decide(const ResidDecide& d, int batch, hipStream_t s);
+
 
 // The HIP device a handle is bound to (-1 for a null handle).
 int handle_device(pmx_handle h);

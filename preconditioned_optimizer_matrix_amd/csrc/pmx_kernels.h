@@ -211,6 +211,15 @@ struct SmallPolarParams {
 };
 
 hipError_t launch_small_root(const SmallRootParams& p, int batch, hipStream_t s);
+// Variable-size polar factor, blocks above kSmallMaxN: pack one shape group
+// (blocks[idx[0 .. count)], all m x n) into dst (count x m x n fp32, dense),
+// and scatter the group's factors and info records back.
+hipError_t launch_varbatch_gather(const pmx_polar_block* blocks, const int32_t* idx, bool bf16,
+                                  float* dst, int m, int n, int count, hipStream_t s);
+hipError_t launch_varbatch_scatter(const pmx_polar_block* blocks, const int32_t* idx, bool bf16,
+                                   const float* src, int m, int n, int count,
+                                   const pmx_matfn_info* info_src, pmx_matfn_info* info_dst,
+                                   hipStream_t s);
 hipError_t launch_small_polar(const SmallPolarParams& p, int batch, hipStream_t s);
 
 // fp64 leading updates of an inverse root (square n x n buffers, ld n).

@@ -858,6 +858,96 @@ __global__ __launch_bounds__(NT) void convert_kernel(const TI* __restrict__ src,
   }
 }
 
+// ---------------------------------------------------------------- variable-size blocks
+// One shape group of large variable-size blocks: blocks[idx[b]] is packed
+// into dst[b] (m x n fp32, dense) and, after the batched iteration, src[b]
+// goes back to blocks[idx[b]].u (rounded to nearest even for bf16) with the
+// group's info record to info[idx[b]].
+__global__ __launch_bounds__(NT) void varbatch_gather_kernel(const pmx_polar_block* blocks,
+                                                             const int32_t* idx, int bf16,
+                                                             float* dst, int m, int n) {
+  const int b = blockIdx.y;
+  const pmx_polar_block bl = blocks[idx[b]];
+  const int64_t total = (int64_t)m * n;
+  float* out = dst + (int64_t)b * total;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int64_t r = e / n, c = e - r * n;
+    const int64_t o = r * bl.ldg + c;
+    out[e] = bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(bl.g)[o] << 16)
+                  : reinterpret_cast<const float*>(bl.g)[o];
+  }
+}
+
+__global__ __launch_bounds__(NT) void varbatch_scatter_kernel(const pmx_polar_block* blocks,
+                                                              const int32_t* idx, int bf16,
+                                                              const float* src, int m, int n,
+                                                              const pmx_matfn_info* info_src,
+                                                              pmx_matfn_info* info_dst) {
+  const int b = blockIdx.y;
+  const int id = idx[b];
+  const pmx_polar_block bl = blocks[id];
+  const int64_t total = (int64_t)m * n;
+  const float* in = src + (int64_t)b * total;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * NT) {
+    const int64_t r = e / n, c = e - r * n;
+    const int64_t o = r * bl.ldu + c;
+    if (bf16) reinterpret_cast<uint16_t*>(bl.u)[o] = from_f32<bf16_t>(in[e]).bits;
+    else reinterpret_cast<float*>(bl.u)[o] = in[e];
+  }
+  if (info_dst && blockIdx.x == 0) {
+    constexpr int W = (int)(sizeof(pmx_matfn_info) / 4);
+    const int32_t* a = reinterpret_cast<const int32_t*>(info_src + b);
+    int32_t* z = reinterpret_cast<int32_t*>(info_dst + id);
+    for (int w = threadIdx.x; w < W; w += NT) z[w] = a[w];
+  }
+}
+
+static unsigned varbatch_grid(int64_t total) {
+  int64_t g = (total + NT - 1) / NT;
+  return (unsigned)(g < 1 ? 1 : (g > 256 ? 256 : g));
+}
+
+hipError_t launch_varbatch_gather(const pmx_polar_block* blocks, const int32_t* idx, bool bf16,
+                                  float* dst, int m, int n, int count, hipStream_t s) {
+  hipLaunchKernelGGL(varbatch_gather_kernel, dim3(varbatch_grid((int64_t)m * n), count),
+                     dim3(NT), 0, s, blocks, idx, bf16 ? 1 : 0, dst, m, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_varbatch_scatter(const pmx_polar_block* blocks, const int32_t* idx, bool bf16,
+                                   const float* src, int m, int n, int count,
+                                   const pmx_matfn_info* info_src, pmx_matfn_info* info_dst,
+                                   hipStream_t s) {
+  hipLaunchKernelGGL(varbatch_scatter_kernel, dim3(varbatch_grid((int64_t)m * n), count),
+                     dim3(NT), 0, s, blocks, idx, bf16 ? 1 : 0, src, m, n, info_src, info_dst);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- residual decision
+__global__ __launch_bounds__(NT) void resid_decide_kernel(ResidDecide d) {
+  const int b = blockIdx.x;
+  Ctrl* cb = d.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const double* part = d.partials + (int64_t)b * d.partial_stride;
+  double v = 0.0;
+  for (int i = threadIdx.x; i < d.tiles; i += NT) v += part[i];
+  __shared__ double red[NT / 64];
+  const double tot = block_sum<NT / 64>(v, red);
+  if (threadIdx.x == 0) {
+    if (d.count_update) cb->iter += 1;
+    // products counts the powers of the configured degree
+    cb->gemms += d.products + (cb->degree - d.cfg.degree);
+    decide(*cb, d.cfg, d.cfg.info ? d.cfg.info + b : nullptr, tot);
+  }
+}
+
+hipError_t launch_resid_decide(const ResidDecide& d, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(resid_decide_kernel, dim3(batch), dim3(NT), 0, s, d);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- statistics operands
 // The operands of the statistics products in the layout of the scheduled
 // GEMM loop (A with k contiguous, B with n contiguous): G^T (cols x rows,

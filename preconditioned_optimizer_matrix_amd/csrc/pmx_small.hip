@@ -394,6 +394,8 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
   int64_t ldg = p.ldg, ldu = p.ldu;
   if (p.blocks) {
     const pmx_polar_block blk = p.blocks[b];
+    // blocks above the fused order go through the batched path instead
+    if (blk.m > SN || blk.n > SN) return;
     transpose = blk.m < blk.n;
     rows = transpose ? blk.n : blk.m;
     cols = transpose ? blk.m : blk.n;

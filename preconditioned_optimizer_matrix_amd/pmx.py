@@ -12,13 +12,16 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpmx.so")
+# PMX_LIBRARY selects another build of the same library (the host-sanitized
+# libpmx_san.so of build.py's --sanitize); there is no other implementation
+LIB_PATH = os.environ.get("PMX_LIBRARY") or os.path.join(_HERE, "libpmx.so")
 
 OK, ERR_INVALID_VALUE, ERR_NOT_SUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(6)
 RUNNING, CONVERGED, MAXITER, STAGNATED, NONFINITE, DIVERGED = -1, 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 OP_STATS, OP_INV_ROOT, OP_POLAR, OP_APPLY, OP_POLAR_VARBATCH = range(5)
 VARBATCH_MAX_DIM = 64
+VARBATCH_MAX_SIDE = 8192
 OPTS_VERSION = 4
 METHOD_NEWTON_SCHULZ, METHOD_INVERSE_NEWTON = 0, 1
 SCALE_FROBENIUS, SCALE_POWER = 0, 1
@@ -37,7 +40,7 @@ EXPORTS = [
     "pmx_trace_enable", "pmx_trace_collect", "pmx_set_host_poll",
     "pmx_shampoo_config_default", "pmx_shampoo_plan_create", "pmx_shampoo_plan_destroy",
     "pmx_shampoo_plan_sizes", "pmx_shampoo_plan_init", "pmx_shampoo_plan_step",
-    "pmx_sketch_gaussian", "pmx_precond_apply_noalloc",
+    "pmx_sketch_gaussian", "pmx_precond_apply_noalloc", "pmx_polar_varbatch_workspace_size",
 ]
 
 # kernel classes of the launch trace (pmx_kernel_class)
@@ -125,6 +128,9 @@ def _load():
         "pmx_precond_apply_batched": (_i32, [_vp, _vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32,
                                              _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32, _vp,
                                              _sz, _vp]),
+        "pmx_polar_varbatch_workspace_size": (_i32, [ctypes.POINTER(PolarBlock), _i32, _i32,
+                                                     ctypes.POINTER(Opts),
+                                                     ctypes.POINTER(_sz)]),
         "pmx_precond_apply_noalloc": (_i32, [_vp, _vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32,
                                              _i64, _vp, _i32, _i64, _vp, _i32, _i64, _i32,
                                              _vp]),
@@ -337,9 +343,10 @@ def polar(G, opts=None, out=None, info=None, ws=None):
 
 
 def polar_varbatch(Gs, opts=None, outs=None, info=None, ws=None):
-    """Polar factors of a list of 2-D blocks of different shapes (each at most
-    VARBATCH_MAX_DIM on a side, one dtype), in one launch; returns
-    (list of U, info_tensor)."""
+    """Polar factors of a list of 2-D blocks of different shapes (sides up to
+    VARBATCH_MAX_SIDE, one dtype) in one call: blocks of sides up to
+    VARBATCH_MAX_DIM in one fused launch, larger ones grouped by shape;
+    returns (list of U, info_tensor)."""
     torch = _torch()
     if opts is None:
         opts = default_opts()
@@ -354,7 +361,11 @@ def polar_varbatch(Gs, opts=None, outs=None, info=None, ws=None):
     dev = Gs[0].device
     if info is None:
         info = new_info(count, dev)
-    need = workspace_bytes(OP_POLAR_VARBATCH, 1, 1, count, _dtype_code(Gs[0]), opts)
+    sz = _sz()
+    check(lib.pmx_polar_varbatch_workspace_size(arr, count, _dtype_code(Gs[0]),
+                                                ctypes.byref(opts), ctypes.byref(sz)),
+          "polar_varbatch_workspace_size")
+    need = sz.value
     if ws is None or ws.numel() < need:
         ws = workspace(need, dev)
     check(lib.pmx_matfn_polar_varbatch(handle(dev.index), arr, count, _dtype_code(Gs[0]),

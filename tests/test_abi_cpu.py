@@ -77,6 +77,22 @@ def test_workspace_sizes_and_option_validation():
     # variable-size polar: the descriptors (32 bytes each), 256-byte aligned
     assert ctypes.sizeof(pmx.PolarBlock) == 32
     assert pmx.workspace_bytes(pmx.OP_POLAR_VARBATCH, 1, 1, 100, pmx.F32, None) == 3328
+    # with blocks above the fused order: descriptors, grouped indices, and one
+    # shape group's scratch (packed input and output, info, batched workspace)
+    blk = (pmx.PolarBlock * 3)(pmx.PolarBlock(None, None, 8, 8, 8, 8),
+                               pmx.PolarBlock(None, None, 100, 30, 30, 30),
+                               pmx.PolarBlock(None, None, 100, 30, 30, 30))
+    sz = ctypes.c_size_t()
+    assert pmx.lib.pmx_polar_varbatch_workspace_size(blk, 1, pmx.F32, None,
+                                                     ctypes.byref(sz)) == pmx.OK
+    assert sz.value == 256
+    assert pmx.lib.pmx_polar_varbatch_workspace_size(blk, 3, pmx.F32, None,
+                                                     ctypes.byref(sz)) == pmx.OK
+    grp = pmx.workspace_bytes(pmx.OP_POLAR, 100, 30, 2, pmx.F32, o)
+    assert sz.value >= 256 + 256 + 2 * 4 * 100 * 30 * 2 + 2 * ctypes.sizeof(pmx.Info) + grp
+    blk[1].m = pmx.VARBATCH_MAX_SIDE + 1
+    assert pmx.lib.pmx_polar_varbatch_workspace_size(blk, 3, pmx.F32, None,
+                                                     ctypes.byref(sz)) == pmx.ERR_INVALID_VALUE
     assert pmx.workspace_bytes(pmx.OP_APPLY, 1024, 4096, 1, pmx.F32, None) >= 4 * 1024 * 4096
     pb = pmx.workspace_bytes(pmx.OP_POLAR, 4096, 1024, 1, pmx.F32, o)
     assert pb >= 2 * 4 * 4096 * 1024 + 2 * 4 * 1024 * 1024

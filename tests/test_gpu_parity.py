@@ -426,7 +426,7 @@ def test_polar_varbatch(env):
         gq = g.float().cpu().numpy()
         assert cf.rel_fro(u.float().cpu().numpy(), cf.polar(gq)[0]) < 1e-2
     # argument errors: a block above the limit, an output overlapping its input
-    big = torch.zeros(65, 8, device=dev)
+    big = torch.zeros(pmx.VARBATCH_MAX_SIDE + 1, 2, device=dev)
     with pytest.raises(pmx.PmxError):
         pmx.polar_varbatch([torch.from_numpy(Gs[0]).to(dev), big])
     g0 = torch.from_numpy(Gs[5]).to(dev)
@@ -435,6 +435,42 @@ def test_polar_varbatch(env):
     with pytest.raises(pmx.PmxError):
         pmx.polar_varbatch([g0], opts=pmx.default_opts(degree=3))
     torch.cuda.synchronize()
+
+
+def test_polar_varbatch_large_blocks(env, margin):
+    # blocks above the fused order (grouped by shape, packed, batched fp32
+    # iteration, scattered back) mixed with small ones in one call, against
+    # the SVD polar factor; sides up to 512, tall and wide, repeated shapes
+    torch, pmx, dev = env
+    shapes = [(65, 40), (100, 300), (300, 100), (512, 512), (128, 128), (7, 9),
+              (128, 128), (200, 64), (64, 200), (128, 128), (40, 65), (384, 96), (33, 1)]
+    Gs = [W.gaussian(m, n, 900 + i) for i, (m, n) in enumerate(shapes)]
+    _say("polar varbatch with large blocks", len(Gs))
+    Us, info = pmx.polar_varbatch([torch.from_numpy(g).to(dev) for g in Gs],
+                                  opts=pmx.default_opts(seed=5))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)
+    worst = 0.0
+    for i, (g, u) in enumerate(zip(Gs, Us)):
+        assert int(inf[i]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), (i, shapes[i])
+        e = cf.rel_fro(u.cpu().numpy(), cf.polar(g)[0])
+        worst = max(worst, e)
+        assert e < 1e-4, (i, shapes[i], e)
+        # a single column is orthonormal after the scaling: no update
+        assert (int(inf[i]["iters"][0]) > 0) == (min(shapes[i]) > 1), (i, shapes[i])
+    margin("varbatch blocks up to 512 vs SVD factor (fp32)", worst, 1e-4)
+    # bf16: fp32 inside, one rounding on store
+    Gb = [_bf16(torch, g).to(dev) for g in Gs[:6]]
+    Ub, _ = pmx.polar_varbatch(Gb)
+    torch.cuda.synchronize()
+    for g, u in zip(Gb, Ub):
+        gq = g.float().cpu().numpy()
+        assert cf.rel_fro(u.float().cpu().numpy(), cf.polar(gq)[0]) < 1e-2
+    # the same large block alone through the batched call: identical factor
+    # (same kernels; the sketch of group position 0 equals batch position 0)
+    U1, _ = pmx.polar(torch.from_numpy(Gs[3]).to(dev), opts=pmx.default_opts(seed=5))
+    torch.cuda.synchronize()
+    assert torch.equal(U1, Us[3])
 
 
 def test_rank_deficient_statistics(env):

@@ -1,7 +1,6 @@
 """Pins for the whole-step Shampoo reference (oracle.shampoo_step)."""
 import numpy as np
 
-from oracle import closed_form as cf
 from oracle import shampoo_step as ss
 
 
@@ -19,9 +18,18 @@ def test_conv_view_matches_the_page_index_map():
     np.testing.assert_array_equal(ss.from_matrix_view(V, K.shape), K)
 
 
+def _root4(A):
+    # an independent route to A^{-1/4}: scipy's Schur-based fractional power
+    # (not the eigendecomposition the oracle uses)
+    from scipy.linalg import fractional_matrix_power
+    return np.real(fractional_matrix_power(A, -0.25))
+
+
 def test_one_block_is_the_dense_shampoo_update():
-    # block >= the matrix: the step is W - lr L^{-1/4} G R^{-1/4} with the
-    # closed-form statistics and roots (the update of the Shampoo page)
+    # block >= the matrix: the step is W - lr L^{-1/4} G R^{-1/4} (the update
+    # of the Shampoo page, section 2.3), checked with Schur-based roots and
+    # the Kronecker form of section 2.1: vec_r(L G R) = (L (x) R^T) vec_r(G)
+    # for row-major vectorisation
     rng = np.random.default_rng(2)
     W = rng.standard_normal((6, 9))
     Gs = [rng.standard_normal((6, 9)) for _ in range(3)]
@@ -30,12 +38,11 @@ def test_one_block_is_the_dense_shampoo_update():
     Wr = W.copy()
     for t, G in enumerate(Gs):
         W = ss.step(st, [W], [G], t, 0.9, 1e-3, 0.1)[0]
-        L = 0.9 * L + 0.1 * G @ G.T + 1e-3 * np.eye(6)
-        R = 0.9 * R + 0.1 * G.T @ G + 1e-3 * np.eye(9)
-        wl, ql = np.linalg.eigh(L)
-        wr, qr = np.linalg.eigh(R)
-        Wr = Wr - 0.1 * (ql * wl ** -0.25) @ ql.T @ G @ (qr * wr ** -0.25) @ qr.T
-    np.testing.assert_allclose(W, Wr, atol=1e-10)
+        L = 0.9 * L + 0.1 * np.einsum("ik,jk->ij", G, G) + 1e-3 * np.eye(6)
+        R = 0.9 * R + 0.1 * np.einsum("ki,kj->ij", G, G) + 1e-3 * np.eye(9)
+        P = (np.kron(_root4(L), _root4(R).T) @ G.reshape(-1)).reshape(6, 9)
+        Wr = Wr - 0.1 * P
+    np.testing.assert_allclose(W, Wr, atol=1e-9)
 
 
 def test_blocks_are_independent_parameters():
@@ -67,8 +74,9 @@ def test_momentum_and_stale_roots_and_adaptive_rate():
     W = W0.copy()
     for t in range(5):
         W = ss.step(st, [W], [G], t, 0.9, 1e-2, 0.1, momentum=0.5, root_every=100)[0]
-    L1, R1 = cf.stats_update(1e-2 * np.eye(4), 1e-2 * np.eye(3), G, 0.9, 1e-2)
-    P = cf.inv_root(L1, 4)[0] @ G @ cf.inv_root(R1, 4)[0]
+    L1 = 0.9 * 1e-2 * np.eye(4) + 0.1 * G @ G.T + 1e-2 * np.eye(4)
+    R1 = 0.9 * 1e-2 * np.eye(3) + 0.1 * G.T @ G + 1e-2 * np.eye(3)
+    P = _root4(L1) @ G @ _root4(R1)
     expect = W0 - 0.1 * sum(P * (1 - 0.5 ** (t + 1)) / 0.5 for t in range(5))
     np.testing.assert_allclose(W, expect, atol=1e-10)
     st2 = ss.ShampooState([(4, 3)], block=8, eps=1e-2)
