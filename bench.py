@@ -59,7 +59,8 @@ def parse():
                     metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE", "BENCH_JSON"),
                     help="only write the update GEMM's HBM traffic record from four "
                          "rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of "
-                         "'--steps 1 --warmup 0 --no-cpu-baseline --no-trace --host-poll 0', "
+                         "'--steps 1 --warmup 0 --no-cpu-baseline --no-trace --no-secondary "
+                         "--host-poll 0', "
                          "then of --calibrate-copy) and the JSON line that profiled bench "
                          "run printed (for its R^-1/4 update counts)")
     ap.add_argument("--sweep", choices=["sketch", "sigma"],
@@ -489,8 +490,8 @@ def write_traffic(dirs):
         "write_scale": round(ws, 5),
         "hbm_bytes_per_product": int(round((f_raw * fs + w_raw * ws) * 1024 / products)),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace --host-poll 0 > <json>",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace --host-poll 0",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace --no-secondary --host-poll 0 > <json>",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-trace --no-secondary --host-poll 0",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --calibrate-copy",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o p -- python3 bench.py --calibrate-copy",
             "python3 bench.py --traffic-from <four dirs> <json>",
