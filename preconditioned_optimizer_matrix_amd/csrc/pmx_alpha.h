@@ -8,17 +8,22 @@
 namespace pmx {
 
 // ---------------------------------------------------------------- alpha fit
-// Real roots of a x^2 + b x + c inside (lo, hi).
-__device__ inline int quad_roots_in(double a, double b, double c, double lo, double hi, double* out) {
-  int n = 0;
+// Real roots of a x^2 + b x + c inside (lo, hi), ascending, in r0 (and r1);
+// returns how many.  Scalars only: an indexed array here would live in
+// scratch memory, whose store-then-load costs a memory round trip.
+__device__ inline int quad_roots_in(double a, double b, double c, double lo, double hi,
+                                    double& r0, double& r1) {
   const double scale = fmax(fabs(a), fmax(fabs(b), fabs(c)));
   if (scale == 0.0) return 0;
   if (fabs(a) <= 1e-14 * scale) {
     if (b != 0.0) {
       const double x = -c / b;
-      if (x > lo && x < hi) out[n++] = x;
+      if (x > lo && x < hi) {
+        r0 = x;
+        return 1;
+      }
     }
-    return n;
+    return 0;
   }
   const double disc = b * b - 4.0 * a * c;
   if (disc < 0.0) return 0;
@@ -26,44 +31,46 @@ __device__ inline int quad_roots_in(double a, double b, double c, double lo, dou
   const double q = -0.5 * (b + (b >= 0.0 ? sq : -sq));
   const double x1 = q / a;
   const double x2 = (q != 0.0) ? c / q : x1;
-  if (x1 > lo && x1 < hi) out[n++] = x1;
-  if (x2 > lo && x2 < hi && x2 != x1) out[n++] = x2;
-  return n;
+  const bool in1 = x1 > lo && x1 < hi;
+  const bool in2 = x2 > lo && x2 < hi && x2 != x1;
+  if (in1 && in2) {
+    r0 = fmin(x1, x2);
+    r1 = fmax(x1, x2);
+    return 2;
+  }
+  if (in1 || in2) {
+    r0 = in1 ? x1 : x2;
+    return 1;
+  }
+  return 0;
 }
 
 // argmin over [lo, hi] of phi(a) = w0 + w1 a + w2 a^2 + w3 a^3 + w4 a^4.
 // phi' is a cubic; the roots of phi'' split [lo, hi] into pieces on which
 // phi' is monotone, and every sign change of phi' on a piece is refined to
-// full double precision by bracketed Newton steps.  Candidates are both ends and those critical
-// points; the smallest phi wins, ties to the smaller alpha.
+// full double precision by bracketed Newton steps.  Candidates are both ends
+// and those critical points, met in ascending order (lo, the pieces left to
+// right, hi); the smallest phi wins, ties to the smaller alpha.
 __device__ inline double argmin_quartic(const double (&w)[5], double lo, double hi) {
   auto phi = [&](double a) { return w[0] + a * (w[1] + a * (w[2] + a * (w[3] + a * w[4]))); };
   auto dphi = [&](double a) { return w[1] + a * (2.0 * w[2] + a * (3.0 * w[3] + a * 4.0 * w[4])); };
   auto d2phi = [&](double a) { return 2.0 * w[2] + a * (6.0 * w[3] + a * 12.0 * w[4]); };
-  double brk[4];
-  int nb = 0;
-  brk[nb++] = lo;
-  double qr[2];
-  const int nq = quad_roots_in(12.0 * w[4], 6.0 * w[3], 2.0 * w[2], lo, hi, qr);
-  if (nq == 2 && qr[1] < qr[0]) {
-    const double t = qr[0];
-    qr[0] = qr[1];
-    qr[1] = t;
-  }
-  for (int i = 0; i < nq; ++i) brk[nb++] = qr[i];
-  brk[nb++] = hi;
-  double cand[6];
-  int nc = 0;
-  cand[nc++] = lo;
-  for (int i = 0; i + 1 < nb; ++i) {
-    double x0 = brk[i], x1 = brk[i + 1];
+  double best = lo, bv = phi(lo);
+  auto consider = [&](double x) {
+    const double v = phi(x);
+    if (v < bv) {
+      bv = v;
+      best = x;
+    }
+  };
+  auto piece = [&](double x0, double x1) {
     double f0 = dphi(x0);
     const double f1 = dphi(x1);
     if (f0 == 0.0) {
-      if (x0 > lo && x0 < hi) cand[nc++] = x0;
-      continue;
+      if (x0 > lo && x0 < hi) consider(x0);
+      return;
     }
-    if ((f0 < 0.0) == (f1 < 0.0) || f1 == 0.0) continue;
+    if ((f0 < 0.0) == (f1 < 0.0) || f1 == 0.0) return;
     // phi' is monotone on the piece: Newton steps on phi' kept inside the
     // sign-change bracket (a bisection step whenever Newton would leave it)
     // converge quadratically; stop at a step within 4 ulp or an exhausted
@@ -91,23 +98,22 @@ __device__ inline double argmin_quartic(const double (&w)[5], double lo, double 
       if (!(xn > x0 && xn < x1)) break;
       x = xn;
     }
-    if (x > lo && x < hi) cand[nc++] = x;
-  }
-  cand[nc++] = hi;
-  for (int i = 1; i < nc; ++i)
-    for (int j = i; j > 0 && cand[j] < cand[j - 1]; --j) {
-      const double t = cand[j];
-      cand[j] = cand[j - 1];
-      cand[j - 1] = t;
-    }
-  double best = cand[0], bv = phi(cand[0]);
-  for (int i = 1; i < nc; ++i) {
-    const double v = phi(cand[i]);
-    if (v < bv) {
-      bv = v;
-      best = cand[i];
+    if (x > lo && x < hi) consider(x);
+  };
+  double q0 = hi, q1 = hi;
+  const int nq = quad_roots_in(12.0 * w[4], 6.0 * w[3], 2.0 * w[2], lo, hi, q0, q1);
+  if (nq == 0) {
+    piece(lo, hi);
+  } else {
+    piece(lo, q0);
+    if (nq == 1) {
+      piece(q0, hi);
+    } else {
+      piece(q0, q1);
+      piece(q1, hi);
     }
   }
+  consider(hi);
   return best;
 }
 

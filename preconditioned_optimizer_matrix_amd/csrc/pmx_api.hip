@@ -1001,7 +1001,10 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   c->split_k = 1;
   if (const char* e = getenv("PMX_SPLITK")) c->split_k = atoi(e);
   // measured slower for the 32 x 4096 x 1024 polar (320 triangle tiles of 256^2
-  // still take two rounds of the compute units, and the mirrored stores cost)
+  // still take two rounds of the compute units, and the mirrored stores cost;
+  // a split-k tail that cut the second round to 64 x 4 pieces took the
+  // residual from 246 to 204 us, but summing the pieces in a second launch
+  // took 96 us on the 64 tail tiles)
   c->bf16_sym = 0;
   if (const char* e = getenv("PMX_BF16_SYM")) c->bf16_sym = atoi(e);
   c->bf16_sym_small = 0;

@@ -238,6 +238,10 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[C::FM][C::FN],
 template <class C>
 constexpr bool kTransposeInLds = C::BN * (C::BM + 8) <= 2 * C::LDS;
 
+// Every loop over the accumulators is unrolled in full (the plain pragma
+// left the 4-wave 256 x 256 tile's loops rolled, and the indexed accumulator
+// array then went through scratch memory: a kilobyte per lane written and
+// read back per tile).
 template <class C, int ROLE, int FM, int FN>
 __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmParams& p,
                                               const GemmProblem& pr, int b, int m0, int n0,
@@ -254,16 +258,16 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
             tp.stride_c % 8 == 0 && ((uintptr_t)tp.c & 15) == 0;
   }
   float fro = 0.f;
-#pragma unroll
+#pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i)
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int j = 0; j < FN; ++j) {
       const int col = n0 + wn + 32 * j + col_in;
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int g = 0; g < 4; ++g) {
         const int row_base = m0 + wm + 32 * i + 8 * g + 4 * hi;
         uint32_t h[4];
-#pragma unroll
+#pragma clang loop unroll(full)
         for (int r = 0; r < 4; ++r) {
           const int row = row_base + r;
           float x = acc[i][j][4 * g + r];
@@ -287,7 +291,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
           // symmetric output: the tile's transpose C[col][row_base .. + 3]
           // (off-diagonal tiles only), and of the bf16 copy of a residual
           float xs[4];
-#pragma unroll
+#pragma clang loop unroll(full)
           for (int r = 0; r < 4; ++r) {
             const int row = row_base + r;
             const float a = acc[i][j][4 * g + r];
@@ -299,7 +303,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
                                    (int64_t)b * p.prob[1].stride_c +
                                    (int64_t)col * p.prob[1].ldc + row_base
                              : nullptr;
-#pragma unroll
+#pragma clang loop unroll(full)
           for (int r = 0; r < 4; ++r)
             if (row_base + r < p.M) {
               Ct[r] = xs[r];
@@ -318,7 +322,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
           if (p.vec && row_base + 3 < p.M) {
             *reinterpret_cast<u32x2*>(T) = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
           } else {
-#pragma unroll
+#pragma clang loop unroll(full)
             for (int r = 0; r < 4; ++r)
               if (row_base + r < p.M) T[r] = (uint16_t)h[r];
           }

@@ -496,6 +496,197 @@ __global__ __launch_bounds__(W * 64) void skinny_mfma_kernel(SkinnyParams p) {
   skinny_finish<Q, RW, GJ, W>(acc, p, job, b, row0 + wid * RW, scale, fro);
 }
 
+// The batched form on the matrix cores (many matrices of a moderate order,
+// where one pass must stream every matrix once at HBM speed): a block of
+// SB_W = 8 waves owns 128 rows of one matrix and each wave 16 of them over
+// the full contraction, so there is no cross-wave reduction.  In (n x q) is
+// staged per SB_CH-row chunk in LDS transposed, In^T[c][k] with row stride
+// SB_LD (SB_LD = 4 mod 32: the 16-byte reads of eight lanes cover all 32
+// banks), so one 16-byte LDS read gives a lane the four values of In that
+// match its 16-byte read of Mat: lane (slot = l / 16, r = l % 16) carries
+// k = 16 u + 4 slot .. + 3 of row r into v_mfma_f32_16x16x4_f32 as A and
+// In[k][r] as B.  Mat is read SB_UN steps at a time into two register sets
+// in turn, so one set is in flight while the other is multiplied, and a
+// chunk's first reads are issued before In is staged.  (Measured on the 32
+// Muon residuals and the 64 blocks of order 512: 8 waves with 4-step sets
+// beat 4 waves and 16-step sets, with or without the second set.)  Rows of In beyond n and columns beyond q
+// are staged as zero.  GJ = 5 (last Krylov pass, J = 2 d + 1 <= 5 blocks):
+// the block's share of the Gram, as in skinny_finish, reduced by recursive
+// halving over the wave and then over the waves in order.
+constexpr int SB_CH = 1024;
+constexpr int SB_LD = SB_CH + 4;
+constexpr int SB_W = 8;
+constexpr int SB_UN = 4;
+
+template <int CNT, int O>
+__device__ __forceinline__ void halve_reduce_d(double* acc, int lane) {
+  if constexpr (O >= 1) {
+    if constexpr (CNT > 1) {
+      constexpr int H = CNT / 2;
+      const bool upper = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const double send = upper ? acc[i] : acc[i + H];
+        const double keep = upper ? acc[i + H] : acc[i];
+        acc[i] = keep + __shfl_xor(send, O, 64);
+      }
+      halve_reduce_d<H, O / 2>(acc, lane);
+    } else {
+      acc[0] += __shfl_xor(acc[0], O, 64);
+      halve_reduce_d<1, O / 2>(acc, lane);
+    }
+  }
+}
+
+template <int Q, int GJ>
+__global__ __launch_bounds__(SB_W * 64) void skinny_batch_kernel(SkinnyParams p) {
+  static_assert(Q == 8 || Q == 16, "Q");
+  static_assert(GJ == 0 || GJ == 5, "GJ");
+  const int b = blockIdx.z;
+  Ctrl* cb = p.ctrl + b;
+  if (load_status(cb) != PMX_RUNNING) return;
+  const SkinnyJob& job = p.job[blockIdx.y];
+  const int n = p.n;
+  const float* __restrict__ mat = job.mat + (int64_t)b * job.mat_stride;
+  float* kb = p.kbuf + (int64_t)b * p.kstride;
+  const double fro = cb->fro;
+  const float scale = skinny_scale(job.pow, fro);
+  __shared__ __attribute__((aligned(16))) float inT[Q * SB_LD];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r = lane & 15, slot = lane >> 4;
+  const int rbase = blockIdx.x * (16 * SB_W) + 16 * wid;
+  const int row = rbase + r;
+  const bool rok = row < n;
+  const float* arow = mat + (int64_t)(rok ? row : 0) * job.mat_ld + 4 * slot;
+  // B reads: column r of In^T (rows q .. Q - 1 are staged as zero; for
+  // Q = 8 the lanes r >= 8 read row 0: a product's column r depends on B's
+  // column r alone, and those columns are not stored)
+  const float* brow = inT + (r < Q ? r : 0) * SB_LD + 4 * slot;
+  const bool in_vec = (p.kld % 4 == 0) && (job.in_col % 4 == 0) && (p.q == Q) &&
+                      ((((uintptr_t)kb) & 15) == 0);
+  sk_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < n; j0 += SB_CH) {
+    const int len = n - j0 < SB_CH ? n - j0 : SB_CH;  // a multiple of 4
+    const int U = (len + 15) >> 4;  // 16-column steps; the last may be partial
+    auto load_a = [&](float4 (&a)[SB_UN], int u0) {
+#pragma unroll
+      for (int i = 0; i < SB_UN; ++i) {
+        const int kk = 16 * (u0 + i) + 4 * slot;  // then kk + 3 < len as well
+        a[i] = (rok && kk < len) ? *reinterpret_cast<const float4*>(arow + j0 + 16 * (u0 + i))
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    // In^T beyond len is zero, and the row stride leaves room for the
+    // partial last step (16 u + 4 slot + 3 < SB_CH + 4)
+    auto mul = [&](const float4 (&a)[SB_UN], int u0) {
+#pragma unroll
+      for (int i = 0; i < SB_UN; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(brow + 16 * (u0 + i));
+        if (u0 + i < U) {
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].x, x.x, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].y, x.y, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].z, x.z, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i].w, x.w, c, 0, 0, 0);
+        }
+      }
+    };
+    float4 ba[SB_UN], bb[SB_UN];
+    load_a(ba, 0);
+    __syncthreads();
+    // rows [0, lim) of the chunk are read by the products below
+    const int lim = 16 * U;
+    if (in_vec) {
+      for (int idx = threadIdx.x; idx < lim * (Q / 4); idx += SB_W * 64) {
+        const int jj = idx / (Q / 4), cc = 4 * (idx - jj * (Q / 4));
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (jj < len)
+          v = *reinterpret_cast<const float4*>(kb + (int64_t)(j0 + jj) * p.kld + job.in_col + cc);
+        inT[(cc + 0) * SB_LD + jj] = v.x;
+        inT[(cc + 1) * SB_LD + jj] = v.y;
+        inT[(cc + 2) * SB_LD + jj] = v.z;
+        inT[(cc + 3) * SB_LD + jj] = v.w;
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < lim * Q; idx += SB_W * 64) {
+        const int jj = idx / Q, cc = idx - jj * Q;
+        float v = 0.f;
+        if (jj < len && cc < p.q) v = kb[(int64_t)(j0 + jj) * p.kld + job.in_col + cc];
+        inT[cc * SB_LD + jj] = v;
+      }
+    }
+    __syncthreads();
+    for (int u0 = 0; u0 < U; u0 += 2 * SB_UN) {
+      load_a(bb, u0 + SB_UN);
+      mul(ba, u0);
+      load_a(ba, u0 + 2 * SB_UN);
+      mul(bb, u0 + SB_UN);
+    }
+  }
+  // lane l holds D[4 (l / 16) + v][l % 16]: rows rbase + 4 slot + v, column r
+  const int col = r;
+  float outv[4];
+  bool valid[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int orow = rbase + 4 * slot + v;
+    valid[v] = orow < n && col < p.q;
+    float a = c[v] * scale;
+    if (job.pow == 0 && valid[v]) a = kb[(int64_t)orow * p.kld + job.in_col + col] - a;
+    if (valid[v]) kb[(int64_t)orow * p.kld + job.out_col + col] = a;
+    outv[v] = a;
+  }
+  if constexpr (GJ != 0) {
+    constexpr int GA = GJ, NE = GA * (GA + 1) / 2;  // 15, reduced as 16
+    const int deg = *(const volatile int32_t*)&cb->degree;
+    const int J = 2 * deg + 1;
+    const int pp = p.cfg.p;
+    const int jo = job.out_col / pp;
+    double g[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) g[e] = 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      double x[GA];
+#pragma unroll
+      for (int j = 0; j < GA; ++j) x[j] = 0.0;
+      if (valid[v]) {
+        const int orow = rbase + 4 * slot + v;
+#pragma unroll
+        for (int j = 1; j <= GA; ++j)
+          if (j <= J)
+            x[j - 1] = j == jo ? (double)outv[v]
+                               : (double)kb[(int64_t)orow * p.kld + j * pp + col];
+      }
+      int t = 0;
+#pragma unroll
+      for (int a = 0; a < GA; ++a)
+#pragma unroll
+        for (int bb = a; bb < GA; ++bb, ++t) g[t] += x[a] * x[bb];
+    }
+    // lane l ends with the wave's sum of value l / 4
+    halve_reduce_d<16, 32>(g, lane);
+    __shared__ double wsum[SB_W][16];
+    if ((lane & 3) == 0) wsum[wid][lane >> 2] = g[0];
+    __syncthreads();
+    const int ng = J * (J + 1) / 2;
+    if (threadIdx.x < ng) {
+      // packed index e -> index t of (a, bb) in the GA enumeration
+      int t = 0, o = 0, te = 0;
+      for (int a = 0; a < GA; ++a)
+        for (int bb = a; bb < GA; ++bb, ++t)
+          if (a < J && bb < J) {
+            if (o == (int)threadIdx.x) te = t;
+            ++o;
+          }
+      double tot = wsum[0][te];
+      for (int w = 1; w < SB_W; ++w) tot += wsum[w][te];
+      double* part = p.gram_partials + (int64_t)b * p.gram_stride;
+      part[(int64_t)blockIdx.x * kGramShare + threadIdx.x] = tot;
+    }
+    (void)NE;
+  }
+}
+
 template <int Q, int RW, int GJ>
 __global__ __launch_bounds__(NT) void skinny_kernel(SkinnyParams p) {
   constexpr int CNT = RW * Q;  // partial sums per lane
@@ -1017,6 +1208,53 @@ __global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
   }
   __shared__ float tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (p.vec4 == 2) {
+    // the same with 16-byte accesses (rows, cols and leading dimensions
+    // multiples of 8): thread t moves the 8 bf16 chunk t % 8 of rows t / 8
+    // and t / 8 + 32 in, and of rows t / 8 and t / 8 + 32 of the transpose
+    // out; both reads are issued before either is used
+    const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.a) + (int64_t)b * p.sa;
+    const int q = threadIdx.x & 7, rr = threadIdx.x >> 3;
+    const int gc = c0 + 8 * q;
+    uint4 w[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int gr = r0 + rr + 32 * i;
+      w[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (gr < p.rows && gc < p.cols)
+        w[i] = *reinterpret_cast<const uint4*>(ab + (int64_t)gr * p.lda + gc);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = rr + 32 * i, gr = r0 + r;
+      const uint32_t u[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(u[j] << 16) * scale;
+        v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u) * scale;
+      }
+      if (p.out_n && gr < p.rows && gc < p.cols)
+        *reinterpret_cast<uint4*>(p.out_n + (int64_t)b * p.sn + (int64_t)gr * p.ldn + gc) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[r][8 * q + j] = v[j];
+    }
+    __syncthreads();
+    if (!p.out_t) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = rr + 32 * i, gcol = c0 + c, gr = r0 + 8 * q;
+      if (gcol < p.cols && gr < p.rows)
+        *reinterpret_cast<uint4*>(p.out_t + (int64_t)b * p.st + (int64_t)gcol * p.ldt + gr) =
+            make_uint4(pack_bf16x2(tile[8 * q][c], tile[8 * q + 1][c]),
+                       pack_bf16x2(tile[8 * q + 2][c], tile[8 * q + 3][c]),
+                       pack_bf16x2(tile[8 * q + 4][c], tile[8 * q + 5][c]),
+                       pack_bf16x2(tile[8 * q + 6][c], tile[8 * q + 7][c]));
+    }
+    return;
+  }
   if (p.vec4) {
     // bf16 input without a polynomial: each thread moves four consecutive
     // bf16 (8 bytes) per access, both reading rows and writing the
@@ -1152,18 +1390,36 @@ __global__ __launch_bounds__(NT) void polar_finish_kernel(PolarFinishParams p) {
   const T* X = reinterpret_cast<const T*>(p.xbuf[it & 1]) + (int64_t)b * p.buf_stride;
   T* U = reinterpret_cast<T*>(p.u) + (int64_t)b * p.u_stride;
   if (p.vec && !p.transpose) {
-    // straight copy, 16 bytes per thread (cols, ldu and the bases aligned)
+    // straight copy, 16 bytes per chunk (cols, ldu and the bases aligned):
+    // the matrix's rows x cols / V chunks in a grid-stride loop, four chunks
+    // a thread with their reads in flight together
     constexpr int V = 16 / sizeof(T);
     const int cv = p.cols / V;
+    const int total = p.rows * cv;
     uint4 nanv;
     {
       const uint32_t w = sizeof(T) == 2 ? 0x7FC07FC0u : 0x7FC00000u;
       nanv = make_uint4(w, w, w, w);
     }
-    for (int r = blockIdx.x; r < p.rows; r += gridDim.x) {
-      const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)r * p.cols);
-      uint4* dst = reinterpret_cast<uint4*>(U + (int64_t)r * p.ldu);
-      for (int c = threadIdx.x; c < cv; c += NT) dst[c] = bad ? nanv : src[c];
+    const int step = gridDim.x * NT;
+    for (int e0 = blockIdx.x * NT + threadIdx.x; e0 < total; e0 += 4 * step) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * step;
+        if (e < total) {
+          const int r = e / cv, c = e - r * cv;
+          v[u] = bad ? nanv : reinterpret_cast<const uint4*>(X + (int64_t)r * p.cols)[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * step;
+        if (e < total) {
+          const int r = e / cv, c = e - r * cv;
+          reinterpret_cast<uint4*>(U + (int64_t)r * p.ldu)[c] = v[u];
+        }
+      }
     }
     return;
   }
@@ -1289,6 +1545,27 @@ hipError_t launch_skinny(const SkinnyParams& pin, int njobs, bool gram, int batc
       ok = ok && p.job[j].mat_ld % 4 == 0 && ((uintptr_t)p.job[j].mat & 15) == 0 &&
            p.job[j].mat_stride % 4 == 0;
     p.mfma = ok ? 1 : 0;
+  }
+  // batches past the matrix-core form's limit: the batched matrix-core form
+  // (Gram passes at degree <= 2 only)
+  if (!p.mfma && p.variant == 0 && p.q <= 16 && p.n % 4 == 0 && p.n >= 64 &&
+      (!gram || (p.gram_j == 0 && p.cfg.degree_max != 3 && p.cfg.degree <= 2))) {
+    bool ok = true;
+    for (int j = 0; j < njobs; ++j)
+      ok = ok && p.job[j].mat_ld % 4 == 0 && ((uintptr_t)p.job[j].mat & 15) == 0 &&
+           p.job[j].mat_stride % 4 == 0;
+    if (ok) {
+      dim3 g((p.n + 16 * SB_W - 1) / (16 * SB_W), njobs, batch);
+      if (p.q <= 8) {
+        if (gram) hipLaunchKernelGGL((skinny_batch_kernel<8, 5>), g, dim3(SB_W * 64), 0, s, p);
+        else hipLaunchKernelGGL((skinny_batch_kernel<8, 0>), g, dim3(SB_W * 64), 0, s, p);
+      } else {
+        if (gram) hipLaunchKernelGGL((skinny_batch_kernel<16, 5>), g, dim3(SB_W * 64), 0, s, p);
+        else hipLaunchKernelGGL((skinny_batch_kernel<16, 0>), g, dim3(SB_W * 64), 0, s, p);
+      }
+      if (gram) hipLaunchKernelGGL(gram_alpha_kernel, dim3(batch), dim3(NT), 0, s, p, (int)g.x);
+      return hipGetLastError();
+    }
   }
   // more rows per wave once that still leaves two blocks per compute unit
   const bool wide = (int64_t)((p.n + 31) / 32) * njobs * batch >= 512;
@@ -1497,6 +1774,12 @@ hipError_t launch_xpose(const XposeParams& pin, int batch, hipStream_t s) {
            (batch == 1 || p.sa % 4 == 0) && al8(p.a) &&
            (!p.out_n || (p.ldn % 4 == 0 && (batch == 1 || p.sn % 4 == 0) && al8(p.out_n))) &&
            (!p.out_t || (p.ldt % 4 == 0 && (batch == 1 || p.st % 4 == 0) && al8(p.out_t)));
+  auto al16 = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
+  if (p.vec4 && p.rows % 8 == 0 && p.cols % 8 == 0 && p.lda % 8 == 0 &&
+      (batch == 1 || p.sa % 8 == 0) && al16(p.a) &&
+      (!p.out_n || (p.ldn % 8 == 0 && (batch == 1 || p.sn % 8 == 0) && al16(p.out_n))) &&
+      (!p.out_t || (p.ldt % 8 == 0 && (batch == 1 || p.st % 8 == 0) && al16(p.out_t))))
+    p.vec4 = 2;
   dim3 grid((p.cols + 63) / 64, (p.rows + 63) / 64, batch);
   hipLaunchKernelGGL(xpose_kernel, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
@@ -1513,9 +1796,18 @@ hipError_t launch_polar_finish(const PolarFinishParams& pin, bool bf16, int batc
   const int V = bf16 ? 8 : 4;
   p.vec = (p.cols % V == 0) && (p.ldu % V == 0) && (p.buf_stride % V == 0) &&
           (batch == 1 || p.u_stride % V == 0) && ((uintptr_t)p.u % 16 == 0) &&
-          ((uintptr_t)p.xbuf[0] % 16 == 0) && ((uintptr_t)p.xbuf[1] % 16 == 0);
+          ((uintptr_t)p.xbuf[0] % 16 == 0) && ((uintptr_t)p.xbuf[1] % 16 == 0) &&
+          (int64_t)p.rows * (p.cols / V) < ((int64_t)1 << 31);  // chunk index in int
   const int per = (4096 + batch - 1) / batch;
   dim3 grid(grid_rows(p.rows, per < 2048 ? per : 2048), batch);
+  if (p.vec && !p.transpose) {
+    // the copy form: enough blocks for four chunks a thread (about 16384
+    // blocks over the batch at most)
+    const int64_t chunks = (int64_t)p.rows * (p.cols / V);
+    const int64_t want = (chunks + 4 * NT - 1) / (4 * NT);
+    const int64_t cap = std::max<int64_t>(1, 16384 / batch);
+    grid.x = (unsigned)std::max<int64_t>(1, std::min(want, cap));
+  }
   if (bf16) hipLaunchKernelGGL(polar_finish_kernel<bf16_t>, grid, dim3(NT), 0, s, p);
   else hipLaunchKernelGGL(polar_finish_kernel<float>, grid, dim3(NT), 0, s, p);
   return hipGetLastError();

@@ -12,8 +12,11 @@
 //  * Dense products on fp32 MFMA, one 32 x 32 quarter per wave.  The
 //    contraction always runs over the padded 64 (the padding and the rows of
 //    the Krylov buffer beyond n are zero), so every loop unrolls.
+//  * The Krylov blocks (64 x p) are 16 x 16 MFMA tiles spread over the four
+//    waves; their Gram is summed in fp64 by 16 threads per entry.
 //  * The control block lives in LDS; thread 0 applies decide() and the
-//    alpha fit, a barrier publishes the outcome.
+//    alpha fit, a barrier publishes the outcome.  While thread 0 solves for
+//    alpha, the other three waves draw the next iteration's sketch.
 #include "pmx_alpha.h"
 #include "pmx_kernels.h"
 
@@ -24,12 +27,15 @@ constexpr int SN = 64;    // padded order
 constexpr int SLD = 68;   // LDS row stride (floats)
 constexpr int SMAT = SN * SLD;
 constexpr int SNT = 256;
-constexpr int SKLD = 6 * 16;  // Krylov buffer row stride: (2d + 2) p <= 96
+// Krylov buffer row stride: (2d + 2) p <= 96 columns, odd so that the four
+// 16-lane groups of an MFMA operand read (rows 16 apart) fall in distinct banks
+constexpr int SKLD = 6 * 16 + 1;
 
 struct SmallShared {
   float m[6][SMAT];
   float kb[SN * SKLD];
   double red[SNT / 64][16];
+  double gpart[SNT];
   double gsum[16];
   Ctrl c;
 };
@@ -98,10 +104,12 @@ __device__ double small_gemm(float* C, const float* A, const float* B, int n_id,
 
 // S (n x p) of matrix b, stage, iteration k into columns [0, p) of the Krylov
 // buffer: the counter layout and transform of the library's sketch generator.
+// Threads [t0, SNT) take part (no barrier here).
 __device__ void small_sketch(SmallShared& sh, int n, int p, int k, int stage, int b,
-                             uint32_t seed_lo, uint32_t seed_hi) {
+                             uint32_t seed_lo, uint32_t seed_hi, int t0 = 0) {
   const int calls = (n * p + 3) / 4;
-  for (int q = threadIdx.x; q < calls; q += SNT) {
+  if ((int)threadIdx.x < t0) return;
+  for (int q = (int)threadIdx.x - t0; q < calls; q += SNT - t0) {
     uint32_t c[4] = {(uint32_t)q, (uint32_t)k, (uint32_t)stage, (uint32_t)b};
     philox4x32_10(c, seed_lo, seed_hi);
     double z[4];
@@ -114,102 +122,147 @@ __device__ void small_sketch(SmallShared& sh, int n, int p, int k, int stage, in
   }
 }
 
-// out cols [oc, oc + q) = scale * Mat * in cols [ic, ic + q) (n x n Mat; rows
-// of the Krylov buffer beyond n are zero, so the sum runs over 64).  Thread t
-// owns row t / 4 and columns 4 (t % 4) + 16 h .. + 3.
-__device__ void small_skinny(SmallShared& sh, const float* mat, int n, int q, int ic, int oc,
-                             float scale) {
-  const int i = threadIdx.x >> 2, cg = (threadIdx.x & 3) * 4;
-  const bool vec = ((q | ic | oc) & 3) == 0;
-  for (int h = 0; h < q; h += 16) {
-    const int c = h + cg;
-    if (c >= q) break;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (vec) {
-#pragma unroll 16
-      for (int j = 0; j < SN; ++j) {
-        const float a = mat[i * SLD + j];
-        const float4 x = *reinterpret_cast<const float4*>(sh.kb + j * SKLD + ic + c);
-        acc[0] += a * x.x;
-        acc[1] += a * x.y;
-        acc[2] += a * x.z;
-        acc[3] += a * x.w;
-      }
-    } else {
-#pragma unroll 8
-      for (int j = 0; j < SN; ++j) {
-        const float a = mat[i * SLD + j];
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One 16 x 16 tile of kb cols [oc, oc + q) = scale * mat * kb cols [ic, ic + q)
+// (rows 16 rt.., block columns 16 ct..) with 16 v_mfma_f32_16x16x4f32.  The
+// contraction runs over the padded 64 (mat and the Krylov rows beyond n are
+// zero).  In step m, lane group g = l / 16 carries k = 16 g + m, so a lane's
+// 16 values of mat are one contiguous run of its row (four 16-byte reads).
+// All 20 operand reads are issued before the first product (the scheduling
+// barrier keeps the compiler from interleaving them with the products, which
+// would wait on LDS once per pair).  A block column at or beyond q reads
+// column q - 1 (in bounds); a product's column j depends on B's column j
+// alone, so those columns are only left unstored.
+__device__ __forceinline__ void krylov_tile(float* kb, const float* mat, int ic, int oc, int q,
+                                            float scale, int rt, int ct) {
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+  const int col = 16 * ct + li;
+  const bool live = col < q;
+  const float* arow = mat + (16 * rt + li) * SLD + 16 * g;
+  const float* bcol = kb + (16 * g) * SKLD + ic + (live ? col : q - 1);
+  float4 a[4];
+  float bv[16];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (c + v < q) acc[v] += a * sh.kb[j * SKLD + ic + c + v];
-      }
-    }
-    if (i < n) {
+  for (int m4 = 0; m4 < 4; ++m4) a[m4] = *reinterpret_cast<const float4*>(arow + 4 * m4);
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (c + v < q) sh.kb[i * SKLD + oc + c + v] = acc[v] * scale;
-    }
+  for (int m = 0; m < 16; ++m) bv[m] = bcol[m * SKLD];
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m4 = 0; m4 < 4; ++m4) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m4].x, bv[4 * m4 + 0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m4].y, bv[4 * m4 + 1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m4].z, bv[4 * m4 + 2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m4].w, bv[4 * m4 + 3], acc, 0, 0, 0);
+  }
+  // lane l holds block column l % 16 of rows 4 (l / 16) + r
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) kb[(16 * rt + 4 * g + r) * SKLD + oc + col] = acc[r] * scale;
+  }
+}
+
+struct KrylovJob {
+  const float* mat;
+  int ic, oc, q;
+  float scale;
+};
+
+// One step of the Krylov recursion: the tiles of up to two independent
+// products, tile t on wave t % 4, then a barrier.
+__device__ void krylov_step(SmallShared& sh, KrylovJob j0, KrylovJob j1, int jobs) {
+  const int w = threadIdx.x >> 6;
+  int t = 0;
+  for (int jb = 0; jb < jobs; ++jb) {
+    const KrylovJob& j = jb ? j1 : j0;
+    const int cts = (j.q + 15) >> 4;
+    for (int ct = 0; ct < cts; ++ct)
+      for (int rt = 0; rt < 4; ++rt, ++t)
+        if ((t & 3) == w) krylov_tile(sh.kb, j.mat, j.ic, j.oc, j.q, j.scale, rt, ct);
   }
   __syncthreads();
 }
 
+// The next iteration's sketch, drawn while thread 0 fits alpha.
+struct NextSketch {
+  int on, k, stage, b;
+};
+
 // Krylov blocks of R (and R2), their Gram and alpha (d = 1 or 2), in the
 // order and scaling of the multi-kernel path; alpha lands in sh.c.alpha.
 __device__ void small_alpha(SmallShared& sh, const float* R, const float* R2, int n,
-                            const IterCfg& cfg, const AlphaCoef& coef) {
+                            const IterCfg& cfg, const AlphaCoef& coef, NextSketch nx) {
   const int p = cfg.p, d = cfg.degree;
   const double fro = sh.c.fro;
   const float s1 = (float)(1.0 / fro), s2 = (float)(1.0 / (fro * fro));
   if (d == 2) {
-    small_skinny(sh, R, n, p, 0, p, s1);           // K1 = R S / s
-    small_skinny(sh, R2, n, p, 0, 2 * p, s2);      // K2 = R^2 S / s^2
-    small_skinny(sh, R2, n, 2 * p, p, 3 * p, s2);  // [K3 | K4] = R^2 [K1 | K2] / s^2
-    small_skinny(sh, R2, n, p, 3 * p, 5 * p, s2);  // K5 = R^2 K3 / s^2
+    // K1 = R S / s and K2 = R^2 S / s^2; [K3 | K4] = R^2 [K1 | K2] / s^2;
+    // K5 = R^2 K3 / s^2
+    krylov_step(sh, {R, 0, p, p, s1}, {R2, 0, 2 * p, p, s2}, 2);
+    krylov_step(sh, {R2, p, 3 * p, 2 * p, s2}, {}, 1);
+    krylov_step(sh, {R2, 3 * p, 5 * p, p, s2}, {}, 1);
   } else {
-    for (int j = 1; j <= 3; ++j) small_skinny(sh, R, n, p, (j - 1) * p, j * p, s1);
+    for (int j = 1; j <= 3; ++j) krylov_step(sh, {R, (j - 1) * p, j * p, p, s1}, {}, 1);
   }
-  const int J = 2 * d + 1;
-  double g[15];
-#pragma unroll
-  for (int e = 0; e < 15; ++e) g[e] = 0.0;
-  for (int e = threadIdx.x; e < n * p; e += SNT) {
-    const int i = e / p, c = e - (e / p) * p;
-    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int a = 0; a < 5; ++a)
-      if (a < J) v[a] = (double)sh.kb[i * SKLD + (a + 1) * p + c];
-    int t = 0;
-#pragma unroll
-    for (int a = 0; a < 5; ++a)
-#pragma unroll
-      for (int bb = a; bb < 5; ++bb, ++t) g[t] += v[a] * v[bb];
-  }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // Gram, packed upper triangle of the J x J: entry e = t / 16 is summed in
+  // fp64 by threads 16 e .. 16 e + 15, thread t over rows t % 16 + 16 r
+  // (r < 4: rows beyond n are zero) and columns in chunks of four (the 32
+  // reads of a chunk in flight together; columns at or beyond p read column
+  // p - 1 and count zero); the 16 partial sums are added in lane order.
+  const int J = 2 * d + 1, NE = J * (J + 1) / 2;
   {
-    int t = 0, o = 0;
+    const int e = threadIdx.x >> 4, sl = threadIdx.x & 15;
+    double part = 0.0;
+    if (e < NE) {
+      int a = 0, rem = e;
+      while (rem >= J - a) {
+        rem -= J - a;
+        ++a;
+      }
+      const float* ka = sh.kb + (a + 1) * p + sl * SKLD;
+      const float* kc = sh.kb + (a + rem + 1) * p + sl * SKLD;
+      double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int c0 = 0; c0 < p; c0 += 4) {
+        float va[4][4], vc[4][4];
 #pragma unroll
-    for (int a = 0; a < 5; ++a)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int bb = a; bb < 5; ++bb, ++t) {
-        const double sv = wave_sum(g[t]);
-        if (a < J && bb < J) {
-          if (lane == 0) sh.red[w][o] = sv;
-          ++o;
+          for (int v = 0; v < 4; ++v) {
+            const int c = min(c0 + v, p - 1);
+            va[r][v] = ka[16 * r * SKLD + c];
+            vc[r][v] = kc[16 * r * SKLD + c];
+          }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (c0 + v >= p) break;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc4[r] += (double)va[r][v] * (double)vc[r][v];
         }
       }
+      part = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    }
+    sh.gpart[threadIdx.x] = part;
   }
   __syncthreads();
-  if (threadIdx.x < J * (J + 1) / 2) {
-    const int e = threadIdx.x;
-    sh.gsum[e] = ((sh.red[0][e] + sh.red[1][e]) + sh.red[2][e]) + sh.red[3][e];
+  if (threadIdx.x < NE) {
+    double v = 0.0;
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl) v += sh.gpart[threadIdx.x * 16 + sl];
+    sh.gsum[threadIdx.x] = v;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const double alpha = alpha_from_gram(sh.gsum, J, fro, coef, cfg.lo, cfg.hi);
+    // d <= 2 here: J = 3 or 5 (no code for the degree-3 solve)
+    const double alpha = J == 3 ? alpha_from_gram_t<3>(sh.gsum, fro, coef, cfg.lo, cfg.hi, nullptr)
+                                : alpha_from_gram_t<5>(sh.gsum, fro, coef, cfg.lo, cfg.hi, nullptr);
     sh.c.alpha = alpha;
     sh.c.sketch_products += J;
     const int k = sh.c.iter;
     if (cfg.info && k < PMX_TRACE_LEN) cfg.info->alpha[sh.c.stage][k] = (float)alpha;
+  } else if (nx.on && threadIdx.x >= 64) {
+    // S_{k+1} into columns [0, p): the Krylov blocks no longer need S_k
+    small_sketch(sh, n, p, nx.k, nx.stage, nx.b, cfg.seed_lo, cfg.seed_hi, 64);
   }
   __syncthreads();
 }
@@ -217,18 +270,26 @@ __device__ void small_alpha(SmallShared& sh, const float* R, const float* R2, in
 // G = c0 I_n + c1 R + alpha R2 (d = 2) or c0 I_n + alpha R (d = 1), in place of R2.
 __device__ void small_poly(float* G, const float* R, int n, int d, float c0, float c1,
                            float alpha) {
-  for (int e = threadIdx.x; e < SN * SN; e += SNT) {
-    const int i = e >> 6, j = e & 63;
-    const float rv = R[i * SLD + j];
-    float v = (d == 2) ? c1 * rv + alpha * G[i * SLD + j] : alpha * rv;
-    if (i == j && i < n) v += c0;
-    G[i * SLD + j] = v;
+#pragma unroll
+  for (int e = threadIdx.x, r_ = 0; r_ < SN * SN / 4 / SNT; e += SNT, ++r_) {
+    const int i = e >> 4, j0 = (e & 15) * 4;
+    const float4 r4 = *reinterpret_cast<const float4*>(R + i * SLD + j0);
+    const float4 g4 = *reinterpret_cast<const float4*>(G + i * SLD + j0);
+    const float rv[4] = {r4.x, r4.y, r4.z, r4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w};
+    float o[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      o[v] = (d == 2) ? c1 * rv[v] + alpha * gv[v] : alpha * rv[v];
+      if (i == j0 + v && i < n) o[v] += c0;
+    }
+    *reinterpret_cast<float4*>(G + i * SLD + j0) = make_float4(o[0], o[1], o[2], o[3]);
   }
   __syncthreads();
 }
 
 __device__ void small_fill(float* M, int n, float diag) {
-  for (int e = threadIdx.x; e < SN * SN; e += SNT) {
+  #pragma unroll
+  for (int e = threadIdx.x, r_ = 0; r_ < SN * SN / SNT; e += SNT, ++r_) {
     const int i = e >> 6, j = e & 63;
     M[i * SLD + j] = (i == j && i < n) ? diag : 0.f;
   }
@@ -293,14 +354,22 @@ __global__ __launch_bounds__(SNT, 1) void small_root_kernel(SmallRootParams p) {
   float* Zn = sh.m[3];
   float* R = sh.m[4];
   float* R2 = sh.m[5];
-  // A into Y (zero padded) and ||A||_F
+  // A into Y (zero padded) and ||A||_F; a thread's 16 loads are all in
+  // flight before the first is used
   double acc = 0.0;
-  for (int e = threadIdx.x; e < SN * SN; e += SNT) {
-    const int i = e >> 6, j = e & 63;
-    float v = 0.f;
-    if (i < n && j < n) v = A[(int64_t)i * p.lda + j];
-    Y[i * SLD + j] = v;
-    acc += (double)v * (double)v;
+  {
+    float v[SN * SN / SNT];
+#pragma unroll
+    for (int r = 0; r < SN * SN / SNT; ++r) {
+      const int e = threadIdx.x + r * SNT, i = e >> 6, j = e & 63;
+      v[r] = (i < n && j < n) ? A[(int64_t)i * p.lda + j] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < SN * SN / SNT; ++r) {
+      const int e = threadIdx.x + r * SNT, i = e >> 6, j = e & 63;
+      Y[i * SLD + j] = v[r];
+      acc += (double)v[r] * (double)v[r];
+    }
   }
   small_start(sh, cfg.info, block_total(acc, sh), cfg.degree);
   const bool accel = cfg.accelerate != 0;
@@ -309,7 +378,8 @@ __global__ __launch_bounds__(SNT, 1) void small_root_kernel(SmallRootParams p) {
     if (stage == 0) {
       if (small_status(sh) != PMX_RUNNING) break;
       const float fs = (float)(1.0 / sh.c.c);
-      for (int e = threadIdx.x; e < SN * SN; e += SNT) {
+      #pragma unroll
+      for (int e = threadIdx.x, r_ = 0; r_ < SN * SN / SNT; e += SNT, ++r_) {
         const int i = e >> 6, j = e & 63;
         Y[i * SLD + j] *= fs;
       }
@@ -320,7 +390,8 @@ __global__ __launch_bounds__(SNT, 1) void small_root_kernel(SmallRootParams p) {
     __syncthreads();
     // R_0 = I - Y_0 (Z_0 = I), the first sketch, the decision on r_0
     double f2 = 0.0;
-    for (int e = threadIdx.x; e < SN * SN; e += SNT) {
+    #pragma unroll
+    for (int e = threadIdx.x, r_ = 0; r_ < SN * SN / SNT; e += SNT, ++r_) {
       const int i = e >> 6, j = e & 63;
       const float rv = ((i == j && i < n) ? 1.f : 0.f) - Y[i * SLD + j];
       R[i * SLD + j] = rv;
@@ -340,11 +411,12 @@ __global__ __launch_bounds__(SNT, 1) void small_root_kernel(SmallRootParams p) {
     while (small_status(sh) == PMX_RUNNING) {
       const int k = sh.c.iter;
       if (d == 2) small_gemm<false, false>(R2, R, R, n, sh);
-      if (accel) small_alpha(sh, R, R2, n, cfg, p.coef);
+      if (accel) small_alpha(sh, R, R2, n, cfg, p.coef, {k + 1 < cfg.max_iter, k + 1, stage, b});
       small_poly(R2, R, n, d, p.c0, p.c1, (float)sh.c.alpha);
       small_gemm<false, false>(Yn, Y, R2, n, sh);  // Y g
       if (k == 0) {
-        for (int e = threadIdx.x; e < SN * SN; e += SNT) {
+        #pragma unroll
+        for (int e = threadIdx.x, r_ = 0; r_ < SN * SN / SNT; e += SNT, ++r_) {
           const int i = e >> 6, j = e & 63;
           Zn[i * SLD + j] = R2[i * SLD + j];  // Z_1 = g
         }
@@ -359,8 +431,6 @@ __global__ __launch_bounds__(SNT, 1) void small_root_kernel(SmallRootParams p) {
       Z = Zn;
       Zn = t;
       const double f = small_gemm<false, true>(R, Z, Y, n, sh);  // I - Z Y
-      if (accel && k + 1 < cfg.max_iter)
-        small_sketch(sh, n, cfg.p, k + 1, stage, b, cfg.seed_lo, cfg.seed_hi);
       if (threadIdx.x == 0) {
         sh.c.iter += 1;
         sh.c.gemms += (d - 1) + 1 + (k > 0 ? 1 : 0) + 1;
@@ -416,19 +486,29 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
   float* R = sh.m[4];
   float* R2 = sh.m[5];
   double acc = 0.0;
-  for (int e = threadIdx.x; e < SN * SN; e += SNT) {
-    const int i = e >> 6, j = e & 63;
-    float v = 0.f;
-    if (i < rows && j < cols) v = transpose ? load((int64_t)j * ldg + i) : load((int64_t)i * ldg + j);
-    X[i * SLD + j] = v;
-    acc += (double)v * (double)v;
+  {
+    float v[SN * SN / SNT];
+#pragma unroll
+    for (int r = 0; r < SN * SN / SNT; ++r) {
+      const int e = threadIdx.x + r * SNT, i = e >> 6, j = e & 63;
+      v[r] = (i < rows && j < cols)
+                 ? (transpose ? load((int64_t)j * ldg + i) : load((int64_t)i * ldg + j))
+                 : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < SN * SN / SNT; ++r) {
+      const int e = threadIdx.x + r * SNT, i = e >> 6, j = e & 63;
+      X[i * SLD + j] = v[r];
+      acc += (double)v[r] * (double)v[r];
+    }
   }
   small_start(sh, cfg.info, block_total(acc, sh), cfg.degree);
   const bool accel = cfg.accelerate != 0;
   const int d = cfg.degree;
   if (small_status(sh) == PMX_RUNNING) {
     const float fs = (float)(1.0 / sh.c.c);
-    for (int e = threadIdx.x; e < SN * SN; e += SNT) {
+    #pragma unroll
+    for (int e = threadIdx.x, r_ = 0; r_ < SN * SN / SNT; e += SNT, ++r_) {
       const int i = e >> 6, j = e & 63;
       X[i * SLD + j] *= fs;
     }
@@ -444,15 +524,13 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
     while (small_status(sh) == PMX_RUNNING) {
       const int k = sh.c.iter;
       if (d == 2) small_gemm<false, false>(R2, R, R, cols, sh);
-      if (accel) small_alpha(sh, R, R2, cols, cfg, p.coef);
+      if (accel) small_alpha(sh, R, R2, cols, cfg, p.coef, {k + 1 < cfg.max_iter, k + 1, 0, b});
       small_poly(R2, R, cols, d, p.c0, p.c1, (float)sh.c.alpha);
       small_gemm<false, false>(Xn, X, R2, cols, sh);  // X g
       float* t = X;
       X = Xn;
       Xn = t;
       const double f2 = small_gemm<true, true>(R, X, X, cols, sh);  // I - X^T X
-      if (accel && k + 1 < cfg.max_iter)
-        small_sketch(sh, cols, cfg.p, k + 1, 0, b, cfg.seed_lo, cfg.seed_hi);
       if (threadIdx.x == 0) {
         sh.c.iter += 1;
         sh.c.gemms += (d - 1) + 1 + 1;
