@@ -81,7 +81,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(G, L0, R0, beta, eps):
+def cpu_baseline(G, L0, R0, beta, eps, updates=0):
     """The fp64 oracle (closed forms: eigendecomposition roots) for one full
     step at the full size, timed on the host cores."""
     from oracle import closed_form as cf
@@ -99,11 +99,30 @@ def cpu_baseline(G, L0, R0, beta, eps):
     t3 = time.perf_counter()
     cf.precond_apply(Linv, G, Rinv)
     t4 = time.perf_counter()
-    return dict(value=round((t3 - t2) * 1e3, 1), unit="ms per inverse-4th-root (n=4096)",
-                cores=int(threads), kind="oracle",
-                sample="one full step at full size (fp64 stats update, eigh-based L^-1/4 and "
-                       "R^-1/4, apply) = %.1f s; value is the R^-1/4 part" % (t4 - t0),
-                step_s=round(t4 - t0, 2))
+    out = dict(value=round((t3 - t2) * 1e3, 1), unit="ms per inverse-4th-root (n=4096)",
+               cores=int(threads), kind="oracle",
+               sample="one full step at full size (fp64 stats update, eigh-based L^-1/4 and "
+                      "R^-1/4, apply) = %.1f s; value is the R^-1/4 part" % (t4 - t0),
+               step_s=round(t4 - t0, 2))
+    if updates:
+        # like for like: the oracle's PRISM iteration itself (fp64, the same
+        # sketch generator) on the same R, two updates of the first coupled
+        # square-root stage from Y_0 = R / ||R||_F, per update times the
+        # updates the device call ran
+        from oracle import prism
+        Y0 = R / np.linalg.norm(R)
+        t5 = time.perf_counter()
+        _, _, tr = prism.coupled_sqrt_stage(Y0, d=2, tol=0.0, max_iter=2,
+                                            sketch_fn=prism.make_sketch_fn(0))
+        t6 = time.perf_counter()
+        per = (t6 - t5) / max(tr.iters, 1)
+        out["prism_like_for_like"] = dict(
+            value=round(per * updates * 1e3, 1), unit="ms per inverse-4th-root (n=4096)",
+            kind="oracle (PRISM iteration, fp64)", cores=int(threads),
+            sample="%d updates of the first stage timed (%.1f s, %d products), scaled by the "
+                   "%d updates of the device call" % (tr.iters, t6 - t5, tr.gemms, updates),
+            ms_per_update=round(per * 1e3, 1))
+    return out
 
 
 def root_exec_flops(n, batch, iters, gemms, method=0):
@@ -151,8 +170,7 @@ def other_workload(args):
 def measure(wl, args, inputs=None):
     """One secondary workload's measurement as a dict (the JSON line of
     `--workload wl`).  `inputs` may hold the workload's host arrays, made
-    beforehand (the default run builds the Muon matrices on a host thread
-    while the GPU measures the others)."""
+    beforehand."""
     import copy
 
     import torch
@@ -572,14 +590,6 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    # the Muon workload's host arrays (QR of 64 Gaussians, ~20 s of LAPACK)
-    # are built on a host thread while the GPU measures the rest
-    muon = {}
-    th = None
-    if not args.no_secondary:
-        import threading
-        th = threading.Thread(target=lambda: muon.update(W.muon_32x4096x1024()), daemon=True)
-        th.start()
     pmx.set_host_poll(args.host_poll)
     cfg = W.shampoo_1024x4096()
     m, n = cfg["Gs"][0].shape
@@ -774,19 +784,20 @@ def main():
         }
         for wl in ("spd_64", "blocks_64x512", "mp_10000", "muon_32x4096x1024"):
             t0 = time.perf_counter()
-            if wl == "muon_32x4096x1024":
-                th.join()
-            r = measure(wl, args, inputs=muon if wl == "muon_32x4096x1024" else None)
+            # (the Muon inputs, QR of 64 Gaussians, are built here with the
+            # GPU idle: built on a host thread during the other measurements
+            # they took the host-polled headline from 28.3 to 28-36 ms a step)
+            r = measure(wl, args)
             secondary[wl] = dict(keep[wl](r), metric=r["metric"], unit=r["unit"],
                                  dtype=r["dtype"], host_poll=r["config"]["host_poll"],
                                  scale=r["config"]["scale"])
             log("%s (%.1f s): %s" % (wl, time.perf_counter() - t0, json.dumps(secondary[wl])))
             torch.cuda.empty_cache()
-        muon.clear()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg["Gs"][-1], L9.cpu().numpy(), R9.cpu().numpy(), beta, eps)
+        cpu = cpu_baseline(cfg["Gs"][-1], L9.cpu().numpy(), R9.cpu().numpy(), beta, eps,
+                           updates=sum(int(x) for x in iR["iters"]))
         log("cpu baseline:", cpu)
 
     out = {

@@ -106,6 +106,31 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Sums of CNT doubles per lane over a 64-lane wave by recursive halving (CNT
+// a power of two <= 64): at offset O the lanes with bit O set keep the upper
+// half of their values and add the partner's copy of it, so CNT - 1 + log
+// exchanges replace CNT full reductions; lane l ends with the wave's sum of
+// value l / (64 / CNT) in acc[0].
+template <int CNT, int O>
+__device__ __forceinline__ void halve_reduce_d(double* acc, int lane) {
+  if constexpr (O >= 1) {
+    if constexpr (CNT > 1) {
+      constexpr int H = CNT / 2;
+      const bool upper = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const double send = upper ? acc[i] : acc[i + H];
+        const double keep = upper ? acc[i + H] : acc[i];
+        acc[i] = keep + __shfl_xor(send, O, 64);
+      }
+      halve_reduce_d<H, O / 2>(acc, lane);
+    } else {
+      acc[0] += __shfl_xor(acc[0], O, 64);
+      halve_reduce_d<1, O / 2>(acc, lane);
+    }
+  }
+}
+
 // Sum over a block of `nwaves` waves; result valid in every thread.
 template <int NWAVES>
 __device__ __forceinline__ double block_sum(double v, double* lds) {

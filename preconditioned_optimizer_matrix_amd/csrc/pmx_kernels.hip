@@ -518,26 +518,6 @@ constexpr int SB_LD = SB_CH + 4;
 constexpr int SB_W = 8;
 constexpr int SB_UN = 4;
 
-template <int CNT, int O>
-__device__ __forceinline__ void halve_reduce_d(double* acc, int lane) {
-  if constexpr (O >= 1) {
-    if constexpr (CNT > 1) {
-      constexpr int H = CNT / 2;
-      const bool upper = (lane & O) != 0;
-#pragma unroll
-      for (int i = 0; i < H; ++i) {
-        const double send = upper ? acc[i] : acc[i + H];
-        const double keep = upper ? acc[i + H] : acc[i];
-        acc[i] = keep + __shfl_xor(send, O, 64);
-      }
-      halve_reduce_d<H, O / 2>(acc, lane);
-    } else {
-      acc[0] += __shfl_xor(acc[0], O, 64);
-      halve_reduce_d<1, O / 2>(acc, lane);
-    }
-  }
-}
-
 template <int Q, int GJ>
 __global__ __launch_bounds__(SB_W * 64) void skinny_batch_kernel(SkinnyParams p) {
   static_assert(Q == 8 || Q == 16, "Q");

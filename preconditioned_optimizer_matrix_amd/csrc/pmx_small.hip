@@ -59,30 +59,54 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // A values of one row are contiguous (16-byte reads when A is not
 // transposed).  RESID: C = I_n - acc and the fp64 sum of squares is returned
 // (block total); otherwise 0.
-template <bool TA, bool RESID>
+// The update polynomial g = c0 I_n + c1 R + alpha R2 (d = 2) or c0 I_n +
+// alpha R (d = 1), formed element by element where a product reads it.
+struct SmallPoly {
+  const float* r;
+  const float* r2;
+  float c0, c1, alpha;
+  int d, n;
+  __device__ __forceinline__ float at(float rv, float r2v, bool diag) const {
+    float v = (d == 2) ? c1 * rv + alpha * r2v : alpha * rv;
+    if (diag) v += c0;
+    return v;
+  }
+};
+
+template <bool TA, bool RESID, int POLY = 0>
 __device__ double small_gemm(float* C, const float* A, const float* B, int n_id,
-                             SmallShared& sh) {
+                             SmallShared& sh, const SmallPoly* pg = nullptr) {
+  // POLY = 2: B is g, formed from pg while loading
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
   const int li = lane & 31, kh = (lane >> 5) * 32;
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  const float* bcol = B + kh * SLD + wn + li;
+  const float* bcol = (POLY == 2 ? pg->r : B) + kh * SLD + wn + li;
+  const float* bcol2 = POLY == 2 ? pg->r2 + kh * SLD + wn + li : nullptr;
+  auto bval = [&](int m) {
+    if constexpr (POLY == 2) {
+      const int k = kh + m;
+      return pg->at(bcol[m * SLD], bcol2[m * SLD], k == wn + li && k < pg->n);
+    } else {
+      return bcol[m * SLD];
+    }
+  };
   if (TA) {
     const float* acol = A + kh * SLD + wm + li;
 #pragma unroll
     for (int m = 0; m < 32; ++m)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(acol[m * SLD], bcol[m * SLD], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(acol[m * SLD], bval(m), acc, 0, 0, 0);
   } else {
     const float* arow = A + (wm + li) * SLD + kh;
 #pragma unroll
     for (int m4 = 0; m4 < 8; ++m4) {
       const float4 a = *reinterpret_cast<const float4*>(arow + 4 * m4);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bcol[(4 * m4 + 0) * SLD], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bcol[(4 * m4 + 1) * SLD], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bcol[(4 * m4 + 2) * SLD], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bcol[(4 * m4 + 3) * SLD], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bval(4 * m4 + 0), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bval(4 * m4 + 1), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bval(4 * m4 + 2), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bval(4 * m4 + 3), acc, 0, 0, 0);
     }
   }
   // lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + (v % 4)
@@ -134,8 +158,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // would wait on LDS once per pair).  A block column at or beyond q reads
 // column q - 1 (in bounds); a product's column j depends on B's column j
 // alone, so those columns are only left unstored.
-__device__ __forceinline__ void krylov_tile(float* kb, const float* mat, int ic, int oc, int q,
-                                            float scale, int rt, int ct) {
+__device__ __forceinline__ f32x4 krylov_tile(float* kb, const float* mat, int ic, int oc, int q,
+                                             float scale, int rt, int ct) {
   const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
   const int col = 16 * ct + li;
   const bool live = col < q;
@@ -157,10 +181,13 @@ __device__ __forceinline__ void krylov_tile(float* kb, const float* mat, int ic,
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m4].w, bv[4 * m4 + 3], acc, 0, 0, 0);
   }
   // lane l holds block column l % 16 of rows 4 (l / 16) + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] *= scale;
   if (live) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kb[(16 * rt + 4 * g + r) * SKLD + oc + col] = acc[r] * scale;
+    for (int r = 0; r < 4; ++r) kb[(16 * rt + 4 * g + r) * SKLD + oc + col] = acc[r];
   }
+  return acc;
 }
 
 struct KrylovJob {
@@ -169,17 +196,67 @@ struct KrylovJob {
   float scale;
 };
 
+// Two independent tiles (rows 16 rt of job a and of job b, block columns
+// 0..15 of each) with their 40 operand reads issued first and the two chains
+// of 16 products interleaved.
+__device__ __forceinline__ void krylov_tiles2(float* kb, const KrylovJob& ja,
+                                              const KrylovJob& jb, int rt) {
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+  const bool la = li < ja.q, lb = li < jb.q;
+  const float* arow_a = ja.mat + (16 * rt + li) * SLD + 16 * g;
+  const float* arow_b = jb.mat + (16 * rt + li) * SLD + 16 * g;
+  const float* bcol_a = kb + (16 * g) * SKLD + ja.ic + (la ? li : ja.q - 1);
+  const float* bcol_b = kb + (16 * g) * SKLD + jb.ic + (lb ? li : jb.q - 1);
+  float4 a0[4], a1[4];
+  float b0[16], b1[16];
+#pragma unroll
+  for (int m4 = 0; m4 < 4; ++m4) {
+    a0[m4] = *reinterpret_cast<const float4*>(arow_a + 4 * m4);
+    a1[m4] = *reinterpret_cast<const float4*>(arow_b + 4 * m4);
+  }
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    b0[m] = bcol_a[m * SKLD];
+    b1[m] = bcol_b[m * SKLD];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m4 = 0; m4 < 4; ++m4) {
+    c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[m4].x, b0[4 * m4 + 0], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[m4].x, b1[4 * m4 + 0], c1, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[m4].y, b0[4 * m4 + 1], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[m4].y, b1[4 * m4 + 1], c1, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[m4].z, b0[4 * m4 + 2], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[m4].z, b1[4 * m4 + 2], c1, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[m4].w, b0[4 * m4 + 3], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[m4].w, b1[4 * m4 + 3], c1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (la) kb[(16 * rt + 4 * g + r) * SKLD + ja.oc + li] = c0[r] * ja.scale;
+    if (lb) kb[(16 * rt + 4 * g + r) * SKLD + jb.oc + li] = c1[r] * jb.scale;
+  }
+}
+
 // One step of the Krylov recursion: the tiles of up to two independent
-// products, tile t on wave t % 4, then a barrier.
+// products, tile t on wave t % 4, then a barrier.  With q <= 16 (p <= 8, or
+// p <= 16 outside the double-width step) every wave owns row band w of each
+// job: one tile, or two interleaved.
 __device__ void krylov_step(SmallShared& sh, KrylovJob j0, KrylovJob j1, int jobs) {
   const int w = threadIdx.x >> 6;
-  int t = 0;
-  for (int jb = 0; jb < jobs; ++jb) {
-    const KrylovJob& j = jb ? j1 : j0;
-    const int cts = (j.q + 15) >> 4;
-    for (int ct = 0; ct < cts; ++ct)
-      for (int rt = 0; rt < 4; ++rt, ++t)
-        if ((t & 3) == w) krylov_tile(sh.kb, j.mat, j.ic, j.oc, j.q, j.scale, rt, ct);
+  if (j0.q <= 16 && (jobs == 1 || j1.q <= 16)) {
+    if (jobs == 2) krylov_tiles2(sh.kb, j0, j1, w);
+    else krylov_tile(sh.kb, j0.mat, j0.ic, j0.oc, j0.q, j0.scale, w, 0);
+  } else {
+    int t = 0;
+    for (int jb = 0; jb < jobs; ++jb) {
+      const KrylovJob& j = jb ? j1 : j0;
+      const int cts = (j.q + 15) >> 4;
+      for (int ct = 0; ct < cts; ++ct)
+        for (int rt = 0; rt < 4; ++rt, ++t)
+          if ((t & 3) == w) krylov_tile(sh.kb, j.mat, j.ic, j.oc, j.q, j.scale, rt, ct);
+    }
   }
   __syncthreads();
 }
@@ -189,6 +266,30 @@ struct NextSketch {
   int on, k, stage, b;
 };
 
+// The products of one lane's four Krylov rows (rows 16 w + 4 g4 + r,
+// column li < p) for the packed upper triangle of the J x J Gram: K_J from
+// the lane's registers, K_1 .. K_{J-1} from LDS.
+template <int J>
+__device__ __forceinline__ void gram_rows(double (&gs)[16], const float* kb, const f32x4& kj,
+                                          int w, int g4, int li, int p) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) gs[e] = 0.0;
+  if (li >= p) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float* row = kb + (16 * w + 4 * g4 + r) * SKLD + li;
+    double x[J];
+#pragma unroll
+    for (int j = 0; j + 1 < J; ++j) x[j] = (double)row[(j + 1) * p];
+    x[J - 1] = (double)kj[r];
+    int t = 0;
+#pragma unroll
+    for (int a = 0; a < J; ++a)
+#pragma unroll
+      for (int b = a; b < J; ++b, ++t) gs[t] += x[a] * x[b];
+  }
+}
+
 // Krylov blocks of R (and R2), their Gram and alpha (d = 1 or 2), in the
 // order and scaling of the multi-kernel path; alpha lands in sh.c.alpha.
 __device__ void small_alpha(SmallShared& sh, const float* R, const float* R2, int n,
@@ -196,62 +297,86 @@ __device__ void small_alpha(SmallShared& sh, const float* R, const float* R2, in
   const int p = cfg.p, d = cfg.degree;
   const double fro = sh.c.fro;
   const float s1 = (float)(1.0 / fro), s2 = (float)(1.0 / (fro * fro));
+  const int J = 2 * d + 1, NE = J * (J + 1) / 2;
+  // the last Krylov block K_J: wave w's tile (rows 16 w .., q = p <= 16)
+  KrylovJob last;
   if (d == 2) {
     // K1 = R S / s and K2 = R^2 S / s^2; [K3 | K4] = R^2 [K1 | K2] / s^2;
     // K5 = R^2 K3 / s^2
     krylov_step(sh, {R, 0, p, p, s1}, {R2, 0, 2 * p, p, s2}, 2);
     krylov_step(sh, {R2, p, 3 * p, 2 * p, s2}, {}, 1);
-    krylov_step(sh, {R2, 3 * p, 5 * p, p, s2}, {}, 1);
+    last = {R2, 3 * p, 5 * p, p, s2};
   } else {
-    for (int j = 1; j <= 3; ++j) krylov_step(sh, {R, (j - 1) * p, j * p, p, s1}, {}, 1);
+    for (int j = 1; j <= 2; ++j) krylov_step(sh, {R, (j - 1) * p, j * p, p, s1}, {}, 1);
+    last = {R, 2 * p, 3 * p, p, s1};
   }
-  // Gram, packed upper triangle of the J x J: entry e = t / 16 is summed in
-  // fp64 by threads 16 e .. 16 e + 15, thread t over rows t % 16 + 16 r
-  // (r < 4: rows beyond n are zero) and columns in chunks of four (the 32
-  // reads of a chunk in flight together; columns at or beyond p read column
-  // p - 1 and count zero); the 16 partial sums are added in lane order.
-  const int J = 2 * d + 1, NE = J * (J + 1) / 2;
-  {
-    const int e = threadIdx.x >> 4, sl = threadIdx.x & 15;
-    double part = 0.0;
-    if (e < NE) {
-      int a = 0, rem = e;
-      while (rem >= J - a) {
-        rem -= J - a;
-        ++a;
-      }
-      const float* ka = sh.kb + (a + 1) * p + sl * SKLD;
-      const float* kc = sh.kb + (a + rem + 1) * p + sl * SKLD;
-      double acc4[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int c0 = 0; c0 < p; c0 += 4) {
-        float va[4][4], vc[4][4];
+  if (p <= 16) {
+    // The last block and the Gram in one step: each wave adds the products
+    // of its own 16 rows (K_J from its registers, the others from LDS) into
+    // 16 fp64 sums, halves them over the wave and leaves one row of wave
+    // shares; entry e is then the shares of waves 0..3 added in order.
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, g4 = lane >> 4;
+    const f32x4 kj = krylov_tile(sh.kb, last.mat, last.ic, last.oc, last.q, last.scale, w, 0);
+    double gs[16];
+    if (J == 5) gram_rows<5>(gs, sh.kb, kj, w, g4, li, p);
+    else gram_rows<3>(gs, sh.kb, kj, w, g4, li, p);
+    halve_reduce_d<16, 32>(gs, lane);
+    if ((lane & 3) == 0) sh.red[w][lane >> 2] = gs[0];
+    __syncthreads();
+    if (threadIdx.x < NE)
+      sh.gsum[threadIdx.x] = ((sh.red[0][threadIdx.x] + sh.red[1][threadIdx.x]) +
+                              sh.red[2][threadIdx.x]) + sh.red[3][threadIdx.x];
+    __syncthreads();
+  } else {
+    krylov_step(sh, last, {}, 1);
+    // Gram, packed upper triangle of the J x J: entry e = t / 16 is summed
+    // in fp64 by threads 16 e .. 16 e + 15, thread t over rows t % 16 + 16 r
+    // (r < 4: rows beyond n are zero) and columns in chunks of four (the 32
+    // reads of a chunk in flight together; columns at or beyond p read
+    // column p - 1 and count zero); the 16 partial sums are added in lane
+    // order.
+    {
+      const int e = threadIdx.x >> 4, sl = threadIdx.x & 15;
+      double part = 0.0;
+      if (e < NE) {
+        int a = 0, rem = e;
+        while (rem >= J - a) {
+          rem -= J - a;
+          ++a;
+        }
+        const float* ka = sh.kb + (a + 1) * p + sl * SKLD;
+        const float* kc = sh.kb + (a + rem + 1) * p + sl * SKLD;
+        double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int c0 = 0; c0 < p; c0 += 4) {
+          float va[4][4], vc[4][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int c = min(c0 + v, p - 1);
+              va[r][v] = ka[16 * r * SKLD + c];
+              vc[r][v] = kc[16 * r * SKLD + c];
+            }
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int c = min(c0 + v, p - 1);
-            va[r][v] = ka[16 * r * SKLD + c];
-            vc[r][v] = kc[16 * r * SKLD + c];
+            if (c0 + v >= p) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc4[r] += (double)va[r][v] * (double)vc[r][v];
           }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (c0 + v >= p) break;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc4[r] += (double)va[r][v] * (double)vc[r][v];
         }
+        part = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
       }
-      part = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+      sh.gpart[threadIdx.x] = part;
     }
-    sh.gpart[threadIdx.x] = part;
-  }
-  __syncthreads();
-  if (threadIdx.x < NE) {
-    double v = 0.0;
+    __syncthreads();
+    if (threadIdx.x < NE) {
+      double v = 0.0;
 #pragma unroll
-    for (int sl = 0; sl < 16; ++sl) v += sh.gpart[threadIdx.x * 16 + sl];
-    sh.gsum[threadIdx.x] = v;
+      for (int sl = 0; sl < 16; ++sl) v += sh.gpart[threadIdx.x * 16 + sl];
+      sh.gsum[threadIdx.x] = v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (threadIdx.x == 0) {
     // d <= 2 here: J = 3 or 5 (no code for the degree-3 solve)
     const double alpha = J == 3 ? alpha_from_gram_t<3>(sh.gsum, fro, coef, cfg.lo, cfg.hi, nullptr)
@@ -412,6 +537,9 @@ __global__ __launch_bounds__(SNT, 1) void small_root_kernel(SmallRootParams p) {
       const int k = sh.c.iter;
       if (d == 2) small_gemm<false, false>(R2, R, R, n, sh);
       if (accel) small_alpha(sh, R, R2, n, cfg, p.coef, {k + 1 < cfg.max_iter, k + 1, stage, b});
+      // g in place of R2 (forming it while loading the two update products'
+      // operands measured slower here: 2.1k cycles of this pass against 3.5k
+      // more in the products; the polar kernel, with one product, forms it)
       small_poly(R2, R, n, d, p.c0, p.c1, (float)sh.c.alpha);
       small_gemm<false, false>(Yn, Y, R2, n, sh);  // Y g
       if (k == 0) {
@@ -525,8 +653,8 @@ __global__ __launch_bounds__(SNT, 1) void small_polar_kernel(SmallPolarParams p)
       const int k = sh.c.iter;
       if (d == 2) small_gemm<false, false>(R2, R, R, cols, sh);
       if (accel) small_alpha(sh, R, R2, cols, cfg, p.coef, {k + 1 < cfg.max_iter, k + 1, 0, b});
-      small_poly(R2, R, cols, d, p.c0, p.c1, (float)sh.c.alpha);
-      small_gemm<false, false>(Xn, X, R2, cols, sh);  // X g
+      const SmallPoly pg{R, R2, p.c0, p.c1, (float)sh.c.alpha, d, cols};
+      small_gemm<false, false, 2>(Xn, X, nullptr, cols, sh, &pg);  // X g, g formed on load
       float* t = X;
       X = Xn;
       Xn = t;
