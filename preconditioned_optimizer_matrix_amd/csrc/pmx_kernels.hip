@@ -346,8 +346,25 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
     }
     // entries of (a, bb) with a <= bb < J, in row order, are packed first
     __shared__ double wsum[NW][NE];
-    __shared__ double gsum[NE];
-    {
+    if constexpr (NE <= 16) {
+      // recursive halving over the wave (17 exchanges for 15 sums): lane l
+      // ends with the sum of entry l / 4, which lands at its packed index
+      // a J - a (a - 1) / 2 + bb - a when a, bb < J
+      double h[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) h[e] = e < NE ? g[e] : 0.0;
+      halve_reduce_d<16, 32>(h, lane);
+      const int t = lane >> 2;
+      if ((lane & 3) == 0 && t < NE) {
+        int a = 0, rem = t;
+        while (rem >= GA - a) {
+          rem -= GA - a;
+          ++a;
+        }
+        const int bb = a + rem;
+        if (a < J && bb < J) wsum[wid][a * J - a * (a - 1) / 2 + (bb - a)] = h[0];
+      }
+    } else {
       int t = 0, o = 0;
 #pragma unroll
       for (int a = 0; a < GA; ++a)
