@@ -24,6 +24,7 @@ struct pmx_context {
   int bf16_map;            // bf16 GEMM: 1 deals whole matrices to XCDs, 0 plain order
   int skinny_variant;      // skinny products: 0 In through LDS, 1 In read directly
   int bf16_dma;            // bf16 GEMM: 1 uses direct global-to-LDS loads for whole tiles (measured slower; off)
+  int bf16_mn;             // bf16 polar: 1 reads X for I - X^T X via LDS transpose reads (no X^T copy)
   int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
   int split_k;             // 1: split-k tail for the fp32 products of the iterations
   int bf16_sym;            // 1: bf16 X^T X and R^2 run upper-triangle tiles, mirrored
@@ -996,6 +997,8 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_SKINNY")) c->skinny_variant = atoi(e);
   c->bf16_dma = 0;
   if (const char* e = getenv("PMX_BF16_DMA")) c->bf16_dma = atoi(e);
+  c->bf16_mn = 1;
+  if (const char* e = getenv("PMX_BF16_MN")) c->bf16_mn = atoi(e);
   c->small_fused = 1;
   if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
   c->split_k = 1;
@@ -1774,11 +1777,24 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
     float* Rh = at<float>(ws, Lw.bufs[6]);  // R in bf16
     float* Gh = at<float>(ws, Lw.bufs[7]);  // g in bf16
     const bool vec = (cols % 8 == 0) && (rows % 8 == 0) && (bs % 8 == 0);
-    auto residual = [&](float* Xtc, int products, int count) {
+    // Where the residual's tiles are whole 256 x 256 x 64 ones (and the
+    // large tile is the launcher's choice), I - X^T X reads the row-major
+    // iterate itself through the LDS transpose reads, and no transposed copy
+    // of X is written (by the update or the set-up).
+    const bool mn = !tr && q.h->bf16_mn && vec && cols % 256 == 0 && rows % 64 == 0 &&
+                    (int64_t)(cols / 256) * (cols / 256) * batch >= q.h->num_cu &&
+                    q.h->bf16_cfg < 0 && !q.h->bf16_sym;
+    auto residual = [&](int it, int products, int count) {
       GemmParams r = bf16_base(q.h, cols, cols, rows, batch);
       r.ctrl = ctrl;
-      r.prob[0].a = {Xtc, rows, bs, nullptr, 0};
-      r.prob[0].b = {Xtc, rows, bs, nullptr, 0};
+      if (mn) {
+        r.prob[0].a = {Xb[it], cols, bs, nullptr, 0};
+        r.prob[0].b = {Xb[it], cols, bs, nullptr, 0};
+        r.mn = 1;
+      } else {
+        r.prob[0].a = {Xt[it], rows, bs, nullptr, 0};
+        r.prob[0].b = {Xt[it], rows, bs, nullptr, 0};
+      }
       r.prob[0].c = Rb;
       r.prob[0].ldc = cols;
       r.prob[0].stride_c = bs;
@@ -1810,13 +1826,13 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       x.out_n = (uint16_t*)(tr ? Xt[0] : Xb[0]);
       x.ldn = n;
       x.sn = bs;
-      x.out_t = (uint16_t*)(tr ? Xb[0] : Xt[0]);
+      x.out_t = mn ? nullptr : (uint16_t*)(tr ? Xb[0] : Xt[0]);
       x.ldt = m;
       x.st = bs;
       x.sketch = make_sketch(Lw, ws, cfg, cols, 0, 0, acc);
       PMX_TRY(q.run(PMX_KC_OTHER, [&] { return launch_xpose(x, batch, q.s); }));
     }
-    PMX_TRY(residual(Xt[0], 1, 0));
+    PMX_TRY(residual(0, 1, 0));
     Poller poll(q, ctrl, batch);
     for (int k = 0; k < o.max_iter; ++k) {
       bool stop = false;
@@ -1859,12 +1875,12 @@ pmx_status pmx_matfn_polar_batched(pmx_handle h, const void* G, pmx_dtype dtype,
       u.prob[0].c = Xb[nxt];
       u.prob[0].ldc = cols;
       u.prob[0].stride_c = bs;
-      u.prob[1].c = Xt[nxt];  // transposed copy of the new iterate
+      u.prob[1].c = mn ? nullptr : Xt[nxt];  // transposed copy of the new iterate
       u.prob[1].ldc = rows;
       u.prob[1].stride_c = bs;
       u.vec = vec ? 1 : 0;
       PMX_TRY(q.run(PMX_KC_GEMM_UPDATE, [&] { return launch_gemm_bf16(u, ROLE_UPDATE, q.s); }));
-      PMX_TRY(residual(Xt[nxt], (d - 1) + 1 + 1, 1));
+      PMX_TRY(residual(nxt, (d - 1) + 1 + 1, 1));
     }
   }
   PolarFinishParams fp;

@@ -224,6 +224,111 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[C::FM][C::FN],
   }
 }
 
+// The same main loop for operands stored m- (n-) contiguous: A is K x M
+// (A^T of the C = A Bs^T form, row k holding M values), Bs likewise K x N,
+// e.g. C = X^T X straight from the row-major iterate X, with no transposed
+// copy.  A k tile is staged untransposed, T[k][i] with row pitch BM + 32
+// (576 bytes for 256: 144 dwords = 16 mod 64, so the four rows of a
+// transpose read fall on distinct banks), with 16-byte loads and stores.
+// The fragments come from gfx950's LDS transpose read ds_read_b64_tr_b16:
+// in each group of 16 lanes, lane j receives element j % 4 of the 8 bytes
+// read by lanes 4 t + j / 4 (t = 0 .. 3), so a lane that addresses row
+// k0 + j / 4, column i0 + 4 (j % 4) gets column i0 + j of rows k0 .. k0 + 3.
+// Lane l (group g = l / 16) addresses k0 = 8 (g / 2) (+ 4 for the second
+// read) and i0 = 16 (g % 2), which gives it row l % 32 and k = 8 (l / 32)
+// .. + 7 of the 32 x 16 MFMA operand: two 8-byte reads per fragment where
+// the k-contiguous form reads 16 bytes once.  Only whole 256 x 256 x 64
+// tiles (the launcher checks).
+typedef short i16x4_tr __attribute__((ext_vector_type(4)));
+typedef short i16x8_tr __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* p, int pitch) {
+  const i16x4_tr lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_tr*)(p));
+  const i16x4_tr hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_tr*)(p + 4 * pitch));
+  const i16x8_tr w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+template <class C>
+__device__ __forceinline__ void mainloop_fast_mn(f32x16 (&acc)[C::FM][C::FN],
+                                                 uint16_t (*smem)[C::LDS], const uint16_t* A,
+                                                 int64_t lda, const uint16_t* B, int64_t ldb,
+                                                 int m0, int n0, int nk, int lane, int wm,
+                                                 int wn) {
+  constexpr int NT = C::NT, FM = C::FM, FN = C::FN, BK = C::BK, STEPS = BK / 16;
+  constexpr int PA = C::BM + 32, PB = C::BN + 32;
+  static_assert(BK * (PA + PB) <= C::LDS, "an m-contiguous k tile fits an LDS stage");
+  constexpr int CPA = C::BM / 8, CPB = C::BN / 8;  // 16-byte chunks per k row
+  constexpr int CA = BK * CPA / NT, CB = BK * CPB / NT;
+  static_assert(CA * NT == BK * CPA && CB * NT == BK * CPB, "chunks per thread");
+  constexpr int RSA = NT / CPA, RSB = NT / CPB;  // k rows per chunk index step
+  constexpr int NF = 2 * (FM + FN);              // transpose reads per step
+  constexpr int MF = FM * FN;                    // MFMAs per step
+  const int t = threadIdx.x;
+  const uint16_t* ga = A + (int64_t)(t / CPA) * lda + m0 + (t % CPA) * 8;
+  const uint16_t* gb = B + (int64_t)(t / CPB) * ldb + n0 + (t % CPB) * 8;
+  const int64_t sta = (int64_t)RSA * lda, stb = (int64_t)RSB * ldb;
+  const int wa = (t / CPA) * PA + (t % CPA) * 8;
+  const int wb = BK * PA + (t / CPB) * PB + (t % CPB) * 8;
+  u32x4 va[CA], vb[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + i * sta);
+#pragma unroll
+  for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + i * stb);
+#pragma unroll
+  for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(smem[0] + wa + i * RSA * PA) = va[i];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(smem[0] + wb + i * RSB * PB) = vb[i];
+  __syncthreads();
+  const int g = lane >> 4, j = lane & 15;
+  const int ra = (8 * (g >> 1) + (j >> 2)) * PA + 16 * (g & 1) + 4 * (j & 3) + wm;
+  const int rb = BK * PA + (8 * (g >> 1) + (j >> 2)) * PB + 16 * (g & 1) + 4 * (j & 3) + wn;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t* sa = smem[kt & 1] + ra;
+    const uint16_t* sb = smem[kt & 1] + rb;
+    uint16_t* dst = smem[(kt & 1) ^ 1];
+    const int64_t kn = (int64_t)(kt + 1 < nk ? kt + 1 : kt) * BK;  // the last tile reloads itself
+    bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = frag_tr(sa + 32 * i, PA);
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) fb[0][jj] = frag_tr(sb + 32 * jj, PB);
+#pragma unroll
+    for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + kn * lda + i * sta);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + kn * ldb + i * stb);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int c = st & 1, n = c ^ 1;
+      if (st + 1 < STEPS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[n][i] = frag_tr(sa + 32 * i + 16 * (st + 1) * PA, PA);
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) fb[n][jj] = frag_tr(sb + 32 * jj + 16 * (st + 1) * PB, PB);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+          acc[i][jj] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][jj], acc[i][jj], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(dst + wa + i * RSA * PA) = va[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(dst + wb + i * RSB * PB) = vb[i];
+    // schedule of the k tile (as in mainloop_fast)
+    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, CA + CB, 0);
+#pragma unroll
+    for (int st = 0; st + 1 < STEPS; ++st) sched_interleave<MF, NF, 0x100, (NF + MF - 1) / MF>();
+    sched_interleave<MF, CA + CB, 0x200, (CA + CB + MF - 1) / MF>();
+    __syncthreads();
+  }
+}
+
 // Epilogue of one tile by role (same accumulator layout as the 32x32 fp32
 // MFMA: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + (v % 4)).
 // ROLE_UPDATE's transposed copy goes through LDS when the whole tile is
@@ -254,7 +359,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
   bool t_lds = false;
   if constexpr (BF16_OUT && kTransposeInLds<C>) {
     const GemmProblem& tp = p.prob[1];
-    t_lds = lds && p.vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && tp.ldc % 8 == 0 &&
+    t_lds = lds && tp.c && p.vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && tp.ldc % 8 == 0 &&
             tp.stride_c % 8 == 0 && ((uintptr_t)tp.c & 15) == 0;
   }
   float fro = 0.f;
@@ -314,7 +419,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
           // Ts[col - n0][row_base - m0 .. + 3]
           *reinterpret_cast<u32x2*>(lds + (col - n0) * PT + (row_base - m0)) = {
               h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        } else if (BF16_OUT && col < p.N) {
+        } else if (BF16_OUT && col < p.N && p.prob[1].c) {
           // transposed copy: X'^T[col][row_base .. row_base + 3]
           const GemmProblem& tp = p.prob[1];
           uint16_t* T = reinterpret_cast<uint16_t*>(tp.c) + (int64_t)b * tp.stride_c +
@@ -355,7 +460,7 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
 // ROLE_RESID: C fp32 = I - acc with the Frobenius share for the decision,
 // and a bf16 copy at prob[1].c when set; ROLE_POWER: C fp32 = acc;
 // ROLE_UPDATE: C bf16 = acc and its transpose at prob[1].c.
-template <class C, int ROLE>
+template <class C, int ROLE, bool MN = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p) {
   constexpr int FM = C::FM, FN = C::FN;
   constexpr int WGN = C::BN / C::WN;
@@ -397,7 +502,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
 
     const int nk = (p.K + C::BK - 1) / C::BK;
     __syncthreads();
-    if (vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && p.K % C::BK == 0) {
+    if constexpr (MN) {
+      // operands m- / n-contiguous (whole tiles only: the launcher checks)
+      mainloop_fast_mn<C>(acc, smem, A, pr.a.ld, B, pr.b.ld, m0, n0, nk, lane, wm, wn);
+    } else if (vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && p.K % C::BK == 0) {
       mainloop_fast<C>(acc, smem, A, pr.a.ld, B, pr.b.ld, m0, n0, nk, lane, wm, wn);
     } else {
     u32x4 va[C::CA], vb[C::CB];
@@ -629,6 +737,24 @@ template <class C>
 hipError_t launch_cfg(GemmParams p, int role, hipStream_t s) {
   p.tiles_m = (p.M + C::BM - 1) / C::BM;
   p.tiles_n = (p.N + C::BN - 1) / C::BN;
+  if (p.mn) {
+    // m- / n-contiguous operands: the residual on whole 256 x 256 x 64 tiles
+    if constexpr (C::BM == 256 && C::BN == 256 && C::BK == 64 && C::WM == 128 && C::WN == 64) {
+      if (role != ROLE_RESID || p.sym || !p.vec || p.M % 256 || p.N % 256 || p.K % 64 ||
+          p.K < 64 || p.prob[0].a.ld % 8 || p.prob[0].b.ld % 8 || p.prob[0].a.stride % 8 ||
+          p.prob[0].b.stride % 8 || ((uintptr_t)p.prob[0].a.ptr & 15) ||
+          ((uintptr_t)p.prob[0].b.ptr & 15))
+        return hipErrorInvalidValue;
+      const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
+      int64_t g = total;
+      if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
+      hipLaunchKernelGGL((gemm_bf16_kernel<C, ROLE_RESID, true>), dim3((unsigned)g),
+                         dim3(C::NT), 0, s, p);
+      return after_resid(p, role, (int)(total / p.batch), s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (p.sym && (C::BM != C::BN || p.M != p.N || role == ROLE_UPDATE)) return hipErrorInvalidValue;
   const int64_t total = (p.sym ? (int64_t)p.tiles_m * (p.tiles_m + 1) / 2
                                : (int64_t)p.tiles_m * p.tiles_n) * p.batch;
@@ -655,6 +781,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int role, hipStream_t s) {
   const int64_t large = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
   int cfg = p.cfg_id;
   if (cfg < 0 || cfg > 3) cfg = (p.M >= 256 && p.N >= 256 && large >= p.num_cu) ? 1 : 0;
+  if (p.mn) return launch_cfg<BLarge>(p, role, s);
   if (p.sym) {
     // square tiles (the 256 x 256 tile, or 128 x 128 when forced with 0)
     if (cfg == 2 || cfg == 3) cfg = 1;

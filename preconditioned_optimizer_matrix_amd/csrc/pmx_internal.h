@@ -296,6 +296,7 @@ struct GemmParams {
   int map_mode;    // tile order: 0 grouped, 1 grouped + XCD rounds, 2 row-major
   int dma;         // bf16: whole-tile variant with direct global-to-LDS loads
   int sym;         // output symmetric, upper-triangle tiles mirrored (M == N)
+  int mn;          // bf16 residual: A and Bs given m- / n-contiguous (K x M, K x N)
   int sym_small;   // bf16 symmetric launches: 128 x 128 tiles instead of 256 x 256
   int num_cu;
   Ctrl* ctrl;      // per-matrix control blocks; null = unconditional

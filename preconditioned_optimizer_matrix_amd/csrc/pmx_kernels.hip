@@ -1235,11 +1235,13 @@ __global__ __launch_bounds__(NT) void xpose_kernel(XposeParams p) {
         *reinterpret_cast<uint4*>(p.out_n + (int64_t)b * p.sn + (int64_t)gr * p.ldn + gc) =
             make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      if (p.out_t) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) tile[r][8 * q + j] = v[j];
+        for (int j = 0; j < 8; ++j) tile[r][8 * q + j] = v[j];
+      }
     }
+    if (!p.out_t) return;  // (uniform over the block)
     __syncthreads();
-    if (!p.out_t) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = rr + 32 * i, gcol = c0 + c, gr = r0 + 8 * q;

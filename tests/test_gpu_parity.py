@@ -716,6 +716,53 @@ def test_polar_bf16_batched_large_tiles(env, m, n):
         assert cf.rel_fro(Ub, Up) < 3e-2, b
 
 
+def test_polar_bf16_transpose_reads(env, monkeypatch):
+    # 64 matrices of 1024 x 512: whole 256 x 256 x 64 residual tiles and
+    # enough of them, so I - X^T X reads the row-major iterate through the
+    # LDS transpose reads (no transposed copy); a handle created with
+    # PMX_BF16_MN=0 runs the transposed-copy form on the same input.  Both
+    # against the SVD factor, and against each other.
+    import ctypes
+    torch, pmx, dev = env
+    _say("polar bf16 transpose reads 64 x 1024 x 512")
+    vals, bits, _ = W.polar_batch(64, 1024, 512, 9001, smin=1e-2)
+    Gt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    opts = pmx.default_opts(tol=1e-2)
+    U, info = pmx.polar(Gt, opts=opts)
+    monkeypatch.setenv("PMX_BF16_MN", "0")
+    h = ctypes.c_void_p()
+    pmx.check(pmx.lib.pmx_create(ctypes.byref(h), 0), "create")
+    monkeypatch.delenv("PMX_BF16_MN")
+    try:
+        U0 = torch.empty_like(Gt)
+        info0 = pmx.new_info(64, dev)
+        need = pmx.workspace_bytes(pmx.OP_POLAR, 1024, 512, 64, pmx.BF16, opts)
+        ws = pmx.workspace(need, dev)
+        pmx.check(pmx.lib.pmx_matfn_polar_batched(
+            h, pmx._ptr(Gt), pmx.BF16, 1024, 512, 512, 1024 * 512, pmx._ptr(U0), 512,
+            1024 * 512, 64, ctypes.byref(opts), pmx._ptr(info0), pmx._ptr(ws), ws.numel(),
+            pmx._stream(Gt)), "polar")
+        torch.cuda.synchronize()
+    finally:
+        pmx.lib.pmx_destroy(h)
+    infs, infs0 = pmx.parse_info(info), pmx.parse_info(info0)
+    Un = U.float().cpu().numpy().astype(np.float64)
+    U0n = U0.float().cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in (0, 1, 17, 40, 63):
+        assert int(infs[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), b
+        assert int(infs0[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), b
+        Up, _ = cf.polar(vals[b].astype(np.float64))
+        for X in (Un[b], U0n[b]):
+            assert np.linalg.norm(X.T @ X - np.eye(512)) / np.sqrt(512) < 1e-2, b
+            assert cf.rel_fro(X, Up) < 3e-2, b
+        worst = max(worst, cf.rel_fro(Un[b], U0n[b]))
+    print("  transpose reads vs transposed copy: worst rel diff %.2e, iters %s / %s" % (
+        worst, [int(i["iters"][0]) for i in infs[:4]], [int(i["iters"][0]) for i in infs0[:4]]),
+        flush=True)
+    assert worst < 1e-2
+
+
 def test_polar_bf16_iterations_follow_reference(env):
     torch, pmx, dev = env
     Gt = _bf16(torch, W.polar_batch(1, 512, 128, 9, smin=1e-2)[0][0])
