@@ -391,11 +391,12 @@ __device__ __forceinline__ void skinny_finish(float (&acc)[RW * Q], const Skinny
 }
 
 // After a Gram pass (the kernel boundary orders the shares before this): one
-// block per matrix sums the pass's `nblocks` shares of every Gram entry, one
-// wave per entry with a fixed lane assignment and reduction tree
-// (deterministic), and solves for alpha: the square-root / polar family's
-// quartic, or the inverse Newton objective (newton_p = 4).  Then the adaptive
-// degree's decision, the product count and the alpha trace.
+// block per matrix sums the pass's `nblocks` shares of every Gram entry with
+// a fixed lane assignment and reduction tree (deterministic; one wave for
+// J <= 5, one wave per entry above), and solves for alpha: the square-root /
+// polar family's quartic, or the inverse Newton objective (newton_p = 4).
+// Then the adaptive degree's decision, the product count and the alpha
+// trace.
 __global__ __launch_bounds__(NT) void gram_alpha_kernel(SkinnyParams p, int nblocks) {
   const int b = blockIdx.x;
   Ctrl* cb = p.ctrl + b;
@@ -407,11 +408,36 @@ __global__ __launch_bounds__(NT) void gram_alpha_kernel(SkinnyParams p, int nblo
   const double fro = cb->fro;
   const double* part = p.gram_partials + (int64_t)b * p.gram_stride;
   __shared__ double gsum[kGramShare];
-  for (int e = wid; e < ng; e += NT / 64) {
-    double sv = 0.0;
-    for (int i = lane; i < nblocks; i += 64) sv += part[(int64_t)i * kGramShare + e];
-    sv = wave_sum(sv);
-    if (lane == 0) gsum[e] = sv;
+  if (ng <= 16) {
+    // one wave: lane l adds the shares of blocks l, l + 64, ... (the 15
+    // entries of up to four blocks read together), then the 16 sums are
+    // halved across the wave (the same fixed tree every call)
+    if (wid == 0) {
+      double h[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) h[e] = 0.0;
+      for (int i0 = lane; i0 < nblocks; i0 += 256) {
+        double v[4][16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + 64 * u;
+          const double* row = part + (int64_t)(i < nblocks ? i : 0) * kGramShare;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[u][e] = (i < nblocks && e < ng) ? row[e] : 0.0;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) h[e] += (v[0][e] + v[1][e]) + (v[2][e] + v[3][e]);
+      }
+      halve_reduce_d<16, 32>(h, lane);
+      if ((lane & 3) == 0 && (lane >> 2) < ng) gsum[lane >> 2] = h[0];
+    }
+  } else {
+    for (int e = wid; e < ng; e += NT / 64) {
+      double sv = 0.0;
+      for (int i = lane; i < nblocks; i += 64) sv += part[(int64_t)i * kGramShare + e];
+      sv = wave_sum(sv);
+      if (lane == 0) gsum[e] = sv;
+    }
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
