@@ -35,7 +35,6 @@ struct SmallShared {
   float m[6][SMAT];
   float kb[SN * SKLD];
   double red[SNT / 64][16];
-  double gpart[SNT];
   double gsum[16];
   Ctrl c;
 };
@@ -310,73 +309,23 @@ __device__ void small_alpha(SmallShared& sh, const float* R, const float* R2, in
     for (int j = 1; j <= 2; ++j) krylov_step(sh, {R, (j - 1) * p, j * p, p, s1}, {}, 1);
     last = {R, 2 * p, 3 * p, p, s1};
   }
-  if (p <= 16) {
-    // The last block and the Gram in one step: each wave adds the products
-    // of its own 16 rows (K_J from its registers, the others from LDS) into
-    // 16 fp64 sums, halves them over the wave and leaves one row of wave
-    // shares; entry e is then the shares of waves 0..3 added in order.
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, g4 = lane >> 4;
-    const f32x4 kj = krylov_tile(sh.kb, last.mat, last.ic, last.oc, last.q, last.scale, w, 0);
-    double gs[16];
-    if (J == 5) gram_rows<5>(gs, sh.kb, kj, w, g4, li, p);
-    else gram_rows<3>(gs, sh.kb, kj, w, g4, li, p);
-    halve_reduce_d<16, 32>(gs, lane);
-    if ((lane & 3) == 0) sh.red[w][lane >> 2] = gs[0];
-    __syncthreads();
-    if (threadIdx.x < NE)
-      sh.gsum[threadIdx.x] = ((sh.red[0][threadIdx.x] + sh.red[1][threadIdx.x]) +
-                              sh.red[2][threadIdx.x]) + sh.red[3][threadIdx.x];
-    __syncthreads();
-  } else {
-    krylov_step(sh, last, {}, 1);
-    // Gram, packed upper triangle of the J x J: entry e = t / 16 is summed
-    // in fp64 by threads 16 e .. 16 e + 15, thread t over rows t % 16 + 16 r
-    // (r < 4: rows beyond n are zero) and columns in chunks of four (the 32
-    // reads of a chunk in flight together; columns at or beyond p read
-    // column p - 1 and count zero); the 16 partial sums are added in lane
-    // order.
-    {
-      const int e = threadIdx.x >> 4, sl = threadIdx.x & 15;
-      double part = 0.0;
-      if (e < NE) {
-        int a = 0, rem = e;
-        while (rem >= J - a) {
-          rem -= J - a;
-          ++a;
-        }
-        const float* ka = sh.kb + (a + 1) * p + sl * SKLD;
-        const float* kc = sh.kb + (a + rem + 1) * p + sl * SKLD;
-        double acc4[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int c0 = 0; c0 < p; c0 += 4) {
-          float va[4][4], vc[4][4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int c = min(c0 + v, p - 1);
-              va[r][v] = ka[16 * r * SKLD + c];
-              vc[r][v] = kc[16 * r * SKLD + c];
-            }
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            if (c0 + v >= p) break;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc4[r] += (double)va[r][v] * (double)vc[r][v];
-          }
-        }
-        part = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-      }
-      sh.gpart[threadIdx.x] = part;
-    }
-    __syncthreads();
-    if (threadIdx.x < NE) {
-      double v = 0.0;
-#pragma unroll
-      for (int sl = 0; sl < 16; ++sl) v += sh.gpart[threadIdx.x * 16 + sl];
-      sh.gsum[threadIdx.x] = v;
-    }
-    __syncthreads();
-  }
+  // The last block and the Gram in one step (q = p <= PMX_MAX_SKETCH = 16:
+  // one tile per wave): each wave adds the products of its own 16 rows (K_J
+  // from its registers, the others from LDS) into 16 fp64 sums, halves them
+  // over the wave and leaves one row of wave shares; entry e is then the
+  // shares of waves 0..3 added in order.
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, g4 = lane >> 4;
+  const f32x4 kj = krylov_tile(sh.kb, last.mat, last.ic, last.oc, last.q, last.scale, w, 0);
+  double gs[16];
+  if (J == 5) gram_rows<5>(gs, sh.kb, kj, w, g4, li, p);
+  else gram_rows<3>(gs, sh.kb, kj, w, g4, li, p);
+  halve_reduce_d<16, 32>(gs, lane);
+  if ((lane & 3) == 0) sh.red[w][lane >> 2] = gs[0];
+  __syncthreads();
+  if (threadIdx.x < NE)
+    sh.gsum[threadIdx.x] = ((sh.red[0][threadIdx.x] + sh.red[1][threadIdx.x]) +
+                            sh.red[2][threadIdx.x]) + sh.red[3][threadIdx.x];
+  __syncthreads();
   if (threadIdx.x == 0) {
     // d <= 2 here: J = 3 or 5 (no code for the degree-3 solve)
     const double alpha = J == 3 ? alpha_from_gram_t<3>(sh.gsum, fro, coef, cfg.lo, cfg.hi, nullptr)
