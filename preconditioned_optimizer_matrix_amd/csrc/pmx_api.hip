@@ -25,6 +25,8 @@ struct pmx_context {
   int skinny_variant;      // skinny products: 0 In through LDS, 1 In read directly
   int bf16_dma;            // bf16 GEMM: 1 uses direct global-to-LDS loads for whole tiles (measured slower; off)
   int bf16_mn;             // bf16 polar: 1 reads X for I - X^T X via LDS transpose reads (no X^T copy)
+  int bf16_persist;        // bf16 GEMM: 1 runs whole-tile launches on persistent blocks, each
+                           // loading its next tile's first k tile ahead of the epilogue
   int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
   int split_k;             // 1: split-k tail for the fp32 products of the iterations
   int bf16_sym;            // 1: bf16 X^T X and R^2 run upper-triangle tiles, mirrored
@@ -422,6 +424,7 @@ GemmParams bf16_base(const pmx_context* h, int M, int N, int K, int batch) {
   g.cfg_id = h->bf16_cfg;
   g.map_mode = h->bf16_map;
   g.dma = h->bf16_dma;
+  g.persist = h->bf16_persist;
   return g;
 }
 
@@ -999,6 +1002,8 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_BF16_DMA")) c->bf16_dma = atoi(e);
   c->bf16_mn = 1;
   if (const char* e = getenv("PMX_BF16_MN")) c->bf16_mn = atoi(e);
+  c->bf16_persist = 1;
+  if (const char* e = getenv("PMX_BF16_PERSIST")) c->bf16_persist = atoi(e);
   c->small_fused = 1;
   if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
   c->split_k = 1;

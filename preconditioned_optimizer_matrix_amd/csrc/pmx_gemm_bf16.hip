@@ -21,6 +21,8 @@
 //    fragments of the next 16-wide k step read while the current one
 //    multiplies; persistent grid over (matrix, tile).
 //  * fp32 -> bf16 rounding is round-to-nearest-even.
+#include <type_traits>
+
 #include "pmx_kernels.h"
 
 namespace pmx {
@@ -151,48 +153,83 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// Operand origins of a whole tile at k tile 0 (wave-uniform) and the
+// thread's offsets from them (the same for every tile of a launch), so a
+// k tile's loads are uniform base + 32-bit offset.
+struct TileBase {
+  const uint16_t* a;
+  const uint16_t* b;
+};
+
 template <class C>
-__device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[C::FM][C::FN],
-                                              uint16_t (*smem)[C::LDS], const uint16_t* A,
-                                              int64_t lda, const uint16_t* B, int64_t ldb,
-                                              int m0, int n0, int nk, int lane, int wm, int wn) {
-  constexpr int NT = C::NT, FM = C::FM, FN = C::FN, CA = C::CA, CB = C::CB;
-  constexpr int BK = C::BK, LDK = C::LDK, CH = C::CH, STEPS = BK / 16;
-  constexpr int NF = FM + FN;  // fragment reads per step
-  constexpr int RS = NT / CH;  // rows covered by one chunk index step
-  constexpr int MF = FM * FN;  // MFMAs per step
-  const int t = threadIdx.x;
-  const uint16_t* ga = A + (int64_t)(m0 + t / CH) * lda + (t % CH) * 8;
-  const uint16_t* gb = B + (int64_t)(n0 + t / CH) * ldb + (t % CH) * 8;
-  const int64_t sta = (int64_t)RS * lda, stb = (int64_t)RS * ldb;
-  const int wofs = (t / CH) * LDK + (t % CH) * 8;
+struct FastOffsets {
+  uint32_t a, b;    // thread offsets (elements) of chunk 0
+  uint32_t sa, sb;  // between a thread's chunks
+  int wofs;         // LDS offset of chunk 0
+  __device__ FastOffsets(int64_t lda, int64_t ldb) {
+    const int t = threadIdx.x;
+    constexpr int RS = C::NT / C::CH;  // rows covered by one chunk index step
+    a = (uint32_t)((t / C::CH) * lda + (t % C::CH) * 8);
+    b = (uint32_t)((t / C::CH) * ldb + (t % C::CH) * 8);
+    sa = (uint32_t)(RS * lda);
+    sb = (uint32_t)(RS * ldb);
+    wofs = (t / C::CH) * C::LDK + (t % C::CH) * 8;
+  }
+};
+
+// k tile 0 of a tile into LDS buffer `buf`.
+template <class C>
+__device__ __forceinline__ void fast_stage0(uint16_t (*smem)[C::LDS], int buf, TileBase tb,
+                                            const FastOffsets<C>& o) {
+  constexpr int CA = C::CA, CB = C::CB, RS = C::NT / C::CH, LDK = C::LDK;
   u32x4 va[CA], vb[CB];
 #pragma unroll
-  for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + i * sta);
+  for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(tb.a + (o.a + i * o.sa));
 #pragma unroll
-  for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + i * stb);
+  for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(tb.b + (o.b + i * o.sb));
 #pragma unroll
-  for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(smem[0] + wofs + i * RS * LDK) = va[i];
+  for (int i = 0; i < CA; ++i)
+    *reinterpret_cast<u32x4*>(smem[buf] + o.wofs + i * RS * LDK) = va[i];
 #pragma unroll
   for (int i = 0; i < CB; ++i)
-    *reinterpret_cast<u32x4*>(smem[0] + C::BM * LDK + wofs + i * RS * LDK) = vb[i];
+    *reinterpret_cast<u32x4*>(smem[buf] + C::BM * LDK + o.wofs + i * RS * LDK) = vb[i];
   __syncthreads();
+}
+
+// The k loop of a tile whose k tile 0 is staged in LDS buffer `buf`: k tile
+// kt is read from buffer (kt + buf) & 1.  The last k tile's loads fetch k
+// tile 0 of `nx` (the next tile of a persistent block, or a reload) into the
+// other buffer, so a following tile finds its first k tile staged.
+template <class C>
+__device__ __forceinline__ void fast_kloop(f32x16 (&acc)[C::FM][C::FN],
+                                           uint16_t (*smem)[C::LDS], int buf, TileBase cur,
+                                           TileBase nx, const FastOffsets<C>& o, int nk,
+                                           int lane, int wm, int wn) {
+  constexpr int FM = C::FM, FN = C::FN, CA = C::CA, CB = C::CB;
+  constexpr int BK = C::BK, LDK = C::LDK, STEPS = BK / 16;
+  constexpr int NF = FM + FN;          // fragment reads per step
+  constexpr int RS = C::NT / C::CH;    // rows covered by one chunk index step
+  constexpr int MF = FM * FN;          // MFMAs per step
   const int ra = (wm + (lane & 31)) * LDK + (lane >> 5) * 8;
   const int rb = (C::BM + wn + (lane & 31)) * LDK + (lane >> 5) * 8;
+  u32x4 va[CA], vb[CB];
   for (int kt = 0; kt < nk; ++kt) {
-    const uint16_t* sa = smem[kt & 1] + ra;
-    const uint16_t* sb = smem[kt & 1] + rb;
-    uint16_t* dst = smem[(kt & 1) ^ 1] + wofs;
-    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;  // the last tile reloads itself
+    const int cb = (kt + buf) & 1;
+    const uint16_t* sa = smem[cb] + ra;
+    const uint16_t* sb = smem[cb] + rb;
+    uint16_t* dst = smem[cb ^ 1] + o.wofs;
+    const bool more = kt + 1 < nk;
+    const uint16_t* la = more ? cur.a + (kt + 1) * BK : nx.a;
+    const uint16_t* lb = more ? cur.b + (kt + 1) * BK : nx.b;
     bf16x8 fa[2][FM], fb[2][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(sa + 32 * i * LDK);
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[0][j] = *reinterpret_cast<const bf16x8*>(sb + 32 * j * LDK);
 #pragma unroll
-    for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + kn + i * sta);
+    for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(la + (o.a + i * o.sa));
 #pragma unroll
-    for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + kn + i * stb);
+    for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(lb + (o.b + i * o.sb));
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       const int c = s & 1, n = c ^ 1;
@@ -224,6 +261,19 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[C::FM][C::FN],
   }
 }
 
+template <class C>
+__device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[C::FM][C::FN],
+                                              uint16_t (*smem)[C::LDS], const uint16_t* A,
+                                              int64_t lda, const uint16_t* B, int64_t ldb,
+                                              int m0, int n0, int nk, int lane, int wm, int wn) {
+  const FastOffsets<C> o(lda, ldb);
+  const TileBase cur = {A + (int64_t)m0 * lda, B + (int64_t)n0 * ldb};
+  fast_stage0<C>(smem, 0, cur, o);
+  // the last k tile reloads itself
+  const TileBase nx = {cur.a + (nk - 1) * C::BK, cur.b + (nk - 1) * C::BK};
+  fast_kloop<C>(acc, smem, 0, cur, nx, o, nk, lane, wm, wn);
+}
+
 // The same main loop for operands stored m- (n-) contiguous: A is K x M
 // (A^T of the C = A Bs^T form, row k holding M values), Bs likewise K x N,
 // e.g. C = X^T X straight from the row-major iterate X, with no transposed
@@ -252,53 +302,78 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* p, int pitch) {
 }
 
 template <class C>
-__device__ __forceinline__ void mainloop_fast_mn(f32x16 (&acc)[C::FM][C::FN],
-                                                 uint16_t (*smem)[C::LDS], const uint16_t* A,
-                                                 int64_t lda, const uint16_t* B, int64_t ldb,
-                                                 int m0, int n0, int nk, int lane, int wm,
-                                                 int wn) {
-  constexpr int NT = C::NT, FM = C::FM, FN = C::FN, BK = C::BK, STEPS = BK / 16;
-  constexpr int PA = C::BM + 32, PB = C::BN + 32;
-  static_assert(BK * (PA + PB) <= C::LDS, "an m-contiguous k tile fits an LDS stage");
-  constexpr int CPA = C::BM / 8, CPB = C::BN / 8;  // 16-byte chunks per k row
-  constexpr int CA = BK * CPA / NT, CB = BK * CPB / NT;
-  static_assert(CA * NT == BK * CPA && CB * NT == BK * CPB, "chunks per thread");
-  constexpr int RSA = NT / CPA, RSB = NT / CPB;  // k rows per chunk index step
-  constexpr int NF = 2 * (FM + FN);              // transpose reads per step
-  constexpr int MF = FM * FN;                    // MFMAs per step
-  const int t = threadIdx.x;
-  const uint16_t* ga = A + (int64_t)(t / CPA) * lda + m0 + (t % CPA) * 8;
-  const uint16_t* gb = B + (int64_t)(t / CPB) * ldb + n0 + (t % CPB) * 8;
-  const int64_t sta = (int64_t)RSA * lda, stb = (int64_t)RSB * ldb;
-  const int wa = (t / CPA) * PA + (t % CPA) * 8;
-  const int wb = BK * PA + (t / CPB) * PB + (t % CPB) * 8;
+struct MnOffsets {
+  static constexpr int PA = C::BM + 32, PB = C::BN + 32;
+  static constexpr int CPA = C::BM / 8, CPB = C::BN / 8;  // 16-byte chunks per k row
+  static constexpr int RSA = C::NT / CPA, RSB = C::NT / CPB;  // k rows per chunk index step
+  uint32_t a, b, sa, sb;
+  int wa, wb;
+  __device__ MnOffsets(int64_t lda, int64_t ldb) {
+    const int t = threadIdx.x;
+    a = (uint32_t)((t / CPA) * lda + (t % CPA) * 8);
+    b = (uint32_t)((t / CPB) * ldb + (t % CPB) * 8);
+    sa = (uint32_t)(RSA * lda);
+    sb = (uint32_t)(RSB * ldb);
+    wa = (t / CPA) * PA + (t % CPA) * 8;
+    wb = C::BK * PA + (t / CPB) * PB + (t % CPB) * 8;
+  }
+};
+
+template <class C>
+__device__ __forceinline__ void mn_stage0(uint16_t (*smem)[C::LDS], int buf, TileBase tb,
+                                          const MnOffsets<C>& o) {
+  using O = MnOffsets<C>;
+  constexpr int CA = C::BK * O::CPA / C::NT, CB = C::BK * O::CPB / C::NT;
   u32x4 va[CA], vb[CB];
 #pragma unroll
-  for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + i * sta);
+  for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(tb.a + (o.a + i * o.sa));
 #pragma unroll
-  for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + i * stb);
+  for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(tb.b + (o.b + i * o.sb));
 #pragma unroll
-  for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(smem[0] + wa + i * RSA * PA) = va[i];
+  for (int i = 0; i < CA; ++i)
+    *reinterpret_cast<u32x4*>(smem[buf] + o.wa + i * O::RSA * O::PA) = va[i];
 #pragma unroll
-  for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(smem[0] + wb + i * RSB * PB) = vb[i];
+  for (int i = 0; i < CB; ++i)
+    *reinterpret_cast<u32x4*>(smem[buf] + o.wb + i * O::RSB * O::PB) = vb[i];
   __syncthreads();
+}
+
+// k loop of the m-contiguous form (as fast_kloop: buffer parity `buf`, the
+// last k tile's loads fetch k tile 0 of `nx`).  A k tile advances BK rows.
+template <class C>
+__device__ __forceinline__ void mn_kloop(f32x16 (&acc)[C::FM][C::FN], uint16_t (*smem)[C::LDS],
+                                         int buf, TileBase cur, TileBase nx,
+                                         const MnOffsets<C>& o, int64_t lda, int64_t ldb,
+                                         int nk, int lane, int wm, int wn) {
+  using O = MnOffsets<C>;
+  constexpr int FM = C::FM, FN = C::FN, BK = C::BK, STEPS = BK / 16;
+  constexpr int PA = O::PA, PB = O::PB;
+  static_assert(BK * (PA + PB) <= C::LDS, "an m-contiguous k tile fits an LDS stage");
+  constexpr int CA = BK * O::CPA / C::NT, CB = BK * O::CPB / C::NT;
+  static_assert(CA * C::NT == BK * O::CPA && CB * C::NT == BK * O::CPB, "chunks per thread");
+  constexpr int NF = 2 * (FM + FN);  // transpose reads per step
+  constexpr int MF = FM * FN;        // MFMAs per step
   const int g = lane >> 4, j = lane & 15;
   const int ra = (8 * (g >> 1) + (j >> 2)) * PA + 16 * (g & 1) + 4 * (j & 3) + wm;
   const int rb = BK * PA + (8 * (g >> 1) + (j >> 2)) * PB + 16 * (g & 1) + 4 * (j & 3) + wn;
+  u32x4 va[CA], vb[CB];
   for (int kt = 0; kt < nk; ++kt) {
-    const uint16_t* sa = smem[kt & 1] + ra;
-    const uint16_t* sb = smem[kt & 1] + rb;
-    uint16_t* dst = smem[(kt & 1) ^ 1];
-    const int64_t kn = (int64_t)(kt + 1 < nk ? kt + 1 : kt) * BK;  // the last tile reloads itself
+    const int cb = (kt + buf) & 1;
+    const uint16_t* sa = smem[cb] + ra;
+    const uint16_t* sb = smem[cb] + rb;
+    uint16_t* dst = smem[cb ^ 1];
+    const bool more = kt + 1 < nk;
+    const uint16_t* la = more ? cur.a + (int64_t)(kt + 1) * BK * lda : nx.a;
+    const uint16_t* lb = more ? cur.b + (int64_t)(kt + 1) * BK * ldb : nx.b;
     bf16x8 fa[2][FM], fb[2][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa[0][i] = frag_tr(sa + 32 * i, PA);
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj) fb[0][jj] = frag_tr(sb + 32 * jj, PB);
 #pragma unroll
-    for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(ga + kn * lda + i * sta);
+    for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(la + (o.a + i * o.sa));
 #pragma unroll
-    for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(gb + kn * ldb + i * stb);
+    for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(lb + (o.b + i * o.sb));
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const int c = st & 1, n = c ^ 1;
@@ -316,10 +391,10 @@ __device__ __forceinline__ void mainloop_fast_mn(f32x16 (&acc)[C::FM][C::FN],
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][jj], acc[i][jj], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(dst + wa + i * RSA * PA) = va[i];
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(dst + o.wa + i * O::RSA * PA) = va[i];
 #pragma unroll
-    for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(dst + wb + i * RSB * PB) = vb[i];
-    // schedule of the k tile (as in mainloop_fast)
+    for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(dst + o.wb + i * O::RSB * PB) = vb[i];
+    // schedule of the k tile (as in fast_kloop)
     __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
     __builtin_amdgcn_sched_group_barrier(0x020, CA + CB, 0);
 #pragma unroll
@@ -327,6 +402,20 @@ __device__ __forceinline__ void mainloop_fast_mn(f32x16 (&acc)[C::FM][C::FN],
     sched_interleave<MF, CA + CB, 0x200, (CA + CB + MF - 1) / MF>();
     __syncthreads();
   }
+}
+
+template <class C>
+__device__ __forceinline__ void mainloop_fast_mn(f32x16 (&acc)[C::FM][C::FN],
+                                                 uint16_t (*smem)[C::LDS], const uint16_t* A,
+                                                 int64_t lda, const uint16_t* B, int64_t ldb,
+                                                 int m0, int n0, int nk, int lane, int wm,
+                                                 int wn) {
+  const MnOffsets<C> o(lda, ldb);
+  const TileBase cur = {A + m0, B + n0};
+  mn_stage0<C>(smem, 0, cur, o);
+  // the last k tile reloads itself
+  const TileBase nx = {cur.a + (int64_t)(nk - 1) * C::BK * lda, cur.b + (int64_t)(nk - 1) * C::BK * ldb};
+  mn_kloop<C>(acc, smem, 0, cur, nx, o, lda, ldb, nk, lane, wm, wn);
 }
 
 // Epilogue of one tile by role (same accumulator layout as the 32x32 fp32
@@ -559,6 +648,88 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
   }
 }
 
+// Persistent form for launches of whole tiles (k-contiguous operands, or the
+// m-contiguous residual): one block per CU walks its items, and the last k
+// tile of an item loads k tile 0 of the block's next item before the item's
+// epilogue stores are issued.  The next item then starts with its first k
+// tile staged, and the stores drain under its main loop (loads and stores
+// share one in-order counter, so a first load issued after the stores would
+// wait for them).  The blocks of one XCD (block index x mod 8) take a
+// contiguous range of items, as many at a time as the XCD has blocks.  The
+// epilogue must leave LDS alone: no staged transposed copy.
+template <class C, int ROLE, bool MN>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_persist_kernel(GemmParams p) {
+  constexpr int FM = C::FM, FN = C::FN;
+  constexpr int WGN = C::BN / C::WN;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][C::LDS];
+  __shared__ double red[C::WAVES];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = (wid / WGN) * C::WM, wn = (wid % WGN) * C::WN;
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int total = tiles * p.batch;
+  const GemmProblem& pr = p.prob[0];
+  const int nk = p.K / C::BK;
+  const int64_t lda = pr.a.ld, ldb = pr.b.ld;
+  const bool xcd = p.map_mode != 0 && (gridDim.x & 7) == 0 && (total & 7) == 0;
+  const int x = blockIdx.x & 7, q = blockIdx.x >> 3, per = total >> 3, g8 = gridDim.x >> 3;
+  int r = 0;
+  // the block's next item of a running matrix
+  auto next_item = [&](int& b, int& tm, int& tn, int& tile) -> bool {
+    for (;;) {
+      int L;
+      if (xcd) {
+        const int jx = q + r * g8;
+        if (jx >= per) return false;
+        L = x * per + jx;
+      } else {
+        L = blockIdx.x + r * (int)gridDim.x;
+        if (L >= total) return false;
+      }
+      ++r;
+      item_tile(L, p.tiles_m, p.tiles_n, &b, &tm, &tn, &tile);
+      if (!p.ctrl || *(volatile int32_t*)&p.ctrl[b].status == PMX_RUNNING) return true;
+    }
+  };
+  auto base_of = [&](int b, int tm, int tn) -> TileBase {
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(pr.a.ptr) + (int64_t)b * pr.a.stride;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(pr.b.ptr) + (int64_t)b * pr.b.stride;
+    if constexpr (MN) return {A + tm * C::BM, B + tn * C::BN};
+    else return {A + (int64_t)(tm * C::BM) * lda, B + (int64_t)(tn * C::BN) * ldb};
+  };
+  int b, tm, tn, tile;
+  if (!next_item(b, tm, tn, tile)) return;
+  TileBase cur = base_of(b, tm, tn);
+  using Off = std::conditional_t<MN, MnOffsets<C>, FastOffsets<C>>;
+  const Off o(lda, ldb);
+  int buf = 0;
+  if constexpr (MN) mn_stage0<C>(smem, buf, cur, o);
+  else fast_stage0<C>(smem, buf, cur, o);
+  for (;;) {
+    int b2 = b, tm2 = tm, tn2 = tn, tile2 = tile;
+    const bool more = next_item(b2, tm2, tn2, tile2);
+    // without a next item the last k tile loads this item's k tile 0 again
+    const TileBase nx = more ? base_of(b2, tm2, tn2) : cur;
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    if constexpr (MN) mn_kloop<C>(acc, smem, buf, cur, nx, o, lda, ldb, nk, lane, wm, wn);
+    else fast_kloop<C>(acc, smem, buf, cur, nx, o, nk, lane, wm, wn);
+    bf16_epilogue<C, ROLE>(acc, p, pr, b, tm * C::BM, tn * C::BN, tile, tiles, lane, wm, wn, red,
+                           false, nullptr);
+    if (!more) break;
+    buf = (buf + nk) & 1;
+    b = b2;
+    tm = tm2;
+    tn = tn2;
+    tile = tile2;
+    cur = nx;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Whole-tile variant with direct global-to-LDS loads (global_load_lds_dwordx4:
 // lane l of a wave writes its 16 bytes at the instruction's LDS base + 16 l).
@@ -733,18 +904,49 @@ hipError_t launch_dma(GemmParams p, int role, hipStream_t s) {
   return after_resid(p, role, (int)(total / p.batch), s);
 }
 
+// Whole 256 x 256 x 64 tiles of 16-byte aligned rows: the shapes the
+// persistent form and the m-contiguous residual take.
+template <class C>
+bool whole_aligned(const GemmParams& p) {
+  return p.vec && p.M % C::BM == 0 && p.N % C::BN == 0 && p.K % C::BK == 0 && p.K >= C::BK &&
+         p.prob[0].a.ld % 8 == 0 && p.prob[0].b.ld % 8 == 0 && p.prob[0].a.stride % 8 == 0 &&
+         p.prob[0].b.stride % 8 == 0 && ((uintptr_t)p.prob[0].a.ptr & 15) == 0 &&
+         ((uintptr_t)p.prob[0].b.ptr & 15) == 0;
+}
+
 template <class C>
 hipError_t launch_cfg(GemmParams p, int role, hipStream_t s) {
   p.tiles_m = (p.M + C::BM - 1) / C::BM;
   p.tiles_n = (p.N + C::BN - 1) / C::BN;
+  if constexpr (C::BM == 256 && C::BN == 256 && C::BK == 64 && C::WM == 128 && C::WN == 64) {
+    if (p.persist && !p.sym && whole_aligned<C>(p) && (role != ROLE_UPDATE || !p.prob[1].c) &&
+        (!p.mn || role == ROLE_RESID)) {
+      const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
+      const int64_t cu = p.num_cu > 0 ? p.num_cu : 256;
+      const dim3 grid((unsigned)(total < cu ? total : cu)), block(C::NT);
+      if (p.mn) {
+        hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_RESID, true>), grid, block, 0, s, p);
+      } else {
+        switch (role) {
+          case ROLE_RESID:
+            hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_RESID, false>), grid, block, 0, s, p);
+            break;
+          case ROLE_POWER:
+            hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_POWER, false>), grid, block, 0, s, p);
+            break;
+          case ROLE_UPDATE:
+            hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_UPDATE, false>), grid, block, 0, s, p);
+            break;
+          default: return hipErrorInvalidValue;
+        }
+      }
+      return after_resid(p, role, (int)(total / p.batch), s);
+    }
+  }
   if (p.mn) {
     // m- / n-contiguous operands: the residual on whole 256 x 256 x 64 tiles
     if constexpr (C::BM == 256 && C::BN == 256 && C::BK == 64 && C::WM == 128 && C::WN == 64) {
-      if (role != ROLE_RESID || p.sym || !p.vec || p.M % 256 || p.N % 256 || p.K % 64 ||
-          p.K < 64 || p.prob[0].a.ld % 8 || p.prob[0].b.ld % 8 || p.prob[0].a.stride % 8 ||
-          p.prob[0].b.stride % 8 || ((uintptr_t)p.prob[0].a.ptr & 15) ||
-          ((uintptr_t)p.prob[0].b.ptr & 15))
-        return hipErrorInvalidValue;
+      if (role != ROLE_RESID || p.sym || !whole_aligned<C>(p)) return hipErrorInvalidValue;
       const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
       int64_t g = total;
       if (p.max_blocks > 0 && g > p.max_blocks) g = p.max_blocks;
