@@ -32,6 +32,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Block tile BM x BN x BK, waves of WM x WN (FM x FN accumulators of
 // 32 x 32), MINB blocks resident per CU.  LDS rows hold BK + 8 bf16: the row
@@ -648,6 +649,113 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
   }
 }
 
+// The epilogue of a whole tile through LDS (`stage`: a free LDS buffer of
+// the main loop).  The accumulator layout gives a lane four consecutive rows
+// of one column, so direct stores write 2 (bf16) or 4 (fp32) bytes per lane,
+// two rows per instruction.  Here the waves write a slice of their values
+// row-major into LDS, then the block stores whole rows of the tile with
+// 16-byte stores: X' (bf16) in two passes of 128 rows (fragments i = 2 p,
+// 2 p + 1 of each wave row), fp32 outputs in four passes of 64 rows
+// (fragment i = p), the residual's bf16 copy converted from the staged
+// fp32 values.  Values, and the residual's Frobenius share (summed in the
+// direct epilogue's order), are the direct epilogue's.
+template <class C, int ROLE>
+__device__ __forceinline__ void staged_epilogue(f32x16 (&acc)[C::FM][C::FN],
+                                                const GemmParams& p, const GemmProblem& pr,
+                                                int b, int m0, int n0, int tile, int lane,
+                                                int wm, int wn, double* red, uint16_t* stage) {
+  static_assert(C::BM == 256 && C::BN == 256 && C::WM == 128 && C::FM == 4, "256 x 256 tiles");
+  constexpr bool RESID = ROLE == ROLE_RESID;
+  const int hi = lane >> 5, col_in = lane & 31;
+  const int wr = wm / 128;  // wave row (0, 1)
+  if constexpr (ROLE == ROLE_UPDATE) {
+    constexpr int PT = C::BN + 8;  // staged row pitch (bf16): 528 bytes
+    static_assert(128 * PT <= C::LDS, "half a tile fits an LDS buffer");
+    uint16_t* out = reinterpret_cast<uint16_t*>(pr.c) + (int64_t)b * pr.stride_c;
+#pragma clang loop unroll(full)
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma clang loop unroll(full)
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * pass + ii;
+#pragma clang loop unroll(full)
+        for (int j = 0; j < C::FN; ++j) {
+          const int c = wn + 32 * j + col_in;
+#pragma clang loop unroll(full)
+          for (int g = 0; g < 4; ++g) {
+#pragma clang loop unroll(full)
+            for (int r = 0; r < 4; ++r) {
+              const int srow = 64 * wr + 32 * ii + 8 * g + 4 * hi + r;
+              stage[srow * PT + c] = (uint16_t)bf16_rne(acc[i][j][4 * g + r]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // staged row R is tile row 128 (R / 64) + 64 pass + R % 64
+#pragma unroll
+      for (int q = threadIdx.x; q < 128 * (C::BN / 8); q += C::NT) {
+        const int R = q / (C::BN / 8), ch = q % (C::BN / 8);
+        const int row = m0 + 128 * (R >> 6) + 64 * pass + (R & 63);
+        *reinterpret_cast<u32x4*>(out + (int64_t)row * pr.ldc + n0 + 8 * ch) =
+            *reinterpret_cast<const u32x4*>(stage + R * PT + 8 * ch);
+      }
+      __syncthreads();
+    }
+  } else {
+    constexpr int PF = C::BN + 4;  // staged row pitch (fp32): 1040 bytes
+    static_assert(64 * PF * 4 <= C::LDS * 2, "a quarter tile fits an LDS buffer");
+    float* st = reinterpret_cast<float*>(stage);
+    float* out = pr.c + (int64_t)b * pr.stride_c;
+    uint16_t* hout = nullptr;
+    int64_t hld = 0;
+    if (RESID && p.prob[1].c) {
+      hout = reinterpret_cast<uint16_t*>(p.prob[1].c) + (int64_t)b * p.prob[1].stride_c;
+      hld = p.prob[1].ldc;
+    }
+    float fro = 0.f;
+#pragma clang loop unroll(full)
+    for (int pass = 0; pass < 4; ++pass) {
+      const int i = pass;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < C::FN; ++j) {
+        const int c = wn + 32 * j + col_in;
+#pragma clang loop unroll(full)
+        for (int g = 0; g < 4; ++g) {
+#pragma clang loop unroll(full)
+          for (int r = 0; r < 4; ++r) {
+            float x = acc[i][j][4 * g + r];
+            if (RESID) {
+              const int row = wm + 32 * i + 8 * g + 4 * hi + r;
+              x = (m0 + row == n0 + c ? 1.f : 0.f) - x;
+              fro += x * x;
+            }
+            st[(32 * wr + 8 * g + 4 * hi + r) * PF + c] = x;
+          }
+        }
+      }
+      __syncthreads();
+      // staged row R is tile row 128 (R / 32) + 32 pass + R % 32
+#pragma unroll
+      for (int q = threadIdx.x; q < 64 * (C::BN / 4); q += C::NT) {
+        const int R = q / (C::BN / 4), ch = q % (C::BN / 4);
+        const int row = m0 + 128 * (R >> 5) + 32 * pass + (R & 31);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + R * PF + 4 * ch);
+        *reinterpret_cast<f32x4*>(out + (int64_t)row * pr.ldc + n0 + 4 * ch) = v;
+        if (RESID && hout) {
+          *reinterpret_cast<u32x2*>(hout + (int64_t)row * hld + n0 + 4 * ch) = {
+              bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
+        }
+      }
+      __syncthreads();
+    }
+    if (RESID) {
+      // the tile's Frobenius share; resid_decide_kernel sums them
+      const double blocksum = block_sum<C::WAVES>((double)fro, red);
+      if (threadIdx.x == 0) p.partials[(int64_t)b * p.partial_stride + tile] = blocksum;
+    }
+  }
+}
+
 // Persistent form for launches of whole tiles (k-contiguous operands, or the
 // m-contiguous residual): one block per CU walks its items, and the last k
 // tile of an item loads k tile 0 of the block's next item before the item's
@@ -656,7 +764,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_kernel(GemmParams p)
 // share one in-order counter, so a first load issued after the stores would
 // wait for them).  The blocks of one XCD (block index x mod 8) take a
 // contiguous range of items, as many at a time as the XCD has blocks.  The
-// epilogue must leave LDS alone: no staged transposed copy.
+// epilogue goes through the free LDS buffer (staged_epilogue): no transposed
+// copy, and output rows that allow 16-byte stores.
 template <class C, int ROLE, bool MN>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_persist_kernel(GemmParams p) {
   constexpr int FM = C::FM, FN = C::FN;
@@ -718,8 +827,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_persist_kernel(GemmP
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     if constexpr (MN) mn_kloop<C>(acc, smem, buf, cur, nx, o, lda, ldb, nk, lane, wm, wn);
     else fast_kloop<C>(acc, smem, buf, cur, nx, o, nk, lane, wm, wn);
-    bf16_epilogue<C, ROLE>(acc, p, pr, b, tm * C::BM, tn * C::BN, tile, tiles, lane, wm, wn, red,
-                           false, nullptr);
+    // the buffer the last k tile was read from is free until the next item's
+    // first k tile step stores into it
+    staged_epilogue<C, ROLE>(acc, p, pr, b, tm * C::BM, tn * C::BN, tile, lane, wm, wn, red,
+                             smem[(buf + nk - 1) & 1]);
     if (!more) break;
     buf = (buf + nk) & 1;
     b = b2;
@@ -919,8 +1030,14 @@ hipError_t launch_cfg(GemmParams p, int role, hipStream_t s) {
   p.tiles_m = (p.M + C::BM - 1) / C::BM;
   p.tiles_n = (p.N + C::BN - 1) / C::BN;
   if constexpr (C::BM == 256 && C::BN == 256 && C::BK == 64 && C::WM == 128 && C::WN == 64) {
-    if (p.persist && !p.sym && whole_aligned<C>(p) && (role != ROLE_UPDATE || !p.prob[1].c) &&
-        (!p.mn || role == ROLE_RESID)) {
+    const GemmProblem& oc = p.prob[0];
+    const int cq = role == ROLE_UPDATE ? 8 : 4;  // elements per 16-byte store
+    bool out_ok = oc.ldc % cq == 0 && oc.stride_c % cq == 0 && ((uintptr_t)oc.c & 15) == 0;
+    if (role == ROLE_UPDATE) out_ok = out_ok && !p.prob[1].c;
+    if (role == ROLE_RESID && p.prob[1].c)
+      out_ok = out_ok && p.prob[1].ldc % 4 == 0 && p.prob[1].stride_c % 4 == 0 &&
+               ((uintptr_t)p.prob[1].c & 7) == 0;
+    if (p.persist && !p.sym && whole_aligned<C>(p) && out_ok && (!p.mn || role == ROLE_RESID)) {
       const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
       const int64_t cu = p.num_cu > 0 ? p.num_cu : 256;
       const dim3 grid((unsigned)(total < cu ? total : cu)), block(C::NT);
