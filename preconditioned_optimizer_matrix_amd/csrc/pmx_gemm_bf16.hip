@@ -468,7 +468,8 @@ __device__ __forceinline__ void bf16_epilogue(f32x16 (&acc)[FM][FN], const GemmP
           float x = acc[i][j][4 * g + r];
           if (RESID) {
             x = (row == col ? 1.f : 0.f) - x;
-            if (row < p.M && col < p.N) fro += x * x;
+            // one rounding per term, as in staged_epilogue (the same shares)
+            if (row < p.M && col < p.N) fro = __builtin_fmaf(x, x, fro);
           }
           h[r] = bf16_rne(x);
           if (row < p.M && col < p.N) {
@@ -727,7 +728,7 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&acc)[C::FM][C::FN],
             if (RESID) {
               const int row = wm + 32 * i + 8 * g + 4 * hi + r;
               x = (m0 + row == n0 + c ? 1.f : 0.f) - x;
-              fro += x * x;
+              fro = __builtin_fmaf(x, x, fro);
             }
             st[(32 * wr + 8 * g + 4 * hi + r) * PF + c] = x;
           }

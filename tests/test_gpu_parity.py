@@ -763,6 +763,68 @@ def test_polar_bf16_transpose_reads(env, monkeypatch):
     assert worst < 1e-2
 
 
+def test_polar_bf16_persistent_mixed_convergence(env, monkeypatch):
+    # 64 matrices of 1024 x 512, alternately well conditioned (sigma_min 0.1)
+    # and ill conditioned (1e-3), so they converge after different numbers of
+    # updates and the later products skip the converged matrices' tiles, also
+    # inside the persistent blocks' item walk (whose last k tile prefetches
+    # the next running item).  The persistent kernel runs each tile's k loop
+    # in the same order and stores the same values as the one-block-per-tile
+    # kernel (a handle created with PMX_BF16_PERSIST=0), so the two calls must
+    # agree bit for bit; both against the SVD factor.
+    import ctypes
+    torch, pmx, dev = env
+    _say("polar bf16 persistent blocks, mixed convergence 64 x 1024 x 512")
+    va, ba, _ = W.polar_batch(32, 1024, 512, 4242, smin=1e-1)
+    vb, bb, _ = W.polar_batch(32, 1024, 512, 4243, smin=1e-3)
+    vals = np.empty((64, 1024, 512), np.float32)
+    bits = np.empty((64, 1024, 512), np.uint16)
+    vals[0::2], vals[1::2] = va, vb
+    bits[0::2], bits[1::2] = ba, bb
+    Gt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    opts = pmx.default_opts(tol=1e-2)
+    U, info = pmx.polar(Gt, opts=opts)
+    monkeypatch.setenv("PMX_BF16_PERSIST", "0")
+    h = ctypes.c_void_p()
+    pmx.check(pmx.lib.pmx_create(ctypes.byref(h), 0), "create")
+    monkeypatch.delenv("PMX_BF16_PERSIST")
+    try:
+        U0 = torch.empty_like(Gt)
+        info0 = pmx.new_info(64, dev)
+        need = pmx.workspace_bytes(pmx.OP_POLAR, 1024, 512, 64, pmx.BF16, opts)
+        ws = pmx.workspace(need, dev)
+        pmx.check(pmx.lib.pmx_matfn_polar_batched(
+            h, pmx._ptr(Gt), pmx.BF16, 1024, 512, 512, 1024 * 512, pmx._ptr(U0), 512,
+            1024 * 512, 64, ctypes.byref(opts), pmx._ptr(info0), pmx._ptr(ws), ws.numel(),
+            pmx._stream(Gt)), "polar")
+        torch.cuda.synchronize()
+    finally:
+        pmx.lib.pmx_destroy(h)
+    infs, infs0 = pmx.parse_info(info), pmx.parse_info(info0)
+    iters = [int(i["iters"][0]) for i in infs]
+    print("  updates: well conditioned %s, ill conditioned %s" % (
+        sorted(set(iters[0::2])), sorted(set(iters[1::2]))), flush=True)
+    assert max(iters[0::2]) < min(iters[1::2])
+    assert torch.equal(U.view(torch.int16), U0.view(torch.int16))
+    for b in range(64):
+        assert int(infs[b]["status"]) == int(infs0[b]["status"]), b
+        assert iters[b] == int(infs0[b]["iters"][0]), b
+        assert np.array_equal(infs[b]["alpha"], infs0[b]["alpha"]), b
+    # against the SVD: the factor itself for the well-conditioned matrices;
+    # for sigma_min 1e-3 at tol 1e-2 in bf16 the directions of the smallest
+    # singular values are resolved only coarsely, so there (as for the Muon
+    # workload) orthogonality and the symmetric factor U^T G = H
+    Un = U.float().cpu().numpy().astype(np.float64)
+    for b in (0, 1, 2, 33, 62, 63):
+        assert int(infs[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), b
+        G = vals[b].astype(np.float64)
+        Up, H = cf.polar(G)
+        assert np.linalg.norm(Un[b].T @ Un[b] - np.eye(512)) / np.sqrt(512) < 1e-2, b
+        assert cf.rel_fro(Un[b].T @ G, H) < 3e-2, b
+        if b % 2 == 0:
+            assert cf.rel_fro(Un[b], Up) < 3e-2, b
+
+
 def test_polar_bf16_iterations_follow_reference(env):
     torch, pmx, dev = env
     Gt = _bf16(torch, W.polar_batch(1, 512, 128, 9, smin=1e-2)[0][0])
