@@ -844,15 +844,17 @@ int gemm_f32_tiles(int M, int N) {
 hipError_t launch_gemm_f32(const GemmParams& p, bool ta, bool tb, int role, hipStream_t s) {
   int id = p.cfg_id;
   if (p.sym) {
-    // square tiles only: the 128 x 128 tile once the triangle still gives
-    // every CU a tile, or when the split-k tail will spread a long k (>= 2048)
-    // over the CUs anyway; else 64 x 64
+    // square tiles only: the 128 x 128 tile when the split-k tail will spread
+    // a long k (>= 2048) over the CUs, or when the triangle gives every CU at
+    // least four tiles; else 64 x 64.  (64 batched triangles of order 512,
+    // k = 512: 640 tiles of 128, 2.5 per CU, took 162-184 us with the split
+    // tail and 111-113 us without; 2304 tiles of 64 took 97-106 us.)
     const int64_t t0 = (p.M + 127) / 128;
     const bool long_split = p.sk_part && p.sk_cnt && p.vec && p.M % 128 == 0 &&
                             p.K % 16 == 0 && p.K >= 2048 && !p.prob[0].a.poly &&
                             !p.prob[0].b.poly;
-    id = (long_split || t0 * (t0 + 1) / 2 * p.batch * p.nprob >= (p.num_cu > 0 ? p.num_cu : 256))
-             ? 0 : 4;
+    const int64_t cu = p.num_cu > 0 ? p.num_cu : 256;
+    id = (long_split || t0 * (t0 + 1) / 2 * p.batch * p.nprob >= 4 * cu) ? 0 : 4;
   } else if (id < 0) {
     const int64_t units = (int64_t)p.batch * p.nprob;
     const int cu = p.num_cu > 0 ? p.num_cu : 256;
