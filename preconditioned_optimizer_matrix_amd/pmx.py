@@ -342,36 +342,58 @@ def polar(G, opts=None, out=None, info=None, ws=None):
     return U, info
 
 
-def polar_varbatch(Gs, opts=None, outs=None, info=None, ws=None):
+class VarBlocks:
+    """The descriptor table of a variable-size polar call: the addresses,
+    shapes and row strides of the blocks Gs (2-D, unit column stride, one
+    dtype) and of their outputs Us (allocated when not given).  Built once and
+    passed to polar_varbatch(blocks=...) on every call over the same tensors,
+    so a call marshals nothing per block; valid while those tensors live."""
+
+    def __init__(self, Gs, Us=None):
+        torch = _torch()
+        self.Gs = list(Gs)
+        if not self.Gs:
+            raise ValueError("no blocks")
+        self.Us = (list(Us) if Us is not None else
+                   [torch.empty_like(g, memory_format=torch.contiguous_format) for g in self.Gs])
+        if len(self.Us) != len(self.Gs):
+            raise ValueError("one output per block")
+        self.count = len(self.Gs)
+        self.arr = (PolarBlock * self.count)()
+        for i, (g, u) in enumerate(zip(self.Gs, self.Us)):
+            if g.dim() != 2 or u.dim() != 2:
+                raise ValueError("blocks are 2-D matrices")
+            m, n, ldg, _, _ = _mat(g)
+            _, _, ldu, _, _ = _mat(u)
+            self.arr[i] = PolarBlock(_ptr(g), _ptr(u), m, n, ldg, ldu)
+        self.dtype = _dtype_code(self.Gs[0])
+        self.device = self.Gs[0].device
+
+
+def polar_varbatch(Gs=None, opts=None, outs=None, info=None, ws=None, blocks=None):
     """Polar factors of a list of 2-D blocks of different shapes (sides up to
     VARBATCH_MAX_SIDE, one dtype) in one call: blocks of sides up to
     VARBATCH_MAX_DIM in one fused launch, larger ones grouped by shape;
-    returns (list of U, info_tensor)."""
-    torch = _torch()
+    returns (list of U, info_tensor).  `blocks` (a VarBlocks) replaces Gs and
+    outs with a descriptor table built beforehand."""
     if opts is None:
         opts = default_opts()
-    Us = outs if outs is not None else [torch.empty_like(g, memory_format=torch.contiguous_format)
-                                        for g in Gs]
-    count = len(Gs)
-    arr = (PolarBlock * count)()
-    for i, (g, u) in enumerate(zip(Gs, Us)):
-        m, n, ldg, _, _ = _mat(g)
-        _, _, ldu, _, _ = _mat(u)
-        arr[i] = PolarBlock(_ptr(g), _ptr(u), m, n, ldg, ldu)
-    dev = Gs[0].device
+    if blocks is None:
+        blocks = VarBlocks(Gs, outs)
+    count, dev = blocks.count, blocks.device
     if info is None:
         info = new_info(count, dev)
     sz = _sz()
-    check(lib.pmx_polar_varbatch_workspace_size(arr, count, _dtype_code(Gs[0]),
+    check(lib.pmx_polar_varbatch_workspace_size(blocks.arr, count, blocks.dtype,
                                                 ctypes.byref(opts), ctypes.byref(sz)),
           "polar_varbatch_workspace_size")
     need = sz.value
     if ws is None or ws.numel() < need:
         ws = workspace(need, dev)
-    check(lib.pmx_matfn_polar_varbatch(handle(dev.index), arr, count, _dtype_code(Gs[0]),
+    check(lib.pmx_matfn_polar_varbatch(handle(dev.index), blocks.arr, count, blocks.dtype,
                                        ctypes.byref(opts), _ptr(info), _ptr(ws), ws.numel(),
-                                       _stream(Gs[0])), "matfn_polar_varbatch")
-    return Us, info
+                                       _stream(blocks.Gs[0])), "matfn_polar_varbatch")
+    return blocks.Us, info
 
 
 def shampoo_config(root_opts=None, **kw):

@@ -195,3 +195,28 @@ def test_shampoo_plan_host_side():
     plan = ctypes.c_void_p()
     assert pmx.lib.pmx_shampoo_plan_create(None, ctypes.byref(c), arr, 1,
                                            ctypes.byref(plan)) == pmx.ERR_INVALID_VALUE
+
+
+def test_varblocks_descriptor_table():
+    # the reusable descriptor table of the variable-size polar call: one
+    # 32-byte entry per block with its addresses, shape and row strides
+    # (host tensors: the table is only built, nothing is launched)
+    import torch
+    from preconditioned_optimizer_matrix_amd import pmx
+    Gs = [torch.zeros(3, 5), torch.zeros(64, 64), torch.zeros(10, 40)[:, :7]]
+    Us = [torch.zeros(3, 5), torch.zeros(64, 64), torch.zeros(10, 7)]
+    vb = pmx.VarBlocks(Gs, Us)
+    assert vb.count == 3 and vb.dtype == pmx.F32
+    for e, g, u in zip(vb.arr, Gs, Us):
+        assert (e.m, e.n, e.ldg, e.ldu) == (g.shape[0], g.shape[1], g.stride(0), u.stride(0))
+        assert e.g == g.data_ptr() and e.u == u.data_ptr()
+    # outputs allocated when not given, contiguous, one per block
+    vb2 = pmx.VarBlocks(Gs)
+    assert [tuple(u.shape) for u in vb2.Us] == [(3, 5), (64, 64), (10, 7)]
+    assert all(u.is_contiguous() for u in vb2.Us)
+    with pytest.raises(ValueError):
+        pmx.VarBlocks(Gs, Us[:2])
+    with pytest.raises(ValueError):
+        pmx.VarBlocks([torch.zeros(2, 3, 4)])
+    with pytest.raises(ValueError):
+        pmx.VarBlocks([])

@@ -418,6 +418,16 @@ def test_polar_varbatch(env):
         for k in range(min(int(inf[i]["iters"][0]), st.iters)):
             if st.r[k] >= 1e-3:
                 assert abs(inf[i]["alpha"][0][k] - st.alpha[k]) < 1e-3, (i, k)
+    # a descriptor table built once and reused: two calls, the same factors
+    # bit for bit as the call that built its own table
+    Gd = [torch.from_numpy(g).to(dev) for g in Gs]
+    vb = pmx.VarBlocks(Gd)
+    for _ in range(2):
+        vb.Us[0].fill_(float("nan"))
+        Ur, _ = pmx.polar_varbatch(blocks=vb, opts=pmx.default_opts(seed=9))
+        torch.cuda.synchronize()
+        for u, ur in zip(Us, Ur):
+            assert torch.equal(u, ur)
     # bf16 blocks: fp32 inside, the factor rounded once on store
     Gb = [_bf16(torch, g).to(dev) for g in Gs[:12]]
     Ub, _ = pmx.polar_varbatch(Gb)
