@@ -1,0 +1,113 @@
+"""Seeded sweep of ragged shapes, batch sizes and options against the fp64
+oracle's closed forms (eigendecomposition roots, SVD polar factors, the EMA
+and the apply).  The cases are drawn once from a fixed seed, so every run
+checks the same ones; each prints its parameters before it runs.
+
+Tolerances are those of the fixed-shape parity tests: relative Frobenius
+error 1e-4 for the fp32 iterations, 3e-2 (and orthogonality 1e-2) for the
+bf16 polar factor, 1e-5 for the single-product statistics and apply.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import closed_form as cf
+
+pytestmark = pytest.mark.gpu
+
+_RNG = np.random.default_rng(20261204)
+# inverse roots: order (multi-kernel path above 64: 64- and 128-tiles with
+# ragged edges), root p, batch, input scale
+ROOT_CASES = [(int(_RNG.integers(65, 1100)), int(_RNG.choice([2, 4])),
+               int(_RNG.integers(1, 4)), int(_RNG.integers(0, 2))) for _ in range(8)]
+# polar factors: rows, cols (tall and wide), fp32 and bf16
+POLAR_CASES = [(int(_RNG.integers(65, 700)), int(_RNG.integers(65, 700))) for _ in range(5)]
+BF16_CASES = [(int(_RNG.integers(65, 700)), int(_RNG.integers(65, 700)), int(_RNG.integers(1, 3)))
+              for _ in range(4)]
+# statistics update and apply: gradient shape
+STATS_CASES = [(int(_RNG.integers(17, 700)), int(_RNG.integers(17, 700))) for _ in range(4)]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from preconditioned_optimizer_matrix_amd import pmx
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    return torch, pmx, dev
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("n,p,batch,scale", ROOT_CASES)
+def test_sweep_inv_root(env, n, p, batch, scale):
+    torch, pmx, dev = env
+    _say("sweep inv_root n=%d p=%d batch=%d scale=%d" % (n, p, batch, scale))
+    As = [W.spd_logu(n, 5000 + 31 * n + b)[0] for b in range(batch)]
+    A = torch.from_numpy(np.stack(As)).to(dev)
+    X, XA, info = pmx.inv_root(A, p, opts=pmx.default_opts(scale_mode=scale))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)
+    Xn, XAn = X.cpu().numpy(), XA.cpu().numpy()
+    for b in range(batch):
+        ref, ref_aux = cf.inv_root(As[b].astype(np.float64), p)
+        assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), b
+        e, ea = cf.rel_fro(Xn[b], ref), cf.rel_fro(XAn[b], ref_aux)
+        assert e < 1e-4 and ea < 1e-4, (b, e, ea)
+
+
+@pytest.mark.parametrize("m,n", POLAR_CASES)
+def test_sweep_polar_fp32(env, m, n):
+    torch, pmx, dev = env
+    _say("sweep polar fp32 %d x %d" % (m, n))
+    G = W.gaussian(m, n, 7000 + m + 3 * n)
+    U, info = pmx.polar(torch.from_numpy(G).to(dev))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)[0]
+    assert int(inf["status"]) in (pmx.CONVERGED, pmx.STAGNATED)
+    assert cf.rel_fro(U.cpu().numpy(), cf.polar(G.astype(np.float64))[0]) < 1e-4
+
+
+@pytest.mark.parametrize("m,n,batch", BF16_CASES)
+def test_sweep_polar_bf16(env, m, n, batch):
+    torch, pmx, dev = env
+    _say("sweep polar bf16 %d x %d batch=%d" % (m, n, batch))
+    Gs = [torch.from_numpy(W.gaussian(m, n, 8000 + m + 5 * n + b)).to(torch.bfloat16)
+          for b in range(batch)]
+    U, info = pmx.polar(torch.stack(Gs).to(dev), opts=pmx.default_opts(tol=1e-2))
+    torch.cuda.synchronize()
+    inf = pmx.parse_info(info)
+    k = min(m, n)
+    for b in range(batch):
+        G = Gs[b].float().numpy().astype(np.float64)
+        Un = U[b].float().cpu().numpy().astype(np.float64)
+        Up, _ = cf.polar(G)
+        Ut = Un if m >= n else Un.T
+        assert int(inf[b]["status"]) in (pmx.CONVERGED, pmx.STAGNATED), b
+        assert np.linalg.norm(Ut.T @ Ut - np.eye(k)) / np.sqrt(k) < 1e-2, b
+        assert cf.rel_fro(Un, Up) < 3e-2, b
+
+
+@pytest.mark.parametrize("m,n", STATS_CASES)
+def test_sweep_stats_and_apply(env, m, n):
+    torch, pmx, dev = env
+    _say("sweep stats/apply %d x %d" % (m, n))
+    G = W.gaussian(m, n, 9000 + m + 11 * n)
+    L0 = W.spd_logu(m, 9100 + m)[0]
+    R0 = W.spd_logu(n, 9200 + n)[0]
+    Lt, Rt = torch.from_numpy(L0).to(dev), torch.from_numpy(R0).to(dev)
+    Gt = torch.from_numpy(G).to(dev)
+    pmx.shampoo_stats_update(Gt, Lt, Rt, 0.95, 1e-6)
+    P = pmx.precond_apply(Lt, Gt, Rt)
+    torch.cuda.synchronize()
+    Lr, Rr = cf.stats_update(L0.astype(np.float64), R0.astype(np.float64), G.astype(np.float64),
+                             0.95, 1e-6)
+    assert cf.rel_fro(Lt.cpu().numpy(), Lr) < 1e-5
+    assert cf.rel_fro(Rt.cpu().numpy(), Rr) < 1e-5
+    # the apply of the updated statistics (as operands, in fp32)
+    Pr = cf.precond_apply(Lt.cpu().numpy().astype(np.float64), G.astype(np.float64),
+                          Rt.cpu().numpy().astype(np.float64))
+    assert cf.rel_fro(P.cpu().numpy(), Pr) < 1e-5
