@@ -384,6 +384,58 @@ __device__ __forceinline__ TileCoord map_item_sym(int it, int tiles, int T) {
   return c;
 }
 
+// Ragged-first order, for split-k launches over matrices whose order is not
+// a multiple of the tile: a matrix's tiles on its ragged last tile-row and
+// last tile-column come first, then its whole tiles in row-major order, so
+// the last items of the launch (the split-k tail) are whole tiles.  `tile`
+// stays the row-major index (the residual's share slot).
+__device__ __forceinline__ TileCoord map_item_ragged(int it, int tiles_m, int tiles_n, bool rrow,
+                                                     bool rcol) {
+  const int tiles = tiles_m * tiles_n;
+  TileCoord c;
+  c.z = it / tiles;
+  const int t = it - c.z * tiles;
+  const int nrow = rrow ? tiles_n : 0;                    // the last tile-row
+  const int ncol = rcol ? tiles_m - (rrow ? 1 : 0) : 0;  // the last tile-column above it
+  if (t < nrow) {
+    c.tm = tiles_m - 1;
+    c.tn = t;
+  } else if (t < nrow + ncol) {
+    c.tm = t - nrow;
+    c.tn = tiles_n - 1;
+  } else {
+    const int wn = tiles_n - (rcol ? 1 : 0), u = t - nrow - ncol;
+    c.tm = u / wn;
+    c.tn = u - c.tm * wn;
+  }
+  c.tile = c.tm * tiles_n + c.tn;
+  return c;
+}
+
+// The same for the upper triangle of T x T tiles (tm <= tn): the ragged last
+// tile-column first, then the whole tiles row by row; `tile` is the
+// row-by-row index of map_item_sym.
+__device__ __forceinline__ TileCoord map_item_sym_ragged(int it, int tiles, int T) {
+  TileCoord c;
+  c.z = it / tiles;
+  int t = it - c.z * tiles;
+  if (t < T) {
+    c.tm = t;
+    c.tn = T - 1;
+  } else {
+    t -= T;
+    int tm = 0;
+    while (t >= T - 1 - tm) {
+      t -= T - 1 - tm;
+      ++tm;
+    }
+    c.tm = tm;
+    c.tn = tm + t;
+  }
+  c.tile = c.tm * T - c.tm * (c.tm - 1) / 2 + (c.tn - c.tm);
+  return c;
+}
+
 // Split-k tail ("stream-k").  When a launch's tiles do not divide evenly
 // over the compute units, the last sk_rem items are not given out whole:
 // their k tiles, laid end to end, are cut into sk_workers equal spans, one per
@@ -405,7 +457,11 @@ __device__ __forceinline__ int span_owner(int64_t u, int64_t U, int W) {
   return w;
 }
 
-template <class C, bool TA, bool TB, int ROLE, bool SPLIT>
+// SPLIT: 0 every item whole; 1 split-k tail over whole tiles (every tile
+// whole); 2 the same on a ragged-first launch (its ragged edge tiles take
+// the general loop, so it is a variant of its own: the whole-tile form keeps
+// its registers).
+template <class C, bool TA, bool TB, int ROLE, int SPLIT>
 __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) {
   constexpr int EPI = ROLE == ROLE_RESID ? EPI_RESID : (ROLE == ROLE_STATS ? EPI_EMA : EPI_STORE);
   constexpr bool AKC = Layout<true, TA>::kc;
@@ -436,7 +492,10 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
   f32x16 acc[C::FM][C::FN];
 
   auto coord = [&](int it) __attribute__((always_inline)) {
-    return sym ? map_item_sym(it, tiles, p.tiles_m)
+    if constexpr (SPLIT == 2)
+      return sym ? map_item_sym_ragged(it, tiles, p.tiles_m)
+                 : map_item_ragged(it, p.tiles_m, p.tiles_n, p.M % C::BM != 0, p.N % C::BN != 0);
+    else return sym ? map_item_sym(it, tiles, p.tiles_m)
                : map_item(it, G > 0 ? G : 1, total, p.tiles_m, p.tiles_n, p.map_mode);
   };
   auto running = [&](const TileCoord& tc) __attribute__((always_inline)) {
@@ -469,11 +528,19 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_f32_kernel(GemmParams p) 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     __syncthreads();  // the previous item's last LDS reads are done
-    if constexpr (SPLIT) {
+    if constexpr (SPLIT == 1) {
       // launched only for whole tiles of plain NN operands
       mainloop_fast<C, false, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B, B2,
                                      pr.b.ld, pc, m0, n0, kb, ke - kb, lane, wm, wn);
       return;
+    } else if constexpr (SPLIT == 2) {
+      // plain NN operands; whole tiles (every split-k span is one) take the
+      // unchecked loop, the ragged edge tiles the general one below
+      if (m0 + C::BM <= p.M && n0 + C::BN <= p.N) {
+        mainloop_fast<C, false, false>(acc, &smem_a[0][0], &smem_b[0][0], A, A2, pr.a.ld, B,
+                                       B2, pr.b.ld, pc, m0, n0, kb, ke - kb, lane, wm, wn);
+        return;
+      }
     }
     if constexpr (AKC && !BKC && C::STAGES == 2 && C::KH == 8) {
       if (vec && m0 + C::BM <= p.M && n0 + C::BN <= p.N && p.K % C::BK == 0 &&
@@ -765,13 +832,23 @@ hipError_t launch_role(GemmParams p, hipStream_t s) {
   p.sk_part = nullptr;
   p.sk_dp = (int)total;
   p.sk_rem = p.sk_workers = 0;
+  p.ragged_first = 0;
   if (kSplitVariant<C, TA, TB, ROLE>) {
     const int cu = p.num_cu > 0 ? p.num_cu : 256;
     const int64_t nk = (p.K + C::BK - 1) / C::BK;
     const int64_t rem = total % cu;
     const int64_t W = std::min<int64_t>(std::min(cu, kSplitMaxWorkers), rem * nk / 2);
-    // split variants run whole tiles of plain operands only
-    bool whole = p.vec && p.M % C::BM == 0 && p.N % C::BN == 0 && p.K % C::BK == 0;
+    // split variants take plain operands; the tail (the last rem items) must
+    // be whole tiles: on ragged matrices the items go ragged-first (row-major
+    // tile order or the triangle), and the tail fits in the last matrix's
+    // whole tiles
+    const bool rrow = p.M % C::BM != 0, rcol = p.N % C::BN != 0;
+    const int64_t whole_tiles =
+        p.sym ? (int64_t)(p.tiles_m - rrow) * (p.tiles_m - rrow + 1) / 2
+              : (int64_t)(p.tiles_m - rrow) * (p.tiles_n - rcol);
+    const bool ragged = rrow || rcol;
+    bool whole = p.vec && p.K % C::BK == 0 && rem <= whole_tiles &&
+                 (!ragged || p.sym || p.map_mode == 2);
     for (int i = 0; i < p.nprob; ++i) whole = whole && !p.prob[i].a.poly && !p.prob[i].b.poly;
     // only as the tail of at least one whole round, or over long k: a launch
     // with fewer items than CUs runs faster unsplit when k is short (measured
@@ -785,6 +862,7 @@ hipError_t launch_role(GemmParams p, hipStream_t s) {
       p.sk_dp = (int)(total - rem);
       p.sk_rem = (int)rem;
       p.sk_workers = (int)W;
+      p.ragged_first = ragged ? 1 : 0;
     }
   }
   int64_t g = p.sk_dp;
@@ -794,11 +872,14 @@ hipError_t launch_role(GemmParams p, hipStream_t s) {
   bool launched = false;
   if constexpr (kSplitVariant<C, TA, TB, ROLE>) {
     if (p.sk_part) {
-      hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, true>), grid, block, 0, s, p);
+      if (p.ragged_first)
+        hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, 2>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, 1>), grid, block, 0, s, p);
       launched = true;
     }
   }
-  if (!launched) hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, false>), grid, block, 0, s, p);
+  if (!launched) hipLaunchKernelGGL((gemm_f32_kernel<C, TA, TB, ROLE, 0>), grid, block, 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ROLE != ROLE_RESID) return e;
   ResidDecide d;
