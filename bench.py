@@ -459,7 +459,7 @@ def sweep_sigma(args):
 
 
 UPDATE_KERNEL = ("gemm_f32_kernel<pmx::(anonymous namespace)::Cfg<128, 128, 16, 2, 2, 3, 2>, "
-                 "false, false, 1, false>")
+                 "false, false, 1, 0>")
 
 
 def write_traffic(dirs):
