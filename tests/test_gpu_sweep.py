@@ -1,7 +1,8 @@
 """Seeded sweep of ragged shapes, batch sizes and options against the fp64
 oracle's closed forms (eigendecomposition roots, SVD polar factors, the EMA
-and the apply).  The cases are drawn once from a fixed seed, so every run
-checks the same ones; each prints its parameters before it runs.
+and the apply).  The cases are drawn once from a fixed seed (plus a few fixed
+ragged orders), so every run checks the same ones; each prints its
+parameters before it runs.
 
 Tolerances are those of the fixed-shape parity tests: relative Frobenius
 error 1e-4 for the fp32 iterations, 3e-2 (and orthogonality 1e-2) for the
@@ -20,6 +21,10 @@ _RNG = np.random.default_rng(20261204)
 # ragged edges), root p, batch, input scale
 ROOT_CASES = [(int(_RNG.integers(65, 1100)), int(_RNG.choice([2, 4])),
                int(_RNG.integers(1, 4)), int(_RNG.integers(0, 2))) for _ in range(8)]
+# orders that are multiples of 16 but not of the tile: the products run
+# ragged-first with a split-k tail over whole tiles (64 x 64 tiles at 784 in
+# batches, 128 x 128 updates and 64 x 64 triangles at 2064)
+ROOT_CASES += [(784, 2, 3, 1), (784, 4, 1, 0), (2064, 4, 1, 0), (1552, 2, 2, 1)]
 # polar factors: rows, cols (tall and wide), fp32 and bf16
 POLAR_CASES = [(int(_RNG.integers(65, 700)), int(_RNG.integers(65, 700))) for _ in range(5)]
 BF16_CASES = [(int(_RNG.integers(65, 700)), int(_RNG.integers(65, 700)), int(_RNG.integers(1, 3)))
