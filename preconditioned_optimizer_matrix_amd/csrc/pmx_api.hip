@@ -27,6 +27,7 @@ struct pmx_context {
   int bf16_mn;             // bf16 polar: 1 reads X for I - X^T X via LDS transpose reads (no X^T copy)
   int bf16_persist;        // bf16 GEMM: 1 runs whole-tile launches on persistent blocks, each
                            // loading its next tile's first k tile ahead of the epilogue
+  int bf16_early;          // bf16 persistent GEMM: 1 issues each k tile's loads before the previous tile's barrier
   int small_fused;         // 1: one fused launch for orders <= kSmallMaxN
   int split_k;             // 1: split-k tail for the fp32 products of the iterations
   int bf16_sym;            // 1: bf16 X^T X and R^2 run upper-triangle tiles, mirrored
@@ -425,6 +426,7 @@ GemmParams bf16_base(const pmx_context* h, int M, int N, int K, int batch) {
   g.map_mode = h->bf16_map;
   g.dma = h->bf16_dma;
   g.persist = h->bf16_persist;
+  g.early = h->bf16_early;
   return g;
 }
 
@@ -1004,6 +1006,8 @@ pmx_status pmx_create(pmx_handle* handle, int device) {
   if (const char* e = getenv("PMX_BF16_MN")) c->bf16_mn = atoi(e);
   c->bf16_persist = 1;
   if (const char* e = getenv("PMX_BF16_PERSIST")) c->bf16_persist = atoi(e);
+  c->bf16_early = 1;
+  if (const char* e = getenv("PMX_BF16_EARLY")) c->bf16_early = atoi(e);
   c->small_fused = 1;
   if (const char* e = getenv("PMX_SMALL")) c->small_fused = atoi(e);
   c->split_k = 1;

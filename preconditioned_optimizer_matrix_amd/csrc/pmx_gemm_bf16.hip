@@ -405,6 +405,183 @@ __device__ __forceinline__ void mn_kloop(f32x16 (&acc)[C::FM][C::FN], uint16_t (
   }
 }
 
+// Early-load forms of the two k loops (persistent kernel, at least two k
+// tiles an item): on entry to k tile kt the registers already hold the loads
+// of tile kt + 1, issued at the end of tile kt - 1.  Tile kt + 1 goes from
+// the registers into the other LDS buffer during the last 16-wide step, then
+// the loads of tile kt + 2 are issued before the barrier, so a load has the
+// barrier wait and the next tile's first fragment reads as extra cover.
+// Tiles past the item's last are k tiles 0 and 1 of `nx`.
+template <class C>
+__device__ __forceinline__ void fast_load(u32x4 (&va)[C::CA], u32x4 (&vb)[C::CB], TileBase t,
+                                          int kt, const FastOffsets<C>& o) {
+  const uint16_t* la = t.a + kt * C::BK;
+  const uint16_t* lb = t.b + kt * C::BK;
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(la + (o.a + i * o.sa));
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(lb + (o.b + i * o.sb));
+}
+
+template <class C>
+__device__ __forceinline__ void fast_stage0_early(uint16_t (*smem)[C::LDS], TileBase tb,
+                                                  const FastOffsets<C>& o, u32x4 (&va)[C::CA],
+                                                  u32x4 (&vb)[C::CB]) {
+  constexpr int RS = C::NT / C::CH, LDK = C::LDK;
+  fast_load<C>(va, vb, tb, 0, o);
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) *reinterpret_cast<u32x4*>(smem[0] + o.wofs + i * RS * LDK) = va[i];
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i)
+    *reinterpret_cast<u32x4*>(smem[0] + C::BM * LDK + o.wofs + i * RS * LDK) = vb[i];
+  fast_load<C>(va, vb, tb, 1, o);
+  __syncthreads();
+}
+
+template <class C>
+__device__ __forceinline__ void fast_kloop_early(f32x16 (&acc)[C::FM][C::FN],
+                                                 uint16_t (*smem)[C::LDS], int buf, TileBase cur,
+                                                 TileBase nx, const FastOffsets<C>& o, int nk,
+                                                 int lane, int wm, int wn, u32x4 (&va)[C::CA],
+                                                 u32x4 (&vb)[C::CB]) {
+  constexpr int FM = C::FM, FN = C::FN, CA = C::CA, CB = C::CB;
+  constexpr int BK = C::BK, LDK = C::LDK, STEPS = BK / 16;
+  constexpr int NF = FM + FN, RS = C::NT / C::CH, MF = FM * FN;
+  const int ra = (wm + (lane & 31)) * LDK + (lane >> 5) * 8;
+  const int rb = (C::BM + wn + (lane & 31)) * LDK + (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cb = (kt + buf) & 1;
+    const uint16_t* sa = smem[cb] + ra;
+    const uint16_t* sb = smem[cb] + rb;
+    uint16_t* dst = smem[cb ^ 1] + o.wofs;
+    const int j = kt + 2;  // the tile the registers load next
+    const TileBase lt = j < nk ? cur : nx;
+    const int lk = j < nk ? j : j - nk;
+    bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(sa + 32 * i * LDK);
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) fb[0][jj] = *reinterpret_cast<const bf16x8*>(sb + 32 * jj * LDK);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const int c = s & 1, n = c ^ 1;
+      if (s + 1 < STEPS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[n][i] = *reinterpret_cast<const bf16x8*>(sa + 32 * i * LDK + 16 * (s + 1));
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+          fb[n][jj] = *reinterpret_cast<const bf16x8*>(sb + 32 * jj * LDK + 16 * (s + 1));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][jj], acc[i][jj], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(dst + i * RS * LDK) = va[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(dst + C::BM * LDK + i * RS * LDK) = vb[i];
+    fast_load<C>(va, vb, lt, lk, o);
+    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // step 0 fragments
+#pragma unroll
+    for (int s = 0; s + 1 < STEPS; ++s) sched_interleave<MF, NF, 0x100, (NF + MF - 1) / MF>();
+    sched_interleave<MF, CA + CB, 0x200, (CA + CB + MF - 1) / MF>();
+    __builtin_amdgcn_sched_group_barrier(0x020, CA + CB, 0);  // tile kt + 2, global
+    __syncthreads();
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mn_load(u32x4 (&va)[C::BK * MnOffsets<C>::CPA / C::NT],
+                                        u32x4 (&vb)[C::BK * MnOffsets<C>::CPB / C::NT],
+                                        TileBase t, int kt, const MnOffsets<C>& o, int64_t lda,
+                                        int64_t ldb) {
+  using O = MnOffsets<C>;
+  constexpr int CA = C::BK * O::CPA / C::NT, CB = C::BK * O::CPB / C::NT;
+  const uint16_t* la = t.a + (int64_t)kt * C::BK * lda;
+  const uint16_t* lb = t.b + (int64_t)kt * C::BK * ldb;
+#pragma unroll
+  for (int i = 0; i < CA; ++i) va[i] = *reinterpret_cast<const u32x4*>(la + (o.a + i * o.sa));
+#pragma unroll
+  for (int i = 0; i < CB; ++i) vb[i] = *reinterpret_cast<const u32x4*>(lb + (o.b + i * o.sb));
+}
+
+template <class C>
+__device__ __forceinline__ void mn_stage0_early(uint16_t (*smem)[C::LDS], TileBase tb,
+                                                const MnOffsets<C>& o, int64_t lda, int64_t ldb,
+                                                u32x4 (&va)[C::BK * MnOffsets<C>::CPA / C::NT],
+                                                u32x4 (&vb)[C::BK * MnOffsets<C>::CPB / C::NT]) {
+  using O = MnOffsets<C>;
+  constexpr int CA = C::BK * O::CPA / C::NT, CB = C::BK * O::CPB / C::NT;
+  mn_load<C>(va, vb, tb, 0, o, lda, ldb);
+#pragma unroll
+  for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(smem[0] + o.wa + i * O::RSA * O::PA) = va[i];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(smem[0] + o.wb + i * O::RSB * O::PB) = vb[i];
+  mn_load<C>(va, vb, tb, 1, o, lda, ldb);
+  __syncthreads();
+}
+
+template <class C>
+__device__ __forceinline__ void mn_kloop_early(f32x16 (&acc)[C::FM][C::FN],
+                                               uint16_t (*smem)[C::LDS], int buf, TileBase cur,
+                                               TileBase nx, const MnOffsets<C>& o, int64_t lda,
+                                               int64_t ldb, int nk, int lane, int wm, int wn,
+                                               u32x4 (&va)[C::BK * MnOffsets<C>::CPA / C::NT],
+                                               u32x4 (&vb)[C::BK * MnOffsets<C>::CPB / C::NT]) {
+  using O = MnOffsets<C>;
+  constexpr int FM = C::FM, FN = C::FN, BK = C::BK, STEPS = BK / 16;
+  constexpr int PA = O::PA, PB = O::PB;
+  constexpr int CA = BK * O::CPA / C::NT, CB = BK * O::CPB / C::NT;
+  constexpr int NF = 2 * (FM + FN), MF = FM * FN;
+  const int g = lane >> 4, jl = lane & 15;
+  const int ra = (8 * (g >> 1) + (jl >> 2)) * PA + 16 * (g & 1) + 4 * (jl & 3) + wm;
+  const int rb = BK * PA + (8 * (g >> 1) + (jl >> 2)) * PB + 16 * (g & 1) + 4 * (jl & 3) + wn;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cb = (kt + buf) & 1;
+    const uint16_t* sa = smem[cb] + ra;
+    const uint16_t* sb = smem[cb] + rb;
+    uint16_t* dst = smem[cb ^ 1];
+    const int j = kt + 2;
+    const TileBase lt = j < nk ? cur : nx;
+    const int lk = j < nk ? j : j - nk;
+    bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = frag_tr(sa + 32 * i, PA);
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) fb[0][jj] = frag_tr(sb + 32 * jj, PB);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int c = st & 1, n = c ^ 1;
+      if (st + 1 < STEPS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[n][i] = frag_tr(sa + 32 * i + 16 * (st + 1) * PA, PA);
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) fb[n][jj] = frag_tr(sb + 32 * jj + 16 * (st + 1) * PB, PB);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+          acc[i][jj] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][jj], acc[i][jj], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(dst + o.wa + i * O::RSA * PA) = va[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(dst + o.wb + i * O::RSB * PB) = vb[i];
+    mn_load<C>(va, vb, lt, lk, o, lda, ldb);
+    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+#pragma unroll
+    for (int st = 0; st + 1 < STEPS; ++st) sched_interleave<MF, NF, 0x100, (NF + MF - 1) / MF>();
+    sched_interleave<MF, CA + CB, 0x200, (CA + CB + MF - 1) / MF>();
+    __builtin_amdgcn_sched_group_barrier(0x020, CA + CB, 0);
+    __syncthreads();
+  }
+}
+
 template <class C>
 __device__ __forceinline__ void mainloop_fast_mn(f32x16 (&acc)[C::FM][C::FN],
                                                  uint16_t (*smem)[C::LDS], const uint16_t* A,
@@ -766,8 +943,11 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&acc)[C::FM][C::FN],
 // wait for them).  The blocks of one XCD (block index x mod 8) take a
 // contiguous range of items, as many at a time as the XCD has blocks.  The
 // epilogue goes through the free LDS buffer (staged_epilogue): no transposed
-// copy, and output rows that allow 16-byte stores.
-template <class C, int ROLE, bool MN>
+// copy, and output rows that allow 16-byte stores.  EARLY (items of at least
+// two k tiles): the k loops issue each k tile's loads before the previous
+// tile's barrier (fast_kloop_early, mn_kloop_early): across the epilogue the
+// next item's k tile 0 is staged and its k tile 1 in flight.
+template <class C, int ROLE, bool MN, bool EARLY = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_persist_kernel(GemmParams p) {
   constexpr int FM = C::FM, FN = C::FN;
   constexpr int WGN = C::BN / C::WN;
@@ -812,8 +992,17 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_persist_kernel(GemmP
   using Off = std::conditional_t<MN, MnOffsets<C>, FastOffsets<C>>;
   const Off o(lda, ldb);
   int buf = 0;
-  if constexpr (MN) mn_stage0<C>(smem, buf, cur, o);
-  else fast_stage0<C>(smem, buf, cur, o);
+  using LA = u32x4[MN ? C::BK * MnOffsets<C>::CPA / C::NT : C::CA];
+  using LB = u32x4[MN ? C::BK * MnOffsets<C>::CPB / C::NT : C::CB];
+  LA va;
+  LB vb;
+  if constexpr (EARLY) {
+    if constexpr (MN) mn_stage0_early<C>(smem, cur, o, lda, ldb, va, vb);
+    else fast_stage0_early<C>(smem, cur, o, va, vb);
+  } else {
+    if constexpr (MN) mn_stage0<C>(smem, buf, cur, o);
+    else fast_stage0<C>(smem, buf, cur, o);
+  }
   for (;;) {
     int b2 = b, tm2 = tm, tn2 = tn, tile2 = tile;
     const bool more = next_item(b2, tm2, tn2, tile2);
@@ -826,8 +1015,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_bf16_persist_kernel(GemmP
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    if constexpr (MN) mn_kloop<C>(acc, smem, buf, cur, nx, o, lda, ldb, nk, lane, wm, wn);
-    else fast_kloop<C>(acc, smem, buf, cur, nx, o, nk, lane, wm, wn);
+    if constexpr (EARLY) {
+      if constexpr (MN) mn_kloop_early<C>(acc, smem, buf, cur, nx, o, lda, ldb, nk, lane, wm, wn, va, vb);
+      else fast_kloop_early<C>(acc, smem, buf, cur, nx, o, nk, lane, wm, wn, va, vb);
+    } else {
+      if constexpr (MN) mn_kloop<C>(acc, smem, buf, cur, nx, o, lda, ldb, nk, lane, wm, wn);
+      else fast_kloop<C>(acc, smem, buf, cur, nx, o, nk, lane, wm, wn);
+    }
     // the buffer the last k tile was read from is free until the next item's
     // first k tile step stores into it
     staged_epilogue<C, ROLE>(acc, p, pr, b, tm * C::BM, tn * C::BN, tile, lane, wm, wn, red,
@@ -1042,6 +1236,26 @@ hipError_t launch_cfg(GemmParams p, int role, hipStream_t s) {
       const int64_t total = (int64_t)p.tiles_m * p.tiles_n * p.batch;
       const int64_t cu = p.num_cu > 0 ? p.num_cu : 256;
       const dim3 grid((unsigned)(total < cu ? total : cu)), block(C::NT);
+      const bool early = p.early && p.K >= 2 * C::BK;
+      if (early) {
+        if (p.mn) {
+          hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_RESID, true, true>), grid, block, 0, s, p);
+        } else {
+          switch (role) {
+            case ROLE_RESID:
+              hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_RESID, false, true>), grid, block, 0, s, p);
+              break;
+            case ROLE_POWER:
+              hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_POWER, false, true>), grid, block, 0, s, p);
+              break;
+            case ROLE_UPDATE:
+              hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_UPDATE, false, true>), grid, block, 0, s, p);
+              break;
+            default: return hipErrorInvalidValue;
+          }
+        }
+        return after_resid(p, role, (int)(total / p.batch), s);
+      }
       if (p.mn) {
         hipLaunchKernelGGL((gemm_bf16_persist_kernel<C, ROLE_RESID, true>), grid, block, 0, s, p);
       } else {
@@ -1111,7 +1325,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int role, hipStream_t s) {
   }
   if (cfg == 2) return launch_cfg<BLarge4>(p, role, s);
   if (cfg == 3) return launch_cfg<BMid2>(p, role, s);
-  if (cfg == 1 && p.dma && p.vec && p.M % 256 == 0 && p.N % 256 == 0 && p.K % DBK == 0 &&
+  if (cfg == 1 && p.dma == 1 && p.vec && p.M % 256 == 0 && p.N % 256 == 0 && p.K % DBK == 0 &&
       p.K >= DBK && ((uintptr_t)p.prob[0].a.ptr & 15) == 0 && ((uintptr_t)p.prob[0].b.ptr & 15) == 0)
     return launch_dma(p, role, s);
   return cfg == 1 ? launch_cfg<BLarge>(p, role, s) : launch_cfg<BSmall>(p, role, s);

@@ -299,6 +299,7 @@ struct GemmParams {
   int mn;          // bf16 residual: A and Bs given m- / n-contiguous (K x M, K x N)
   int sym_small;   // bf16 symmetric launches: 128 x 128 tiles instead of 256 x 256
   int persist;     // bf16 whole 256 x 256 tiles: persistent blocks, next tile's loads overlapped
+  int early;       // bf16 persistent blocks: each k tile's loads issued before the previous tile's barrier
   int ragged_first; // fp32 split-k launches over ragged matrices: edge tiles first (set by the launcher)
   int num_cu;
   Ctrl* ctrl;      // per-matrix control blocks; null = unconditional

@@ -780,8 +780,9 @@ def test_polar_bf16_persistent_mixed_convergence(env, monkeypatch):
     # inside the persistent blocks' item walk (whose last k tile prefetches
     # the next running item).  The persistent kernel runs each tile's k loop
     # in the same order and stores the same values as the one-block-per-tile
-    # kernel (a handle created with PMX_BF16_PERSIST=0), so the two calls must
-    # agree bit for bit; both against the SVD factor.
+    # kernel (a handle created with PMX_BF16_PERSIST=0) and as the persistent
+    # kernel without the early loads (PMX_BF16_EARLY=0), so the calls must
+    # agree bit for bit; all against the SVD factor.
     import ctypes
     torch, pmx, dev = env
     _say("polar bf16 persistent blocks, mixed convergence 64 x 1024 x 512")
@@ -794,22 +795,32 @@ def test_polar_bf16_persistent_mixed_convergence(env, monkeypatch):
     Gt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
     opts = pmx.default_opts(tol=1e-2)
     U, info = pmx.polar(Gt, opts=opts)
-    monkeypatch.setenv("PMX_BF16_PERSIST", "0")
-    h = ctypes.c_void_p()
-    pmx.check(pmx.lib.pmx_create(ctypes.byref(h), 0), "create")
-    monkeypatch.delenv("PMX_BF16_PERSIST")
-    try:
-        U0 = torch.empty_like(Gt)
-        info0 = pmx.new_info(64, dev)
-        need = pmx.workspace_bytes(pmx.OP_POLAR, 1024, 512, 64, pmx.BF16, opts)
-        ws = pmx.workspace(need, dev)
-        pmx.check(pmx.lib.pmx_matfn_polar_batched(
-            h, pmx._ptr(Gt), pmx.BF16, 1024, 512, 512, 1024 * 512, pmx._ptr(U0), 512,
-            1024 * 512, 64, ctypes.byref(opts), pmx._ptr(info0), pmx._ptr(ws), ws.numel(),
-            pmx._stream(Gt)), "polar")
-        torch.cuda.synchronize()
-    finally:
-        pmx.lib.pmx_destroy(h)
+
+    def with_env(var):
+        # the same call on a handle created with `var` = 0
+        monkeypatch.setenv(var, "0")
+        h = ctypes.c_void_p()
+        pmx.check(pmx.lib.pmx_create(ctypes.byref(h), 0), "create")
+        monkeypatch.delenv(var)
+        try:
+            Uo = torch.empty_like(Gt)
+            info_o = pmx.new_info(64, dev)
+            need = pmx.workspace_bytes(pmx.OP_POLAR, 1024, 512, 64, pmx.BF16, opts)
+            ws = pmx.workspace(need, dev)
+            pmx.check(pmx.lib.pmx_matfn_polar_batched(
+                h, pmx._ptr(Gt), pmx.BF16, 1024, 512, 512, 1024 * 512, pmx._ptr(Uo), 512,
+                1024 * 512, 64, ctypes.byref(opts), pmx._ptr(info_o), pmx._ptr(ws), ws.numel(),
+                pmx._stream(Gt)), "polar")
+            torch.cuda.synchronize()
+        finally:
+            pmx.lib.pmx_destroy(h)
+        return Uo, info_o
+
+    U0, info0 = with_env("PMX_BF16_PERSIST")
+    # persistent blocks whose loads are issued after each k tile's barrier
+    # (the early loads switched off): the same values again
+    U1, _ = with_env("PMX_BF16_EARLY")
+    assert torch.equal(U.view(torch.int16), U1.view(torch.int16))
     infs, infs0 = pmx.parse_info(info), pmx.parse_info(info0)
     iters = [int(i["iters"][0]) for i in infs]
     print("  updates: well conditioned %s, ill conditioned %s" % (
