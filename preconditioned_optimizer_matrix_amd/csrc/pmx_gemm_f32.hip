@@ -191,11 +191,14 @@ __device__ __forceinline__ void read_frag(float (&f)[8], const float* __restrict
 // A stored k-contiguous and B stored m/n-contiguous, the layout of every
 // square product of the iteration.  A k tile is one basic block whose
 // schedule is fixed with scheduling-group barriers: the A fragments of the
-// whole k tile and the first B fragments are read, the next tile's global
-// loads issued (with the polynomial formed as they arrive), and each k step's
-// MFMAs are interleaved with the B fragment reads of the following step; the
-// last step's MFMAs are interleaved with the LDS stores of the next tile
-// (into the other buffer, which no wave reads in this k tile).
+// whole k tile and the first B fragments are read, and each k step's MFMAs
+// are interleaved with the B fragment reads of the following step; the last
+// step's MFMAs are interleaved with the LDS stores of the next tile (into
+// the other buffer, which no wave reads in this k tile; the polynomial is
+// formed as they are stored), and the loads of the tile after it are issued
+// right after those stores, before the barrier, so that they have the
+// barrier wait and the next tile's first fragment reads as cover (the
+// registers hold one tile in flight throughout).
 template <int MF, int OPS, int MASK, int PER>
 __device__ __forceinline__ void sched_interleave() {
   if constexpr (MF > 0) {
@@ -284,12 +287,14 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[FM_][FN_], float* sm
   };
   gload(kb * BK);
   lstore(0, kb * BK);
+  gload((kb + (nk > 1 ? 1 : 0)) * BK);  // early: tile 1 in flight
   __syncthreads();
   const int fa_ofs = (wm + (lane & 31)) * TA::LD + (lane >> 5) * KH;
   const int fb_ofs = ((lane >> 5) * KH) * TB::LD + wn + (lane & 31);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const int kn = (kb + (kt + 1 < nk ? kt + 1 : kt)) * BK;  // the last tile reloads itself
+    const int kn2 = (kb + (kt + 2 < nk ? kt + 2 : nk - 1)) * BK;  // early: the tile after it
     const float* sa = smem_a(cur) + fa_ofs;
     const float* sb = smem_b(cur) + fb_ofs;
     f32x4 fa[FM][2];
@@ -301,7 +306,6 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[FM_][FN_], float* sm
     float fb[2][FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[0][j] = sb[32 * j];
-    gload(kn);
 #pragma unroll
     for (int s = 0; s < KH; ++s) {
       const int c = s & 1, n = c ^ 1;
@@ -317,12 +321,13 @@ __device__ __forceinline__ void mainloop_fast(f32x16 (&acc)[FM_][FN_], float* sm
                                                            acc[i][j], 0, 0, 0);
     }
     lstore(cur ^ 1, kn);
+    gload(kn2);
     // schedule of the k tile
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM + FN, 0);  // A, first B fragments
-    __builtin_amdgcn_sched_group_barrier(0x020, (NA + NB) * ((APOLY || BPOLY) ? 2 : 1), 0);
 #pragma unroll
     for (int s = 0; s + 1 < KH; ++s) sched_interleave<MF, FN, 0x100, (FN + MF - 1) / MF>();
     sched_interleave<MF, NA + NB, 0x200, (NA + NB + MF - 1) / MF>();
+    __builtin_amdgcn_sched_group_barrier(0x020, (NA + NB) * ((APOLY || BPOLY) ? 2 : 1), 0);
     __syncthreads();
   }
 }
